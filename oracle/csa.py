@@ -1,0 +1,248 @@
+"""The compressed sparse attention path, one sequence and one query at a time.
+
+Notation: D = d_nope + d_rope channels per KV row (512 + 64 in every
+workload); m tokens fold into one compressed entry; entry j covers raw
+positions [j*m, (j+1)*m); a query at raw position p (0-based) sees entry j
+when (j+1)*m - 1 <= p and j is below the sequence's entry count.
+
+Readings of the pages taken here (each is listed with its reason in the
+design notes of the repository):
+
+* Pooling [V4, "ハイブリッド注意：CSAとHCA", CSA paragraph and Fig. 3]:
+  softmax-gated pooling with a learned positional bias.  The gate logit z is
+  a per-token, per-channel stream of the same shape as the KV rows (the
+  parallel projections C and Z of [V4.1], CED paragraph, eq. 1); a single
+  gate channel (G = 1) is broadcast.  The bias b_i (one value per slot i of
+  the m-token block) is added to the logit, and the softmax runs over the m
+  tokens of the block independently per channel.  Blocks do not overlap
+  ([V4.1], CSA2 paragraph: CSA2 drops the overlap of compressed entries).
+* Indexer key [V4.1], CSA2 paragraph: the indexer key is a projection of
+  the main KV entry; it is taken from the pooled entry before quantisation,
+  kI = W_IK^T c, and stored in MXFP4 like the main entry.
+* Indexer score [V4], CSA paragraph: FP4 keys, ReLU-scored multi-head dot
+  product; one key per entry shared by all indexer heads, per-head weights
+  w_h of any sign: s_j = sum_h w_h * max(0, qI_h . kI_j).
+* Top-k: the min(k, |visible|) entries of largest score, exact ties to the
+  lower entry index, returned in ascending entry order and padded with -1.
+* Attention [V4], Fig. 3 and Fig. 4: one softmax over the union of the
+  selected (or, for HCA, all visible) compressed entries and the sliding
+  window of raw rows at positions max(0, p - n_win + 1) .. p; the key and
+  the value are the same full D-channel decoded entry; no rotation is
+  applied to the positional channels (they are data here).
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+from .formats import (
+    bf16_to_f64,
+    e4m3_to_f64,
+    f32_to_bf16,
+    mxfp4_decode,
+    mxfp4_encode,
+)
+
+
+def visible_count(p: int, m: int, n_entries: int) -> int:
+    """Number of compressed entries visible to a query at raw position p."""
+    if p < 0:
+        return 0
+    return int(max(0, min(int(n_entries), (int(p) + 1) // int(m))))
+
+
+def pool_block(x_rows: np.ndarray, z_rows: np.ndarray, bias: np.ndarray) -> np.ndarray:
+    """Softmax-gated pooling of one m-token block.
+
+    x_rows: float64 [m][D]; z_rows: float64 [m][G] with G = D or 1;
+    bias: float64 [m].  Returns c[d] = sum_i softmax_i(z[i, d] + bias[i]) * x[i, d].
+    """
+    a = z_rows + bias[:, None]
+    a = np.broadcast_to(a, x_rows.shape)
+    e = np.exp(a - a.max(axis=0, keepdims=True))
+    w = e / e.sum(axis=0, keepdims=True)
+    return (w * x_rows).sum(axis=0)
+
+
+def compress(x_u16, z_u16, bias_f32, w_ik_u16, m: int, d_nope: int = 512) -> dict:
+    """Compressor of one sequence: raw rows -> compressed cache planes.
+
+    x_u16 bf16 bits [T][D]; z_u16 bf16 bits [T][G]; bias_f32 [m];
+    w_ik_u16 bf16 bits [D][d_idx] or None (no indexer keys, as in HCA).
+    T must be a multiple of m.  The quantisation decisions are taken on the
+    float32 rounding of the float64 pooled value, the precision in which the
+    GPU kernel holds it (the pages fix no precision for this step).
+
+    Returns a dict with the cache planes (``nope`` uint8 [N][d_nope/2],
+    ``nscale`` uint8 [N][d_nope/32], ``rope`` uint16 [N][D-d_nope],
+    ``ikey`` uint8 [N][d_idx/2], ``iscale`` uint8 [N][d_idx/32]) and the
+    float64 intermediates ``pooled`` [N][D], ``pooled_abs`` (sum of the
+    absolute weighted terms, a bound on the size of the rounding error of any
+    evaluation order), ``kI`` [N][d_idx] and ``kI_abs``.
+    """
+    x = bf16_to_f64(x_u16)
+    z = bf16_to_f64(z_u16)
+    bias = np.asarray(bias_f32, dtype=np.float32).astype(np.float64)
+    T, D = x.shape
+    if T % m:
+        raise ValueError("T must be a multiple of m")
+    if bias.shape != (m,):
+        raise ValueError("one bias value per block slot")
+    N = T // m
+    G = z.shape[1]
+    xb = x.reshape(N, m, D)
+    zb = z.reshape(N, m, G)
+    a = np.broadcast_to(zb + bias[None, :, None], (N, m, D))
+    e = np.exp(a - a.max(axis=1, keepdims=True))
+    w = e / e.sum(axis=1, keepdims=True)
+    pooled = (w * xb).sum(axis=1)
+    pooled_abs = (w * np.abs(xb)).sum(axis=1)
+
+    c32 = pooled.astype(np.float32)
+    nope, nscale = mxfp4_encode(c32[:, :d_nope])
+    rope = f32_to_bf16(c32[:, d_nope:])
+    out = dict(pooled=pooled, pooled_abs=pooled_abs, nope=nope, nscale=nscale, rope=rope,
+               ikey=None, iscale=None, kI=None, kI_abs=None)
+    if w_ik_u16 is not None:
+        W = bf16_to_f64(w_ik_u16)
+        kI = pooled @ W
+        out["kI"] = kI
+        out["kI_abs"] = np.abs(pooled) @ np.abs(W)
+        out["ikey"], out["iscale"] = mxfp4_encode(kI.astype(np.float32))
+    return out
+
+
+def decode_entries(nope, nscale, rope) -> np.ndarray:
+    """Cache planes of some entries -> float64 [n][d_nope + d_rope]."""
+    return np.concatenate([mxfp4_decode(nope, nscale), bf16_to_f64(rope)], axis=-1)
+
+
+def index_scores(ikey, iscale, qI_u8, w_f32, js) -> np.ndarray:
+    """Lightning-indexer scores of entries ``js`` for one query.
+
+    ikey uint8 [N][d_idx/2], iscale uint8 [N][d_idx/32] (MXFP4 keys);
+    qI_u8 E4M3 codes [H_I][d_idx]; w_f32 [H_I].
+    s_j = sum_h w_h * max(0, qI_h . kI_j), all in float64 from exact decodes.
+    """
+    js = np.asarray(js, dtype=np.int64)
+    k = mxfp4_decode(np.asarray(ikey)[js], np.asarray(iscale)[js])
+    q = e4m3_to_f64(qI_u8)
+    w = np.asarray(w_f32, dtype=np.float32).astype(np.float64)
+    dots = k @ q.T
+    return (np.maximum(dots, 0.0) * w[None, :]).sum(axis=1)
+
+
+def topk_select(scores, js, k: int) -> tuple[np.ndarray, np.ndarray]:
+    """Top-k of (score, entry) pairs: largest scores, ties to the lower entry.
+
+    Returns (idx int32 [k] ascending and padded with -1, score of each
+    selected entry in the same order, NaN in the padding).
+    """
+    scores = np.asarray(scores, dtype=np.float64)
+    js = np.asarray(js, dtype=np.int64)
+    order = np.lexsort((js, -scores))
+    take = order[: min(int(k), len(js))]
+    sel = np.sort(js[take])
+    pos = {int(j): i for i, j in enumerate(js)}
+    idx = np.full(int(k), -1, dtype=np.int32)
+    sc = np.full(int(k), np.nan, dtype=np.float64)
+    idx[: len(sel)] = sel
+    sc[: len(sel)] = [scores[pos[int(j)]] for j in sel]
+    return idx, sc
+
+
+def index_topk(ikey, iscale, qI_u8, w_f32, p: int, m: int, n_entries: int, k: int, cand=None):
+    """Indexer plus top-k for one query at raw position p.
+
+    Without ``cand`` every visible entry is scored.  With ``cand`` (the
+    entries an earlier layer selected, -1 meaning none; [V4.1] Fig. 4,
+    Reindex mode) only the visible candidates are rescored; repeated
+    candidates count once.  Returns (idx [k], selected scores [k], all
+    scored entries, their scores).
+    """
+    V = visible_count(p, m, n_entries)
+    if cand is None:
+        js = np.arange(V, dtype=np.int64)
+    else:
+        c = np.asarray(cand, dtype=np.int64)
+        js = np.unique(c[(c >= 0) & (c < V)])
+    s = index_scores(ikey, iscale, qI_u8, w_f32, js) if len(js) else np.zeros(0)
+    idx, sc = topk_select(s, js, k)
+    return idx, sc, js, s
+
+
+def attention(q_u16, keys: np.ndarray, scale) -> tuple[np.ndarray, np.ndarray]:
+    """Softmax attention of H query heads over n keys, the value equal to the key.
+
+    q_u16 bf16 bits [H][D]; keys float64 [n][D]; scale is the float32
+    softmax scale.  Returns (o float64 [H][D], lse float64 [H]); with no key
+    at all o = 0 and lse = -inf.
+    """
+    q = bf16_to_f64(q_u16)
+    H, D = q.shape
+    if keys.shape[0] == 0:
+        return np.zeros((H, D)), np.full(H, -np.inf)
+    s = float(np.float32(scale))
+    logits = s * (q @ keys.T)
+    mx = logits.max(axis=1, keepdims=True)
+    e = np.exp(logits - mx)
+    den = e.sum(axis=1, keepdims=True)
+    o = (e / den) @ keys
+    lse = (mx + np.log(den))[:, 0]
+    return o, lse
+
+
+def _window_rows(swa_u16, swa_pos0: int, p: int, n_win: int) -> np.ndarray:
+    """Raw rows of the sliding window of a query at p that the buffer holds."""
+    if n_win <= 0 or p < 0:
+        return np.zeros((0, np.asarray(swa_u16).shape[-1]))
+    lo = max(0, p - n_win + 1, int(swa_pos0))
+    hi = min(p, int(swa_pos0) + np.asarray(swa_u16).shape[0] - 1)
+    if hi < lo:
+        return np.zeros((0, np.asarray(swa_u16).shape[-1]))
+    return bf16_to_f64(np.asarray(swa_u16)[lo - swa_pos0: hi - swa_pos0 + 1])
+
+
+def sparse_attention(q_u16, nope, nscale, rope, idx, swa_u16, swa_pos0, p, n_win, scale,
+                     m: int, n_entries: int):
+    """Attention over the selected compressed entries plus the sliding window.
+
+    ``idx`` lists entry indices; -1 and entries not visible at p are
+    skipped; a repeated index is attended once per occurrence.  Returns
+    (o [H][D], lse [H]).
+    """
+    V = visible_count(p, m, n_entries)
+    idx = np.asarray(idx, dtype=np.int64)
+    sel = idx[(idx >= 0) & (idx < V)]
+    ent = decode_entries(np.asarray(nope)[sel], np.asarray(nscale)[sel], np.asarray(rope)[sel])
+    win = _window_rows(swa_u16, swa_pos0, p, n_win)
+    return attention(q_u16, np.concatenate([ent, win], axis=0), scale)
+
+
+def dense_attention(q_u16, nope, nscale, rope, swa_u16, swa_pos0, p, n_win, scale, m, n_entries):
+    """HCA [V4], Fig. 4: every visible compressed entry plus the same window."""
+    V = visible_count(p, m, n_entries)
+    return sparse_attention(q_u16, nope, nscale, rope, np.arange(V), swa_u16, swa_pos0, p,
+                            n_win, scale, m, n_entries)
+
+
+def csa2_pair(cache: dict, layer_a: dict, layer_b: dict, p: int, m: int, n_entries: int,
+              n_win: int, scale, k_a: int, k_b: int):
+    """Two CSA2 layers for one query, [V4.1] Fig. 4: a Full layer then a Reindex layer.
+
+    Layer A scores every visible entry with its own indexer query and keeps
+    k_a; layer B reuses A's main and indexer-key caches, rescores only A's
+    selection with its own indexer query and weights, keeps k_b, and attends
+    with its own query and its own window rows over A's main cache.
+    ``layer_*`` hold ``qI``, ``w``, ``q``, ``swa`` and ``swa_pos0``.
+    """
+    idx_a, sc_a, _, _ = index_topk(cache["ikey"], cache["iscale"], layer_a["qI"], layer_a["w"],
+                                   p, m, n_entries, k_a)
+    o_a, lse_a = sparse_attention(layer_a["q"], cache["nope"], cache["nscale"], cache["rope"], idx_a,
+                                  layer_a["swa"], layer_a["swa_pos0"], p, n_win, scale, m, n_entries)
+    idx_b, sc_b, _, _ = index_topk(cache["ikey"], cache["iscale"], layer_b["qI"], layer_b["w"],
+                                   p, m, n_entries, k_b, cand=idx_a)
+    o_b, lse_b = sparse_attention(layer_b["q"], cache["nope"], cache["nscale"], cache["rope"], idx_b,
+                                  layer_b["swa"], layer_b["swa_pos0"], p, n_win, scale, m, n_entries)
+    return dict(idx_a=idx_a, score_a=sc_a, o_a=o_a, lse_a=lse_a,
+                idx_b=idx_b, score_b=sc_b, o_b=o_b, lse_b=lse_b)

@@ -1,0 +1,51 @@
+"""Mutation check of the oracle pins (CPU only; run: python tests/oracle_mutations.py).
+
+Each entry plants one plausible mistake in a scratch copy of oracle/ and
+expects at least one oracle pin test to fail.  Not collected by pytest.
+"""
+import os
+import shutil
+import subprocess
+import sys
+import tempfile
+
+MUT = os.path.join(tempfile.gettempdir(), "csa_oracle_mutant")
+muts = [
+ ("csa.py", "a = z_rows + bias[:, None]", "a = z_rows"),
+ ("csa.py", "np.broadcast_to(zb + bias[None, :, None]", "np.broadcast_to(zb"),
+ ("csa.py", "np.maximum(dots, 0.0) * w[None, :]", "np.minimum(dots, 0.0) * w[None, :]"),
+ ("csa.py", "(int(p) + 1) // int(m)", "int(p) // int(m)"),
+ ("csa.py", "lo = max(0, p - n_win + 1, int(swa_pos0))", "lo = max(0, p - n_win, int(swa_pos0))"),
+ ("csa.py", "order = np.lexsort((js, -scores))", "order = np.lexsort((-js, -scores))"),
+ ("csa.py", "logits = s * (q @ keys.T)", "logits = (q @ keys.T)"),
+ ("csa.py", "e = np.exp(a - a.max(axis=1, keepdims=True))\n    w = e / e.sum(axis=1", "e = np.exp(a - a.max(axis=2, keepdims=True))\n    w = e / e.sum(axis=2"),
+ ("csa.py", "kI = pooled @ W", "kI = pooled[:, ::-1] @ W"),
+ ("csa.py", "o = (e / den) @ keys", "o = (e / den) @ keys[::-1]"),
+ ("csa.py", "rope = f32_to_bf16(c32[:, d_nope:])", "rope = f32_to_bf16(c32[:, d_nope - 1:-1])"),
+ ("formats.py", "packed = (code[..., 0::2] | (code[..., 1::2] << 4))", "packed = (code[..., 1::2] | (code[..., 0::2] << 4))"),
+ ("formats.py", "ex.astype(np.int64) - 1 - 2", "ex.astype(np.int64) - 2"),
+ ("formats.py", "_E2M1_TIE_UP = np.array([False, True, False, True, False, True, False])", "_E2M1_TIE_UP = np.array([False] * 7)"),
+ ("formats.py", "mant / 8.0 * 2.0 ** -6", "mant / 8.0 * 2.0 ** -7"),
+ ("formats.py", "(e.astype(np.float64) - 7.0)", "(e.astype(np.float64) - 8.0)"),
+ ("formats.py", "np.uint64(0x7FFF) + ((u >> np.uint64(16)) & np.uint64(1))", "np.uint64(0x8000)"),
+ ("formats.py", "code = _e2m1_round(np.abs(scaled)) | np.where(scaled < 0, 8, 0)", "code = _e2m1_round(np.abs(scaled)) | np.where(scaled < -1e-30, 8, 0) & np.where(np.abs(scaled) > 0.25, 15, 0)"),
+ ("formats.py", "x = np.clip(x, -127, 127)", "x = np.clip(x, -126, 127)"),
+]
+missed = 0
+root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+for f, a, b in muts:
+    shutil.rmtree(MUT, ignore_errors=True)
+    os.makedirs(MUT)
+    for d in ("oracle", "synth", "tests"):
+        shutil.copytree(os.path.join(root, d), os.path.join(MUT, d))
+    p = MUT + "/oracle/" + f
+    s = open(p).read()
+    assert s.count(a) >= 1, a
+    open(p, "w").write(s.replace(a, b, 1))
+    r = subprocess.run(["python", "-m", "pytest", "tests", "-q", "-x", "-p", "no:cacheprovider"],
+                       cwd=MUT, capture_output=True, text=True, timeout=600)
+    last = r.stdout.strip().splitlines()[-1]
+    failed = [l for l in r.stdout.splitlines() if l.startswith("FAILED")]
+    missed += 0 if r.returncode else 1
+    print("CAUGHT" if r.returncode else "MISSED", "|", a[:60], "|", failed[0][7:80] if failed else last)
+sys.exit(1 if missed else 0)

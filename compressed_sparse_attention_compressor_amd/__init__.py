@@ -1,0 +1,21 @@
+"""Compressed sparse attention (CSA / HCA / CSA2) on MI355X (gfx950).
+
+The compute path is libcsa.so (hand-written HIP kernels behind the C ABI of
+include/csa.h); this package only marshals torch tensors into it.
+"""
+
+from ._lib import CacheT, CsaError, lib  # noqa: F401
+from .ops import (  # noqa: F401
+    D,
+    D_NOPE,
+    D_ROPE,
+    Cache,
+    compress,
+    hca_dense_attn,
+    index_topk,
+    sparse_attn,
+    workspace_bytes,
+    WS_DENSE_ATTN,
+    WS_INDEX_TOPK,
+    WS_SPARSE_ATTN,
+)

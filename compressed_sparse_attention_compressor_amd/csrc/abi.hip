@@ -1,0 +1,190 @@
+// C ABI of the CSA library: argument checks on the host, then launches.
+// No HIP call is made before every check has passed.
+#include <math.h>
+
+#include "../../include/csa.h"
+#include "csa_device.hpp"
+#include "csa_internal.hpp"
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+constexpr int kMaxH = 128;
+constexpr int kMaxHI = 64;
+constexpr int kMaxM = 256;
+constexpr int kMaxK = 1 << 20;
+constexpr int kMaxWin = 1 << 20;
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int status_of(hipError_t e) {
+  if (e == hipSuccess) return CSA_OK;
+  g_last_hip_error = (int)e;
+  return CSA_ERR_HIP;
+}
+
+// Checks shared by every call that reads a cache.
+int check_cache(const csa_cache_t *c, bool need_ikey) {
+  if (!c) return CSA_ERR_NULL;
+  if (!c->nope || !c->nscale || !c->rope || !c->n_entries) return CSA_ERR_NULL;
+  if (need_ikey && (!c->ikey || !c->iscale)) return CSA_ERR_NULL;
+  if (c->B < 0 || c->N_cap < 0) return CSA_ERR_SHAPE;
+  if (c->d_nope != csa::kDNope || c->d_rope != csa::kDRope) return CSA_ERR_UNSUPPORTED;
+  if (c->m < 1 || c->m > kMaxM) return CSA_ERR_UNSUPPORTED;
+  if (need_ikey && c->d_idx != 64 && c->d_idx != 128) return CSA_ERR_UNSUPPORTED;
+  if (c->d_idx != 0 && c->d_idx != 64 && c->d_idx != 128) return CSA_ERR_UNSUPPORTED;
+  if (!aligned16(c->nope) || !aligned16(c->nscale) || !aligned16(c->rope)) return CSA_ERR_ALIGN;
+  if (c->ikey && (!aligned16(c->ikey) || !aligned16(c->iscale))) return CSA_ERR_ALIGN;
+  return CSA_OK;
+}
+
+csa::CacheView view_of(const csa_cache_t *c) {
+  csa::CacheView v;
+  v.nope = c->nope;
+  v.nscale = c->nscale;
+  v.rope = c->rope;
+  v.ikey = c->ikey;
+  v.iscale = c->iscale;
+  v.n_entries = c->n_entries;
+  v.B = c->B;
+  v.N_cap = c->N_cap;
+  v.d_idx = c->d_idx;
+  v.m = c->m;
+  return v;
+}
+
+size_t index_ws_bytes(int B, int Q, int N_cap, int C) {
+  const int Ns = C > 0 ? C : N_cap;
+  return (size_t)B * Q * Ns * sizeof(float);
+}
+
+int check_attn_common(const csa_cache_t *cache, const uint16_t *q, int H, const int32_t *q_pos, int Q,
+                      const uint16_t *swa, const int32_t *swa_pos0, int S, int n_win, float scale, int out_dtype,
+                      void *out) {
+  int st = check_cache(cache, false);
+  if (st) return st;
+  if (!q || !q_pos || !out) return CSA_ERR_NULL;
+  if (Q < 0 || S < 0 || n_win < 0) return CSA_ERR_SHAPE;
+  if (n_win > 0 && (!swa || !swa_pos0)) return CSA_ERR_NULL;
+  if (H < 16 || H > kMaxH || (H != 16 && H != 32 && H != 64 && H != 128)) return CSA_ERR_UNSUPPORTED;
+  if (n_win > kMaxWin) return CSA_ERR_UNSUPPORTED;
+  if (out_dtype != CSA_OUT_F32 && out_dtype != CSA_OUT_BF16) return CSA_ERR_UNSUPPORTED;
+  if (!(scale == scale) || isinf(scale)) return CSA_ERR_SHAPE;
+  if (!aligned16(q) || !aligned16(out) || (n_win > 0 && !aligned16(swa))) return CSA_ERR_ALIGN;
+  return CSA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int csa_version(void) { return 10000; }
+
+int csa_last_hip_error(void) { return g_last_hip_error; }
+
+const char *csa_status_str(int status) {
+  switch (status) {
+    case CSA_OK: return "ok";
+    case CSA_ERR_NULL: return "a required pointer is NULL";
+    case CSA_ERR_SHAPE: return "inconsistent sizes";
+    case CSA_ERR_ALIGN: return "a buffer is not 16-byte aligned";
+    case CSA_ERR_UNSUPPORTED: return "sizes outside the supported envelope";
+    case CSA_ERR_WORKSPACE: return "workspace too small";
+    case CSA_ERR_HIP: return "HIP launch failure";
+    default: return "unknown status";
+  }
+}
+
+size_t csa_workspace_bytes(int op, int B, int Q, int H, int n_or_k, int C) {
+  if (B <= 0 || Q <= 0) return 0;
+  switch (op) {
+    case CSA_WS_INDEX_TOPK: return index_ws_bytes(B, Q, n_or_k, C);
+    case CSA_WS_SPARSE_ATTN:
+    case CSA_WS_DENSE_ATTN: return csa::attn_workspace_bytes(B, Q, H, n_or_k + (C > 0 ? C : 0));
+    default: return 0;
+  }
+}
+
+int csa_compress(const uint16_t *x, int64_t x_stride_b, const uint16_t *z, int64_t z_stride_b, int G,
+                 const float *pos_bias, const uint16_t *w_ik, int64_t tok_begin, int64_t T,
+                 const csa_cache_t *cache, hipStream_t stream) {
+  int st = check_cache(cache, w_ik != nullptr);
+  if (st) return st;
+  if (!x || !z || !pos_bias) return CSA_ERR_NULL;
+  if (G != 1 && G != csa::kD) return CSA_ERR_UNSUPPORTED;
+  if (T < 0 || tok_begin < 0) return CSA_ERR_SHAPE;
+  if (tok_begin % cache->m || T % cache->m) return CSA_ERR_SHAPE;
+  if ((tok_begin + T) / cache->m > cache->N_cap) return CSA_ERR_SHAPE;
+  if (cache->B > 1 && (x_stride_b < T * csa::kD || z_stride_b < T * G)) return CSA_ERR_SHAPE;
+  if (!aligned16(x) || (G == csa::kD && !aligned16(z))) return CSA_ERR_ALIGN;
+  if (G == csa::kD && (z_stride_b % 4)) return CSA_ERR_ALIGN;
+  if (x_stride_b % 4) return CSA_ERR_ALIGN;
+  if (T == 0 || cache->B == 0) return CSA_OK;
+  const csa::CacheView v = view_of(cache);
+  return status_of(csa::launch_compress(x, x_stride_b, z, z_stride_b, G, pos_bias, w_ik, tok_begin / cache->m,
+                                        (int)(T / cache->m), v, stream));
+}
+
+int csa_index_topk(const csa_cache_t *cache, const uint8_t *q_idx, const float *w_idx, int H_I,
+                   const int32_t *q_pos, int Q, const int32_t *cand, int C, int k, int32_t *idx_out,
+                   float *score_out, void *ws, size_t ws_bytes, hipStream_t stream) {
+  int st = check_cache(cache, true);
+  if (st) return st;
+  if (!q_idx || !w_idx || !q_pos || !idx_out) return CSA_ERR_NULL;
+  if (Q < 0 || k < 0 || (cand && C < 0)) return CSA_ERR_SHAPE;
+  if (H_I < 1 || H_I > kMaxHI) return CSA_ERR_UNSUPPORTED;
+  if (k > kMaxK) return CSA_ERR_UNSUPPORTED;
+  if (cand && Q > 65535) return CSA_ERR_UNSUPPORTED;
+  if (!aligned16(q_idx)) return CSA_ERR_ALIGN;
+  if (Q == 0 || cache->B == 0 || k == 0) return CSA_OK;
+  const int Cn = cand ? C : 0;
+  const size_t need = index_ws_bytes(cache->B, Q, cache->N_cap, Cn);
+  if (need > 0 && !ws) return CSA_ERR_NULL;
+  if (ws_bytes < need) return CSA_ERR_WORKSPACE;
+  if (!aligned16(ws)) return CSA_ERR_ALIGN;
+  const csa::CacheView v = view_of(cache);
+  float *scores = reinterpret_cast<float *>(ws);
+  const int Ns = cand ? C : cache->N_cap;
+  if (Ns > 0) {
+    st = status_of(csa::launch_index_scores(v, q_idx, w_idx, H_I, q_pos, Q, cand, C, scores, stream));
+    if (st) return st;
+  }
+  return status_of(csa::launch_topk(v, scores, Ns, q_pos, Q, cand, C, k, idx_out, score_out, stream));
+}
+
+int csa_sparse_attn(const csa_cache_t *cache, const uint16_t *q, int H, const int32_t *q_pos, int Q,
+                    const int32_t *idx, int k, const uint16_t *swa, const int32_t *swa_pos0, int S, int n_win,
+                    float softmax_scale, int out_dtype, void *out, float *lse, void *ws, size_t ws_bytes,
+                    hipStream_t stream) {
+  int st = check_attn_common(cache, q, H, q_pos, Q, swa, swa_pos0, S, n_win, softmax_scale, out_dtype, out);
+  if (st) return st;
+  if (k < 0) return CSA_ERR_SHAPE;
+  if (k > 0 && !idx) return CSA_ERR_NULL;
+  if (k > kMaxK) return CSA_ERR_UNSUPPORTED;
+  if (Q == 0 || cache->B == 0) return CSA_OK;
+  const size_t need = csa::attn_workspace_bytes(cache->B, Q, H, k + n_win);
+  if (need > 0 && !ws) return CSA_ERR_NULL;
+  if (ws_bytes < need) return CSA_ERR_WORKSPACE;
+  if (need > 0 && !aligned16(ws)) return CSA_ERR_ALIGN;
+  const csa::CacheView v = view_of(cache);
+  return status_of(csa::launch_attention(v, q, H, q_pos, Q, idx, k, false, swa, swa_pos0, S, n_win, softmax_scale,
+                                         out_dtype == CSA_OUT_BF16, out, lse, ws, stream));
+}
+
+int hca_dense_attn(const csa_cache_t *cache, const uint16_t *q, int H, const int32_t *q_pos, int Q,
+                   const uint16_t *swa, const int32_t *swa_pos0, int S, int n_win, float softmax_scale,
+                   int out_dtype, void *out, float *lse, void *ws, size_t ws_bytes, hipStream_t stream) {
+  int st = check_attn_common(cache, q, H, q_pos, Q, swa, swa_pos0, S, n_win, softmax_scale, out_dtype, out);
+  if (st) return st;
+  if (Q == 0 || cache->B == 0) return CSA_OK;
+  const size_t need = csa::attn_workspace_bytes(cache->B, Q, H, cache->N_cap + n_win);
+  if (need > 0 && !ws) return CSA_ERR_NULL;
+  if (ws_bytes < need) return CSA_ERR_WORKSPACE;
+  if (need > 0 && !aligned16(ws)) return CSA_ERR_ALIGN;
+  const csa::CacheView v = view_of(cache);
+  return status_of(csa::launch_attention(v, q, H, q_pos, Q, nullptr, 0, true, swa, swa_pos0, S, n_win, softmax_scale,
+                                         out_dtype == CSA_OUT_BF16, out, lse, ws, stream));
+}
+
+}  // extern "C"

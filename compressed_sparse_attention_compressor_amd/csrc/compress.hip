@@ -1,0 +1,167 @@
+// Compressor: softmax-gated pooling of m raw rows into one cache entry
+// ([V4] "ハイブリッド注意：CSAとHCA", CSA paragraph and Fig. 3; Fig. 4 for
+// HCA's m = 128), then the MXFP4 main entry, the bf16 rope channels and
+// the MXFP4 indexer key kI = W_IK^T c ([V4.1] CSA2 paragraph: the indexer
+// key is a projection of the main entry, and entries do not overlap).
+//
+// One workgroup handles kEPB consecutive entries of one sequence:
+//   1. pooling: each task is (entry, 4 channels); it reads the m gate
+//      logits twice (max, then exp-weighted sums) and the m KV rows once,
+//      with 8-byte vector loads that are contiguous across tasks;
+//   2. the pooled fp32 rows sit in LDS and are encoded 2 channels per
+//      thread, 16 threads per 32-channel scale block (shuffle max);
+//   3. the projection runs on the fp32 pooled values in a fixed channel
+//      order (fmaf from channel 0 to 575), W_IK read once per workgroup.
+#include "csa_device.hpp"
+#include "csa_internal.hpp"
+
+namespace csa {
+
+constexpr int kEPB = 16;
+constexpr int kCompThreads = 256;
+constexpr int kMaxIdx = 128;
+
+// Encodes the pair (v0, v1) of channels 2t, 2t+1 of a 32-channel block
+// spread over 16 consecutive lanes; returns the packed byte and the block's
+// scale byte (valid in every lane of the group).
+__device__ __forceinline__ uint32_t encode_pair(float v0, float v1, uint32_t &sbyte) {
+  float amax = group_max<16>(fmaxf(fabsf(v0), fabsf(v1)));
+  sbyte = mx_scale_byte(amax);
+  float inv = mx_inv_scale(sbyte);
+  return e2m1_encode(v0, inv) | (e2m1_encode(v1, inv) << 4);
+}
+
+template <bool kGateFull>
+__global__ __launch_bounds__(kCompThreads) void compress_kernel(
+    const uint16_t *__restrict__ x, int64_t x_stride_b, const uint16_t *__restrict__ z, int64_t z_stride_b,
+    const float *__restrict__ bias, const uint16_t *__restrict__ w_ik, int m, int n_chunk, int64_t entry0,
+    uint8_t *__restrict__ nope, uint8_t *__restrict__ nscale, uint16_t *__restrict__ rope,
+    uint8_t *__restrict__ ikey, uint8_t *__restrict__ iscale, int N_cap, int d_idx) {
+  __shared__ float cs[kEPB][kD];
+  __shared__ float ks[kEPB][kMaxIdx];
+
+  const int b = blockIdx.y;
+  const int j0 = blockIdx.x * kEPB;
+  const int ne = min(kEPB, n_chunk - j0);
+  const int tid = threadIdx.x;
+  const uint16_t *xb = x + (int64_t)b * x_stride_b;
+  const uint16_t *zb = z + (int64_t)b * z_stride_b;
+
+  // 1. pooling
+  for (int t = tid; t < ne * (kD / 4); t += kCompThreads) {
+    const int e = t / (kD / 4);
+    const int c = (t % (kD / 4)) * 4;
+    const int64_t row0 = (int64_t)(j0 + e) * m;
+    float mx[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+    for (int i = 0; i < m; ++i) {
+      const float bi = bias[i];
+      if (kGateFull) {
+        uint2 g = *reinterpret_cast<const uint2 *>(zb + (row0 + i) * kD + c);
+        mx[0] = fmaxf(mx[0], bf16_to_f32(g.x & 0xFFFFu) + bi);
+        mx[1] = fmaxf(mx[1], bf16_to_f32(g.x >> 16) + bi);
+        mx[2] = fmaxf(mx[2], bf16_to_f32(g.y & 0xFFFFu) + bi);
+        mx[3] = fmaxf(mx[3], bf16_to_f32(g.y >> 16) + bi);
+      } else {
+        const float a = bf16_to_f32(zb[row0 + i]) + bi;
+        mx[0] = fmaxf(mx[0], a);
+      }
+    }
+    if (!kGateFull) mx[1] = mx[2] = mx[3] = mx[0];
+    float den[4] = {0.f, 0.f, 0.f, 0.f};
+    float num[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int i = 0; i < m; ++i) {
+      const float bi = bias[i];
+      float a[4];
+      if (kGateFull) {
+        uint2 g = *reinterpret_cast<const uint2 *>(zb + (row0 + i) * kD + c);
+        a[0] = bf16_to_f32(g.x & 0xFFFFu) + bi;
+        a[1] = bf16_to_f32(g.x >> 16) + bi;
+        a[2] = bf16_to_f32(g.y & 0xFFFFu) + bi;
+        a[3] = bf16_to_f32(g.y >> 16) + bi;
+      } else {
+        a[0] = a[1] = a[2] = a[3] = bf16_to_f32(zb[row0 + i]) + bi;
+      }
+      uint2 v = *reinterpret_cast<const uint2 *>(xb + (row0 + i) * kD + c);
+      const float xv[4] = {bf16_to_f32(v.x & 0xFFFFu), bf16_to_f32(v.x >> 16), bf16_to_f32(v.y & 0xFFFFu),
+                           bf16_to_f32(v.y >> 16)};
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const float w = expf(a[u] - mx[u]);
+        den[u] += w;
+        num[u] = fmaf(w, xv[u], num[u]);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) cs[e][c + u] = num[u] / den[u];
+  }
+  __syncthreads();
+
+  // 2. MXFP4 main entry (bytes 0..255) and bf16 rope channels
+  for (int e = 0; e < ne; ++e) {
+    const int64_t row = (int64_t)b * N_cap + entry0 + j0 + e;
+    uint32_t sb;
+    const uint32_t byte = encode_pair(cs[e][2 * tid], cs[e][2 * tid + 1], sb);
+    nope[row * kNopeBytes + tid] = (uint8_t)byte;
+    if ((tid & 15) == 0) nscale[row * kNopeScales + (tid >> 4)] = (uint8_t)sb;
+  }
+  for (int t = tid; t < ne * kDRope; t += kCompThreads) {
+    const int e = t / kDRope, c = t % kDRope;
+    const int64_t row = (int64_t)b * N_cap + entry0 + j0 + e;
+    rope[row * kDRope + c] = (uint16_t)f32_to_bf16(cs[e][kDNope + c]);
+  }
+  if (w_ik == nullptr) return;
+
+  // 3. indexer key: kI[o] = sum_d c[d] * W[d][o], fp32, channel order 0..575
+  {
+    const int o = tid % d_idx;
+    const int groups = kCompThreads / d_idx;  // 2 (d_idx 128) or 4 (d_idx 64)
+    const int g = tid / d_idx;
+    float acc[kEPB / 2];
+    const int per = kEPB / groups;            // entries per thread: 8 or 4
+#pragma unroll
+    for (int r = 0; r < kEPB / 2; ++r) acc[r] = 0.f;
+    for (int d = 0; d < kD; ++d) {
+      const float w = bf16_to_f32(w_ik[d * d_idx + o]);
+#pragma unroll
+      for (int r = 0; r < kEPB / 2; ++r)
+        if (r < per) acc[r] = fmaf(cs[g + r * groups][d], w, acc[r]);
+    }
+#pragma unroll
+    for (int r = 0; r < kEPB / 2; ++r)
+      if (r < per) ks[g + r * groups][o] = acc[r];
+  }
+  __syncthreads();
+  {
+    const int bytes = d_idx / 2;                 // 64 or 32 per entry
+    const int epp = kCompThreads / bytes;        // entries per pass: 4 or 8
+    for (int e = tid / bytes; e < ((ne + epp - 1) / epp) * epp; e += epp) {
+      const int t = tid % bytes;
+      const int ec = e < ne ? e : ne - 1;        // keep every lane in the shuffles
+      uint32_t sb;
+      const uint32_t byte = encode_pair(ks[ec][2 * t], ks[ec][2 * t + 1], sb);
+      if (e < ne) {
+        const int64_t row = (int64_t)b * N_cap + entry0 + j0 + e;
+        ikey[row * bytes + t] = (uint8_t)byte;
+        if ((t & 15) == 0) iscale[row * (d_idx / 32) + (t >> 4)] = (uint8_t)sb;
+      }
+    }
+  }
+}
+
+hipError_t launch_compress(const uint16_t *x, int64_t x_stride_b, const uint16_t *z, int64_t z_stride_b,
+                           int G, const float *bias, const uint16_t *w_ik, int64_t entry0, int n_chunk,
+                           const CacheView &c, hipStream_t stream) {
+  if (n_chunk <= 0 || c.B <= 0) return hipSuccess;
+  dim3 grid((n_chunk + kEPB - 1) / kEPB, c.B);
+  if (G == kD)
+    compress_kernel<true><<<grid, kCompThreads, 0, stream>>>(x, x_stride_b, z, z_stride_b, bias, w_ik, c.m, n_chunk,
+                                                             entry0, c.nope, c.nscale, c.rope, c.ikey, c.iscale,
+                                                             c.N_cap, c.d_idx);
+  else
+    compress_kernel<false><<<grid, kCompThreads, 0, stream>>>(x, x_stride_b, z, z_stride_b, bias, w_ik, c.m, n_chunk,
+                                                              entry0, c.nope, c.nscale, c.rope, c.ikey, c.iscale,
+                                                              c.N_cap, c.d_idx);
+  return hipGetLastError();
+}
+
+}  // namespace csa

@@ -1,0 +1,47 @@
+// Host-side launchers shared between the kernel translation units and the
+// C ABI (abi.hip).  Arguments are validated by the caller.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace csa {
+
+struct CacheView {
+  uint8_t *nope;
+  uint8_t *nscale;
+  uint16_t *rope;
+  uint8_t *ikey;
+  uint8_t *iscale;
+  const int32_t *n_entries;
+  int B, N_cap, d_idx, m;
+};
+
+hipError_t launch_compress(const uint16_t *x, int64_t x_stride_b, const uint16_t *z, int64_t z_stride_b,
+                           int G, const float *bias, const uint16_t *w_ik, int64_t entry0, int n_chunk_entries,
+                           const CacheView &c, hipStream_t stream);
+
+// Scores of every scanned entry (full scan: [B][Q][N_cap], candidates:
+// [B][Q][C]) into `scores`; slots without a candidate get kNoScoreBits.
+hipError_t launch_index_scores(const CacheView &c, const uint8_t *q_idx, const float *w_idx, int H_I,
+                               const int32_t *q_pos, int Q, const int32_t *cand, int C, float *scores,
+                               hipStream_t stream);
+
+hipError_t launch_topk(const CacheView &c, const float *scores, int Ns, const int32_t *q_pos, int Q,
+                       const int32_t *cand, int C, int k, int32_t *idx_out, float *score_out,
+                       hipStream_t stream);
+
+struct AttnShape {
+  int nsplit;       // key-range splits per query
+  int per_split;    // key slots per split (a multiple of the chunk size)
+};
+AttnShape attn_shape(int B, int Q, int n_slots_max);
+size_t attn_workspace_bytes(int B, int Q, int H, int n_slots_max);
+
+hipError_t launch_attention(const CacheView &c, const uint16_t *q, int H, const int32_t *q_pos, int Q,
+                            const int32_t *idx, int k, bool dense, const uint16_t *swa,
+                            const int32_t *swa_pos0, int S, int n_win, float scale, bool out_bf16,
+                            void *out, float *lse, void *ws, hipStream_t stream);
+
+}  // namespace csa

@@ -1,0 +1,154 @@
+"""torch-facing wrappers of the C ABI: argument marshalling only.
+
+Every step of the path runs in the HIP kernels of libcsa.so; these
+functions pass device pointers, sizes and the current HIP stream.
+"""
+
+from __future__ import annotations
+
+import ctypes
+
+import torch
+
+from ._lib import CacheT, check, lib
+
+D, D_NOPE, D_ROPE = 576, 512, 64
+WS_INDEX_TOPK, WS_SPARSE_ATTN, WS_DENSE_ATTN = 0, 1, 2
+OUT_F32, OUT_BF16 = 0, 1
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _need(t, dtype, name):
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_cuda:
+        raise TypeError(f"{name} must be a device tensor")
+
+
+class Cache:
+    """Planes of one compressed cache (caller-owned device memory).
+
+    nope uint8 [B][N_cap][256], nscale uint8 [B][N_cap][16], rope bf16
+    [B][N_cap][64], ikey uint8 [B][N_cap][d_idx/2], iscale uint8
+    [B][N_cap][d_idx/32] (absent when d_idx = 0), n_entries int32 [B].
+    """
+
+    def __init__(self, B, N_cap, m, d_idx, device="cuda", planes=None):
+        self.B, self.N_cap, self.m, self.d_idx = int(B), int(N_cap), int(m), int(d_idx)
+        if planes is None:
+            u8 = dict(dtype=torch.uint8, device=device)
+            planes = dict(
+                nope=torch.zeros(B, N_cap, D_NOPE // 2, **u8),
+                nscale=torch.zeros(B, N_cap, D_NOPE // 32, **u8),
+                rope=torch.zeros(B, N_cap, D_ROPE, dtype=torch.bfloat16, device=device),
+                ikey=torch.zeros(B, N_cap, d_idx // 2, **u8) if d_idx else None,
+                iscale=torch.zeros(B, N_cap, d_idx // 32, **u8) if d_idx else None,
+                n_entries=torch.zeros(B, dtype=torch.int32, device=device),
+            )
+        for k, v in planes.items():
+            setattr(self, k, v)
+
+    def struct(self) -> CacheT:
+        return CacheT(
+            self.nope.data_ptr(), self.nscale.data_ptr(), self.rope.data_ptr(),
+            self.ikey.data_ptr() if self.ikey is not None else None,
+            self.iscale.data_ptr() if self.iscale is not None else None,
+            self.n_entries.data_ptr(), self.B, self.N_cap, D_NOPE, D_ROPE, self.d_idx, self.m)
+
+
+def workspace_bytes(op, B, Q, H, n_or_k, C=0) -> int:
+    return int(lib().csa_workspace_bytes(op, B, Q, H, n_or_k, C))
+
+
+def _workspace(nbytes, ws, device):
+    if nbytes == 0:
+        return None, 0
+    if ws is None:
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=device)
+    return ws, ws.numel() * ws.element_size()
+
+
+def compress(cache: Cache, x, z, pos_bias, w_ik=None, tok_begin=0):
+    """Writes entries tok_begin/m .. (tok_begin+T)/m - 1 from x [B][T][576] and z [B][T][G]."""
+    _need(x, torch.bfloat16, "x")
+    _need(z, torch.bfloat16, "z")
+    _need(pos_bias, torch.float32, "pos_bias")
+    B, T = x.shape[0], x.shape[1]
+    G = z.shape[2]
+    if x.stride(2) != 1 or x.stride(1) != D or z.stride(2) != 1 or z.stride(1) != G:
+        raise ValueError("x and z rows must be contiguous")
+    if w_ik is not None:
+        _need(w_ik, torch.bfloat16, "w_ik")
+    cs = cache.struct()
+    check(lib().csa_compress(_ptr(x), x.stride(0), _ptr(z), z.stride(0), G, _ptr(pos_bias), _ptr(w_ik),
+                             int(tok_begin), int(T), ctypes.byref(cs), _stream()), "csa_compress")
+
+
+def index_topk(cache: Cache, q_idx, w_idx, q_pos, k, cand=None, want_scores=False, ws=None, out=None):
+    """Returns (idx int32 [B][Q][k], scores fp32 [B][Q][k] or None)."""
+    _need(q_idx, torch.uint8, "q_idx")
+    _need(w_idx, torch.float32, "w_idx")
+    _need(q_pos, torch.int32, "q_pos")
+    B, Q, H_I = q_idx.shape[0], q_idx.shape[1], q_idx.shape[2]
+    C = 0
+    if cand is not None:
+        _need(cand, torch.int32, "cand")
+        C = cand.shape[2]
+    dev = q_idx.device
+    idx = out if out is not None else torch.empty(B, Q, k, dtype=torch.int32, device=dev)
+    sc = torch.empty(B, Q, k, dtype=torch.float32, device=dev) if want_scores else None
+    need = workspace_bytes(WS_INDEX_TOPK, B, Q, 0, cache.N_cap, C)
+    ws, wsb = _workspace(need, ws, dev)
+    cs = cache.struct()
+    check(lib().csa_index_topk(ctypes.byref(cs), _ptr(q_idx), _ptr(w_idx), H_I, _ptr(q_pos), Q, _ptr(cand), C, int(k),
+                               _ptr(idx), _ptr(sc), _ptr(ws), wsb, _stream()), "csa_index_topk")
+    return idx, sc
+
+
+def _attn_out(B, Q, H, out_dtype, dev, out):
+    if out is not None:
+        return out
+    return torch.empty(B, Q, H, D, dtype=out_dtype, device=dev)
+
+
+def sparse_attn(cache: Cache, q, q_pos, idx, swa, swa_pos0, n_win, scale, out_dtype=torch.bfloat16, ws=None,
+                out=None, lse=None):
+    """Returns (out [B][Q][H][576], lse fp32 [B][Q][H])."""
+    _need(q, torch.bfloat16, "q")
+    B, Q, H = q.shape[0], q.shape[1], q.shape[2]
+    k = idx.shape[2] if idx is not None else 0
+    S = swa.shape[1] if swa is not None else 0
+    dev = q.device
+    out = _attn_out(B, Q, H, out_dtype, dev, out)
+    lse = lse if lse is not None else torch.empty(B, Q, H, dtype=torch.float32, device=dev)
+    need = workspace_bytes(WS_SPARSE_ATTN, B, Q, H, k, n_win)
+    ws, wsb = _workspace(need, ws, dev)
+    cs = cache.struct()
+    check(lib().csa_sparse_attn(ctypes.byref(cs), _ptr(q), H, _ptr(q_pos), Q, _ptr(idx), k, _ptr(swa), _ptr(swa_pos0),
+                                S, int(n_win), float(scale), OUT_BF16 if out_dtype == torch.bfloat16 else OUT_F32,
+                                _ptr(out), _ptr(lse), _ptr(ws), wsb, _stream()), "csa_sparse_attn")
+    return out, lse
+
+
+def hca_dense_attn(cache: Cache, q, q_pos, swa, swa_pos0, n_win, scale, out_dtype=torch.bfloat16, ws=None,
+                   out=None, lse=None):
+    _need(q, torch.bfloat16, "q")
+    B, Q, H = q.shape[0], q.shape[1], q.shape[2]
+    S = swa.shape[1] if swa is not None else 0
+    dev = q.device
+    out = _attn_out(B, Q, H, out_dtype, dev, out)
+    lse = lse if lse is not None else torch.empty(B, Q, H, dtype=torch.float32, device=dev)
+    need = workspace_bytes(WS_DENSE_ATTN, B, Q, H, cache.N_cap, n_win)
+    ws, wsb = _workspace(need, ws, dev)
+    cs = cache.struct()
+    check(lib().hca_dense_attn(ctypes.byref(cs), _ptr(q), H, _ptr(q_pos), Q, _ptr(swa), _ptr(swa_pos0), S,
+                               int(n_win), float(scale), OUT_BF16 if out_dtype == torch.bfloat16 else OUT_F32,
+                               _ptr(out), _ptr(lse), _ptr(ws), wsb, _stream()), "hca_dense_attn")
+    return out, lse

@@ -1,0 +1,161 @@
+/*
+ * csa.h -- C ABI of the compressed sparse attention (CSA / HCA / CSA2) path
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * Pages this interface follows (cited by title, section and figure):
+ *   [V4]   "DeepSeek-V4: エージェントが実際に使える100万トークンのコンテキスト"
+ *          (DeepSeek-V4 blog post, Japanese translation), section
+ *          "ハイブリッド注意：CSAとHCA", Fig. 3 (CSA) and Fig. 4 (HCA).
+ *   [V4.1] "DeepSeek-V4.1-Flash: Pushing the Limits of KV Cache Compression"
+ *          (digest of the V4.1-Flash technical report), section
+ *          "アーキテクチャ": CSA2 paragraph and Fig. 4 (Full / Reindex / Reuse
+ *          modes), "FP4 主 KV キャッシュ" (MXFP4 main KV cache).
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * - Every pointer argument is a DEVICE pointer owned by the caller, except
+ *   the csa_cache_t struct itself, which is read on the host during the
+ *   call and not kept.  The library keeps no pointer after it returns.
+ * - Every call is asynchronous on `stream`, allocates nothing, never
+ *   synchronises, and makes no HIP call before its host-side argument
+ *   checks have passed; a failed check returns a negative csa_status and
+ *   launches nothing.
+ * - Channels: D = 576 = d_nope 512 (MXFP4) + d_rope 64 (bf16) per KV row.
+ * - bf16 values are passed as their uint16 bit patterns; E4M3 and MXFP4
+ *   data as bytes.
+ * - A query at raw position p (0-based) sees compressed entry j when
+ *   (j + 1) * m - 1 <= p and j < n_entries[b]; its sliding window is the raw
+ *   rows at positions max(0, p - n_win + 1, swa_pos0[b]) .. p that the
+ *   window buffer holds.
+ * - Data-dependent problems (an index outside the visible range, a window
+ *   row the buffer does not hold) are skipped on the device, never trapped.
+ */
+#ifndef CSA_H_
+#define CSA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  CSA_OK = 0,
+  CSA_ERR_NULL = -1,        /* a required pointer is NULL                       */
+  CSA_ERR_SHAPE = -2,       /* sizes inconsistent with each other               */
+  CSA_ERR_ALIGN = -3,       /* a plane or tensor is not 16-byte aligned         */
+  CSA_ERR_UNSUPPORTED = -4, /* sizes outside the supported envelope             */
+  CSA_ERR_WORKSPACE = -5,   /* workspace smaller than csa_workspace_bytes()     */
+  CSA_ERR_HIP = -6          /* a kernel launch failed (csa_last_hip_error())    */
+} csa_status;
+
+typedef enum { CSA_OUT_F32 = 0, CSA_OUT_BF16 = 1 } csa_out_dtype;
+
+/* One compressed cache: one layer's, or one shared by CSA2 layers
+ * ([V4.1] CSA2 paragraph: main KV and indexer K are shared across layers).
+ * Plane layouts (row-major, one row per entry, N_cap rows per sequence):
+ *   nope   uint8  [B][N_cap][d_nope/2]   E2M1 codes, channel 2i in the low nibble
+ *   nscale uint8  [B][N_cap][d_nope/32]  E8M0 scale of channels 32s..32s+31
+ *   rope   uint16 [B][N_cap][d_rope]     bf16
+ *   ikey   uint8  [B][N_cap][d_idx/2]    indexer key, MXFP4 like nope
+ *   iscale uint8  [B][N_cap][d_idx/32]
+ * ikey/iscale may be NULL (HCA caches, d_idx = 0).
+ * n_entries: int32 [B] on the device, entries valid per sequence. */
+typedef struct {
+  uint8_t *nope;
+  uint8_t *nscale;
+  uint16_t *rope;
+  uint8_t *ikey;
+  uint8_t *iscale;
+  const int32_t *n_entries;
+  int32_t B, N_cap, d_nope, d_rope, d_idx, m;
+} csa_cache_t;
+
+/* Compressor ([V4] CSA paragraph and Fig. 3: softmax-gated pooling with a
+ * learned positional bias folds every m raw tokens into one entry; Fig. 4:
+ * HCA uses m = 128; [V4.1] CSA2 paragraph: no overlap between entries, the
+ * indexer key is a projection of the main entry).
+ *
+ * For sequence b and every entry j of the chunk, per channel d:
+ *   c[d] = sum_i softmax_i(z[jm+i][d or 0] + pos_bias[i]) * x[jm+i][d]
+ * then c[0:512] -> MXFP4 (scale X = floor(log2 max|v|) - 2 clamped to
+ * [-127,127], elements rounded to nearest E2M1 with ties to even, saturated
+ * at 6), c[512:576] -> bf16 (round to nearest even), and, when w_ik is not
+ * NULL, kI = W_IK^T c (fp32) -> MXFP4.
+ *
+ *   x        bf16 [B][*][576]; row t of sequence b at x + b*x_stride_b + t*576,
+ *            t = 0..T-1 holding raw positions tok_begin + t
+ *   z        bf16 [B][*][G] gate logits, G = 576 (per channel) or 1, row
+ *            stride G, sequence stride z_stride_b
+ *   pos_bias fp32 [m]
+ *   w_ik     bf16 [576][d_idx] or NULL (then ikey/iscale are not written)
+ *   tok_begin, T: multiples of cache->m; entries tok_begin/m .. (tok_begin+T)/m - 1
+ *            are written and must lie below N_cap.
+ * n_entries is not modified: the caller publishes new entries. */
+int csa_compress(const uint16_t *x, int64_t x_stride_b, const uint16_t *z, int64_t z_stride_b, int G,
+                 const float *pos_bias, const uint16_t *w_ik, int64_t tok_begin, int64_t T,
+                 const csa_cache_t *cache, hipStream_t stream);
+
+/* Lightning indexer + per-query top-k ([V4] CSA paragraph: FP4,
+ * ReLU-scored multi-head dot product; top-k compressed blocks per query.
+ * [V4.1] Fig. 4, Reindex mode: with `cand`, only an earlier layer's
+ * selection is rescored).
+ *
+ *   score(j) = sum_h w_idx[h] * max(0, q_idx[h] . kI_j)   (fp32 accumulation
+ *              of exact E4M3 x E2M1 products)
+ *   idx_out  = the min(k, n) highest-scoring entries, exact ties to the lower
+ *              entry index, ascending, padded with -1; n = visible entries
+ *              (or visible, non-negative candidates)
+ *
+ *   q_idx    E4M3 [B][Q][H_I][d_idx] (unit scale)      w_idx fp32 [B][Q][H_I]
+ *   q_pos    int32 [B][Q] raw positions
+ *   cand     int32 [B][Q][C] ascending entry indices, -1 = none, no repeats;
+ *            NULL for a full scan (C ignored)
+ *   idx_out  int32 [B][Q][k]      score_out fp32 [B][Q][k] or NULL (NaN in padding)
+ *   ws       >= csa_workspace_bytes(CSA_WS_INDEX_TOPK, ...) bytes, 256-byte aligned. */
+int csa_index_topk(const csa_cache_t *cache, const uint8_t *q_idx, const float *w_idx, int H_I,
+                   const int32_t *q_pos, int Q, const int32_t *cand, int C, int k, int32_t *idx_out,
+                   float *score_out, void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* Sparse attention over selected entries plus the sliding window ([V4]
+ * Fig. 3).  One softmax over the union of the entries listed in idx and the
+ * window rows; key = value = the decoded 576-channel row; no rotation is
+ * applied to the rope channels.
+ *
+ *   q        bf16 [B][Q][H][576]         q_pos int32 [B][Q]
+ *   idx      int32 [B][Q][k]; -1 and entries not visible at q_pos are skipped
+ *   swa      bf16 [B][S][576] raw rows, row r of sequence b = position swa_pos0[b] + r
+ *   swa_pos0 int32 [B]                   n_win >= 0 (0 = no window branch)
+ *   out      [B][Q][H][576] fp32 or bf16 (out_dtype)
+ *   lse      fp32 [B][Q][H] natural-log sum of exp of the scaled logits, or NULL
+ *   ws       >= csa_workspace_bytes(CSA_WS_SPARSE_ATTN, ...) bytes. */
+int csa_sparse_attn(const csa_cache_t *cache, const uint16_t *q, int H, const int32_t *q_pos, int Q,
+                    const int32_t *idx, int k, const uint16_t *swa, const int32_t *swa_pos0, int S,
+                    int n_win, float softmax_scale, int out_dtype, void *out, float *lse, void *ws,
+                    size_t ws_bytes, hipStream_t stream);
+
+/* Dense attention over every visible entry plus the window ([V4] Fig. 4,
+ * HCA: no selection; the compressed stream is short).  Arguments as in
+ * csa_sparse_attn without idx/k. */
+int hca_dense_attn(const csa_cache_t *cache, const uint16_t *q, int H, const int32_t *q_pos, int Q,
+                   const uint16_t *swa, const int32_t *swa_pos0, int S, int n_win, float softmax_scale,
+                   int out_dtype, void *out, float *lse, void *ws, size_t ws_bytes, hipStream_t stream);
+
+enum { CSA_WS_INDEX_TOPK = 0, CSA_WS_SPARSE_ATTN = 1, CSA_WS_DENSE_ATTN = 2 };
+
+/* Workspace bytes for one call.  For CSA_WS_INDEX_TOPK, `n_or_k` is N_cap
+ * (full scan) and `C` the candidate count (0 for a full scan).  For the
+ * attention ops `n_or_k` is k (sparse) or N_cap (dense) and C is n_win. */
+size_t csa_workspace_bytes(int op, int B, int Q, int H, int n_or_k, int C);
+
+const char *csa_status_str(int status);
+int csa_version(void);
+/* hipError_t of the last CSA_ERR_HIP on this host thread. */
+int csa_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* CSA_H_ */

@@ -15,5 +15,6 @@ from .gen import (  # noqa: F401
     normal_f32,
     normal_e4m3,
     uniform_int,
+    uniform_bytes,
     config_seed,
 )

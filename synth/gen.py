@@ -44,6 +44,11 @@ class TensorId(enum.IntEnum):
     NENT = 13      # random entry counts
     POS = 14       # random query positions
     SWA = 15       # sliding-window rows when they are not the raw stream
+    NOPE = 16      # synthetic cache planes for stage-wise checks
+    NSCALE = 17
+    ROPE = 18
+    IKEY = 19
+    ISCALE = 20
 
 
 def config_seed(cfg: int) -> int:
@@ -135,6 +140,20 @@ def normal_f32(seed, tid, shape, scale=1.0, device="cpu", first_seq=0, first_ele
 def normal_e4m3(seed, tid, shape, scale=1.0, device="cpu", first_seq=0, first_elem=0):
     """uint8 tensor of OCP E4M3 codes (torch's float8_e4m3fn cast of the quantiles)."""
     return _fill("e4m3", seed, tid, shape, scale, device, first_seq, first_elem)
+
+
+def uniform_bytes(seed, tid, shape, device="cpu"):
+    """uint8 tensor of ``shape`` = (B, ...) with independent uniform bytes."""
+    shape = tuple(int(s) for s in shape)
+    B = shape[0]
+    inner = int(np.prod(shape[1:], dtype=np.int64)) if len(shape) > 1 else 1
+    out = torch.empty((B, inner), dtype=torch.uint8, device=device)
+    step = 1 << 24
+    for b in range(B):
+        for s in range(0, inner, step):
+            n = min(step, inner - s)
+            out[b, s:s + n] = (hash32(seed, tid, b, s, n, device) & 0xFF).to(torch.uint8)
+    return out.view(shape)
 
 
 def uniform_int(seed, tid, shape, low, high, device="cpu"):

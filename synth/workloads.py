@@ -1,0 +1,152 @@
+"""Shapes and input recipes of the five measured workloads, plus small variants.
+
+Input recipe (every value from synth.gen, so CPU and GPU agree bit for bit):
+  x   raw KV rows      bf16 N(0,1)                 [B][T][576]
+  z   gate logits      bf16 N(0,1)                 [B][T][576]
+  bias positional bias fp32 N(0,1)                 [m]
+  W_IK projection      bf16 N(0,1)/sqrt(576)       [576][d_idx]
+  qI  indexer queries  E4M3 N(0,1) * q_idx_scale   [B][Q][H_I][d_idx]
+  w   head weights     fp32 N(0,1)                 [B][Q][H_I]
+  q   queries          bf16 N(0,1) * q_scale       [B][Q][H][576]
+The sliding-window rows are the raw rows x themselves.  The batched
+128K-context decode pre-scales the queries (q by 1/sqrt(576), qI by
+1/sqrt(128)) and uses a softmax scale of 1; the other workloads use unit
+queries and a softmax scale of 1/sqrt(576).
+"""
+
+from __future__ import annotations
+
+import dataclasses
+import math
+
+import numpy as np
+import torch
+
+from .gen import TensorId, config_seed, normal_bf16, normal_e4m3, normal_f32
+
+D = 576
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    name: str
+    cfg: int                # seed selector
+    B: int
+    T: int                  # raw tokens per sequence in the cache
+    m: int
+    d_idx: int              # 0 = no indexer (HCA)
+    H_I: int
+    k: int                  # top-k (layer A's k for the two-layer case)
+    H: int
+    n_win: int
+    Q: int = 1              # query tokens per sequence (decode: the last token)
+    k_b: int = 0            # second layer's k (two-layer reindex case)
+    prescaled: bool = False
+    prefill: bool = False   # queries at every position 0..T-1
+
+    @property
+    def N(self) -> int:
+        return self.T // self.m
+
+    @property
+    def seed(self) -> int:
+        return config_seed(self.cfg)
+
+    @property
+    def softmax_scale(self) -> float:
+        return 1.0 if self.prescaled else float(np.float32(1.0 / math.sqrt(D)))
+
+    @property
+    def q_scale(self) -> float:
+        return 1.0 / math.sqrt(D) if self.prescaled else 1.0
+
+    @property
+    def q_idx_scale(self) -> float:
+        return 1.0 / math.sqrt(self.d_idx) if (self.prescaled and self.d_idx) else 1.0
+
+    def positions(self) -> np.ndarray:
+        if self.prefill:
+            return np.tile(np.arange(self.Q, dtype=np.int32), (self.B, 1))
+        return np.full((self.B, self.Q), self.T - 1, dtype=np.int32)
+
+
+TINY_DECODE = Workload("csa-decode-tiny-4k", 1, B=1, T=4096, m=4, d_idx=64, H_I=4, k=64, H=16, n_win=128)
+BATCHED_DECODE = Workload("csa-decode-b32-128k", 2, B=32, T=131072, m=4, d_idx=128, H_I=32, k=512, H=64, n_win=128,
+                          prescaled=True)
+PREFILL = Workload("csa-prefill-64k", 3, B=1, T=65536, m=4, d_idx=128, H_I=32, k=1024, H=64, n_win=128, Q=65536,
+                   prefill=True)
+HCA_DECODE = Workload("hca-decode-b8-1m", 4, B=8, T=1048576, m=128, d_idx=0, H_I=0, k=0, H=64, n_win=128)
+CSA2_DECODE = Workload("csa2-decode-b4-1m", 5, B=4, T=1048576, m=4, d_idx=128, H_I=32, k=2048, H=64, n_win=128,
+                       k_b=512)
+
+ALL = [TINY_DECODE, BATCHED_DECODE, PREFILL, HCA_DECODE, CSA2_DECODE]
+
+
+def raw_rows(w: Workload, t0: int, t1: int, device="cpu", seq0=0, nseq=None):
+    """(x, z) rows t0..t1-1 of sequences seq0..seq0+nseq-1: bf16 [nseq][t1-t0][576] each."""
+    nseq = w.B if nseq is None else nseq
+    x = normal_bf16(w.seed, TensorId.X, (nseq, t1 - t0, D), device=device, first_seq=seq0, first_elem=t0 * D)
+    z = normal_bf16(w.seed, TensorId.Z, (nseq, t1 - t0, D), device=device, first_seq=seq0, first_elem=t0 * D)
+    return x, z
+
+
+def params(w: Workload, device="cpu"):
+    """bias fp32 [m] and W_IK bf16 [576][d_idx] (None without an indexer)."""
+    bias = normal_f32(w.seed, TensorId.BIAS, (1, w.m), device=device)[0]
+    wik = None
+    if w.d_idx:
+        wik = normal_bf16(w.seed, TensorId.W_IK, (1, D, w.d_idx), scale=1.0 / math.sqrt(D), device=device)[0]
+    return bias, wik
+
+
+def queries(w: Workload, device="cpu", second=False, q0=0, nq=None):
+    """Per-layer query-side inputs for query tokens q0..q0+nq-1: dict of tensors."""
+    nq = w.Q if nq is None else nq
+    tq, tqi, tw = (TensorId.Q_B, TensorId.QI_B, TensorId.W_B) if second else (TensorId.Q, TensorId.QI, TensorId.W)
+    out = dict(q=normal_bf16(w.seed, tq, (w.B, nq, w.H, D), scale=w.q_scale, device=device,
+                             first_elem=q0 * w.H * D))
+    if w.d_idx:
+        out["qI"] = normal_e4m3(w.seed, tqi, (w.B, nq, w.H_I, w.d_idx), scale=w.q_idx_scale, device=device,
+                                first_elem=q0 * w.H_I * w.d_idx)
+        out["w"] = normal_f32(w.seed, tw, (w.B, nq, w.H_I), device=device, first_elem=q0 * w.H_I)
+    pos = torch.from_numpy(w.positions()[:, q0:q0 + nq].copy())
+    out["q_pos"] = pos.to(device)
+    return out
+
+
+def second_layer_window(w: Workload, t0: int, t1: int, device="cpu"):
+    """The second layer's own window rows (positions t0..t1-1)."""
+    return normal_bf16(w.seed, TensorId.SWA_B, (w.B, t1 - t0, D), device=device, first_elem=t0 * D)
+
+
+def as_u16(t: torch.Tensor) -> np.ndarray:
+    """bf16 tensor -> numpy uint16 bit patterns (CPU copy)."""
+    return t.detach().cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
+
+
+def synthetic_cache(w: Workload, device="cpu", N_cap=None, seq0=0, nseq=None):
+    """Cache planes drawn directly (for checking the stages after the compressor
+    at full size): uniform E2M1 code bytes, E8M0 scales in 124..127 (values up
+    to 6 in magnitude, like encoded N(0,1) data), bf16 N(0,1) rope channels."""
+    N_cap = w.N if N_cap is None else N_cap
+    nseq = w.B if nseq is None else nseq
+    out = {}
+    out["nope"] = _rows_bytes(w, TensorId.NOPE, nseq, N_cap, 256, device, seq0)
+    out["nscale"] = (124 + _rows_bytes(w, TensorId.NSCALE, nseq, N_cap, 16, device, seq0) % 4).to(torch.uint8)
+    out["rope"] = normal_bf16(w.seed, TensorId.ROPE, (nseq, N_cap, 64), device=device, first_seq=seq0)
+    if w.d_idx:
+        out["ikey"] = _rows_bytes(w, TensorId.IKEY, nseq, N_cap, w.d_idx // 2, device, seq0)
+        out["iscale"] = (124 + _rows_bytes(w, TensorId.ISCALE, nseq, N_cap, w.d_idx // 32, device, seq0)
+                         % 4).to(torch.uint8)
+    return out
+
+
+def _rows_bytes(w, tid, nseq, N_cap, width, device, seq0):
+    from .gen import hash32
+    out = torch.empty((nseq, N_cap * width), dtype=torch.uint8, device=device)
+    step = 1 << 24
+    for b in range(nseq):
+        for s in range(0, N_cap * width, step):
+            n = min(step, N_cap * width - s)
+            out[b, s:s + n] = (hash32(w.seed, tid, seq0 + b, s, n, device) & 0xFF).to(torch.uint8)
+    return out.view(nseq, N_cap, width)

@@ -1,0 +1,104 @@
+"""Comparison rules between the HIP path and the oracle (test infrastructure).
+
+* FP4 codes and scales: bit-exact, except where the GPU's fp32 pre-image
+  may legitimately land on the other side of a rounding decision: the
+  oracle's float64 pre-image lies within `bound` (an error bound of the fp32
+  evaluation, derived from the magnitudes of the summed terms) of an E2M1
+  rounding boundary, of a power of two that changes the block scale, or of
+  zero (sign).  Each exemption is counted.
+* Top-k: the same number of selected entries, ascending and unique; entries
+  in only one of the two selections must have oracle scores within 1e-4
+  relative of the oracle's k-th score.
+* Attention: row-normalised max error max_c |g - r| / max_c |r| per
+  (sequence, query, head) row, 1e-3 for fp32 outputs and 2e-2 for bf16.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+from oracle import bf16_to_f64, mxfp4_decode
+
+_BOUNDS = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0])
+
+
+def _nibbles(packed):
+    packed = np.asarray(packed, dtype=np.uint8)
+    out = np.empty(packed.shape[:-1] + (packed.shape[-1] * 2,), dtype=np.uint8)
+    out[..., 0::2] = packed & 0xF
+    out[..., 1::2] = packed >> 4
+    return out
+
+
+def compare_mxfp4(g_packed, g_scales, o_packed, o_scales, pre, bound, what=""):
+    """Returns the number of exempted (mismatching but explained) elements."""
+    g_c = _nibbles(g_packed).reshape(-1, 32)
+    o_c = _nibbles(o_packed).reshape(-1, 32)
+    gs = np.asarray(g_scales).reshape(-1)
+    os_ = np.asarray(o_scales).reshape(-1)
+    pre = np.asarray(pre, np.float64).reshape(-1, 32)
+    bnd = np.asarray(bound, np.float64).reshape(-1, 32)
+    exempt = 0
+    amax = np.abs(pre).max(axis=1)
+    bmax = bnd.max(axis=1)
+    p2 = np.exp2(np.round(np.log2(np.where(amax > 0, amax, 1.0))))
+    near_p2 = np.abs(amax - p2) <= bmax + 1e-300
+    bad_scale = (gs != os_) & ~near_p2
+    assert not bad_scale.any(), f"{what}: {bad_scale.sum()} block scales differ away from a power of two"
+    skip = gs != os_
+    exempt += int(skip.sum()) * 32
+    X = os_.astype(np.float64) - 127.0
+    scaled = np.abs(pre) / np.exp2(X)[:, None]
+    dist = np.min(np.abs(scaled[..., None] - _BOUNDS), axis=-1) * np.exp2(X)[:, None]
+    diff = (g_c != o_c) & ~skip[:, None]
+    mag_diff = ((g_c & 7) != (o_c & 7)) & diff
+    sign_diff = ((g_c & 8) != (o_c & 8)) & diff
+    bad = (mag_diff & (dist > bnd)) | (sign_diff & (np.abs(pre) > bnd))
+    assert not bad.any(), (f"{what}: {bad.sum()} codes differ away from a rounding boundary "
+                           f"(first at {np.argwhere(bad)[0]})")
+    exempt += int(diff.sum())
+    return exempt
+
+
+def compare_bf16_rounding(g_u16, pre, bound, what=""):
+    """bf16 of an fp32 value: the GPU choice may be at most `bound` worse than the nearest."""
+    g = bf16_to_f64(g_u16)
+    pre = np.asarray(pre, np.float64)
+    v32 = pre.astype(np.float32)
+    u = v32.view(np.uint32).astype(np.uint64)
+    o = ((u + np.uint64(0x7FFF) + ((u >> np.uint64(16)) & np.uint64(1))) >> np.uint64(16)).astype(np.uint16)
+    od = bf16_to_f64(o)
+    ok = np.abs(g - pre) <= np.abs(od - pre) + np.asarray(bound) + 1e-300
+    assert ok.all(), f"{what}: {(~ok).sum()} bf16 values off"
+    return int((g != od).sum())
+
+
+def check_topk(g_idx, o_idx, js, scores, rel=1e-4, what=""):
+    """g_idx, o_idx: int [k] rows; js/scores: every scored entry and its oracle score."""
+    g = np.asarray(g_idx)
+    o = np.asarray(o_idx)
+    gv, ov = g[g >= 0], o[o >= 0]
+    assert len(gv) == len(ov), f"{what}: {len(gv)} selected vs {len(ov)}"
+    assert np.all(g[len(gv):] == -1), f"{what}: -1 padding not at the end"
+    assert np.all(np.diff(gv) > 0), f"{what}: selection not strictly ascending"
+    d = set(gv.tolist()) ^ set(ov.tolist())
+    if not d:
+        return 0
+    sc = dict(zip(np.asarray(js).tolist(), np.asarray(scores).tolist()))
+    sk = min(sc[j] for j in ov.tolist())
+    for j in d:
+        assert j in sc, f"{what}: entry {j} was not a scored entry"
+        assert abs(sc[j] - sk) <= rel * abs(sk) + 1e-30, f"{what}: entry {j} score {sc[j]} vs k-th {sk}"
+    return len(d) // 2
+
+
+def row_rel_err(g, r):
+    g = np.asarray(g, np.float64)
+    r = np.asarray(r, np.float64)
+    den = np.abs(r).max(axis=-1)
+    num = np.abs(g - r).max(axis=-1)
+    return np.where(den > 0, num / np.where(den > 0, den, 1), num)
+
+
+def decode_cache_rows(nope, nscale, rope):
+    return np.concatenate([mxfp4_decode(nope, nscale), bf16_to_f64(rope)], axis=-1)

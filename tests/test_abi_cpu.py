@@ -1,0 +1,127 @@
+"""The C ABI on a machine without a GPU: symbols and host-side argument checks.
+
+Only calls that fail their host-side checks are made here; such calls
+return before any HIP call, so no GPU is needed.
+"""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from compressed_sparse_attention_compressor_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "csa.h")
+
+OK, ENULL, ESHAPE, EALIGN, EUNSUP, EWS = 0, -1, -2, -3, -4, -5
+P = 0x10000          # a fake, 16-byte aligned device address (never dereferenced)
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(_lib.LIB_PATH):
+        pytest.fail("libcsa.so is not built (run __graft_entry__.build())")
+    return _lib.lib()
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*((?:csa|hca)_\w+)\s*\(", src, flags=re.M)))
+
+
+def test_every_declared_symbol_is_exported(L):
+    names = _declared()
+    assert {"csa_compress", "csa_index_topk", "csa_sparse_attn", "hca_dense_attn"} <= set(names)
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(_lib._SIGS) == set(names)
+
+
+def test_status_strings_and_version(L):
+    assert L.csa_version() >= 10000
+    for s in (OK, ENULL, ESHAPE, EALIGN, EUNSUP, EWS, -6):
+        assert L.csa_status_str(s)
+
+
+def _cache(B=2, N=64, m=4, d_idx=128, **kw):
+    c = _lib.CacheT(P, P, P, P if d_idx else None, P if d_idx else None, P, B, N, 512, 64, d_idx, m)
+    for k, v in kw.items():
+        setattr(c, k, v)
+    return c
+
+
+def _compress(L, c, x=P, z=P, G=576, bias=P, w=P, tb=0, T=64, xs=64 * 576, zs=64 * 576):
+    return L.csa_compress(x, xs, z, zs, G, bias, w, tb, T, ctypes.byref(c) if c is not None else None, None)
+
+
+def test_compress_checks(L):
+    assert _compress(L, None) == ENULL
+    assert _compress(L, _cache(), x=None) == ENULL
+    assert _compress(L, _cache(d_idx=0)) == ENULL            # w_ik given, no key planes
+    assert _compress(L, _cache(d_nope=256)) == EUNSUP
+    assert _compress(L, _cache(m=0)) == EUNSUP
+    assert _compress(L, _cache(m=300)) == EUNSUP
+    assert _compress(L, _cache(d_idx=96)) == EUNSUP
+    assert _compress(L, _cache(), G=7) == EUNSUP
+    assert _compress(L, _cache(), tb=2) == ESHAPE             # not a multiple of m
+    assert _compress(L, _cache(), T=6) == ESHAPE
+    assert _compress(L, _cache(N=8), T=64) == ESHAPE          # beyond N_cap
+    assert _compress(L, _cache(), xs=10) == ESHAPE            # rows overlap across sequences
+    assert _compress(L, _cache(), x=P + 2) == EALIGN
+    assert _compress(L, _cache(nope=P + 8)) == EALIGN
+    assert _compress(L, _cache(), T=0) == OK                  # nothing to do, no launch
+
+
+def _index(L, c, qi=P, w=P, HI=32, qp=P, Q=1, cand=None, C=0, k=8, out=P, ws=P, wsb=1 << 30):
+    return L.csa_index_topk(ctypes.byref(c), qi, w, HI, qp, Q, cand, C, k, out, None, ws, wsb, None)
+
+
+def test_index_topk_checks(L):
+    assert _index(L, _cache(ikey=None)) == ENULL
+    assert _index(L, _cache(), qi=None) == ENULL
+    assert _index(L, _cache(), out=None) == ENULL
+    assert _index(L, _cache(), HI=0) == EUNSUP
+    assert _index(L, _cache(), HI=65) == EUNSUP
+    assert _index(L, _cache(), k=-1) == ESHAPE
+    assert _index(L, _cache(), qi=P + 4) == EALIGN
+    need = L.csa_workspace_bytes(0, 2, 1, 0, 64, 0)
+    assert need == 2 * 64 * 4
+    assert _index(L, _cache(), wsb=need - 1) == EWS
+    assert _index(L, _cache(), ws=None) == ENULL
+    assert _index(L, _cache(), Q=0) == OK
+    assert _index(L, _cache(), k=0) == OK
+
+
+def _attn(L, c, q=P, H=64, qp=P, Q=1, idx=P, k=16, swa=P, s0=P, S=128, nw=128, scale=1.0, od=1, out=P,
+          ws=P, wsb=1 << 30):
+    return L.csa_sparse_attn(ctypes.byref(c), q, H, qp, Q, idx, k, swa, s0, S, nw, scale, od, out, None, ws, wsb, None)
+
+
+def test_attention_checks(L):
+    assert _attn(L, _cache(), q=None) == ENULL
+    assert _attn(L, _cache(), idx=None) == ENULL
+    assert _attn(L, _cache(), swa=None) == ENULL
+    assert _attn(L, _cache(), H=48) == EUNSUP
+    assert _attn(L, _cache(), H=256) == EUNSUP
+    assert _attn(L, _cache(), od=5) == EUNSUP
+    assert _attn(L, _cache(), scale=float("nan")) == ESHAPE
+    assert _attn(L, _cache(), k=-2) == ESHAPE
+    assert _attn(L, _cache(), nw=-1) == ESHAPE
+    assert _attn(L, _cache(), out=P + 2) == EALIGN
+    need = L.csa_workspace_bytes(1, 2, 1, 64, 16, 128)
+    assert need > 0
+    assert _attn(L, _cache(), wsb=need - 1) == EWS
+    assert _attn(L, _cache(), Q=0) == OK
+    assert L.hca_dense_attn(ctypes.byref(_cache(d_idx=0)), None, 64, P, 1, P, P, 128, 128, 1.0, 1, P, None, P,
+                            1 << 30, None) == ENULL
+
+
+def test_workspace_sizes_consistent(L):
+    # one split (no partials) once there are enough query rows
+    assert L.csa_workspace_bytes(1, 1, 65536, 64, 1024, 128) == 0
+    # several splits for a single long row, with (O, max, sum) per head
+    w = L.csa_workspace_bytes(2, 8, 1, 64, 8192, 128)
+    assert w > 0 and w % (8 * 64 * (576 + 2) * 4) == 0

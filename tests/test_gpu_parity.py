@@ -1,0 +1,395 @@
+"""HIP path vs the float64 oracle on the same seeded inputs (small sizes).
+
+Sizes span several workgroup tiles and ragged tails; the comparison rules
+are in gpu_check.py.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import compressed_sparse_attention_compressor_amd as csa
+import oracle as O
+from gpu_check import (
+    check_topk,
+    compare_bf16_rounding,
+    compare_mxfp4,
+    decode_cache_rows,
+    row_rel_err,
+)
+from synth import TensorId, normal_bf16, normal_e4m3, normal_f32, uniform_int
+from synth.workloads import (
+    TINY_DECODE,
+    Workload,
+    as_u16,
+    params,
+    queries,
+    raw_rows,
+    synthetic_cache,
+)
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+TOL = {torch.float32: 1e-3, torch.bfloat16: 2e-2}
+
+
+def _np(t):
+    t = t.detach().cpu().contiguous()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy().view(np.uint16)
+    return t.numpy()
+
+
+def _gpu_cache(planes, B, N_cap, m, d_idx, n_entries):
+    def up(a, dt=None):
+        if a is None:
+            return None
+        if isinstance(a, torch.Tensor):
+            return a.contiguous().to(DEV)
+        t = torch.from_numpy(np.ascontiguousarray(a))
+        if dt is not None:
+            t = t.view(dt)
+        return t.to(DEV)
+    p = dict(nope=up(planes["nope"]), nscale=up(planes["nscale"]),
+             rope=up(planes["rope"], torch.bfloat16) if isinstance(planes["rope"], np.ndarray) else up(planes["rope"]),
+             ikey=up(planes.get("ikey")), iscale=up(planes.get("iscale")),
+             n_entries=torch.tensor(n_entries, dtype=torch.int32, device=DEV))
+    if isinstance(planes["rope"], np.ndarray):
+        p["rope"] = torch.from_numpy(np.ascontiguousarray(planes["rope"]).view(np.int16)).view(torch.bfloat16).to(DEV)
+    return csa.Cache(B, N_cap, m, d_idx, planes=p)
+
+
+def _compress_bounds(out, m, W=None):
+    pool_b = (8 + 2 * m) * 2.0 ** -22 * out["pooled_abs"]
+    kb = None
+    if W is not None:
+        Wa = np.abs(O.bf16_to_f64(W))
+        kb = 2.0 ** -14 * out["kI_abs"] + (8 + 2 * m) * 2.0 ** -22 * (out["pooled_abs"] @ Wa)
+    return pool_b, kb
+
+
+# ----------------------------------------------------------------------------- generators
+
+
+def test_synth_bit_identical_on_gpu():
+    for fn, tid, shape, sc in [(normal_bf16, TensorId.X, (2, 300, 576), 1.0),
+                               (normal_bf16, TensorId.Q, (1, 3, 64, 576), 1 / 24),
+                               (normal_e4m3, TensorId.QI, (2, 5, 32, 128), 1 / 11.3),
+                               (normal_f32, TensorId.W, (2, 5, 32), 1.0)]:
+        a = fn(7, tid, shape, scale=sc)
+        b = fn(7, tid, shape, scale=sc, device=DEV).cpu()
+        assert torch.equal(a.view(torch.uint8), b.view(torch.uint8))
+
+
+# ----------------------------------------------------------------------------- compressor
+
+
+@pytest.mark.parametrize("d_idx", [64, 128])
+def test_codec_bit_exact_on_identical_fp32_values(d_idx):
+    """m = 1 makes the pooled value the bf16 input itself, so every code must match."""
+    rng = np.random.default_rng(d_idx)
+    B, T = 2, 96
+    x = rng.standard_normal((B, T, 576)).astype(np.float32) * np.exp2(rng.integers(-20, 20, (B, T, 1)))
+    mids = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 6.0, 7.0, 0.5, 3.0])
+    for t in range(0, T, 3):
+        for blk in range(18):
+            k = int(rng.integers(-30, 30))
+            v = rng.choice(mids, 32) * rng.choice([-1.0, 1.0], 32) * 2.0 ** k
+            v[0] = 6.0 * 2.0 ** k
+            x[t % B, t, 32 * blk:32 * blk + 32] = v
+    x[0, 1, :64] = 0.0
+    x[1, 2, 32:64] = -2.0 ** -130
+    xb = O.f32_to_bf16(x)
+    z = O.f32_to_bf16(rng.standard_normal((B, T, 576)))
+    pick = rng.permutation(576)[:d_idx]
+    W = np.zeros((576, d_idx), np.float32)
+    W[pick, np.arange(d_idx)] = 1.0
+    Wb = O.f32_to_bf16(W)
+    bias = np.zeros(1, np.float32)
+    cache = csa.Cache(B, T, 1, d_idx)
+    tb = lambda a: torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(DEV)
+    csa.compress(cache, tb(xb), tb(z), torch.from_numpy(bias).to(DEV), tb(Wb))
+    torch.cuda.synchronize()
+    for b in range(B):
+        o = O.compress(xb[b], z[b], bias, Wb, 1)
+        np.testing.assert_array_equal(_np(cache.nope[b]), o["nope"])
+        np.testing.assert_array_equal(_np(cache.nscale[b]), o["nscale"])
+        np.testing.assert_array_equal(_np(cache.rope[b]), o["rope"])
+        np.testing.assert_array_equal(_np(cache.ikey[b]), o["ikey"])
+        np.testing.assert_array_equal(_np(cache.iscale[b]), o["iscale"])
+
+
+COMPRESS_CASES = [
+    # (name, workload, T per call list, G, with index keys)
+    ("tiny-decode-cache", TINY_DECODE, [4096], 576, True),
+    ("hca-m128", Workload("hca-small", 4, B=2, T=2048, m=128, d_idx=0, H_I=0, k=0, H=64, n_win=128), [2048], 576,
+     False),
+    ("gate1-chunked-ragged", Workload("g1", 6, B=3, T=148, m=4, d_idx=128, H_I=32, k=8, H=64, n_win=8), [64, 84], 1,
+     True),
+]
+
+
+@pytest.mark.parametrize("name,w,chunks,G,with_keys", COMPRESS_CASES, ids=[c[0] for c in COMPRESS_CASES])
+def test_compress_parity(name, w, chunks, G, with_keys):
+    bias, wik = params(w)
+    x, z = raw_rows(w, 0, w.T)
+    if G == 1:
+        z = z[:, :, :1].contiguous()
+    cache = csa.Cache(w.B, w.N, w.m, w.d_idx)
+    bias_d = bias.to(DEV)
+    wik_d = wik.to(DEV) if with_keys else None
+    t0 = 0
+    for T in chunks:
+        csa.compress(cache, x[:, t0:t0 + T].to(DEV), z[:, t0:t0 + T].to(DEV), bias_d, wik_d, tok_begin=t0)
+        t0 += T
+    torch.cuda.synchronize()
+    total = exempt = 0
+    for b in range(w.B):
+        o = O.compress(as_u16(x[b]), as_u16(z[b]), bias.numpy(), as_u16(wik) if with_keys else None, w.m)
+        pb, kb = _compress_bounds(o, w.m, as_u16(wik) if with_keys else None)
+        exempt += compare_mxfp4(_np(cache.nope[b]), _np(cache.nscale[b]), o["nope"], o["nscale"],
+                                o["pooled"][:, :512], pb[:, :512], f"{name} nope b={b}")
+        exempt += compare_bf16_rounding(_np(cache.rope[b]), o["pooled"][:, 512:], pb[:, 512:], f"{name} rope")
+        total += o["pooled"].size
+        if with_keys:
+            exempt += compare_mxfp4(_np(cache.ikey[b]), _np(cache.iscale[b]), o["ikey"], o["iscale"], o["kI"], kb,
+                                    f"{name} ikey b={b}")
+            total += o["kI"].size
+    assert exempt <= max(4, 1e-3 * total), f"{exempt} exemptions of {total}"
+
+
+# ----------------------------------------------------------------------------- indexer + top-k
+
+
+def _index_case(w, N_cap, n_entries, pos, k, seed_off=0):
+    planes = synthetic_cache(w, N_cap=N_cap)
+    qs = queries(w, nq=pos.shape[1])
+    qs["q_pos"] = torch.from_numpy(pos.astype(np.int32))
+    return planes, qs
+
+
+INDEX_CASES = [
+    ("tiny", TINY_DECODE, 1024, [1024], [[4095]], 64),
+    ("ragged-causal-qb4", Workload("r", 7, B=2, T=4000, m=4, d_idx=128, H_I=32, k=64, H=64, n_win=0, Q=6),
+     1000, [1000, 700], [[3, 100, 1999, 2001, 3999, 3999], [0, 7, 400, 2799, 3999, 1000]], 64),
+    ("fewer-than-k", Workload("f", 8, B=1, T=400, m=4, d_idx=128, H_I=32, k=64, H=64, n_win=0, Q=2),
+     100, [100], [[40, 2]], 64),
+    ("heads64", Workload("h64", 9, B=1, T=8192, m=4, d_idx=128, H_I=64, k=100, H=64, n_win=0), 2048, [2048],
+     [[8191]], 100),
+    ("heads48-d64", Workload("h48", 10, B=2, T=3000, m=4, d_idx=64, H_I=48, k=33, H=64, n_win=0), 750, [750, 750],
+     [[2999], [1500]], 33),
+]
+
+
+@pytest.mark.parametrize("name,w,N_cap,n_entries,pos,k", INDEX_CASES, ids=[c[0] for c in INDEX_CASES])
+def test_index_topk_parity(name, w, N_cap, n_entries, pos, k):
+    pos = np.array(pos, dtype=np.int32)
+    planes, qs = _index_case(w, N_cap, n_entries, pos, k)
+    cache = _gpu_cache(planes, w.B, N_cap, w.m, w.d_idx, n_entries)
+    idx, sc = csa.index_topk(cache, qs["qI"].to(DEV), qs["w"].to(DEV), qs["q_pos"].to(DEV), k, want_scores=True)
+    idx, sc = _np(idx), _np(sc)
+    ik, isc = planes["ikey"].numpy(), planes["iscale"].numpy()
+    for b in range(w.B):
+        for t in range(pos.shape[1]):
+            oi, os_, js, s = O.index_topk(ik[b], isc[b], qs["qI"][b, t].numpy(), qs["w"][b, t].numpy(),
+                                          int(pos[b, t]), w.m, n_entries[b], k)
+            check_topk(idx[b, t], oi, js, s, what=f"{name} b={b} t={t}")
+            sel = idx[b, t][idx[b, t] >= 0]
+            ref = dict(zip(js.tolist(), s.tolist()))
+            if len(sel):
+                r = np.array([ref[j] for j in sel])
+                scale = np.abs(s).max() + 1e-30
+                assert np.abs(sc[b, t, :len(sel)] - r).max() <= 1e-5 * scale
+            assert np.all(np.isnan(sc[b, t, len(sel):]))
+
+
+def test_reindex_candidates_parity():
+    """Second layer rescoring the first layer's selection ([V4.1] Fig. 4, Reindex)."""
+    w = Workload("c2", 11, B=3, T=16384, m=4, d_idx=128, H_I=32, k=256, H=64, n_win=0, k_b=64)
+    N = w.N
+    planes = synthetic_cache(w)
+    qa = queries(w)
+    qb = queries(w, second=True)
+    n_ent = [N, N - 5, 300]
+    cache = _gpu_cache(planes, w.B, N, w.m, w.d_idx, n_ent)
+    pos = qa["q_pos"].to(DEV)
+    ik, isc = planes["ikey"].numpy(), planes["iscale"].numpy()
+    # Layer A on the GPU against the oracle.
+    ia, _ = csa.index_topk(cache, qa["qI"].to(DEV), qa["w"].to(DEV), pos, w.k)
+    ia = _np(ia)
+    oa_all = np.full((w.B, 1, w.k), -1, np.int32)
+    for b in range(w.B):
+        oa, _, js, s = O.index_topk(ik[b], isc[b], qa["qI"][b, 0].numpy(), qa["w"][b, 0].numpy(), w.T - 1, w.m,
+                                    n_ent[b], w.k)
+        check_topk(ia[b, 0], oa, js, s, what=f"layer A b={b}")
+        oa_all[b, 0] = oa
+    # Layer B, stage-wise: both sides rescore the oracle's layer-A selection.
+    ib, _ = csa.index_topk(cache, qb["qI"].to(DEV), qb["w"].to(DEV), pos, w.k_b,
+                           cand=torch.from_numpy(oa_all).to(DEV))
+    ib = _np(ib)
+    for b in range(w.B):
+        ob, _, jb, sb = O.index_topk(ik[b], isc[b], qb["qI"][b, 0].numpy(), qb["w"][b, 0].numpy(), w.T - 1, w.m,
+                                     n_ent[b], w.k_b, cand=oa_all[b, 0])
+        check_topk(ib[b, 0], ob, jb, sb, what=f"layer B b={b}")
+        assert set(ib[b, 0][ib[b, 0] >= 0]) <= set(oa_all[b, 0][oa_all[b, 0] >= 0])
+
+
+# ----------------------------------------------------------------------------- attention
+
+
+def _attn_inputs(w, N_cap, n_entries, pos, S=None, swa_pos0=None):
+    planes = synthetic_cache(w, N_cap=N_cap)
+    qs = queries(w, nq=pos.shape[1])
+    S = S if S is not None else max(1, w.T)
+    swa_pos0 = np.zeros(w.B, np.int32) if swa_pos0 is None else np.asarray(swa_pos0, np.int32)
+    swa = torch.stack([normal_bf16(w.seed, TensorId.SWA, (1, S, 576), first_seq=b)[0] for b in range(w.B)])
+    return planes, qs, swa, swa_pos0
+
+
+def _oracle_attn(planes, qs, swa, swa_pos0, pos, idx, w, n_entries, dense, scale):
+    B, Q = pos.shape
+    H = w.H
+    o = np.zeros((B, Q, H, 576))
+    l = np.zeros((B, Q, H))
+    nope, nsc, rope = planes["nope"].numpy(), planes["nscale"].numpy(), as_u16(planes["rope"])
+    sw = as_u16(swa)
+    for b in range(B):
+        for t in range(Q):
+            qb = as_u16(qs["q"][b, t])
+            if dense:
+                o[b, t], l[b, t] = O.dense_attention(qb, nope[b], nsc[b], rope[b], sw[b], int(swa_pos0[b]),
+                                                     int(pos[b, t]), w.n_win, scale, w.m, n_entries[b])
+            else:
+                o[b, t], l[b, t] = O.sparse_attention(qb, nope[b], nsc[b], rope[b], idx[b, t], sw[b],
+                                                      int(swa_pos0[b]), int(pos[b, t]), w.n_win, scale, w.m,
+                                                      n_entries[b])
+    return o, l
+
+
+def _check_attn(g_out, g_lse, o, l, dtype, what):
+    err = row_rel_err(_np(g_out).astype(np.float64) if dtype == torch.float32 else
+                      O.bf16_to_f64(_np(g_out)), o)
+    assert err.max() <= TOL[dtype], f"{what}: row error {err.max():.3e}"
+    gl = _np(g_lse).astype(np.float64)
+    fin = np.isfinite(l)
+    assert np.array_equal(np.isfinite(gl), fin), f"{what}: lse finiteness differs"
+    assert np.all(np.abs(gl[fin] - l[fin]) <= 1e-4 * np.maximum(1.0, np.abs(l[fin]))), f"{what}: lse"
+    assert np.all(np.isneginf(gl[~fin]))
+
+
+SPARSE_CASES = [
+    ("tiny-decode", TINY_DECODE, 1024, [1024], [[4095]], None, None),
+    ("multi-query-causal", Workload("mq", 12, B=2, T=2400, m=4, d_idx=0, H_I=0, k=96, H=64, n_win=128, Q=5), 600,
+     [600, 450], [[5, 130, 1700, 2399, 2399], [0, 2, 1000, 1799, 2399]], None, None),
+    ("window-buffer-start", Workload("wb", 13, B=1, T=1000, m=4, d_idx=0, H_I=0, k=40, H=32, n_win=100, Q=3), 250,
+     [250], [[999, 950, 930]], 60, [940]),
+    ("no-window", Workload("nw", 14, B=1, T=800, m=4, d_idx=0, H_I=0, k=70, H=64, n_win=0, Q=2), 200, [200],
+     [[799, 3]], None, None),
+]
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=["f32", "bf16"])
+@pytest.mark.parametrize("name,w,N_cap,n_entries,pos,S,swa_pos0", SPARSE_CASES, ids=[c[0] for c in SPARSE_CASES])
+def test_sparse_attention_parity(name, w, N_cap, n_entries, pos, S, swa_pos0, dtype):
+    pos = np.array(pos, np.int32)
+    planes, qs, swa, s0 = _attn_inputs(w, N_cap, n_entries, pos, S, swa_pos0)
+    B, Q = pos.shape
+    # selections: random visible entries, a -1, and one index beyond the visible range
+    rng = np.random.default_rng(w.cfg)
+    idx = np.full((B, Q, w.k), -1, np.int32)
+    for b in range(B):
+        for t in range(Q):
+            V = O.visible_count(int(pos[b, t]), w.m, n_entries[b])
+            n = min(w.k - 2, V)
+            sel = np.sort(rng.choice(V, n, replace=False)) if n > 0 else np.zeros(0, np.int64)
+            idx[b, t, :n] = sel
+            idx[b, t, n] = V + 3
+    cache = _gpu_cache(planes, B, N_cap, w.m, 0, n_entries)
+    out, lse = csa.sparse_attn(cache, qs["q"].to(DEV), torch.from_numpy(pos).to(DEV), torch.from_numpy(idx).to(DEV),
+                               swa.to(DEV), torch.from_numpy(s0).to(DEV), w.n_win, w.softmax_scale, out_dtype=dtype)
+    torch.cuda.synchronize()
+    o, l = _oracle_attn(planes, qs, swa, s0, pos, idx, w, n_entries, False, w.softmax_scale)
+    _check_attn(out, lse, o, l, dtype, name)
+
+
+DENSE_CASES = [
+    ("hca-small", Workload("hs", 15, B=2, T=8192, m=128, d_idx=0, H_I=0, k=0, H=64, n_win=128, Q=3), 64, [64, 40],
+     [[8191, 127, 5000], [8191, 126, 3]]),
+    ("dense-m4-many-splits", Workload("dm", 16, B=1, T=12000, m=4, d_idx=0, H_I=0, k=0, H=16, n_win=128), 3000,
+     [3000], [[11999]]),
+]
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=["f32", "bf16"])
+@pytest.mark.parametrize("name,w,N_cap,n_entries,pos", DENSE_CASES, ids=[c[0] for c in DENSE_CASES])
+def test_dense_attention_parity(name, w, N_cap, n_entries, pos, dtype):
+    pos = np.array(pos, np.int32)
+    planes, qs, swa, s0 = _attn_inputs(w, N_cap, n_entries, pos)
+    cache = _gpu_cache(planes, w.B, N_cap, w.m, 0, n_entries)
+    out, lse = csa.hca_dense_attn(cache, qs["q"].to(DEV), torch.from_numpy(pos).to(DEV), swa.to(DEV),
+                                  torch.from_numpy(s0).to(DEV), w.n_win, w.softmax_scale, out_dtype=dtype)
+    torch.cuda.synchronize()
+    o, l = _oracle_attn(planes, qs, swa, s0, pos, None, w, n_entries, True, w.softmax_scale)
+    _check_attn(out, lse, o, l, dtype, name)
+
+
+def test_attention_with_no_keys_is_zero():
+    w = Workload("nk", 17, B=1, T=64, m=4, d_idx=0, H_I=0, k=8, H=16, n_win=0, Q=2)
+    planes, qs, swa, s0 = _attn_inputs(w, 16, [16], np.array([[2, 1]], np.int32))
+    cache = _gpu_cache(planes, 1, 16, 4, 0, [16])
+    idx = torch.full((1, 2, 8), -1, dtype=torch.int32, device=DEV)
+    out, lse = csa.sparse_attn(cache, qs["q"].to(DEV), torch.tensor([[2, 1]], dtype=torch.int32, device=DEV), idx,
+                               None, None, 0, 1.0, out_dtype=torch.float32)
+    assert torch.all(out == 0) and torch.all(torch.isneginf(lse))
+
+
+def test_hca_equals_sparse_with_every_entry():
+    w = Workload("eq", 18, B=1, T=4096, m=4, d_idx=0, H_I=0, k=1024, H=64, n_win=128)
+    planes, qs, swa, s0 = _attn_inputs(w, 1024, [1024], np.array([[4095]], np.int32))
+    cache = _gpu_cache(planes, 1, 1024, 4, 0, [1024])
+    pos = torch.tensor([[4095]], dtype=torch.int32, device=DEV)
+    idx = torch.arange(1024, dtype=torch.int32, device=DEV).view(1, 1, 1024)
+    a, la = csa.sparse_attn(cache, qs["q"].to(DEV), pos, idx, swa.to(DEV), torch.from_numpy(s0).to(DEV), 128,
+                            w.softmax_scale, out_dtype=torch.float32)
+    b, lb = csa.hca_dense_attn(cache, qs["q"].to(DEV), pos, swa.to(DEV), torch.from_numpy(s0).to(DEV), 128,
+                               w.softmax_scale, out_dtype=torch.float32)
+    err = row_rel_err(a.cpu().numpy(), b.cpu().numpy())
+    assert err.max() <= 1e-5
+
+
+# ----------------------------------------------------------------------------- whole path
+
+
+def test_end_to_end_tiny_decode():
+    """Compressor -> indexer/top-k -> sparse attention on the tiny decode
+    workload, against the oracle pipeline from the same raw inputs."""
+    w = TINY_DECODE
+    bias, wik = params(w)
+    x, z = raw_rows(w, 0, w.T)
+    qs = queries(w)
+    cache = csa.Cache(w.B, w.N, w.m, w.d_idx)
+    cache.n_entries.fill_(w.N)
+    csa.compress(cache, x.to(DEV), z.to(DEV), bias.to(DEV), wik.to(DEV))
+    idx, _ = csa.index_topk(cache, qs["qI"].to(DEV), qs["w"].to(DEV), qs["q_pos"].to(DEV), w.k)
+    swa = x[:, w.T - w.n_win:].contiguous()
+    s0 = torch.full((w.B,), w.T - w.n_win, dtype=torch.int32)
+    out, lse = csa.sparse_attn(cache, qs["q"].to(DEV), qs["q_pos"].to(DEV), idx, swa.to(DEV), s0.to(DEV), w.n_win,
+                               w.softmax_scale, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    o = O.compress(as_u16(x[0]), as_u16(z[0]), bias.numpy(), as_u16(wik), w.m)
+    pb, kb = _compress_bounds(o, w.m, as_u16(wik))
+    ex = compare_mxfp4(_np(cache.nope[0]), _np(cache.nscale[0]), o["nope"], o["nscale"], o["pooled"][:, :512],
+                       pb[:, :512], "e2e nope")
+    ex += compare_mxfp4(_np(cache.ikey[0]), _np(cache.iscale[0]), o["ikey"], o["iscale"], o["kI"], kb, "e2e ikey")
+    p = w.T - 1
+    oi, _, js, s = O.index_topk(o["ikey"], o["iscale"], qs["qI"][0, 0].numpy(), qs["w"][0, 0].numpy(), p, w.m, w.N,
+                                w.k)
+    swaps = check_topk(_np(idx)[0, 0], oi, js, s, what="e2e top-k")
+    if ex == 0 and swaps == 0:
+        oo, ol = O.sparse_attention(as_u16(qs["q"][0, 0]), o["nope"], o["nscale"], o["rope"], oi, as_u16(swa[0]),
+                                    w.T - w.n_win, p, w.n_win, w.softmax_scale, w.m, w.N)
+        err = row_rel_err(_np(out)[0, 0], oo)
+        assert err.max() <= 1e-3, err.max()
+        assert np.abs(_np(lse)[0, 0] - ol).max() <= 1e-4 * max(1.0, np.abs(ol).max())

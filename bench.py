@@ -1,0 +1,309 @@
+#!/usr/bin/env python3
+"""Decode benchmark of the compressed sparse attention path on one MI355X.
+
+Workload (default): batched CSA decode, 32 sequences at 131,072 raw tokens
+(32,768 entries of m = 4), indexer 32 heads x 128 channels (FP4 keys), top-512,
+64 query heads, window 128.  One step is one decode step of one layer for
+the 32 sequences (one new query token each):
+  csa_compress     the newest 4-token block of every sequence -> entry N-1
+  csa_index_scores indexer scores of all 32,768 entries per sequence
+  csa_topk         top-512 per sequence
+  csa_sparse_attn  attention over the 512 entries + 128 window rows (bf16 out)
+Layer caches are rotated over --layers copies so that consecutive steps
+touch different memory (the working set of the rotation is far above the
+256 MB Infinity Cache), as the layers of a model would.  The timed region
+replays HIP graphs of these launches; inputs are resident in HBM.
+
+Prints one JSON line (see the keys below); everything else goes to stderr.
+"""
+
+from __future__ import annotations
+
+import argparse
+import dataclasses
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "CSA decode query-tokens/s + achieved HBM GB/s at 128K ctx (1 MI355X)"
+HBM_PEAK_GBPS = 8000.0
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def step_bytes(w) -> dict:
+    """Algorithmic (compulsory) HBM bytes of one decode step, per stage."""
+    B, N, dI = w.B, w.N, w.d_idx
+    key = dI // 2 + dI // 32
+    entry = 256 + 16 + 128
+    per_q = {
+        "index": N * key + w.H_I * (dI + 4),
+        "attn": w.k * entry + 2 * w.n_win * 576 + 2 * (2 * w.H * 576),
+        "compress": w.m * 576 * 2 * 2 + entry + key,
+    }
+    shared = {"compress": w.m * 4 + 576 * dI * 2}
+    out = {s: B * v + shared.get(s, 0) for s, v in per_q.items()}
+    out["topk_io"] = B * (w.k * 4)
+    out["step"] = out["index"] + out["attn"] + out["compress"]
+    return out
+
+
+class Layer:
+    pass
+
+
+def build_layers(w, L, dev, log_every=8):
+    import torch
+
+    import compressed_sparse_attention_compressor_amd as csa
+    from synth.workloads import params, queries, raw_rows
+
+    bias, wik = params(w, device=dev)
+    cache0 = csa.Cache(w.B, w.N, w.m, w.d_idx, device=dev)
+    chunk = 4096
+    t_start = time.time()
+    for i, t0 in enumerate(range(0, w.T, chunk)):
+        x, z = raw_rows(w, t0, t0 + chunk, device=dev)
+        csa.compress(cache0, x, z, bias, wik, tok_begin=t0)
+        if t0 + chunk == w.T:
+            x_last, z_last = x[:, -max(w.n_win, w.m):].contiguous(), z[:, -w.m:].contiguous()
+        if i % log_every == 0:
+            torch.cuda.synchronize()
+            log(f"[bench] cache build: {t0 + chunk}/{w.T} tokens ({time.time() - t_start:.1f}s)")
+    cache0.n_entries.fill_(w.N)
+    torch.cuda.synchronize()
+    layers = []
+    for l in range(L):
+        ly = Layer()
+        if l == 0:
+            ly.cache = cache0
+        else:
+            ly.cache = csa.Cache(w.B, w.N, w.m, w.d_idx, device=dev, planes=dict(
+                nope=cache0.nope.clone(), nscale=cache0.nscale.clone(), rope=cache0.rope.clone(),
+                ikey=cache0.ikey.clone(), iscale=cache0.iscale.clone(), n_entries=cache0.n_entries.clone()))
+        wl = dataclasses.replace(w, cfg=w.cfg + 100 * l)
+        qs = queries(wl, device=dev)
+        ly.q, ly.qI, ly.w, ly.q_pos = qs["q"], qs["qI"], qs["w"], qs["q_pos"].to(dev)
+        ly.x_blk = x_last[:, -w.m:].clone()
+        ly.z_blk = z_last.clone()
+        ly.swa = x_last[:, -w.n_win:].clone()
+        ly.swa_pos0 = torch.full((w.B,), w.T - w.n_win, dtype=torch.int32, device=dev)
+        ly.idx = torch.empty(w.B, 1, w.k, dtype=torch.int32, device=dev)
+        ly.out = torch.empty(w.B, 1, w.H, 576, dtype=torch.bfloat16, device=dev)
+        ly.lse = torch.empty(w.B, 1, w.H, dtype=torch.float32, device=dev)
+        layers.append(ly)
+        torch.cuda.synchronize()
+    log(f"[bench] {L} layer caches ready ({time.time() - t_start:.1f}s)")
+    return layers, bias, wik
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=800)
+    ap.add_argument("--warmup", type=int, default=40)
+    ap.add_argument("--layers", type=int, default=8)
+    ap.add_argument("--kernel-reps", type=int, default=64)
+    ap.add_argument("--cpu-sample", type=int, default=32, help="sequences the oracle baseline runs (0 = skip)")
+    ap.add_argument("--only-index", action="store_true", help="run only indexer launches (for counter passes)")
+    ap.add_argument("--copy-calibration", action="store_true", help="run a plain device copy of known size")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the path has no multi-GPU "
+              "component in this build", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import compressed_sparse_attention_compressor_amd as csa
+    from synth.workloads import BATCHED_DECODE as w
+
+    dev = "cuda"
+    torch.cuda.set_device(0)
+    csa.lib()
+
+    if args.copy_calibration:
+        n = 1 << 30
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"[bench] copy calibration: {n} bytes read and written per copy")
+        return
+
+    L = args.layers
+    layers, bias, wik = build_layers(w, L, dev)
+    scores_ws = torch.empty(w.B, 1, w.N, dtype=torch.float32, device=dev)
+    attn_ws_bytes = csa.workspace_bytes(csa.WS_SPARSE_ATTN, w.B, 1, w.H, w.k, w.n_win)
+    attn_ws = torch.empty(max(attn_ws_bytes, 16), dtype=torch.uint8, device=dev)
+
+    def st_compress(ly):
+        csa.compress(ly.cache, ly.x_blk, ly.z_blk, bias, wik, tok_begin=w.T - w.m)
+
+    def st_index(ly):
+        csa.index_scores(ly.cache, ly.qI, ly.w, ly.q_pos, scores=scores_ws)
+
+    def st_topk(ly):
+        csa.topk(ly.cache, scores_ws, ly.q_pos, w.k, out=ly.idx)
+
+    def st_attn(ly):
+        csa.sparse_attn(ly.cache, ly.q, ly.q_pos, ly.idx, ly.swa, ly.swa_pos0, w.n_win, w.softmax_scale,
+                        out_dtype=torch.bfloat16, ws=attn_ws, out=ly.out, lse=ly.lse)
+
+    stages = [st_compress, st_index, st_topk, st_attn]
+    if args.only_index:
+        stages = [st_index]
+
+    def step(l):
+        for f in stages:
+            f(layers[l])
+
+    # warmup (eager)
+    for i in range(args.warmup):
+        step(i % L)
+    torch.cuda.synchronize()
+    log(f"[bench] warmup {args.warmup} steps done")
+
+    def capture(fn):
+        g = torch.cuda.CUDAGraph()
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            fn()
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g):
+            fn()
+        torch.cuda.synchronize()
+        return g
+
+    g_all = capture(lambda: [step(l) for l in range(L)])
+    g_one = [capture(lambda l=l: step(l)) for l in range(L)]
+    K = args.steps
+    for _ in range(2):
+        g_all.replay()
+    torch.cuda.synchronize()
+
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record()
+    for _ in range(K // L):
+        g_all.replay()
+    for j in range(K % L):
+        g_one[j].replay()
+    e1.record()
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3
+    gpu_ms = e0.elapsed_time(e1)
+    ms = max(gpu_ms, 0.0) / K
+    log(f"[bench] timed {K} steps: {gpu_ms:.3f} ms (GPU events), {wall_ms:.3f} ms wall")
+
+    # Per-stage average launch durations: graphs of back-to-back launches of
+    # one stage over the rotating layers, timed with events on the stream
+    # the kernels run on.
+    R = args.kernel_reps
+    stage_us = {}
+    names = {st_compress: "compress", st_index: "index_scores", st_topk: "topk", st_attn: "sparse_attn"}
+    for f in stages:
+        g = capture(lambda f=f: [f(layers[i % L]) for i in range(R)])
+        g.replay()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        reps = 5
+        a.record()
+        for _ in range(reps):
+            g.replay()
+        b.record()
+        torch.cuda.synchronize()
+        stage_us[names[f]] = a.elapsed_time(b) * 1e3 / (reps * R)
+    log(f"[bench] stage averages (us): {stage_us}")
+
+    by = step_bytes(w)
+    idx_us = stage_us["index_scores"]
+    achieved = by["index"] / (idx_us * 1e-6) / 1e9
+    traffic = None
+    prof = os.path.join(ROOT, "profiles", "index_scores_counters.json")
+    if os.path.exists(prof):
+        with open(prof) as fh:
+            pc = json.load(fh)
+        src = os.path.join(ROOT, "compressed_sparse_attention_compressor_amd", "csrc", "index.hip")
+        sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+        if pc.get("index_hip_sha256") == sha:
+            traffic = pc.get("traffic_bytes_per_launch")
+
+    result = {
+        "metric": METRIC,
+        "value": round(w.B / (ms * 1e-3), 1),
+        "unit": "query-tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8xfp4+bf16 (fp32 accumulate)",
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "context": w.T, "m": w.m, "entries": w.N, "top_k": w.k,
+                   "heads": w.H, "index_heads": w.H_I, "d_idx": w.d_idx, "n_win": w.n_win, "layers_rotated": L,
+                   "stages": [names[f] for f in stages]},
+        "achieved_GBps": round(by["step"] / (ms * 1e-3) / 1e9, 1),
+        "step_bytes": by["step"],
+        "stage_us": {k: round(v, 3) for k, v in stage_us.items()},
+        "roofline": {"bound": "hbm", "kernel": "index_scores", "achieved": round(achieved, 1),
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                     "traffic": traffic, "bytes_per_launch": by["index"], "avg_launch_us": round(idx_us, 3)},
+    }
+    if args.only_index:
+        result["value"] = None
+
+    if args.cpu_sample > 0 and not args.only_index:
+        result["cpu_baseline"] = cpu_baseline(w, args.cpu_sample)
+
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline(w, nseq):
+    """The float64 oracle on `nseq` sequences of the same decode step (host cores)."""
+    import numpy as np
+
+    import oracle as O
+    from synth.workloads import as_u16, params, queries, raw_rows, synthetic_cache
+
+    try:
+        import threadpoolctl
+        threads = max([p.get("num_threads", 1) for p in threadpoolctl.threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    bias, wik = params(w)
+    qs = queries(w)
+    planes = synthetic_cache(w, nseq=nseq)
+    x, z = raw_rows(w, w.T - max(w.n_win, w.m), w.T, nseq=nseq)
+    t0 = time.perf_counter()
+    p = w.T - 1
+    for b in range(nseq):
+        O.compress(as_u16(x[b, -w.m:]), as_u16(z[b, -w.m:]), bias.numpy(), as_u16(wik), w.m)
+        ik, isc = planes["ikey"][b].numpy(), planes["iscale"][b].numpy()
+        idx, _, _, _ = O.index_topk(ik, isc, qs["qI"][b, 0].numpy(), qs["w"][b, 0].numpy(), p, w.m, w.N, w.k)
+        O.sparse_attention(as_u16(qs["q"][b, 0]), planes["nope"][b].numpy(), planes["nscale"][b].numpy(),
+                           as_u16(planes["rope"][b]), idx, as_u16(x[b, -w.n_win:]), w.T - w.n_win, p, w.n_win,
+                           w.softmax_scale, w.m, w.N)
+    dt = time.perf_counter() - t0
+    return {"value": round(nseq / dt, 3), "unit": "query-tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{nseq} of {w.B} sequences of one decode step (compress block, index {w.N} entries, "
+                      f"top-{w.k}, attention), {dt:.2f} s"}
+
+
+if __name__ == "__main__":
+    main()

@@ -12,7 +12,9 @@ from .ops import (  # noqa: F401
     Cache,
     compress,
     hca_dense_attn,
+    index_scores,
     index_topk,
+    topk,
     sparse_attn,
     workspace_bytes,
     WS_DENSE_ATTN,

@@ -126,31 +126,67 @@ int csa_compress(const uint16_t *x, int64_t x_stride_b, const uint16_t *z, int64
                                         (int)(T / cache->m), v, stream));
 }
 
+static int check_index_args(const csa_cache_t *cache, const uint8_t *q_idx, const float *w_idx, int H_I,
+                            const int32_t *q_pos, int Q, const int32_t *cand, int C) {
+  int st = check_cache(cache, true);
+  if (st) return st;
+  if (!q_idx || !w_idx || !q_pos) return CSA_ERR_NULL;
+  if (Q < 0 || (cand && C < 0)) return CSA_ERR_SHAPE;
+  if (H_I < 1 || H_I > kMaxHI) return CSA_ERR_UNSUPPORTED;
+  if (cand && Q > 65535) return CSA_ERR_UNSUPPORTED;
+  if (!aligned16(q_idx)) return CSA_ERR_ALIGN;
+  return CSA_OK;
+}
+
+static int check_topk_args(const csa_cache_t *cache, const int32_t *q_pos, int Q, const int32_t *cand, int C, int k,
+                           const int32_t *idx_out) {
+  int st = check_cache(cache, false);
+  if (st) return st;
+  if (!q_pos || !idx_out) return CSA_ERR_NULL;
+  if (Q < 0 || k < 0 || (cand && C < 0)) return CSA_ERR_SHAPE;
+  if (k > kMaxK) return CSA_ERR_UNSUPPORTED;
+  return CSA_OK;
+}
+
+int csa_index_scores(const csa_cache_t *cache, const uint8_t *q_idx, const float *w_idx, int H_I,
+                     const int32_t *q_pos, int Q, const int32_t *cand, int C, float *scores, size_t scores_bytes,
+                     hipStream_t stream) {
+  int st = check_index_args(cache, q_idx, w_idx, H_I, q_pos, Q, cand, C);
+  if (st) return st;
+  if (!scores) return CSA_ERR_NULL;
+  if (Q == 0 || cache->B == 0) return CSA_OK;
+  if (scores_bytes < index_ws_bytes(cache->B, Q, cache->N_cap, cand ? C : 0)) return CSA_ERR_WORKSPACE;
+  const int Ns = cand ? C : cache->N_cap;
+  if (Ns == 0) return CSA_OK;
+  return status_of(csa::launch_index_scores(view_of(cache), q_idx, w_idx, H_I, q_pos, Q, cand, C, scores, stream));
+}
+
+int csa_topk(const csa_cache_t *cache, const float *scores, const int32_t *q_pos, int Q, const int32_t *cand, int C,
+             int k, int32_t *idx_out, float *score_out, hipStream_t stream) {
+  int st = check_topk_args(cache, q_pos, Q, cand, C, k, idx_out);
+  if (st) return st;
+  if (Q == 0 || cache->B == 0 || k == 0) return CSA_OK;
+  const int Ns = cand ? C : cache->N_cap;
+  if (Ns > 0 && !scores) return CSA_ERR_NULL;
+  return status_of(csa::launch_topk(view_of(cache), scores, Ns, q_pos, Q, cand, C, k, idx_out, score_out, stream));
+}
+
 int csa_index_topk(const csa_cache_t *cache, const uint8_t *q_idx, const float *w_idx, int H_I,
                    const int32_t *q_pos, int Q, const int32_t *cand, int C, int k, int32_t *idx_out,
                    float *score_out, void *ws, size_t ws_bytes, hipStream_t stream) {
-  int st = check_cache(cache, true);
+  int st = check_index_args(cache, q_idx, w_idx, H_I, q_pos, Q, cand, C);
   if (st) return st;
-  if (!q_idx || !w_idx || !q_pos || !idx_out) return CSA_ERR_NULL;
-  if (Q < 0 || k < 0 || (cand && C < 0)) return CSA_ERR_SHAPE;
-  if (H_I < 1 || H_I > kMaxHI) return CSA_ERR_UNSUPPORTED;
-  if (k > kMaxK) return CSA_ERR_UNSUPPORTED;
-  if (cand && Q > 65535) return CSA_ERR_UNSUPPORTED;
-  if (!aligned16(q_idx)) return CSA_ERR_ALIGN;
+  st = check_topk_args(cache, q_pos, Q, cand, C, k, idx_out);
+  if (st) return st;
   if (Q == 0 || cache->B == 0 || k == 0) return CSA_OK;
-  const int Cn = cand ? C : 0;
-  const size_t need = index_ws_bytes(cache->B, Q, cache->N_cap, Cn);
+  const size_t need = index_ws_bytes(cache->B, Q, cache->N_cap, cand ? C : 0);
   if (need > 0 && !ws) return CSA_ERR_NULL;
   if (ws_bytes < need) return CSA_ERR_WORKSPACE;
   if (!aligned16(ws)) return CSA_ERR_ALIGN;
-  const csa::CacheView v = view_of(cache);
   float *scores = reinterpret_cast<float *>(ws);
-  const int Ns = cand ? C : cache->N_cap;
-  if (Ns > 0) {
-    st = status_of(csa::launch_index_scores(v, q_idx, w_idx, H_I, q_pos, Q, cand, C, scores, stream));
-    if (st) return st;
-  }
-  return status_of(csa::launch_topk(v, scores, Ns, q_pos, Q, cand, C, k, idx_out, score_out, stream));
+  st = csa_index_scores(cache, q_idx, w_idx, H_I, q_pos, Q, cand, C, scores, ws_bytes, stream);
+  if (st) return st;
+  return csa_topk(cache, scores, q_pos, Q, cand, C, k, idx_out, score_out, stream);
 }
 
 int csa_sparse_attn(const csa_cache_t *cache, const uint16_t *q, int H, const int32_t *q_pos, int Q,

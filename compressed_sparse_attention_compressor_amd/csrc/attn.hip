@@ -7,16 +7,21 @@
 // and the value are the same decoded 576-channel row.
 //
 // Work split: one workgroup per (query, key-range split), one wave per 16
-// query heads (heads are the MFMA M dimension, so every key is loaded once
+// query heads (heads are the MFMA M dimension, so every key is decoded once
 // per workgroup and shared by all heads).  Per chunk of 32 key slots:
 //   1. the slot list is resolved (selected entry, window row, or nothing);
-//   2. the workgroup decodes the 32 rows (E2M1 x E8M0 -> bf16 is exact)
-//      into LDS twice: key-major for Q K^T and channel-major for P V;
+//   2. the workgroup decodes the 32 rows into a key-major bf16 LDS tile
+//      (E2M1 x E8M0 -> bf16 is exact; gfx950's v_cvt_scalef32_pk_bf16_fp4
+//      converts two codes per instruction); when a chunk's loads fit one
+//      register batch, the next chunk's raw bytes are fetched while the
+//      current chunk is computed (the tile is double buffered);
 //   3. S = Q K^T on v_mfma_f32_16x16x32_bf16 (lane: key l%16, heads
 //      4(l/16)..+3), online softmax in the log2 domain;
-//   4. P goes through a small per-wave LDS tile to become the A operand
-//      of O += P V.  With fp32 outputs P is split into two bf16 parts
-//      (hi + lo) so that the probabilities keep ~16 bits.
+//   4. P goes through a small per-wave LDS tile to become the A operand of
+//      O += P V; the V operand (keys along K) is read transposed from the
+//      same key-major tile with ds_read_b64_tr_b16, so no second copy of
+//      the keys is written.  With fp32 outputs P is split into two bf16
+//      parts (hi + lo) so that the probabilities keep ~16 bits.
 // Splits write unnormalised (O, max, sum) partials that a merge kernel
 // combines; a single split writes the normalised output directly.
 #include "csa_device.hpp"
@@ -26,9 +31,10 @@ namespace csa {
 
 constexpr int kKC = 32;           // key slots per chunk
 constexpr int kKRow = kD + 8;     // key-major LDS row (bf16 elements)
-constexpr int kVRow = kKC + 8;    // channel-major LDS row
 constexpr int kPRow = kKC + 8;
 constexpr int kNT = kD / 16;      // 36 channel tiles of 16
+constexpr int kHalfD = kD / 2;    // channels per wave of a wave pair
+constexpr int kHalfNT = kNT / 2;
 
 struct AttnArgs {
   const uint8_t *nope;
@@ -54,17 +60,80 @@ struct AttnArgs {
   int nsplit, per_split;
 };
 
+// Raw bytes of one decode task: 16 channels of one key.
+struct RawTask {
+  uint4 a, b;       // bf16 rows: 32 bytes; MXFP4: a.x, a.y hold 16 codes
+  uint32_t meta;    // kind (0 nothing, 1 MXFP4, 2 bf16) | E8M0 scale byte << 8
+};
+
+constexpr int kSegs = kD / 16;          // 36 tasks of 16 channels per key
+constexpr int kChunkTasks = kKC * kSegs;
+
+__device__ __forceinline__ void load_task(const AttnArgs &a, int b, int src, int seg, RawTask &t) {
+  t.meta = 0;
+  if (src < 0) return;
+  const int ch = seg * 16;
+  if (src & 0x40000000) {
+    const int64_t rr = src & 0x3FFFFFFF;
+    const uint4 *p = reinterpret_cast<const uint4 *>(a.swa + ((int64_t)b * a.S + rr) * kD + ch);
+    t.a = p[0];
+    t.b = p[1];
+    t.meta = 2;
+  } else {
+    const int64_t row = (int64_t)b * a.N_cap + src;
+    if (ch < kDNope) {
+      const uint2 c = *reinterpret_cast<const uint2 *>(a.nope + row * kNopeBytes + ch / 2);
+      t.a.x = c.x;
+      t.a.y = c.y;
+      t.meta = 1u | ((uint32_t)a.nscale[row * kNopeScales + ch / 32] << 8);
+    } else {
+      const uint4 *p = reinterpret_cast<const uint4 *>(a.rope + row * kDRope + (ch - kDNope));
+      t.a = p[0];
+      t.b = p[1];
+      t.meta = 2;
+    }
+  }
+}
+
+// Writes the 16 decoded bf16 channels of a task (zeros for an empty slot).
+__device__ __forceinline__ void store_task(uint16_t *row, const RawTask &t) {
+  uint4 lo = {0u, 0u, 0u, 0u}, hi = {0u, 0u, 0u, 0u};
+  const uint32_t kind = t.meta & 0xFFu;
+  if (kind == 2) {
+    lo = t.a;
+    hi = t.b;
+  } else if (kind == 1) {
+    // E2M1 x 2^(s-127) -> bf16 is exact (hardware conversion, two codes per byte)
+    const float sc = e8m0_to_f32(t.meta >> 8);
+#define CSA_CVT(src, sel) __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(src, sc, sel))
+    lo = uint4{CSA_CVT(t.a.x, 0), CSA_CVT(t.a.x, 1), CSA_CVT(t.a.x, 2), CSA_CVT(t.a.x, 3)};
+    hi = uint4{CSA_CVT(t.a.y, 0), CSA_CVT(t.a.y, 1), CSA_CVT(t.a.y, 2), CSA_CVT(t.a.y, 3)};
+#undef CSA_CVT
+  }
+  reinterpret_cast<uint4 *>(row)[0] = lo;
+  reinterpret_cast<uint4 *>(row)[1] = hi;
+}
+
 template <int HG, bool kSplitP, bool kDense>
-__global__ __launch_bounds__(HG * 64) void attn_kernel(AttnArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t Kl[kKC * kKRow];
-  __shared__ __attribute__((aligned(16))) uint16_t Vt[kD * kVRow];
-  __shared__ __attribute__((aligned(16))) uint16_t Pl[HG][kSplitP ? 2 : 1][16 * kPRow];
-  __shared__ int src_s[kKC];
+__global__ __launch_bounds__(HG * 128) void attn_kernel(AttnArgs a) {
+  // Key-major bf16 tiles of the chunk (double buffered); the P V operand is
+  // read transposed from the same tile with ds_read_b64_tr_b16.
+  __shared__ __attribute__((aligned(16))) uint16_t Kl[2][kKC * kKRow];
+  __shared__ __attribute__((aligned(16))) uint16_t Pl[2 * HG][kSplitP ? 2 : 1][16 * kPRow];
+  __shared__ __attribute__((aligned(16))) float Sx[2 * HG][2 * 4 * 64];
+  __shared__ int src_s[2][kKC];
+
+  constexpr int nthr = HG * 128;
+  constexpr int kTasksPerThread = (kChunkTasks + nthr - 1) / nthr;
+  constexpr int kBatch = kTasksPerThread < 5 ? kTasksPerThread : 5;
+  constexpr bool kOneBatch = kBatch == kTasksPerThread;  // prefetch the next chunk in registers
 
   const int split = blockIdx.x % a.nsplit, q = blockIdx.x / a.nsplit, b = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, r = lane & 15;
-  constexpr int nthr = HG * 64;
+  // wave pair (2hg, 2hg+1) shares heads 16hg..16hg+15; `half` picks channels [288 half, +288)
+  const int hg = wave >> 1, half = wave & 1;
+  const int cbase = half * kHalfD;
   const int64_t qrow = (int64_t)b * a.Q + q;
   const int p = a.q_pos[qrow];
   const int nE = min(a.n_entries[b], a.N_cap);
@@ -81,25 +150,7 @@ __global__ __launch_bounds__(HG * 64) void attn_kernel(AttnArgs a) {
   const int s_begin = split * a.per_split;
   const int s_end = min(n_slots, s_begin + a.per_split);
 
-  const int h0 = wave * 16;
-  v8bf Qf[kD / 32];
-  {
-    const uint16_t *qp = a.q + (qrow * a.H + h0 + r) * kD + 8 * g;
-#pragma unroll
-    for (int kk = 0; kk < kD / 32; ++kk) Qf[kk] = *reinterpret_cast<const v8bf *>(qp + 32 * kk);
-  }
-
-  float m2[4], lsum[4];
-  v4f O[kNT];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    m2[i] = -INFINITY;
-    lsum[i] = 0.f;
-  }
-#pragma unroll
-  for (int j = 0; j < kNT; ++j) O[j] = v4f{0.f, 0.f, 0.f, 0.f};
-
-  for (int c0 = s_begin; c0 < s_end; c0 += kKC) {
+  auto resolve = [&](int c0, int buf) {
     if (tid < kKC) {
       const int slot = c0 + tid;
       int src = -1;
@@ -111,55 +162,109 @@ __global__ __launch_bounds__(HG * 64) void attn_kernel(AttnArgs a) {
           src = 0x40000000 | (win_lo + (slot - n_main) - swa0);
         }
       }
-      src_s[tid] = src;
+      src_s[buf][tid] = src;
     }
-    __syncthreads();
+  };
 
-    for (int t = tid; t < kKC * (kD / 8); t += nthr) {
-      const int key = t / (kD / 8);
-      const int ch = (t % (kD / 8)) * 8;
-      const int src = src_s[key];
-      uint4 w = {0u, 0u, 0u, 0u};
-      if (src >= 0) {
-        if (src & 0x40000000) {
-          const int64_t rr = src & 0x3FFFFFFF;
-          w = *reinterpret_cast<const uint4 *>(a.swa + ((int64_t)b * a.S + rr) * kD + ch);
-        } else {
-          const int64_t row = (int64_t)b * a.N_cap + src;
-          if (ch < kDNope) {
-            const uint32_t codes = *reinterpret_cast<const uint32_t *>(a.nope + row * kNopeBytes + ch / 2);
-            const float sc = e8m0_to_f32(a.nscale[row * kNopeScales + ch / 32]);
-            uint32_t hw[8];
+  const int h0 = hg * 16;
+  v8bf Qf[kHalfD / 32];
+  {
+    const uint16_t *qp = a.q + (qrow * a.H + h0 + r) * kD + cbase + 8 * g;
 #pragma unroll
-            for (int i = 0; i < 8; ++i) hw[i] = __float_as_uint(e2m1_to_f32((codes >> (4 * i)) & 15u) * sc) >> 16;
-            w.x = hw[0] | (hw[1] << 16);
-            w.y = hw[2] | (hw[3] << 16);
-            w.z = hw[4] | (hw[5] << 16);
-            w.w = hw[6] | (hw[7] << 16);
-          } else {
-            w = *reinterpret_cast<const uint4 *>(a.rope + row * kDRope + (ch - kDNope));
-          }
+    for (int kk = 0; kk < kHalfD / 32; ++kk) Qf[kk] = *reinterpret_cast<const v8bf *>(qp + 32 * kk);
+  }
+
+  float m2[4], lsum[4];
+  v4f O[kHalfNT];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    m2[i] = -INFINITY;
+    lsum[i] = 0.f;
+  }
+#pragma unroll
+  for (int j = 0; j < kHalfNT; ++j) O[j] = v4f{0.f, 0.f, 0.f, 0.f};
+
+  RawTask pre[kBatch];
+  if (s_begin < s_end) {
+    resolve(s_begin, 0);
+    __syncthreads();
+    if (kOneBatch) {
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        const int t = tid + u * nthr;
+        if (t < kChunkTasks) load_task(a, b, src_s[0][t / kSegs], t % kSegs, pre[u]);
+        else pre[u].meta = 0;
+      }
+    }
+  }
+
+  int buf = 0;
+  for (int c0 = s_begin; c0 < s_end; c0 += kKC, buf ^= 1) {
+    uint16_t *K = Kl[buf];
+    // 1. decode this chunk into K
+    if (kOneBatch) {
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        const int t = tid + u * nthr;
+        if (t < kChunkTasks) store_task(K + (t / kSegs) * kKRow + (t % kSegs) * 16, pre[u]);
+      }
+    } else {
+      for (int t0 = 0; t0 < kChunkTasks; t0 += kBatch * nthr) {
+        RawTask tk[kBatch];
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+          const int t = t0 + tid + u * nthr;
+          if (t < kChunkTasks) load_task(a, b, src_s[buf][t / kSegs], t % kSegs, tk[u]);
+        }
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+          const int t = t0 + tid + u * nthr;
+          if (t < kChunkTasks) store_task(K + (t / kSegs) * kKRow + (t % kSegs) * 16, tk[u]);
         }
       }
-      *reinterpret_cast<uint4 *>(&Kl[key * kKRow + ch]) = w;
-      const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-      for (int i = 0; i < 8; ++i) Vt[(ch + i) * kVRow + key] = (uint16_t)(ww[i >> 1] >> (16 * (i & 1)));
     }
+    if (c0 + kKC < s_end) resolve(c0 + kKC, buf ^ 1);
     __syncthreads();
+    // key-slot flags of this chunk, read before the next barrier (the list of
+    // this buffer is resolved again one iteration later)
+    const bool kv0 = src_s[buf][r] >= 0, kv1 = src_s[buf][16 + r] >= 0;
+    // 2. prefetch the next chunk's raw bytes while this one is computed
+    if (kOneBatch && c0 + kKC < s_end) {
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        const int t = tid + u * nthr;
+        if (t < kChunkTasks) load_task(a, b, src_s[buf ^ 1][t / kSegs], t % kSegs, pre[u]);
+        else pre[u].meta = 0;
+      }
+    }
 
+    // 3. half of S = Q K^T (this wave's 288 channels) for two tiles of 16 keys,
+    //    then the partner's half through LDS
     v4f S2[2];
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
       v4f acc = {0.f, 0.f, 0.f, 0.f};
-      const uint16_t *kp = &Kl[(kt * 16 + r) * kKRow + 8 * g];
+      const uint16_t *kp = K + (kt * 16 + r) * kKRow + cbase + 8 * g;
 #pragma unroll
-      for (int kk = 0; kk < kD / 32; ++kk)
+      for (int kk = 0; kk < kHalfD / 32; ++kk)
         acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Qf[kk], *reinterpret_cast<const v8bf *>(kp + 32 * kk), acc, 0,
                                                       0, 0);
       S2[kt] = acc;
     }
-    const bool kv0 = src_s[r] >= 0, kv1 = src_s[16 + r] >= 0;
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) Sx[wave][(kt * 4 + i) * 64 + lane] = S2[kt][i];
+    __syncthreads();
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        // a fixed order of the two halves, so both waves of the pair agree bit for bit
+        const float mine = S2[kt][i], other = Sx[wave ^ 1][(kt * 4 + i) * 64 + lane];
+        S2[kt][i] = half == 0 ? mine + other : other + mine;
+      }
+
     float alpha[4], p0[4], p1[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -179,10 +284,12 @@ __global__ __launch_bounds__(HG * 64) void attn_kernel(AttnArgs a) {
       m2[i] = mn;
     }
 #pragma unroll
-    for (int j = 0; j < kNT; ++j) {
+    for (int j = 0; j < kHalfNT; ++j) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) O[j][i] *= alpha[i];
     }
+    // 4. P (bf16, or hi + lo) through this wave's LDS tile into the A layout
+    //    (LDS operations of one wave complete in order)
     uint16_t *pw = &Pl[wave][0][0];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -195,17 +302,27 @@ __global__ __launch_bounds__(HG * 64) void attn_kernel(AttnArgs a) {
         pl[(4 * g + i) * kPRow + 16 + r] = (uint16_t)f32_to_bf16(p1[i] - bf16_to_f32(hi1));
       }
     }
-    __syncthreads();
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     const v8bf Pa = *reinterpret_cast<const v8bf *>(&Pl[wave][0][r * kPRow + 8 * g]);
     v8bf Pb;
     if (kSplitP) Pb = *reinterpret_cast<const v8bf *>(&Pl[wave][kSplitP ? 1 : 0][r * kPRow + 8 * g]);
+    // 5. O += P V for this wave's channels; lane (g, r) needs V[keys 8g..8g+7]
+    //    [channel c + r]: two transposed 4x16 reads of the key-major tile.
+    typedef __attribute__((address_space(3))) v4s lds_v4s;
+    const uint16_t *vb = K + (8 * g + (r >> 2)) * kKRow + cbase + 4 * (r & 3);
 #pragma unroll
-    for (int j = 0; j < kNT; ++j) {
-      const v8bf Bv = *reinterpret_cast<const v8bf *>(&Vt[(16 * j + r) * kVRow + 8 * g]);
+    for (int j = 0; j < kHalfNT; ++j) {
+      const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s *)(vb + 16 * j));
+      const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s *)(vb + 4 * kKRow + 16 * j));
+      const v8s both = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+      const v8bf Bv = __builtin_bit_cast(v8bf, both);
       O[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Pa, Bv, O[j], 0, 0, 0);
       if (kSplitP) O[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Pb, Bv, O[j], 0, 0, 0);
     }
-    __syncthreads();
+    // The next iteration writes the other K buffer and Sx only after its own
+    // barrier; the K buffer read here is rewritten two iterations later.
   }
 
   if (a.nsplit == 1) {
@@ -213,17 +330,17 @@ __global__ __launch_bounds__(HG * 64) void attn_kernel(AttnArgs a) {
     for (int i = 0; i < 4; ++i) {
       const int hh = h0 + 4 * g + i;
       const float inv = lsum[i] > 0.f ? 1.f / lsum[i] : 0.f;
-      const int64_t ob = (qrow * a.H + hh) * kD;
+      const int64_t ob = (qrow * a.H + hh) * kD + cbase;
       if (a.out_bf16) {
         uint16_t *o = reinterpret_cast<uint16_t *>(a.out) + ob;
 #pragma unroll
-        for (int j = 0; j < kNT; ++j) o[16 * j + r] = (uint16_t)f32_to_bf16(O[j][i] * inv);
+        for (int j = 0; j < kHalfNT; ++j) o[16 * j + r] = (uint16_t)f32_to_bf16(O[j][i] * inv);
       } else {
         float *o = reinterpret_cast<float *>(a.out) + ob;
 #pragma unroll
-        for (int j = 0; j < kNT; ++j) o[16 * j + r] = O[j][i] * inv;
+        for (int j = 0; j < kHalfNT; ++j) o[16 * j + r] = O[j][i] * inv;
       }
-      if (a.lse && r == 0)
+      if (a.lse && r == 0 && half == 0)
         a.lse[qrow * a.H + hh] = lsum[i] > 0.f ? (m2[i] + log2f(lsum[i])) * 0.69314718055994531f : -INFINITY;
     }
   } else {
@@ -231,10 +348,10 @@ __global__ __launch_bounds__(HG * 64) void attn_kernel(AttnArgs a) {
     for (int i = 0; i < 4; ++i) {
       const int hh = h0 + 4 * g + i;
       const int64_t pr = (qrow * a.nsplit + split) * a.H + hh;
-      float *o = a.ws_o + pr * kD;
+      float *o = a.ws_o + pr * kD + cbase;
 #pragma unroll
-      for (int j = 0; j < kNT; ++j) o[16 * j + r] = O[j][i];
-      if (r == 0) {
+      for (int j = 0; j < kHalfNT; ++j) o[16 * j + r] = O[j][i];
+      if (r == 0 && half == 0) {
         a.ws_ml[pr * 2 + 0] = m2[i];
         a.ws_ml[pr * 2 + 1] = lsum[i];
       }
@@ -298,9 +415,9 @@ size_t attn_workspace_bytes(int B, int Q, int H, int n_slots_max) {
 template <int HG, bool kSplitP>
 static void launch_hg(const AttnArgs &a, bool dense, dim3 grid, hipStream_t stream) {
   if (dense)
-    attn_kernel<HG, kSplitP, true><<<grid, HG * 64, 0, stream>>>(a);
+    attn_kernel<HG, kSplitP, true><<<grid, HG * 128, 0, stream>>>(a);
   else
-    attn_kernel<HG, kSplitP, false><<<grid, HG * 64, 0, stream>>>(a);
+    attn_kernel<HG, kSplitP, false><<<grid, HG * 128, 0, stream>>>(a);
 }
 
 template <bool kSplitP>

@@ -10,8 +10,10 @@
 //      with 8-byte vector loads that are contiguous across tasks;
 //   2. the pooled fp32 rows sit in LDS and are encoded 2 channels per
 //      thread, 16 threads per 32-channel scale block (shuffle max);
-//   3. the projection runs on the fp32 pooled values in a fixed channel
-//      order (fmaf from channel 0 to 575), W_IK read once per workgroup.
+//   3. the projection runs on the fp32 pooled values: for each 32-channel
+//      key block, 8 slices of 72 channels are accumulated in channel order
+//      (fmaf) and then added in slice order; when there are few workgroups
+//      (decode appends) the key blocks are spread over gridDim.z.
 #include "csa_device.hpp"
 #include "csa_internal.hpp"
 
@@ -19,7 +21,6 @@ namespace csa {
 
 constexpr int kEPB = 16;
 constexpr int kCompThreads = 256;
-constexpr int kMaxIdx = 128;
 
 // Encodes the pair (v0, v1) of channels 2t, 2t+1 of a 32-channel block
 // spread over 16 consecutive lanes; returns the packed byte and the block's
@@ -38,7 +39,8 @@ __global__ __launch_bounds__(kCompThreads) void compress_kernel(
     uint8_t *__restrict__ nope, uint8_t *__restrict__ nscale, uint16_t *__restrict__ rope,
     uint8_t *__restrict__ ikey, uint8_t *__restrict__ iscale, int N_cap, int d_idx) {
   __shared__ float cs[kEPB][kD];
-  __shared__ float ks[kEPB][kMaxIdx];
+  __shared__ float ks[kEPB][32];
+  __shared__ float kpart[kCompThreads / 32][kEPB][32];
 
   const int b = blockIdx.y;
   const int j0 = blockIdx.x * kEPB;
@@ -96,53 +98,71 @@ __global__ __launch_bounds__(kCompThreads) void compress_kernel(
   }
   __syncthreads();
 
-  // 2. MXFP4 main entry (bytes 0..255) and bf16 rope channels
-  for (int e = 0; e < ne; ++e) {
+  // 2. MXFP4 main entry (bytes 0..255) and bf16 rope channels (workgroup z = 0)
+  for (int e = 0; e < (blockIdx.z == 0 ? ne : 0); ++e) {
     const int64_t row = (int64_t)b * N_cap + entry0 + j0 + e;
     uint32_t sb;
     const uint32_t byte = encode_pair(cs[e][2 * tid], cs[e][2 * tid + 1], sb);
     nope[row * kNopeBytes + tid] = (uint8_t)byte;
     if ((tid & 15) == 0) nscale[row * kNopeScales + (tid >> 4)] = (uint8_t)sb;
   }
-  for (int t = tid; t < ne * kDRope; t += kCompThreads) {
+  for (int t = tid; t < (blockIdx.z == 0 ? ne * kDRope : 0); t += kCompThreads) {
     const int e = t / kDRope, c = t % kDRope;
     const int64_t row = (int64_t)b * N_cap + entry0 + j0 + e;
     rope[row * kDRope + c] = (uint16_t)f32_to_bf16(cs[e][kDNope + c]);
   }
   if (w_ik == nullptr) return;
 
-  // 3. indexer key: kI[o] = sum_d c[d] * W[d][o], fp32, channel order 0..575
-  {
-    const int o = tid % d_idx;
-    const int groups = kCompThreads / d_idx;  // 2 (d_idx 128) or 4 (d_idx 64)
-    const int g = tid / d_idx;
-    float acc[kEPB / 2];
-    const int per = kEPB / groups;            // entries per thread: 8 or 4
+  // 3. indexer key, one 32-channel block (= one MX block) at a time:
+  //    kI[o] = sum_d c[d] * W[d][o].  Thread t owns output o = 32*kb + t%32 and
+  //    the channel slice [72p, 72p+72), p = t/32; the 8 partial sums are
+  //    added in slice order.  Workgroup z handles blocks z, z+gridDim.z, ...
+  const int nkb = d_idx / 32;
+  const int ol = tid & 31;
+  const int part = tid >> 5;
+  constexpr int kParts = kCompThreads / 32;
+  constexpr int kSlice = kD / kParts;
+  for (int kb = blockIdx.z; kb < nkb; kb += gridDim.z) {
+    const int o = kb * 32 + ol;
+    float acc[kEPB];
 #pragma unroll
-    for (int r = 0; r < kEPB / 2; ++r) acc[r] = 0.f;
-    for (int d = 0; d < kD; ++d) {
-      const float w = bf16_to_f32(w_ik[d * d_idx + o]);
+    for (int r = 0; r < kEPB; ++r) acc[r] = 0.f;
+    const uint16_t *wp = w_ik + (int64_t)(part * kSlice) * d_idx + o;
+    for (int d0 = 0; d0 < kSlice; d0 += 8) {
+      float w8[8];
 #pragma unroll
-      for (int r = 0; r < kEPB / 2; ++r)
-        if (r < per) acc[r] = fmaf(cs[g + r * groups][d], w, acc[r]);
+      for (int u = 0; u < 8; ++u) w8[u] = bf16_to_f32(wp[(int64_t)(d0 + u) * d_idx]);
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int d = part * kSlice + d0 + u;
+#pragma unroll
+        for (int r = 0; r < kEPB; ++r)
+          if (r < ne) acc[r] = fmaf(cs[r][d], w8[u], acc[r]);
+      }
     }
+    __syncthreads();  // ks is reused across blocks
 #pragma unroll
-    for (int r = 0; r < kEPB / 2; ++r)
-      if (r < per) ks[g + r * groups][o] = acc[r];
-  }
-  __syncthreads();
-  {
-    const int bytes = d_idx / 2;                 // 64 or 32 per entry
-    const int epp = kCompThreads / bytes;        // entries per pass: 4 or 8
-    for (int e = tid / bytes; e < ((ne + epp - 1) / epp) * epp; e += epp) {
-      const int t = tid % bytes;
-      const int ec = e < ne ? e : ne - 1;        // keep every lane in the shuffles
+    for (int r = 0; r < kEPB; ++r)
+      if (r < ne) kpart[part][r][ol] = acc[r];
+    __syncthreads();
+    for (int t = tid; t < ne * 32; t += kCompThreads) {
+      const int r = t >> 5;
+      float s = 0.f;
+#pragma unroll
+      for (int pp = 0; pp < kParts; ++pp) s += kpart[pp][r][ol];
+      ks[r][ol] = s;
+    }
+    __syncthreads();
+    // encode: 16 lanes per (entry, block), two channels each
+    {
+      const int e = tid >> 4, t = tid & 15;
+      const int ec = e < ne ? e : ne - 1;
       uint32_t sb;
       const uint32_t byte = encode_pair(ks[ec][2 * t], ks[ec][2 * t + 1], sb);
       if (e < ne) {
         const int64_t row = (int64_t)b * N_cap + entry0 + j0 + e;
-        ikey[row * bytes + t] = (uint8_t)byte;
-        if ((t & 15) == 0) iscale[row * (d_idx / 32) + (t >> 4)] = (uint8_t)sb;
+        ikey[row * (d_idx / 2) + kb * 16 + t] = (uint8_t)byte;
+        if (t == 0) iscale[row * nkb + kb] = (uint8_t)sb;
       }
     }
   }
@@ -152,7 +172,12 @@ hipError_t launch_compress(const uint16_t *x, int64_t x_stride_b, const uint16_t
                            int G, const float *bias, const uint16_t *w_ik, int64_t entry0, int n_chunk,
                            const CacheView &c, hipStream_t stream) {
   if (n_chunk <= 0 || c.B <= 0) return hipSuccess;
-  dim3 grid((n_chunk + kEPB - 1) / kEPB, c.B);
+  // Few workgroups (decode appends): spread the key blocks over workgroups,
+  // each recomputing the pooled rows it needs; many: one workgroup per group.
+  const int groups = (n_chunk + kEPB - 1) / kEPB;
+  const int nkb = w_ik ? c.d_idx / 32 : 1;
+  const int zsplit = (int64_t)groups * c.B < 1024 ? nkb : 1;
+  dim3 grid(groups, c.B, zsplit);
   if (G == kD)
     compress_kernel<true><<<grid, kCompThreads, 0, stream>>>(x, x_stride_b, z, z_stride_b, bias, w_ik, c.m, n_chunk,
                                                              entry0, c.nope, c.nscale, c.rope, c.ikey, c.iscale,

@@ -13,7 +13,8 @@
 //   * a last pass keeps every key > T plus the first (by entry index)
 //     elements equal to T, and writes them in ascending order through two
 //     block-wide prefix sums.
-// Rows longer than kTile are processed tile by tile in every pass.
+// Rows longer than kTile are processed tile by tile in every pass.  Rows of
+// at most 32,768 scores take the register-resident variant further below.
 #include "csa_device.hpp"
 #include "csa_internal.hpp"
 
@@ -53,7 +54,7 @@ __device__ __forceinline__ int block_excl_scan(int v, int *sh, int &total) {
   return res;
 }
 
-__global__ __launch_bounds__(kTopkThreads) void topk_kernel(const float *__restrict__ scores, int Ns,
+__global__ __launch_bounds__(kTopkThreads) void topk_tiled_kernel(const float *__restrict__ scores, int Ns,
                                                              const int32_t *__restrict__ n_entries, int N_cap, int m,
                                                              const int32_t *__restrict__ q_pos, int Q,
                                                              const int32_t *__restrict__ cand, int C, int k,
@@ -215,11 +216,200 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const float *__restr
   }
 }
 
+
+// Rows of at most kRegN scores: every thread keeps its kRegPer consecutive
+// keys in registers; digits of 11, 11 and 10 bits (the first, which every
+// element takes part in, spreads over four bins per octave of the score,
+// so same-bin atomics within a wave stay few); per-wave histograms in LDS.
+constexpr int kRegPer = 32;
+constexpr int kRegN = kTopkThreads * kRegPer;
+constexpr int kBins = 2048;
+
+// Finds the digit (of `nb` bins, nb = 2048 or 1024) holding the k_rem-th
+// largest remaining element; the counts are summed over `nh` per-wave
+// histograms.  Every thread returns the same (digit, elements above it).
+__device__ __forceinline__ void find_digit(const int (*hist)[kBins], int nh, int nb, int k_rem, int *sh, int &digit,
+                                           int &above_out) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int per = nb / kTopkThreads;  // 2 or 1 bins per thread, in descending digit order
+  int c[2] = {0, 0};
+  for (int j = 0; j < per; ++j) {
+    const int d = nb - 1 - (tid * per + j);
+    int s = 0;
+    for (int w = 0; w < nh; ++w) s += hist[w][d];
+    c[j] = s;
+  }
+  const int tot = c[0] + c[1];
+  int inc = tot;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int t = __shfl_up(inc, o);
+    if (lane >= o) inc += t;
+  }
+  if (lane == 63) sh[wave] = inc;
+  __syncthreads();
+  if (tid == 0) {
+    int run = 0;
+    for (int w = 0; w < kTopkWaves; ++w) {
+      const int t = sh[w];
+      sh[w] = run;
+      run += t;
+    }
+  }
+  __syncthreads();
+  int above = sh[wave] + inc - tot;
+  for (int j = 0; j < per; ++j) {
+    if (above < k_rem && k_rem <= above + c[j]) {
+      sh[kTopkWaves + 1] = nb - 1 - (tid * per + j);
+      sh[kTopkWaves + 2] = above;
+    }
+    above += c[j];
+  }
+  __syncthreads();
+  digit = sh[kTopkWaves + 1];
+  above_out = sh[kTopkWaves + 2];
+  __syncthreads();
+}
+
+__global__ __launch_bounds__(kTopkThreads) void topk_reg_kernel(const float *__restrict__ scores, int Ns,
+                                                                 const int32_t *__restrict__ n_entries, int N_cap,
+                                                                 int m, const int32_t *__restrict__ q_pos, int Q,
+                                                                 const int32_t *__restrict__ cand, int C, int k,
+                                                                 int32_t *__restrict__ idx_out,
+                                                                 float *__restrict__ score_out) {
+  __shared__ int hist[kTopkWaves][kBins];
+  __shared__ int sh[kTopkWaves + 4];
+
+  const int q = blockIdx.x, b = blockIdx.y;
+  const int tid = threadIdx.x, wave = tid >> 6;
+  const int64_t row = (int64_t)b * Q + q;
+  const float *src = scores + row * Ns;
+  int n;
+  if (cand) {
+    n = C;
+  } else {
+    const int nE = min(n_entries[b], N_cap);
+    n = max(0, min(nE, (q_pos[row] + 1) / m));
+  }
+
+  // keys of elements tid*kRegPer .. +kRegPer-1; 0 = not a candidate
+  uint32_t key[kRegPer];
+  const int i0 = tid * kRegPer;
+  if (i0 + kRegPer <= n && (Ns & 3) == 0) {
+#pragma unroll
+    for (int v = 0; v < kRegPer / 4; ++v) {
+      const float4 f = *reinterpret_cast<const float4 *>(src + i0 + 4 * v);
+      const float ff[4] = {f.x, f.y, f.z, f.w};
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const uint32_t bits = __float_as_uint(ff[u]);
+        key[4 * v + u] = bits == kNoScoreBits ? 0u : score_key(ff[u]);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < kRegPer; ++j) {
+      uint32_t kk = 0;
+      if (i0 + j < n) {
+        const uint32_t bits = __float_as_uint(src[i0 + j]);
+        kk = bits == kNoScoreBits ? 0u : score_key(__uint_as_float(bits));
+      }
+      key[j] = kk;
+    }
+  }
+
+  int n_valid = n;
+  if (cand) {
+    int cnt = 0;
+#pragma unroll
+    for (int j = 0; j < kRegPer; ++j) cnt += key[j] != 0u;
+    int tot;
+    block_excl_scan(cnt, sh, tot);
+    n_valid = tot;
+  }
+  const int k_eff = min(k, n_valid);
+
+  uint32_t thr = 0;   // full key of the k_eff-th largest element
+  int need = 0;       // elements equal to thr that are taken
+  if (k_eff > 0 && k_eff < n_valid) {
+    // pass 1: bits 31..21, per-wave histograms
+    for (int i = tid; i < kTopkWaves * kBins; i += kTopkThreads) (&hist[0][0])[i] = 0;
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < kRegPer; ++j) atomicAdd(&hist[wave][key[j] >> 21], 1);
+    __syncthreads();
+    int d1, above;
+    find_digit(hist, kTopkWaves, kBins, k_eff, sh, d1, above);
+    int k_rem = k_eff - above;
+    // pass 2: bits 20..10 of the elements in bin d1
+    for (int i = tid; i < kBins; i += kTopkThreads) hist[0][i] = 0;
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < kRegPer; ++j)
+      if ((key[j] >> 21) == (uint32_t)d1) atomicAdd(&hist[0][(key[j] >> 10) & 0x7FFu], 1);
+    __syncthreads();
+    int d2;
+    find_digit(hist, 1, kBins, k_rem, sh, d2, above);
+    k_rem -= above;
+    const uint32_t p12 = ((uint32_t)d1 << 11) | (uint32_t)d2;
+    // pass 3: bits 9..0
+    for (int i = tid; i < kBins; i += kTopkThreads) hist[0][i] = 0;
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < kRegPer; ++j)
+      if ((key[j] >> 10) == p12) atomicAdd(&hist[0][key[j] & 0x3FFu], 1);
+    __syncthreads();
+    int d3;
+    find_digit(hist, 1, 1024, k_rem, sh, d3, above);
+    k_rem -= above;
+    thr = (p12 << 10) | (uint32_t)d3;
+    need = k_rem;
+  }
+
+  int32_t *out_i = idx_out + row * k;
+  float *out_s = score_out ? score_out + row * k : nullptr;
+  if (k_eff > 0) {
+    int gt = 0, eq = 0;
+#pragma unroll
+    for (int j = 0; j < kRegPer; ++j) {
+      gt += key[j] > thr;
+      eq += need > 0 && key[j] == thr;
+    }
+    int eq_tot;
+    const int eq_before = block_excl_scan(eq, sh, eq_tot);
+    const int take_eq = max(0, min(eq, need - eq_before));
+    int sel_tot;
+    int off = block_excl_scan(gt + take_eq, sh, sel_tot);
+    int eq_seen = 0;
+#pragma unroll
+    for (int j = 0; j < kRegPer; ++j) {
+      bool take = key[j] > thr;
+      if (!take && need > 0 && key[j] == thr) {
+        take = eq_seen < take_eq;
+        ++eq_seen;
+      }
+      if (take && off < k_eff) {
+        out_i[off] = cand ? cand[row * C + i0 + j] : i0 + j;
+        if (out_s) out_s[off] = key_score(key[j]);
+        ++off;
+      }
+    }
+  }
+  for (int j = k_eff + tid; j < k; j += kTopkThreads) {
+    out_i[j] = -1;
+    if (out_s) out_s[j] = __uint_as_float(0x7FC00000u);
+  }
+}
+
 hipError_t launch_topk(const CacheView &c, const float *scores, int Ns, const int32_t *q_pos, int Q,
                        const int32_t *cand, int C, int k, int32_t *idx_out, float *score_out, hipStream_t stream) {
   dim3 grid(Q, c.B);
-  topk_kernel<<<grid, kTopkThreads, 0, stream>>>(scores, Ns, c.n_entries, c.N_cap, c.m, q_pos, Q, cand, C, k, idx_out,
-                                                 score_out);
+  if (Ns <= kRegN)
+    topk_reg_kernel<<<grid, kTopkThreads, 0, stream>>>(scores, Ns, c.n_entries, c.N_cap, c.m, q_pos, Q, cand, C, k,
+                                                       idx_out, score_out);
+  else
+    topk_tiled_kernel<<<grid, kTopkThreads, 0, stream>>>(scores, Ns, c.n_entries, c.N_cap, c.m, q_pos, Q, cand, C, k,
+                                                         idx_out, score_out);
   return hipGetLastError();
 }
 

@@ -112,6 +112,35 @@ def index_topk(cache: Cache, q_idx, w_idx, q_pos, k, cand=None, want_scores=Fals
     return idx, sc
 
 
+def index_scores(cache: Cache, q_idx, w_idx, q_pos, cand=None, scores=None):
+    """Indexer stage alone: fp32 scores [B][Q][Ns] (Ns = N_cap, or C with candidates)."""
+    _need(q_idx, torch.uint8, "q_idx")
+    _need(w_idx, torch.float32, "w_idx")
+    _need(q_pos, torch.int32, "q_pos")
+    B, Q, H_I = q_idx.shape[0], q_idx.shape[1], q_idx.shape[2]
+    C = cand.shape[2] if cand is not None else 0
+    Ns = C if cand is not None else cache.N_cap
+    if scores is None:
+        scores = torch.empty(B, Q, Ns, dtype=torch.float32, device=q_idx.device)
+    cs = cache.struct()
+    check(lib().csa_index_scores(ctypes.byref(cs), _ptr(q_idx), _ptr(w_idx), H_I, _ptr(q_pos), Q, _ptr(cand), C,
+                                 _ptr(scores), scores.numel() * 4, _stream()), "csa_index_scores")
+    return scores
+
+
+def topk(cache: Cache, scores, q_pos, k, cand=None, want_scores=False, out=None):
+    """Top-k stage alone, from the scores of index_scores()."""
+    B, Q = q_pos.shape
+    C = cand.shape[2] if cand is not None else 0
+    dev = q_pos.device
+    idx = out if out is not None else torch.empty(B, Q, k, dtype=torch.int32, device=dev)
+    sc = torch.empty(B, Q, k, dtype=torch.float32, device=dev) if want_scores else None
+    cs = cache.struct()
+    check(lib().csa_topk(ctypes.byref(cs), _ptr(scores), _ptr(q_pos), Q, _ptr(cand), C, int(k), _ptr(idx), _ptr(sc),
+                         _stream()), "csa_topk")
+    return idx, sc
+
+
 def _attn_out(B, Q, H, out_dtype, dev, out):
     if out is not None:
         return out

@@ -119,6 +119,18 @@ int csa_index_topk(const csa_cache_t *cache, const uint8_t *q_idx, const float *
                    const int32_t *q_pos, int Q, const int32_t *cand, int C, int k, int32_t *idx_out,
                    float *score_out, void *ws, size_t ws_bytes, hipStream_t stream);
 
+/* The two stages of csa_index_topk as separate calls (same semantics):
+ * csa_index_scores writes the score of every scanned entry into
+ * scores fp32 [B][Q][Ns] (Ns = N_cap for a full scan, C with `cand`;
+ * entries not visible at q_pos are left unwritten in a full scan, empty
+ * candidate slots get the bit pattern 0xFFFFFFFF); csa_topk selects from
+ * such a score array.  scores_bytes >= B*Q*Ns*4. */
+int csa_index_scores(const csa_cache_t *cache, const uint8_t *q_idx, const float *w_idx, int H_I,
+                     const int32_t *q_pos, int Q, const int32_t *cand, int C, float *scores, size_t scores_bytes,
+                     hipStream_t stream);
+int csa_topk(const csa_cache_t *cache, const float *scores, const int32_t *q_pos, int Q, const int32_t *cand,
+             int C, int k, int32_t *idx_out, float *score_out, hipStream_t stream);
+
 /* Sparse attention over selected entries plus the sliding window ([V4]
  * Fig. 3).  One softmax over the union of the entries listed in idx and the
  * window rows; key = value = the decoded 576-channel row; no rotation is

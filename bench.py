@@ -144,6 +144,8 @@ def main():
     L = args.layers
     layers, bias, wik = build_layers(w, L, dev)
     scores_ws = torch.empty(w.B, 1, w.N, dtype=torch.float32, device=dev)
+    topk_ws_bytes = csa.workspace_bytes(csa.WS_TOPK, w.B, 1, w.k, w.N)
+    topk_ws = torch.empty(max(topk_ws_bytes, 16), dtype=torch.uint8, device=dev)
     attn_ws_bytes = csa.workspace_bytes(csa.WS_SPARSE_ATTN, w.B, 1, w.H, w.k, w.n_win)
     attn_ws = torch.empty(max(attn_ws_bytes, 16), dtype=torch.uint8, device=dev)
 
@@ -154,7 +156,7 @@ def main():
         csa.index_scores(ly.cache, ly.qI, ly.w, ly.q_pos, scores=scores_ws)
 
     def st_topk(ly):
-        csa.topk(ly.cache, scores_ws, ly.q_pos, w.k, out=ly.idx)
+        csa.topk(ly.cache, scores_ws, ly.q_pos, w.k, out=ly.idx, ws=topk_ws if topk_ws_bytes else None)
 
     def st_attn(ly):
         csa.sparse_attn(ly.cache, ly.q, ly.q_pos, ly.idx, ly.swa, ly.swa_pos0, w.n_win, w.softmax_scale,

@@ -20,4 +20,5 @@ from .ops import (  # noqa: F401
     WS_DENSE_ATTN,
     WS_INDEX_TOPK,
     WS_SPARSE_ATTN,
+    WS_TOPK,
 )

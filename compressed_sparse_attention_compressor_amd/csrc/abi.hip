@@ -59,6 +59,14 @@ size_t index_ws_bytes(int B, int Q, int N_cap, int C) {
   return (size_t)B * Q * Ns * sizeof(float);
 }
 
+size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
+
+// Top-k workspace; candidate rows are selected in one launch.
+size_t topk_ws_bytes(int B, int Q, int Ns, int k, bool cand) {
+  if (cand) return 0;
+  return csa::topk_plan(B, Q, Ns, k).ws_bytes;
+}
+
 int check_attn_common(const csa_cache_t *cache, const uint16_t *q, int H, const int32_t *q_pos, int Q,
                       const uint16_t *swa, const int32_t *swa_pos0, int S, int n_win, float scale, int out_dtype,
                       void *out) {
@@ -96,12 +104,14 @@ const char *csa_status_str(int status) {
   }
 }
 
-size_t csa_workspace_bytes(int op, int B, int Q, int H, int n_or_k, int C) {
+size_t csa_workspace_bytes(int op, int B, int Q, int H_or_k, int n, int C) {
   if (B <= 0 || Q <= 0) return 0;
   switch (op) {
-    case CSA_WS_INDEX_TOPK: return index_ws_bytes(B, Q, n_or_k, C);
+    case CSA_WS_INDEX_TOPK:
+      return align256(index_ws_bytes(B, Q, n, C)) + topk_ws_bytes(B, Q, C > 0 ? C : n, H_or_k, C > 0);
+    case CSA_WS_TOPK: return topk_ws_bytes(B, Q, n, H_or_k, false);
     case CSA_WS_SPARSE_ATTN:
-    case CSA_WS_DENSE_ATTN: return csa::attn_workspace_bytes(B, Q, H, n_or_k + (C > 0 ? C : 0));
+    case CSA_WS_DENSE_ATTN: return csa::attn_workspace_bytes(B, Q, H_or_k, n + (C > 0 ? C : 0));
     default: return 0;
   }
 }
@@ -162,13 +172,18 @@ int csa_index_scores(const csa_cache_t *cache, const uint8_t *q_idx, const float
 }
 
 int csa_topk(const csa_cache_t *cache, const float *scores, const int32_t *q_pos, int Q, const int32_t *cand, int C,
-             int k, int32_t *idx_out, float *score_out, hipStream_t stream) {
+             int k, int32_t *idx_out, float *score_out, void *ws, size_t ws_bytes, hipStream_t stream) {
   int st = check_topk_args(cache, q_pos, Q, cand, C, k, idx_out);
   if (st) return st;
   if (Q == 0 || cache->B == 0 || k == 0) return CSA_OK;
   const int Ns = cand ? C : cache->N_cap;
   if (Ns > 0 && !scores) return CSA_ERR_NULL;
-  return status_of(csa::launch_topk(view_of(cache), scores, Ns, q_pos, Q, cand, C, k, idx_out, score_out, stream));
+  const size_t need = topk_ws_bytes(cache->B, Q, Ns, k, cand != nullptr);
+  if (need > 0 && !ws) return CSA_ERR_NULL;
+  if (ws_bytes < need) return CSA_ERR_WORKSPACE;
+  if (need > 0 && !aligned16(ws)) return CSA_ERR_ALIGN;
+  return status_of(
+      csa::launch_topk(view_of(cache), scores, Ns, q_pos, Q, cand, C, k, idx_out, score_out, ws, stream));
 }
 
 int csa_index_topk(const csa_cache_t *cache, const uint8_t *q_idx, const float *w_idx, int H_I,
@@ -179,14 +194,17 @@ int csa_index_topk(const csa_cache_t *cache, const uint8_t *q_idx, const float *
   st = check_topk_args(cache, q_pos, Q, cand, C, k, idx_out);
   if (st) return st;
   if (Q == 0 || cache->B == 0 || k == 0) return CSA_OK;
-  const size_t need = index_ws_bytes(cache->B, Q, cache->N_cap, cand ? C : 0);
+  const size_t sbytes = index_ws_bytes(cache->B, Q, cache->N_cap, cand ? C : 0);
+  const size_t tbytes = topk_ws_bytes(cache->B, Q, cand ? C : cache->N_cap, k, cand != nullptr);
+  const size_t need = align256(sbytes) + tbytes;
   if (need > 0 && !ws) return CSA_ERR_NULL;
   if (ws_bytes < need) return CSA_ERR_WORKSPACE;
   if (!aligned16(ws)) return CSA_ERR_ALIGN;
   float *scores = reinterpret_cast<float *>(ws);
-  st = csa_index_scores(cache, q_idx, w_idx, H_I, q_pos, Q, cand, C, scores, ws_bytes, stream);
+  st = csa_index_scores(cache, q_idx, w_idx, H_I, q_pos, Q, cand, C, scores, sbytes, stream);
   if (st) return st;
-  return csa_topk(cache, scores, q_pos, Q, cand, C, k, idx_out, score_out, stream);
+  void *tws = tbytes ? reinterpret_cast<char *>(ws) + align256(sbytes) : nullptr;
+  return csa_topk(cache, scores, q_pos, Q, cand, C, k, idx_out, score_out, tws, tbytes, stream);
 }
 
 int csa_sparse_attn(const csa_cache_t *cache, const uint16_t *q, int H, const int32_t *q_pos, int Q,

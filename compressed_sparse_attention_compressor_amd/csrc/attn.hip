@@ -69,30 +69,30 @@ struct RawTask {
 constexpr int kSegs = kD / 16;          // 36 tasks of 16 channels per key
 constexpr int kChunkTasks = kKC * kSegs;
 
-__device__ __forceinline__ void load_task(const AttnArgs &a, int b, int src, int seg, RawTask &t) {
-  t.meta = 0;
-  if (src < 0) return;
+// Branch-free: three unconditional loads from clamped addresses (codes,
+// scale byte, 32 bf16 bytes) with a known-valid stand-in address for the
+// parts a task does not use; loads inside per-lane branches would make the
+// compiler wait for each one before issuing the next.
+__device__ __forceinline__ void load_task(const AttnArgs &a, int b, int src, int seg, const uint8_t *dummy,
+                                          RawTask &t) {
   const int ch = seg * 16;
-  if (src & 0x40000000) {
-    const int64_t rr = src & 0x3FFFFFFF;
-    const uint4 *p = reinterpret_cast<const uint4 *>(a.swa + ((int64_t)b * a.S + rr) * kD + ch);
-    t.a = p[0];
-    t.b = p[1];
-    t.meta = 2;
-  } else {
-    const int64_t row = (int64_t)b * a.N_cap + src;
-    if (ch < kDNope) {
-      const uint2 c = *reinterpret_cast<const uint2 *>(a.nope + row * kNopeBytes + ch / 2);
-      t.a.x = c.x;
-      t.a.y = c.y;
-      t.meta = 1u | ((uint32_t)a.nscale[row * kNopeScales + ch / 32] << 8);
-    } else {
-      const uint4 *p = reinterpret_cast<const uint4 *>(a.rope + row * kDRope + (ch - kDNope));
-      t.a = p[0];
-      t.b = p[1];
-      t.meta = 2;
-    }
-  }
+  const bool none = src < 0;
+  const bool win = !none && (src & 0x40000000);
+  const bool ent = !none && !win;
+  const bool fp4 = ent && ch < kDNope;
+  const int64_t row = (int64_t)b * a.N_cap + (ent ? src : 0);
+  const uint8_t *pc = fp4 ? a.nope + row * kNopeBytes + ch / 2 : dummy;
+  const uint8_t *ps = fp4 ? a.nscale + row * kNopeScales + ch / 32 : dummy;
+  const uint8_t *pb = dummy;
+  if (win) pb = reinterpret_cast<const uint8_t *>(a.swa + ((int64_t)b * a.S + (src & 0x3FFFFFFF)) * kD + ch);
+  if (ent && !fp4) pb = reinterpret_cast<const uint8_t *>(a.rope + row * kDRope + (ch - kDNope));
+  const uint2 c = *reinterpret_cast<const uint2 *>(pc);
+  const uint32_t sc = *ps;
+  const uint4 lo = reinterpret_cast<const uint4 *>(pb)[0];
+  const uint4 hi = reinterpret_cast<const uint4 *>(pb)[1];
+  t.a = fp4 ? uint4{c.x, c.y, 0u, 0u} : lo;
+  t.b = hi;
+  t.meta = none ? 0u : (fp4 ? (1u | (sc << 8)) : 2u);
 }
 
 // Writes the 16 decoded bf16 channels of a task (zeros for an empty slot).
@@ -166,6 +166,8 @@ __global__ __launch_bounds__(HG * 128) void attn_kernel(AttnArgs a) {
     }
   };
 
+  // a known-valid address for loads a task does not need: this query's row
+  const uint8_t *dummy = reinterpret_cast<const uint8_t *>(a.q + qrow * a.H * kD);
   const int h0 = hg * 16;
   v8bf Qf[kHalfD / 32];
   {
@@ -192,7 +194,7 @@ __global__ __launch_bounds__(HG * 128) void attn_kernel(AttnArgs a) {
 #pragma unroll
       for (int u = 0; u < kBatch; ++u) {
         const int t = tid + u * nthr;
-        if (t < kChunkTasks) load_task(a, b, src_s[0][t / kSegs], t % kSegs, pre[u]);
+        if (t < kChunkTasks) load_task(a, b, src_s[0][t / kSegs], t % kSegs, dummy, pre[u]);
         else pre[u].meta = 0;
       }
     }
@@ -214,7 +216,7 @@ __global__ __launch_bounds__(HG * 128) void attn_kernel(AttnArgs a) {
 #pragma unroll
         for (int u = 0; u < kBatch; ++u) {
           const int t = t0 + tid + u * nthr;
-          if (t < kChunkTasks) load_task(a, b, src_s[buf][t / kSegs], t % kSegs, tk[u]);
+          if (t < kChunkTasks) load_task(a, b, src_s[buf][t / kSegs], t % kSegs, dummy, tk[u]);
         }
 #pragma unroll
         for (int u = 0; u < kBatch; ++u) {
@@ -233,7 +235,7 @@ __global__ __launch_bounds__(HG * 128) void attn_kernel(AttnArgs a) {
 #pragma unroll
       for (int u = 0; u < kBatch; ++u) {
         const int t = tid + u * nthr;
-        if (t < kChunkTasks) load_task(a, b, src_s[buf ^ 1][t / kSegs], t % kSegs, pre[u]);
+        if (t < kChunkTasks) load_task(a, b, src_s[buf ^ 1][t / kSegs], t % kSegs, dummy, pre[u]);
         else pre[u].meta = 0;
       }
     }

@@ -21,6 +21,7 @@ namespace csa {
 
 constexpr int kEPB = 16;
 constexpr int kCompThreads = 256;
+constexpr int kSmallM = 8;   // blocks up to this many rows are pooled from registers
 
 // Encodes the pair (v0, v1) of channels 2t, 2t+1 of a 32-channel block
 // spread over 16 consecutive lanes; returns the packed byte and the block's
@@ -49,48 +50,106 @@ __global__ __launch_bounds__(kCompThreads) void compress_kernel(
   const uint16_t *xb = x + (int64_t)b * x_stride_b;
   const uint16_t *zb = z + (int64_t)b * z_stride_b;
 
+  // The W_IK slice of this thread's first key block is loaded before the
+  // pooling, so its latency overlaps the raw-row loads.
+  constexpr int kParts = kCompThreads / 32;
+  constexpr int kSlice = kD / kParts;
+  const int ol = tid & 31;
+  const int part = tid >> 5;
+  const int nkb = w_ik ? d_idx / 32 : 0;
+  uint16_t wr[kSlice];
+  if ((int)blockIdx.z < nkb) {
+    const uint16_t *wp = w_ik + (int64_t)(part * kSlice) * d_idx + blockIdx.z * 32 + ol;
+#pragma unroll
+    for (int u = 0; u < kSlice; ++u) wr[u] = wp[(int64_t)u * d_idx];
+  }
+
   // 1. pooling
   for (int t = tid; t < ne * (kD / 4); t += kCompThreads) {
     const int e = t / (kD / 4);
     const int c = (t % (kD / 4)) * 4;
     const int64_t row0 = (int64_t)(j0 + e) * m;
     float mx[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
-    for (int i = 0; i < m; ++i) {
-      const float bi = bias[i];
-      if (kGateFull) {
-        uint2 g = *reinterpret_cast<const uint2 *>(zb + (row0 + i) * kD + c);
-        mx[0] = fmaxf(mx[0], bf16_to_f32(g.x & 0xFFFFu) + bi);
-        mx[1] = fmaxf(mx[1], bf16_to_f32(g.x >> 16) + bi);
-        mx[2] = fmaxf(mx[2], bf16_to_f32(g.y & 0xFFFFu) + bi);
-        mx[3] = fmaxf(mx[3], bf16_to_f32(g.y >> 16) + bi);
-      } else {
-        const float a = bf16_to_f32(zb[row0 + i]) + bi;
-        mx[0] = fmaxf(mx[0], a);
-      }
-    }
-    if (!kGateFull) mx[1] = mx[2] = mx[3] = mx[0];
     float den[4] = {0.f, 0.f, 0.f, 0.f};
     float num[4] = {0.f, 0.f, 0.f, 0.f};
-    for (int i = 0; i < m; ++i) {
-      const float bi = bias[i];
-      float a[4];
-      if (kGateFull) {
-        uint2 g = *reinterpret_cast<const uint2 *>(zb + (row0 + i) * kD + c);
-        a[0] = bf16_to_f32(g.x & 0xFFFFu) + bi;
-        a[1] = bf16_to_f32(g.x >> 16) + bi;
-        a[2] = bf16_to_f32(g.y & 0xFFFFu) + bi;
-        a[3] = bf16_to_f32(g.y >> 16) + bi;
-      } else {
-        a[0] = a[1] = a[2] = a[3] = bf16_to_f32(zb[row0 + i]) + bi;
-      }
-      uint2 v = *reinterpret_cast<const uint2 *>(xb + (row0 + i) * kD + c);
-      const float xv[4] = {bf16_to_f32(v.x & 0xFFFFu), bf16_to_f32(v.x >> 16), bf16_to_f32(v.y & 0xFFFFu),
-                           bf16_to_f32(v.y >> 16)};
+    if (m <= kSmallM) {
+      // short blocks: every row of the block is loaded once, up front
+      // unconditional loads (row index clamped to the block): loads inside
+      // per-lane branches would be issued one after another
+      uint2 gz[kSmallM], gx[kSmallM];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const float w = expf(a[u] - mx[u]);
-        den[u] += w;
-        num[u] = fmaf(w, xv[u], num[u]);
+      for (int i = 0; i < kSmallM; ++i) {
+        const int64_t rr = row0 + min(i, m - 1);
+        gx[i] = *reinterpret_cast<const uint2 *>(xb + rr * kD + c);
+        if (kGateFull) {
+          gz[i] = *reinterpret_cast<const uint2 *>(zb + rr * kD + c);
+        } else {
+          const uint32_t h = zb[rr];
+          gz[i] = uint2{h | (h << 16), h | (h << 16)};
+        }
+      }
+      float a[kSmallM][4];
+#pragma unroll
+      for (int i = 0; i < kSmallM; ++i) {
+        if (i < m) {
+          const float bi = bias[i];
+          a[i][0] = bf16_to_f32(gz[i].x & 0xFFFFu) + bi;
+          a[i][1] = bf16_to_f32(gz[i].x >> 16) + bi;
+          a[i][2] = bf16_to_f32(gz[i].y & 0xFFFFu) + bi;
+          a[i][3] = bf16_to_f32(gz[i].y >> 16) + bi;
+#pragma unroll
+          for (int u = 0; u < 4; ++u) mx[u] = fmaxf(mx[u], a[i][u]);
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < kSmallM; ++i) {
+        if (i < m) {
+          const float xv[4] = {bf16_to_f32(gx[i].x & 0xFFFFu), bf16_to_f32(gx[i].x >> 16),
+                               bf16_to_f32(gx[i].y & 0xFFFFu), bf16_to_f32(gx[i].y >> 16)};
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const float w = expf(a[i][u] - mx[u]);
+            den[u] += w;
+            num[u] = fmaf(w, xv[u], num[u]);
+          }
+        }
+      }
+    } else {
+      for (int i = 0; i < m; ++i) {
+        const float bi = bias[i];
+        if (kGateFull) {
+          uint2 gg = *reinterpret_cast<const uint2 *>(zb + (row0 + i) * kD + c);
+          mx[0] = fmaxf(mx[0], bf16_to_f32(gg.x & 0xFFFFu) + bi);
+          mx[1] = fmaxf(mx[1], bf16_to_f32(gg.x >> 16) + bi);
+          mx[2] = fmaxf(mx[2], bf16_to_f32(gg.y & 0xFFFFu) + bi);
+          mx[3] = fmaxf(mx[3], bf16_to_f32(gg.y >> 16) + bi);
+        } else {
+          const float av = bf16_to_f32(zb[row0 + i]) + bi;
+          mx[0] = fmaxf(mx[0], av);
+        }
+      }
+      if (!kGateFull) mx[1] = mx[2] = mx[3] = mx[0];
+      for (int i = 0; i < m; ++i) {
+        const float bi = bias[i];
+        float a[4];
+        if (kGateFull) {
+          uint2 gg = *reinterpret_cast<const uint2 *>(zb + (row0 + i) * kD + c);
+          a[0] = bf16_to_f32(gg.x & 0xFFFFu) + bi;
+          a[1] = bf16_to_f32(gg.x >> 16) + bi;
+          a[2] = bf16_to_f32(gg.y & 0xFFFFu) + bi;
+          a[3] = bf16_to_f32(gg.y >> 16) + bi;
+        } else {
+          a[0] = a[1] = a[2] = a[3] = bf16_to_f32(zb[row0 + i]) + bi;
+        }
+        uint2 v = *reinterpret_cast<const uint2 *>(xb + (row0 + i) * kD + c);
+        const float xv[4] = {bf16_to_f32(v.x & 0xFFFFu), bf16_to_f32(v.x >> 16), bf16_to_f32(v.y & 0xFFFFu),
+                             bf16_to_f32(v.y >> 16)};
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const float w = expf(a[u] - mx[u]);
+          den[u] += w;
+          num[u] = fmaf(w, xv[u], num[u]);
+        }
       }
     }
 #pragma unroll
@@ -117,33 +176,36 @@ __global__ __launch_bounds__(kCompThreads) void compress_kernel(
   //    kI[o] = sum_d c[d] * W[d][o].  Thread t owns output o = 32*kb + t%32 and
   //    the channel slice [72p, 72p+72), p = t/32; the 8 partial sums are
   //    added in slice order.  Workgroup z handles blocks z, z+gridDim.z, ...
-  const int nkb = d_idx / 32;
-  const int ol = tid & 31;
-  const int part = tid >> 5;
-  constexpr int kParts = kCompThreads / 32;
-  constexpr int kSlice = kD / kParts;
   for (int kb = blockIdx.z; kb < nkb; kb += gridDim.z) {
     const int o = kb * 32 + ol;
+    if (kb != (int)blockIdx.z) {
+      // later blocks (many entries per workgroup): the whole slice at once
+      const uint16_t *wp = w_ik + (int64_t)(part * kSlice) * d_idx + o;
+#pragma unroll
+      for (int u = 0; u < kSlice; ++u) wr[u] = wp[(int64_t)u * d_idx];
+    }
+    float wf[kSlice];
+#pragma unroll
+    for (int u = 0; u < kSlice; ++u) wf[u] = bf16_to_f32(wr[u]);
+    // one entry at a time (a runtime loop: decode appends have ne = 1); the
+    // pooled values of the slice are read as 16-byte LDS vectors (the 32
+    // lanes of a slice read the same address)
     float acc[kEPB];
+    for (int r = 0; r < ne; ++r) {
+      const float4 *cp = reinterpret_cast<const float4 *>(&cs[r][part * kSlice]);
+      float a = 0.f;
 #pragma unroll
-    for (int r = 0; r < kEPB; ++r) acc[r] = 0.f;
-    const uint16_t *wp = w_ik + (int64_t)(part * kSlice) * d_idx + o;
-    for (int d0 = 0; d0 < kSlice; d0 += 8) {
-      float w8[8];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) w8[u] = bf16_to_f32(wp[(int64_t)(d0 + u) * d_idx]);
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int d = part * kSlice + d0 + u;
-#pragma unroll
-        for (int r = 0; r < kEPB; ++r)
-          if (r < ne) acc[r] = fmaf(cs[r][d], w8[u], acc[r]);
+      for (int u4 = 0; u4 < kSlice / 4; ++u4) {
+        const float4 c4 = cp[u4];
+        a = fmaf(c4.x, wf[4 * u4 + 0], a);
+        a = fmaf(c4.y, wf[4 * u4 + 1], a);
+        a = fmaf(c4.z, wf[4 * u4 + 2], a);
+        a = fmaf(c4.w, wf[4 * u4 + 3], a);
       }
+      acc[r] = a;
     }
     __syncthreads();  // ks is reused across blocks
-#pragma unroll
-    for (int r = 0; r < kEPB; ++r)
-      if (r < ne) kpart[part][r][ol] = acc[r];
+    for (int r = 0; r < ne; ++r) kpart[part][r][ol] = acc[r];
     __syncthreads();
     for (int t = tid; t < ne * 32; t += kCompThreads) {
       const int r = t >> 5;

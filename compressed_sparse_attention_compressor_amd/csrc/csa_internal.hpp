@@ -28,8 +28,18 @@ hipError_t launch_index_scores(const CacheView &c, const uint8_t *q_idx, const f
                                const int32_t *q_pos, int Q, const int32_t *cand, int C, float *scores,
                                hipStream_t stream);
 
+// Top-k plan: rows with few siblings are split into `nsl` slices of S
+// scores whose own top-k candidates (ws_bytes of workspace) are reduced in
+// a second launch.  nsl = 1: one workgroup per row.
+struct TopkPlan {
+  int nsl;
+  int S;
+  size_t ws_bytes;
+};
+TopkPlan topk_plan(int B, int Q, int Ns, int k);
+
 hipError_t launch_topk(const CacheView &c, const float *scores, int Ns, const int32_t *q_pos, int Q,
-                       const int32_t *cand, int C, int k, int32_t *idx_out, float *score_out,
+                       const int32_t *cand, int C, int k, int32_t *idx_out, float *score_out, void *ws,
                        hipStream_t stream);
 
 struct AttnShape {

@@ -33,6 +33,10 @@ __global__ __launch_bounds__(kIdxThreads) void index_scores_kernel(
     int N_cap, int d_idx, int m, const uint8_t *__restrict__ q_idx, const float *__restrict__ w_idx, int H_I,
     const int32_t *__restrict__ q_pos, int Q, const int32_t *__restrict__ cand, int C, float *__restrict__ scores,
     int Ns) {
+  // Indexer queries of this workgroup (QB queries x 16*HT heads x d_idx bytes),
+  // staged once so that the waves read their MFMA fragments from LDS.
+  __shared__ __attribute__((aligned(16))) uint8_t qs[QB * HT * 16 * 128];
+  __shared__ __attribute__((aligned(16))) float sc[kIdxThreads / 64][QB][kIdxWaveEntries];
   const int b = blockIdx.z;
   const int q0 = blockIdx.y * QB;
   const int lane = threadIdx.x & 63;
@@ -40,94 +44,154 @@ __global__ __launch_bounds__(kIdxThreads) void index_scores_kernel(
   const int g = lane >> 4;   // 32-channel block (K group)
   const int r = lane & 15;   // entry within the tile / head row within the head tile
   const int kb = d_idx / 32; // key blocks per entry (2 or 4)
-  const int nE = min(n_entries[b], N_cap);
+  const int base = blockIdx.x * kIdxWGEntries + wave * kIdxWaveEntries;
+  constexpr int kIters = kIdxWaveEntries / 16;
 
-  v8i A[QB][HT];
-  float wv[QB][HT][4];
-  int vis[QB];
-  int vis_max = 0;
+  // 1. Small, cache-resident loads first (queries for LDS staging, head
+  //    weights, visibility): vector-memory counters retire in order, so
+  //    what is issued before the key stream can be waited for alone.
+  constexpr int kQBytes = HT * 16 * 128;
+  constexpr int kQVec = (QB * kQBytes / 16 + kIdxThreads - 1) / kIdxThreads;
+  uint4 qv_stage[kQVec];
+#pragma unroll
+  for (int u = 0; u < kQVec; ++u) {
+    const int i = threadIdx.x + u * kIdxThreads;
+    const int qb = i / (kQBytes / 16), rem = (i % (kQBytes / 16)) * 16;
+    const int h = rem / 128, c = rem % 128;
+    const int q = q0 + qb;
+    const bool ok = i < QB * kQBytes / 16 && q < Q && h < H_I && c < d_idx;
+    const int64_t off = ok ? (((int64_t)b * Q + q) * H_I + h) * d_idx + c : 0;
+    const uint4 v = *reinterpret_cast<const uint4 *>(q_idx + off);
+    qv_stage[u] = ok ? v : uint4{0u, 0u, 0u, 0u};
+  }
+  float w_raw[QB][HT][4];
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
-    const int q = q0 + qb;
-    const bool qv = q < Q;
-    const int p = qv ? q_pos[(int64_t)b * Q + q] : -1;
-    vis[qb] = qv ? max(0, min(nE, (p + 1) / m)) : 0;
-    vis_max = max(vis_max, vis[qb]);
+    const int qc = min(q0 + qb, Q - 1);
 #pragma unroll
-    for (int ht = 0; ht < HT; ++ht) {
-      const int h = ht * 16 + r;
-      // E4M3 operand layout of the instruction: bytes 0..15 of lane group g
-      // hold channels 16g..16g+15, bytes 16..31 hold channels 64+16g..+15.
-      v8i a = {0, 0, 0, 0, 0, 0, 0, 0};
-      if (qv && h < H_I) {
-        const uint8_t *qr = q_idx + (((int64_t)b * Q + q) * H_I + h) * d_idx;
-        const v4i lo = *reinterpret_cast<const v4i *>(qr + 16 * g);
-        a[0] = lo[0];
-        a[1] = lo[1];
-        a[2] = lo[2];
-        a[3] = lo[3];
-        if (d_idx > 64) {
-          const v4i hi = *reinterpret_cast<const v4i *>(qr + 64 + 16 * g);
-          a[4] = hi[0];
-          a[5] = hi[1];
-          a[6] = hi[2];
-          a[7] = hi[3];
-        }
-      }
-      A[qb][ht] = a;
+    for (int ht = 0; ht < HT; ++ht)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int hh = ht * 16 + g * 4 + i;
-        wv[qb][ht][i] = (qv && hh < H_I) ? w_idx[((int64_t)b * Q + q) * H_I + hh] : 0.f;
+        w_raw[qb][ht][i] = w_idx[((int64_t)b * Q + qc) * H_I + (hh < H_I ? hh : 0)];
       }
-    }
   }
 
-  const int limit = kCand ? C : vis_max;
-  const int base = blockIdx.x * kIdxWGEntries + wave * kIdxWaveEntries;
-  for (int it = 0; it < kIdxWaveEntries / 16; ++it) {
-    const int e0 = base + it * 16;
-    if (e0 >= limit) break;
-    const int slot = e0 + r;
-    int ent = slot;
-    bool valid;
-    if (kCand) {
-      ent = slot < C ? cand[((int64_t)b * Q + q0) * C + slot] : -1;
-      valid = ent >= 0 && ent < vis[0];
-    } else {
-      valid = slot < nE;
+  // 2. Key loads: their addresses depend only on the grid position
+  //    (and, for candidates, on the candidate list), so the HBM stream
+  //    starts before anything else is known.
+  //    The loads are unconditional, from clamped (always in-bounds)
+  //    addresses, and masked afterwards: loads inside per-lane branches make
+  //    the compiler wait for each one before issuing the next.
+  v4i kv[kIters];
+  int sbv[kIters];
+  int ent[kIters];
+  bool use[kIters];
+#pragma unroll
+  for (int it = 0; it < kIters; ++it) {
+    const int slot = base + it * 16 + r;
+    int e = slot;
+    if (kCand) e = cand[((int64_t)b * Q + q0) * C + min(slot, C - 1)];
+    ent[it] = (kCand && slot >= C) ? -1 : e;
+    const bool inb = kCand ? (ent[it] >= 0 && ent[it] < N_cap) : (slot < N_cap);
+    use[it] = inb && g < kb;
+    const int64_t row = (int64_t)b * N_cap + (inb ? e : 0);
+    const int gg = g < kb ? g : 0;
+    kv[it] = *reinterpret_cast<const v4i *>(ikey + row * (d_idx / 2) + gg * 16);
+    sbv[it] = iscale[row * kb + gg];
+  }
+
+  float wv[QB][HT][4];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const bool qv = q0 + qb < Q;
+#pragma unroll
+    for (int ht = 0; ht < HT; ++ht)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int hh = ht * 16 + g * 4 + i;
+        wv[qb][ht][i] = (qv && hh < H_I) ? w_raw[qb][ht][i] : 0.f;
+      }
+  }
+
+  // 3. Queries into LDS (zero rows beyond H_I and beyond Q).
+#pragma unroll
+  for (int u = 0; u < kQVec; ++u) {
+    const int i = threadIdx.x + u * kIdxThreads;
+    if (i < QB * kQBytes / 16) {
+      const int qb = i / (kQBytes / 16), rem = (i % (kQBytes / 16)) * 16;
+      *reinterpret_cast<uint4 *>(qs + qb * kQBytes + rem) = qv_stage[u];
     }
-    v8i B = {0, 0, 0, 0, 0, 0, 0, 0};
-    int sb = 127;
-    if (valid && g < kb) {
-      const int64_t row = (int64_t)b * N_cap + ent;
-      const v4i kv = *reinterpret_cast<const v4i *>(ikey + row * (d_idx / 2) + g * 16);
-      B[0] = kv[0];
-      B[1] = kv[1];
-      B[2] = kv[2];
-      B[3] = kv[3];
-      sb = iscale[row * kb + g];
+  }
+  __syncthreads();
+  // E4M3 operand layout of the instruction: bytes 0..15 of lane group g hold
+  // channels 16g..16g+15, bytes 16..31 hold channels 64+16g..+15.
+  v8i A[QB][HT];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+    for (int ht = 0; ht < HT; ++ht) {
+      const uint8_t *qr = qs + qb * (HT * 16 * 128) + (ht * 16 + r) * 128;
+      const v4i lo = *reinterpret_cast<const v4i *>(qr + 16 * g);
+      const v4i hi = *reinterpret_cast<const v4i *>(qr + 64 + 16 * g);
+      A[qb][ht] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
     }
+
+  // 4. Scores: MFMA, ReLU, head weights, head sum; staged in LDS.
+#pragma unroll
+  for (int it = 0; it < kIters; ++it) {
+    const v4i kk = use[it] ? kv[it] : v4i{0, 0, 0, 0};
+    const int sbu = use[it] ? sbv[it] : 127;
+    const v8i Bm = {kk[0], kk[1], kk[2], kk[3], 0, 0, 0, 0};
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
       float s = 0.f;
 #pragma unroll
       for (int ht = 0; ht < HT; ++ht) {
         v4f acc = {0.f, 0.f, 0.f, 0.f};
-        acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A[qb][ht], B, acc, 0, 4, 0, 127, 0, sb);
+        acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A[qb][ht], Bm, acc, 0, 4, 0, 127, 0, sbu);
 #pragma unroll
         for (int i = 0; i < 4; ++i) s = fmaf(fmaxf(acc[i], 0.f), wv[qb][ht][i], s);
       }
       s += __shfl_xor(s, 16);
       s += __shfl_xor(s, 32);
+      if (g == 0) sc[wave][qb][it * 16 + r] = s;
+    }
+  }
+  // 5. Visibility (the entry count and positions are read only now, after
+  //    the key stream has been consumed), then 16-byte stores of this wave's
+  //    scores (LDS operations of one wave complete in order).
+  const int nE = min(n_entries[b], N_cap);
+  int vis[QB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const int q = q0 + qb;
+    vis[qb] = q < Q ? max(0, min(nE, (q_pos[(int64_t)b * Q + q] + 1) / m)) : 0;
+  }
+  if (kCand && g == 0) {
+#pragma unroll
+    for (int it = 0; it < kIters; ++it)
+      if (!(ent[it] >= 0 && ent[it] < vis[0])) sc[wave][0][it * 16 + r] = __uint_as_float(kNoScoreBits);
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  if (lane < kIdxWaveEntries / 4) {
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
       const int q = q0 + qb;
-      if (g == 0 && q < Q) {
-        float *dst = scores + ((int64_t)b * Q + q) * Ns;
-        if (kCand) {
-          if (slot < C) dst[slot] = valid ? s : __uint_as_float(kNoScoreBits);
-        } else if (slot < vis[qb]) {
-          dst[slot] = s;
-        }
+      if (q >= Q) continue;
+      const int lim = kCand ? C : vis[qb];
+      const int e0 = base + 4 * lane;
+      float *dst = scores + ((int64_t)b * Q + q) * Ns + e0;
+      const float4 v = reinterpret_cast<const float4 *>(&sc[wave][qb][0])[lane];
+      if (e0 + 4 <= lim && (Ns & 3) == 0) {
+        *reinterpret_cast<float4 *>(dst) = v;
+      } else {
+        const float vv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          if (e0 + u < lim) dst[u] = vv[u];
       }
     }
   }

@@ -27,8 +27,28 @@ constexpr int kTilePadded = kTile + kTile / 32;
 
 __device__ __forceinline__ int lds_pos(int i) { return i + (i >> 5); }
 
-// Exclusive prefix sum over the 1024 threads in thread order; also returns the total.
+// Exclusive prefix of the kW per-wave totals in sh[0..kW) (in place), total
+// in sh[kW]; done by the first wave with shuffles (one LDS read per lane).
+template <int kW>
+__device__ __forceinline__ void scan_wave_totals(int *sh) {
+  if (threadIdx.x < 64) {
+    const int lane = threadIdx.x;
+    const int v = lane < kW ? sh[lane] : 0;
+    int inc = v;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int t = __shfl_up(inc, o);
+      if (lane >= o) inc += t;
+    }
+    if (lane < kW) sh[lane] = inc - v;
+    if (lane == kW - 1) sh[kW] = inc;
+  }
+}
+
+// Exclusive prefix sum over the NT threads in thread order; also returns the total.
+template <int NT = kTopkThreads>
 __device__ __forceinline__ int block_excl_scan(int v, int *sh, int &total) {
+  constexpr int kW = NT / 64;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   int inc = v;
 #pragma unroll
@@ -38,18 +58,10 @@ __device__ __forceinline__ int block_excl_scan(int v, int *sh, int &total) {
   }
   if (lane == 63) sh[wave] = inc;
   __syncthreads();
-  if (threadIdx.x == 0) {
-    int run = 0;
-    for (int w = 0; w < kTopkWaves; ++w) {
-      const int t = sh[w];
-      sh[w] = run;
-      run += t;
-    }
-    sh[kTopkWaves] = run;
-  }
+  scan_wave_totals<kW>(sh);
   __syncthreads();
   const int res = sh[wave] + inc - v;
-  total = sh[kTopkWaves];
+  total = sh[kW];
   __syncthreads();
   return res;
 }
@@ -212,34 +224,44 @@ __global__ __launch_bounds__(kTopkThreads) void topk_tiled_kernel(const float *_
   }
   for (int j = k_eff + tid; j < k; j += kTopkThreads) {
     out_i[j] = -1;
-    if (out_s) out_s[j] = __uint_as_float(0x7FC00000u);
+    if (out_s) out_s[j] = __uint_as_float(kNoScoreBits);  // a NaN
   }
 }
 
 
-// Rows of at most kRegN scores: every thread keeps its kRegPer consecutive
-// keys in registers; digits of 11, 11 and 10 bits (the first, which every
+// Rows of at most kRegN scores: every thread keeps kRegPer keys in
+// registers; digits of 11, 11 and 10 bits (the first, which every
 // element takes part in, spreads over four bins per octave of the score,
 // so same-bin atomics within a wave stay few); per-wave histograms in LDS.
-constexpr int kRegPer = 32;
-constexpr int kRegN = kTopkThreads * kRegPer;
+constexpr int kRegThreads = 512;
+constexpr int kRegN = kRegThreads * 64;
 constexpr int kBins = 2048;
 
 // Finds the digit (of `nb` bins, nb = 2048 or 1024) holding the k_rem-th
 // largest remaining element; the counts are summed over `nh` per-wave
 // histograms.  Every thread returns the same (digit, elements above it).
+template <int NT>
 __device__ __forceinline__ void find_digit(const int (*hist)[kBins], int nh, int nb, int k_rem, int *sh, int &digit,
                                            int &above_out) {
+  constexpr int kW = NT / 64;
+  constexpr int kMaxPer = kBins / NT;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int per = nb / kTopkThreads;  // 2 or 1 bins per thread, in descending digit order
-  int c[2] = {0, 0};
-  for (int j = 0; j < per; ++j) {
-    const int d = nb - 1 - (tid * per + j);
-    int s = 0;
-    for (int w = 0; w < nh; ++w) s += hist[w][d];
-    c[j] = s;
+  const int per = nb >= NT ? nb / NT : 1;  // bins per thread, in descending digit order
+  int c[kMaxPer];
+#pragma unroll
+  for (int j = 0; j < kMaxPer; ++j) c[j] = 0;
+  int tot = 0;
+#pragma unroll
+  for (int j = 0; j < kMaxPer; ++j) {
+    const int bin = tid * per + j;
+    if (j < per && bin < nb) {
+      const int d = nb - 1 - bin;
+      int s = 0;
+      for (int w = 0; w < nh; ++w) s += hist[w][d];
+      c[j] = s;
+      tot += s;
+    }
   }
-  const int tot = c[0] + c[1];
   int inc = tot;
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {
@@ -248,42 +270,96 @@ __device__ __forceinline__ void find_digit(const int (*hist)[kBins], int nh, int
   }
   if (lane == 63) sh[wave] = inc;
   __syncthreads();
-  if (tid == 0) {
-    int run = 0;
-    for (int w = 0; w < kTopkWaves; ++w) {
-      const int t = sh[w];
-      sh[w] = run;
-      run += t;
-    }
-  }
+  scan_wave_totals<kW>(sh);
   __syncthreads();
   int above = sh[wave] + inc - tot;
-  for (int j = 0; j < per; ++j) {
-    if (above < k_rem && k_rem <= above + c[j]) {
-      sh[kTopkWaves + 1] = nb - 1 - (tid * per + j);
-      sh[kTopkWaves + 2] = above;
+#pragma unroll
+  for (int j = 0; j < kMaxPer; ++j) {
+    if (j < per && above < k_rem && k_rem <= above + c[j]) {
+      sh[kW + 1] = nb - 1 - (tid * per + j);
+      sh[kW + 2] = above;
     }
     above += c[j];
   }
   __syncthreads();
-  digit = sh[kTopkWaves + 1];
-  above_out = sh[kTopkWaves + 2];
+  digit = sh[kW + 1];
+  above_out = sh[kW + 2];
   __syncthreads();
 }
 
-__global__ __launch_bounds__(kTopkThreads) void topk_reg_kernel(const float *__restrict__ scores, int Ns,
+// Rows (or row slices) of at most kPer*kRegThreads scores.  Element
+// i = v*(4*kRegThreads) + 4*tid + u (u < 4) is held by thread tid, so every
+// load instruction is fully coalesced.
+// With nsl > 1 the workgroup handles slice blockIdx.x % nsl (elements
+// [slice*S, slice*S + S) of the row) and writes that slice's own top-k to
+// row (row*nsl + slice) of the outputs, empty slots marked -1 and
+// kNoScoreBits; a second launch in candidate mode then selects among them.
+//
+// Selection, with few block-wide synchronisations:
+//   1. row maximum and valid count (one barrier);
+//   2. histogram of the distance below the maximum, (max - key) >> 14 (bins
+//      of 1/512 octave, elements further down take no part) and the digit
+//      holding the k-th element;
+//   3. when that bin holds at most 64 elements, one wave ranks them and
+//      fixes the exact threshold key T and how many elements equal to T are
+//      taken; otherwise, and when the window holds fewer than k elements,
+//      radix passes over the remaining bits do it;
+//   4. placement in ascending entry order: per (slice, wave) ballots of
+//      "key > T" and "key == T", one scan of the per-wave counts, and
+//      in-wave ranks from masked popcounts.
+template <int kPer>
+__global__ __launch_bounds__(kRegThreads) void topk_reg_kernel(const float *__restrict__ scores, int Ns,
                                                                  const int32_t *__restrict__ n_entries, int N_cap,
                                                                  int m, const int32_t *__restrict__ q_pos, int Q,
                                                                  const int32_t *__restrict__ cand, int C, int k,
                                                                  int32_t *__restrict__ idx_out,
-                                                                 float *__restrict__ score_out) {
-  __shared__ int hist[kTopkWaves][kBins];
-  __shared__ int sh[kTopkWaves + 4];
+                                                                 float *__restrict__ score_out, int nsl, int S) {
+  constexpr int kRegPer = kPer;
+  constexpr int NT = kRegThreads;
+  constexpr int kW = NT / 64;
+  constexpr int kV = kRegPer / 4;           // slices of 4*NT elements
+  constexpr int kSlice = NT * 4;
+  static_assert(kV * kW <= 128, "one wave scans the per-wave counts, two per lane");
+  __shared__ int hist[kW][kBins];
+  __shared__ int sh[(kW + 1) * 16 + 8];
+  __shared__ uint32_t bin_keys[64];
+  __shared__ int cnt[2][kV * kW];           // per (slice, wave): elements > T, elements == T
+  __shared__ unsigned red_max;
+  __shared__ int red_cnt, n_bin, sel_need;
+  __shared__ uint32_t sel_thr;
 
-  const int q = blockIdx.x, b = blockIdx.y;
-  const int tid = threadIdx.x, wave = tid >> 6;
+  const int q = blockIdx.x / nsl, sl = blockIdx.x % nsl, b = blockIdx.y;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t row = (int64_t)b * Q + q;
-  const float *src = scores + row * Ns;
+  const int off = sl * S;                   // first element of this slice
+  const int len = nsl > 1 ? min(S, Ns - off) : Ns;
+  const float *src = scores + row * Ns + off;
+
+  // Unconditional loads from clamped addresses first (loads inside per-lane
+  // branches are serialised by the compiler); the row length is applied after.
+  uint32_t key[kRegPer];  // key[4v + u]; 0 = not a candidate
+  auto to_key = [](float x) { return __float_as_uint(x) != kNoScoreBits ? score_key(x) : 0u; };
+  if (len >= 4 && ((Ns | off | len) & 3) == 0) {
+#pragma unroll
+    for (int v = 0; v < kV; ++v) {
+      const int i0 = min(v * kSlice + 4 * tid, len - 4);
+      const float4 t4 = *reinterpret_cast<const float4 *>(src + i0);
+      key[4 * v + 0] = to_key(t4.x);
+      key[4 * v + 1] = to_key(t4.y);
+      key[4 * v + 2] = to_key(t4.z);
+      key[4 * v + 3] = to_key(t4.w);
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < kRegPer; ++j)
+      key[j] = len > 0 ? to_key(src[min((j >> 2) * kSlice + 4 * tid + (j & 3), len - 1)]) : 0u;
+  }
+  for (int i = tid; i < kBins; i += NT) hist[0][i] = 0;
+  if (tid == 0) {
+    red_max = 0u;
+    red_cnt = 0;
+    n_bin = 0;
+  }
   int n;
   if (cand) {
     n = C;
@@ -291,125 +367,272 @@ __global__ __launch_bounds__(kTopkThreads) void topk_reg_kernel(const float *__r
     const int nE = min(n_entries[b], N_cap);
     n = max(0, min(nE, (q_pos[row] + 1) / m));
   }
+  n = max(0, min(n - off, len));            // elements of this slice
+#pragma unroll
+  for (int j = 0; j < kRegPer; ++j)
+    if ((j >> 2) * kSlice + 4 * tid + (j & 3) >= n) key[j] = 0u;
 
-  // keys of elements tid*kRegPer .. +kRegPer-1; 0 = not a candidate
-  uint32_t key[kRegPer];
-  const int i0 = tid * kRegPer;
-  if (i0 + kRegPer <= n && (Ns & 3) == 0) {
+  // 1. maximum and valid count
+  uint32_t mx = 0;
+  int nv = 0;
 #pragma unroll
-    for (int v = 0; v < kRegPer / 4; ++v) {
-      const float4 f = *reinterpret_cast<const float4 *>(src + i0 + 4 * v);
-      const float ff[4] = {f.x, f.y, f.z, f.w};
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const uint32_t bits = __float_as_uint(ff[u]);
-        key[4 * v + u] = bits == kNoScoreBits ? 0u : score_key(ff[u]);
-      }
-    }
-  } else {
-#pragma unroll
-    for (int j = 0; j < kRegPer; ++j) {
-      uint32_t kk = 0;
-      if (i0 + j < n) {
-        const uint32_t bits = __float_as_uint(src[i0 + j]);
-        kk = bits == kNoScoreBits ? 0u : score_key(__uint_as_float(bits));
-      }
-      key[j] = kk;
-    }
+  for (int j = 0; j < kRegPer; ++j) {
+    mx = key[j] > mx ? key[j] : mx;
+    nv += key[j] != 0u;
   }
-
-  int n_valid = n;
-  if (cand) {
-    int cnt = 0;
 #pragma unroll
-    for (int j = 0; j < kRegPer; ++j) cnt += key[j] != 0u;
-    int tot;
-    block_excl_scan(cnt, sh, tot);
-    n_valid = tot;
+  for (int o = 32; o > 0; o >>= 1) {
+    const uint32_t t = __shfl_xor(mx, o);
+    mx = t > mx ? t : mx;
+    nv += __shfl_xor(nv, o);
   }
+  __syncthreads();
+  if (lane == 0) {
+    atomicMax(&red_max, mx);
+    atomicAdd(&red_cnt, nv);
+  }
+  __syncthreads();
+  mx = red_max;
+  const int n_valid = red_cnt;
   const int k_eff = min(k, n_valid);
 
   uint32_t thr = 0;   // full key of the k_eff-th largest element
   int need = 0;       // elements equal to thr that are taken
   if (k_eff > 0 && k_eff < n_valid) {
-    // pass 1: bits 31..21, per-wave histograms
-    for (int i = tid; i < kTopkWaves * kBins; i += kTopkThreads) (&hist[0][0])[i] = 0;
-    __syncthreads();
+    constexpr int kRelShift = 14;
 #pragma unroll
-    for (int j = 0; j < kRegPer; ++j) atomicAdd(&hist[wave][key[j] >> 21], 1);
+    for (int j = 0; j < kRegPer; ++j) {
+      const uint32_t d = (mx - key[j]) >> kRelShift;
+      if (key[j] != 0u && d < (uint32_t)(kBins - 1)) atomicAdd(&hist[0][kBins - 2 - d], 1);
+    }
     __syncthreads();
     int d1, above;
-    find_digit(hist, kTopkWaves, kBins, k_eff, sh, d1, above);
-    int k_rem = k_eff - above;
-    // pass 2: bits 20..10 of the elements in bin d1
-    for (int i = tid; i < kBins; i += kTopkThreads) hist[0][i] = 0;
-    __syncthreads();
+    find_digit<NT>(hist, 1, kBins, k_eff, sh, d1, above);
+    const int in_window = sh[kW];             // total of the histogram (written by the digit search)
+    const int c1 = in_window >= k_eff ? hist[0][d1] : 0;  // d1 is only defined then
+    if (in_window >= k_eff && c1 <= 64) {
+      // 3a. rank the few elements of the threshold bin in one wave
+      const uint32_t dhi = (uint32_t)(kBins - 2 - d1);
 #pragma unroll
-    for (int j = 0; j < kRegPer; ++j)
-      if ((key[j] >> 21) == (uint32_t)d1) atomicAdd(&hist[0][(key[j] >> 10) & 0x7FFu], 1);
-    __syncthreads();
-    int d2;
-    find_digit(hist, 1, kBins, k_rem, sh, d2, above);
-    k_rem -= above;
-    const uint32_t p12 = ((uint32_t)d1 << 11) | (uint32_t)d2;
-    // pass 3: bits 9..0
-    for (int i = tid; i < kBins; i += kTopkThreads) hist[0][i] = 0;
-    __syncthreads();
+      for (int j = 0; j < kRegPer; ++j)
+        if (key[j] != 0u && ((mx - key[j]) >> kRelShift) == dhi) bin_keys[atomicAdd(&n_bin, 1)] = key[j];
+      __syncthreads();
+      if (wave == 0) {
+        const int k_rem = k_eff - above;
+        const uint32_t kl = lane < c1 ? bin_keys[lane] : 0u;
+        int gt = 0, ge = 0;
+        for (int j = 0; j < c1; ++j) {
+          const uint32_t kj = bin_keys[j];
+          gt += kj > kl;
+          ge += kj >= kl;
+        }
+        if (lane < c1 && gt < k_rem && k_rem <= ge) {  // every lane holding the threshold key agrees
+          sel_thr = kl;
+          sel_need = k_rem - gt;
+        }
+      }
+      __syncthreads();
+      thr = sel_thr;
+      need = sel_need;
+    } else if (in_window >= k_eff) {
+      // 3b. radix passes over the remaining 14 distance bits (7 + 7)
+      int k_rem = k_eff - above;
+      const uint32_t dhi = (uint32_t)(kBins - 2 - d1);
+      for (int i = tid; i < kBins; i += NT) hist[0][i] = 0;
+      __syncthreads();
 #pragma unroll
-    for (int j = 0; j < kRegPer; ++j)
-      if ((key[j] >> 10) == p12) atomicAdd(&hist[0][key[j] & 0x3FFu], 1);
-    __syncthreads();
-    int d3;
-    find_digit(hist, 1, 1024, k_rem, sh, d3, above);
-    k_rem -= above;
-    thr = (p12 << 10) | (uint32_t)d3;
-    need = k_rem;
+      for (int j = 0; j < kRegPer; ++j) {
+        const uint32_t dist = mx - key[j];
+        if (key[j] != 0u && (dist >> kRelShift) == dhi) atomicAdd(&hist[0][127 - ((dist >> 7) & 127u)], 1);
+      }
+      __syncthreads();
+      int d2;
+      find_digit<NT>(hist, 1, 128, k_rem, sh, d2, above);
+      k_rem -= above;
+      const uint32_t dmid = (dhi << 7) | (uint32_t)(127 - d2);
+      for (int i = tid; i < 128; i += NT) hist[0][i] = 0;
+      __syncthreads();
+#pragma unroll
+      for (int j = 0; j < kRegPer; ++j) {
+        const uint32_t dist = mx - key[j];
+        if (key[j] != 0u && (dist >> 7) == dmid) atomicAdd(&hist[0][127 - (dist & 127u)], 1);
+      }
+      __syncthreads();
+      int d3;
+      find_digit<NT>(hist, 1, 128, k_rem, sh, d3, above);
+      k_rem -= above;
+      thr = mx - ((dmid << 7) | (uint32_t)(127 - d3));
+      need = k_rem;
+    } else {
+      // 3c. full-range passes: bits 31..21 (per-wave histograms), 20..10, 9..0
+      for (int i = tid; i < kW * kBins; i += NT) (&hist[0][0])[i] = 0;
+      __syncthreads();
+#pragma unroll
+      for (int j = 0; j < kRegPer; ++j) atomicAdd(&hist[wave][key[j] >> 21], 1);
+      __syncthreads();
+      int e1, ab;
+      find_digit<NT>(hist, kW, kBins, k_eff, sh, e1, ab);
+      int k_rem = k_eff - ab;
+      for (int i = tid; i < kBins; i += NT) hist[0][i] = 0;
+      __syncthreads();
+#pragma unroll
+      for (int j = 0; j < kRegPer; ++j)
+        if ((key[j] >> 21) == (uint32_t)e1) atomicAdd(&hist[0][(key[j] >> 10) & 0x7FFu], 1);
+      __syncthreads();
+      int e2;
+      find_digit<NT>(hist, 1, kBins, k_rem, sh, e2, ab);
+      k_rem -= ab;
+      const uint32_t p12 = ((uint32_t)e1 << 11) | (uint32_t)e2;
+      for (int i = tid; i < kBins; i += NT) hist[0][i] = 0;
+      __syncthreads();
+#pragma unroll
+      for (int j = 0; j < kRegPer; ++j)
+        if ((key[j] >> 10) == p12) atomicAdd(&hist[0][key[j] & 0x3FFu], 1);
+      __syncthreads();
+      int e3;
+      find_digit<NT>(hist, 1, 1024, k_rem, sh, e3, ab);
+      k_rem -= ab;
+      thr = (p12 << 10) | (uint32_t)e3;
+      need = k_rem;
+    }
   }
 
-  int32_t *out_i = idx_out + row * k;
-  float *out_s = score_out ? score_out + row * k : nullptr;
+  // 4. placement in ascending entry order
+  const int64_t orow = row * nsl + sl;
+  int32_t *out_i = idx_out + orow * k;
+  float *out_s = score_out ? score_out + orow * k : nullptr;
   if (k_eff > 0) {
-    int gt = 0, eq = 0;
+    const uint64_t below = lane ? (~0ull >> (64 - lane)) : 0ull;
 #pragma unroll
-    for (int j = 0; j < kRegPer; ++j) {
-      gt += key[j] > thr;
-      eq += need > 0 && key[j] == thr;
-    }
-    int eq_tot;
-    const int eq_before = block_excl_scan(eq, sh, eq_tot);
-    const int take_eq = max(0, min(eq, need - eq_before));
-    int sel_tot;
-    int off = block_excl_scan(gt + take_eq, sh, sel_tot);
-    int eq_seen = 0;
+    for (int v = 0; v < kV; ++v) {
+      int gc = 0, ec = 0;
 #pragma unroll
-    for (int j = 0; j < kRegPer; ++j) {
-      bool take = key[j] > thr;
-      if (!take && need > 0 && key[j] == thr) {
-        take = eq_seen < take_eq;
-        ++eq_seen;
+      for (int u = 0; u < 4; ++u) {
+        gc += __popcll(__ballot(key[4 * v + u] > thr));
+        ec += __popcll(__ballot(need > 0 && key[4 * v + u] == thr));
       }
-      if (take && off < k_eff) {
-        out_i[off] = cand ? cand[row * C + i0 + j] : i0 + j;
-        if (out_s) out_s[off] = key_score(key[j]);
-        ++off;
+      if (lane == 0) {
+        cnt[0][v * kW + wave] = gc;
+        cnt[1][v * kW + wave] = ec;
+      }
+    }
+    __syncthreads();
+    if (wave == 0) {
+      // exclusive prefix over (slice, wave) in v-major order; two entries per lane
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const int e0 = 2 * lane, e1 = 2 * lane + 1;
+        const int a0 = e0 < kV * kW ? cnt[t][e0] : 0, a1 = e1 < kV * kW ? cnt[t][e1] : 0;
+        int inc = a0 + a1;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+          const int x = __shfl_up(inc, o);
+          if (lane >= o) inc += x;
+        }
+        const int ex = inc - a0 - a1;
+        if (e0 < kV * kW) cnt[t][e0] = ex;
+        if (e1 < kV * kW) cnt[t][e1] = ex + a0;
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int v = 0; v < kV; ++v) {
+      uint64_t gm[4], em[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        gm[u] = __ballot(key[4 * v + u] > thr);
+        em[u] = __ballot(need > 0 && key[4 * v + u] == thr);
+      }
+      int gb = cnt[0][v * kW + wave], eb = cnt[1][v * kW + wave];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        gb += __popcll(gm[u] & below);
+        eb += __popcll(em[u] & below);
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const uint32_t kk = key[4 * v + u];
+        const bool is_gt = kk > thr, is_eq = need > 0 && kk == thr;
+        if (is_gt || (is_eq && eb < need)) {
+          const int pos = gb + min(eb, need);
+          if (pos < k_eff) {
+            const int i = v * kSlice + 4 * tid + u;
+            out_i[pos] = cand ? cand[row * C + i] : off + i;
+            if (out_s) out_s[pos] = key_score(kk);
+          }
+        }
+        gb += is_gt;
+        eb += is_eq;
       }
     }
   }
-  for (int j = k_eff + tid; j < k; j += kTopkThreads) {
+  for (int j = k_eff + tid; j < k; j += NT) {
     out_i[j] = -1;
-    if (out_s) out_s[j] = __uint_as_float(0x7FC00000u);
+    if (out_s) out_s[j] = __uint_as_float(kNoScoreBits);  // a NaN
   }
 }
 
-hipError_t launch_topk(const CacheView &c, const float *scores, int Ns, const int32_t *q_pos, int Q,
-                       const int32_t *cand, int C, int k, int32_t *idx_out, float *score_out, hipStream_t stream) {
-  dim3 grid(Q, c.B);
-  if (Ns <= kRegN)
-    topk_reg_kernel<<<grid, kTopkThreads, 0, stream>>>(scores, Ns, c.n_entries, c.N_cap, c.m, q_pos, Q, cand, C, k,
-                                                       idx_out, score_out);
+TopkPlan topk_plan(int B, int Q, int Ns, int k) {
+  TopkPlan p{1, Ns, 0};
+  const int64_t rows = (int64_t)B * Q;
+  if (rows >= 256 || Ns <= 4096 || k <= 0) return p;
+  // Smallest power-of-two slice (>= 4096, >= k) whose candidates fit one
+  // register-resident row in the second stage.
+  for (int S = 4096; S <= kRegN; S *= 2) {
+    if (S < k) continue;
+    const int nsl = (Ns + S - 1) / S;
+    if (nsl < 2) break;
+    if ((int64_t)nsl * k <= kRegN) {
+      p.nsl = nsl;
+      p.S = S;
+      p.ws_bytes = (size_t)rows * nsl * k * (sizeof(int32_t) + sizeof(float));
+      return p;
+    }
+  }
+  return p;
+}
+
+template <int kPer>
+static void launch_reg(dim3 grid, hipStream_t stream, const float *scores, int Ns, const CacheView &c,
+                       const int32_t *q_pos, int Q, const int32_t *cand, int C, int k, int32_t *idx_out,
+                       float *score_out, int nsl, int S) {
+  topk_reg_kernel<kPer><<<grid, kRegThreads, 0, stream>>>(scores, Ns, c.n_entries, c.N_cap, c.m, q_pos, Q, cand, C, k,
+                                                         idx_out, score_out, nsl, S);
+}
+
+static void launch_one(const CacheView &c, const float *scores, int Ns, int len, const int32_t *q_pos, int Q,
+                       const int32_t *cand, int C, int k, int32_t *idx_out, float *score_out, int nsl, int S,
+                       hipStream_t stream) {
+  dim3 grid(Q * nsl, c.B);
+  if (len <= kRegThreads * 8)
+    launch_reg<8>(grid, stream, scores, Ns, c, q_pos, Q, cand, C, k, idx_out, score_out, nsl, S);
+  else if (len <= kRegThreads * 16)
+    launch_reg<16>(grid, stream, scores, Ns, c, q_pos, Q, cand, C, k, idx_out, score_out, nsl, S);
+  else if (len <= kRegThreads * 32)
+    launch_reg<32>(grid, stream, scores, Ns, c, q_pos, Q, cand, C, k, idx_out, score_out, nsl, S);
+  else if (len <= kRegN)
+    launch_reg<64>(grid, stream, scores, Ns, c, q_pos, Q, cand, C, k, idx_out, score_out, nsl, S);
   else
-    topk_tiled_kernel<<<grid, kTopkThreads, 0, stream>>>(scores, Ns, c.n_entries, c.N_cap, c.m, q_pos, Q, cand, C, k,
-                                                         idx_out, score_out);
+    topk_tiled_kernel<<<dim3(Q, c.B), kTopkThreads, 0, stream>>>(scores, Ns, c.n_entries, c.N_cap, c.m, q_pos, Q, cand,
+                                                                 C, k, idx_out, score_out);
+}
+
+hipError_t launch_topk(const CacheView &c, const float *scores, int Ns, const int32_t *q_pos, int Q,
+                       const int32_t *cand, int C, int k, int32_t *idx_out, float *score_out, void *ws,
+                       hipStream_t stream) {
+  const TopkPlan p = cand ? TopkPlan{1, Ns, 0} : topk_plan(c.B, Q, Ns, k);
+  if (p.nsl == 1) {
+    launch_one(c, scores, Ns, Ns, q_pos, Q, cand, C, k, idx_out, score_out, 1, Ns, stream);
+    return hipGetLastError();
+  }
+  // stage 1: exact top-k of every slice; stage 2: top-k of the candidates
+  const int Cc = p.nsl * k;
+  int32_t *ci = reinterpret_cast<int32_t *>(ws);
+  float *cs = reinterpret_cast<float *>(ci + (size_t)c.B * Q * Cc);
+  launch_one(c, scores, Ns, p.S, q_pos, Q, nullptr, 0, k, ci, cs, p.nsl, p.S, stream);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  launch_one(c, cs, Cc, Cc, q_pos, Q, ci, Cc, k, idx_out, score_out, 1, Cc, stream);
   return hipGetLastError();
 }
 

@@ -13,7 +13,7 @@ import torch
 from ._lib import CacheT, check, lib
 
 D, D_NOPE, D_ROPE = 576, 512, 64
-WS_INDEX_TOPK, WS_SPARSE_ATTN, WS_DENSE_ATTN = 0, 1, 2
+WS_INDEX_TOPK, WS_SPARSE_ATTN, WS_DENSE_ATTN, WS_TOPK = 0, 1, 2, 3
 OUT_F32, OUT_BF16 = 0, 1
 
 
@@ -104,7 +104,7 @@ def index_topk(cache: Cache, q_idx, w_idx, q_pos, k, cand=None, want_scores=Fals
     dev = q_idx.device
     idx = out if out is not None else torch.empty(B, Q, k, dtype=torch.int32, device=dev)
     sc = torch.empty(B, Q, k, dtype=torch.float32, device=dev) if want_scores else None
-    need = workspace_bytes(WS_INDEX_TOPK, B, Q, 0, cache.N_cap, C)
+    need = workspace_bytes(WS_INDEX_TOPK, B, Q, k, cache.N_cap, C)
     ws, wsb = _workspace(need, ws, dev)
     cs = cache.struct()
     check(lib().csa_index_topk(ctypes.byref(cs), _ptr(q_idx), _ptr(w_idx), H_I, _ptr(q_pos), Q, _ptr(cand), C, int(k),
@@ -128,16 +128,18 @@ def index_scores(cache: Cache, q_idx, w_idx, q_pos, cand=None, scores=None):
     return scores
 
 
-def topk(cache: Cache, scores, q_pos, k, cand=None, want_scores=False, out=None):
+def topk(cache: Cache, scores, q_pos, k, cand=None, want_scores=False, out=None, ws=None):
     """Top-k stage alone, from the scores of index_scores()."""
     B, Q = q_pos.shape
     C = cand.shape[2] if cand is not None else 0
     dev = q_pos.device
     idx = out if out is not None else torch.empty(B, Q, k, dtype=torch.int32, device=dev)
     sc = torch.empty(B, Q, k, dtype=torch.float32, device=dev) if want_scores else None
+    need = 0 if cand is not None else workspace_bytes(WS_TOPK, B, Q, k, cache.N_cap)
+    ws, wsb = _workspace(need, ws, dev)
     cs = cache.struct()
     check(lib().csa_topk(ctypes.byref(cs), _ptr(scores), _ptr(q_pos), Q, _ptr(cand), C, int(k), _ptr(idx), _ptr(sc),
-                         _stream()), "csa_topk")
+                         _ptr(ws), wsb, _stream()), "csa_topk")
     return idx, sc
 
 

@@ -114,7 +114,8 @@ int csa_compress(const uint16_t *x, int64_t x_stride_b, const uint16_t *z, int64
  *   cand     int32 [B][Q][C] ascending entry indices, -1 = none, no repeats;
  *            NULL for a full scan (C ignored)
  *   idx_out  int32 [B][Q][k]      score_out fp32 [B][Q][k] or NULL (NaN in padding)
- *   ws       >= csa_workspace_bytes(CSA_WS_INDEX_TOPK, ...) bytes, 256-byte aligned. */
+ *   ws       >= csa_workspace_bytes(CSA_WS_INDEX_TOPK, ...) bytes, 256-byte aligned
+ *            (fp32 scores of every scanned entry, then the top-k workspace). */
 int csa_index_topk(const csa_cache_t *cache, const uint8_t *q_idx, const float *w_idx, int H_I,
                    const int32_t *q_pos, int Q, const int32_t *cand, int C, int k, int32_t *idx_out,
                    float *score_out, void *ws, size_t ws_bytes, hipStream_t stream);
@@ -129,7 +130,7 @@ int csa_index_scores(const csa_cache_t *cache, const uint8_t *q_idx, const float
                      const int32_t *q_pos, int Q, const int32_t *cand, int C, float *scores, size_t scores_bytes,
                      hipStream_t stream);
 int csa_topk(const csa_cache_t *cache, const float *scores, const int32_t *q_pos, int Q, const int32_t *cand,
-             int C, int k, int32_t *idx_out, float *score_out, hipStream_t stream);
+             int C, int k, int32_t *idx_out, float *score_out, void *ws, size_t ws_bytes, hipStream_t stream);
 
 /* Sparse attention over selected entries plus the sliding window ([V4]
  * Fig. 3).  One softmax over the union of the entries listed in idx and the
@@ -155,12 +156,17 @@ int hca_dense_attn(const csa_cache_t *cache, const uint16_t *q, int H, const int
                    const uint16_t *swa, const int32_t *swa_pos0, int S, int n_win, float softmax_scale,
                    int out_dtype, void *out, float *lse, void *ws, size_t ws_bytes, hipStream_t stream);
 
-enum { CSA_WS_INDEX_TOPK = 0, CSA_WS_SPARSE_ATTN = 1, CSA_WS_DENSE_ATTN = 2 };
+enum { CSA_WS_INDEX_TOPK = 0, CSA_WS_SPARSE_ATTN = 1, CSA_WS_DENSE_ATTN = 2, CSA_WS_TOPK = 3 };
 
-/* Workspace bytes for one call.  For CSA_WS_INDEX_TOPK, `n_or_k` is N_cap
- * (full scan) and `C` the candidate count (0 for a full scan).  For the
- * attention ops `n_or_k` is k (sparse) or N_cap (dense) and C is n_win. */
-size_t csa_workspace_bytes(int op, int B, int Q, int H, int n_or_k, int C);
+/* Workspace bytes for one call (0 = none needed).
+ *   CSA_WS_INDEX_TOPK: H_or_k = k, n = N_cap, C = candidate count (0 for a
+ *                      full scan); scores plus the top-k workspace.
+ *   CSA_WS_TOPK:       H_or_k = k, n = scores per row (N_cap or C), C unused.
+ *                      Rows with few siblings are selected in two launches
+ *                      (per-slice candidates, then their top-k), which uses it.
+ *   CSA_WS_SPARSE_ATTN / CSA_WS_DENSE_ATTN: H_or_k = query heads H, n = k
+ *                      (sparse) or N_cap (dense), C = n_win. */
+size_t csa_workspace_bytes(int op, int B, int Q, int H_or_k, int n, int C);
 
 const char *csa_status_str(int status);
 int csa_version(void);

@@ -393,3 +393,40 @@ def test_end_to_end_tiny_decode():
         err = row_rel_err(_np(out)[0, 0], oo)
         assert err.max() <= 1e-3, err.max()
         assert np.abs(_np(lse)[0, 0] - ol).max() <= 1e-4 * max(1.0, np.abs(ol).max())
+
+
+TOPK_CASES = [
+    # (name, B, Q, Ns, visible per row, k, rounding that creates ties)
+    ("two-stage-ties", 2, 1, 20000, [20000, 13001], 300, 1.0),
+    ("two-stage-k-over-slice", 1, 1, 32768, [32768], 5000, 0.05),
+    ("single-stage-ragged", 3, 2, 1003, [1003, 999, 17], 64, 0.5),
+    ("tiled-long-row", 1, 1, 70001, [70001], 777, 0.1),
+]
+
+
+@pytest.mark.parametrize("name,B,Q,Ns,vis,k,rnd", TOPK_CASES, ids=[c[0] for c in TOPK_CASES])
+def test_topk_stage_parity(name, B, Q, Ns, vis, k, rnd):
+    """The top-k stage on generated scores with many exact ties, against
+    the oracle's selection rule (largest first, ties to the lower entry)."""
+    raw = normal_f32(99, TensorId.W, (B * Q, Ns)).numpy().astype(np.float64)
+    sc = (np.round(raw / rnd) * rnd).astype(np.float32).reshape(B, Q, Ns)
+    # visibility through positions: m = 1, entry j visible when j <= p
+    vis = np.array(vis[:B * Q] + [Ns] * (B * Q - len(vis)))[:B * Q].reshape(B, Q)
+    pos = (vis - 1).astype(np.int32)
+    planes = dict(nope=np.zeros((B, 1, 256), np.uint8), nscale=np.zeros((B, 1, 16), np.uint8),
+                  rope=np.zeros((B, 1, 64), np.uint16))
+    cache = csa.Cache(B, Ns, 1, 0, planes=dict(
+        nope=torch.zeros(B, 1, 256, dtype=torch.uint8, device=DEV), nscale=torch.zeros(B, 1, 16, dtype=torch.uint8,
+                                                                                     device=DEV),
+        rope=torch.zeros(B, 1, 64, dtype=torch.bfloat16, device=DEV), ikey=None, iscale=None,
+        n_entries=torch.full((B,), Ns, dtype=torch.int32, device=DEV)))
+    idx, s_out = csa.topk(cache, torch.from_numpy(sc).to(DEV), torch.from_numpy(pos).to(DEV), k, want_scores=True)
+    g, gs = _np(idx), _np(s_out)
+    for b in range(B):
+        for t in range(Q):
+            n = int(vis[b, t])
+            oi, os_ = O.topk_select(sc[b, t, :n].astype(np.float64), np.arange(n), k)
+            np.testing.assert_array_equal(g[b, t], oi, err_msg=f"{name} b={b} t={t}")
+            sel = oi >= 0
+            np.testing.assert_array_equal(gs[b, t][sel], os_[sel].astype(np.float32))
+            assert np.all(np.isnan(gs[b, t][~sel]))

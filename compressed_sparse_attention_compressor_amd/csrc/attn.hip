@@ -272,7 +272,7 @@ __global__ __launch_bounds__(HG * 128) void attn_kernel(AttnArgs a) {
     for (int i = 0; i < 4; ++i) {
       const float x0 = kv0 ? S2[0][i] * a.scale_log2 : -INFINITY;
       const float x1 = kv1 ? S2[1][i] * a.scale_log2 : -INFINITY;
-      const float tmax = group_max<16>(fmaxf(x0, x1));
+      const float tmax = row16_max(fmaxf(x0, x1));
       const float mn = fmaxf(m2[i], tmax);
       if (mn == -INFINITY) {
         alpha[i] = 1.f;
@@ -282,7 +282,7 @@ __global__ __launch_bounds__(HG * 128) void attn_kernel(AttnArgs a) {
         p0[i] = exp2f(x0 - mn);
         p1[i] = exp2f(x1 - mn);
       }
-      lsum[i] = lsum[i] * alpha[i] + group_sum<16>(p0[i] + p1[i]);
+      lsum[i] = lsum[i] * alpha[i] + row16_sum(p0[i] + p1[i]);
       m2[i] = mn;
     }
 #pragma unroll

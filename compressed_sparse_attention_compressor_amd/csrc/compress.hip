@@ -27,7 +27,7 @@ constexpr int kSmallM = 8;   // blocks up to this many rows are pooled from regi
 // spread over 16 consecutive lanes; returns the packed byte and the block's
 // scale byte (valid in every lane of the group).
 __device__ __forceinline__ uint32_t encode_pair(float v0, float v1, uint32_t &sbyte) {
-  float amax = group_max<16>(fmaxf(fabsf(v0), fabsf(v1)));
+  float amax = row16_max(fmaxf(fabsf(v0), fabsf(v1)));
   sbyte = mx_scale_byte(amax);
   float inv = mx_inv_scale(sbyte);
   return e2m1_encode(v0, inv) | (e2m1_encode(v1, inv) << 4);

@@ -66,18 +66,70 @@ __device__ __forceinline__ uint32_t e2m1_encode(float v, float inv_scale) {
 // 1 / 2^X for the block byte s (X = s - 127), exactly: 2^(127 - s).
 __device__ __forceinline__ float mx_inv_scale(uint32_t s) { return __uint_as_float((254u - s) << 23); }
 
-template <int W>
-__device__ __forceinline__ float group_max(float v) {
-#pragma unroll
-  for (int o = W / 2; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
-  return v;
+// Cross-lane steps on DPP (data-parallel primitives): they run at VALU
+// latency, where a ds_bpermute shuffle makes an LDS round trip.  Lanes
+// whose DPP source lies outside their row (or rows left out by the row
+// mask) read 0.
+template <int kCtrl, int kRowMask = 0xF>
+__device__ __forceinline__ int dpp_i32(int x) {
+  return __builtin_amdgcn_update_dpp(0, x, kCtrl, kRowMask, 0xF, false);
 }
 
-template <int W>
-__device__ __forceinline__ float group_sum(float v) {
-#pragma unroll
-  for (int o = W / 2; o > 0; o >>= 1) v += __shfl_xor(v, o);
-  return v;
+// Inclusive prefix sum over the 64 lanes of a wave: shifts by 1, 2, 4, 8
+// within each row of 16 lanes, then the row totals carried into the rows
+// above (row_bcast:15 into rows 1 and 3, row_bcast:31 into rows 2 and 3).
+__device__ __forceinline__ int wave_incl_scan(int x) {
+  x += dpp_i32<0x111>(x);
+  x += dpp_i32<0x112>(x);
+  x += dpp_i32<0x114>(x);
+  x += dpp_i32<0x118>(x);
+  x += dpp_i32<0x142, 0xA>(x);
+  x += dpp_i32<0x143, 0xC>(x);
+  return x;
+}
+
+// Wave-uniform sum and maximum: a butterfly within each row of 16 lanes
+// (quad permutes, then rotations by 4 and 8), then the four row results
+// read into scalar registers.
+__device__ __forceinline__ int wave_sum(int x) {
+  x += dpp_i32<0xB1>(x);   // quad_perm [1,0,3,2]
+  x += dpp_i32<0x4E>(x);   // quad_perm [2,3,0,1]
+  x += dpp_i32<0x124>(x);  // row_ror:4
+  x += dpp_i32<0x128>(x);  // row_ror:8
+  return __builtin_amdgcn_readlane(x, 0) + __builtin_amdgcn_readlane(x, 16) + __builtin_amdgcn_readlane(x, 32) +
+         __builtin_amdgcn_readlane(x, 48);
+}
+
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t x) {
+  x = max(x, (uint32_t)dpp_i32<0xB1>((int)x));
+  x = max(x, (uint32_t)dpp_i32<0x4E>((int)x));
+  x = max(x, (uint32_t)dpp_i32<0x124>((int)x));
+  x = max(x, (uint32_t)dpp_i32<0x128>((int)x));
+  const uint32_t a = max((uint32_t)__builtin_amdgcn_readlane((int)x, 0), (uint32_t)__builtin_amdgcn_readlane((int)x, 16));
+  const uint32_t b = max((uint32_t)__builtin_amdgcn_readlane((int)x, 32), (uint32_t)__builtin_amdgcn_readlane((int)x, 48));
+  return max(a, b);
+}
+
+// Reductions over each row of 16 lanes (lanes 16r .. 16r+15), every lane
+// of the row receiving the same bits: partners at xor 1 and xor 2 (quad
+// permutes), then the mirrored lane within 8 and within 16, so each step
+// adds two equal-shaped partial results and the addition order is the same
+// (up to commutation) in every lane.
+template <int kCtrl>
+__device__ __forceinline__ float dpp_f32(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), kCtrl, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float row16_max(float v) {
+  v = fmaxf(v, dpp_f32<0xB1>(v));   // quad_perm [1,0,3,2]
+  v = fmaxf(v, dpp_f32<0x4E>(v));   // quad_perm [2,3,0,1]
+  v = fmaxf(v, dpp_f32<0x141>(v));  // row_half_mirror
+  return fmaxf(v, dpp_f32<0x140>(v));  // row_mirror
+}
+__device__ __forceinline__ float row16_sum(float v) {
+  v += dpp_f32<0xB1>(v);
+  v += dpp_f32<0x4E>(v);
+  v += dpp_f32<0x141>(v);
+  return v + dpp_f32<0x140>(v);
 }
 
 // Order-preserving map of an fp32 score to uint32 (larger score, larger key).

@@ -237,54 +237,55 @@ constexpr int kRegThreads = 512;
 constexpr int kRegN = kRegThreads * 64;
 constexpr int kBins = 2048;
 
-// Finds the digit (of `nb` bins, nb = 2048 or 1024) holding the k_rem-th
-// largest remaining element; the counts are summed over `nh` per-wave
-// histograms.  Every thread returns the same (digit, elements above it).
+// Finds the digit (of `nb` <= kBins bins) holding the k_rem-th largest
+// remaining element; the counts are summed over `nh` per-wave histograms.
+// Every thread returns the same digit, the number of elements in higher
+// digits and the histogram total; when the total is below k_rem the digit
+// is undefined.  Two barriers; uses sh[0 .. kW+2).
 template <int NT>
 __device__ __forceinline__ void find_digit(const int (*hist)[kBins], int nh, int nb, int k_rem, int *sh, int &digit,
-                                           int &above_out) {
+                                           int &above_out, int &total) {
   constexpr int kW = NT / 64;
   constexpr int kMaxPer = kBins / NT;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int per = nb >= NT ? nb / NT : 1;  // bins per thread, in descending digit order
   int c[kMaxPer];
-#pragma unroll
-  for (int j = 0; j < kMaxPer; ++j) c[j] = 0;
   int tot = 0;
 #pragma unroll
   for (int j = 0; j < kMaxPer; ++j) {
     const int bin = tid * per + j;
-    if (j < per && bin < nb) {
-      const int d = nb - 1 - bin;
-      int s = 0;
-      for (int w = 0; w < nh; ++w) s += hist[w][d];
-      c[j] = s;
-      tot += s;
-    }
+    int s = 0;
+    if (j < per && bin < nb)
+      for (int w = 0; w < nh; ++w) s += hist[w][nb - 1 - bin];
+    c[j] = s;
+    tot += s;
   }
-  int inc = tot;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int t = __shfl_up(inc, o);
-    if (lane >= o) inc += t;
-  }
+  const int inc = wave_incl_scan(tot);
   if (lane == 63) sh[wave] = inc;
   __syncthreads();
-  scan_wave_totals<kW>(sh);
-  __syncthreads();
-  int above = sh[wave] + inc - tot;
+  int base = 0, all = 0;
+#pragma unroll
+  for (int w = 0; w < kW; ++w) {
+    const int t = sh[w];
+    base += w < wave ? t : 0;
+    all += t;
+  }
+  int above = base + inc - tot;
 #pragma unroll
   for (int j = 0; j < kMaxPer; ++j) {
     if (j < per && above < k_rem && k_rem <= above + c[j]) {
-      sh[kW + 1] = nb - 1 - (tid * per + j);
-      sh[kW + 2] = above;
+      sh[kW] = nb - 1 - (tid * per + j);
+      sh[kW + 1] = above;
     }
     above += c[j];
   }
   __syncthreads();
-  digit = sh[kW + 1];
-  above_out = sh[kW + 2];
-  __syncthreads();
+  // A later call writes sh only after its first barrier, which every thread
+  // reaches after these reads.
+  digit = __builtin_amdgcn_readfirstlane(sh[kW]);
+  above_out = __builtin_amdgcn_readfirstlane(sh[kW + 1]);
+  total = __builtin_amdgcn_readfirstlane(all);
 }
 
 // Rows (or row slices) of at most kPer*kRegThreads scores.  Element
@@ -293,51 +294,59 @@ __device__ __forceinline__ void find_digit(const int (*hist)[kBins], int nh, int
 // With nsl > 1 the workgroup handles slice blockIdx.x % nsl (elements
 // [slice*S, slice*S + S) of the row) and writes that slice's own top-k to
 // row (row*nsl + slice) of the outputs, empty slots marked -1 and
-// kNoScoreBits; a second launch in candidate mode then selects among them.
+// kNoScoreBits; a second launch in candidate mode (kCand) then selects
+// among them.
 //
-// Selection, with few block-wide synchronisations:
-//   1. row maximum and valid count (one barrier);
+// Selection is a short chain of block-wide steps; cross-lane work runs on
+// DPP and readlane, and small scans are repeated by every wave rather than
+// published through a further barrier:
+//   1. row maximum and valid count;
 //   2. histogram of the distance below the maximum, (max - key) >> 14 (bins
 //      of 1/512 octave, elements further down take no part) and the digit
 //      holding the k-th element;
-//   3. when that bin holds at most 64 elements, one wave ranks them and
-//      fixes the exact threshold key T and how many elements equal to T are
-//      taken; otherwise, and when the window holds fewer than k elements,
-//      radix passes over the remaining bits do it;
+//   3. when that bin holds at most 64 elements they are gathered (one LDS
+//      atomic per wave) and every wave ranks them to fix the exact threshold
+//      key T and how many elements equal to T are taken; otherwise, and when
+//      the window holds fewer than k elements, radix passes over the
+//      remaining bits do it;
 //   4. placement in ascending entry order: per (slice, wave) ballots of
-//      "key > T" and "key == T", one scan of the per-wave counts, and
-//      in-wave ranks from masked popcounts.
-template <int kPer>
+//      "key > T" and "key == T", a scan of those counts, and in-wave ranks
+//      from masked popcounts.
+template <int kPer, bool kCand>
 __global__ __launch_bounds__(kRegThreads) void topk_reg_kernel(const float *__restrict__ scores, int Ns,
                                                                  const int32_t *__restrict__ n_entries, int N_cap,
                                                                  int m, const int32_t *__restrict__ q_pos, int Q,
                                                                  const int32_t *__restrict__ cand, int C, int k,
                                                                  int32_t *__restrict__ idx_out,
                                                                  float *__restrict__ score_out, int nsl, int S) {
-  constexpr int kRegPer = kPer;
   constexpr int NT = kRegThreads;
   constexpr int kW = NT / 64;
-  constexpr int kV = kRegPer / 4;           // slices of 4*NT elements
+  constexpr int kV = kPer / 4;              // slices of 4*NT elements
   constexpr int kSlice = NT * 4;
-  static_assert(kV * kW <= 128, "one wave scans the per-wave counts, two per lane");
+  constexpr int kE = kV * kW;               // (slice, wave) pairs
+  constexpr bool kPrefetch = kCand && kPer <= 32;  // candidate ids loaded with the scores
+  static_assert(kE <= 128, "a wave scans the (slice, wave) counts two per lane");
   __shared__ int hist[kW][kBins];
-  __shared__ int sh[(kW + 1) * 16 + 8];
+  __shared__ int sh[kW + 2];
+  __shared__ uint32_t wmax[kW];
+  __shared__ int wcnt[kW];
   __shared__ uint32_t bin_keys[64];
-  __shared__ int cnt[2][kV * kW];           // per (slice, wave): elements > T, elements == T
-  __shared__ unsigned red_max;
-  __shared__ int red_cnt, n_bin, sel_need;
-  __shared__ uint32_t sel_thr;
+  __shared__ int cnt[2][kE];                // per (slice, wave): elements > T, elements == T
+  __shared__ int n_bin;
 
   const int q = blockIdx.x / nsl, sl = blockIdx.x % nsl, b = blockIdx.y;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int64_t row = (int64_t)b * Q + q;
   const int off = sl * S;                   // first element of this slice
   const int len = nsl > 1 ? min(S, Ns - off) : Ns;
   const float *src = scores + row * Ns + off;
+  const int32_t *csrc = kCand ? cand + row * C : nullptr;
 
   // Unconditional loads from clamped addresses first (loads inside per-lane
   // branches are serialised by the compiler); the row length is applied after.
-  uint32_t key[kRegPer];  // key[4v + u]; 0 = not a candidate
+  uint32_t key[kPer];  // key[4v + u]; 0 = not a candidate
+  int32_t cid[kPrefetch ? kPer : 1];
   auto to_key = [](float x) { return __float_as_uint(x) != kNoScoreBits ? score_key(x) : 0u; };
   if (len >= 4 && ((Ns | off | len) & 3) == 0) {
 #pragma unroll
@@ -348,20 +357,26 @@ __global__ __launch_bounds__(kRegThreads) void topk_reg_kernel(const float *__re
       key[4 * v + 1] = to_key(t4.y);
       key[4 * v + 2] = to_key(t4.z);
       key[4 * v + 3] = to_key(t4.w);
+      if constexpr (kPrefetch) {
+        const int4 c4 = *reinterpret_cast<const int4 *>(csrc + i0);
+        cid[4 * v + 0] = c4.x;
+        cid[4 * v + 1] = c4.y;
+        cid[4 * v + 2] = c4.z;
+        cid[4 * v + 3] = c4.w;
+      }
     }
   } else {
 #pragma unroll
-    for (int j = 0; j < kRegPer; ++j)
-      key[j] = len > 0 ? to_key(src[min((j >> 2) * kSlice + 4 * tid + (j & 3), len - 1)]) : 0u;
+    for (int j = 0; j < kPer; ++j) {
+      const int i = min((j >> 2) * kSlice + 4 * tid + (j & 3), len - 1);
+      key[j] = len > 0 ? to_key(src[i]) : 0u;
+      if constexpr (kPrefetch) cid[j] = len > 0 ? csrc[i] : -1;
+    }
   }
   for (int i = tid; i < kBins; i += NT) hist[0][i] = 0;
-  if (tid == 0) {
-    red_max = 0u;
-    red_cnt = 0;
-    n_bin = 0;
-  }
+  if (tid == 0) n_bin = 0;
   int n;
-  if (cand) {
+  if (kCand) {
     n = C;
   } else {
     const int nE = min(n_entries[b], N_cap);
@@ -369,31 +384,35 @@ __global__ __launch_bounds__(kRegThreads) void topk_reg_kernel(const float *__re
   }
   n = max(0, min(n - off, len));            // elements of this slice
 #pragma unroll
-  for (int j = 0; j < kRegPer; ++j)
+  for (int j = 0; j < kPer; ++j)
     if ((j >> 2) * kSlice + 4 * tid + (j & 3) >= n) key[j] = 0u;
 
   // 1. maximum and valid count
+  {
+    uint32_t mx = 0;
+    int nv = 0;
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      mx = key[j] > mx ? key[j] : mx;
+      nv += key[j] != 0u;
+    }
+    mx = wave_max_u32(mx);
+    nv = wave_sum(nv);
+    if (lane == 0) {
+      wmax[wave] = mx;
+      wcnt[wave] = nv;
+    }
+  }
+  __syncthreads();
   uint32_t mx = 0;
-  int nv = 0;
+  int n_valid = 0;
 #pragma unroll
-  for (int j = 0; j < kRegPer; ++j) {
-    mx = key[j] > mx ? key[j] : mx;
-    nv += key[j] != 0u;
+  for (int w = 0; w < kW; ++w) {
+    mx = max(mx, wmax[w]);
+    n_valid += wcnt[w];
   }
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    const uint32_t t = __shfl_xor(mx, o);
-    mx = t > mx ? t : mx;
-    nv += __shfl_xor(nv, o);
-  }
-  __syncthreads();
-  if (lane == 0) {
-    atomicMax(&red_max, mx);
-    atomicAdd(&red_cnt, nv);
-  }
-  __syncthreads();
-  mx = red_max;
-  const int n_valid = red_cnt;
+  mx = __builtin_amdgcn_readfirstlane(mx);
+  n_valid = __builtin_amdgcn_readfirstlane(n_valid);
   const int k_eff = min(k, n_valid);
 
   uint32_t thr = 0;   // full key of the k_eff-th largest element
@@ -401,96 +420,109 @@ __global__ __launch_bounds__(kRegThreads) void topk_reg_kernel(const float *__re
   if (k_eff > 0 && k_eff < n_valid) {
     constexpr int kRelShift = 14;
 #pragma unroll
-    for (int j = 0; j < kRegPer; ++j) {
+    for (int j = 0; j < kPer; ++j) {
       const uint32_t d = (mx - key[j]) >> kRelShift;
       if (key[j] != 0u && d < (uint32_t)(kBins - 1)) atomicAdd(&hist[0][kBins - 2 - d], 1);
     }
     __syncthreads();
-    int d1, above;
-    find_digit<NT>(hist, 1, kBins, k_eff, sh, d1, above);
-    const int in_window = sh[kW];             // total of the histogram (written by the digit search)
-    const int c1 = in_window >= k_eff ? hist[0][d1] : 0;  // d1 is only defined then
+    int d1, above, in_window;
+    find_digit<NT>(hist, 1, kBins, k_eff, sh, d1, above, in_window);
+    const int c1 = in_window >= k_eff ? __builtin_amdgcn_readfirstlane(hist[0][d1]) : 0;  // d1 is defined then
     if (in_window >= k_eff && c1 <= 64) {
-      // 3a. rank the few elements of the threshold bin in one wave
+      // 3a. gather the threshold bin and rank its few elements
       const uint32_t dhi = (uint32_t)(kBins - 2 - d1);
+      int mine = 0;
 #pragma unroll
-      for (int j = 0; j < kRegPer; ++j)
-        if (key[j] != 0u && ((mx - key[j]) >> kRelShift) == dhi) bin_keys[atomicAdd(&n_bin, 1)] = key[j];
+      for (int j = 0; j < kPer; ++j) mine += key[j] != 0u && ((mx - key[j]) >> kRelShift) == dhi;
+      const int inc = wave_incl_scan(mine);
+      const int wtot = __builtin_amdgcn_readlane(inc, 63);
+      int base = 0;
+      if (wtot > 0) {
+        if (lane == 63) base = atomicAdd(&n_bin, wtot);
+        base = __builtin_amdgcn_readlane(base, 63);
+      }
+      int pos = base + inc - mine;
+#pragma unroll
+      for (int j = 0; j < kPer; ++j)
+        if (key[j] != 0u && ((mx - key[j]) >> kRelShift) == dhi) bin_keys[pos++] = key[j];
       __syncthreads();
+      const int k_rem = k_eff - above;
+      // wave 0 ranks the gathered keys (lanes past c1 take no part) and
+      // publishes the threshold
       if (wave == 0) {
-        const int k_rem = k_eff - above;
         const uint32_t kl = lane < c1 ? bin_keys[lane] : 0u;
         int gt = 0, ge = 0;
         for (int j = 0; j < c1; ++j) {
-          const uint32_t kj = bin_keys[j];
+          const uint32_t kj = (uint32_t)__builtin_amdgcn_readlane((int)kl, j);
           gt += kj > kl;
           ge += kj >= kl;
         }
         if (lane < c1 && gt < k_rem && k_rem <= ge) {  // every lane holding the threshold key agrees
-          sel_thr = kl;
-          sel_need = k_rem - gt;
+          sh[kW] = (int)kl;
+          sh[kW + 1] = k_rem - gt;
         }
       }
       __syncthreads();
-      thr = sel_thr;
-      need = sel_need;
+      thr = (uint32_t)__builtin_amdgcn_readfirstlane(sh[kW]);
+      need = __builtin_amdgcn_readfirstlane(sh[kW + 1]);
     } else if (in_window >= k_eff) {
       // 3b. radix passes over the remaining 14 distance bits (7 + 7)
-      int k_rem = k_eff - above;
+      int k_rem = k_eff - above, tot;
       const uint32_t dhi = (uint32_t)(kBins - 2 - d1);
       for (int i = tid; i < kBins; i += NT) hist[0][i] = 0;
       __syncthreads();
 #pragma unroll
-      for (int j = 0; j < kRegPer; ++j) {
+      for (int j = 0; j < kPer; ++j) {
         const uint32_t dist = mx - key[j];
         if (key[j] != 0u && (dist >> kRelShift) == dhi) atomicAdd(&hist[0][127 - ((dist >> 7) & 127u)], 1);
       }
       __syncthreads();
       int d2;
-      find_digit<NT>(hist, 1, 128, k_rem, sh, d2, above);
+      find_digit<NT>(hist, 1, 128, k_rem, sh, d2, above, tot);
       k_rem -= above;
       const uint32_t dmid = (dhi << 7) | (uint32_t)(127 - d2);
       for (int i = tid; i < 128; i += NT) hist[0][i] = 0;
       __syncthreads();
 #pragma unroll
-      for (int j = 0; j < kRegPer; ++j) {
+      for (int j = 0; j < kPer; ++j) {
         const uint32_t dist = mx - key[j];
         if (key[j] != 0u && (dist >> 7) == dmid) atomicAdd(&hist[0][127 - (dist & 127u)], 1);
       }
       __syncthreads();
       int d3;
-      find_digit<NT>(hist, 1, 128, k_rem, sh, d3, above);
+      find_digit<NT>(hist, 1, 128, k_rem, sh, d3, above, tot);
       k_rem -= above;
       thr = mx - ((dmid << 7) | (uint32_t)(127 - d3));
       need = k_rem;
     } else {
       // 3c. full-range passes: bits 31..21 (per-wave histograms), 20..10, 9..0
+      int tot;
       for (int i = tid; i < kW * kBins; i += NT) (&hist[0][0])[i] = 0;
       __syncthreads();
 #pragma unroll
-      for (int j = 0; j < kRegPer; ++j) atomicAdd(&hist[wave][key[j] >> 21], 1);
+      for (int j = 0; j < kPer; ++j) atomicAdd(&hist[wave][key[j] >> 21], 1);
       __syncthreads();
       int e1, ab;
-      find_digit<NT>(hist, kW, kBins, k_eff, sh, e1, ab);
+      find_digit<NT>(hist, kW, kBins, k_eff, sh, e1, ab, tot);
       int k_rem = k_eff - ab;
       for (int i = tid; i < kBins; i += NT) hist[0][i] = 0;
       __syncthreads();
 #pragma unroll
-      for (int j = 0; j < kRegPer; ++j)
+      for (int j = 0; j < kPer; ++j)
         if ((key[j] >> 21) == (uint32_t)e1) atomicAdd(&hist[0][(key[j] >> 10) & 0x7FFu], 1);
       __syncthreads();
       int e2;
-      find_digit<NT>(hist, 1, kBins, k_rem, sh, e2, ab);
+      find_digit<NT>(hist, 1, kBins, k_rem, sh, e2, ab, tot);
       k_rem -= ab;
       const uint32_t p12 = ((uint32_t)e1 << 11) | (uint32_t)e2;
       for (int i = tid; i < kBins; i += NT) hist[0][i] = 0;
       __syncthreads();
 #pragma unroll
-      for (int j = 0; j < kRegPer; ++j)
+      for (int j = 0; j < kPer; ++j)
         if ((key[j] >> 10) == p12) atomicAdd(&hist[0][key[j] & 0x3FFu], 1);
       __syncthreads();
       int e3;
-      find_digit<NT>(hist, 1, 1024, k_rem, sh, e3, ab);
+      find_digit<NT>(hist, 1, 1024, k_rem, sh, e3, ab, tot);
       k_rem -= ab;
       thr = (p12 << 10) | (uint32_t)e3;
       need = k_rem;
@@ -501,6 +533,12 @@ __global__ __launch_bounds__(kRegThreads) void topk_reg_kernel(const float *__re
   const int64_t orow = row * nsl + sl;
   int32_t *out_i = idx_out + orow * k;
   float *out_s = score_out ? score_out + orow * k : nullptr;
+  // Up to kStage selections are placed in LDS (over the histograms, whose
+  // last reads precede the barrier below) and written out coalesced.
+  constexpr int kStage = kW * kBins / 2;
+  const bool staged = k_eff <= kStage;
+  int32_t *st_i = &hist[0][0];
+  float *st_s = reinterpret_cast<float *>(&hist[0][0] + kStage);
   if (k_eff > 0) {
     const uint64_t below = lane ? (~0ull >> (64 - lane)) : 0ull;
 #pragma unroll
@@ -517,33 +555,29 @@ __global__ __launch_bounds__(kRegThreads) void topk_reg_kernel(const float *__re
       }
     }
     __syncthreads();
-    if (wave == 0) {
-      // exclusive prefix over (slice, wave) in v-major order; two entries per lane
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const int e0 = 2 * lane, e1 = 2 * lane + 1;
-        const int a0 = e0 < kV * kW ? cnt[t][e0] : 0, a1 = e1 < kV * kW ? cnt[t][e1] : 0;
-        int inc = a0 + a1;
-#pragma unroll
-        for (int o = 1; o < 64; o <<= 1) {
-          const int x = __shfl_up(inc, o);
-          if (lane >= o) inc += x;
-        }
-        const int ex = inc - a0 - a1;
-        if (e0 < kV * kW) cnt[t][e0] = ex;
-        if (e1 < kV * kW) cnt[t][e1] = ex + a0;
-      }
+    // every wave scans the counts in (slice, wave) order, two per lane
+    int gx[2], ex[2];
+    {
+      const int e0 = 2 * lane, e1 = 2 * lane + 1;
+      const int g0 = e0 < kE ? cnt[0][e0] : 0, g1 = e1 < kE ? cnt[0][e1] : 0;
+      const int q0 = e0 < kE ? cnt[1][e0] : 0, q1 = e1 < kE ? cnt[1][e1] : 0;
+      const int gi = wave_incl_scan(g0 + g1), qi = wave_incl_scan(q0 + q1);
+      gx[0] = gi - g0 - g1;
+      gx[1] = gi - g1;
+      ex[0] = qi - q0 - q1;
+      ex[1] = qi - q1;
     }
-    __syncthreads();
 #pragma unroll
     for (int v = 0; v < kV; ++v) {
+      const int e = v * kW + wave;
+      int gb = (e & 1) ? __builtin_amdgcn_readlane(gx[1], e >> 1) : __builtin_amdgcn_readlane(gx[0], e >> 1);
+      int eb = (e & 1) ? __builtin_amdgcn_readlane(ex[1], e >> 1) : __builtin_amdgcn_readlane(ex[0], e >> 1);
       uint64_t gm[4], em[4];
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         gm[u] = __ballot(key[4 * v + u] > thr);
         em[u] = __ballot(need > 0 && key[4 * v + u] == thr);
       }
-      int gb = cnt[0][v * kW + wave], eb = cnt[1][v * kW + wave];
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         gb += __popcll(gm[u] & below);
@@ -554,11 +588,19 @@ __global__ __launch_bounds__(kRegThreads) void topk_reg_kernel(const float *__re
         const uint32_t kk = key[4 * v + u];
         const bool is_gt = kk > thr, is_eq = need > 0 && kk == thr;
         if (is_gt || (is_eq && eb < need)) {
-          const int pos = gb + min(eb, need);
-          if (pos < k_eff) {
+          const int p = gb + min(eb, need);
+          if (p < k_eff) {
             const int i = v * kSlice + 4 * tid + u;
-            out_i[pos] = cand ? cand[row * C + i] : off + i;
-            if (out_s) out_s[pos] = key_score(kk);
+            int32_t id;
+            if constexpr (kPrefetch) id = cid[4 * v + u];
+            else id = kCand ? csrc[i] : off + i;
+            if (staged) {
+              st_i[p] = id;
+              st_s[p] = key_score(kk);
+            } else {
+              out_i[p] = id;
+              if (out_s) out_s[p] = key_score(kk);
+            }
           }
         }
         gb += is_gt;
@@ -566,9 +608,18 @@ __global__ __launch_bounds__(kRegThreads) void topk_reg_kernel(const float *__re
       }
     }
   }
-  for (int j = k_eff + tid; j < k; j += NT) {
-    out_i[j] = -1;
-    if (out_s) out_s[j] = __uint_as_float(kNoScoreBits);  // a NaN
+  if (staged) {
+    __syncthreads();
+    for (int j = tid; j < k; j += NT) {
+      const bool sel = j < k_eff;
+      out_i[j] = sel ? st_i[j] : -1;
+      if (out_s) out_s[j] = sel ? st_s[j] : __uint_as_float(kNoScoreBits);  // a NaN marks an empty slot
+    }
+  } else {
+    for (int j = k_eff + tid; j < k; j += NT) {
+      out_i[j] = -1;
+      if (out_s) out_s[j] = __uint_as_float(kNoScoreBits);
+    }
   }
 }
 
@@ -596,8 +647,12 @@ template <int kPer>
 static void launch_reg(dim3 grid, hipStream_t stream, const float *scores, int Ns, const CacheView &c,
                        const int32_t *q_pos, int Q, const int32_t *cand, int C, int k, int32_t *idx_out,
                        float *score_out, int nsl, int S) {
-  topk_reg_kernel<kPer><<<grid, kRegThreads, 0, stream>>>(scores, Ns, c.n_entries, c.N_cap, c.m, q_pos, Q, cand, C, k,
-                                                         idx_out, score_out, nsl, S);
+  if (cand)
+    topk_reg_kernel<kPer, true><<<grid, kRegThreads, 0, stream>>>(scores, Ns, c.n_entries, c.N_cap, c.m, q_pos, Q,
+                                                                  cand, C, k, idx_out, score_out, nsl, S);
+  else
+    topk_reg_kernel<kPer, false><<<grid, kRegThreads, 0, stream>>>(scores, Ns, c.n_entries, c.N_cap, c.m, q_pos, Q,
+                                                                   nullptr, 0, k, idx_out, score_out, nsl, S);
 }
 
 static void launch_one(const CacheView &c, const float *scores, int Ns, int len, const int32_t *q_pos, int Q,

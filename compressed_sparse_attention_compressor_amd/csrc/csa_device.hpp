@@ -133,8 +133,9 @@ __device__ __forceinline__ float row16_sum(float v) {
 }
 
 // Order-preserving map of an fp32 score to uint32 (larger score, larger key).
+// -0 and +0 are the same number and get the same key (that of +0).
 __device__ __forceinline__ uint32_t score_key(float s) {
-  uint32_t u = __float_as_uint(s);
+  const uint32_t u = s == 0.f ? 0u : __float_as_uint(s);
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 __device__ __forceinline__ float key_score(uint32_t k) {

@@ -327,8 +327,8 @@ __global__ __launch_bounds__(kRegThreads) void topk_reg_kernel(const float *__re
   constexpr bool kPrefetch = kCand && kPer <= 32;  // candidate ids loaded with the scores
   static_assert(kE <= 128, "a wave scans the (slice, wave) counts two per lane");
   __shared__ int hist[kW][kBins];
-  __shared__ int sh[kW + 2];
-  __shared__ uint32_t wmax[kW];
+  __shared__ int sh[kW + 3];
+  __shared__ uint32_t wmax[kW], wmin[kW];
   __shared__ int wcnt[kW];
   __shared__ uint32_t bin_keys[64];
   __shared__ int cnt[2][kE];                // per (slice, wave): elements > T, elements == T
@@ -387,53 +387,67 @@ __global__ __launch_bounds__(kRegThreads) void topk_reg_kernel(const float *__re
   for (int j = 0; j < kPer; ++j)
     if ((j >> 2) * kSlice + 4 * tid + (j & 3) >= n) key[j] = 0u;
 
-  // 1. maximum and valid count
+  // 1. maximum, minimum and count of the valid keys
   {
-    uint32_t mx = 0;
+    uint32_t mx = 0, mnc = 0;  // mnc: complement of the minimum
     int nv = 0;
 #pragma unroll
     for (int j = 0; j < kPer; ++j) {
       mx = key[j] > mx ? key[j] : mx;
+      const uint32_t c = key[j] ? ~key[j] : 0u;
+      mnc = c > mnc ? c : mnc;
       nv += key[j] != 0u;
     }
     mx = wave_max_u32(mx);
+    mnc = wave_max_u32(mnc);
     nv = wave_sum(nv);
     if (lane == 0) {
       wmax[wave] = mx;
+      wmin[wave] = mnc;
       wcnt[wave] = nv;
     }
   }
   __syncthreads();
-  uint32_t mx = 0;
+  uint32_t mx = 0, mnc = 0;
   int n_valid = 0;
 #pragma unroll
   for (int w = 0; w < kW; ++w) {
     mx = max(mx, wmax[w]);
+    mnc = max(mnc, wmin[w]);
     n_valid += wcnt[w];
   }
   mx = __builtin_amdgcn_readfirstlane(mx);
+  mnc = __builtin_amdgcn_readfirstlane(mnc);
   n_valid = __builtin_amdgcn_readfirstlane(n_valid);
   const int k_eff = min(k, n_valid);
 
-  uint32_t thr = 0;   // full key of the k_eff-th largest element
+  // Linear bins in score space between the extremes: bin(v) = (vmax - v) * inv
+  // is non-increasing in v (each rounding step is monotone), so keys in a
+  // lower bin are strictly larger than keys in a higher one; the exact order
+  // inside the threshold bin is settled on the keys themselves.
+  const float vmax = key_score(mx), vmin = key_score(~mnc);
+  float inv = (float)(kBins - 2) / (vmax - vmin);
+  if (!(inv < INFINITY)) inv = 0.f;  // equal extremes, or a span beyond fp32
+  auto bin_of = [&](uint32_t kk) { return (uint32_t)fminf((vmax - key_score(kk)) * inv, (float)(kBins - 2)); };
+
+  uint32_t thr = 1u;  // full key of the k_eff-th largest element (1: every valid key)
   int need = 0;       // elements equal to thr that are taken
+  int n_eq = 0;       // elements equal to thr
   if (k_eff > 0 && k_eff < n_valid) {
-    constexpr int kRelShift = 14;
 #pragma unroll
-    for (int j = 0; j < kPer; ++j) {
-      const uint32_t d = (mx - key[j]) >> kRelShift;
-      if (key[j] != 0u && d < (uint32_t)(kBins - 1)) atomicAdd(&hist[0][kBins - 2 - d], 1);
-    }
+    for (int j = 0; j < kPer; ++j)
+      if (key[j] != 0u) atomicAdd(&hist[0][kBins - 2 - bin_of(key[j])], 1);
     __syncthreads();
-    int d1, above, in_window;
-    find_digit<NT>(hist, 1, kBins, k_eff, sh, d1, above, in_window);
-    const int c1 = in_window >= k_eff ? __builtin_amdgcn_readfirstlane(hist[0][d1]) : 0;  // d1 is defined then
-    if (in_window >= k_eff && c1 <= 64) {
-      // 3a. gather the threshold bin and rank its few elements
-      const uint32_t dhi = (uint32_t)(kBins - 2 - d1);
+    int d1, above, tot;
+    find_digit<NT>(hist, 1, kBins, k_eff, sh, d1, above, tot);
+    const int c1 = __builtin_amdgcn_readfirstlane(hist[0][d1]);
+    const uint32_t dhi = (uint32_t)(kBins - 2 - d1);
+    int k_rem = k_eff - above;
+    if (c1 <= 64) {
+      // 2a. gather the threshold bin (one LDS atomic per wave) and rank it
       int mine = 0;
 #pragma unroll
-      for (int j = 0; j < kPer; ++j) mine += key[j] != 0u && ((mx - key[j]) >> kRelShift) == dhi;
+      for (int j = 0; j < kPer; ++j) mine += key[j] != 0u && bin_of(key[j]) == dhi;
       const int inc = wave_incl_scan(mine);
       const int wtot = __builtin_amdgcn_readlane(inc, 63);
       int base = 0;
@@ -444,9 +458,8 @@ __global__ __launch_bounds__(kRegThreads) void topk_reg_kernel(const float *__re
       int pos = base + inc - mine;
 #pragma unroll
       for (int j = 0; j < kPer; ++j)
-        if (key[j] != 0u && ((mx - key[j]) >> kRelShift) == dhi) bin_keys[pos++] = key[j];
+        if (key[j] != 0u && bin_of(key[j]) == dhi) bin_keys[pos++] = key[j];
       __syncthreads();
-      const int k_rem = k_eff - above;
       // wave 0 ranks the gathered keys (lanes past c1 take no part) and
       // publishes the threshold
       if (wave == 0) {
@@ -460,56 +473,31 @@ __global__ __launch_bounds__(kRegThreads) void topk_reg_kernel(const float *__re
         if (lane < c1 && gt < k_rem && k_rem <= ge) {  // every lane holding the threshold key agrees
           sh[kW] = (int)kl;
           sh[kW + 1] = k_rem - gt;
+          sh[kW + 2] = ge - gt;
         }
       }
       __syncthreads();
       thr = (uint32_t)__builtin_amdgcn_readfirstlane(sh[kW]);
       need = __builtin_amdgcn_readfirstlane(sh[kW + 1]);
-    } else if (in_window >= k_eff) {
-      // 3b. radix passes over the remaining 14 distance bits (7 + 7)
-      int k_rem = k_eff - above, tot;
-      const uint32_t dhi = (uint32_t)(kBins - 2 - d1);
-      for (int i = tid; i < kBins; i += NT) hist[0][i] = 0;
-      __syncthreads();
-#pragma unroll
-      for (int j = 0; j < kPer; ++j) {
-        const uint32_t dist = mx - key[j];
-        if (key[j] != 0u && (dist >> kRelShift) == dhi) atomicAdd(&hist[0][127 - ((dist >> 7) & 127u)], 1);
-      }
-      __syncthreads();
-      int d2;
-      find_digit<NT>(hist, 1, 128, k_rem, sh, d2, above, tot);
-      k_rem -= above;
-      const uint32_t dmid = (dhi << 7) | (uint32_t)(127 - d2);
-      for (int i = tid; i < 128; i += NT) hist[0][i] = 0;
-      __syncthreads();
-#pragma unroll
-      for (int j = 0; j < kPer; ++j) {
-        const uint32_t dist = mx - key[j];
-        if (key[j] != 0u && (dist >> 7) == dmid) atomicAdd(&hist[0][127 - (dist & 127u)], 1);
-      }
-      __syncthreads();
-      int d3;
-      find_digit<NT>(hist, 1, 128, k_rem, sh, d3, above, tot);
-      k_rem -= above;
-      thr = mx - ((dmid << 7) | (uint32_t)(127 - d3));
-      need = k_rem;
+      n_eq = __builtin_amdgcn_readfirstlane(sh[kW + 2]);
     } else {
-      // 3c. full-range passes: bits 31..21 (per-wave histograms), 20..10, 9..0
-      int tot;
-      for (int i = tid; i < kW * kBins; i += NT) (&hist[0][0])[i] = 0;
-      __syncthreads();
-#pragma unroll
-      for (int j = 0; j < kPer; ++j) atomicAdd(&hist[wave][key[j] >> 21], 1);
-      __syncthreads();
-      int e1, ab;
-      find_digit<NT>(hist, kW, kBins, k_eff, sh, e1, ab, tot);
-      int k_rem = k_eff - ab;
+      // 2b. a crowded bin (many equal or nearly equal scores): radix passes
+      //     over the keys of that bin, bits 31..21, 20..10 and 9..0
       for (int i = tid; i < kBins; i += NT) hist[0][i] = 0;
       __syncthreads();
 #pragma unroll
       for (int j = 0; j < kPer; ++j)
-        if ((key[j] >> 21) == (uint32_t)e1) atomicAdd(&hist[0][(key[j] >> 10) & 0x7FFu], 1);
+        if (key[j] != 0u && bin_of(key[j]) == dhi) atomicAdd(&hist[0][key[j] >> 21], 1);
+      __syncthreads();
+      int e1, ab;
+      find_digit<NT>(hist, 1, kBins, k_rem, sh, e1, ab, tot);
+      k_rem -= ab;
+      for (int i = tid; i < kBins; i += NT) hist[0][i] = 0;
+      __syncthreads();
+#pragma unroll
+      for (int j = 0; j < kPer; ++j)
+        if (key[j] != 0u && bin_of(key[j]) == dhi && (key[j] >> 21) == (uint32_t)e1)
+          atomicAdd(&hist[0][(key[j] >> 10) & 0x7FFu], 1);
       __syncthreads();
       int e2;
       find_digit<NT>(hist, 1, kBins, k_rem, sh, e2, ab, tot);
@@ -519,17 +507,20 @@ __global__ __launch_bounds__(kRegThreads) void topk_reg_kernel(const float *__re
       __syncthreads();
 #pragma unroll
       for (int j = 0; j < kPer; ++j)
-        if ((key[j] >> 10) == p12) atomicAdd(&hist[0][key[j] & 0x3FFu], 1);
+        if (key[j] != 0u && bin_of(key[j]) == dhi && (key[j] >> 10) == p12) atomicAdd(&hist[0][key[j] & 0x3FFu], 1);
       __syncthreads();
       int e3;
       find_digit<NT>(hist, 1, 1024, k_rem, sh, e3, ab, tot);
       k_rem -= ab;
       thr = (p12 << 10) | (uint32_t)e3;
       need = k_rem;
+      n_eq = __builtin_amdgcn_readfirstlane(hist[0][e3]);  // every key equal to thr lies in this bin
     }
   }
 
-  // 4. placement in ascending entry order
+  // 3. placement in ascending entry order.  When every element equal to the
+  // threshold is taken the selection is simply key >= thr; otherwise the
+  // elements above it and the first `need` equal ones (by entry) are taken.
   const int64_t orow = row * nsl + sl;
   int32_t *out_i = idx_out + orow * k;
   float *out_s = score_out ? score_out + orow * k : nullptr;
@@ -540,14 +531,17 @@ __global__ __launch_bounds__(kRegThreads) void topk_reg_kernel(const float *__re
   int32_t *st_i = &hist[0][0];
   float *st_s = reinterpret_cast<float *>(&hist[0][0] + kStage);
   if (k_eff > 0) {
+    const bool simple = need == n_eq;
+    // taken outright: key >= thr when simple, key > thr otherwise
+    auto sure = [&](uint32_t kk) { return simple ? kk >= thr : kk > thr; };
     const uint64_t below = lane ? (~0ull >> (64 - lane)) : 0ull;
 #pragma unroll
     for (int v = 0; v < kV; ++v) {
       int gc = 0, ec = 0;
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        gc += __popcll(__ballot(key[4 * v + u] > thr));
-        ec += __popcll(__ballot(need > 0 && key[4 * v + u] == thr));
+        gc += __popcll(__ballot(sure(key[4 * v + u])));
+        if (!simple) ec += __popcll(__ballot(key[4 * v + u] == thr));
       }
       if (lane == 0) {
         cnt[0][v * kW + wave] = gc;
@@ -556,37 +550,35 @@ __global__ __launch_bounds__(kRegThreads) void topk_reg_kernel(const float *__re
     }
     __syncthreads();
     // every wave scans the counts in (slice, wave) order, two per lane
-    int gx[2], ex[2];
+    int gx[2], ex[2] = {0, 0};
     {
       const int e0 = 2 * lane, e1 = 2 * lane + 1;
       const int g0 = e0 < kE ? cnt[0][e0] : 0, g1 = e1 < kE ? cnt[0][e1] : 0;
-      const int q0 = e0 < kE ? cnt[1][e0] : 0, q1 = e1 < kE ? cnt[1][e1] : 0;
-      const int gi = wave_incl_scan(g0 + g1), qi = wave_incl_scan(q0 + q1);
+      const int gi = wave_incl_scan(g0 + g1);
       gx[0] = gi - g0 - g1;
       gx[1] = gi - g1;
-      ex[0] = qi - q0 - q1;
-      ex[1] = qi - q1;
+      if (!simple) {
+        const int q0 = e0 < kE ? cnt[1][e0] : 0, q1 = e1 < kE ? cnt[1][e1] : 0;
+        const int qi = wave_incl_scan(q0 + q1);
+        ex[0] = qi - q0 - q1;
+        ex[1] = qi - q1;
+      }
     }
 #pragma unroll
     for (int v = 0; v < kV; ++v) {
       const int e = v * kW + wave;
       int gb = (e & 1) ? __builtin_amdgcn_readlane(gx[1], e >> 1) : __builtin_amdgcn_readlane(gx[0], e >> 1);
-      int eb = (e & 1) ? __builtin_amdgcn_readlane(ex[1], e >> 1) : __builtin_amdgcn_readlane(ex[0], e >> 1);
-      uint64_t gm[4], em[4];
+      int eb = 0;
+      if (!simple) eb = (e & 1) ? __builtin_amdgcn_readlane(ex[1], e >> 1) : __builtin_amdgcn_readlane(ex[0], e >> 1);
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        gm[u] = __ballot(key[4 * v + u] > thr);
-        em[u] = __ballot(need > 0 && key[4 * v + u] == thr);
-      }
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        gb += __popcll(gm[u] & below);
-        eb += __popcll(em[u] & below);
+        gb += __popcll(__ballot(sure(key[4 * v + u])) & below);
+        if (!simple) eb += __popcll(__ballot(key[4 * v + u] == thr) & below);
       }
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const uint32_t kk = key[4 * v + u];
-        const bool is_gt = kk > thr, is_eq = need > 0 && kk == thr;
+        const bool is_gt = sure(kk), is_eq = !simple && kk == thr;
         if (is_gt || (is_eq && eb < need)) {
           const int p = gb + min(eb, need);
           if (p < k_eff) {

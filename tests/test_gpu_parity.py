@@ -401,6 +401,8 @@ TOPK_CASES = [
     ("two-stage-k-over-slice", 1, 1, 32768, [32768], 5000, 0.05),
     ("single-stage-ragged", 3, 2, 1003, [1003, 999, 17], 64, 0.5),
     ("tiled-long-row", 1, 1, 70001, [70001], 777, 0.1),
+    ("sign-crossing", 2, 1, 8192, [8192, 6000], 5000, 0.001),   # the k-th score is negative
+    ("all-equal", 1, 2, 3000, [3000, 2500], 100, 1e9),         # every score rounds to 0
 ]
 
 

@@ -276,7 +276,7 @@ def main():
     print(json.dumps(result), flush=True)
 
 
-def cpu_baseline(w, nseq):
+def cpu_baseline(w, nseq, min_seconds=10.0):
     """The float64 oracle on `nseq` sequences of the same decode step (host cores)."""
     import numpy as np
 
@@ -292,19 +292,24 @@ def cpu_baseline(w, nseq):
     qs = queries(w)
     planes = synthetic_cache(w, nseq=nseq)
     x, z = raw_rows(w, w.T - max(w.n_win, w.m), w.T, nseq=nseq)
-    t0 = time.perf_counter()
     p = w.T - 1
-    for b in range(nseq):
-        O.compress(as_u16(x[b, -w.m:]), as_u16(z[b, -w.m:]), bias.numpy(), as_u16(wik), w.m)
-        ik, isc = planes["ikey"][b].numpy(), planes["iscale"][b].numpy()
-        idx, _, _, _ = O.index_topk(ik, isc, qs["qI"][b, 0].numpy(), qs["w"][b, 0].numpy(), p, w.m, w.N, w.k)
-        O.sparse_attention(as_u16(qs["q"][b, 0]), planes["nope"][b].numpy(), planes["nscale"][b].numpy(),
-                           as_u16(planes["rope"][b]), idx, as_u16(x[b, -w.n_win:]), w.T - w.n_win, p, w.n_win,
-                           w.softmax_scale, w.m, w.N)
+    done, passes = 0, 0
+    t0 = time.perf_counter()
+    # whole passes over the sample until about min_seconds of CPU work
+    while passes == 0 or time.perf_counter() - t0 < min_seconds:
+        for b in range(nseq):
+            O.compress(as_u16(x[b, -w.m:]), as_u16(z[b, -w.m:]), bias.numpy(), as_u16(wik), w.m)
+            ik, isc = planes["ikey"][b].numpy(), planes["iscale"][b].numpy()
+            idx, _, _, _ = O.index_topk(ik, isc, qs["qI"][b, 0].numpy(), qs["w"][b, 0].numpy(), p, w.m, w.N, w.k)
+            O.sparse_attention(as_u16(qs["q"][b, 0]), planes["nope"][b].numpy(), planes["nscale"][b].numpy(),
+                               as_u16(planes["rope"][b]), idx, as_u16(x[b, -w.n_win:]), w.T - w.n_win, p, w.n_win,
+                               w.softmax_scale, w.m, w.N)
+            done += 1
+        passes += 1
     dt = time.perf_counter() - t0
-    return {"value": round(nseq / dt, 3), "unit": "query-tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{nseq} of {w.B} sequences of one decode step (compress block, index {w.N} entries, "
-                      f"top-{w.k}, attention), {dt:.2f} s"}
+    return {"value": round(done / dt, 3), "unit": "query-tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{passes} passes over {nseq} of {w.B} sequences of one decode step (compress block, index "
+                      f"{w.N} entries, top-{w.k}, attention): {done} query tokens in {dt:.2f} s"}
 
 
 if __name__ == "__main__":

@@ -111,7 +111,7 @@ size_t csa_workspace_bytes(int op, int B, int Q, int H_or_k, int n, int C) {
       return align256(index_ws_bytes(B, Q, n, C)) + topk_ws_bytes(B, Q, C > 0 ? C : n, H_or_k, C > 0);
     case CSA_WS_TOPK: return topk_ws_bytes(B, Q, n, H_or_k, false);
     case CSA_WS_SPARSE_ATTN:
-    case CSA_WS_DENSE_ATTN: return csa::attn_workspace_bytes(B, Q, H_or_k, n + (C > 0 ? C : 0));
+    case CSA_WS_DENSE_ATTN: return csa::attn_workspace_bytes(B, Q, H_or_k, n, C > 0 ? C : 0);
     default: return 0;
   }
 }
@@ -217,7 +217,7 @@ int csa_sparse_attn(const csa_cache_t *cache, const uint16_t *q, int H, const in
   if (k > 0 && !idx) return CSA_ERR_NULL;
   if (k > kMaxK) return CSA_ERR_UNSUPPORTED;
   if (Q == 0 || cache->B == 0) return CSA_OK;
-  const size_t need = csa::attn_workspace_bytes(cache->B, Q, H, k + n_win);
+  const size_t need = csa::attn_workspace_bytes(cache->B, Q, H, k, n_win);
   if (need > 0 && !ws) return CSA_ERR_NULL;
   if (ws_bytes < need) return CSA_ERR_WORKSPACE;
   if (need > 0 && !aligned16(ws)) return CSA_ERR_ALIGN;
@@ -232,7 +232,7 @@ int hca_dense_attn(const csa_cache_t *cache, const uint16_t *q, int H, const int
   int st = check_attn_common(cache, q, H, q_pos, Q, swa, swa_pos0, S, n_win, softmax_scale, out_dtype, out);
   if (st) return st;
   if (Q == 0 || cache->B == 0) return CSA_OK;
-  const size_t need = csa::attn_workspace_bytes(cache->B, Q, H, cache->N_cap + n_win);
+  const size_t need = csa::attn_workspace_bytes(cache->B, Q, H, cache->N_cap, n_win);
   if (need > 0 && !ws) return CSA_ERR_NULL;
   if (ws_bytes < need) return CSA_ERR_WORKSPACE;
   if (need > 0 && !aligned16(ws)) return CSA_ERR_ALIGN;

@@ -6,24 +6,33 @@
 // window).  One softmax runs over the union of the two key sets; the key
 // and the value are the same decoded 576-channel row.
 //
-// Work split: one workgroup per (query, key-range split), one wave per 16
-// query heads (heads are the MFMA M dimension, so every key is decoded once
-// per workgroup and shared by all heads).  Per chunk of 32 key slots:
-//   1. the slot list is resolved (selected entry, window row, or nothing);
-//   2. the workgroup decodes the 32 rows into a key-major bf16 LDS tile
+// Work split: one workgroup per (query, key-range split), a pair of waves
+// per 16 query heads (heads are the MFMA M dimension, so a key is decoded
+// once per workgroup and shared by every head); each wave of a pair owns
+// half of the 576 output channels.  The logits either come from both waves
+// computing the full Q K^T (kDupQK: no exchange, twice the products) or
+// from each wave's half of the channels, the halves swapped through LDS.
+// A query's key slots are its selected
+// entries (padded to a multiple of the chunk size) followed by its window
+// rows, so every chunk of 32 slots holds one kind of row and is fetched
+// with the loads of that kind only.  Per chunk:
+//   1. the workgroup decodes the 32 rows into a key-major bf16 LDS tile
 //      (E2M1 x E8M0 -> bf16 is exact; gfx950's v_cvt_scalef32_pk_bf16_fp4
-//      converts two codes per instruction); when a chunk's loads fit one
-//      register batch, the next chunk's raw bytes are fetched while the
-//      current chunk is computed (the tile is double buffered);
-//   3. S = Q K^T on v_mfma_f32_16x16x32_bf16 (lane: key l%16, heads
-//      4(l/16)..+3), online softmax in the log2 domain;
-//   4. P goes through a small per-wave LDS tile to become the A operand of
+//      converts two codes per instruction); the raw bytes of the next chunk
+//      are fetched into registers while the current one is computed (the
+//      tile and the slot lists are multi-buffered, one barrier per chunk);
+//   2. S = Q K^T on v_mfma_f32_16x16x32_bf16 (lane: key l%16, heads
+//      4(l/16)..+3), online softmax in the log2 domain with DPP row
+//      reductions (both waves of a pair hold bit-identical logits);
+//   3. P goes through a small per-wave LDS tile to become the A operand of
 //      O += P V; the V operand (keys along K) is read transposed from the
 //      same key-major tile with ds_read_b64_tr_b16, so no second copy of
 //      the keys is written.  With fp32 outputs P is split into two bf16
 //      parts (hi + lo) so that the probabilities keep ~16 bits.
 // Splits write unnormalised (O, max, sum) partials that a merge kernel
 // combines; a single split writes the normalised output directly.
+#include <type_traits>
+
 #include "csa_device.hpp"
 #include "csa_internal.hpp"
 
@@ -32,9 +41,13 @@ namespace csa {
 constexpr int kKC = 32;           // key slots per chunk
 constexpr int kKRow = kD + 8;     // key-major LDS row (bf16 elements)
 constexpr int kPRow = kKC + 8;
-constexpr int kNT = kD / 16;      // 36 channel tiles of 16
-constexpr int kHalfD = kD / 2;    // channels per wave of a wave pair
-constexpr int kHalfNT = kNT / 2;
+constexpr int kHalfD = kD / 2;    // output channels per wave of a pair
+constexpr int kHalfNT = kHalfD / 16;  // 18 channel tiles of 16 (P V)
+constexpr int kKSteps = kD / 32;  // 18 channel steps of 32 (Q K^T)
+constexpr int kFp4Tasks = kKC * (kDNope / 32);  // one MXFP4 block (16 code bytes + scale) each
+constexpr int kRopeTasks = kKC * (kDRope / 8);  // 8 bf16 channels each
+constexpr int kRowPieces = kD / 8;              // 16-byte pieces of a bf16 window row
+constexpr int kWinTasks = kKC * kRowPieces;
 
 struct AttnArgs {
   const uint8_t *nope;
@@ -60,85 +73,155 @@ struct AttnArgs {
   int nsplit, per_split;
 };
 
-// Raw bytes of one decode task: 16 channels of one key.
-struct RawTask {
-  uint4 a, b;       // bf16 rows: 32 bytes; MXFP4: a.x, a.y hold 16 codes
-  uint32_t meta;    // kind (0 nothing, 1 MXFP4, 2 bf16) | E8M0 scale byte << 8
+// Per-thread share of one chunk's raw bytes for NT threads.
+template <int NT>
+struct ChunkShare {
+  static constexpr int kFp4 = kFp4Tasks / NT > 0 ? kFp4Tasks / NT : 1;
+  static constexpr int kRope = (kRopeTasks + NT - 1) / NT;
+  static constexpr int kEnt = kFp4 + kRope;
+  static constexpr int kWin = (kWinTasks + NT - 1) / NT;
+  // hold a whole chunk in registers (and fetch it ahead) when it is small
+  static constexpr bool kAhead = kEnt <= 9 && kWin <= 9;
+  static constexpr int kWinBatch = kAhead ? kWin : 9;
+  static constexpr int kRaw = kEnt > kWinBatch ? kEnt : kWinBatch;
 };
 
-constexpr int kSegs = kD / 16;          // 36 tasks of 16 channels per key
-constexpr int kChunkTasks = kKC * kSegs;
+template <int NT>
+struct RawChunk {
+  uint4 v[ChunkShare<NT>::kRaw];
+  uint32_t s[ChunkShare<NT>::kFp4];
+};
 
-// Branch-free: three unconditional loads from clamped addresses (codes,
-// scale byte, 32 bf16 bytes) with a known-valid stand-in address for the
-// parts a task does not use; loads inside per-lane branches would make the
-// compiler wait for each one before issuing the next.
-__device__ __forceinline__ void load_task(const AttnArgs &a, int b, int src, int seg, const uint8_t *dummy,
-                                          RawTask &t) {
-  const int ch = seg * 16;
-  const bool none = src < 0;
-  const bool win = !none && (src & 0x40000000);
-  const bool ent = !none && !win;
-  const bool fp4 = ent && ch < kDNope;
-  const int64_t row = (int64_t)b * a.N_cap + (ent ? src : 0);
-  const uint8_t *pc = fp4 ? a.nope + row * kNopeBytes + ch / 2 : dummy;
-  const uint8_t *ps = fp4 ? a.nscale + row * kNopeScales + ch / 32 : dummy;
-  const uint8_t *pb = dummy;
-  if (win) pb = reinterpret_cast<const uint8_t *>(a.swa + ((int64_t)b * a.S + (src & 0x3FFFFFFF)) * kD + ch);
-  if (ent && !fp4) pb = reinterpret_cast<const uint8_t *>(a.rope + row * kDRope + (ch - kDNope));
-  const uint2 c = *reinterpret_cast<const uint2 *>(pc);
-  const uint32_t sc = *ps;
-  const uint4 lo = reinterpret_cast<const uint4 *>(pb)[0];
-  const uint4 hi = reinterpret_cast<const uint4 *>(pb)[1];
-  t.a = fp4 ? uint4{c.x, c.y, 0u, 0u} : lo;
-  t.b = hi;
-  t.meta = none ? 0u : (fp4 ? (1u | (sc << 8)) : 2u);
-}
-
-// Writes the 16 decoded bf16 channels of a task (zeros for an empty slot).
-__device__ __forceinline__ void store_task(uint16_t *row, const RawTask &t) {
-  uint4 lo = {0u, 0u, 0u, 0u}, hi = {0u, 0u, 0u, 0u};
-  const uint32_t kind = t.meta & 0xFFu;
-  if (kind == 2) {
-    lo = t.a;
-    hi = t.b;
-  } else if (kind == 1) {
-    // E2M1 x 2^(s-127) -> bf16 is exact (hardware conversion, two codes per byte)
-    const float sc = e8m0_to_f32(t.meta >> 8);
-#define CSA_CVT(src, sel) __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(src, sc, sel))
-    lo = uint4{CSA_CVT(t.a.x, 0), CSA_CVT(t.a.x, 1), CSA_CVT(t.a.x, 2), CSA_CVT(t.a.x, 3)};
-    hi = uint4{CSA_CVT(t.a.y, 0), CSA_CVT(t.a.y, 1), CSA_CVT(t.a.y, 2), CSA_CVT(t.a.y, 3)};
-#undef CSA_CVT
+// Loads of an entry chunk: MXFP4 blocks and rope pieces.  Slots without an
+// entry read row 0 (a valid address) and are zeroed when stored.
+template <int NT>
+__device__ __forceinline__ void load_entries(const AttnArgs &a, int b, const int *src, RawChunk<NT> &r) {
+  using CS = ChunkShare<NT>;
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int u = 0; u < CS::kFp4; ++u) {
+    const int t = tid + u * NT;  // < kFp4Tasks (NT divides it)
+    const int key = t >> 4, blk = t & 15;
+    const int64_t row = (int64_t)b * a.N_cap + min(max(src[key], 0), a.N_cap - 1);
+    r.v[u] = *reinterpret_cast<const uint4 *>(a.nope + row * kNopeBytes + blk * 16);
+    r.s[u] = a.nscale[row * kNopeScales + blk];
   }
-  reinterpret_cast<uint4 *>(row)[0] = lo;
-  reinterpret_cast<uint4 *>(row)[1] = hi;
+#pragma unroll
+  for (int u = 0; u < CS::kRope; ++u) {
+    const int t = min(tid + u * NT, kRopeTasks - 1);
+    const int key = t >> 3, part = t & 7;
+    const int64_t row = (int64_t)b * a.N_cap + min(max(src[key], 0), a.N_cap - 1);
+    r.v[CS::kFp4 + u] = *reinterpret_cast<const uint4 *>(a.rope + row * kDRope + part * 8);
+  }
 }
 
-template <int HG, bool kSplitP, bool kDense>
+template <int NT>
+__device__ __forceinline__ void store_entries(uint16_t *K, const int *src, const RawChunk<NT> &r) {
+  using CS = ChunkShare<NT>;
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int u = 0; u < CS::kFp4; ++u) {
+    const int t = tid + u * NT;
+    const int key = t >> 4, blk = t & 15;
+    uint4 *dst = reinterpret_cast<uint4 *>(K + key * kKRow + blk * 32);
+    if (src[key] >= 0) {
+      // E2M1 x 2^(s-127) -> bf16 is exact (hardware conversion, two codes per byte)
+      const float sc = e8m0_to_f32(r.s[u]);
+      const uint4 c = r.v[u];
+#define CSA_CVT(w, sel) __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, sel))
+#define CSA_CVT4(w) uint4 { CSA_CVT(w, 0), CSA_CVT(w, 1), CSA_CVT(w, 2), CSA_CVT(w, 3) }
+      dst[0] = CSA_CVT4(c.x);
+      dst[1] = CSA_CVT4(c.y);
+      dst[2] = CSA_CVT4(c.z);
+      dst[3] = CSA_CVT4(c.w);
+#undef CSA_CVT4
+#undef CSA_CVT
+    } else {
+      const uint4 z = {0u, 0u, 0u, 0u};
+      dst[0] = z;
+      dst[1] = z;
+      dst[2] = z;
+      dst[3] = z;
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < CS::kRope; ++u) {
+    const int t = tid + u * NT;
+    if (t < kRopeTasks) {
+      const int key = t >> 3, part = t & 7;
+      uint4 v = r.v[CS::kFp4 + u];  // a value copy: a conditional between lvalues would pin r to memory
+      if (src[key] < 0) v = uint4{0u, 0u, 0u, 0u};
+      *reinterpret_cast<uint4 *>(K + key * kKRow + kDNope + part * 8) = v;
+    }
+  }
+}
+
+// Window rows: `nb` 16-byte pieces per thread starting at task t0.
+template <int NT, int nb>
+__device__ __forceinline__ void load_window(const AttnArgs &a, int b, const int *src, int t0, RawChunk<NT> &r) {
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int u = 0; u < nb; ++u) {
+    const int t = min(t0 + tid + u * NT, kWinTasks - 1);
+    const int key = t / kRowPieces, part = t % kRowPieces;
+    const int64_t row = (int64_t)b * a.S + min(max(src[key], 0), a.S - 1);
+    r.v[u] = *reinterpret_cast<const uint4 *>(a.swa + row * kD + part * 8);
+  }
+}
+
+template <int NT, int nb>
+__device__ __forceinline__ void store_window(uint16_t *K, const int *src, int t0, const RawChunk<NT> &r) {
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int u = 0; u < nb; ++u) {
+    const int t = t0 + tid + u * NT;
+    if (t < kWinTasks) {
+      const int key = t / kRowPieces, part = t % kRowPieces;
+      uint4 v = r.v[u];
+      if (src[key] < 0) v = uint4{0u, 0u, 0u, 0u};
+      *reinterpret_cast<uint4 *>(K + key * kKRow + part * 8) = v;
+    }
+  }
+}
+
+template <int HG, bool kSplitP, bool kDense, bool kDupQK>
 __global__ __launch_bounds__(HG * 128) void attn_kernel(AttnArgs a) {
+  constexpr int NT = HG * 128;
+  constexpr int kQSteps = kDupQK ? kKSteps : kKSteps / 2;  // channel steps of this wave's Q K^T
+  using CS = ChunkShare<NT>;
   // Key-major bf16 tiles of the chunk (double buffered); the P V operand is
   // read transposed from the same tile with ds_read_b64_tr_b16.
   __shared__ __attribute__((aligned(16))) uint16_t Kl[2][kKC * kKRow];
   __shared__ __attribute__((aligned(16))) uint16_t Pl[2 * HG][kSplitP ? 2 : 1][16 * kPRow];
-  __shared__ __attribute__((aligned(16))) float Sx[2 * HG][2 * 4 * 64];
-  __shared__ int src_s[2][kKC];
-
-  constexpr int nthr = HG * 128;
-  constexpr int kTasksPerThread = (kChunkTasks + nthr - 1) / nthr;
-  constexpr int kBatch = kTasksPerThread < 5 ? kTasksPerThread : 5;
-  constexpr bool kOneBatch = kBatch == kTasksPerThread;  // prefetch the next chunk in registers
+  __shared__ __attribute__((aligned(16))) float Sx[kDupQK ? 1 : 2 * HG][2 * 4 * 64];
+  // Slot lists of three consecutive chunks: the list of chunk c + 1 is
+  // written while a slower wave may still read that of chunk c.
+  __shared__ int src_s[3][kKC];
 
   const int split = blockIdx.x % a.nsplit, q = blockIdx.x / a.nsplit, b = blockIdx.y;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4, r = lane & 15;
   // wave pair (2hg, 2hg+1) shares heads 16hg..16hg+15; `half` picks channels [288 half, +288)
   const int hg = wave >> 1, half = wave & 1;
   const int cbase = half * kHalfD;
   const int64_t qrow = (int64_t)b * a.Q + q;
+  const int s_begin = split * a.per_split;
+  // A slot's index load and its publication are split so that other loads
+  // can be issued in between.
+  auto fetch_slot = [&](int c0) __attribute__((always_inline)) {
+    // unconditional load from a clamped address (no wait on the query's
+    // position); the slot's validity is applied when it is published
+    const int slot = c0 + (tid & (kKC - 1));
+    if (kDense || a.k <= 0) return slot;
+    return a.idx[qrow * a.k + min(slot, a.k - 1)];
+  };
+  const int j_first = fetch_slot(s_begin);
   const int p = a.q_pos[qrow];
   const int nE = min(a.n_entries[b], a.N_cap);
   const int V = p >= 0 ? max(0, min(nE, (p + 1) / a.m)) : 0;
   const int n_main = kDense ? V : a.k;
+  const int n_main_pad = (n_main + kKC - 1) / kKC * kKC;
   int win_lo = 0, n_swa = 0, swa0 = 0;
   if (a.n_win > 0 && p >= 0) {
     swa0 = a.swa_pos0[b];
@@ -146,35 +229,25 @@ __global__ __launch_bounds__(HG * 128) void attn_kernel(AttnArgs a) {
     const int win_hi = min(p, swa0 + a.S - 1);
     n_swa = max(0, win_hi - win_lo + 1);
   }
-  const int n_slots = n_main + n_swa;
-  const int s_begin = split * a.per_split;
+  const int n_slots = n_main_pad + n_swa;
   const int s_end = min(n_slots, s_begin + a.per_split);
 
-  auto resolve = [&](int c0, int buf) {
+  // Slot -> source row: an entry index (entry chunks) or a row of the window
+  // buffer (window chunks); -1 = nothing.
+  auto publish_slot = [&](int c0, int j, int sb) __attribute__((always_inline)) {
     if (tid < kKC) {
       const int slot = c0 + tid;
       int src = -1;
       if (slot < s_end) {
-        if (slot < n_main) {
-          const int j = kDense ? slot : a.idx[qrow * a.k + slot];
-          if (j >= 0 && j < V) src = j;
+        if (slot < n_main_pad) {
+          if (slot < n_main && j >= 0 && j < V) src = j;
         } else {
-          src = 0x40000000 | (win_lo + (slot - n_main) - swa0);
+          src = win_lo + (slot - n_main_pad) - swa0;
         }
       }
-      src_s[buf][tid] = src;
+      src_s[sb][tid] = src;
     }
   };
-
-  // a known-valid address for loads a task does not need: this query's row
-  const uint8_t *dummy = reinterpret_cast<const uint8_t *>(a.q + qrow * a.H * kD);
-  const int h0 = hg * 16;
-  v8bf Qf[kHalfD / 32];
-  {
-    const uint16_t *qp = a.q + (qrow * a.H + h0 + r) * kD + cbase + 8 * g;
-#pragma unroll
-    for (int kk = 0; kk < kHalfD / 32; ++kk) Qf[kk] = *reinterpret_cast<const v8bf *>(qp + 32 * kk);
-  }
 
   float m2[4], lsum[4];
   v4f O[kHalfNT];
@@ -186,112 +259,80 @@ __global__ __launch_bounds__(HG * 128) void attn_kernel(AttnArgs a) {
 #pragma unroll
   for (int j = 0; j < kHalfNT; ++j) O[j] = v4f{0.f, 0.f, 0.f, 0.f};
 
-  RawTask pre[kBatch];
+  v8bf Qf[kQSteps];
   if (s_begin < s_end) {
-    resolve(s_begin, 0);
-    __syncthreads();
-    if (kOneBatch) {
+    const int j0 = j_first;  // issued before the query loads
+    const uint16_t *qp = a.q + (qrow * a.H + hg * 16 + r) * kD + (kDupQK ? 0 : cbase) + 8 * g;
 #pragma unroll
-      for (int u = 0; u < kBatch; ++u) {
-        const int t = tid + u * nthr;
-        if (t < kChunkTasks) load_task(a, b, src_s[0][t / kSegs], t % kSegs, dummy, pre[u]);
-        else pre[u].meta = 0;
-      }
-    }
+    for (int kk = 0; kk < kQSteps; ++kk) Qf[kk] = *reinterpret_cast<const v8bf *>(qp + 32 * kk);
+    publish_slot(s_begin, j0, 0);
   }
 
-  int buf = 0;
-  for (int c0 = s_begin; c0 < s_end; c0 += kKC, buf ^= 1) {
-    uint16_t *K = Kl[buf];
-    // 1. decode this chunk into K
-    if (kOneBatch) {
+  // One chunk of decoded keys in K: logits, online softmax, O += P V.
+  auto compute_chunk = [&](const uint16_t *K, bool kv0, bool kv1) __attribute__((always_inline)) {
+    // S = Q K^T for two tiles of 16 keys (two independent MFMA chains)
+    v4f S0 = {0.f, 0.f, 0.f, 0.f}, S1 = {0.f, 0.f, 0.f, 0.f};
+    {
+      const uint16_t *k0 = K + r * kKRow + (kDupQK ? 0 : cbase) + 8 * g;
+      const uint16_t *k1 = k0 + 16 * kKRow;
 #pragma unroll
-      for (int u = 0; u < kBatch; ++u) {
-        const int t = tid + u * nthr;
-        if (t < kChunkTasks) store_task(K + (t / kSegs) * kKRow + (t % kSegs) * 16, pre[u]);
-      }
-    } else {
-      for (int t0 = 0; t0 < kChunkTasks; t0 += kBatch * nthr) {
-        RawTask tk[kBatch];
-#pragma unroll
-        for (int u = 0; u < kBatch; ++u) {
-          const int t = t0 + tid + u * nthr;
-          if (t < kChunkTasks) load_task(a, b, src_s[buf][t / kSegs], t % kSegs, dummy, tk[u]);
-        }
-#pragma unroll
-        for (int u = 0; u < kBatch; ++u) {
-          const int t = t0 + tid + u * nthr;
-          if (t < kChunkTasks) store_task(K + (t / kSegs) * kKRow + (t % kSegs) * 16, tk[u]);
-        }
+      for (int kk = 0; kk < kQSteps; ++kk) {
+        S0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Qf[kk], *reinterpret_cast<const v8bf *>(k0 + 32 * kk), S0, 0, 0,
+                                                     0);
+        S1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Qf[kk], *reinterpret_cast<const v8bf *>(k1 + 32 * kk), S1, 0, 0,
+                                                     0);
       }
     }
-    if (c0 + kKC < s_end) resolve(c0 + kKC, buf ^ 1);
-    __syncthreads();
-    // key-slot flags of this chunk, read before the next barrier (the list of
-    // this buffer is resolved again one iteration later)
-    const bool kv0 = src_s[buf][r] >= 0, kv1 = src_s[buf][16 + r] >= 0;
-    // 2. prefetch the next chunk's raw bytes while this one is computed
-    if (kOneBatch && c0 + kKC < s_end) {
-#pragma unroll
-      for (int u = 0; u < kBatch; ++u) {
-        const int t = tid + u * nthr;
-        if (t < kChunkTasks) load_task(a, b, src_s[buf ^ 1][t / kSegs], t % kSegs, dummy, pre[u]);
-        else pre[u].meta = 0;
-      }
-    }
-
-    // 3. half of S = Q K^T (this wave's 288 channels) for two tiles of 16 keys,
-    //    then the partner's half through LDS
-    v4f S2[2];
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
-      v4f acc = {0.f, 0.f, 0.f, 0.f};
-      const uint16_t *kp = K + (kt * 16 + r) * kKRow + cbase + 8 * g;
-#pragma unroll
-      for (int kk = 0; kk < kHalfD / 32; ++kk)
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Qf[kk], *reinterpret_cast<const v8bf *>(kp + 32 * kk), acc, 0,
-                                                      0, 0);
-      S2[kt] = acc;
-    }
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) Sx[wave][(kt * 4 + i) * 64 + lane] = S2[kt][i];
-    __syncthreads();
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
+    if (!kDupQK) {
+      // the partner's half of the channels, added in a fixed order of the
+      // halves so that both waves of the pair agree bit for bit
+      float *sx = &Sx[kDupQK ? 0 : wave][0];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        // a fixed order of the two halves, so both waves of the pair agree bit for bit
-        const float mine = S2[kt][i], other = Sx[wave ^ 1][(kt * 4 + i) * 64 + lane];
-        S2[kt][i] = half == 0 ? mine + other : other + mine;
+        sx[i * 64 + lane] = S0[i];
+        sx[(4 + i) * 64 + lane] = S1[i];
       }
+      lds_barrier();
+      const float *so = &Sx[kDupQK ? 0 : wave ^ 1][0];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float o0 = so[i * 64 + lane], o1 = so[(4 + i) * 64 + lane];
+        S0[i] = half == 0 ? S0[i] + o0 : o0 + S0[i];
+        S1[i] = half == 0 ? S1[i] + o1 : o1 + S1[i];
+      }
+    }
 
     float alpha[4], p0[4], p1[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const float x0 = kv0 ? S2[0][i] * a.scale_log2 : -INFINITY;
-      const float x1 = kv1 ? S2[1][i] * a.scale_log2 : -INFINITY;
+      const float x0 = kv0 ? S0[i] * a.scale_log2 : -INFINITY;
+      const float x1 = kv1 ? S1[i] * a.scale_log2 : -INFINITY;
       const float tmax = row16_max(fmaxf(x0, x1));
-      const float mn = fmaxf(m2[i], tmax);
-      if (mn == -INFINITY) {
-        alpha[i] = 1.f;
-        p0[i] = p1[i] = 0.f;
-      } else {
-        alpha[i] = exp2f(m2[i] - mn);
-        p0[i] = exp2f(x0 - mn);
-        p1[i] = exp2f(x1 - mn);
-      }
+      // The running maximum moves only when the chunk's maximum exceeds it by
+      // more than 2^8 (or on the first keys): the result is the same for any
+      // reference value, probabilities stay below 256, and the rescale of O
+      // below is skipped in the common case.
+      const float mn = (tmax > m2[i] + 8.f) ? tmax : m2[i];
+      // branch-free: with no key yet (mn = -inf) the reference 0 gives
+      // p = 0 and alpha = 0 on an empty state.  v_exp_f32 directly: results
+      // below 2^-126 of the reference do not matter to these sums.
+      const float mref = mn == -INFINITY ? 0.f : mn;
+      alpha[i] = __builtin_amdgcn_exp2f(m2[i] - mref);
+      p0[i] = __builtin_amdgcn_exp2f(x0 - mref);
+      p1[i] = __builtin_amdgcn_exp2f(x1 - mref);
       lsum[i] = lsum[i] * alpha[i] + row16_sum(p0[i] + p1[i]);
       m2[i] = mn;
     }
+    const bool moved = alpha[0] != 1.f || alpha[1] != 1.f || alpha[2] != 1.f || alpha[3] != 1.f;
+    if (__builtin_amdgcn_ballot_w64(moved)) {
 #pragma unroll
-    for (int j = 0; j < kHalfNT; ++j) {
+      for (int j = 0; j < kHalfNT; ++j) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) O[j][i] *= alpha[i];
+        for (int i = 0; i < 4; ++i) O[j][i] *= alpha[i];
+      }
     }
-    // 4. P (bf16, or hi + lo) through this wave's LDS tile into the A layout
-    //    (LDS operations of one wave complete in order)
+    // P (bf16, or hi + lo) through this wave's LDS tile into the A layout
+    // (LDS operations of one wave complete in order)
     uint16_t *pw = &Pl[wave][0][0];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -304,14 +345,15 @@ __global__ __launch_bounds__(HG * 128) void attn_kernel(AttnArgs a) {
         pl[(4 * g + i) * kPRow + 16 + r] = (uint16_t)f32_to_bf16(p1[i] - bf16_to_f32(hi1));
       }
     }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
     __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
     const v8bf Pa = *reinterpret_cast<const v8bf *>(&Pl[wave][0][r * kPRow + 8 * g]);
     v8bf Pb;
     if (kSplitP) Pb = *reinterpret_cast<const v8bf *>(&Pl[wave][kSplitP ? 1 : 0][r * kPRow + 8 * g]);
-    // 5. O += P V for this wave's channels; lane (g, r) needs V[keys 8g..8g+7]
-    //    [channel c + r]: two transposed 4x16 reads of the key-major tile.
+    // O += P V over this wave's 18 channel tiles; lane (g, r) needs
+    // V[keys 8g..8g+7][channel c + r]: two transposed 4x16 reads of the
+    // key-major tile.
     typedef __attribute__((address_space(3))) v4s lds_v4s;
     const uint16_t *vb = K + (8 * g + (r >> 2)) * kKRow + cbase + 4 * (r & 3);
 #pragma unroll
@@ -323,10 +365,56 @@ __global__ __launch_bounds__(HG * 128) void attn_kernel(AttnArgs a) {
       O[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Pa, Bv, O[j], 0, 0, 0);
       if (kSplitP) O[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Pb, Bv, O[j], 0, 0, 0);
     }
-    // The next iteration writes the other K buffer and Sx only after its own
-    // barrier; the K buffer read here is rewritten two iterations later.
-  }
+  };
 
+  // Chunks of one kind in [c_lo, c_hi): decode the fetched rows into K,
+  // publish the next slot list, one LDS-only barrier, fetch the next rows
+  // (unconditionally: slots past the range read a clamped valid row), then
+  // compute.  Buffers: K alternates between two tiles; slot lists rotate over
+  // three (the list of chunk c + 1 is written while a slower wave may still
+  // read that of chunk c); Sx is rewritten only after the next barrier.  The
+  // list of c_lo is published and its rows fetched before the call.
+  int ci = 0;
+  auto run_chunks = [&](auto win_tag, int c_lo, int c_hi) __attribute__((always_inline)) {
+    constexpr bool kWin = decltype(win_tag)::value;
+    RawChunk<NT> raw;
+    lds_barrier();
+    if (CS::kAhead) {
+      if (kWin) load_window<NT, CS::kWinBatch>(a, b, src_s[ci % 3], 0, raw);
+      else load_entries<NT>(a, b, src_s[ci % 3], raw);
+    }
+    for (int c0 = c_lo; c0 < c_hi; c0 += kKC, ++ci) {
+      uint16_t *K = Kl[ci & 1];
+      const int sb = ci % 3, sn = (ci + 1) % 3;
+      const int jn = kWin ? -1 : fetch_slot(c0 + kKC);
+      if (CS::kAhead) {
+        if (kWin) store_window<NT, CS::kWinBatch>(K, src_s[sb], 0, raw);
+        else store_entries<NT>(K, src_s[sb], raw);
+      } else if (kWin) {
+        for (int t0 = 0; t0 < kWinTasks; t0 += CS::kWinBatch * NT) {
+          load_window<NT, CS::kWinBatch>(a, b, src_s[sb], t0, raw);
+          store_window<NT, CS::kWinBatch>(K, src_s[sb], t0, raw);
+        }
+      } else {
+        load_entries<NT>(a, b, src_s[sb], raw);
+        store_entries<NT>(K, src_s[sb], raw);
+      }
+      publish_slot(c0 + kKC, jn, sn);
+      lds_barrier();
+      const bool kv0 = src_s[sb][r] >= 0, kv1 = src_s[sb][16 + r] >= 0;
+      if (CS::kAhead) {
+        if (kWin) load_window<NT, CS::kWinBatch>(a, b, src_s[sn], 0, raw);
+        else load_entries<NT>(a, b, src_s[sn], raw);
+      }
+      compute_chunk(K, kv0, kv1);
+    }
+  };
+  const int e_hi = min(s_end, n_main_pad);
+  if (s_begin < e_hi) run_chunks(std::false_type{}, s_begin, e_hi);
+  const int w_lo = max(s_begin, n_main_pad);
+  if (w_lo < s_end) run_chunks(std::true_type{}, w_lo, s_end);  // its first list was published by the last entry chunk
+
+  const int h0 = hg * 16;
   if (a.nsplit == 1) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -350,9 +438,17 @@ __global__ __launch_bounds__(HG * 128) void attn_kernel(AttnArgs a) {
     for (int i = 0; i < 4; ++i) {
       const int hh = h0 + 4 * g + i;
       const int64_t pr = (qrow * a.nsplit + split) * a.H + hh;
-      float *o = a.ws_o + pr * kD + cbase;
+      if (a.out_bf16) {
+        // bf16 partials for a bf16 result: the merged error stays near the
+        // output's own rounding (about 2^-9 of the row maximum per split)
+        uint16_t *o = reinterpret_cast<uint16_t *>(a.ws_o) + pr * kD + cbase;
 #pragma unroll
-      for (int j = 0; j < kHalfNT; ++j) o[16 * j + r] = O[j][i];
+        for (int j = 0; j < kHalfNT; ++j) o[16 * j + r] = (uint16_t)f32_to_bf16(O[j][i]);
+      } else {
+        float *o = a.ws_o + pr * kD + cbase;
+#pragma unroll
+        for (int j = 0; j < kHalfNT; ++j) o[16 * j + r] = O[j][i];
+      }
       if (r == 0 && half == 0) {
         a.ws_ml[pr * 2 + 0] = m2[i];
         a.ws_ml[pr * 2 + 1] = lsum[i];
@@ -361,9 +457,11 @@ __global__ __launch_bounds__(HG * 128) void attn_kernel(AttnArgs a) {
   }
 }
 
-// Combines the splits of one (query, head): weights 2^(m_s - M).
+// Combines the splits of one (query, head): weights 2^(m_s - M).  Partials
+// are fp32, or bf16 when the result is bf16.
+template <bool kBf16>
 __global__ __launch_bounds__(64) void attn_merge_kernel(const float *__restrict__ ws_o, const float *__restrict__ ws_ml,
-                                                        int nsplit, int H, int out_bf16, void *out, float *lse) {
+                                                        int nsplit, int H, void *out, float *lse) {
   const int64_t qh = blockIdx.x;           // qrow * H + h
   const int64_t qrow = qh / H, hh = qh % H;
   const int tid = threadIdx.x;
@@ -380,13 +478,17 @@ __global__ __launch_bounds__(64) void attn_merge_kernel(const float *__restrict_
       if (ms == -INFINITY) continue;
       const float wgt = exp2f(ms - M);
       L += wgt * ws_ml[pr * 2 + 1];
-      const float *o = ws_o + pr * kD;
 #pragma unroll
-      for (int c = 0; c < kD / 64; ++c) acc[c] = fmaf(wgt, o[tid + 64 * c], acc[c]);
+      for (int c = 0; c < kD / 64; ++c) {
+        float v;
+        if (kBf16) v = bf16_to_f32(reinterpret_cast<const uint16_t *>(ws_o)[pr * kD + tid + 64 * c]);
+        else v = ws_o[pr * kD + tid + 64 * c];
+        acc[c] = fmaf(wgt, v, acc[c]);
+      }
     }
   }
   const float inv = L > 0.f ? 1.f / L : 0.f;
-  if (out_bf16) {
+  if (kBf16) {
     uint16_t *o = reinterpret_cast<uint16_t *>(out) + qh * kD;
 #pragma unroll
     for (int c = 0; c < kD / 64; ++c) o[tid + 64 * c] = (uint16_t)f32_to_bf16(acc[c] * inv);
@@ -398,7 +500,12 @@ __global__ __launch_bounds__(64) void attn_merge_kernel(const float *__restrict_
   if (lse && tid == 0) lse[qh] = L > 0.f ? (M + log2f(L)) * 0.69314718055994531f : -INFINITY;
 }
 
-AttnShape attn_shape(int B, int Q, int n_slots_max) {
+// Slots per query: the selected entries rounded up to whole chunks, then
+// the window rows.
+static int slots_max(int n_main, int n_win) { return (n_main + kKC - 1) / kKC * kKC + n_win; }
+
+AttnShape attn_shape(int B, int Q, int n_main, int n_win) {
+  const int n_slots_max = slots_max(n_main, n_win);
   const int chunks = n_slots_max > 0 ? (n_slots_max + kKC - 1) / kKC : 1;
   const int64_t rows = (int64_t)B * Q;
   int want = (int)(rows >= 256 ? 1 : (256 + rows - 1) / rows);
@@ -408,18 +515,22 @@ AttnShape attn_shape(int B, int Q, int n_slots_max) {
   return AttnShape{nsplit, per_chunks * kKC};
 }
 
-size_t attn_workspace_bytes(int B, int Q, int H, int n_slots_max) {
-  const AttnShape s = attn_shape(B, Q, n_slots_max);
+size_t attn_workspace_bytes(int B, int Q, int H, int n_main, int n_win) {
+  const AttnShape s = attn_shape(B, Q, n_main, n_win);
   if (s.nsplit <= 1) return 0;
   return (size_t)B * Q * s.nsplit * H * (kD + 2) * sizeof(float);
 }
 
+#ifndef CSA_ATTN_DUP_QK
+#define CSA_ATTN_DUP_QK 0
+#endif
 template <int HG, bool kSplitP>
 static void launch_hg(const AttnArgs &a, bool dense, dim3 grid, hipStream_t stream) {
+  constexpr bool kDup = CSA_ATTN_DUP_QK != 0;
   if (dense)
-    attn_kernel<HG, kSplitP, true><<<grid, HG * 128, 0, stream>>>(a);
+    attn_kernel<HG, kSplitP, true, kDup><<<grid, HG * 128, 0, stream>>>(a);
   else
-    attn_kernel<HG, kSplitP, false><<<grid, HG * 128, 0, stream>>>(a);
+    attn_kernel<HG, kSplitP, false, kDup><<<grid, HG * 128, 0, stream>>>(a);
 }
 
 template <bool kSplitP>
@@ -436,8 +547,7 @@ hipError_t launch_attention(const CacheView &c, const uint16_t *q, int H, const 
                             const int32_t *idx, int k, bool dense, const uint16_t *swa, const int32_t *swa_pos0,
                             int S, int n_win, float scale, bool out_bf16, void *out, float *lse, void *ws,
                             hipStream_t stream) {
-  const int n_slots_max = (dense ? c.N_cap : k) + n_win;
-  const AttnShape sh = attn_shape(c.B, Q, n_slots_max);
+  const AttnShape sh = attn_shape(c.B, Q, dense ? c.N_cap : k, n_win);
   AttnArgs a;
   a.nope = c.nope;
   a.nscale = c.nscale;
@@ -471,8 +581,11 @@ hipError_t launch_attention(const CacheView &c, const uint16_t *q, int H, const 
     launch_split<true>(a, dense, grid, stream);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || sh.nsplit == 1) return e;
-  attn_merge_kernel<<<(unsigned)((int64_t)c.B * Q * H), 64, 0, stream>>>(a.ws_o, a.ws_ml, sh.nsplit, H, a.out_bf16,
-                                                                        out, lse);
+  const unsigned nq = (unsigned)((int64_t)c.B * Q * H);
+  if (out_bf16)
+    attn_merge_kernel<true><<<nq, 64, 0, stream>>>(a.ws_o, a.ws_ml, sh.nsplit, H, out, lse);
+  else
+    attn_merge_kernel<false><<<nq, 64, 0, stream>>>(a.ws_o, a.ws_ml, sh.nsplit, H, out, lse);
   return hipGetLastError();
 }
 

@@ -29,10 +29,9 @@ typedef short v8s __attribute__((ext_vector_type(8)));
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
 
-// Round to nearest even; finite inputs only.
+// Round to nearest even (gfx950's v_cvt_pk_bf16_f32); finite inputs only.
 __device__ __forceinline__ uint32_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+  return __builtin_bit_cast(uint16_t, (__bf16)f);
 }
 
 // 2^(s - 127) for an E8M0 byte s < 255, exactly (s = 0 is an fp32 subnormal).
@@ -65,6 +64,15 @@ __device__ __forceinline__ uint32_t e2m1_encode(float v, float inv_scale) {
 
 // 1 / 2^X for the block byte s (X = s - 127), exactly: 2^(127 - s).
 __device__ __forceinline__ float mx_inv_scale(uint32_t s) { return __uint_as_float((254u - s) << 23); }
+
+// Workgroup barrier that orders LDS only: global loads still in flight stay
+// in flight (a __syncthreads() also waits for every outstanding global load,
+// which defeats fetching ahead across it).
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
 
 // Cross-lane steps on DPP (data-parallel primitives): they run at VALU
 // latency, where a ds_bpermute shuffle makes an LDS round trip.  Lanes

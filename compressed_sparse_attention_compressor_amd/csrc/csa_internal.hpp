@@ -46,8 +46,9 @@ struct AttnShape {
   int nsplit;       // key-range splits per query
   int per_split;    // key slots per split (a multiple of the chunk size)
 };
-AttnShape attn_shape(int B, int Q, int n_slots_max);
-size_t attn_workspace_bytes(int B, int Q, int H, int n_slots_max);
+// n_main: selected entries per query (k), or N_cap for dense attention.
+AttnShape attn_shape(int B, int Q, int n_main, int n_win);
+size_t attn_workspace_bytes(int B, int Q, int H, int n_main, int n_win);
 
 hipError_t launch_attention(const CacheView &c, const uint16_t *q, int H, const int32_t *q_pos, int Q,
                             const int32_t *idx, int k, bool dense, const uint16_t *swa,

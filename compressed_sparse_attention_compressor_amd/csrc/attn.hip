@@ -457,47 +457,72 @@ __global__ __launch_bounds__(HG * 128) void attn_kernel(AttnArgs a) {
   }
 }
 
-// Combines the splits of one (query, head): weights 2^(m_s - M).  Partials
-// are fp32, or bf16 when the result is bf16.
+// Combines the splits: output = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s
+// with M the largest m_s.  One thread per 8 channels of one (query, head):
+// 16-byte loads of bf16 partials (8-byte halves of fp32 ones), the split
+// weights formed once per thread, and the loads over splits issued together
+// (up to kMergeUnroll at a time).  Partials are fp32, or bf16 when the
+// result is bf16.
+constexpr int kMergeThreads = 256;
+constexpr int kMergeUnroll = 8;
 template <bool kBf16>
-__global__ __launch_bounds__(64) void attn_merge_kernel(const float *__restrict__ ws_o, const float *__restrict__ ws_ml,
-                                                        int nsplit, int H, void *out, float *lse) {
-  const int64_t qh = blockIdx.x;           // qrow * H + h
+__global__ __launch_bounds__(kMergeThreads) void attn_merge_kernel(const float *__restrict__ ws_o,
+                                                                   const float *__restrict__ ws_ml, int nsplit, int H,
+                                                                   int64_t n_items, void *out, float *lse) {
+  const int64_t item = (int64_t)blockIdx.x * kMergeThreads + threadIdx.x;  // (qrow, head, channel group of 8)
+  if (item >= n_items) return;
+  constexpr int kGroups = kD / 8;
+  const int64_t qh = item / kGroups;  // qrow * H + head
+  const int c8 = (int)(item % kGroups) * 8;
   const int64_t qrow = qh / H, hh = qh % H;
-  const int tid = threadIdx.x;
+  auto pr_of = [&](int s) { return (qrow * nsplit + s) * H + hh; };
   float M = -INFINITY;
-  for (int s = 0; s < nsplit; ++s) M = fmaxf(M, ws_ml[((qrow * nsplit + s) * H + hh) * 2]);
-  float acc[kD / 64];
-#pragma unroll
-  for (int c = 0; c < kD / 64; ++c) acc[c] = 0.f;
+  for (int s = 0; s < nsplit; ++s) M = fmaxf(M, ws_ml[pr_of(s) * 2]);
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   float L = 0.f;
   if (M != -INFINITY) {
-    for (int s = 0; s < nsplit; ++s) {
-      const int64_t pr = (qrow * nsplit + s) * H + hh;
-      const float ms = ws_ml[pr * 2];
-      if (ms == -INFINITY) continue;
-      const float wgt = exp2f(ms - M);
-      L += wgt * ws_ml[pr * 2 + 1];
+    for (int s0 = 0; s0 < nsplit; s0 += kMergeUnroll) {
+      float wgt[kMergeUnroll], v[kMergeUnroll][8];
 #pragma unroll
-      for (int c = 0; c < kD / 64; ++c) {
-        float v;
-        if (kBf16) v = bf16_to_f32(reinterpret_cast<const uint16_t *>(ws_o)[pr * kD + tid + 64 * c]);
-        else v = ws_o[pr * kD + tid + 64 * c];
-        acc[c] = fmaf(wgt, v, acc[c]);
+      for (int u = 0; u < kMergeUnroll; ++u) {
+        const int s = min(s0 + u, nsplit - 1);
+        const int64_t pr = pr_of(s);
+        const float2 ml = *reinterpret_cast<const float2 *>(ws_ml + pr * 2);
+        wgt[u] = (s0 + u < nsplit && ml.x != -INFINITY) ? exp2f(ml.x - M) : 0.f;
+        L += wgt[u] * (wgt[u] != 0.f ? ml.y : 0.f);
+        if (kBf16) {
+          const uint4 p = *reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(ws_o) + pr * kD + c8);
+          const uint32_t w4[4] = {p.x, p.y, p.z, p.w};
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            v[u][2 * j] = bf16_to_f32(w4[j] & 0xFFFFu);
+            v[u][2 * j + 1] = bf16_to_f32(w4[j] >> 16);
+          }
+        } else {
+          const float4 p0 = *reinterpret_cast<const float4 *>(ws_o + pr * kD + c8);
+          const float4 p1 = *reinterpret_cast<const float4 *>(ws_o + pr * kD + c8 + 4);
+          v[u][0] = p0.x; v[u][1] = p0.y; v[u][2] = p0.z; v[u][3] = p0.w;
+          v[u][4] = p1.x; v[u][5] = p1.y; v[u][6] = p1.z; v[u][7] = p1.w;
+        }
       }
+#pragma unroll
+      for (int u = 0; u < kMergeUnroll; ++u)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[j] = fmaf(wgt[u], v[u][j], acc[j]);
     }
   }
   const float inv = L > 0.f ? 1.f / L : 0.f;
   if (kBf16) {
-    uint16_t *o = reinterpret_cast<uint16_t *>(out) + qh * kD;
+    uint32_t w4[4];
 #pragma unroll
-    for (int c = 0; c < kD / 64; ++c) o[tid + 64 * c] = (uint16_t)f32_to_bf16(acc[c] * inv);
+    for (int j = 0; j < 4; ++j) w4[j] = f32_to_bf16(acc[2 * j] * inv) | (f32_to_bf16(acc[2 * j + 1] * inv) << 16);
+    *reinterpret_cast<uint4 *>(reinterpret_cast<uint16_t *>(out) + qh * kD + c8) = uint4{w4[0], w4[1], w4[2], w4[3]};
   } else {
-    float *o = reinterpret_cast<float *>(out) + qh * kD;
-#pragma unroll
-    for (int c = 0; c < kD / 64; ++c) o[tid + 64 * c] = acc[c] * inv;
+    float *o = reinterpret_cast<float *>(out) + qh * kD + c8;
+    *reinterpret_cast<float4 *>(o) = float4{acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv};
+    *reinterpret_cast<float4 *>(o + 4) = float4{acc[4] * inv, acc[5] * inv, acc[6] * inv, acc[7] * inv};
   }
-  if (lse && tid == 0) lse[qh] = L > 0.f ? (M + log2f(L)) * 0.69314718055994531f : -INFINITY;
+  if (lse && c8 == 0) lse[qh] = L > 0.f ? (M + log2f(L)) * 0.69314718055994531f : -INFINITY;
 }
 
 // Slots per query: the selected entries rounded up to whole chunks, then
@@ -581,11 +606,12 @@ hipError_t launch_attention(const CacheView &c, const uint16_t *q, int H, const 
     launch_split<true>(a, dense, grid, stream);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || sh.nsplit == 1) return e;
-  const unsigned nq = (unsigned)((int64_t)c.B * Q * H);
+  const int64_t n_items = (int64_t)c.B * Q * H * (kD / 8);
+  const unsigned nb = (unsigned)((n_items + kMergeThreads - 1) / kMergeThreads);
   if (out_bf16)
-    attn_merge_kernel<true><<<nq, 64, 0, stream>>>(a.ws_o, a.ws_ml, sh.nsplit, H, out, lse);
+    attn_merge_kernel<true><<<nb, kMergeThreads, 0, stream>>>(a.ws_o, a.ws_ml, sh.nsplit, H, n_items, out, lse);
   else
-    attn_merge_kernel<false><<<nq, 64, 0, stream>>>(a.ws_o, a.ws_ml, sh.nsplit, H, out, lse);
+    attn_merge_kernel<false><<<nb, kMergeThreads, 0, stream>>>(a.ws_o, a.ws_ml, sh.nsplit, H, n_items, out, lse);
   return hipGetLastError();
 }
 

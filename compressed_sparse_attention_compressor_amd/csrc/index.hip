@@ -123,7 +123,9 @@ __global__ __launch_bounds__(kIdxThreads) void index_scores_kernel(
       *reinterpret_cast<uint4 *>(qs + qb * kQBytes + rem) = qv_stage[u];
     }
   }
-  __syncthreads();
+  // LDS-only barrier: the key loads stay in flight, each MFMA below waits
+  // only for its own tile.
+  lds_barrier();
   // E4M3 operand layout of the instruction: bytes 0..15 of lane group g hold
   // channels 16g..16g+15, bytes 16..31 hold channels 64+16g..+15.
   v8i A[QB][HT];
@@ -173,9 +175,9 @@ __global__ __launch_bounds__(kIdxThreads) void index_scores_kernel(
     for (int it = 0; it < kIters; ++it)
       if (!(ent[it] >= 0 && ent[it] < vis[0])) sc[wave][0][it * 16 + r] = __uint_as_float(kNoScoreBits);
   }
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
   __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
   if (lane < kIdxWaveEntries / 4) {
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {

@@ -78,12 +78,19 @@ def test_batched_decode_128k_fullsize():
     g_idx = _np(idx)
     o_idx = np.zeros_like(g_idx)
     qI, wt = _np(qs["qI"]), _np(qs["w"])
+    # the combined entry point (scores in its workspace, then both selections)
+    f_idx, f_sc = csa.index_topk(cache, qs["qI"], qs["w"], qs["q_pos"], w.k, want_scores=True)
+    f_idx, f_sc = _np(f_idx), _np(f_sc)
     swaps = 0
     for b in range(w.B):
         oi, _, js, s = O.index_topk(pc["ikey"][b], pc["iscale"][b], qI[b, 0], wt[b, 0], w.T - 1, w.m, w.N, w.k)
         swaps += check_topk(g_idx[b, 0], oi, js, s, what=f"b={b}")
+        swaps += check_topk(f_idx[b, 0], oi, js, s, what=f"index_topk b={b}")
+        ref = dict(zip(js.tolist(), s.tolist()))
+        r = np.array([ref[j] for j in f_idx[b, 0]])
+        assert np.abs(f_sc[b, 0] - r).max() <= 1e-5 * (np.abs(s).max() + 1e-30)
         o_idx[b, 0] = oi
-    assert swaps <= 2
+    assert swaps <= 4
     # attention stage-wise on the oracle's selection, as the benchmark launches it (bf16 out)
     out, lse = csa.sparse_attn(cache, qs["q"], qs["q_pos"], torch.from_numpy(o_idx).to(DEV), x_win, s0, w.n_win,
                                w.softmax_scale, out_dtype=torch.bfloat16)

@@ -180,6 +180,13 @@ INDEX_CASES = [
      [[8191]], 100),
     ("heads48-d64", Workload("h48", 10, B=2, T=3000, m=4, d_idx=64, H_I=48, k=33, H=64, n_win=0), 750, [750, 750],
      [[2999], [1500]], 33),
+    # rows long enough for the two-stage selection (4,096-entry slices, then
+    # row-wide): a ragged last slice, visibility ending mid-slice, one row's
+    # count below the cache capacity, a query whose last slice sees nothing
+    ("fused-slices", Workload("fs", 11, B=2, T=40000, m=4, d_idx=128, H_I=32, k=300, H=64, n_win=0), 10000,
+     [10000, 6000], [[39999], [17003]], 300),
+    ("fused-d64-h16-q2", Workload("fd", 12, B=1, T=32768, m=4, d_idx=64, H_I=16, k=128, H=64, n_win=0, Q=2), 8192,
+     [8192], [[32767, 5001]], 128),
 ]
 
 

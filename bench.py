@@ -32,6 +32,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "CSA decode query-tokens/s + achieved HBM GB/s at 128K ctx (1 MI355X)"
 HBM_PEAK_GBPS = 8000.0
+FP8_PEAK_TFLOPS = 5000.0
 
 
 def log(*a):
@@ -113,6 +114,7 @@ def main():
     ap.add_argument("--kernel-reps", type=int, default=64)
     ap.add_argument("--cpu-sample", type=int, default=32, help="sequences the oracle baseline runs (0 = skip)")
     ap.add_argument("--only-index", action="store_true", help="run only indexer launches (for counter passes)")
+    ap.add_argument("--prefill-reps", type=int, default=3, help="timed passes of the 64K prefill chunk (0 = skip)")
     ap.add_argument("--copy-calibration", action="store_true", help="run a plain device copy of known size")
     args = ap.parse_args()
 
@@ -270,10 +272,91 @@ def main():
     if args.only_index:
         result["value"] = None
 
+    if args.prefill_reps > 0 and not args.only_index:
+        del layers, scores_ws, topk_ws, attn_ws
+        torch.cuda.empty_cache()
+        result["prefill"] = prefill_leg(args.prefill_reps)
+
     if args.cpu_sample > 0 and not args.only_index:
         result["cpu_baseline"] = cpu_baseline(w, args.cpu_sample)
 
     print(json.dumps(result), flush=True)
+
+
+def prefill_flops(w) -> float:
+    """Useful indexer multiply-adds (x2) of a causal prefill chunk: query t
+    sees the entries completed by token t, min(N, (t+1) // m) of them."""
+    import numpy as np
+
+    t = np.arange(w.Q, dtype=np.int64)
+    vis = np.minimum(w.N, (t + 1) // w.m)
+    return float(vis.sum()) * w.H_I * w.d_idx * 2.0 * w.B
+
+
+def prefill_leg(reps):
+    """One 65,536-token causal prefill chunk of one layer: compress all 16,384
+    entries, indexer scores (FP8 queries x FP4 keys on the scaled MFMA),
+    top-1024 per query, sparse attention with the window.  Each stage is
+    timed alone with HIP events on the stream it runs on (eager launches:
+    every stage runs for milliseconds)."""
+    import torch
+
+    import compressed_sparse_attention_compressor_amd as csa
+    from synth.workloads import PREFILL as w, params, queries, raw_rows
+
+    dev = "cuda"
+    t_start = time.time()
+    bias, wik = params(w, device=dev)
+    cache = csa.Cache(w.B, w.N, w.m, w.d_idx, device=dev)
+    x, z = raw_rows(w, 0, w.T, device=dev)
+    qs = queries(w, device=dev)
+    q_pos = qs["q_pos"].to(dev)
+    s0 = torch.zeros(w.B, dtype=torch.int32, device=dev)
+    scores = torch.empty(w.B, w.Q, w.N, dtype=torch.float32, device=dev)
+    tws_bytes = csa.workspace_bytes(csa.WS_TOPK, w.B, w.Q, w.k, w.N)
+    tws = torch.empty(max(tws_bytes, 16), dtype=torch.uint8, device=dev)
+    idx = torch.empty(w.B, w.Q, w.k, dtype=torch.int32, device=dev)
+    out = torch.empty(w.B, w.Q, w.H, 576, dtype=torch.bfloat16, device=dev)
+    lse = torch.empty(w.B, w.Q, w.H, dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+    log(f"[bench] prefill inputs ready ({time.time() - t_start:.1f}s)")
+
+    def st_compress():
+        csa.compress(cache, x, z, bias, wik, tok_begin=0)
+        cache.n_entries.fill_(w.N)
+
+    def st_index():
+        csa.index_scores(cache, qs["qI"], qs["w"], q_pos, scores=scores)
+
+    def st_topk():
+        csa.topk(cache, scores, q_pos, w.k, out=idx, ws=tws if tws_bytes else None)
+
+    def st_attn():
+        csa.sparse_attn(cache, qs["q"], q_pos, idx, x, s0, w.n_win, w.softmax_scale, out_dtype=torch.bfloat16,
+                        out=out, lse=lse)
+
+    stages = {"compress": st_compress, "index_scores": st_index, "topk": st_topk, "sparse_attn": st_attn}
+    ms = {}
+    for name, f in stages.items():
+        f()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            f()
+        b.record()
+        torch.cuda.synchronize()
+        ms[name] = a.elapsed_time(b) / reps
+        log(f"[bench] prefill {name}: {ms[name]:.3f} ms")
+    total = sum(ms.values())
+    flops = prefill_flops(w)
+    tflops = flops / (ms["index_scores"] * 1e-3) / 1e12
+    return {"workload": w.name, "q_tokens": w.B * w.Q, "entries": w.N, "top_k": w.k, "index_heads": w.H_I,
+            "d_idx": w.d_idx, "stage_ms": {k: round(v, 4) for k, v in ms.items()}, "ms": round(total, 4),
+            "q_tokens_per_s": round(w.B * w.Q / (total * 1e-3), 1),
+            "indexer_mfma": {"achieved": round(tflops, 2), "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
+                             "frac": round(tflops / FP8_PEAK_TFLOPS, 4), "useful_flops": flops,
+                             "note": "causal useful work only; E4M3 x E2M1 scaled MFMA issues at the FP8 rate"}}
 
 
 def cpu_baseline(w, nseq, min_seconds=10.0):

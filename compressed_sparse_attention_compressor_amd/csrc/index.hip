@@ -47,6 +47,19 @@ __global__ __launch_bounds__(kIdxThreads) void index_scores_kernel(
   const int base = blockIdx.x * kIdxWGEntries + wave * kIdxWaveEntries;
   constexpr int kIters = kIdxWaveEntries / 16;
 
+  // Several queries per workgroup (prefill): a workgroup whose entries are
+  // visible to none of its queries has nothing to score (causal prefill skips
+  // about half the pairs this way; nothing reads those score slots).  One
+  // query (decode) keeps its key stream free of this dependent read.
+  if (QB > 1 && !kCand) {
+    const int nE = min(n_entries[b], N_cap);
+    int vmax = 0;
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb)
+      if (q0 + qb < Q) vmax = max(vmax, min(nE, (q_pos[(int64_t)b * Q + q0 + qb] + 1) / m));
+    if ((int)blockIdx.x * kIdxWGEntries >= vmax) return;
+  }
+
   // 1. Small, cache-resident loads first (queries for LDS staging, head
   //    weights, visibility): vector-memory counters retire in order, so
   //    what is issued before the key stream can be waited for alone.

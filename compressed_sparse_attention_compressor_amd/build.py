@@ -30,11 +30,14 @@ FLAGS = [
     "-I" + os.path.join(ROOT, "include"),
 ]
 SOURCES = ["abi.hip", "compress.hip", "index.hip", "topk.hip", "attn.hip"]
+# The indexer folds every MFMA result through ReLU and the head weights on
+# the vector unit: results written to AGPRs would each need a copy first.
+EXTRA = {"index.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def _compile(src: str) -> str:
     obj = os.path.join(OBJ, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *FLAGS, *EXTRA.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed on {src}:\n{r.stderr}")

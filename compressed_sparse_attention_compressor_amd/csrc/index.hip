@@ -219,6 +219,180 @@ static void launch_idx(dim3 grid, hipStream_t stream, const CacheView &c, const 
       c.ikey, c.iscale, c.n_entries, c.N_cap, c.d_idx, c.m, q_idx, w_idx, H_I, q_pos, Q, cand, C, scores, Ns);
 }
 
+// ---------------------------------------------------------------------------
+// Prefill (many queries, full scan): a GEMM-shaped pass.  Each wave keeps the
+// MFMA fragments of its QW queries (A operands) and head weights in registers
+// for the whole launch and walks one chunk of kPfChunk entries in 64-entry
+// groups; nothing goes through LDS.  Key tiles come in through range-checked
+// buffer loads (reads past the cache row return zero), one group ahead.
+// Per 16-entry tile and query, ReLU + head weights give each lane a partial
+// head sum for one entry; the four tiles of a group are then summed across
+// the four lane groups with two rounds of permlane swaps (a reduce-scatter:
+// lane l ends with entry 16*(l/16) + l%16 = l of the group), so that each
+// query's 64 scores leave in one coalesced 256-byte store.  Causal prefill:
+// a wave stops at the last entry any of its queries can see, and chunks past
+// it exit at once.
+// max(x, 0) as one integer max on the bit pattern (negative floats, -0
+// included, are negative integers): a float max would first quiet its
+// operand, one more instruction per score term.
+__device__ __forceinline__ float relu_bits(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
+
+constexpr int kPfWaves = 4;
+constexpr int kPfChunk = 2048;
+constexpr int kPfMinQ = 64;  // from this many queries per launch on
+
+template <int HT>
+__global__ __launch_bounds__(kPfWaves * 64) void index_prefill_kernel(
+    const uint8_t *__restrict__ ikey, const uint8_t *__restrict__ iscale, const int32_t *__restrict__ n_entries,
+    int N_cap, int d_idx, int m, const uint8_t *__restrict__ q_idx, const float *__restrict__ w_idx, int H_I,
+    const int32_t *__restrict__ q_pos, int Q, float *__restrict__ scores, int n_qblk, int n_chunk) {
+  constexpr int QW = 8 / HT;  // queries per wave
+  // Workgroup i runs on XCD i % 8: the chunks of one query block follow each
+  // other on one XCD, whose L2 then serves that block's queries to all of them.
+  const int L = blockIdx.x;
+  const int sidx = L >> 3;
+  const int c = sidx % n_chunk;
+  const int qblk = (sidx / n_chunk) * 8 + (L & 7);
+  if (qblk >= n_qblk) return;
+  const int b = blockIdx.y;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int g = lane >> 4, r = lane & 15;
+  const int q0 = (qblk * kPfWaves + wave) * QW;
+  if (q0 >= Q) return;
+  const int kb = d_idx / 32;
+
+  // Loads below are unconditional, from clamped addresses, and masked with
+  // bit operations: a load under a condition (even a uniform one) is moved
+  // into a branch that waits for it before the next load is issued.
+  const int nE = min(n_entries[b], N_cap);
+  int pos[QW];
+#pragma unroll
+  for (int qw = 0; qw < QW; ++qw) pos[qw] = q_pos[(int64_t)b * Q + min(q0 + qw, Q - 1)];
+  int vis[QW];
+  int vmax = 0;
+#pragma unroll
+  for (int qw = 0; qw < QW; ++qw) {
+    vis[qw] = max(0, min(nE, (pos[qw] + 1) / m)) & -(int)(q0 + qw < Q);
+    vmax = max(vmax, vis[qw]);
+  }
+  const int e_begin = c * kPfChunk;
+  const int e_end = min(e_begin + kPfChunk, vmax);
+  if (e_begin >= e_end) return;
+
+  // Key tiles: lane (r, g) reads entry e+r's channel block g (16 bytes) and
+  // its scale byte.  Blocks past d_idx (d_idx = 64) read block 0 and meet
+  // zero query channels; their scale is forced to 1.
+  const int rowb = d_idx / 2;
+  const int gg = g < kb ? g : 0;
+  const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
+      (void *)(ikey + (int64_t)b * N_cap * rowb), 0, N_cap * rowb, 0x00020000);
+  const __amdgpu_buffer_rsrc_t srs = __builtin_amdgcn_make_buffer_rsrc(
+      (void *)(iscale + (int64_t)b * N_cap * kb), 0, N_cap * kb, 0x00020000);
+  v4i kv[4];
+  int sb[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int e = e_begin + 16 * j + r;
+    kv[j] = __builtin_amdgcn_raw_buffer_load_b128(krs, e * rowb + gg * 16, 0, 0);
+    sb[j] = __builtin_amdgcn_raw_buffer_load_b8(srs, e * kb + gg, 0, 0);
+  }
+
+  // Query fragments (E4M3 layout: lane group g holds channels 16g..+15 and
+  // 64+16g..+15 of head row r) and head weights (lane l: heads 4(l/16)..+3
+  // of each 16-head tile).  Head rows past H_I and channels past d_idx are
+  // zeroed in A, which zeroes their scores whatever weight they meet; rows
+  // of queries past Q are never stored.
+  v8i A[QW][HT];
+  float w[QW][HT][4];
+#pragma unroll
+  for (int qw = 0; qw < QW; ++qw) {
+    const int64_t qrow = ((int64_t)b * Q + min(q0 + qw, Q - 1)) * H_I;
+#pragma unroll
+    for (int ht = 0; ht < HT; ++ht) {
+      const int h = ht * 16 + r;
+      const uint8_t *qr = q_idx + (qrow + (h < H_I ? h : 0)) * d_idx;
+      const v4i lo = *reinterpret_cast<const v4i *>(qr + 16 * g);
+      const v4i hi = *reinterpret_cast<const v4i *>(qr + (d_idx > 64 ? 64 : 0) + 16 * g);
+      const int ml = -(int)(h < H_I);
+      const int mh = ml & -(int)(d_idx > 64);
+      A[qw][ht] = v8i{lo[0] & ml, lo[1] & ml, lo[2] & ml, lo[3] & ml, hi[0] & mh, hi[1] & mh, hi[2] & mh, hi[3] & mh};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int hh = ht * 16 + g * 4 + i;
+        w[qw][ht][i] = w_idx[qrow + (hh < H_I ? hh : 0)];
+      }
+    }
+  }
+
+  // Score rows: buffer stores through a range of vis[qw] floats, so that
+  // the entries a query cannot see are left untouched without a branch.
+  __amdgpu_buffer_rsrc_t ors[QW];
+#pragma unroll
+  for (int qw = 0; qw < QW; ++qw)
+    ors[qw] = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(scores + ((int64_t)b * Q + min(q0 + qw, Q - 1)) * N_cap), 0, vis[qw] * 4, 0x00020000);
+
+  for (int e64 = e_begin; e64 < e_end; e64 += 64) {
+    float p[QW][4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int sbu = g < kb ? sb[j] : 127;
+      const v8i Bm = {kv[j][0], kv[j][1], kv[j][2], kv[j][3], 0, 0, 0, 0};
+      // query by query: the MFMAs of query qw+1 run while the vector unit
+      // folds the heads of query qw
+      v4f acc[2][HT];
+#pragma unroll
+      for (int qw = 0; qw <= QW; ++qw) {
+        if (qw < QW) {
+#pragma unroll
+          for (int ht = 0; ht < HT; ++ht)
+            acc[qw & 1][ht] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                A[qw][ht], Bm, v4f{0.f, 0.f, 0.f, 0.f}, 0, 4, 0, 127, 0, sbu);
+        }
+        if (qw > 0) {
+          float s = 0.f;
+#pragma unroll
+          for (int ht = 0; ht < HT; ++ht)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) s = fmaf(relu_bits(acc[(qw - 1) & 1][ht][i]), w[qw - 1][ht][i], s);
+          p[qw - 1][j] = s;
+        }
+      }
+      // refill this slot with the same tile of the next group
+      const int en = e64 + 64 + 16 * j + r;
+      kv[j] = __builtin_amdgcn_raw_buffer_load_b128(krs, en * rowb + gg * 16, 0, 0);
+      sb[j] = __builtin_amdgcn_raw_buffer_load_b8(srs, en * kb + gg, 0, 0);
+    }
+    // Reduce-scatter over the lane groups: after the 32-lane swaps the low
+    // half holds tiles 0/1 and the high half tiles 2/3 (sums over lane groups
+    // g and g^2); after the 16-lane swap, row g holds tile g (all four groups).
+#pragma unroll
+    for (int qw = 0; qw < QW; ++qw) {
+      const auto x = __builtin_amdgcn_permlane32_swap(__float_as_uint(p[qw][0]), __float_as_uint(p[qw][2]), false,
+                                                      false);
+      const auto y = __builtin_amdgcn_permlane32_swap(__float_as_uint(p[qw][1]), __float_as_uint(p[qw][3]), false,
+                                                      false);
+      const float k0 = __uint_as_float(x[0]) + __uint_as_float(x[1]);
+      const float k1 = __uint_as_float(y[0]) + __uint_as_float(y[1]);
+      const auto z = __builtin_amdgcn_permlane16_swap(__float_as_uint(k0), __float_as_uint(k1), false, false);
+      const float res = __uint_as_float(z[0]) + __uint_as_float(z[1]);
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(res), ors[qw], (e64 + lane) * 4, 0, 0);
+    }
+  }
+}
+
+template <int HT>
+static void launch_prefill(const CacheView &c, const uint8_t *q_idx, const float *w_idx, int H_I,
+                           const int32_t *q_pos, int Q, float *scores, hipStream_t stream) {
+  constexpr int QW = 8 / HT;
+  const int n_qblk = (Q + kPfWaves * QW - 1) / (kPfWaves * QW);
+  const int n_chunk = (c.N_cap + kPfChunk - 1) / kPfChunk;
+  dim3 grid(((n_qblk + 7) / 8) * 8 * n_chunk, c.B);
+  index_prefill_kernel<HT><<<grid, kPfWaves * 64, 0, stream>>>(c.ikey, c.iscale, c.n_entries, c.N_cap, c.d_idx, c.m,
+                                                                q_idx, w_idx, H_I, q_pos, Q, scores, n_qblk, n_chunk);
+}
+
 template <int HT>
 static void dispatch_idx(const CacheView &c, const uint8_t *q_idx, const float *w_idx, int H_I, const int32_t *q_pos,
                          int Q, const int32_t *cand, int C, float *scores, hipStream_t stream) {
@@ -226,6 +400,8 @@ static void dispatch_idx(const CacheView &c, const uint8_t *q_idx, const float *
     const int Ns = C;
     dim3 grid((C + kIdxWGEntries - 1) / kIdxWGEntries, Q, c.B);
     launch_idx<HT, 1, true>(grid, stream, c, q_idx, w_idx, H_I, q_pos, Q, cand, C, scores, Ns);
+  } else if (Q >= kPfMinQ) {
+    launch_prefill<HT>(c, q_idx, w_idx, H_I, q_pos, Q, scores, stream);
   } else if (Q >= 4) {
     dim3 grid((c.N_cap + kIdxWGEntries - 1) / kIdxWGEntries, (Q + 3) / 4, c.B);
     launch_idx<HT, 4, false>(grid, stream, c, q_idx, w_idx, H_I, q_pos, Q, nullptr, 0, scores, c.N_cap);

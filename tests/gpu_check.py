@@ -92,6 +92,28 @@ def check_topk(g_idx, o_idx, js, scores, rel=1e-4, what=""):
     return len(d) // 2
 
 
+def index_score_tol(qI_u8, w_f32, iscale_rows, ref):
+    """Per-entry bound on |GPU score - oracle score| for the indexer.
+
+    Two parts: fp32 accumulation (1e-5 of the row's largest score), and the
+    matrix instruction's handling of E4M3 subnormal query codes (exponent
+    field 0, mantissa m): their products with E2M1 codes are kept only to a
+    multiple of 2^-9 before the block scale, so each such product may lose up
+    to 2^-10 x its block's scale (measured on gfx950; E4M3 x E2M1 products of
+    normal codes come out exact).  The loss passes through ReLU (1-Lipschitz)
+    and the head weight: sum_h |w_h| * sum_c [q_hc subnormal] 2^-10 * S_j(c).
+    """
+    q = np.asarray(qI_u8, dtype=np.uint8)
+    sub = ((q & 0x78) == 0) & ((q & 0x07) != 0)                 # [H][d]
+    nb = q.shape[1] // 32
+    n_hb = sub.reshape(q.shape[0], nb, 32).sum(axis=2)           # [H][nb]
+    wa = np.abs(np.asarray(w_f32, dtype=np.float64))
+    per_blk = (n_hb * wa[:, None]).sum(axis=0)                   # [nb]
+    S = np.exp2(np.asarray(iscale_rows, dtype=np.float64)[:, :nb] - 127.0)  # [V][nb]
+    scale = np.abs(ref).max() if len(ref) else 0.0
+    return 1e-5 * scale + 2.0 ** -10 * (S @ per_blk)
+
+
 def row_rel_err(g, r):
     g = np.asarray(g, np.float64)
     r = np.asarray(r, np.float64)

@@ -17,6 +17,7 @@ from gpu_check import (
     compare_bf16_rounding,
     compare_mxfp4,
     decode_cache_rows,
+    index_score_tol,
     row_rel_err,
 )
 from synth import TensorId, normal_bf16, normal_e4m3, normal_f32, uniform_int
@@ -210,6 +211,99 @@ def test_index_topk_parity(name, w, N_cap, n_entries, pos, k):
                 scale = np.abs(s).max() + 1e-30
                 assert np.abs(sc[b, t, :len(sel)] - r).max() <= 1e-5 * scale
             assert np.all(np.isnan(sc[b, t, len(sel):]))
+
+
+@pytest.mark.parametrize("Q", [1, 6, 254])
+def test_indexer_single_products(Q):
+    """Every E4M3 code against every E2M1 code, one product per score: query
+    t has one nonzero channel (code t, skipping the two NaN codes) in head 0,
+    weight 1, every key channel of entry j holds E2M1 code j, so that
+    score(t, j) = max(0, e4m3(t) * e2m1(j)).  Normal E4M3 codes must come out
+    exact; subnormal ones within the 2^-10 the indexer tolerance allows.
+    Q picks the launch shape (one query, several per workgroup, prefill)."""
+    codes = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], dtype=np.uint8)
+    sel = codes if Q == len(codes) else np.resize(np.array([0x01, 0x83, 0x08, 0xB5, 0x7E, 0xFE], np.uint8), Q)
+    H_I, d, N = 16, 128, 16
+    qI = np.zeros((1, Q, H_I, d), np.uint8)
+    for t, c in enumerate(sel):
+        qI[0, t, 0, (37 * t) % d] = c
+    wI = np.zeros((1, Q, H_I), np.float32)
+    wI[0, :, 0] = 1.0
+    e2 = np.arange(16, dtype=np.uint8)
+    ikey = np.repeat((e2 | (e2 << 4))[:, None], d // 2, axis=1)[None]
+    iscale = np.full((1, N, d // 32), 127, np.uint8)
+    planes = dict(nope=np.zeros((1, N, 256), np.uint8), nscale=np.full((1, N, 16), 127, np.uint8),
+                  rope=np.zeros((1, N, 64), np.uint16), ikey=ikey, iscale=iscale)
+    cache = _gpu_cache(planes, 1, N, 4, d, [N])
+    pos = torch.full((1, Q), 4 * N - 1, dtype=torch.int32, device=DEV)
+    sc = csa.index_scores(cache, torch.from_numpy(qI).to(DEV), torch.from_numpy(wI).to(DEV), pos)
+    got = _np(sc)[0].astype(np.float64)
+    qv = O.e4m3_to_f64(sel)
+    kv = O.e2m1_to_f64(e2)
+    ref = np.maximum(qv[:, None] * kv[None, :], 0.0)
+    sub = ((sel & 0x78) == 0) & ((sel & 0x07) != 0)
+    assert np.array_equal(got[~sub], ref[~sub])
+    if sub.any():
+        assert np.abs(got[sub] - ref[sub]).max() <= 2.0 ** -10
+
+
+SCORE_CASES = [
+    # one query (decode), a handful (several queries per workgroup), then
+    # prefill-sized launches: ragged query blocks, entry chunks with a ragged
+    # tail, head counts of 16 / 20 / 32 / 64, both key widths, sorted causal
+    # positions and unsorted ones
+    ("decode", Workload("s1", 21, B=2, T=8000, m=4, d_idx=128, H_I=32, k=1, H=64, n_win=0), 2000, [2000, 1234],
+     "last"),
+    ("qb4", Workload("s2", 22, B=1, T=8000, m=4, d_idx=128, H_I=32, k=1, H=64, n_win=0, Q=7), 2000, [2000],
+     "causal"),
+    ("prefill-h32", Workload("s3", 23, B=2, T=9300, m=4, d_idx=128, H_I=32, k=1, H=64, n_win=0, Q=100), 2300,
+     [2300, 1500], "causal"),
+    ("prefill-h32-unsorted", Workload("s4", 24, B=1, T=9300, m=4, d_idx=128, H_I=32, k=1, H=64, n_win=0, Q=64),
+     2300, [2290], "random"),
+    ("prefill-h16-d64", Workload("s5", 25, B=1, T=18000, m=4, d_idx=64, H_I=16, k=1, H=64, n_win=0, Q=70), 4500,
+     [4500], "causal"),
+    ("qb4-h16-d64", Workload("s5", 25, B=1, T=18000, m=4, d_idx=64, H_I=16, k=1, H=64, n_win=0, Q=30), 4500,
+     [4500], "causal"),
+    ("prefill-h20", Workload("s6", 26, B=1, T=4000, m=4, d_idx=128, H_I=20, k=1, H=64, n_win=0, Q=66), 1000, [1000],
+     "causal"),
+    ("prefill-h64", Workload("s7", 27, B=1, T=2800, m=4, d_idx=128, H_I=64, k=1, H=64, n_win=0, Q=65), 700, [700],
+     "causal"),
+]
+
+
+@pytest.mark.parametrize("name,w,N_cap,n_entries,kind", SCORE_CASES, ids=[c[0] for c in SCORE_CASES])
+def test_index_scores_stage_parity(name, w, N_cap, n_entries, kind):
+    """Every score the indexer writes against the oracle, and every slot it
+    must not write (entries a query cannot see) left as it was."""
+    rng = np.random.default_rng(w.cfg)
+    if kind == "last":
+        pos = np.array([[w.T - 1 - 7 * b] for b in range(w.B)], dtype=np.int32)
+    elif kind == "causal":
+        pos = np.stack([np.sort(rng.integers(0, w.T + 40, w.Q)) for _ in range(w.B)]).astype(np.int32)
+        pos[:, 0] = 0
+        pos[:, -1] = w.T - 1
+    else:
+        pos = rng.integers(-1, w.T, (w.B, w.Q)).astype(np.int32)
+    planes, qs = _index_case(w, N_cap, n_entries, pos, 1)
+    cache = _gpu_cache(planes, w.B, N_cap, w.m, w.d_idx, n_entries)
+    sentinel = 0x7FC0ABCD
+    buf = torch.full((w.B, pos.shape[1], N_cap), sentinel, dtype=torch.int32, device=DEV)
+    csa.index_scores(cache, qs["qI"].to(DEV), qs["w"].to(DEV), qs["q_pos"].to(DEV), scores=buf.view(torch.float32))
+    got = _np(buf)
+    ik, isc = planes["ikey"].numpy(), planes["iscale"].numpy()
+    for b in range(w.B):
+        for t in range(pos.shape[1]):
+            V = O.visible_count(int(pos[b, t]), w.m, n_entries[b])
+            assert np.all(got[b, t, V:] == sentinel), f"{name} b={b} t={t}: wrote past the visible entries"
+            if V == 0:
+                continue
+            qI, wt = qs["qI"][b, t].numpy(), qs["w"][b, t].numpy()
+            ref = O.index_scores(ik[b], isc[b], qI, wt, np.arange(V))
+            g = got[b, t, :V].view(np.float32).astype(np.float64)
+            tol = index_score_tol(qI, wt, isc[b, :V], ref)
+            bad = np.nonzero(np.abs(g - ref) > tol)[0]
+            assert len(bad) == 0, (f"{name} b={b} t={t} pos={pos[b, t]} V={V}: {len(bad)} bad entries, first "
+                                   f"{bad[:8].tolist()}, got {g[bad[:4]].tolist()} want {ref[bad[:4]].tolist()}")
 
 
 def test_reindex_candidates_parity():

@@ -32,7 +32,10 @@ FLAGS = [
 SOURCES = ["abi.hip", "compress.hip", "index.hip", "topk.hip", "attn.hip"]
 # The indexer folds every MFMA result through ReLU and the head weights on
 # the vector unit: results written to AGPRs would each need a copy first.
-EXTRA = {"index.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+# Attention has no NaN inputs or intermediates by construction (masked logits
+# are -inf, never NaN): without NaN semantics a float max needs no operand
+# quieting first and folds with its DPP source.
+EXTRA = {"index.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"], "attn.hip": ["-fno-honor-nans"]}
 
 
 def _compile(src: str) -> str:

@@ -343,17 +343,23 @@ __global__ __launch_bounds__(HG * 128) void attn_kernel(AttnArgs a) {
       }
     }
     // P (bf16, or hi + lo) through this wave's LDS tile into the A layout
-    // (LDS operations of one wave complete in order)
+    // (LDS operations of one wave complete in order).  The product's key
+    // order is permuted against the tile rows: MFMA key 8b + 4h + e (b < 4,
+    // h, e < 4) is tile row 16h + 4b + e, so that each transposed V read
+    // below covers 8 consecutive rows per 32 lanes, which a 1184-byte row
+    // stride spreads over all LDS banks (measured conflict-free); tile row
+    // r goes to P column 8(r/4) + r%4, tile row 16 + r to 8(r/4) + 4 + r%4.
     uint16_t *pw = &Pl[wave][0][0];
+    const int pc0 = 8 * (r >> 2) + (r & 3);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const uint32_t hi0 = f32_to_bf16(p0[i]), hi1 = f32_to_bf16(p1[i]);
-      pw[(4 * g + i) * kPRow + r] = (uint16_t)hi0;
-      pw[(4 * g + i) * kPRow + 16 + r] = (uint16_t)hi1;
+      pw[(4 * g + i) * kPRow + pc0] = (uint16_t)hi0;
+      pw[(4 * g + i) * kPRow + pc0 + 4] = (uint16_t)hi1;
       if (kSplitP) {
         uint16_t *pl = &Pl[wave][kSplitP ? 1 : 0][0];
-        pl[(4 * g + i) * kPRow + r] = (uint16_t)f32_to_bf16(p0[i] - bf16_to_f32(hi0));
-        pl[(4 * g + i) * kPRow + 16 + r] = (uint16_t)f32_to_bf16(p1[i] - bf16_to_f32(hi1));
+        pl[(4 * g + i) * kPRow + pc0] = (uint16_t)f32_to_bf16(p0[i] - bf16_to_f32(hi0));
+        pl[(4 * g + i) * kPRow + pc0 + 4] = (uint16_t)f32_to_bf16(p1[i] - bf16_to_f32(hi1));
       }
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
@@ -363,14 +369,14 @@ __global__ __launch_bounds__(HG * 128) void attn_kernel(AttnArgs a) {
     v8bf Pb;
     if (kSplitP) Pb = *reinterpret_cast<const v8bf *>(&Pl[wave][kSplitP ? 1 : 0][r * kPRow + 8 * g]);
     // O += P V over this wave's 18 channel tiles; lane (g, r) needs
-    // V[keys 8g..8g+7][channel c + r]: two transposed 4x16 reads of the
-    // key-major tile.
+    // V[MFMA keys 8g..8g+7][channel c + r], i.e. tile rows 4g..4g+3 and
+    // 16+4g..16+4g+3: two transposed 4x16 reads of the key-major tile.
     typedef __attribute__((address_space(3))) v4s lds_v4s;
-    const uint16_t *vb = K + (8 * g + (r >> 2)) * kKRow + cbase + 4 * (r & 3);
+    const uint16_t *vb = K + (4 * g + (r >> 2)) * kKRow + cbase + 4 * (r & 3);
 #pragma unroll
     for (int j = 0; j < kHalfNT; ++j) {
       const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s *)(vb + 16 * j));
-      const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s *)(vb + 4 * kKRow + 16 * j));
+      const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s *)(vb + 16 * kKRow + 16 * j));
       const v8s both = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
       const v8bf Bv = __builtin_bit_cast(v8bf, both);
       O[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Pa, Bv, O[j], 0, 0, 0);

@@ -125,7 +125,10 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t x) {
 // (up to commutation) in every lane.
 template <int kCtrl>
 __device__ __forceinline__ float dpp_f32(float x) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), kCtrl, 0xF, 0xF, false));
+  // every lane has a valid source under these controls, so the old value is
+  // never used: leaving it undefined lets the move fold into the consuming
+  // max/add as its DPP source operand
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), kCtrl, 0xF, 0xF, true));
 }
 __device__ __forceinline__ float row16_max(float v) {
   v = fmaxf(v, dpp_f32<0xB1>(v));   // quad_perm [1,0,3,2]

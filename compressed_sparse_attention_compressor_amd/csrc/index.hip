@@ -238,15 +238,19 @@ static void launch_idx(dim3 grid, hipStream_t stream, const CacheView &c, const 
 __device__ __forceinline__ float relu_bits(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
 
 constexpr int kPfWaves = 4;
-constexpr int kPfChunk = 2048;
+constexpr int kPfChunk = 1024;
 constexpr int kPfMinQ = 64;  // from this many queries per launch on
 
-template <int HT>
+// HT: head tiles of 16; DI: d_idx (64 or 128), fixed at compile time so that
+// key addresses are a per-lane constant plus a uniform group offset plus an
+// immediate per tile (no per-load address arithmetic).
+template <int HT, int DI>
 __global__ __launch_bounds__(kPfWaves * 64) void index_prefill_kernel(
     const uint8_t *__restrict__ ikey, const uint8_t *__restrict__ iscale, const int32_t *__restrict__ n_entries,
-    int N_cap, int d_idx, int m, const uint8_t *__restrict__ q_idx, const float *__restrict__ w_idx, int H_I,
+    int N_cap, int m, const uint8_t *__restrict__ q_idx, const float *__restrict__ w_idx, int H_I,
     const int32_t *__restrict__ q_pos, int Q, float *__restrict__ scores, int n_qblk, int n_chunk) {
   constexpr int QW = 8 / HT;  // queries per wave
+  constexpr int d_idx = DI;
   // Workgroup i runs on XCD i % 8: the chunks of one query block follow each
   // other on one XCD, whose L2 then serves that block's queries to all of them.
   const int L = blockIdx.x;
@@ -260,7 +264,7 @@ __global__ __launch_bounds__(kPfWaves * 64) void index_prefill_kernel(
   const int g = lane >> 4, r = lane & 15;
   const int q0 = (qblk * kPfWaves + wave) * QW;
   if (q0 >= Q) return;
-  const int kb = d_idx / 32;
+  constexpr int kb = d_idx / 32;
 
   // Loads below are unconditional, from clamped addresses, and masked with
   // bit operations: a load under a condition (even a uniform one) is moved
@@ -283,19 +287,21 @@ __global__ __launch_bounds__(kPfWaves * 64) void index_prefill_kernel(
   // Key tiles: lane (r, g) reads entry e+r's channel block g (16 bytes) and
   // its scale byte.  Blocks past d_idx (d_idx = 64) read block 0 and meet
   // zero query channels; their scale is forced to 1.
-  const int rowb = d_idx / 2;
+  constexpr int rowb = d_idx / 2;
   const int gg = g < kb ? g : 0;
   const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
       (void *)(ikey + (int64_t)b * N_cap * rowb), 0, N_cap * rowb, 0x00020000);
   const __amdgpu_buffer_rsrc_t srs = __builtin_amdgcn_make_buffer_rsrc(
       (void *)(iscale + (int64_t)b * N_cap * kb), 0, N_cap * kb, 0x00020000);
+  // per-lane part of the key / scale offsets; the group part is uniform
+  // (scalar offset), the tile part an immediate
+  const int kvo = r * rowb + gg * 16, svo = r * kb + gg;
   v4i kv[4];
   int sb[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const int e = e_begin + 16 * j + r;
-    kv[j] = __builtin_amdgcn_raw_buffer_load_b128(krs, e * rowb + gg * 16, 0, 0);
-    sb[j] = __builtin_amdgcn_raw_buffer_load_b8(srs, e * kb + gg, 0, 0);
+    kv[j] = __builtin_amdgcn_raw_buffer_load_b128(krs, kvo + 16 * j * rowb, e_begin * rowb, 0);
+    sb[j] = __builtin_amdgcn_raw_buffer_load_b8(srs, svo + 16 * j * kb, e_begin * kb, 0);
   }
 
   // Query fragments (E4M3 layout: lane group g holds channels 16g..+15 and
@@ -360,9 +366,8 @@ __global__ __launch_bounds__(kPfWaves * 64) void index_prefill_kernel(
         }
       }
       // refill this slot with the same tile of the next group
-      const int en = e64 + 64 + 16 * j + r;
-      kv[j] = __builtin_amdgcn_raw_buffer_load_b128(krs, en * rowb + gg * 16, 0, 0);
-      sb[j] = __builtin_amdgcn_raw_buffer_load_b8(srs, en * kb + gg, 0, 0);
+      kv[j] = __builtin_amdgcn_raw_buffer_load_b128(krs, kvo + 16 * j * rowb, (e64 + 64) * rowb, 0);
+      sb[j] = __builtin_amdgcn_raw_buffer_load_b8(srs, svo + 16 * j * kb, (e64 + 64) * kb, 0);
     }
     // Reduce-scatter over the lane groups: after the 32-lane swaps the low
     // half holds tiles 0/1 and the high half tiles 2/3 (sums over lane groups
@@ -377,7 +382,7 @@ __global__ __launch_bounds__(kPfWaves * 64) void index_prefill_kernel(
       const float k1 = __uint_as_float(y[0]) + __uint_as_float(y[1]);
       const auto z = __builtin_amdgcn_permlane16_swap(__float_as_uint(k0), __float_as_uint(k1), false, false);
       const float res = __uint_as_float(z[0]) + __uint_as_float(z[1]);
-      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(res), ors[qw], (e64 + lane) * 4, 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(res), ors[qw], lane * 4, e64 * 4, 0);
     }
   }
 }
@@ -389,8 +394,12 @@ static void launch_prefill(const CacheView &c, const uint8_t *q_idx, const float
   const int n_qblk = (Q + kPfWaves * QW - 1) / (kPfWaves * QW);
   const int n_chunk = (c.N_cap + kPfChunk - 1) / kPfChunk;
   dim3 grid(((n_qblk + 7) / 8) * 8 * n_chunk, c.B);
-  index_prefill_kernel<HT><<<grid, kPfWaves * 64, 0, stream>>>(c.ikey, c.iscale, c.n_entries, c.N_cap, c.d_idx, c.m,
-                                                                q_idx, w_idx, H_I, q_pos, Q, scores, n_qblk, n_chunk);
+  if (c.d_idx == 128)
+    index_prefill_kernel<HT, 128><<<grid, kPfWaves * 64, 0, stream>>>(
+        c.ikey, c.iscale, c.n_entries, c.N_cap, c.m, q_idx, w_idx, H_I, q_pos, Q, scores, n_qblk, n_chunk);
+  else
+    index_prefill_kernel<HT, 64><<<grid, kPfWaves * 64, 0, stream>>>(
+        c.ikey, c.iscale, c.n_entries, c.N_cap, c.m, q_idx, w_idx, H_I, q_pos, Q, scores, n_qblk, n_chunk);
 }
 
 template <int HT>

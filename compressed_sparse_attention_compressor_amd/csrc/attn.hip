@@ -493,39 +493,53 @@ __global__ __launch_bounds__(kMergeThreads) void attn_merge_kernel(const float *
   const int c8 = (int)(item % kGroups) * 8;
   const int64_t qrow = qh / H, hh = qh % H;
   auto pr_of = [&](int s) { return (qrow * nsplit + s) * H + hh; };
-  float M = -INFINITY;
-  for (int s = 0; s < nsplit; ++s) M = fmaxf(M, ws_ml[pr_of(s) * 2]);
+  // One round of loads for up to kMergeUnroll splits: every split's (m, l)
+  // and partial row are issued together and the maximum is formed from the
+  // loaded values (a separate pass for the maximum would wait on memory twice).
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   float L = 0.f;
-  if (M != -INFINITY) {
-    for (int s0 = 0; s0 < nsplit; s0 += kMergeUnroll) {
-      float wgt[kMergeUnroll], v[kMergeUnroll][8];
+  float M = -INFINITY;
+  for (int s0 = 0; s0 < nsplit; s0 += kMergeUnroll) {
+    float2 ml[kMergeUnroll];
+    float v[kMergeUnroll][8];
+#pragma unroll
+    for (int u = 0; u < kMergeUnroll; ++u) {
+      const int64_t pr = pr_of(min(s0 + u, nsplit - 1));
+      ml[u] = *reinterpret_cast<const float2 *>(ws_ml + pr * 2);
+      if (kBf16) {
+        const uint4 p = *reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(ws_o) + pr * kD + c8);
+        const uint32_t w4[4] = {p.x, p.y, p.z, p.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          v[u][2 * j] = bf16_to_f32(w4[j] & 0xFFFFu);
+          v[u][2 * j + 1] = bf16_to_f32(w4[j] >> 16);
+        }
+      } else {
+        const float4 p0 = *reinterpret_cast<const float4 *>(ws_o + pr * kD + c8);
+        const float4 p1 = *reinterpret_cast<const float4 *>(ws_o + pr * kD + c8 + 4);
+        v[u][0] = p0.x; v[u][1] = p0.y; v[u][2] = p0.z; v[u][3] = p0.w;
+        v[u][4] = p1.x; v[u][5] = p1.y; v[u][6] = p1.z; v[u][7] = p1.w;
+      }
+    }
+    // running maximum over the splits seen so far; earlier sums are rescaled
+    // when it moves (only with more than kMergeUnroll splits)
+    float Mn = M;
+#pragma unroll
+    for (int u = 0; u < kMergeUnroll; ++u)
+      if (s0 + u < nsplit) Mn = fmaxf(Mn, ml[u].x);
+    if (Mn != -INFINITY) {
+      const float r = M == -INFINITY ? 0.f : exp2f(M - Mn);
+      L *= r;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) acc[j] *= r;
 #pragma unroll
       for (int u = 0; u < kMergeUnroll; ++u) {
-        const int s = min(s0 + u, nsplit - 1);
-        const int64_t pr = pr_of(s);
-        const float2 ml = *reinterpret_cast<const float2 *>(ws_ml + pr * 2);
-        wgt[u] = (s0 + u < nsplit && ml.x != -INFINITY) ? exp2f(ml.x - M) : 0.f;
-        L += wgt[u] * (wgt[u] != 0.f ? ml.y : 0.f);
-        if (kBf16) {
-          const uint4 p = *reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(ws_o) + pr * kD + c8);
-          const uint32_t w4[4] = {p.x, p.y, p.z, p.w};
+        const float wgt = (s0 + u < nsplit && ml[u].x != -INFINITY) ? exp2f(ml[u].x - Mn) : 0.f;
+        L += wgt * (wgt != 0.f ? ml[u].y : 0.f);
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            v[u][2 * j] = bf16_to_f32(w4[j] & 0xFFFFu);
-            v[u][2 * j + 1] = bf16_to_f32(w4[j] >> 16);
-          }
-        } else {
-          const float4 p0 = *reinterpret_cast<const float4 *>(ws_o + pr * kD + c8);
-          const float4 p1 = *reinterpret_cast<const float4 *>(ws_o + pr * kD + c8 + 4);
-          v[u][0] = p0.x; v[u][1] = p0.y; v[u][2] = p0.z; v[u][3] = p0.w;
-          v[u][4] = p1.x; v[u][5] = p1.y; v[u][6] = p1.z; v[u][7] = p1.w;
-        }
+        for (int j = 0; j < 8; ++j) acc[j] = fmaf(wgt, v[u][j], acc[j]);
       }
-#pragma unroll
-      for (int u = 0; u < kMergeUnroll; ++u)
-#pragma unroll
-        for (int j = 0; j < 8; ++j) acc[j] = fmaf(wgt[u], v[u][j], acc[j]);
+      M = Mn;
     }
   }
   const float inv = L > 0.f ? 1.f / L : 0.f;

@@ -115,6 +115,8 @@ def main():
     ap.add_argument("--cpu-sample", type=int, default=32, help="sequences the oracle baseline runs (0 = skip)")
     ap.add_argument("--only-index", action="store_true", help="run only indexer launches (for counter passes)")
     ap.add_argument("--prefill-reps", type=int, default=3, help="timed passes of the 64K prefill chunk (0 = skip)")
+    ap.add_argument("--hca-steps", type=int, default=256, help="graph-timed HCA 1M decode steps (0 = skip)")
+    ap.add_argument("--csa2-steps", type=int, default=64, help="graph-timed CSA2 two-layer 1M decode steps (0 = skip)")
     ap.add_argument("--copy-calibration", action="store_true", help="run a plain device copy of known size")
     args = ap.parse_args()
 
@@ -277,6 +279,13 @@ def main():
         torch.cuda.empty_cache()
         result["prefill"] = prefill_leg(args.prefill_reps)
 
+    if args.hca_steps > 0 and not args.only_index:
+        torch.cuda.empty_cache()
+        result["hca"] = hca_leg(K=args.hca_steps)
+    if args.csa2_steps > 0 and not args.only_index:
+        torch.cuda.empty_cache()
+        result["csa2"] = csa2_leg(K=args.csa2_steps)
+
     if args.cpu_sample > 0 and not args.only_index:
         result["cpu_baseline"] = cpu_baseline(w, args.cpu_sample)
 
@@ -357,6 +366,226 @@ def prefill_leg(reps):
             "indexer_mfma": {"achieved": round(tflops, 2), "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
                              "frac": round(tflops / FP8_PEAK_TFLOPS, 4), "useful_flops": flops,
                              "note": "causal useful work only; E4M3 x E2M1 scaled MFMA issues at the FP8 rate"}}
+
+
+def _capture(fn):
+    """A HIP graph of fn's launches (after one eager run on the capture stream)."""
+    import torch
+
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fn()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        fn()
+    torch.cuda.synchronize()
+    return g
+
+
+def _graph_ms(fn, units, reps=5):
+    """Milliseconds per unit of a graph of fn (which launches `units` units)."""
+    import torch
+
+    g = _capture(fn)
+    g.replay()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        g.replay()
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / (reps * units)
+
+
+def _layer_caches(w, planes, L, dev):
+    import torch
+
+    import compressed_sparse_attention_compressor_amd as csa
+
+    n_ent = torch.full((w.B,), w.N, dtype=torch.int32, device=dev)
+    out = []
+    for l in range(L):
+        pl = {k: (v if l == 0 else v.clone()) for k, v in planes.items()}
+        out.append(csa.Cache(w.B, w.N, w.m, w.d_idx, device=dev, planes=dict(
+            nope=pl["nope"], nscale=pl["nscale"], rope=pl["rope"], ikey=pl.get("ikey"), iscale=pl.get("iscale"),
+            n_entries=n_ent.clone())))
+    return out
+
+
+def _oracle_threads():
+    try:
+        import threadpoolctl
+        return int(max([p.get("num_threads", 1) for p in threadpoolctl.threadpool_info()] or [1]))
+    except Exception:  # pragma: no cover
+        return 1
+
+
+def hca_leg(L=16, K=256):
+    """HCA dense decode: 8 sequences at 1,048,576 raw tokens (m = 128, 8,192
+    entries), every head attending to every entry plus the window; one step
+    = one decode query per sequence.  Layer caches rotate over L copies
+    (16 x 26 MB).  The compressor runs once per 128 tokens and is timed on
+    its own (one block per sequence).  The oracle times one sequence."""
+    import dataclasses
+
+    import torch
+
+    import compressed_sparse_attention_compressor_amd as csa
+    import oracle as O
+    from synth.workloads import HCA_DECODE as w, as_u16, params, queries, raw_rows, synthetic_cache
+
+    dev = "cuda"
+    planes = synthetic_cache(w, device=dev)
+    caches = _layer_caches(w, planes, L, dev)
+    x_win, _ = raw_rows(w, w.T - w.n_win, w.T, device=dev)
+    s0 = torch.full((w.B,), w.T - w.n_win, dtype=torch.int32, device=dev)
+    qs = [queries(dataclasses.replace(w, cfg=w.cfg + 100 * l), device=dev) for l in range(L)]
+    outs = [torch.empty(w.B, 1, w.H, 576, dtype=torch.bfloat16, device=dev) for _ in range(L)]
+    lses = [torch.empty(w.B, 1, w.H, dtype=torch.float32, device=dev) for _ in range(L)]
+    wsb = csa.workspace_bytes(csa.WS_DENSE_ATTN, w.B, 1, w.H, w.N, w.n_win)
+    ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device=dev)
+
+    def steps():
+        for i in range(K):
+            l = i % L
+            csa.hca_dense_attn(caches[l], qs[l]["q"], qs[l]["q_pos"], x_win, s0, w.n_win, w.softmax_scale,
+                               out_dtype=torch.bfloat16, ws=ws, out=outs[l], lse=lses[l])
+
+    ms = _graph_ms(steps, K)
+    bias, _ = params(w, device=dev)
+    xb, zb = raw_rows(w, w.T - w.m, w.T, device=dev)
+
+    def blocks():
+        for _ in range(16):
+            csa.compress(caches[0], xb, zb, bias, None, tok_begin=w.T - w.m)
+
+    comp_ms = _graph_ms(blocks, 16)
+    per_q = w.N * 400 + 2 * w.n_win * 576 + 2 * 2 * w.H * 576
+    step_bytes = w.B * per_q
+    flops = w.B * 4.0 * w.H * 576 * (w.N + w.n_win)
+    gbps = step_bytes / (ms * 1e-3) / 1e9
+    tfs = flops / (ms * 1e-3) / 1e12
+    log(f"[bench] hca step {ms * 1e3:.2f} us, {gbps:.0f} GB/s, {tfs:.1f} TFLOP/s; compress block {comp_ms * 1e3:.2f} us")
+
+    # oracle, one sequence of the same step
+    pc = {k: v[0].cpu() for k, v in planes.items()}
+    t0 = time.perf_counter()
+    O.dense_attention(as_u16(qs[0]["q"][0, 0]), pc["nope"].numpy(), pc["nscale"].numpy(), as_u16(pc["rope"]),
+                      as_u16(x_win[0]), w.T - w.n_win, w.T - 1, w.n_win, w.softmax_scale, w.m, w.N)
+    dt = time.perf_counter() - t0
+    return {"workload": w.name, "B": w.B, "context": w.T, "m": w.m, "entries": w.N, "heads": w.H, "n_win": w.n_win,
+            "layers_rotated": L, "steps": K, "ms_per_step": round(ms, 6),
+            "q_tokens_per_s": round(w.B / (ms * 1e-3), 1), "step_bytes": step_bytes,
+            "achieved_GBps": round(gbps, 1), "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4),
+            "step_flops": flops, "achieved_TFLOPs_bf16": round(tfs, 2), "mfma_frac_bf16": round(tfs / 2500.0, 4),
+            "compress_block_us": round(comp_ms * 1e3, 3),
+            "cpu_oracle": {"value": round(1.0 / dt, 3), "unit": "query-tokens/s", "cores": _oracle_threads(),
+                           "sample": f"one sequence's decode query over {w.N} entries + {w.n_win} window rows: "
+                                     f"{dt:.2f} s"}}
+
+
+def csa2_leg(L=8, K=64):
+    """CSA2 two-layer decode: 4 sequences at 1,048,576 raw tokens (262,144
+    entries); layer A scores every entry and keeps its top-2,048 and attends
+    to them; layer B rescores A's 2,048 with its own indexer queries, keeps
+    512 and attends over A's cache with its own window.  One step = both
+    layers for one query per sequence.  L rotating cache copies (8 x 491 MB).
+    The oracle times layer A's indexer and both attentions for one sequence."""
+    import dataclasses
+
+    import torch
+
+    import compressed_sparse_attention_compressor_amd as csa
+    import oracle as O
+    from synth.workloads import CSA2_DECODE as w, as_u16, queries, raw_rows, second_layer_window, synthetic_cache
+
+    dev = "cuda"
+    planes = synthetic_cache(w, device=dev)
+    caches = _layer_caches(w, planes, L, dev)
+    x_win, _ = raw_rows(w, w.T - w.n_win, w.T, device=dev)
+    xb_win = second_layer_window(w, w.T - w.n_win, w.T, device=dev)
+    s0 = torch.full((w.B,), w.T - w.n_win, dtype=torch.int32, device=dev)
+    wl = [dataclasses.replace(w, cfg=w.cfg + 100 * l) for l in range(L)]
+    qa = [queries(x, device=dev) for x in wl]
+    qb = [queries(x, device=dev, second=True) for x in wl]
+    ia = [torch.empty(w.B, 1, w.k, dtype=torch.int32, device=dev) for _ in range(L)]
+    ib = [torch.empty(w.B, 1, w.k_b, dtype=torch.int32, device=dev) for _ in range(L)]
+    oa = [torch.empty(w.B, 1, w.H, 576, dtype=torch.bfloat16, device=dev) for _ in range(L)]
+    ob = [torch.empty(w.B, 1, w.H, 576, dtype=torch.bfloat16, device=dev) for _ in range(L)]
+    la = [torch.empty(w.B, 1, w.H, dtype=torch.float32, device=dev) for _ in range(L)]
+    lb = [torch.empty(w.B, 1, w.H, dtype=torch.float32, device=dev) for _ in range(L)]
+    sc_a = torch.empty(w.B, 1, w.N, dtype=torch.float32, device=dev)
+    sc_b = torch.empty(w.B, 1, w.k, dtype=torch.float32, device=dev)
+    tws_b = csa.workspace_bytes(csa.WS_TOPK, w.B, 1, w.k, w.N)
+    tws = torch.empty(max(tws_b, 16), dtype=torch.uint8, device=dev)
+    aws = torch.empty(max(csa.workspace_bytes(csa.WS_SPARSE_ATTN, w.B, 1, w.H, w.k, w.n_win), 16), dtype=torch.uint8,
+                      device=dev)
+    bws = torch.empty(max(csa.workspace_bytes(csa.WS_SPARSE_ATTN, w.B, 1, w.H, w.k_b, w.n_win), 16),
+                      dtype=torch.uint8, device=dev)
+
+    def layer_a(l):
+        c = caches[l]
+        csa.index_scores(c, qa[l]["qI"], qa[l]["w"], qa[l]["q_pos"], scores=sc_a)
+        csa.topk(c, sc_a, qa[l]["q_pos"], w.k, out=ia[l], ws=tws if tws_b else None)
+        csa.sparse_attn(c, qa[l]["q"], qa[l]["q_pos"], ia[l], x_win, s0, w.n_win, w.softmax_scale,
+                        out_dtype=torch.bfloat16, ws=aws, out=oa[l], lse=la[l])
+
+    def layer_b(l):
+        c = caches[l]
+        csa.index_scores(c, qb[l]["qI"], qb[l]["w"], qb[l]["q_pos"], cand=ia[l], scores=sc_b)
+        csa.topk(c, sc_b, qb[l]["q_pos"], w.k_b, cand=ia[l], out=ib[l])
+        csa.sparse_attn(c, qb[l]["q"], qb[l]["q_pos"], ib[l], xb_win, s0, w.n_win, w.softmax_scale,
+                        out_dtype=torch.bfloat16, ws=bws, out=ob[l], lse=lb[l])
+
+    ms = _graph_ms(lambda: [(layer_a(i % L), layer_b(i % L)) for i in range(K)], K)
+    ms_a = _graph_ms(lambda: [layer_a(i % L) for i in range(K)], K)
+    ms_b = ms - ms_a
+    # stage by stage (each a graph of K launches over the rotating layers)
+    stage_us = {
+        "a_index_scores": _graph_ms(lambda: [csa.index_scores(caches[i % L], qa[i % L]["qI"], qa[i % L]["w"],
+                                                              qa[i % L]["q_pos"], scores=sc_a) for i in range(K)], K),
+        "a_topk": _graph_ms(lambda: [csa.topk(caches[i % L], sc_a, qa[i % L]["q_pos"], w.k, out=ia[i % L],
+                                              ws=tws if tws_b else None) for i in range(K)], K),
+        "a_sparse_attn": _graph_ms(lambda: [csa.sparse_attn(caches[i % L], qa[i % L]["q"], qa[i % L]["q_pos"], ia[i % L],
+                                                            x_win, s0, w.n_win, w.softmax_scale, out_dtype=torch.bfloat16,
+                                                            ws=aws, out=oa[i % L], lse=la[i % L]) for i in range(K)], K),
+        "b_index_scores": _graph_ms(lambda: [csa.index_scores(caches[i % L], qb[i % L]["qI"], qb[i % L]["w"],
+                                                              qb[i % L]["q_pos"], cand=ia[i % L], scores=sc_b)
+                                             for i in range(K)], K),
+        "b_topk": _graph_ms(lambda: [csa.topk(caches[i % L], sc_b, qb[i % L]["q_pos"], w.k_b, cand=ia[i % L],
+                                              out=ib[i % L]) for i in range(K)], K),
+        "b_sparse_attn": _graph_ms(lambda: [csa.sparse_attn(caches[i % L], qb[i % L]["q"], qb[i % L]["q_pos"], ib[i % L],
+                                                            xb_win, s0, w.n_win, w.softmax_scale, out_dtype=torch.bfloat16,
+                                                            ws=bws, out=ob[i % L], lse=lb[i % L]) for i in range(K)], K),
+    }
+    stage_us = {k: round(v * 1e3, 3) for k, v in stage_us.items()}
+    log(f"[bench] csa2 stages (us): {stage_us}")
+    per_a = w.N * 68 + w.H_I * (w.d_idx + 4) + w.k * 400 + 2 * w.n_win * 576 + 2 * 2 * w.H * 576
+    per_b = w.k * 68 + w.H_I * (w.d_idx + 4) + w.k_b * 400 + 2 * w.n_win * 576 + 2 * 2 * w.H * 576
+    step_bytes = w.B * (per_a + per_b)
+    gbps = step_bytes / (ms * 1e-3) / 1e9
+    log(f"[bench] csa2 step {ms * 1e3:.2f} us (layer A {ms_a * 1e3:.2f}), {gbps:.0f} GB/s")
+
+    pc = {k: v[0].cpu().numpy() if k != "rope" else as_u16(v[0]) for k, v in planes.items()}
+    t0 = time.perf_counter()
+    idx, _, _, _ = O.index_topk(pc["ikey"], pc["iscale"], qa[0]["qI"][0, 0].cpu().numpy(),
+                                qa[0]["w"][0, 0].cpu().numpy(), w.T - 1, w.m, w.N, w.k)
+    O.sparse_attention(as_u16(qa[0]["q"][0, 0]), pc["nope"], pc["nscale"], pc["rope"], idx, as_u16(x_win[0]),
+                       w.T - w.n_win, w.T - 1, w.n_win, w.softmax_scale, w.m, w.N)
+    dt = time.perf_counter() - t0
+    return {"workload": w.name, "B": w.B, "context": w.T, "entries": w.N, "top_k_a": w.k, "top_k_b": w.k_b,
+            "heads": w.H, "index_heads": w.H_I, "d_idx": w.d_idx, "n_win": w.n_win, "layers_rotated": L, "steps": K,
+            "ms_per_step": round(ms, 6), "layer_a_ms": round(ms_a, 6), "layer_b_ms": round(ms_b, 6),
+            "stage_us": stage_us,
+            "q_tokens_per_s": round(w.B / (ms * 1e-3), 1), "step_bytes": step_bytes,
+            "achieved_GBps": round(gbps, 1), "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4),
+            "cpu_oracle": {"value": round(1.0 / dt, 3), "unit": "layer-A query-tokens/s", "cores": _oracle_threads(),
+                           "sample": f"one sequence's layer-A step (scores of {w.N} entries, top-{w.k}, "
+                                     f"attention): {dt:.2f} s"}}
 
 
 def cpu_baseline(w, nseq, min_seconds=10.0):

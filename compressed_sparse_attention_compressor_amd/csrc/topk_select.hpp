@@ -153,20 +153,28 @@ __device__ __forceinline__ void select_keys(uint32_t (&key)[kPer], const int32_t
   int need = 0;       // elements equal to thr that are taken
   int n_eq = 0;       // elements equal to thr
   if (k_eff > 0 && k_eff < n_valid) {
+    // each key's bin is computed once and kept (two 16-bit bins per
+    // register; 0xFFFF for an invalid key) for the threshold-bin passes
+    uint32_t binp[(kPer + 1) / 2];
 #pragma unroll
-    for (int j = 0; j < kPer; ++j)
-      if (key[j] != 0u) atomicAdd(&hist[0][kBins - 2 - bin_of(key[j])], 1);
+    for (int j = 0; j < kPer; ++j) {
+      const uint32_t bj = key[j] != 0u ? bin_of(key[j]) : 0xFFFFu;
+      if (j & 1) binp[j >> 1] |= bj << 16;
+      else binp[j >> 1] = bj;
+      if (key[j] != 0u) atomicAdd(&hist[0][kBins - 2 - bj], 1);
+    }
     __syncthreads();
     int d1, above, tot;
     find_digit<NT>(hist, 1, kBins, k_eff, sh, d1, above, tot);
     const int c1 = __builtin_amdgcn_readfirstlane(hist[0][d1]);
     const uint32_t dhi = (uint32_t)(kBins - 2 - d1);
+    auto in_dhi = [&](int j) { return ((binp[j >> 1] >> (16 * (j & 1))) & 0xFFFFu) == dhi; };
     int k_rem = k_eff - above;
     if (c1 <= 64) {
       // 2a. gather the threshold bin (one LDS atomic per wave) and rank it
       int mine = 0;
 #pragma unroll
-      for (int j = 0; j < kPer; ++j) mine += key[j] != 0u && bin_of(key[j]) == dhi;
+      for (int j = 0; j < kPer; ++j) mine += in_dhi(j);
       const int inc = wave_incl_scan(mine);
       const int wtot = __builtin_amdgcn_readlane(inc, 63);
       int base = 0;
@@ -177,7 +185,7 @@ __device__ __forceinline__ void select_keys(uint32_t (&key)[kPer], const int32_t
       int pos = base + inc - mine;
 #pragma unroll
       for (int j = 0; j < kPer; ++j)
-        if (key[j] != 0u && bin_of(key[j]) == dhi) bin_keys[pos++] = key[j];
+        if (in_dhi(j)) bin_keys[pos++] = key[j];
       __syncthreads();
       // wave 0 ranks the gathered keys (lanes past c1 take no part) and
       // publishes the threshold
@@ -206,7 +214,7 @@ __device__ __forceinline__ void select_keys(uint32_t (&key)[kPer], const int32_t
       __syncthreads();
 #pragma unroll
       for (int j = 0; j < kPer; ++j)
-        if (key[j] != 0u && bin_of(key[j]) == dhi) atomicAdd(&hist[0][key[j] >> 21], 1);
+        if (in_dhi(j)) atomicAdd(&hist[0][key[j] >> 21], 1);
       __syncthreads();
       int e1, ab;
       find_digit<NT>(hist, 1, kBins, k_rem, sh, e1, ab, tot);
@@ -215,7 +223,7 @@ __device__ __forceinline__ void select_keys(uint32_t (&key)[kPer], const int32_t
       __syncthreads();
 #pragma unroll
       for (int j = 0; j < kPer; ++j)
-        if (key[j] != 0u && bin_of(key[j]) == dhi && (key[j] >> 21) == (uint32_t)e1)
+        if (in_dhi(j) && (key[j] >> 21) == (uint32_t)e1)
           atomicAdd(&hist[0][(key[j] >> 10) & 0x7FFu], 1);
       __syncthreads();
       int e2;
@@ -226,7 +234,7 @@ __device__ __forceinline__ void select_keys(uint32_t (&key)[kPer], const int32_t
       __syncthreads();
 #pragma unroll
       for (int j = 0; j < kPer; ++j)
-        if (key[j] != 0u && bin_of(key[j]) == dhi && (key[j] >> 10) == p12) atomicAdd(&hist[0][key[j] & 0x3FFu], 1);
+        if (in_dhi(j) && (key[j] >> 10) == p12) atomicAdd(&hist[0][key[j] & 0x3FFu], 1);
       __syncthreads();
       int e3;
       find_digit<NT>(hist, 1, 1024, k_rem, sh, e3, ab, tot);

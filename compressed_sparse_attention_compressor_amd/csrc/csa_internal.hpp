@@ -32,9 +32,10 @@ hipError_t launch_index_scores(const CacheView &c, const uint8_t *q_idx, const f
 // scores whose own top-k candidates (ws_bytes of workspace) are reduced in
 // a second launch.  nsl = 1: one workgroup per row.
 struct TopkPlan {
-  int nsl;
-  int S;
-  size_t ws_bytes;
+  int nsl;          // slices per row (1: one workgroup per row)
+  int S;            // elements per slice
+  size_t ws_bytes;  // workspace needed
+  bool radix = false;  // multi-workgroup radix selection (few, long rows)
 };
 TopkPlan topk_plan(int B, int Q, int Ns, int k);
 

@@ -305,9 +305,308 @@ __global__ __launch_bounds__(kRegThreads) void topk_reg_kernel(const float *__re
                                [&](int i) { return kCand ? csrc[i] : off + i; });
 }
 
+// ---------------------------------------------------------------------------
+// Few, long rows (B*Q < 256 rows of at least 65,536 scores): a radix
+// selection spread over slices of 4,096 scores per workgroup, the digits of
+// the order-preserving key (11, 11 and 10 bits) resolved one launch at a
+// time through per-row histograms in global memory, so that every launch
+// keeps the whole GPU busy however large k is (the slice-and-reduce path
+// must pass k candidates per slice on, which for k = 2,048 barely shrinks
+// the rows).  Launches: zero the histograms; digit-1 histogram; digit-2
+// histogram of the keys in the threshold digit-1 bin; digit-3 likewise;
+// per-slice counts of the keys above / equal to the threshold key T;
+// placement in ascending entry order from the prefix of those counts.  Ties
+// at T go to the lower entries: the first `need` keys equal to T are taken.
+constexpr int kRxPer = 8;
+constexpr int kRxSlice = kRegThreads * kRxPer;  // 4,096 scores per workgroup
+
+struct RxArgs {
+  const float *scores;
+  int Ns;
+  const int32_t *n_entries;
+  int N_cap, m;
+  const int32_t *q_pos;
+  int Q, k, nsl;
+  int *hist1;   // [rows][2048] digit 1 (key >> 21)
+  int *hist2;   // [rows][2048] digit 2 ((key >> 10) & 2047) inside the digit-1 threshold bin
+  int *hist3;   // [rows][1024] digit 3 (key & 1023) inside the digit-2 threshold bin
+  int *counts;  // [rows][nsl][2]: keys > T, keys == T
+  int *desc;    // [rows][4]: T, need, k_eff
+  int32_t *idx_out;
+  float *score_out;
+};
+
+// This workgroup's slice as keys (0 = not visible / no score); element
+// i = v*(4*kRegThreads) + 4*tid + u is key[4v + u].
+__device__ __forceinline__ void rx_load(const RxArgs &a, int64_t row, int b, int sl, uint32_t (&key)[kRxPer]) {
+  constexpr int kSlice = kRegThreads * 4;
+  const int tid = threadIdx.x;
+  const int off = sl * kRxSlice;
+  const int len = min(kRxSlice, a.Ns - off);
+  const float *src = a.scores + row * a.Ns + off;
+  if (len >= 4 && ((a.Ns | off | len) & 3) == 0) {
+#pragma unroll
+    for (int v = 0; v < kRxPer / 4; ++v) {
+      const float4 t4 = *reinterpret_cast<const float4 *>(src + min(v * kSlice + 4 * tid, len - 4));
+      const float t[4] = {t4.x, t4.y, t4.z, t4.w};
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        key[4 * v + u] = __float_as_uint(t[u]) != kNoScoreBits ? score_key(t[u]) : 0u;
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < kRxPer; ++j) {
+      const float x = src[min((j >> 2) * kSlice + 4 * tid + (j & 3), max(len - 1, 0))];
+      key[j] = len > 0 && __float_as_uint(x) != kNoScoreBits ? score_key(x) : 0u;
+    }
+  }
+  const int nE = min(a.n_entries[b], a.N_cap);
+  const int n = max(0, min(max(0, min(nE, (a.q_pos[row] + 1) / a.m)) - off, len));
+#pragma unroll
+  for (int j = 0; j < kRxPer; ++j)
+    if ((j >> 2) * kSlice + 4 * tid + (j & 3) >= n) key[j] = 0u;
+}
+
+// The row's histogram of `nb` bins into LDS, then the digit holding the
+// k_rem-th largest key.
+__device__ __forceinline__ void rx_digit(const int *g, int nb, int k_rem, int (*hs)[kBins], int *sh, int &digit,
+                                         int &above, int &total) {
+  for (int i = threadIdx.x; i < nb; i += kRegThreads) hs[0][i] = g[i];
+  __syncthreads();
+  find_digit<kRegThreads>(hs, 1, nb, k_rem, sh, digit, above, total);
+}
+
+// Adds this workgroup's histogram (LDS, nb bins) into the row's.
+__device__ __forceinline__ void rx_flush(int (*hs)[kBins], int nb, int *g) {
+  __syncthreads();
+  for (int i = threadIdx.x; i < nb; i += kRegThreads) {
+    const int c = hs[0][i];
+    if (c) atomicAdd(g + i, c);
+  }
+}
+
+__global__ void rx_zero_kernel(int *p, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0;
+}
+
+// Stage s: 1 = digit-1 histogram, 2 = digit 2, 3 = digit 3, 4 = counts at T.
+template <int kStage>
+__global__ __launch_bounds__(kRegThreads) void rx_hist_kernel(RxArgs a) {
+  __shared__ int hs[1][kBins];
+  __shared__ int sh[kRegThreads / 64 + 3];
+  const int q = blockIdx.x / a.nsl, sl = blockIdx.x % a.nsl, b = blockIdx.y;
+  const int64_t row = (int64_t)b * a.Q + q;
+  uint32_t key[kRxPer];
+  rx_load(a, row, b, sl, key);
+  int k_eff = 0, k_rem = a.k;
+  uint32_t prefix = 0;  // resolved high bits of T
+  if (kStage >= 2) {
+    int d1, above, total;
+    rx_digit(a.hist1 + row * 2048, 2048, a.k, hs, sh, d1, above, total);
+    k_eff = min(a.k, total);
+    if (k_eff == total || k_eff == 0) {
+      // every visible key is taken (T = 0: key > 0), or none
+      if (kStage == 4) {
+        const uint32_t T = k_eff == 0 ? 0xFFFFFFFFu : 0u;
+        int ng = 0;
+#pragma unroll
+        for (int j = 0; j < kRxPer; ++j) ng += key[j] > T;
+        ng = wave_sum(ng);
+        if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = ng;
+        __syncthreads();
+        if (threadIdx.x == 0) {
+          int t = 0;
+          for (int w = 0; w < kRegThreads / 64; ++w) t += sh[w];
+          a.counts[(row * a.nsl + sl) * 2] = t;
+          a.counts[(row * a.nsl + sl) * 2 + 1] = 0;
+          if (sl == 0) {
+            a.desc[row * 4] = (int)T;
+            a.desc[row * 4 + 1] = 0;
+            a.desc[row * 4 + 2] = k_eff;
+          }
+        }
+      }
+      return;
+    }
+    k_rem = k_eff - above;
+    prefix = (uint32_t)d1;
+    if (kStage >= 3) {
+      int d2;
+      rx_digit(a.hist2 + row * 2048, 2048, k_rem, hs, sh, d2, above, total);
+      k_rem -= above;
+      prefix = (prefix << 11) | (uint32_t)d2;
+      if (kStage >= 4) {
+        int d3;
+        rx_digit(a.hist3 + row * 1024, 1024, k_rem, hs, sh, d3, above, total);
+        k_rem -= above;
+        const uint32_t T = (prefix << 10) | (uint32_t)d3;
+        int ng = 0, ne = 0;
+#pragma unroll
+        for (int j = 0; j < kRxPer; ++j) {
+          ng += key[j] > T;
+          ne += key[j] == T;
+        }
+        ng = wave_sum(ng);
+        ne = wave_sum(ne);
+        __syncthreads();  // sh reads of find_digit are done
+        if ((threadIdx.x & 63) == 0) {
+          sh[threadIdx.x >> 6] = ng;
+          hs[0][threadIdx.x >> 6] = ne;
+        }
+        __syncthreads();
+        if (threadIdx.x == 0) {
+          int tg = 0, te = 0;
+          for (int w = 0; w < kRegThreads / 64; ++w) {
+            tg += sh[w];
+            te += hs[0][w];
+          }
+          a.counts[(row * a.nsl + sl) * 2] = tg;
+          a.counts[(row * a.nsl + sl) * 2 + 1] = te;
+          if (sl == 0) {
+            a.desc[row * 4] = (int)T;
+            a.desc[row * 4 + 1] = k_rem;  // keys equal to T that are taken
+            a.desc[row * 4 + 2] = k_eff;
+          }
+        }
+        return;
+      }
+    }
+    __syncthreads();  // the histogram buffer is reused below
+  }
+  const int nb = kStage == 3 ? 1024 : 2048;
+  for (int i = threadIdx.x; i < nb; i += kRegThreads) hs[0][i] = 0;
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < kRxPer; ++j) {
+    const uint32_t kk = key[j];
+    if (kk == 0u) continue;
+    if (kStage == 1) atomicAdd(&hs[0][kk >> 21], 1);
+    if (kStage == 2 && (kk >> 21) == prefix) atomicAdd(&hs[0][(kk >> 10) & 2047u], 1);
+    if (kStage == 3 && (kk >> 10) == prefix) atomicAdd(&hs[0][kk & 1023u], 1);
+  }
+  int *g = kStage == 1 ? a.hist1 + row * 2048 : kStage == 2 ? a.hist2 + row * 2048 : a.hist3 + row * 1024;
+  rx_flush(hs, nb, g);
+}
+
+// Placement: the keys above T and the first `need` keys equal to T (in
+// entry order over the whole row) go to their rank among the selected, in
+// ascending entry order.
+__global__ __launch_bounds__(kRegThreads) void rx_place_kernel(RxArgs a) {
+  constexpr int kW = kRegThreads / 64;
+  constexpr int kV = kRxPer / 4;
+  constexpr int kSlice = kRegThreads * 4;
+  __shared__ int cnt[2][kV * kW];
+  const int q = blockIdx.x / a.nsl, sl = blockIdx.x % a.nsl, b = blockIdx.y;
+  const int64_t row = (int64_t)b * a.Q + q;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  uint32_t key[kRxPer];
+  rx_load(a, row, b, sl, key);
+  const uint32_t T = (uint32_t)a.desc[row * 4];
+  const int need = a.desc[row * 4 + 1], k_eff = a.desc[row * 4 + 2];
+  // counts of the slices before this one (every thread sums a few)
+  int bg = 0, be = 0;
+  for (int s = lane; s < sl; s += 64) {
+    bg += a.counts[(row * a.nsl + s) * 2];
+    be += a.counts[(row * a.nsl + s) * 2 + 1];
+  }
+  bg = wave_sum(bg);
+  be = wave_sum(be);
+  const uint64_t below = lane ? (~0ull >> (64 - lane)) : 0ull;
+#pragma unroll
+  for (int v = 0; v < kV; ++v) {
+    int gc = 0, ec = 0;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      gc += __popcll(__ballot(key[4 * v + u] > T));
+      ec += __popcll(__ballot(key[4 * v + u] == T));
+    }
+    if (lane == 0) {
+      cnt[0][v * kW + wave] = gc;
+      cnt[1][v * kW + wave] = ec;
+    }
+  }
+  __syncthreads();
+  int32_t *oi = a.idx_out + row * a.k;
+  float *os = a.score_out ? a.score_out + row * a.k : nullptr;
+#pragma unroll
+  for (int v = 0; v < kV; ++v) {
+    int gb = bg, eb = be;
+    for (int e = 0; e < v * kW + wave; ++e) {
+      gb += cnt[0][e];
+      eb += cnt[1][e];
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      gb += __popcll(__ballot(key[4 * v + u] > T) & below);
+      eb += __popcll(__ballot(key[4 * v + u] == T) & below);
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const uint32_t kk = key[4 * v + u];
+      const bool gt = kk > T, eq = kk == T;
+      if (gt || (eq && eb < need)) {
+        const int p = gb + min(eb, need);
+        if (p < k_eff) {
+          oi[p] = sl * kRxSlice + v * kSlice + 4 * tid + u;
+          if (os) os[p] = key_score(kk);
+        }
+      }
+      gb += gt;
+      eb += eq;
+    }
+  }
+  if (sl == a.nsl - 1) {
+    for (int j = k_eff + tid; j < a.k; j += kRegThreads) {
+      oi[j] = -1;
+      if (os) os[j] = __uint_as_float(kNoScoreBits);
+    }
+  }
+}
+
+static hipError_t launch_radix(const CacheView &c, const float *scores, int Ns, const int32_t *q_pos, int Q, int k,
+                               int32_t *idx_out, float *score_out, void *ws, hipStream_t stream) {
+  const int rows = c.B * Q;
+  const int nsl = (Ns + kRxSlice - 1) / kRxSlice;
+  RxArgs a;
+  a.scores = scores;
+  a.Ns = Ns;
+  a.n_entries = c.n_entries;
+  a.N_cap = c.N_cap;
+  a.m = c.m;
+  a.q_pos = q_pos;
+  a.Q = Q;
+  a.k = k;
+  a.nsl = nsl;
+  a.hist1 = reinterpret_cast<int *>(ws);
+  a.hist2 = a.hist1 + (size_t)rows * 2048;
+  a.hist3 = a.hist2 + (size_t)rows * 2048;
+  a.counts = a.hist3 + (size_t)rows * 1024;
+  a.desc = a.counts + (size_t)rows * nsl * 2;
+  a.idx_out = idx_out;
+  a.score_out = score_out;
+  const int nz = rows * (2048 + 2048 + 1024);
+  rx_zero_kernel<<<(nz + 255) / 256, 256, 0, stream>>>(a.hist1, nz);
+  const dim3 grid(Q * nsl, c.B);
+  rx_hist_kernel<1><<<grid, kRegThreads, 0, stream>>>(a);
+  rx_hist_kernel<2><<<grid, kRegThreads, 0, stream>>>(a);
+  rx_hist_kernel<3><<<grid, kRegThreads, 0, stream>>>(a);
+  rx_hist_kernel<4><<<grid, kRegThreads, 0, stream>>>(a);
+  rx_place_kernel<<<grid, kRegThreads, 0, stream>>>(a);
+  return hipGetLastError();
+}
+
 TopkPlan topk_plan(int B, int Q, int Ns, int k) {
   TopkPlan p{1, Ns, 0};
   const int64_t rows = (int64_t)B * Q;
+  if (rows < 256 && Ns >= 65536 && k > 0) {
+    p.radix = true;
+    p.nsl = (Ns + kRxSlice - 1) / kRxSlice;
+    p.S = kRxSlice;
+    p.ws_bytes = (size_t)rows * (2048 + 2048 + 1024 + 2 * p.nsl + 4) * sizeof(int);
+    return p;
+  }
   if (rows >= 256 || Ns <= 4096 || k <= 0) return p;
   // Smallest power-of-two slice (>= 4096, >= k) whose candidates fit one
   // register-resident row in the second stage.
@@ -358,6 +657,7 @@ hipError_t launch_topk(const CacheView &c, const float *scores, int Ns, const in
                        const int32_t *cand, int C, int k, int32_t *idx_out, float *score_out, void *ws,
                        hipStream_t stream) {
   const TopkPlan p = cand ? TopkPlan{1, Ns, 0} : topk_plan(c.B, Q, Ns, k);
+  if (p.radix) return launch_radix(c, scores, Ns, q_pos, Q, k, idx_out, score_out, ws, stream);
   if (p.nsl == 1) {
     launch_one(c, scores, Ns, Ns, q_pos, Q, cand, C, k, idx_out, score_out, 1, Ns, stream);
     return hipGetLastError();

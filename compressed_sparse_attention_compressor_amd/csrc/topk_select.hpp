@@ -73,10 +73,10 @@ __device__ __forceinline__ void find_digit(const int (*hist)[kBins], int nh, int
 // Selection is a short chain of block-wide steps; cross-lane work runs on
 // DPP and readlane, and small scans are repeated by every wave rather than
 // published through a further barrier:
-//   1. row maximum and valid count;
-//   2. histogram of the distance below the maximum, (max - key) >> 14 (bins
-//      of 1/512 octave, elements further down take no part) and the digit
-//      holding the k-th element;
+//   1. row maximum, minimum and valid count;
+//   2. histogram of 2,047 linear bins in score space between the extremes
+//      (each key's bin kept in registers) and the bin holding the k-th
+//      element;
 //   3. when that bin holds at most 64 elements they are gathered (one LDS
 //      atomic per wave) and every wave ranks them to fix the exact threshold
 //      key T and how many elements equal to T are taken; otherwise, and when

@@ -501,7 +501,15 @@ TOPK_CASES = [
     ("two-stage-ties", 2, 1, 20000, [20000, 13001], 300, 1.0),
     ("two-stage-k-over-slice", 1, 1, 32768, [32768], 5000, 0.05),
     ("single-stage-ragged", 3, 2, 1003, [1003, 999, 17], 64, 0.5),
-    ("tiled-long-row", 1, 1, 70001, [70001], 777, 0.1),
+    # rows of at least 65,536 with few siblings: multi-workgroup radix selection
+    ("radix-long-row", 1, 1, 70001, [70001], 777, 0.1),
+    ("radix-ties", 2, 1, 70000, [70000, 50001], 700, 0.5),
+    ("radix-k-over-visible", 2, 1, 65536, [65536, 300], 700, 0.1),
+    ("radix-all-equal", 1, 1, 65536, [65536], 1000, 1e9),
+    ("radix-k1", 1, 2, 80000, [80000, 1], 1, 0.01),
+    ("radix-k2048", 1, 1, 262144, [262144], 2048, 0.001),
+    # 256 rows longer than a register-resident row: the tiled selection
+    ("tiled-many-rows", 16, 16, 33000, [33000, 32769, 100], 100, 0.1),
     ("sign-crossing", 2, 1, 8192, [8192, 6000], 5000, 0.001),   # the k-th score is negative
     ("all-equal", 1, 2, 3000, [3000, 2500], 100, 1e9),         # every score rounds to 0
 ]

@@ -47,4 +47,6 @@ from .csa import (  # noqa: F401
     sparse_attention,
     dense_attention,
     csa2_pair,
+    block_pool,
+    hier_pair,
 )

@@ -171,6 +171,35 @@ def index_topk(ikey, iscale, qI_u8, w_f32, p: int, m: int, n_entries: int, k: in
     return idx, sc, js, s
 
 
+def block_pool(scores, V: int, block: int, n_blocks: int) -> tuple[np.ndarray, np.ndarray]:
+    """Candidate pool of the hierarchical sparse indexer for one query
+    ([V4.1], "Hierarchical Sparse Indexer" bullet and Fig. 5).
+
+    ``scores`` float [>= V]: the Full layer's indexer scores of the visible
+    entries 0..V-1.  Entries fall into blocks of ``block`` consecutive
+    entries (block b holds entries b*block .. b*block + block - 1; the last
+    visible block may be partly visible).  A block's score is the largest
+    score among its visible entries.  The ``n_blocks`` blocks of largest
+    score are kept, exact ties going to the lower block (the top-k rule), and
+    the pool lists every visible entry of the kept blocks in ascending order,
+    padded with -1 to n_blocks * block slots.
+
+    Returns (pool int32 [n_blocks*block], kept blocks int32 [n_blocks],
+    ascending and padded with -1).
+    """
+    scores = np.asarray(scores, dtype=np.float64)
+    V, block, n_blocks = int(V), int(block), int(n_blocks)
+    nb = -(-V // block)
+    starts = np.arange(nb, dtype=np.int64) * block
+    bmax = np.maximum.reduceat(scores[:V], starts) if nb else np.zeros(0)
+    kept, _ = topk_select(bmax, np.arange(nb), n_blocks)
+    ents = [np.arange(b * block, min((b + 1) * block, V)) for b in kept if b >= 0]
+    sel = np.concatenate(ents) if ents else np.zeros(0, dtype=np.int64)
+    pool = np.full(n_blocks * block, -1, dtype=np.int32)
+    pool[: len(sel)] = sel
+    return pool, kept
+
+
 def attention(q_u16, keys: np.ndarray, scale) -> tuple[np.ndarray, np.ndarray]:
     """Softmax attention of H query heads over n keys, the value equal to the key.
 
@@ -245,4 +274,29 @@ def csa2_pair(cache: dict, layer_a: dict, layer_b: dict, p: int, m: int, n_entri
     o_b, lse_b = sparse_attention(layer_b["q"], cache["nope"], cache["nscale"], cache["rope"], idx_b,
                                   layer_b["swa"], layer_b["swa_pos0"], p, n_win, scale, m, n_entries)
     return dict(idx_a=idx_a, score_a=sc_a, o_a=o_a, lse_a=lse_a,
+                idx_b=idx_b, score_b=sc_b, o_b=o_b, lse_b=lse_b)
+
+
+def hier_pair(cache: dict, layer_a: dict, layer_b: dict, p: int, m: int, n_entries: int,
+              n_win: int, scale, k_a: int, k_b: int, block: int, n_blocks: int):
+    """A Full layer that also builds the hierarchical candidate pool, then a
+    Reindex layer over that pool ([V4.1], "Hierarchical Sparse Indexer"
+    bullet and Fig. 5).
+
+    Layer A scores every visible entry, keeps its own top-k_a over all of
+    them and attends to it, and builds the pool of ``block_pool`` from the
+    same scores; layer B rescores only the pool with its own indexer query
+    and weights, keeps k_b and attends over A's main cache with its own
+    query and window.  ``layer_*`` as in ``csa2_pair``.
+    """
+    idx_a, sc_a, js, s = index_topk(cache["ikey"], cache["iscale"], layer_a["qI"], layer_a["w"],
+                                    p, m, n_entries, k_a)
+    pool, kept = block_pool(s, len(js), block, n_blocks)
+    o_a, lse_a = sparse_attention(layer_a["q"], cache["nope"], cache["nscale"], cache["rope"], idx_a,
+                                  layer_a["swa"], layer_a["swa_pos0"], p, n_win, scale, m, n_entries)
+    idx_b, sc_b, _, _ = index_topk(cache["ikey"], cache["iscale"], layer_b["qI"], layer_b["w"],
+                                   p, m, n_entries, k_b, cand=pool)
+    o_b, lse_b = sparse_attention(layer_b["q"], cache["nope"], cache["nscale"], cache["rope"], idx_b,
+                                  layer_b["swa"], layer_b["swa_pos0"], p, n_win, scale, m, n_entries)
+    return dict(idx_a=idx_a, score_a=sc_a, pool=pool, kept=kept, o_a=o_a, lse_a=lse_a,
                 idx_b=idx_b, score_b=sc_b, o_b=o_b, lse_b=lse_b)

@@ -117,6 +117,8 @@ def main():
     ap.add_argument("--prefill-reps", type=int, default=3, help="timed passes of the 64K prefill chunk (0 = skip)")
     ap.add_argument("--hca-steps", type=int, default=256, help="graph-timed HCA 1M decode steps (0 = skip)")
     ap.add_argument("--csa2-steps", type=int, default=64, help="graph-timed CSA2 two-layer 1M decode steps (0 = skip)")
+    ap.add_argument("--hier-steps", type=int, default=64,
+                    help="graph-timed two-layer 1M decode steps with the hierarchical pool (0 = skip)")
     ap.add_argument("--replays", type=int, default=20, help="individually timed graph replays (>= 20)")
     ap.add_argument("--copy-calibration", action="store_true", help="run a plain device copy of known size")
     args = ap.parse_args()
@@ -317,6 +319,9 @@ def main():
     if args.csa2_steps > 0 and not args.only_index:
         torch.cuda.empty_cache()
         result["csa2"] = csa2_leg(K=args.csa2_steps)
+    if args.hier_steps > 0 and not args.only_index:
+        torch.cuda.empty_cache()
+        result["csa2_hier"] = hier_leg(K=args.hier_steps)
 
     if args.cpu_sample > 0 and not args.only_index:
         result["cpu_baseline"] = cpu_baseline(w, args.cpu_sample)
@@ -657,6 +662,107 @@ def csa2_leg(L=8, K=64):
             "cpu_oracle": {"value": round(1.0 / dt, 3), "unit": "layer-A query-tokens/s", "cores": _oracle_threads(),
                            "sample": f"one sequence's layer-A step (scores of {w.N} entries, top-{w.k}, "
                                      f"attention): {dt:.2f} s"}}
+
+
+def hier_leg(L=8, K=64):
+    """CSA2 two-layer 1M decode with the hierarchical sparse indexer pool:
+    4 sequences at 1,048,576 raw tokens (262,144 entries).  The Full layer
+    scores every entry, keeps its own top-512, attends to it and builds the
+    pool of its 2,048 best blocks of 8 entries (16,384 candidates); the
+    Reindex layer rescores the pool, keeps 512 and attends over the shared
+    cache with its own window.  One step = both layers for one query per
+    sequence; L rotating cache copies (8 x 491 MB).  The oracle times both
+    layers of one sequence."""
+    import dataclasses
+
+    import torch
+
+    import compressed_sparse_attention_compressor_amd as csa
+    import oracle as O
+    from synth.workloads import (CSA2_HIER_DECODE as w, as_u16, queries, raw_rows, second_layer_window,
+                                 synthetic_cache)
+
+    dev = "cuda"
+    C = w.pool_block * w.pool_blocks
+    planes = synthetic_cache(w, device=dev)
+    caches = _layer_caches(w, planes, L, dev)
+    x_win, _ = raw_rows(w, w.T - w.n_win, w.T, device=dev)
+    xb_win = second_layer_window(w, w.T - w.n_win, w.T, device=dev)
+    s0 = torch.full((w.B,), w.T - w.n_win, dtype=torch.int32, device=dev)
+    wl = [dataclasses.replace(w, cfg=w.cfg + 100 * l) for l in range(L)]
+    qa = [queries(x, device=dev) for x in wl]
+    qb = [queries(x, device=dev, second=True) for x in wl]
+
+    def buf(*shape, dt=torch.int32):
+        return [torch.empty(*shape, dtype=dt, device=dev) for _ in range(L)]
+
+    ia, ib, pools = buf(w.B, 1, w.k), buf(w.B, 1, w.k_b), buf(w.B, 1, C)
+    oa, ob = buf(w.B, 1, w.H, 576, dt=torch.bfloat16), buf(w.B, 1, w.H, 576, dt=torch.bfloat16)
+    la, lb = buf(w.B, 1, w.H, dt=torch.float32), buf(w.B, 1, w.H, dt=torch.float32)
+    sc_a = torch.empty(w.B, 1, w.N, dtype=torch.float32, device=dev)
+    sc_b = torch.empty(w.B, 1, C, dtype=torch.float32, device=dev)
+    tws_b = csa.workspace_bytes(csa.WS_TOPK, w.B, 1, w.k, w.N)
+    tws = torch.empty(max(tws_b, 16), dtype=torch.uint8, device=dev)
+    pws = torch.empty(max(csa.workspace_bytes(csa.WS_INDEX_POOL, w.B, 1, w.pool_blocks, w.N, w.pool_block), 16),
+                      dtype=torch.uint8, device=dev)
+    aws = torch.empty(max(csa.workspace_bytes(csa.WS_SPARSE_ATTN, w.B, 1, w.H, w.k, w.n_win), 16), dtype=torch.uint8,
+                      device=dev)
+    bws = torch.empty(max(csa.workspace_bytes(csa.WS_SPARSE_ATTN, w.B, 1, w.H, w.k_b, w.n_win), 16),
+                      dtype=torch.uint8, device=dev)
+
+    def a_index(l):
+        csa.index_scores(caches[l], qa[l]["qI"], qa[l]["w"], qa[l]["q_pos"], scores=sc_a)
+
+    def a_topk(l):
+        csa.topk(caches[l], sc_a, qa[l]["q_pos"], w.k, out=ia[l], ws=tws if tws_b else None)
+
+    def a_pool(l):
+        csa.index_pool(caches[l], sc_a, qa[l]["q_pos"], w.pool_block, w.pool_blocks, out=pools[l], ws=pws)
+
+    def a_attn(l):
+        csa.sparse_attn(caches[l], qa[l]["q"], qa[l]["q_pos"], ia[l], x_win, s0, w.n_win, w.softmax_scale,
+                        out_dtype=torch.bfloat16, ws=aws, out=oa[l], lse=la[l])
+
+    def b_index(l):
+        csa.index_scores(caches[l], qb[l]["qI"], qb[l]["w"], qb[l]["q_pos"], cand=pools[l], scores=sc_b)
+
+    def b_topk(l):
+        csa.topk(caches[l], sc_b, qb[l]["q_pos"], w.k_b, cand=pools[l], out=ib[l])
+
+    def b_attn(l):
+        csa.sparse_attn(caches[l], qb[l]["q"], qb[l]["q_pos"], ib[l], xb_win, s0, w.n_win, w.softmax_scale,
+                        out_dtype=torch.bfloat16, ws=bws, out=ob[l], lse=lb[l])
+
+    stages_a = [a_index, a_topk, a_pool, a_attn]
+    stages_b = [b_index, b_topk, b_attn]
+    ms = _graph_ms(lambda: [f(i % L) for i in range(K) for f in stages_a + stages_b], K)
+    ms_a = _graph_ms(lambda: [f(i % L) for i in range(K) for f in stages_a], K)
+    stage_us = {}
+    for f in stages_a + stages_b:
+        stage_us[f.__name__] = round(_graph_ms(lambda f=f: [f(i % L) for i in range(K)], K) * 1e3, 3)
+    log(f"[bench] hier stages (us): {stage_us}")
+    per_a = w.N * 68 + w.H_I * (w.d_idx + 4) + w.k * 400 + 2 * w.n_win * 576 + 2 * 2 * w.H * 576
+    per_b = C * 68 + w.H_I * (w.d_idx + 4) + w.k_b * 400 + 2 * w.n_win * 576 + 2 * 2 * w.H * 576
+    step_bytes = w.B * (per_a + per_b)
+    gbps = step_bytes / (ms * 1e-3) / 1e9
+    log(f"[bench] hier step {ms * 1e3:.2f} us (Full layer {ms_a * 1e3:.2f}), {gbps:.0f} GB/s")
+
+    pc = {k: v[0].cpu().numpy() if k != "rope" else as_u16(v[0]) for k, v in planes.items()}
+    lay = [dict(qI=q["qI"][0, 0].cpu().numpy(), w=q["w"][0, 0].cpu().numpy(), q=as_u16(q["q"][0, 0]),
+                swa=as_u16(win[0]), swa_pos0=w.T - w.n_win) for q, win in ((qa[0], x_win), (qb[0], xb_win))]
+    t0 = time.perf_counter()
+    O.hier_pair(pc, lay[0], lay[1], w.T - 1, w.m, w.N, w.n_win, w.softmax_scale, w.k, w.k_b, w.pool_block,
+                w.pool_blocks)
+    dt = time.perf_counter() - t0
+    return {"workload": w.name, "B": w.B, "context": w.T, "entries": w.N, "top_k_full": w.k, "top_k_reindex": w.k_b,
+            "pool": {"block": w.pool_block, "blocks": w.pool_blocks, "candidates": C}, "heads": w.H,
+            "index_heads": w.H_I, "d_idx": w.d_idx, "n_win": w.n_win, "layers_rotated": L, "steps": K,
+            "ms_per_step": round(ms, 6), "full_layer_ms": round(ms_a, 6), "reindex_layer_ms": round(ms - ms_a, 6),
+            "stage_us": stage_us, "q_tokens_per_s": round(w.B / (ms * 1e-3), 1), "step_bytes": step_bytes,
+            "achieved_GBps": round(gbps, 1), "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4),
+            "cpu_oracle": {"value": round(1.0 / dt, 3), "unit": "two-layer query-tokens/s", "cores": _oracle_threads(),
+                           "sample": f"one sequence's Full layer (scores of {w.N} entries, top-{w.k}, pool, "
+                                     f"attention) and Reindex layer ({C} candidates): {dt:.2f} s"}}
 
 
 def cpu_baseline(w, nseq, min_seconds=10.0):

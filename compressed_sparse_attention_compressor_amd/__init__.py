@@ -13,11 +13,13 @@ from .ops import (  # noqa: F401
     compress,
     hca_dense_attn,
     index_scores,
+    index_pool,
     index_topk,
     topk,
     sparse_attn,
     workspace_bytes,
     WS_DENSE_ATTN,
+    WS_INDEX_POOL,
     WS_INDEX_TOPK,
     WS_SPARSE_ATTN,
     WS_TOPK,

@@ -45,6 +45,8 @@ _SIGS = {
                                  c_int, c_void_p, c_size_t, c_void_p]),
     "csa_topk": (c_int, [ctypes.POINTER(CacheT), c_void_p, c_void_p, c_int, c_void_p, c_int, c_int, c_void_p,
                          c_void_p, c_void_p, c_size_t, c_void_p]),
+    "csa_index_pool": (c_int, [ctypes.POINTER(CacheT), c_void_p, c_void_p, c_int, c_int, c_int, c_void_p, c_void_p,
+                               c_size_t, c_void_p]),
     "csa_sparse_attn": (c_int, [ctypes.POINTER(CacheT), c_void_p, c_int, c_void_p, c_int, c_void_p, c_int, c_void_p,
                                 c_void_p, c_int, c_int, c_float, c_int, c_void_p, c_void_p, c_void_p, c_size_t,
                                 c_void_p]),

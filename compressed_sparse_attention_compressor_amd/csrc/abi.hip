@@ -15,6 +15,7 @@ constexpr int kMaxHI = 64;
 constexpr int kMaxM = 256;
 constexpr int kMaxK = 1 << 20;
 constexpr int kMaxWin = 1 << 20;
+constexpr int kMaxPoolBlock = 64;
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -110,6 +111,9 @@ size_t csa_workspace_bytes(int op, int B, int Q, int H_or_k, int n, int C) {
     case CSA_WS_INDEX_TOPK:
       return align256(index_ws_bytes(B, Q, n, C)) + topk_ws_bytes(B, Q, C > 0 ? C : n, H_or_k, C > 0);
     case CSA_WS_TOPK: return topk_ws_bytes(B, Q, n, H_or_k, false);
+    case CSA_WS_INDEX_POOL:
+      if (C < 1 || C > kMaxPoolBlock || H_or_k < 1 || n < 0) return 0;
+      return csa::pool_workspace_bytes(B, Q, n, C, H_or_k);
     case CSA_WS_SPARSE_ATTN:
     case CSA_WS_DENSE_ATTN: return csa::attn_workspace_bytes(B, Q, H_or_k, n, C > 0 ? C : 0);
     default: return 0;
@@ -205,6 +209,24 @@ int csa_index_topk(const csa_cache_t *cache, const uint8_t *q_idx, const float *
   if (st) return st;
   void *tws = tbytes ? reinterpret_cast<char *>(ws) + align256(sbytes) : nullptr;
   return csa_topk(cache, scores, q_pos, Q, cand, C, k, idx_out, score_out, tws, tbytes, stream);
+}
+
+int csa_index_pool(const csa_cache_t *cache, const float *scores, const int32_t *q_pos, int Q, int block,
+                   int n_blocks, int32_t *pool_out, void *ws, size_t ws_bytes, hipStream_t stream) {
+  int st = check_cache(cache, false);
+  if (st) return st;
+  if (!q_pos || !pool_out) return CSA_ERR_NULL;
+  if (Q < 0) return CSA_ERR_SHAPE;
+  if (block < 1 || block > kMaxPoolBlock || n_blocks < 1) return CSA_ERR_UNSUPPORTED;
+  if ((int64_t)n_blocks * block > kMaxK) return CSA_ERR_UNSUPPORTED;
+  if (Q == 0 || cache->B == 0) return CSA_OK;
+  if (cache->N_cap > 0 && !scores) return CSA_ERR_NULL;
+  const size_t need = csa::pool_workspace_bytes(cache->B, Q, cache->N_cap, block, n_blocks);
+  if (!ws) return CSA_ERR_NULL;
+  if (ws_bytes < need) return CSA_ERR_WORKSPACE;
+  if (!aligned16(ws)) return CSA_ERR_ALIGN;
+  return status_of(
+      csa::launch_index_pool(view_of(cache), scores, q_pos, Q, block, n_blocks, pool_out, ws, stream));
 }
 
 int csa_sparse_attn(const csa_cache_t *cache, const uint16_t *q, int H, const int32_t *q_pos, int Q,

@@ -43,6 +43,13 @@ hipError_t launch_topk(const CacheView &c, const float *scores, int Ns, const in
                        const int32_t *cand, int C, int k, int32_t *idx_out, float *score_out, void *ws,
                        hipStream_t stream);
 
+// Hierarchical indexer pool: block maxima of full-scan scores, the best
+// n_blocks blocks, and their visible entries as a candidate list
+// [B][Q][n_blocks * block].
+size_t pool_workspace_bytes(int B, int Q, int N_cap, int block, int n_blocks);
+hipError_t launch_index_pool(const CacheView &c, const float *scores, const int32_t *q_pos, int Q, int block,
+                             int n_blocks, int32_t *pool, void *ws, hipStream_t stream);
+
 struct AttnShape {
   int nsplit;       // key-range splits per query
   int per_split;    // key slots per split (a multiple of the chunk size)

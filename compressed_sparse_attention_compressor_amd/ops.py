@@ -13,7 +13,7 @@ import torch
 from ._lib import CacheT, check, lib
 
 D, D_NOPE, D_ROPE = 576, 512, 64
-WS_INDEX_TOPK, WS_SPARSE_ATTN, WS_DENSE_ATTN, WS_TOPK = 0, 1, 2, 3
+WS_INDEX_TOPK, WS_SPARSE_ATTN, WS_DENSE_ATTN, WS_TOPK, WS_INDEX_POOL = 0, 1, 2, 3, 4
 OUT_F32, OUT_BF16 = 0, 1
 
 
@@ -141,6 +141,20 @@ def topk(cache: Cache, scores, q_pos, k, cand=None, want_scores=False, out=None,
     check(lib().csa_topk(ctypes.byref(cs), _ptr(scores), _ptr(q_pos), Q, _ptr(cand), C, int(k), _ptr(idx), _ptr(sc),
                          _ptr(ws), wsb, _stream()), "csa_topk")
     return idx, sc
+
+
+def index_pool(cache: Cache, scores, q_pos, block, n_blocks, out=None, ws=None):
+    """Hierarchical indexer candidate pool [B][Q][n_blocks*block] from full-scan scores."""
+    B, Q = q_pos.shape
+    dev = q_pos.device
+    C = int(n_blocks) * int(block)
+    pool = out if out is not None else torch.empty(B, Q, C, dtype=torch.int32, device=dev)
+    need = workspace_bytes(WS_INDEX_POOL, B, Q, int(n_blocks), cache.N_cap, int(block))
+    ws, wsb = _workspace(max(need, 16), ws, dev)
+    cs = cache.struct()
+    check(lib().csa_index_pool(ctypes.byref(cs), _ptr(scores), _ptr(q_pos), Q, int(block), int(n_blocks), _ptr(pool),
+                               _ptr(ws), wsb, _stream()), "csa_index_pool")
+    return pool
 
 
 def _attn_out(B, Q, H, out_dtype, dev, out):

@@ -132,6 +132,31 @@ int csa_index_scores(const csa_cache_t *cache, const uint8_t *q_idx, const float
 int csa_topk(const csa_cache_t *cache, const float *scores, const int32_t *q_pos, int Q, const int32_t *cand,
              int C, int k, int32_t *idx_out, float *score_out, void *ws, size_t ws_bytes, hipStream_t stream);
 
+/* Candidate pool of the hierarchical sparse indexer ([V4.1] "Hierarchical
+ * Sparse Indexer" bullet and Fig. 5: the first Full layer ranks blocks of
+ * consecutive positions by their largest indexer score and hands the
+ * positions of the best blocks to the Reindex layers that follow).
+ *
+ * For each query row, from a full scan's scores:
+ *   block score(b) = max of score(j) over the visible entries j of block b
+ *                    (entries b*block .. b*block+block-1; blocks without a
+ *                    visible entry take no part)
+ *   kept           = the min(n_blocks, visible blocks) blocks of largest block
+ *                    score, exact ties to the lower block
+ *   pool_out       = every visible entry of the kept blocks, ascending, then -1
+ *
+ *   scores   fp32 [B][Q][N_cap] as csa_index_scores writes in a full scan
+ *            (slots of entries not visible at q_pos are not read)
+ *   q_pos    int32 [B][Q] raw positions
+ *   block    entries per block, 1..64;  n_blocks >= 1, n_blocks*block <= 2^20
+ *   pool_out int32 [B][Q][n_blocks*block]: the `cand` list (C = n_blocks*block)
+ *            of csa_index_topk / csa_index_scores / csa_topk for a Reindex layer
+ *   ws       >= csa_workspace_bytes(CSA_WS_INDEX_POOL, B, Q, n_blocks, N_cap,
+ *            block) bytes, 16-byte aligned (block scores, the kept blocks and
+ *            their top-k workspace); contents need not be initialised. */
+int csa_index_pool(const csa_cache_t *cache, const float *scores, const int32_t *q_pos, int Q, int block,
+                   int n_blocks, int32_t *pool_out, void *ws, size_t ws_bytes, hipStream_t stream);
+
 /* Sparse attention over selected entries plus the sliding window ([V4]
  * Fig. 3).  One softmax over the union of the entries listed in idx and the
  * window rows; key = value = the decoded 576-channel row; no rotation is
@@ -156,7 +181,7 @@ int hca_dense_attn(const csa_cache_t *cache, const uint16_t *q, int H, const int
                    const uint16_t *swa, const int32_t *swa_pos0, int S, int n_win, float softmax_scale,
                    int out_dtype, void *out, float *lse, void *ws, size_t ws_bytes, hipStream_t stream);
 
-enum { CSA_WS_INDEX_TOPK = 0, CSA_WS_SPARSE_ATTN = 1, CSA_WS_DENSE_ATTN = 2, CSA_WS_TOPK = 3 };
+enum { CSA_WS_INDEX_TOPK = 0, CSA_WS_SPARSE_ATTN = 1, CSA_WS_DENSE_ATTN = 2, CSA_WS_TOPK = 3, CSA_WS_INDEX_POOL = 4 };
 
 /* Workspace bytes for one call (0 = none needed).
  *   CSA_WS_INDEX_TOPK: H_or_k = k, n = N_cap, C = candidate count (0 for a
@@ -164,6 +189,8 @@ enum { CSA_WS_INDEX_TOPK = 0, CSA_WS_SPARSE_ATTN = 1, CSA_WS_DENSE_ATTN = 2, CSA
  *   CSA_WS_TOPK:       H_or_k = k, n = scores per row (N_cap or C), C unused.
  *                      Rows with few siblings are selected in two launches
  *                      (per-slice candidates, then their top-k), which uses it.
+ *   CSA_WS_INDEX_POOL: H_or_k = n_blocks, n = N_cap, C = block (0 when
+ *                      block or n_blocks is outside the supported range).
  *   CSA_WS_SPARSE_ATTN / CSA_WS_DENSE_ATTN: H_or_k = query heads H, n = k
  *                      (sparse) or N_cap (dense), C = n_win. */
 size_t csa_workspace_bytes(int op, int B, int Q, int H_or_k, int n, int C);

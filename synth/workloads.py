@@ -43,6 +43,8 @@ class Workload:
     k_b: int = 0            # second layer's k (two-layer reindex case)
     prescaled: bool = False
     prefill: bool = False   # queries at every position 0..T-1
+    pool_block: int = 0     # hierarchical pool: entries per block (0 = no pool)
+    pool_blocks: int = 0    # hierarchical pool: blocks kept per query
 
     @property
     def N(self) -> int:
@@ -79,7 +81,13 @@ HCA_DECODE = Workload("hca-decode-b8-1m", 4, B=8, T=1048576, m=128, d_idx=0, H_I
 CSA2_DECODE = Workload("csa2-decode-b4-1m", 5, B=4, T=1048576, m=4, d_idx=128, H_I=32, k=2048, H=64, n_win=128,
                        k_b=512)
 
-ALL = [TINY_DECODE, BATCHED_DECODE, PREFILL, HCA_DECODE, CSA2_DECODE]
+# The same 1M two-layer decode with the hierarchical pool: the Full layer
+# keeps its own top-512 and a pool of 2,048 blocks x 8 entries; the Reindex
+# layer rescores the 16,384 pool entries and keeps 512.
+CSA2_HIER_DECODE = Workload("csa2-hier-decode-b4-1m", 6, B=4, T=1048576, m=4, d_idx=128, H_I=32, k=512, H=64,
+                            n_win=128, k_b=512, pool_block=8, pool_blocks=2048)
+
+ALL = [TINY_DECODE, BATCHED_DECODE, PREFILL, HCA_DECODE, CSA2_DECODE, CSA2_HIER_DECODE]
 
 
 def raw_rows(w: Workload, t0: int, t1: int, device="cpu", seq0=0, nseq=None):

@@ -125,3 +125,26 @@ def test_workspace_sizes_consistent(L):
     # several splits for a single long row, with (O, max, sum) per head
     w = L.csa_workspace_bytes(2, 8, 1, 64, 8192, 128)
     assert w > 0 and w % (8 * 64 * (576 + 2) * 4) == 0
+
+
+def _pool(L, c, sc=P, qp=P, Q=1, block=8, nb=16, out=P, ws=P, wsb=1 << 30):
+    return L.csa_index_pool(ctypes.byref(c), sc, qp, Q, block, nb, out, ws, wsb, None)
+
+
+def test_index_pool_checks(L):
+    assert _pool(L, _cache(), sc=None) == ENULL
+    assert _pool(L, _cache(), qp=None) == ENULL
+    assert _pool(L, _cache(), out=None) == ENULL
+    assert _pool(L, _cache(), ws=None) == ENULL
+    assert _pool(L, _cache(), Q=-1) == ESHAPE
+    assert _pool(L, _cache(), block=0) == EUNSUP
+    assert _pool(L, _cache(), block=65) == EUNSUP
+    assert _pool(L, _cache(), nb=0) == EUNSUP
+    assert _pool(L, _cache(), block=64, nb=(1 << 14) + 1) == EUNSUP     # pool beyond 2^20 slots
+    assert _pool(L, _cache(), ws=P + 8) == EALIGN
+    need = L.csa_workspace_bytes(4, 2, 1, 16, 64, 8)
+    # block scores (2 rows x 8 blocks), positions, counts, kept blocks: 256-byte aligned pieces
+    assert need >= 4 * 256
+    assert _pool(L, _cache(), wsb=need - 1) == EWS
+    assert _pool(L, _cache(), Q=0) == OK
+    assert L.csa_workspace_bytes(4, 2, 1, 16, 64, 0) == 0        # unsupported block

@@ -17,6 +17,7 @@ from gpu_check import check_topk, compare_bf16_rounding, compare_mxfp4, row_rel_
 from synth.workloads import (
     BATCHED_DECODE,
     CSA2_DECODE,
+    CSA2_HIER_DECODE,
     HCA_DECODE,
     PREFILL,
     as_u16,
@@ -199,6 +200,51 @@ def test_csa2_two_layer_1m_fullsize():
         outs.append(out)
     torch.cuda.synchronize()
     for (qs, sel, win), out in zip(((qa, o_a, x_win), (qb, o_b, xb_win)), outs):
+        g = O.bf16_to_f64(_np(out))
+        wc = _np(win)
+        for b in range(w.B):
+            o, _ = _oracle_rows(pc, b, {"q": qs["q"].cpu()}, 0, sel[b, 0], wc[b], w.T - w.n_win, w.T - 1, w, w.N)
+            assert row_rel_err(g[b, 0], o).max() <= 2e-2
+
+
+def test_csa2_hier_pool_1m_fullsize():
+    """4 sequences x 262,144 entries with the hierarchical pool: the Full
+    layer's scores, its own top-512, the pool of the 2,048 best blocks of 8
+    entries, the Reindex layer's top-512 over the 16,384 pool entries, and
+    both attentions (the second over the shared cache with its own window)."""
+    w = CSA2_HIER_DECODE
+    planes = synthetic_cache(w, device=DEV)
+    pc = _cpu_planes(planes)
+    cache = _cache_from(planes, w, [w.N] * w.B)
+    qa = queries(w, device=DEV)
+    qb = queries(w, device=DEV, second=True)
+    scores = csa.index_scores(cache, qa["qI"], qa["w"], qa["q_pos"])
+    ia, _ = csa.topk(cache, scores, qa["q_pos"], w.k)
+    pool = csa.index_pool(cache, scores, qa["q_pos"], w.pool_block, w.pool_blocks)
+    ib, _ = csa.index_topk(cache, qb["qI"], qb["w"], qb["q_pos"], w.k_b, cand=pool)
+    torch.cuda.synchronize()
+    g_s, g_a, g_p, g_b = _np(scores), _np(ia), _np(pool), _np(ib)
+    C = w.pool_block * w.pool_blocks
+    assert g_p.shape == (w.B, 1, C)
+    for b in range(w.B):
+        oi, _, js, s = O.index_topk(pc["ikey"][b], pc["iscale"][b], _np(qa["qI"])[b, 0], _np(qa["w"])[b, 0],
+                                    w.T - 1, w.m, w.N, w.k)
+        check_topk(g_a[b, 0], oi, js, s, what=f"own top-k b={b}")
+        ref, _ = O.block_pool(g_s[b, 0].astype(np.float64), w.N, w.pool_block, w.pool_blocks)
+        np.testing.assert_array_equal(g_p[b, 0], ref, err_msg=f"pool b={b}")
+        assert np.all(g_p[b, 0] >= 0)                 # every sequence fills the pool
+        assert set(g_a[b, 0].tolist()) <= set(g_p[b, 0].tolist())
+        ob, _, jb, sb = O.index_topk(pc["ikey"][b], pc["iscale"][b], _np(qb["qI"])[b, 0], _np(qb["w"])[b, 0],
+                                     w.T - 1, w.m, w.N, w.k_b, cand=g_p[b, 0])
+        check_topk(g_b[b, 0], ob, jb, sb, what=f"reindex b={b}")
+    x_win, _ = raw_rows(w, w.T - w.n_win, w.T, device=DEV)
+    xb_win = second_layer_window(w, w.T - w.n_win, w.T, device=DEV)
+    s0 = torch.full((w.B,), w.T - w.n_win, dtype=torch.int32, device=DEV)
+    runs = ((qa, g_a, x_win), (qb, g_b, xb_win))
+    outs = [csa.sparse_attn(cache, qs["q"], qs["q_pos"], torch.from_numpy(sel).to(DEV), win, s0, w.n_win,
+                            w.softmax_scale, out_dtype=torch.bfloat16)[0] for qs, sel, win in runs]
+    torch.cuda.synchronize()
+    for (qs, sel, win), out in zip(runs, outs):
         g = O.bf16_to_f64(_np(out))
         wc = _np(win)
         for b in range(w.B):

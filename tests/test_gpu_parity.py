@@ -337,6 +337,91 @@ def test_reindex_candidates_parity():
         assert set(ib[b, 0][ib[b, 0] >= 0]) <= set(oa_all[b, 0][oa_all[b, 0] >= 0])
 
 
+# ----------------------------------------------------------------------------- hierarchical pool
+
+POOL_CASES = [
+    # (name, B, Q, Ns, visible per row (None: spread over the rows), block, n_blocks, rounding)
+    ("ragged-rows", 2, 3, 1003, [1003, 999, 17, 0, 8, 9], 8, 20, 0.5),
+    ("blocks-over-visible", 1, 2, 100, [100, 57], 8, 20, 0.1),
+    ("block-1-is-topk", 1, 2, 5000, [5000, 4321], 1, 300, 0.5),
+    ("block-3-ties", 2, 1, 3001, [3001, 2999], 3, 100, 1.0),
+    ("all-equal", 1, 1, 4096, [4096], 8, 100, 1e9),
+    ("many-rows", 1, 300, 16384, None, 8, 256, 0.01),
+    ("long-rows", 4, 1, 262144, [262144, 200001, 131072, 5], 8, 2048, 0.001),
+    ("block-64", 1, 1, 70000, [69999], 64, 50, 0.05),
+]
+
+
+@pytest.mark.parametrize("name,B,Q,Ns,vis,block,nb,rnd", POOL_CASES, ids=[c[0] for c in POOL_CASES])
+def test_index_pool_stage_parity(name, B, Q, Ns, vis, block, nb, rnd):
+    """The hierarchical pool from generated scores with many exact ties,
+    against the oracle's block maxima, block ranking and pool, bit-exact."""
+    rows = B * Q
+    raw = normal_f32(98, TensorId.W, (rows, Ns)).numpy().astype(np.float64)
+    sc = (np.round(raw / rnd) * rnd).astype(np.float32).reshape(B, Q, Ns)
+    if vis is None:
+        vis = [min(Ns, (r * Ns) // rows + 1) for r in range(rows)]
+    vis = np.array(vis[:rows] + [Ns] * (rows - len(vis)))[:rows].reshape(B, Q)
+    # m = 1: entry j visible when j <= p; unwritten (invisible) slots hold NaN
+    for b in range(B):
+        for t in range(Q):
+            sc[b, t, vis[b, t]:] = np.nan
+    pos = (vis - 1).astype(np.int32)
+    cache = csa.Cache(B, Ns, 1, 0, planes=dict(
+        nope=torch.zeros(B, 1, 256, dtype=torch.uint8, device=DEV),
+        nscale=torch.zeros(B, 1, 16, dtype=torch.uint8, device=DEV),
+        rope=torch.zeros(B, 1, 64, dtype=torch.bfloat16, device=DEV), ikey=None, iscale=None,
+        n_entries=torch.full((B,), Ns, dtype=torch.int32, device=DEV)))
+    pool = _np(csa.index_pool(cache, torch.from_numpy(sc).to(DEV), torch.from_numpy(pos).to(DEV), block, nb))
+    assert pool.shape == (B, Q, nb * block)
+    for b in range(B):
+        for t in range(Q):
+            n = int(vis[b, t])
+            ref, _ = O.block_pool(sc[b, t, :n].astype(np.float64), n, block, nb)
+            np.testing.assert_array_equal(pool[b, t], ref, err_msg=f"{name} b={b} t={t}")
+
+
+def test_hier_pool_reindex_parity():
+    """Full layer scores -> pool of the best blocks -> Reindex layer over the
+    pool ([V4.1] "Hierarchical Sparse Indexer" bullet, Fig. 5), m = 4 with
+    ragged entry counts; the pool is compared bit-exactly with the oracle's
+    pool of the GPU scores (the selection decided in the same precision), and
+    the block choice against the oracle's own float64 scores up to near-ties."""
+    w = Workload("hp", 12, B=3, T=16384, m=4, d_idx=128, H_I=32, k=32, H=64, n_win=0, k_b=48)
+    N, block, nb = w.N, 8, 32
+    planes = synthetic_cache(w)
+    qa = queries(w)
+    qb = queries(w, second=True)
+    n_ent = [N, N - 5, 301]
+    cache = _gpu_cache(planes, w.B, N, w.m, w.d_idx, n_ent)
+    pos = qa["q_pos"].to(DEV)
+    ik, isc = planes["ikey"].numpy(), planes["iscale"].numpy()
+    scores = csa.index_scores(cache, qa["qI"].to(DEV), qa["w"].to(DEV), pos)
+    ia, _ = csa.topk(cache, scores, pos, w.k)
+    pool = csa.index_pool(cache, scores, pos, block, nb)
+    ib, _ = csa.index_topk(cache, qb["qI"].to(DEV), qb["w"].to(DEV), pos, w.k_b, cand=pool)
+    g_s, g_a, g_p, g_b = _np(scores), _np(ia), _np(pool), _np(ib)
+    for b in range(w.B):
+        oa, _, js, s = O.index_topk(ik[b], isc[b], qa["qI"][b, 0].numpy(), qa["w"][b, 0].numpy(), w.T - 1, w.m,
+                                    n_ent[b], w.k)
+        V = len(js)
+        check_topk(g_a[b, 0], oa, js, s, what=f"own top-k b={b}")
+        ref, _ = O.block_pool(g_s[b, 0, :V].astype(np.float64), V, block, nb)
+        np.testing.assert_array_equal(g_p[b, 0], ref, err_msg=f"pool b={b}")
+        # the block choice against the oracle's float64 scores, up to near-ties
+        _, kept_o = O.block_pool(s, V, block, nb)
+        nbv = -(-V // block)
+        bmax = np.maximum.reduceat(s, np.arange(nbv) * block)
+        kept_g = np.unique(g_p[b, 0][g_p[b, 0] >= 0] // block)
+        kept_g = np.concatenate([kept_g, -np.ones(nb - len(kept_g), np.int64)])
+        check_topk(kept_g, kept_o, np.arange(nbv), bmax, what=f"kept blocks b={b}")
+        # the Full layer's own top-k lies inside its pool (k <= n_blocks)
+        assert set(g_a[b, 0][g_a[b, 0] >= 0]) <= set(g_p[b, 0][g_p[b, 0] >= 0])
+        ob, _, jb, sb = O.index_topk(ik[b], isc[b], qb["qI"][b, 0].numpy(), qb["w"][b, 0].numpy(), w.T - 1, w.m,
+                                     n_ent[b], w.k_b, cand=g_p[b, 0])
+        check_topk(g_b[b, 0], ob, jb, sb, what=f"reindex b={b}")
+
+
 # ----------------------------------------------------------------------------- attention
 
 

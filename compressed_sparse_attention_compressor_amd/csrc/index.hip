@@ -23,7 +23,7 @@
 namespace csa {
 
 constexpr int kIdxThreads = 256;     // 4 waves
-constexpr int kIdxWaveEntries = 64;  // entries per wave per workgroup
+constexpr int kIdxWaveEntries = 128; // entries per wave per workgroup (groups of 64)
 constexpr int kIdxWGEntries = kIdxThreads / 64 * kIdxWaveEntries;
 
 // HT: head tiles of 16 (H_I <= 16 * HT).  QB: queries per wave.
@@ -36,7 +36,6 @@ __global__ __launch_bounds__(kIdxThreads) void index_scores_kernel(
   // Indexer queries of this workgroup (QB queries x 16*HT heads x d_idx bytes),
   // staged once so that the waves read their MFMA fragments from LDS.
   __shared__ __attribute__((aligned(16))) uint8_t qs[QB * HT * 16 * 128];
-  __shared__ __attribute__((aligned(16))) float sc[kIdxThreads / 64][QB][kIdxWaveEntries];
   const int b = blockIdx.z;
   const int q0 = blockIdx.y * QB;
   const int lane = threadIdx.x & 63;
@@ -46,6 +45,7 @@ __global__ __launch_bounds__(kIdxThreads) void index_scores_kernel(
   const int kb = d_idx / 32; // key blocks per entry (2 or 4)
   const int base = blockIdx.x * kIdxWGEntries + wave * kIdxWaveEntries;
   constexpr int kIters = kIdxWaveEntries / 16;
+  static_assert(kIters % 4 == 0, "whole groups of four 16-entry tiles");
 
   // Several queries per workgroup (prefill): a workgroup whose entries are
   // visible to none of its queries has nothing to score (causal prefill skips
@@ -77,17 +77,38 @@ __global__ __launch_bounds__(kIdxThreads) void index_scores_kernel(
     const uint4 v = *reinterpret_cast<const uint4 *>(q_idx + off);
     qv_stage[u] = ok ? v : uint4{0u, 0u, 0u, 0u};
   }
+  // Head weights of lane group g: heads 16*ht + 4g .. +3, one 16-byte load
+  // per head tile when H_I is a multiple of 4 (then the four are all valid
+  // or all beyond H_I) and the weights are 16-byte aligned, else one load
+  // per head.
   float w_raw[QB][HT][4];
+  if ((H_I & 3) == 0 && (reinterpret_cast<uintptr_t>(w_idx) & 15) == 0) {
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    const int qc = min(q0 + qb, Q - 1);
+    for (int qb = 0; qb < QB; ++qb) {
+      const int qc = min(q0 + qb, Q - 1);
 #pragma unroll
-    for (int ht = 0; ht < HT; ++ht)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int hh = ht * 16 + g * 4 + i;
-        w_raw[qb][ht][i] = w_idx[((int64_t)b * Q + qc) * H_I + (hh < H_I ? hh : 0)];
+      for (int ht = 0; ht < HT; ++ht) {
+        const int h0 = ht * 16 + g * 4;
+        const float4 v =
+            *reinterpret_cast<const float4 *>(w_idx + ((int64_t)b * Q + qc) * H_I + (h0 < H_I ? h0 : 0));
+        w_raw[qb][ht][0] = v.x;
+        w_raw[qb][ht][1] = v.y;
+        w_raw[qb][ht][2] = v.z;
+        w_raw[qb][ht][3] = v.w;
       }
+    }
+  } else {
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      const int qc = min(q0 + qb, Q - 1);
+#pragma unroll
+      for (int ht = 0; ht < HT; ++ht)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int hh = ht * 16 + g * 4 + i;
+          w_raw[qb][ht][i] = w_idx[((int64_t)b * Q + qc) * H_I + (hh < H_I ? hh : 0)];
+        }
+    }
   }
 
   // 2. Key loads: their addresses depend only on the grid position
@@ -152,30 +173,7 @@ __global__ __launch_bounds__(kIdxThreads) void index_scores_kernel(
       A[qb][ht] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
     }
 
-  // 4. Scores: MFMA, ReLU, head weights, head sum; staged in LDS.
-#pragma unroll
-  for (int it = 0; it < kIters; ++it) {
-    const v4i kk = use[it] ? kv[it] : v4i{0, 0, 0, 0};
-    const int sbu = use[it] ? sbv[it] : 127;
-    const v8i Bm = {kk[0], kk[1], kk[2], kk[3], 0, 0, 0, 0};
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      float s = 0.f;
-#pragma unroll
-      for (int ht = 0; ht < HT; ++ht) {
-        v4f acc = {0.f, 0.f, 0.f, 0.f};
-        acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A[qb][ht], Bm, acc, 0, 4, 0, 127, 0, sbu);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) s = fmaf(fmaxf(acc[i], 0.f), wv[qb][ht][i], s);
-      }
-      s += __shfl_xor(s, 16);
-      s += __shfl_xor(s, 32);
-      if (g == 0) sc[wave][qb][it * 16 + r] = s;
-    }
-  }
-  // 5. Visibility (the entry count and positions are read only now, after
-  //    the key stream has been consumed), then 16-byte stores of this wave's
-  //    scores (LDS operations of one wave complete in order).
+  // 4. Visibility of this workgroup's queries (uniform loads).
   const int nE = min(n_entries[b], N_cap);
   int vis[QB];
 #pragma unroll
@@ -183,30 +181,60 @@ __global__ __launch_bounds__(kIdxThreads) void index_scores_kernel(
     const int q = q0 + qb;
     vis[qb] = q < Q ? max(0, min(nE, (q_pos[(int64_t)b * Q + q] + 1) / m)) : 0;
   }
-  if (kCand && g == 0) {
+
+  // 5. Scores, four 16-entry tiles (64 entries) at a time: MFMA, ReLU and
+  //    head weights give each lane a partial head sum (its lane group's
+  //    heads) for entry r of every tile; a reduce-scatter over the lane
+  //    groups (two rounds of permlane swaps, no LDS) leaves lane l with the
+  //    full sum of entry l of the 64, stored with one coalesced 256-byte
+  //    write per query.
 #pragma unroll
-    for (int it = 0; it < kIters; ++it)
-      if (!(ent[it] >= 0 && ent[it] < vis[0])) sc[wave][0][it * 16 + r] = __uint_as_float(kNoScoreBits);
-  }
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
-  if (lane < kIdxWaveEntries / 4) {
+  for (int grp = 0; grp < kIters / 4; ++grp) {
+    float p[QB][4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int it = grp * 4 + j;
+      const v4i kk = use[it] ? kv[it] : v4i{0, 0, 0, 0};
+      const int sbu = use[it] ? sbv[it] : 127;
+      const v8i Bm = {kk[0], kk[1], kk[2], kk[3], 0, 0, 0, 0};
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        float sum = 0.f;
+#pragma unroll
+        for (int ht = 0; ht < HT; ++ht) {
+          v4f acc = {0.f, 0.f, 0.f, 0.f};
+          acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A[qb][ht], Bm, acc, 0, 4, 0, 127, 0, sbu);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) sum = fmaf(fmaxf(acc[i], 0.f), wv[qb][ht][i], sum);
+        }
+        p[qb][j] = sum;
+      }
+    }
+    // lane l holds tile g = l/16; its entry slot is base + 64*grp + l
+    const int slot = base + grp * 64 + lane;
+    int e_l = 0;
+    if (kCand) {
+      const int t0 = ent[grp * 4], t1 = ent[grp * 4 + 1], t2 = ent[grp * 4 + 2], t3 = ent[grp * 4 + 3];
+      e_l = g == 0 ? t0 : g == 1 ? t1 : g == 2 ? t2 : t3;
+    }
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
+      const auto x = __builtin_amdgcn_permlane32_swap(__float_as_uint(p[qb][0]), __float_as_uint(p[qb][2]), false,
+                                                      false);
+      const auto y = __builtin_amdgcn_permlane32_swap(__float_as_uint(p[qb][1]), __float_as_uint(p[qb][3]), false,
+                                                      false);
+      const float k0 = __uint_as_float(x[0]) + __uint_as_float(x[1]);
+      const float k1 = __uint_as_float(y[0]) + __uint_as_float(y[1]);
+      const auto z = __builtin_amdgcn_permlane16_swap(__float_as_uint(k0), __float_as_uint(k1), false, false);
+      float res = __uint_as_float(z[0]) + __uint_as_float(z[1]);
       const int q = q0 + qb;
       if (q >= Q) continue;
-      const int lim = kCand ? C : vis[qb];
-      const int e0 = base + 4 * lane;
-      float *dst = scores + ((int64_t)b * Q + q) * Ns + e0;
-      const float4 v = reinterpret_cast<const float4 *>(&sc[wave][qb][0])[lane];
-      if (e0 + 4 <= lim && (Ns & 3) == 0) {
-        *reinterpret_cast<float4 *>(dst) = v;
-      } else {
-        const float vv[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-        for (int u = 0; u < 4; ++u)
-          if (e0 + u < lim) dst[u] = vv[u];
+      float *dst = scores + ((int64_t)b * Q + q) * Ns;
+      if (kCand) {
+        if (!(e_l >= 0 && e_l < vis[0])) res = __uint_as_float(kNoScoreBits);
+        if (slot < C) dst[slot] = res;
+      } else if (slot < vis[qb]) {
+        dst[slot] = res;
       }
     }
   }

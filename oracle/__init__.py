@@ -49,4 +49,12 @@ from .csa import (  # noqa: F401
     csa2_pair,
     block_pool,
     hier_pair,
+    csa2_stack,
+    FULL,
+    REINDEX,
+    REUSE,
+    CAND_AUTO,
+    CAND_SCAN,
+    CAND_SELECTION,
+    CAND_POOL,
 )

@@ -300,3 +300,72 @@ def hier_pair(cache: dict, layer_a: dict, layer_b: dict, p: int, m: int, n_entri
                                   layer_b["swa"], layer_b["swa_pos0"], p, n_win, scale, m, n_entries)
     return dict(idx_a=idx_a, score_a=sc_a, pool=pool, kept=kept, o_a=o_a, lse_a=lse_a,
                 idx_b=idx_b, score_b=sc_b, o_b=o_b, lse_b=lse_b)
+
+
+# Candidate sources of a Reindex layer (see ``csa2_stack``).
+CAND_AUTO, CAND_SCAN, CAND_SELECTION, CAND_POOL = 0, 1, 2, 3
+FULL, REINDEX, REUSE = 0, 1, 2
+
+
+def csa2_stack(layers: list, p: int, m: int, n_win: int) -> list:
+    """A stack of CSA2 layers for one query, each statically Full, Reindex or
+    Reuse ([V4.1], CSA2 paragraph and Fig. 4; hierarchical pool: the
+    "Hierarchical Sparse Indexer" bullet and Fig. 5).
+
+    * Full: scores every visible entry of its own cache (``cache`` holds the
+      planes and ``n_entries``) with its own indexer query, keeps its top-k,
+      optionally builds the block pool (``pool_block`` / ``pool_blocks``),
+      and attends to its selection.
+    * Reindex: reuses the cache of the most recent Full layer, scores
+      candidates with its own indexer query and keeps its own top-k.  The
+      candidates (``cand``): CAND_SCAN every visible entry; CAND_SELECTION
+      the selection of the most recent index-producing layer (Full or
+      Reindex); CAND_POOL the pool of the most recent Full layer; CAND_AUTO
+      the pool when that Full layer built one, else the selection.
+    * Reuse: reuses the most recent Full layer's cache and the selection of
+      the most recent index-producing layer; no indexer work.
+
+    Every layer attends with its own query ``q`` and window (``swa``,
+    ``swa_pos0``) and ``scale``.  Returns one dict per layer with ``idx``
+    (the selection it attended to), ``pool`` (Full layers with a pool) and
+    ``o`` / ``lse``.
+    """
+    out = []
+    full = None        # most recent Full layer's cache
+    pool = None        # ... and its pool (None when it built none)
+    sel = None         # most recent index-producing layer's selection
+    for L in layers:
+        mode = L["mode"]
+        r = {}
+        if mode == FULL:
+            full = L["cache"]
+            idx, _, js, s = index_topk(full["ikey"], full["iscale"], L["qI"], L["w"], p, m, full["n_entries"],
+                                       L["k"])
+            pool = None
+            if L.get("pool_blocks", 0) > 0:
+                pool, _ = block_pool(s, len(js), L["pool_block"], L["pool_blocks"])
+                r["pool"] = pool
+            sel = idx
+        elif mode == REINDEX:
+            if full is None:
+                raise ValueError("a Reindex layer needs an earlier Full layer")
+            src = L.get("cand", CAND_AUTO)
+            if src == CAND_AUTO:
+                src = CAND_POOL if pool is not None else CAND_SELECTION
+            if src == CAND_POOL and pool is None:
+                raise ValueError("no pool to rescore")
+            cand = None if src == CAND_SCAN else (pool if src == CAND_POOL else sel)
+            idx, _, _, _ = index_topk(full["ikey"], full["iscale"], L["qI"], L["w"], p, m, full["n_entries"],
+                                      L["k"], cand=cand)
+            sel = idx
+        elif mode == REUSE:
+            if full is None or sel is None:
+                raise ValueError("a Reuse layer needs an earlier index-producing layer")
+            idx = sel
+        else:
+            raise ValueError(f"unknown mode {mode}")
+        r["idx"] = idx
+        r["o"], r["lse"] = sparse_attention(L["q"], full["nope"], full["nscale"], full["rope"], idx, L["swa"],
+                                            L["swa_pos0"], p, n_win, L["scale"], m, full["n_entries"])
+        out.append(r)
+    return out

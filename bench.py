@@ -119,6 +119,8 @@ def main():
     ap.add_argument("--csa2-steps", type=int, default=64, help="graph-timed CSA2 two-layer 1M decode steps (0 = skip)")
     ap.add_argument("--hier-steps", type=int, default=64,
                     help="graph-timed two-layer 1M decode steps with the hierarchical pool (0 = skip)")
+    ap.add_argument("--stack-steps", type=int, default=64,
+                    help="graph-timed four-layer CSA2 stack steps at 1M context (0 = skip)")
     ap.add_argument("--replays", type=int, default=20, help="individually timed graph replays (>= 20)")
     ap.add_argument("--copy-calibration", action="store_true", help="run a plain device copy of known size")
     args = ap.parse_args()
@@ -322,6 +324,9 @@ def main():
     if args.hier_steps > 0 and not args.only_index:
         torch.cuda.empty_cache()
         result["csa2_hier"] = hier_leg(K=args.hier_steps)
+    if args.stack_steps > 0 and not args.only_index:
+        torch.cuda.empty_cache()
+        result["csa2_stack"] = stack_leg(K=args.stack_steps)
 
     if args.cpu_sample > 0 and not args.only_index:
         result["cpu_baseline"] = cpu_baseline(w, args.cpu_sample)
@@ -763,6 +768,89 @@ def hier_leg(L=8, K=64):
             "cpu_oracle": {"value": round(1.0 / dt, 3), "unit": "two-layer query-tokens/s", "cores": _oracle_threads(),
                            "sample": f"one sequence's Full layer (scores of {w.N} entries, top-{w.k}, pool, "
                                      f"attention) and Reindex layer ({C} candidates): {dt:.2f} s"}}
+
+
+def stack_leg(L=8, K=64):
+    """A four-layer CSA2 stack at 1M context ([V4.1] Fig. 4 modes, Fig. 5
+    pool) through csa2_layer_stack: Full (top-512 and a pool of 2,048 blocks
+    x 8), Reuse, Reindex over the pool (top-512), Reuse.  4 sequences,
+    262,144 entries; one step = the four layers for one query per sequence;
+    L rotating caches.  The oracle times the stack for one sequence."""
+    import dataclasses
+
+    import torch
+
+    import compressed_sparse_attention_compressor_amd as csa
+    import oracle as O
+    from synth.workloads import CSA2_HIER_DECODE as w, as_u16, queries, raw_rows, synthetic_cache
+
+    dev = "cuda"
+    C = w.pool_block * w.pool_blocks
+    planes = synthetic_cache(w, device=dev)
+    caches = _layer_caches(w, planes, L, dev)
+    x_win, _ = raw_rows(w, w.T - w.n_win, w.T, device=dev)
+    s0 = torch.full((w.B,), w.T - w.n_win, dtype=torch.int32, device=dev)
+    modes = [csa.CSA2_FULL, csa.CSA2_REUSE, csa.CSA2_REINDEX, csa.CSA2_REUSE]
+    names = ["full+pool", "reuse", "reindex(pool)", "reuse"]
+    qs = [queries(dataclasses.replace(w, cfg=w.cfg + 100 * (i + 1)), device=dev) for i in range(len(modes))]
+    pos = qs[0]["q_pos"]
+
+    def layers_for(l, upto=None):
+        out = []
+        for i, md in enumerate(modes[:upto]):
+            d = dict(mode=md, q=qs[i]["q"], swa=x_win, swa_pos0=s0, n_win=w.n_win, scale=w.softmax_scale,
+                     out=bufs[l]["out"][i], lse=bufs[l]["lse"][i])
+            if md != csa.CSA2_REUSE:
+                d.update(qI=qs[i]["qI"], w=qs[i]["w"], k=w.k, idx_out=bufs[l]["idx"][i])
+            if md == csa.CSA2_FULL:
+                d.update(cache=caches[l], pool_block=w.pool_block, pool_blocks=w.pool_blocks, pool_out=bufs[l]["pool"])
+            if md == csa.CSA2_REINDEX:
+                d["cand"] = csa.CAND_POOL
+            out.append(d)
+        return out
+
+    bufs = []
+    for _ in range(L):
+        bufs.append(dict(out=[torch.empty(w.B, 1, w.H, 576, dtype=torch.bfloat16, device=dev) for _ in modes],
+                         lse=[torch.empty(w.B, 1, w.H, dtype=torch.float32, device=dev) for _ in modes],
+                         idx=[torch.empty(w.B, 1, w.k, dtype=torch.int32, device=dev) for _ in modes],
+                         pool=torch.empty(w.B, 1, C, dtype=torch.int32, device=dev)))
+    stacks = [layers_for(l) for l in range(L)]
+    fulls = [layers_for(l, 1) for l in range(L)]
+    ws = torch.empty(1 << 28, dtype=torch.uint8, device=dev)
+    ms = _graph_ms(lambda: [csa.layer_stack(stacks[i % L], pos, ws=ws) for i in range(K)], K)
+    ms_full = _graph_ms(lambda: [csa.layer_stack(fulls[i % L], pos, ws=ws) for i in range(K)], K)
+    per_q = 2 * w.n_win * 576 + 2 * 2 * w.H * 576
+    by = {"full+pool": w.N * 68 + w.H_I * (w.d_idx + 4) + w.k * 400 + per_q, "reuse": w.k * 400 + per_q,
+          "reindex(pool)": C * 68 + w.H_I * (w.d_idx + 4) + w.k * 400 + per_q}
+    step_bytes = w.B * sum(by[n] for n in names)
+    gbps = step_bytes / (ms * 1e-3) / 1e9
+    log(f"[bench] stack step {ms * 1e3:.2f} us (Full layer {ms_full * 1e3:.2f}), {gbps:.0f} GB/s")
+
+    pc = {k: v[0].cpu().numpy() if k != "rope" else as_u16(v[0]) for k, v in planes.items()}
+    pc["n_entries"] = w.N
+    ol = []
+    for i, md in enumerate(modes):
+        d = dict(mode=md, q=as_u16(qs[i]["q"][0, 0]), swa=as_u16(x_win[0]), swa_pos0=w.T - w.n_win,
+                 scale=w.softmax_scale)
+        if md != csa.CSA2_REUSE:
+            d.update(qI=qs[i]["qI"][0, 0].cpu().numpy(), w=qs[i]["w"][0, 0].cpu().numpy(), k=w.k)
+        if md == csa.CSA2_FULL:
+            d.update(cache=pc, pool_block=w.pool_block, pool_blocks=w.pool_blocks)
+        if md == csa.CSA2_REINDEX:
+            d["cand"] = O.CAND_POOL
+        ol.append(d)
+    t0 = time.perf_counter()
+    O.csa2_stack(ol, w.T - 1, w.m, w.n_win)
+    dt = time.perf_counter() - t0
+    return {"workload": "csa2-stack4-decode-b4-1m", "B": w.B, "context": w.T, "entries": w.N, "layers": names,
+            "top_k": w.k, "pool": {"block": w.pool_block, "blocks": w.pool_blocks, "candidates": C}, "heads": w.H,
+            "index_heads": w.H_I, "d_idx": w.d_idx, "n_win": w.n_win, "layers_rotated": L, "steps": K,
+            "ms_per_step": round(ms, 6), "full_layer_ms": round(ms_full, 6),
+            "q_tokens_per_s": round(w.B / (ms * 1e-3), 1), "step_bytes": step_bytes,
+            "achieved_GBps": round(gbps, 1), "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4),
+            "cpu_oracle": {"value": round(1.0 / dt, 3), "unit": "four-layer query-tokens/s", "cores": _oracle_threads(),
+                           "sample": f"one sequence's four-layer stack: {dt:.2f} s"}}
 
 
 def cpu_baseline(w, nseq, min_seconds=10.0):

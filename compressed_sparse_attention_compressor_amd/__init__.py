@@ -15,6 +15,14 @@ from .ops import (  # noqa: F401
     index_scores,
     index_pool,
     index_topk,
+    layer_stack,
+    CSA2_FULL,
+    CSA2_REINDEX,
+    CSA2_REUSE,
+    CAND_AUTO,
+    CAND_SCAN,
+    CAND_SELECTION,
+    CAND_POOL,
     topk,
     sparse_attn,
     workspace_bytes,

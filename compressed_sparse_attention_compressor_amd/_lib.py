@@ -36,6 +36,32 @@ class CacheT(ctypes.Structure):
     ]
 
 
+class Csa2LayerT(ctypes.Structure):
+    _fields_ = [
+        ("mode", ctypes.c_int32),
+        ("cand", ctypes.c_int32),
+        ("cache", ctypes.POINTER(CacheT)),
+        ("q_idx", c_void_p),
+        ("w_idx", c_void_p),
+        ("H_I", ctypes.c_int32),
+        ("k", ctypes.c_int32),
+        ("pool_block", ctypes.c_int32),
+        ("pool_blocks", ctypes.c_int32),
+        ("idx_out", c_void_p),
+        ("pool_out", c_void_p),
+        ("q", c_void_p),
+        ("H", ctypes.c_int32),
+        ("n_win", ctypes.c_int32),
+        ("swa", c_void_p),
+        ("swa_pos0", c_void_p),
+        ("S", ctypes.c_int32),
+        ("softmax_scale", c_float),
+        ("out_dtype", ctypes.c_int32),
+        ("out", c_void_p),
+        ("lse", c_void_p),
+    ]
+
+
 _SIGS = {
     "csa_compress": (c_int, [c_void_p, c_int64, c_void_p, c_int64, c_int, c_void_p, c_void_p, c_int64, c_int64,
                              ctypes.POINTER(CacheT), c_void_p]),
@@ -52,6 +78,8 @@ _SIGS = {
                                 c_void_p]),
     "hca_dense_attn": (c_int, [ctypes.POINTER(CacheT), c_void_p, c_int, c_void_p, c_int, c_void_p, c_void_p, c_int,
                                c_int, c_float, c_int, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]),
+    "csa2_layer_stack": (c_int, [ctypes.POINTER(Csa2LayerT), c_int, c_void_p, c_int, c_void_p, c_size_t, c_void_p]),
+    "csa2_stack_workspace_bytes": (c_size_t, [ctypes.POINTER(Csa2LayerT), c_int, c_int]),
     "csa_workspace_bytes": (c_size_t, [c_int, c_int, c_int, c_int, c_int, c_int]),
     "csa_status_str": (ctypes.c_char_p, [c_int]),
     "csa_version": (c_int, []),

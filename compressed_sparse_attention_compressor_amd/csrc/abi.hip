@@ -263,4 +263,157 @@ int hca_dense_attn(const csa_cache_t *cache, const uint16_t *q, int H, const int
                                          out_dtype == CSA_OUT_BF16, out, lse, ws, stream));
 }
 
+// ---------------------------------------------------------------------------
+// CSA2 layer stack: host orchestration of the calls above.
+
+static int check_pool_args(int block, int n_blocks, const int32_t *pool_out) {
+  if (!pool_out) return CSA_ERR_NULL;
+  if (block < 1 || block > kMaxPoolBlock || n_blocks < 1) return CSA_ERR_UNSUPPORTED;
+  if ((int64_t)n_blocks * block > kMaxK) return CSA_ERR_UNSUPPORTED;
+  return CSA_OK;
+}
+
+// What one layer of a stack reads: its cache, its candidates (Reindex), and
+// the selection it attends to.
+struct StackStep {
+  const csa_cache_t *cache;
+  const int32_t *cand;
+  int C;
+  const int32_t *sel;
+  int k;
+  size_t ws_scores;  // 256-byte aligned score buffer at the front of ws
+  size_t ws_rest;    // top-k / pool / attention workspace behind it
+};
+
+// Walks the stack, applying every check of the calls it will make; fills
+// steps[] and the workspace needed.  Launches nothing.
+static int stack_plan(const csa2_layer_t *L, int n, const int32_t *q_pos, int Q, StackStep *steps, size_t *ws_need) {
+  if (!L || !q_pos) return CSA_ERR_NULL;
+  if (n < 1 || Q < 0) return CSA_ERR_SHAPE;
+  const csa_cache_t *full = nullptr;
+  const int32_t *pool = nullptr;
+  int pool_C = 0;
+  const int32_t *sel = nullptr;
+  int sel_k = 0;
+  int B = -1;
+  size_t need = 0;
+  for (int i = 0; i < n; ++i) {
+    const csa2_layer_t &l = L[i];
+    StackStep st{};
+    int rc;
+    if (l.mode == CSA2_FULL) {
+      if (!l.cache) return CSA_ERR_NULL;
+      if (B >= 0 && l.cache->B != B) return CSA_ERR_SHAPE;
+      B = l.cache->B;
+      if (l.k < 1) return CSA_ERR_SHAPE;
+      if ((rc = check_index_args(l.cache, l.q_idx, l.w_idx, l.H_I, q_pos, Q, nullptr, 0))) return rc;
+      if ((rc = check_topk_args(l.cache, q_pos, Q, nullptr, 0, l.k, l.idx_out))) return rc;
+      full = l.cache;
+      pool = nullptr;
+      pool_C = 0;
+      size_t rest = topk_ws_bytes(B, Q, full->N_cap, l.k, false);
+      if (l.pool_blocks > 0) {
+        if ((rc = check_pool_args(l.pool_block, l.pool_blocks, l.pool_out))) return rc;
+        pool = l.pool_out;
+        pool_C = l.pool_blocks * l.pool_block;
+        const size_t pb = csa::pool_workspace_bytes(B, Q, full->N_cap, l.pool_block, l.pool_blocks);
+        rest = rest > pb ? rest : pb;
+      } else if (l.pool_blocks < 0) {
+        return CSA_ERR_SHAPE;
+      }
+      st.ws_scores = align256(index_ws_bytes(B, Q, full->N_cap, 0));
+      st.ws_rest = rest;
+      sel = l.idx_out;
+      sel_k = l.k;
+    } else if (l.mode == CSA2_REINDEX) {
+      if (!full) return CSA_ERR_SHAPE;
+      if (l.k < 1) return CSA_ERR_SHAPE;
+      int src = l.cand;
+      if (src == CSA2_CAND_AUTO) src = pool ? CSA2_CAND_POOL : CSA2_CAND_SELECTION;
+      if (src == CSA2_CAND_POOL) {
+        if (!pool) return CSA_ERR_SHAPE;
+        st.cand = pool;
+        st.C = pool_C;
+      } else if (src == CSA2_CAND_SELECTION) {
+        st.cand = sel;
+        st.C = sel_k;
+      } else if (src != CSA2_CAND_SCAN) {
+        return CSA_ERR_UNSUPPORTED;
+      }
+      if ((rc = check_index_args(full, l.q_idx, l.w_idx, l.H_I, q_pos, Q, st.cand, st.C))) return rc;
+      if ((rc = check_topk_args(full, q_pos, Q, st.cand, st.C, l.k, l.idx_out))) return rc;
+      const int Ns = st.cand ? st.C : full->N_cap;
+      st.ws_scores = align256(index_ws_bytes(B, Q, full->N_cap, st.cand ? st.C : 0));
+      st.ws_rest = topk_ws_bytes(B, Q, Ns, l.k, st.cand != nullptr);
+      sel = l.idx_out;
+      sel_k = l.k;
+    } else if (l.mode == CSA2_REUSE) {
+      if (!full || !sel) return CSA_ERR_SHAPE;
+    } else {
+      return CSA_ERR_UNSUPPORTED;
+    }
+    st.cache = full;
+    st.sel = sel;
+    st.k = sel_k;
+    if ((rc = check_attn_common(full, l.q, l.H, q_pos, Q, l.swa, l.swa_pos0, l.S, l.n_win, l.softmax_scale,
+                                l.out_dtype, l.out)))
+      return rc;
+    if (st.k > kMaxK) return CSA_ERR_UNSUPPORTED;
+    if (Q == 0 || B == 0) {
+      // nothing will be launched: no workspace
+      st.ws_scores = st.ws_rest = 0;
+    } else {
+      const size_t aw = csa::attn_workspace_bytes(B, Q, l.H, st.k, l.n_win);
+      st.ws_rest = st.ws_rest > aw ? st.ws_rest : aw;
+    }
+    const size_t total = st.ws_scores + st.ws_rest;
+    need = need > total ? need : total;
+    if (steps) steps[i] = st;
+  }
+  *ws_need = need;
+  return CSA_OK;
+}
+
+size_t csa2_stack_workspace_bytes(const csa2_layer_t *layers, int n_layers, int Q) {
+  if (!layers || n_layers < 1 || Q < 0) return 0;
+  // a q_pos pointer only has to be non-null for the walk
+  static const int32_t dummy = 0;
+  size_t need = 0;
+  if (stack_plan(layers, n_layers, &dummy, Q, nullptr, &need) != CSA_OK) return 0;
+  return need;
+}
+
+int csa2_layer_stack(const csa2_layer_t *layers, int n_layers, const int32_t *q_pos, int Q, void *ws,
+                     size_t ws_bytes, hipStream_t stream) {
+  if (!layers) return CSA_ERR_NULL;
+  if (n_layers < 1 || n_layers > 4096) return CSA_ERR_SHAPE;
+  StackStep steps_small[16];
+  StackStep *steps = n_layers <= 16 ? steps_small : new StackStep[n_layers];
+  size_t need = 0;
+  int st = stack_plan(layers, n_layers, q_pos, Q, steps, &need);
+  if (st == CSA_OK && need > 0 && !ws) st = CSA_ERR_NULL;
+  if (st == CSA_OK && ws_bytes < need) st = CSA_ERR_WORKSPACE;
+  if (st == CSA_OK && ws && !aligned16(ws)) st = CSA_ERR_ALIGN;
+  const int B = st == CSA_OK ? steps[0].cache->B : 0;
+  for (int i = 0; st == CSA_OK && i < n_layers && Q > 0 && B > 0; ++i) {
+    const csa2_layer_t &l = layers[i];
+    const StackStep &s = steps[i];
+    float *scores = reinterpret_cast<float *>(ws);
+    void *rest = s.ws_rest ? reinterpret_cast<char *>(ws) + s.ws_scores : nullptr;
+    if (l.mode != CSA2_REUSE) {
+      st = csa_index_scores(s.cache, l.q_idx, l.w_idx, l.H_I, q_pos, Q, s.cand, s.C, scores, s.ws_scores, stream);
+      if (st == CSA_OK)
+        st = csa_topk(s.cache, scores, q_pos, Q, s.cand, s.C, l.k, l.idx_out, nullptr, rest, s.ws_rest, stream);
+      if (st == CSA_OK && l.mode == CSA2_FULL && l.pool_blocks > 0)
+        st = csa_index_pool(s.cache, scores, q_pos, Q, l.pool_block, l.pool_blocks, l.pool_out, rest, s.ws_rest,
+                            stream);
+    }
+    if (st == CSA_OK)
+      st = csa_sparse_attn(s.cache, l.q, l.H, q_pos, Q, s.sel, s.k, l.swa, l.swa_pos0, l.S, l.n_win,
+                           l.softmax_scale, l.out_dtype, l.out, l.lse, rest, s.ws_rest, stream);
+  }
+  if (steps != steps_small) delete[] steps;
+  return st;
+}
+
 }  // extern "C"

@@ -10,7 +10,7 @@ import ctypes
 
 import torch
 
-from ._lib import CacheT, check, lib
+from ._lib import CacheT, Csa2LayerT, check, lib
 
 D, D_NOPE, D_ROPE = 576, 512, 64
 WS_INDEX_TOPK, WS_SPARSE_ATTN, WS_DENSE_ATTN, WS_TOPK, WS_INDEX_POOL = 0, 1, 2, 3, 4
@@ -155,6 +155,66 @@ def index_pool(cache: Cache, scores, q_pos, block, n_blocks, out=None, ws=None):
     check(lib().csa_index_pool(ctypes.byref(cs), _ptr(scores), _ptr(q_pos), Q, int(block), int(n_blocks), _ptr(pool),
                                _ptr(ws), wsb, _stream()), "csa_index_pool")
     return pool
+
+
+CSA2_FULL, CSA2_REINDEX, CSA2_REUSE = 0, 1, 2
+CAND_AUTO, CAND_SCAN, CAND_SELECTION, CAND_POOL = 0, 1, 2, 3
+
+
+def layer_stack(layers, q_pos, ws=None):
+    """A stack of CSA2 layers (Full / Reindex / Reuse) in one call.
+
+    ``layers``: dicts with ``mode`` and, as the mode needs them, ``cache``
+    (Full), ``qI``, ``w``, ``k``, ``cand`` (Reindex), ``pool_block`` /
+    ``pool_blocks`` (Full), and for every layer ``q``, ``swa``, ``swa_pos0``,
+    ``n_win``, ``scale`` and optionally ``out_dtype``, ``out``, ``lse``,
+    ``idx_out``, ``pool_out``.  Returns one dict per layer with ``out``,
+    ``lse``, and ``idx`` / ``pool`` where the layer writes them.
+    """
+    B, Q = q_pos.shape
+    dev = q_pos.device
+    n = len(layers)
+    arr = (Csa2LayerT * n)()
+    keep, res = [], []
+    for i, L in enumerate(layers):
+        mode = int(L["mode"])
+        q = L["q"]
+        _need(q, torch.bfloat16, "q")
+        H = q.shape[2]
+        od = L.get("out_dtype", torch.bfloat16)
+        r = {"out": L.get("out") if L.get("out") is not None else _attn_out(B, Q, H, od, dev, None)}
+        r["lse"] = L.get("lse") if L.get("lse") is not None else torch.empty(B, Q, H, dtype=torch.float32, device=dev)
+        e = arr[i]
+        e.mode = mode
+        e.cand = int(L.get("cand", CAND_AUTO))
+        if mode == CSA2_FULL:
+            cs = L["cache"].struct()
+            keep.append(cs)
+            e.cache = ctypes.pointer(cs)
+        if mode != CSA2_REUSE:
+            k = int(L["k"])
+            r["idx"] = L.get("idx_out") if L.get("idx_out") is not None else torch.empty(
+                B, Q, k, dtype=torch.int32, device=dev)
+            e.q_idx, e.w_idx, e.H_I, e.k = _ptr(L["qI"]), _ptr(L["w"]), L["qI"].shape[2], k
+            e.idx_out = _ptr(r["idx"])
+        if mode == CSA2_FULL and int(L.get("pool_blocks", 0)) > 0:
+            C = int(L["pool_blocks"]) * int(L["pool_block"])
+            r["pool"] = L.get("pool_out") if L.get("pool_out") is not None else torch.empty(
+                B, Q, C, dtype=torch.int32, device=dev)
+            e.pool_block, e.pool_blocks = int(L["pool_block"]), int(L["pool_blocks"])
+            e.pool_out = _ptr(r["pool"])
+        swa = L.get("swa")
+        e.q, e.H, e.n_win = _ptr(q), H, int(L["n_win"])
+        e.swa, e.swa_pos0, e.S = _ptr(swa), _ptr(L.get("swa_pos0")), swa.shape[1] if swa is not None else 0
+        e.softmax_scale = float(L["scale"])
+        e.out_dtype = OUT_BF16 if od == torch.bfloat16 else OUT_F32
+        e.out, e.lse = _ptr(r["out"]), _ptr(r["lse"])
+        res.append(r)
+    L_ = lib()
+    need = L_.csa2_stack_workspace_bytes(arr, n, Q)
+    ws, wsb = _workspace(max(need, 16), ws, dev)
+    check(L_.csa2_layer_stack(arr, n, _ptr(q_pos), Q, _ptr(ws), wsb, _stream()), "csa2_layer_stack")
+    return res
 
 
 def _attn_out(B, Q, H, out_dtype, dev, out):

@@ -181,6 +181,60 @@ int hca_dense_attn(const csa_cache_t *cache, const uint16_t *q, int H, const int
                    const uint16_t *swa, const int32_t *swa_pos0, int S, int n_win, float softmax_scale,
                    int out_dtype, void *out, float *lse, void *ws, size_t ws_bytes, hipStream_t stream);
 
+/* A stack of CSA2 layers for the same query tokens ([V4.1], CSA2 paragraph
+ * and Fig. 4: every layer is statically Full, Reindex or Reuse; Fig. 5: the
+ * first Full layer may build the hierarchical candidate pool).  The stack is
+ * walked in order on `stream`:
+ *   Full     scores every visible entry of its own `cache` with q_idx/w_idx,
+ *            writes its top-k to idx_out, builds the pool into pool_out when
+ *            pool_blocks > 0, and attends to its selection; it becomes the
+ *            cache of the layers that follow and drops any earlier pool.
+ *   Reindex  scores candidates of the latest Full layer's cache with its own
+ *            q_idx/w_idx and writes its own top-k to idx_out; the candidates
+ *            (`cand`): CSA2_CAND_POOL the latest Full layer's pool,
+ *            CSA2_CAND_SELECTION the latest Full or Reindex layer's
+ *            selection, CSA2_CAND_SCAN every visible entry, CSA2_CAND_AUTO the
+ *            pool when the latest Full layer built one, else the selection.
+ *   Reuse    attends to the latest Full or Reindex layer's selection on the
+ *            latest Full layer's cache; no indexer work.
+ * Every layer attends with its own q, window rows and output buffers, as in
+ * csa_sparse_attn.  The first layer must be Full.  Layer fields that a mode
+ * does not use are ignored.  All checks of every layer (those of the calls
+ * named above plus the stack rules) run before the first launch. */
+enum { CSA2_FULL = 0, CSA2_REINDEX = 1, CSA2_REUSE = 2 };
+enum { CSA2_CAND_AUTO = 0, CSA2_CAND_SCAN = 1, CSA2_CAND_SELECTION = 2, CSA2_CAND_POOL = 3 };
+typedef struct {
+  int32_t mode;              /* CSA2_FULL, CSA2_REINDEX or CSA2_REUSE              */
+  int32_t cand;              /* Reindex: CSA2_CAND_*                                 */
+  const csa_cache_t *cache;  /* Full: this layer's cache                             */
+  const uint8_t *q_idx;      /* Full, Reindex: E4M3 [B][Q][H_I][d_idx]               */
+  const float *w_idx;        /* Full, Reindex: fp32 [B][Q][H_I]                      */
+  int32_t H_I;
+  int32_t k;                 /* Full, Reindex: entries selected (>= 1)              */
+  int32_t pool_block;        /* Full: entries per pool block (when pool_blocks > 0)  */
+  int32_t pool_blocks;       /* Full: blocks kept; 0 = no pool                       */
+  int32_t *idx_out;          /* Full, Reindex: int32 [B][Q][k]                       */
+  int32_t *pool_out;         /* Full with a pool: int32 [B][Q][pool_blocks*pool_block] */
+  const uint16_t *q;         /* bf16 [B][Q][H][576]                                  */
+  int32_t H;
+  int32_t n_win;
+  const uint16_t *swa;       /* bf16 window rows [B][S][576] from raw position swa_pos0[b] */
+  const int32_t *swa_pos0;
+  int32_t S;
+  float softmax_scale;
+  int32_t out_dtype;         /* CSA_OUT_F32 or CSA_OUT_BF16                          */
+  void *out;                 /* [B][Q][H][576]                                       */
+  float *lse;                /* fp32 [B][Q][H] or NULL                               */
+} csa2_layer_t;
+
+/*   q_pos  int32 [B][Q] raw positions, shared by every layer
+ *   ws     >= csa2_stack_workspace_bytes(layers, n_layers, Q) bytes, 16-byte
+ *          aligned, reused by each layer in turn. */
+int csa2_layer_stack(const csa2_layer_t *layers, int n_layers, const int32_t *q_pos, int Q, void *ws,
+                     size_t ws_bytes, hipStream_t stream);
+/* Workspace of csa2_layer_stack; 0 when the stack is not valid. */
+size_t csa2_stack_workspace_bytes(const csa2_layer_t *layers, int n_layers, int Q);
+
 enum { CSA_WS_INDEX_TOPK = 0, CSA_WS_SPARSE_ATTN = 1, CSA_WS_DENSE_ATTN = 2, CSA_WS_TOPK = 3, CSA_WS_INDEX_POOL = 4 };
 
 /* Workspace bytes for one call (0 = none needed).

@@ -29,7 +29,7 @@ def L():
 def _declared():
     src = open(HEADER).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*((?:csa|hca)_\w+)\s*\(", src, flags=re.M)))
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*((?:csa2?|hca)_\w+)\s*\(", src, flags=re.M)))
 
 
 def test_every_declared_symbol_is_exported(L):
@@ -148,3 +148,50 @@ def test_index_pool_checks(L):
     assert _pool(L, _cache(), wsb=need - 1) == EWS
     assert _pool(L, _cache(), Q=0) == OK
     assert L.csa_workspace_bytes(4, 2, 1, 16, 64, 0) == 0        # unsupported block
+
+
+def _layer(mode, cache=None, k=8, cand=0, pool_block=0, pool_blocks=0, q=P, idx=P, pool=P, H=64, od=1):
+    e = _lib.Csa2LayerT()
+    e.mode, e.cand, e.k, e.pool_block, e.pool_blocks = mode, cand, k, pool_block, pool_blocks
+    if cache is not None:
+        e.cache = ctypes.pointer(cache)
+    e.q_idx, e.w_idx, e.H_I, e.idx_out, e.pool_out = P, P, 32, idx, pool
+    e.q, e.H, e.n_win, e.swa, e.swa_pos0, e.S = q, H, 128, P, P, 128
+    e.softmax_scale, e.out_dtype, e.out, e.lse = 1.0, od, P, None
+    return e
+
+
+def _arr(layers):
+    return (_lib.Csa2LayerT * len(layers))(*layers)
+
+
+def _stack(L, layers, qp=P, Q=1, ws=P, wsb=1 << 30):
+    """Only for stacks that fail a check (a valid one would launch kernels)."""
+    return L.csa2_layer_stack(_arr(layers), len(layers), qp, Q, ws, wsb, None)
+
+
+def test_layer_stack_checks(L):
+    c = _cache()
+    full, reuse = _layer(0, c), _layer(2)
+    assert _stack(L, [full, reuse], Q=0) == OK                 # valid, nothing to launch
+    assert _stack(L, [reuse]) == ESHAPE                        # first layer must be Full
+    assert _stack(L, [_layer(1)]) == ESHAPE                    # Reindex without a Full layer
+    assert _stack(L, [full, _layer(1, cand=3)]) == ESHAPE      # no pool to rescore
+    assert _stack(L, [full, _layer(1, cand=9)]) == EUNSUP
+    assert _stack(L, [_layer(7, c)]) == EUNSUP
+    assert _stack(L, [_layer(0, c, k=0)]) == ESHAPE
+    assert _stack(L, [_layer(0)]) == ENULL                     # Full layer without a cache
+    assert _stack(L, [full, _layer(2, q=None)]) == ENULL       # a later layer's check fails first
+    assert _stack(L, [full, _layer(2, H=48)]) == EUNSUP
+    assert _stack(L, [_layer(0, c, pool_block=65, pool_blocks=4)]) == EUNSUP
+    assert _stack(L, [_layer(0, c, pool_block=8, pool_blocks=4, pool=None)]) == ENULL
+    assert _stack(L, [full, _layer(0, _cache(B=3))]) == ESHAPE  # every cache holds the same sequences
+    assert _stack(L, [full, reuse], qp=None) == ENULL
+    good = [_layer(0, c, pool_block=8, pool_blocks=4), _layer(1, cand=0), reuse]
+    need = L.csa2_stack_workspace_bytes(_arr(good), 3, 1)
+    # scores of 2 x 64 entries, then the largest of the pool, top-k and attention workspaces
+    assert need >= 2 * 64 * 4
+    assert L.csa2_stack_workspace_bytes(_arr([reuse]), 1, 1) == 0      # invalid stack
+    assert _stack(L, good, wsb=need - 1) == EWS
+    assert _stack(L, good, ws=P + 8) == EALIGN
+    assert _stack(L, good, ws=None) == ENULL

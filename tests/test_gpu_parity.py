@@ -422,6 +422,91 @@ def test_hier_pool_reindex_parity():
         check_topk(g_b[b, 0], ob, jb, sb, what=f"reindex b={b}")
 
 
+def test_layer_stack_parity():
+    """An 8-layer CSA2 stack through csa2_layer_stack ([V4.1] Fig. 4 modes,
+    Fig. 5 pool): Full with a pool, Reuse, Reindex over the pool, Reuse, a
+    second Full on another cache, Reindex over its selection, Reindex by a
+    full scan, Reuse.  Checked stage by stage: each layer's selection
+    against the oracle's (up to near-ties) given the GPU's upstream pool or
+    selection, the pool's blocks against the oracle's block maxima, and every
+    layer's attention against the oracle over the selection that layer used."""
+    import dataclasses
+    w = Workload("st", 13, B=3, T=16384, m=4, d_idx=128, H_I=32, k=64, H=64, n_win=64)
+    N = w.N
+    ents = [[N, N - 5, 301], [N - 100, N, 500]]
+    caches_np = [synthetic_cache(w), synthetic_cache(dataclasses.replace(w, cfg=w.cfg + 50))]
+    caches = [_gpu_cache(pl, w.B, N, w.m, w.d_idx, ne) for pl, ne in zip(caches_np, ents)]
+    pos = torch.full((w.B, 1), w.T - 1, dtype=torch.int32, device=DEV)
+    swa, _ = raw_rows(w, w.T - w.n_win, w.T)
+    s0 = torch.full((w.B,), w.T - w.n_win, dtype=torch.int32, device=DEV)
+    spec = [dict(mode=csa.CSA2_FULL, c=0, k=64, pool_block=8, pool_blocks=16), dict(mode=csa.CSA2_REUSE),
+            dict(mode=csa.CSA2_REINDEX, k=32, cand=csa.CAND_AUTO), dict(mode=csa.CSA2_REUSE),
+            dict(mode=csa.CSA2_FULL, c=1, k=48), dict(mode=csa.CSA2_REINDEX, k=16, cand=csa.CAND_SELECTION),
+            dict(mode=csa.CSA2_REINDEX, k=40, cand=csa.CAND_SCAN), dict(mode=csa.CSA2_REUSE)]
+    layers, qs = [], []
+    for i, sp in enumerate(spec):
+        q = queries(dataclasses.replace(w, cfg=w.cfg + 100 * (i + 1)))
+        qs.append(q)
+        L = dict(mode=sp["mode"], q=q["q"].to(DEV), swa=swa.to(DEV), swa_pos0=s0, n_win=w.n_win,
+                 scale=w.softmax_scale, out_dtype=torch.float32)
+        if sp["mode"] != csa.CSA2_REUSE:
+            L.update(qI=q["qI"].to(DEV), w=q["w"].to(DEV), k=sp["k"])
+        if sp["mode"] == csa.CSA2_FULL:
+            L.update(cache=caches[sp["c"]], pool_block=sp.get("pool_block", 0), pool_blocks=sp.get("pool_blocks", 0))
+        if sp["mode"] == csa.CSA2_REINDEX:
+            L["cand"] = sp["cand"]
+        layers.append(L)
+    res = csa.layer_stack(layers, pos)
+    torch.cuda.synchronize()
+    sw = as_u16(swa)
+    p = w.T - 1
+    for b in range(w.B):
+        cur, pool, sel = None, None, None
+        for i, (sp, r) in enumerate(zip(spec, res)):
+            q = qs[i]
+            if sp["mode"] == csa.CSA2_FULL:
+                cur = sp["c"]
+                pl = caches_np[cur]
+                ne = ents[cur][b]
+                g_idx = _np(r["idx"])[b, 0]
+                oi, _, js, sc = O.index_topk(pl["ikey"][b].numpy(), pl["iscale"][b].numpy(), q["qI"][b, 0].numpy(),
+                                             q["w"][b, 0].numpy(), p, w.m, ne, sp["k"])
+                check_topk(g_idx, oi, js, sc, what=f"layer {i} b={b}")
+                pool = None
+                if sp.get("pool_blocks", 0):
+                    g_pool = _np(r["pool"])[b, 0]
+                    V, blk, nb = len(js), sp["pool_block"], sp["pool_blocks"]
+                    _, kept_o = O.block_pool(sc, V, blk, nb)
+                    nbv = -(-V // blk)
+                    bmax = np.maximum.reduceat(sc, np.arange(nbv) * blk)
+                    kept_g = np.unique(g_pool[g_pool >= 0] // blk)
+                    members = np.concatenate([np.arange(kb * blk, min(V, (kb + 1) * blk)) for kb in kept_g])
+                    np.testing.assert_array_equal(g_pool[:len(members)], members)
+                    assert np.all(g_pool[len(members):] == -1)
+                    kept_g = np.concatenate([kept_g, -np.ones(nb - len(kept_g), np.int64)])
+                    check_topk(kept_g, kept_o, np.arange(nbv), bmax, what=f"pool {i} b={b}")
+                    pool = g_pool
+                sel = g_idx
+            elif sp["mode"] == csa.CSA2_REINDEX:
+                pl = caches_np[cur]
+                ne = ents[cur][b]
+                src = sp["cand"]
+                if src == csa.CAND_AUTO:
+                    src = csa.CAND_POOL if pool is not None else csa.CAND_SELECTION
+                cand = None if src == csa.CAND_SCAN else (pool if src == csa.CAND_POOL else sel)
+                g_idx = _np(r["idx"])[b, 0]
+                oi, _, js, sc = O.index_topk(pl["ikey"][b].numpy(), pl["iscale"][b].numpy(), q["qI"][b, 0].numpy(),
+                                             q["w"][b, 0].numpy(), p, w.m, ne, sp["k"], cand=cand)
+                check_topk(g_idx, oi, js, sc, what=f"layer {i} b={b}")
+                sel = g_idx
+            pl = caches_np[cur]
+            o, _ = O.sparse_attention(as_u16(q["q"][b, 0]), pl["nope"][b].numpy(), pl["nscale"][b].numpy(),
+                                      as_u16(pl["rope"][b]), sel, sw[b], w.T - w.n_win, p, w.n_win, w.softmax_scale,
+                                      w.m, ents[cur][b])
+            g = _np(r["out"])[b, 0].astype(np.float64)
+            assert row_rel_err(g, o).max() <= TOL[torch.float32], f"layer {i} b={b}"
+
+
 # ----------------------------------------------------------------------------- attention
 
 

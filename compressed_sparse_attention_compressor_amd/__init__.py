@@ -11,6 +11,7 @@ from .ops import (  # noqa: F401
     D_ROPE,
     Cache,
     compress,
+    compress_index_scores,
     hca_dense_attn,
     index_scores,
     index_pool,

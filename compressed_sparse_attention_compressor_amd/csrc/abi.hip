@@ -120,9 +120,9 @@ size_t csa_workspace_bytes(int op, int B, int Q, int H_or_k, int n, int C) {
   }
 }
 
-int csa_compress(const uint16_t *x, int64_t x_stride_b, const uint16_t *z, int64_t z_stride_b, int G,
-                 const float *pos_bias, const uint16_t *w_ik, int64_t tok_begin, int64_t T,
-                 const csa_cache_t *cache, hipStream_t stream) {
+static int check_compress_args(const uint16_t *x, int64_t x_stride_b, const uint16_t *z, int64_t z_stride_b, int G,
+                               const float *pos_bias, const uint16_t *w_ik, int64_t tok_begin, int64_t T,
+                               const csa_cache_t *cache) {
   int st = check_cache(cache, w_ik != nullptr);
   if (st) return st;
   if (!x || !z || !pos_bias) return CSA_ERR_NULL;
@@ -134,6 +134,14 @@ int csa_compress(const uint16_t *x, int64_t x_stride_b, const uint16_t *z, int64
   if (!aligned16(x) || (G == csa::kD && !aligned16(z))) return CSA_ERR_ALIGN;
   if (G == csa::kD && (z_stride_b % 4)) return CSA_ERR_ALIGN;
   if (x_stride_b % 4) return CSA_ERR_ALIGN;
+  return CSA_OK;
+}
+
+int csa_compress(const uint16_t *x, int64_t x_stride_b, const uint16_t *z, int64_t z_stride_b, int G,
+                 const float *pos_bias, const uint16_t *w_ik, int64_t tok_begin, int64_t T,
+                 const csa_cache_t *cache, hipStream_t stream) {
+  int st = check_compress_args(x, x_stride_b, z, z_stride_b, G, pos_bias, w_ik, tok_begin, T, cache);
+  if (st) return st;
   if (T == 0 || cache->B == 0) return CSA_OK;
   const csa::CacheView v = view_of(cache);
   return status_of(csa::launch_compress(x, x_stride_b, z, z_stride_b, G, pos_bias, w_ik, tok_begin / cache->m,
@@ -209,6 +217,25 @@ int csa_index_topk(const csa_cache_t *cache, const uint8_t *q_idx, const float *
   if (st) return st;
   void *tws = tbytes ? reinterpret_cast<char *>(ws) + align256(sbytes) : nullptr;
   return csa_topk(cache, scores, q_pos, Q, cand, C, k, idx_out, score_out, tws, tbytes, stream);
+}
+
+int csa_compress_index_scores(const uint16_t *x, int64_t x_stride_b, const uint16_t *z, int64_t z_stride_b, int G,
+                              const float *pos_bias, const uint16_t *w_ik, int64_t tok_begin, int64_t T,
+                              const csa_cache_t *cache, const uint8_t *q_idx, const float *w_idx, int H_I,
+                              const int32_t *q_pos, int Q, float *scores, size_t scores_bytes, hipStream_t stream) {
+  int st = check_compress_args(x, x_stride_b, z, z_stride_b, G, pos_bias, w_ik, tok_begin, T, cache);
+  if (st) return st;
+  st = check_index_args(cache, q_idx, w_idx, H_I, q_pos, Q, nullptr, 0);
+  if (st) return st;
+  if (!scores) return CSA_ERR_NULL;
+  if (cache->B > 0 && Q > 0 && scores_bytes < index_ws_bytes(cache->B, Q, cache->N_cap, 0)) return CSA_ERR_WORKSPACE;
+  if (cache->B > 0 && Q > 0 && T > 0 && cache->N_cap > 0 &&
+      csa::append_index_fusable(cache->m, T, Q, G, w_ik, cache->B))
+    return status_of(csa::launch_append_index(x, x_stride_b, z, z_stride_b, G, pos_bias, w_ik, tok_begin / cache->m,
+                                              view_of(cache), q_idx, w_idx, H_I, q_pos, scores, stream));
+  st = csa_compress(x, x_stride_b, z, z_stride_b, G, pos_bias, w_ik, tok_begin, T, cache, stream);
+  if (st) return st;
+  return csa_index_scores(cache, q_idx, w_idx, H_I, q_pos, Q, nullptr, 0, scores, scores_bytes, stream);
 }
 
 int csa_index_pool(const csa_cache_t *cache, const float *scores, const int32_t *q_pos, int Q, int block,

@@ -23,16 +23,6 @@ constexpr int kEPB = 16;
 constexpr int kCompThreads = 256;
 constexpr int kSmallM = 8;   // blocks up to this many rows are pooled from registers
 
-// Encodes the pair (v0, v1) of channels 2t, 2t+1 of a 32-channel block
-// spread over 16 consecutive lanes; returns the packed byte and the block's
-// scale byte (valid in every lane of the group).
-__device__ __forceinline__ uint32_t encode_pair(float v0, float v1, uint32_t &sbyte) {
-  float amax = row16_max(fmaxf(fabsf(v0), fabsf(v1)));
-  sbyte = mx_scale_byte(amax);
-  float inv = mx_inv_scale(sbyte);
-  return e2m1_encode(v0, inv) | (e2m1_encode(v1, inv) << 4);
-}
-
 template <bool kGateFull>
 __global__ __launch_bounds__(kCompThreads) void compress_kernel(
     const uint16_t *__restrict__ x, int64_t x_stride_b, const uint16_t *__restrict__ z, int64_t z_stride_b,

@@ -153,6 +153,16 @@ __device__ __forceinline__ float key_score(uint32_t k) {
   return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
 }
 
+// Encodes the pair (v0, v1) of channels 2t, 2t+1 of a 32-channel block
+// spread over 16 consecutive lanes; returns the packed byte and the block's
+// scale byte (valid in every lane of the group).
+__device__ __forceinline__ uint32_t encode_pair(float v0, float v1, uint32_t &sbyte) {
+  float amax = row16_max(fmaxf(fabsf(v0), fabsf(v1)));
+  sbyte = mx_scale_byte(amax);
+  float inv = mx_inv_scale(sbyte);
+  return e2m1_encode(v0, inv) | (e2m1_encode(v1, inv) << 4);
+}
+
 // Marks a workspace score slot that holds no candidate.
 constexpr uint32_t kNoScoreBits = 0xFFFFFFFFu;
 

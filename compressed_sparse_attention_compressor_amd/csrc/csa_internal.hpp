@@ -28,6 +28,17 @@ hipError_t launch_index_scores(const CacheView &c, const uint8_t *q_idx, const f
                                const int32_t *q_pos, int Q, const int32_t *cand, int C, float *scores,
                                hipStream_t stream);
 
+// Decode append fused with the indexer: csa_compress of one entry per
+// sequence (entry `entry`, from rows 0..m-1 of the x/z chunk) followed by
+// a full-scan csa_index_scores of one query per sequence, in
+// one launch, with identical results.  Only for the shapes
+// append_index_fusable() accepts.
+bool append_index_fusable(int m, int64_t T, int Q, int G, const uint16_t *w_ik, int B);
+hipError_t launch_append_index(const uint16_t *x, int64_t x_stride_b, const uint16_t *z, int64_t z_stride_b, int G,
+                               const float *bias, const uint16_t *w_ik, int64_t entry, const CacheView &c,
+                               const uint8_t *q_idx, const float *w_idx, int H_I, const int32_t *q_pos,
+                               float *scores, hipStream_t stream);
+
 // Top-k plan: rows with few siblings are split into `nsl` slices of S
 // scores whose own top-k candidates (ws_bytes of workspace) are reduced in
 // a second launch.  nsl = 1: one workgroup per row.

@@ -26,24 +26,38 @@ constexpr int kIdxThreads = 256;     // 4 waves
 constexpr int kIdxWaveEntries = 128; // entries per wave per workgroup (groups of 64)
 constexpr int kIdxWGEntries = kIdxThreads / 64 * kIdxWaveEntries;
 
-// HT: head tiles of 16 (H_I <= 16 * HT).  QB: queries per wave.
+// Sum over the four lane groups of per-lane partial sums of four 16-entry
+// tiles (p_j: tile j, entry lane%16): two rounds of permlane swaps, after
+// which lane l holds the total of tile l/16, entry l%16.
+__device__ __forceinline__ float reduce_scatter4(float p0, float p1, float p2, float p3) {
+  const auto x = __builtin_amdgcn_permlane32_swap(__float_as_uint(p0), __float_as_uint(p2), false, false);
+  const auto y = __builtin_amdgcn_permlane32_swap(__float_as_uint(p1), __float_as_uint(p3), false, false);
+  const float k0 = __uint_as_float(x[0]) + __uint_as_float(x[1]);
+  const float k1 = __uint_as_float(y[0]) + __uint_as_float(y[1]);
+  const auto z = __builtin_amdgcn_permlane16_swap(__float_as_uint(k0), __float_as_uint(k1), false, false);
+  return __uint_as_float(z[0]) + __uint_as_float(z[1]);
+}
+
+// HT: head tiles of 16 (H_I <= 16 * HT).  QB: queries per wave.  The body of
+// one workgroup: entry tile bx, query block by, sequence b; the score of
+// entry `skip` (-1: none) is left to another workgroup.
 template <int HT, int QB, bool kCand>
-__global__ __launch_bounds__(kIdxThreads) void index_scores_kernel(
+__device__ __forceinline__ void index_body(
     const uint8_t *__restrict__ ikey, const uint8_t *__restrict__ iscale, const int32_t *__restrict__ n_entries,
     int N_cap, int d_idx, int m, const uint8_t *__restrict__ q_idx, const float *__restrict__ w_idx, int H_I,
     const int32_t *__restrict__ q_pos, int Q, const int32_t *__restrict__ cand, int C, float *__restrict__ scores,
-    int Ns) {
+    int Ns, int bx, int by, int bz, int skip) {
   // Indexer queries of this workgroup (QB queries x 16*HT heads x d_idx bytes),
   // staged once so that the waves read their MFMA fragments from LDS.
   __shared__ __attribute__((aligned(16))) uint8_t qs[QB * HT * 16 * 128];
-  const int b = blockIdx.z;
-  const int q0 = blockIdx.y * QB;
+  const int b = bz;
+  const int q0 = by * QB;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int g = lane >> 4;   // 32-channel block (K group)
   const int r = lane & 15;   // entry within the tile / head row within the head tile
   const int kb = d_idx / 32; // key blocks per entry (2 or 4)
-  const int base = blockIdx.x * kIdxWGEntries + wave * kIdxWaveEntries;
+  const int base = bx * kIdxWGEntries + wave * kIdxWaveEntries;
   constexpr int kIters = kIdxWaveEntries / 16;
   static_assert(kIters % 4 == 0, "whole groups of four 16-entry tiles");
 
@@ -57,7 +71,7 @@ __global__ __launch_bounds__(kIdxThreads) void index_scores_kernel(
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb)
       if (q0 + qb < Q) vmax = max(vmax, min(nE, (q_pos[(int64_t)b * Q + q0 + qb] + 1) / m));
-    if ((int)blockIdx.x * kIdxWGEntries >= vmax) return;
+    if (bx * kIdxWGEntries >= vmax) return;
   }
 
   // 1. Small, cache-resident loads first (queries for LDS staging, head
@@ -219,25 +233,299 @@ __global__ __launch_bounds__(kIdxThreads) void index_scores_kernel(
     }
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
-      const auto x = __builtin_amdgcn_permlane32_swap(__float_as_uint(p[qb][0]), __float_as_uint(p[qb][2]), false,
-                                                      false);
-      const auto y = __builtin_amdgcn_permlane32_swap(__float_as_uint(p[qb][1]), __float_as_uint(p[qb][3]), false,
-                                                      false);
-      const float k0 = __uint_as_float(x[0]) + __uint_as_float(x[1]);
-      const float k1 = __uint_as_float(y[0]) + __uint_as_float(y[1]);
-      const auto z = __builtin_amdgcn_permlane16_swap(__float_as_uint(k0), __float_as_uint(k1), false, false);
-      float res = __uint_as_float(z[0]) + __uint_as_float(z[1]);
+      float res = reduce_scatter4(p[qb][0], p[qb][1], p[qb][2], p[qb][3]);
       const int q = q0 + qb;
       if (q >= Q) continue;
       float *dst = scores + ((int64_t)b * Q + q) * Ns;
       if (kCand) {
         if (!(e_l >= 0 && e_l < vis[0])) res = __uint_as_float(kNoScoreBits);
         if (slot < C) dst[slot] = res;
-      } else if (slot < vis[qb]) {
+      } else if (slot < vis[qb] && slot != skip) {
         dst[slot] = res;
       }
     }
   }
+}
+
+template <int HT, int QB, bool kCand>
+__global__ __launch_bounds__(kIdxThreads) void index_scores_kernel(
+    const uint8_t *__restrict__ ikey, const uint8_t *__restrict__ iscale, const int32_t *__restrict__ n_entries,
+    int N_cap, int d_idx, int m, const uint8_t *__restrict__ q_idx, const float *__restrict__ w_idx, int H_I,
+    const int32_t *__restrict__ q_pos, int Q, const int32_t *__restrict__ cand, int C, float *__restrict__ scores,
+    int Ns) {
+  index_body<HT, QB, kCand>(ikey, iscale, n_entries, N_cap, d_idx, m, q_idx, w_idx, H_I, q_pos, Q, cand, C, scores, Ns,
+                            blockIdx.x, blockIdx.y, blockIdx.z, -1);
+}
+
+// ---------------------------------------------------------------------------
+// Decode append fused with the indexer.  When every sequence appends one
+// entry (one block of m <= 8 raw rows) and then scores it with one query,
+// the first B workgroups of the launch pool and encode the new entry (the
+// compressor's arithmetic, step for step: the same pooling order, MXFP4
+// encoding and 8-slice projection sums as compress.hip, so the cache bytes
+// are identical) and score it from the codes they just produced; the other
+// workgroups run the indexer body on every other visible entry.  The new
+// entry's score goes through the same scaled MFMA (its column of a 16-entry
+// tile, the other columns zero), the same ReLU/weight FMA order and the
+// same reduce-scatter as in the indexer body, so it is identical too.  The
+// indexer workgroups may read the new entry's key while it is being
+// written; its score slot is the one they do not store.
+struct AppendArgs {
+  const uint16_t *x;
+  int64_t x_stride_b;
+  const uint16_t *z;
+  int64_t z_stride_b;
+  const float *bias;
+  const uint16_t *w_ik;
+  int m;
+  int entry;  // the appended entry (the same index in every sequence)
+  uint8_t *nope;
+  uint8_t *nscale;
+  uint16_t *rope;
+};
+
+constexpr int kAppSlices = kIdxThreads / 32;     // projection slices
+constexpr int kAppSlice = kD / kAppSlices;       // channels per slice
+constexpr int kAppMaxM = 8;
+
+template <int HT, bool kGateFull>
+__device__ __forceinline__ void append_and_score(const AppendArgs &ap, uint8_t *__restrict__ ikey,
+                                                 uint8_t *__restrict__ iscale, const int32_t *__restrict__ n_entries,
+                                                 int N_cap, int d_idx, const uint8_t *__restrict__ q_idx,
+                                                 const float *__restrict__ w_idx, int H_I,
+                                                 const int32_t *__restrict__ q_pos, int Q, float *__restrict__ scores,
+                                                 int Ns, int b) {
+  __shared__ __attribute__((aligned(16))) float cs[kD];
+  __shared__ float kpart[kAppSlices][128];
+  __shared__ float ks[128];
+  __shared__ __attribute__((aligned(16))) uint8_t kc[64];
+  __shared__ uint32_t ksc[4];
+  __shared__ __attribute__((aligned(16))) uint8_t qs[HT * 16 * 128];
+  const int tid = threadIdx.x;
+  const int m = ap.m;
+  const int nkb = d_idx / 32;
+  const int64_t row = (int64_t)b * N_cap + ap.entry;
+
+  // queries for LDS staging first (as in the indexer body, one query)
+  constexpr int kQBytes = HT * 16 * 128;
+  constexpr int kQVec = (kQBytes / 16 + kIdxThreads - 1) / kIdxThreads;
+  uint4 qv_stage[kQVec];
+#pragma unroll
+  for (int u = 0; u < kQVec; ++u) {
+    const int i = tid + u * kIdxThreads;
+    const int rem = (i % (kQBytes / 16)) * 16;
+    const int h = rem / 128, c = rem % 128;
+    const bool ok = i < kQBytes / 16 && h < H_I && c < d_idx;
+    const int64_t off = ok ? ((int64_t)b * Q * H_I + h) * d_idx + c : 0;
+    const uint4 v = *reinterpret_cast<const uint4 *>(q_idx + off);
+    qv_stage[u] = ok ? v : uint4{0u, 0u, 0u, 0u};
+  }
+
+  // 1. pooling: thread t < 144 owns channels 4t..4t+3; the chunk holds
+  //    exactly the m raw rows of the new entry (rows 0..m-1)
+  const uint16_t *xb = ap.x + (int64_t)b * ap.x_stride_b;
+  const uint16_t *zb = ap.z + (int64_t)b * ap.z_stride_b;
+  if (tid < kD / 4) {
+    const int c = tid * 4;
+    const int64_t row0 = 0;
+    float mx[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+    float den[4] = {0.f, 0.f, 0.f, 0.f};
+    float num[4] = {0.f, 0.f, 0.f, 0.f};
+    uint2 gz[kAppMaxM], gx[kAppMaxM];
+#pragma unroll
+    for (int i = 0; i < kAppMaxM; ++i) {
+      const int64_t rr = row0 + min(i, m - 1);
+      gx[i] = *reinterpret_cast<const uint2 *>(xb + rr * kD + c);
+      if (kGateFull) {
+        gz[i] = *reinterpret_cast<const uint2 *>(zb + rr * kD + c);
+      } else {
+        const uint32_t h = zb[rr];
+        gz[i] = uint2{h | (h << 16), h | (h << 16)};
+      }
+    }
+    float a[kAppMaxM][4];
+#pragma unroll
+    for (int i = 0; i < kAppMaxM; ++i) {
+      if (i < m) {
+        const float bi = ap.bias[i];
+        a[i][0] = bf16_to_f32(gz[i].x & 0xFFFFu) + bi;
+        a[i][1] = bf16_to_f32(gz[i].x >> 16) + bi;
+        a[i][2] = bf16_to_f32(gz[i].y & 0xFFFFu) + bi;
+        a[i][3] = bf16_to_f32(gz[i].y >> 16) + bi;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) mx[u] = fmaxf(mx[u], a[i][u]);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < kAppMaxM; ++i) {
+      if (i < m) {
+        const float xv[4] = {bf16_to_f32(gx[i].x & 0xFFFFu), bf16_to_f32(gx[i].x >> 16),
+                             bf16_to_f32(gx[i].y & 0xFFFFu), bf16_to_f32(gx[i].y >> 16)};
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const float w = expf(a[i][u] - mx[u]);
+          den[u] += w;
+          num[u] = fmaf(w, xv[u], num[u]);
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) cs[c + u] = num[u] / den[u];
+  }
+#pragma unroll
+  for (int u = 0; u < kQVec; ++u) {
+    const int i = tid + u * kIdxThreads;
+    if (i < kQBytes / 16) *reinterpret_cast<uint4 *>(qs + i * 16) = qv_stage[u];
+  }
+  __syncthreads();
+
+  // 2. MXFP4 main entry and bf16 rope channels
+  {
+    uint32_t sb;
+    const uint32_t byte = encode_pair(cs[2 * tid], cs[2 * tid + 1], sb);
+    ap.nope[row * kNopeBytes + tid] = (uint8_t)byte;
+    if ((tid & 15) == 0) ap.nscale[row * kNopeScales + (tid >> 4)] = (uint8_t)sb;
+  }
+  if (tid < kDRope) ap.rope[row * kDRope + tid] = (uint16_t)f32_to_bf16(cs[kDNope + tid]);
+
+  // 3. indexer key: thread (slice p, output quad q) accumulates channels
+  //    [72p, 72p+72) of outputs 4q..4q+3 in channel order (one 8-byte W_IK
+  //    load per channel serves the four); the slices are added in order
+  {
+    const int nq = d_idx / 4;
+    const int part = tid / nq, q = tid % nq;
+    if (part < kAppSlices) {
+      const uint2 *wp = reinterpret_cast<const uint2 *>(ap.w_ik + (int64_t)(part * kAppSlice) * d_idx + 4 * q);
+      const float4 *cp = reinterpret_cast<const float4 *>(&cs[part * kAppSlice]);
+      float acc[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 6
+      for (int u4 = 0; u4 < kAppSlice / 4; ++u4) {
+        const float4 c4 = cp[u4];
+        const float cc[4] = {c4.x, c4.y, c4.z, c4.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const uint2 wv = wp[(int64_t)(4 * u4 + j) * nq];
+          acc[0] = fmaf(cc[j], bf16_to_f32(wv.x & 0xFFFFu), acc[0]);
+          acc[1] = fmaf(cc[j], bf16_to_f32(wv.x >> 16), acc[1]);
+          acc[2] = fmaf(cc[j], bf16_to_f32(wv.y & 0xFFFFu), acc[2]);
+          acc[3] = fmaf(cc[j], bf16_to_f32(wv.y >> 16), acc[3]);
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) kpart[part][4 * q + j] = acc[j];
+    }
+  }
+  __syncthreads();
+  if (tid < d_idx) {
+    float s = 0.f;
+#pragma unroll
+    for (int pp = 0; pp < kAppSlices; ++pp) s += kpart[pp][tid];
+    ks[tid] = s;
+  }
+  __syncthreads();
+  if (tid < 64) {
+    // 16 lanes per key block (a DPP row), two channels each; rows past the
+    // key's blocks encode a copy of block 0 and store nothing
+    const int kb = tid >> 4, t = tid & 15;
+    const int kbc = kb < nkb ? kb : 0;
+    uint32_t sb;
+    const uint32_t byte = encode_pair(ks[kbc * 32 + 2 * t], ks[kbc * 32 + 2 * t + 1], sb);
+    if (kb < nkb) {
+      ikey[row * (d_idx / 2) + kb * 16 + t] = (uint8_t)byte;
+      kc[kb * 16 + t] = (uint8_t)byte;
+      if (t == 0) {
+        iscale[row * nkb + kb] = (uint8_t)sb;
+        ksc[kb] = sb;
+      }
+    }
+  }
+  __syncthreads();
+
+  // 4. the new entry's score (one wave; one query)
+  if (tid >= 64) return;
+  const int lane = tid, g = lane >> 4, r = lane & 15;
+  float wv[HT][4];
+#pragma unroll
+  for (int ht = 0; ht < HT; ++ht)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int hh = ht * 16 + g * 4 + i;
+      wv[ht][i] = hh < H_I ? w_idx[(int64_t)b * Q * H_I + hh] : 0.f;
+    }
+  const int r_new = ap.entry & 15, t_new = (ap.entry & 63) >> 4;
+  const bool mine = r == r_new && g < nkb;
+  const v4i kk = mine ? *reinterpret_cast<const v4i *>(&kc[g * 16]) : v4i{0, 0, 0, 0};
+  const int sbu = mine ? (int)ksc[g] : 127;
+  const v8i Bm = {kk[0], kk[1], kk[2], kk[3], 0, 0, 0, 0};
+  float sum = 0.f;
+#pragma unroll
+  for (int ht = 0; ht < HT; ++ht) {
+    const uint8_t *qr = qs + (ht * 16 + r) * 128;
+    const v4i lo = *reinterpret_cast<const v4i *>(qr + 16 * g);
+    const v4i hi = *reinterpret_cast<const v4i *>(qr + 64 + 16 * g);
+    const v8i A = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    v4f acc = {0.f, 0.f, 0.f, 0.f};
+    acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, Bm, acc, 0, 4, 0, 127, 0, sbu);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sum = fmaf(fmaxf(acc[i], 0.f), wv[ht][i], sum);
+  }
+  const float res = reduce_scatter4(t_new == 0 ? sum : 0.f, t_new == 1 ? sum : 0.f, t_new == 2 ? sum : 0.f,
+                                    t_new == 3 ? sum : 0.f);
+  const int nE = min(n_entries[b], N_cap);
+  const int vis = max(0, min(nE, (q_pos[(int64_t)b * Q] + 1) / m));
+  if (lane == 16 * t_new + r_new && ap.entry < vis) scores[(int64_t)b * Q * Ns + ap.entry] = res;
+}
+
+// Grid: B append workgroups first, then B x tiles indexer workgroups.
+template <int HT, bool kGateFull>
+__global__ __launch_bounds__(kIdxThreads) void append_index_kernel(
+    AppendArgs ap, uint8_t *__restrict__ ikey, uint8_t *__restrict__ iscale, const int32_t *__restrict__ n_entries,
+    int N_cap, int d_idx, const uint8_t *__restrict__ q_idx, const float *__restrict__ w_idx, int H_I,
+    const int32_t *__restrict__ q_pos, int Q, float *__restrict__ scores, int B, int tiles) {
+  const int w = blockIdx.x;
+  if (w < B) {
+    append_and_score<HT, kGateFull>(ap, ikey, iscale, n_entries, N_cap, d_idx, q_idx, w_idx, H_I, q_pos, Q, scores,
+                                    N_cap, w);
+    return;
+  }
+  const int t = w - B;
+  index_body<HT, 1, false>(ikey, iscale, n_entries, N_cap, d_idx, ap.m, q_idx, w_idx, H_I, q_pos, Q, nullptr, 0,
+                           scores, N_cap, t % tiles, 0, t / tiles, ap.entry);
+}
+
+template <int HT>
+static void launch_append(const AppendArgs &ap, bool gate_full, const CacheView &c, const uint8_t *q_idx,
+                          const float *w_idx, int H_I, const int32_t *q_pos, float *scores, hipStream_t stream) {
+  const int tiles = (c.N_cap + kIdxWGEntries - 1) / kIdxWGEntries;
+  const unsigned grid = (unsigned)(c.B + c.B * tiles);
+  if (gate_full)
+    append_index_kernel<HT, true><<<grid, kIdxThreads, 0, stream>>>(ap, c.ikey, c.iscale, c.n_entries, c.N_cap,
+                                                                    c.d_idx, q_idx, w_idx, H_I, q_pos, 1, scores,
+                                                                    c.B, tiles);
+  else
+    append_index_kernel<HT, false><<<grid, kIdxThreads, 0, stream>>>(ap, c.ikey, c.iscale, c.n_entries, c.N_cap,
+                                                                     c.d_idx, q_idx, w_idx, H_I, q_pos, 1, scores,
+                                                                     c.B, tiles);
+}
+
+bool append_index_fusable(int m, int64_t T, int Q, int G, const uint16_t *w_ik, int B) {
+  return w_ik && (reinterpret_cast<uintptr_t>(w_ik) & 7) == 0 && m <= kAppMaxM && T == m && Q == 1 &&
+         (G == kD || G == 1) && B > 0;
+}
+
+hipError_t launch_append_index(const uint16_t *x, int64_t x_stride_b, const uint16_t *z, int64_t z_stride_b, int G,
+                               const float *bias, const uint16_t *w_ik, int64_t entry, const CacheView &c,
+                               const uint8_t *q_idx, const float *w_idx, int H_I, const int32_t *q_pos,
+                               float *scores, hipStream_t stream) {
+  AppendArgs ap{x, x_stride_b, z, z_stride_b, bias, w_ik, c.m, (int)entry, c.nope, c.nscale, c.rope};
+  const bool full = G == kD;
+  if (H_I <= 16)
+    launch_append<1>(ap, full, c, q_idx, w_idx, H_I, q_pos, scores, stream);
+  else if (H_I <= 32)
+    launch_append<2>(ap, full, c, q_idx, w_idx, H_I, q_pos, scores, stream);
+  else
+    launch_append<4>(ap, full, c, q_idx, w_idx, H_I, q_pos, scores, stream);
+  return hipGetLastError();
 }
 
 template <int HT, int QB, bool kCand>

@@ -91,6 +91,31 @@ def compress(cache: Cache, x, z, pos_bias, w_ik=None, tok_begin=0):
                              int(tok_begin), int(T), ctypes.byref(cs), _stream()), "csa_compress")
 
 
+def compress_index_scores(cache: Cache, x, z, pos_bias, w_ik, tok_begin, q_idx, w_idx, q_pos, scores=None):
+    """compress() then a full-scan index_scores() (one launch for a one-entry decode append)."""
+    _need(x, torch.bfloat16, "x")
+    _need(z, torch.bfloat16, "z")
+    _need(pos_bias, torch.float32, "pos_bias")
+    _need(q_idx, torch.uint8, "q_idx")
+    _need(w_idx, torch.float32, "w_idx")
+    _need(q_pos, torch.int32, "q_pos")
+    B, T = x.shape[0], x.shape[1]
+    G = z.shape[2]
+    if x.stride(2) != 1 or x.stride(1) != D or z.stride(2) != 1 or z.stride(1) != G:
+        raise ValueError("x and z rows must be contiguous")
+    if w_ik is not None:
+        _need(w_ik, torch.bfloat16, "w_ik")
+    Q, H_I = q_idx.shape[1], q_idx.shape[2]
+    if scores is None:
+        scores = torch.empty(B, Q, cache.N_cap, dtype=torch.float32, device=q_idx.device)
+    cs = cache.struct()
+    check(lib().csa_compress_index_scores(_ptr(x), x.stride(0), _ptr(z), z.stride(0), G, _ptr(pos_bias), _ptr(w_ik),
+                                          int(tok_begin), int(T), ctypes.byref(cs), _ptr(q_idx), _ptr(w_idx), H_I,
+                                          _ptr(q_pos), Q, _ptr(scores), scores.numel() * 4, _stream()),
+          "csa_compress_index_scores")
+    return scores
+
+
 def index_topk(cache: Cache, q_idx, w_idx, q_pos, k, cand=None, want_scores=False, ws=None, out=None):
     """Returns (idx int32 [B][Q][k], scores fp32 [B][Q][k] or None)."""
     _need(q_idx, torch.uint8, "q_idx")

@@ -132,6 +132,20 @@ int csa_index_scores(const csa_cache_t *cache, const uint8_t *q_idx, const float
 int csa_topk(const csa_cache_t *cache, const float *scores, const int32_t *q_pos, int Q, const int32_t *cand,
              int C, int k, int32_t *idx_out, float *score_out, void *ws, size_t ws_bytes, hipStream_t stream);
 
+/* csa_compress followed by a full-scan csa_index_scores (no candidates), the
+ * decode append: the same arguments as those two calls, the same checks and
+ * the same results (the cache bytes written and every score, bit for bit).
+ * When every sequence appends one entry (T == m, m <= 8), there is one query
+ * per sequence (Q == 1) and w_ik is given and 8-byte aligned, both run in
+ * one launch: the new entry is compressed and scored while the older
+ * entries are scored; other shapes run the two calls one after the other.  n_entries must already
+ * count the appended entry for it to be visible to the query (the caller
+ * publishes it before the call). */
+int csa_compress_index_scores(const uint16_t *x, int64_t x_stride_b, const uint16_t *z, int64_t z_stride_b, int G,
+                              const float *pos_bias, const uint16_t *w_ik, int64_t tok_begin, int64_t T,
+                              const csa_cache_t *cache, const uint8_t *q_idx, const float *w_idx, int H_I,
+                              const int32_t *q_pos, int Q, float *scores, size_t scores_bytes, hipStream_t stream);
+
 /* Candidate pool of the hierarchical sparse indexer ([V4.1] "Hierarchical
  * Sparse Indexer" bullet and Fig. 5: the first Full layer ranks blocks of
  * consecutive positions by their largest indexer score and hands the

@@ -106,6 +106,29 @@ def test_batched_decode_128k_fullsize():
     assert worst <= 2e-2, worst
 
 
+def test_batched_decode_fused_append_fullsize():
+    """The benchmark's fused decode append at full size (32 sequences x
+    32,768 entries, the newest 4-token block compressed and every entry
+    scored): cache bytes and all 1,048,576 scores identical to
+    csa_compress followed by csa_index_scores."""
+    w = BATCHED_DECODE
+    planes = synthetic_cache(w, device=DEV)
+    c1 = _cache_from(planes, w, [w.N] * w.B)
+    c2 = _cache_from({k: v.clone() for k, v in planes.items()}, w, [w.N] * w.B)
+    x, z = raw_rows(w, w.T - w.m, w.T, device=DEV)
+    bias, wik = params(w, device=DEV)
+    qs = queries(w, device=DEV)
+    csa.compress(c1, x, z, bias, wik, tok_begin=w.T - w.m)
+    s1 = csa.index_scores(c1, qs["qI"], qs["w"], qs["q_pos"])
+    s2 = csa.compress_index_scores(c2, x, z, bias, wik, w.T - w.m, qs["qI"], qs["w"], qs["q_pos"])
+    torch.cuda.synchronize()
+    for plane in ("nope", "nscale", "rope", "ikey", "iscale"):
+        a, b = getattr(c1, plane), getattr(c2, plane)
+        assert torch.equal(a.view(torch.uint8) if a.dtype != torch.uint8 else a,
+                           b.view(torch.uint8) if b.dtype != torch.uint8 else b), plane
+    assert torch.equal(s1.view(torch.int32), s2.view(torch.int32))
+
+
 def test_batched_decode_compress_fullsize_sampled():
     """The decode-step compressor launch (newest block of 32 sequences) and a
     4,096-token chunk of every sequence, compared entry by entry."""

@@ -337,6 +337,65 @@ def test_reindex_candidates_parity():
         assert set(ib[b, 0][ib[b, 0] >= 0]) <= set(oa_all[b, 0][oa_all[b, 0] >= 0])
 
 
+# ----------------------------------------------------------------------------- fused decode append
+
+FUSED_CASES = [
+    # (name, B, N, m, G, d_idx, H_I, entries appended (T/m), queries per sequence)
+    ("h32-d128", 3, 4096, 4, 576, 128, 32, 1, 1),
+    ("h16-d64-gate1", 3, 2048, 4, 1, 64, 16, 1, 1),
+    ("h64-d128", 2, 2048, 4, 576, 128, 64, 1, 1),
+    ("h20-d128", 2, 1500, 4, 576, 128, 20, 1, 1),
+    ("m8", 2, 1024, 8, 576, 128, 32, 1, 1),
+    ("m1", 2, 3000, 1, 576, 128, 32, 1, 1),
+    ("two-entries-two-launches", 2, 1024, 4, 576, 128, 32, 2, 1),
+    ("two-queries-two-launches", 2, 1024, 4, 576, 128, 32, 1, 2),
+]
+
+
+@pytest.mark.parametrize("name,B,N,m,G,d_idx,H_I,ne,Q", FUSED_CASES, ids=[c[0] for c in FUSED_CASES])
+def test_compress_index_fused_matches_separate(name, B, N, m, G, d_idx, H_I, ne, Q):
+    """csa_compress_index_scores against csa_compress followed by
+    csa_index_scores on a copy of the same cache: every cache byte and every
+    score slot (unwritten ones included) bit for bit.  Sequence 0 sees the
+    appended entries, sequence 1's query stops one raw token short of the
+    last one, and (B > 2) sequence 2 has not published it."""
+    w = Workload("fu", 14, B=B, T=N * m, m=m, d_idx=d_idx, H_I=H_I, k=8, H=16, n_win=0)
+    planes = synthetic_cache(w)
+    n_ent = [N, N, N - ne][:B]
+    c1 = _gpu_cache(planes, B, N, m, d_idx, n_ent)
+    c2 = _gpu_cache(planes, B, N, m, d_idx, n_ent)
+    tok0 = (N - ne) * m
+    x, z = raw_rows(w, tok0, N * m)
+    if G == 1:
+        z = z[:, :, :1].contiguous()
+    x, z = x.to(DEV), z.to(DEV)
+    bias, wik = params(w)
+    bias, wik = bias.to(DEV), wik.to(DEV)
+    qs = queries(w, nq=Q)
+    pos = torch.full((B, Q), N * m - 1, dtype=torch.int32)
+    pos[1, :] = N * m - 2
+    pos = pos.to(DEV)
+    qI, wt = qs["qI"].to(DEV), qs["w"].to(DEV)
+    fill = torch.full((B, Q, N), float("nan"), dtype=torch.float32, device=DEV).view(torch.int32).fill_(0x7FC0ABCD)
+    s1 = fill.clone().view(torch.float32)
+    s2 = fill.clone().view(torch.float32)
+    csa.compress(c1, x, z, bias, wik, tok_begin=tok0)
+    csa.index_scores(c1, qI, wt, pos, scores=s1)
+    csa.compress_index_scores(c2, x, z, bias, wik, tok0, qI, wt, pos, scores=s2)
+    torch.cuda.synchronize()
+    for plane in ("nope", "nscale", "rope", "ikey", "iscale"):
+        a, b2 = getattr(c1, plane), getattr(c2, plane)
+        assert torch.equal(a.view(torch.uint8) if a.dtype != torch.uint8 else a,
+                           b2.view(torch.uint8) if b2.dtype != torch.uint8 else b2), plane
+    np.testing.assert_array_equal(_np(s1.view(torch.int32)), _np(s2.view(torch.int32)))
+    # the appended entry was scored where it is visible, and only there
+    g = _np(s2.view(torch.int32))
+    assert g[0, 0, N - 1] != 0x7FC0ABCD
+    assert g[1, 0, N - 1] == 0x7FC0ABCD
+    if B > 2:
+        assert g[2, 0, N - 1] == 0x7FC0ABCD
+
+
 # ----------------------------------------------------------------------------- hierarchical pool
 
 POOL_CASES = [

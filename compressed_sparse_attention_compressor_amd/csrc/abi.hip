@@ -16,6 +16,7 @@ constexpr int kMaxM = 256;
 constexpr int kMaxK = 1 << 20;
 constexpr int kMaxWin = 1 << 20;
 constexpr int kMaxPoolBlock = 64;
+constexpr int kMaxStackLayers = 256;
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -248,6 +249,13 @@ int csa_index_pool(const csa_cache_t *cache, const float *scores, const int32_t 
   if ((int64_t)n_blocks * block > kMaxK) return CSA_ERR_UNSUPPORTED;
   if (Q == 0 || cache->B == 0) return CSA_OK;
   if (cache->N_cap > 0 && !scores) return CSA_ERR_NULL;
+  {
+    // flattened launch grids: rows x tiles of 256 blocks / pool slots
+    const int64_t rows = (int64_t)cache->B * Q;
+    const int64_t nb = ((int64_t)cache->N_cap + block - 1) / block;
+    const int64_t tiles = ((nb > (int64_t)n_blocks * block ? nb : (int64_t)n_blocks * block) + 255) / 256;
+    if (rows * tiles > INT32_MAX) return CSA_ERR_UNSUPPORTED;
+  }
   const size_t need = csa::pool_workspace_bytes(cache->B, Q, cache->N_cap, block, n_blocks);
   if (!ws) return CSA_ERR_NULL;
   if (ws_bytes < need) return CSA_ERR_WORKSPACE;
@@ -317,6 +325,7 @@ struct StackStep {
 static int stack_plan(const csa2_layer_t *L, int n, const int32_t *q_pos, int Q, StackStep *steps, size_t *ws_need) {
   if (!L || !q_pos) return CSA_ERR_NULL;
   if (n < 1 || Q < 0) return CSA_ERR_SHAPE;
+  if (n > kMaxStackLayers) return CSA_ERR_UNSUPPORTED;
   const csa_cache_t *full = nullptr;
   const int32_t *pool = nullptr;
   int pool_C = 0;
@@ -413,9 +422,9 @@ size_t csa2_stack_workspace_bytes(const csa2_layer_t *layers, int n_layers, int 
 int csa2_layer_stack(const csa2_layer_t *layers, int n_layers, const int32_t *q_pos, int Q, void *ws,
                      size_t ws_bytes, hipStream_t stream) {
   if (!layers) return CSA_ERR_NULL;
-  if (n_layers < 1 || n_layers > 4096) return CSA_ERR_SHAPE;
-  StackStep steps_small[16];
-  StackStep *steps = n_layers <= 16 ? steps_small : new StackStep[n_layers];
+  if (n_layers < 1) return CSA_ERR_SHAPE;
+  if (n_layers > kMaxStackLayers) return CSA_ERR_UNSUPPORTED;
+  StackStep steps[kMaxStackLayers];
   size_t need = 0;
   int st = stack_plan(layers, n_layers, q_pos, Q, steps, &need);
   if (st == CSA_OK && need > 0 && !ws) st = CSA_ERR_NULL;
@@ -439,7 +448,6 @@ int csa2_layer_stack(const csa2_layer_t *layers, int n_layers, const int32_t *q_
       st = csa_sparse_attn(s.cache, l.q, l.H, q_pos, Q, s.sel, s.k, l.swa, l.swa_pos0, l.S, l.n_win,
                            l.softmax_scale, l.out_dtype, l.out, l.lse, rest, s.ws_rest, stream);
   }
-  if (steps != steps_small) delete[] steps;
   return st;
 }
 

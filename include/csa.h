@@ -241,7 +241,8 @@ typedef struct {
   float *lse;                /* fp32 [B][Q][H] or NULL                               */
 } csa2_layer_t;
 
-/*   q_pos  int32 [B][Q] raw positions, shared by every layer
+/*   n_layers  1..256
+ *   q_pos  int32 [B][Q] raw positions, shared by every layer
  *   ws     >= csa2_stack_workspace_bytes(layers, n_layers, Q) bytes, 16-byte
  *          aligned, reused by each layer in turn. */
 int csa2_layer_stack(const csa2_layer_t *layers, int n_layers, const int32_t *q_pos, int Q, void *ws,

@@ -195,3 +195,11 @@ def test_layer_stack_checks(L):
     assert _stack(L, good, wsb=need - 1) == EWS
     assert _stack(L, good, ws=P + 8) == EALIGN
     assert _stack(L, good, ws=None) == ENULL
+    many = [_layer(0, c)] + [_layer(2) for _ in range(256)]          # 257 layers
+    assert _stack(L, many) == EUNSUP
+    assert L.csa2_stack_workspace_bytes(_arr(many), len(many), 1) == 0
+
+
+def test_index_pool_grid_limit(L):
+    # 2^24 query rows x 128 blocks of 256: beyond a 32-bit flattened grid
+    assert _pool(L, _cache(B=1, N=32768), Q=1 << 24, block=1, nb=1) == EUNSUP

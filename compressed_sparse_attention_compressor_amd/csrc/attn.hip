@@ -104,7 +104,9 @@ __device__ __forceinline__ void load_entries(const AttnArgs &a, int b, const int
   const int tid = threadIdx.x;
 #pragma unroll
   for (int u = 0; u < CS::kFp4; ++u) {
-    const int t = tid + u * NT;  // < kFp4Tasks (NT divides it)
+    // clamped: with more threads than MXFP4 blocks in a chunk (1,024) the
+    // surplus threads repeat the last block and store nothing
+    const int t = min(tid + u * NT, kFp4Tasks - 1);
     const int key = t >> 4, blk = t & 15;
     const int64_t row = (int64_t)b * a.N_cap + min(max(src[key], 0), a.N_cap - 1);
     r.v[u] = *reinterpret_cast<const uint4 *>(a.nope + row * kNopeBytes + blk * 16);
@@ -126,6 +128,7 @@ __device__ __forceinline__ void store_entries(uint16_t *K, const int *src, const
 #pragma unroll
   for (int u = 0; u < CS::kFp4; ++u) {
     const int t = tid + u * NT;
+    if (t >= kFp4Tasks) break;
     const int key = t >> 4, blk = t & 15;
     uint4 *dst = reinterpret_cast<uint4 *>(K + key * kKRow + blk * 32);
     if (src[key] >= 0) {

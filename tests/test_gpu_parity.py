@@ -617,6 +617,9 @@ SPARSE_CASES = [
      [250], [[999, 950, 930]], 60, [940]),
     ("no-window", Workload("nw", 14, B=1, T=800, m=4, d_idx=0, H_I=0, k=70, H=64, n_win=0, Q=2), 200, [200],
      [[799, 3]], None, None),
+    # 128 heads: 1,024 threads per workgroup, more than the chunk's 512 MXFP4 blocks
+    ("h128", Workload("h8", 19, B=2, T=2000, m=4, d_idx=0, H_I=0, k=100, H=128, n_win=64, Q=2), 500, [500, 321],
+     [[1999, 700], [1283, 1999]], None, None),
 ]
 
 
@@ -649,6 +652,8 @@ DENSE_CASES = [
      [[8191, 127, 5000], [8191, 126, 3]]),
     ("dense-m4-many-splits", Workload("dm", 16, B=1, T=12000, m=4, d_idx=0, H_I=0, k=0, H=16, n_win=128), 3000,
      [3000], [[11999]]),
+    ("dense-h128", Workload("d8", 20, B=1, T=4096, m=4, d_idx=0, H_I=0, k=0, H=128, n_win=32), 1024, [1000],
+     [[4095]]),
 ]
 
 

@@ -282,10 +282,11 @@ __global__ __launch_bounds__(HG * 128) void attn_kernel(AttnArgs a) {
     publish_slot(s_begin, j0, 0);
   }
 
-  // One chunk of decoded keys in K: logits, online softmax, O += P V.
-  auto compute_chunk = [&](const uint16_t *K, bool kv0, bool kv1) __attribute__((always_inline)) {
-    // S = Q K^T for two tiles of 16 keys (two independent MFMA chains)
-    v4f S0 = {0.f, 0.f, 0.f, 0.f}, S1 = {0.f, 0.f, 0.f, 0.f};
+  // S = Q K^T of one chunk for two tiles of 16 keys (two independent MFMA
+  // chains), over this wave's channels.
+  auto qk_part = [&](const uint16_t *K, v4f &S0, v4f &S1) __attribute__((always_inline)) {
+    S0 = v4f{0.f, 0.f, 0.f, 0.f};
+    S1 = v4f{0.f, 0.f, 0.f, 0.f};
     {
       const uint16_t *k0 = K + r * kKRow + (kDupQK ? 0 : cbase) + 8 * g;
       const uint16_t *k1 = k0 + 16 * kKRow;
@@ -297,6 +298,9 @@ __global__ __launch_bounds__(HG * 128) void attn_kernel(AttnArgs a) {
                                                      0);
       }
     }
+  };
+  // Adds the partner wave's half of the channels (one LDS-only barrier).
+  auto exchange = [&](v4f &S0, v4f &S1) __attribute__((always_inline)) {
     if (!kDupQK) {
       // the partner's half of the channels, added in a fixed order of the
       // halves so that both waves of the pair agree bit for bit
@@ -315,7 +319,11 @@ __global__ __launch_bounds__(HG * 128) void attn_kernel(AttnArgs a) {
         S1[i] = half == 0 ? S1[i] + o1 : o1 + S1[i];
       }
     }
-
+  };
+  // Online softmax of one chunk's logits, then O += P V with the chunk's
+  // rows as V.
+  auto softmax_pv = [&](const uint16_t *K, const v4f &S0, const v4f &S1, bool kv0, bool kv1)
+                        __attribute__((always_inline)) {
     float alpha[4], p0[4], p1[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -385,6 +393,13 @@ __global__ __launch_bounds__(HG * 128) void attn_kernel(AttnArgs a) {
       O[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Pa, Bv, O[j], 0, 0, 0);
       if (kSplitP) O[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Pb, Bv, O[j], 0, 0, 0);
     }
+  };
+  // One chunk of decoded keys in K: logits, online softmax, O += P V.
+  auto compute_chunk = [&](const uint16_t *K, bool kv0, bool kv1) __attribute__((always_inline)) {
+    v4f S0, S1;
+    qk_part(K, S0, S1);
+    exchange(S0, S1);
+    softmax_pv(K, S0, S1, kv0, kv1);
   };
 
   // Chunks of one kind in [c_lo, c_hi): decode the fetched rows into K,

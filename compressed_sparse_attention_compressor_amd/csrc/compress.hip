@@ -105,6 +105,10 @@ __global__ __launch_bounds__(kCompThreads) void compress_kernel(
         }
       }
     } else {
+      // long blocks (HCA): two passes over the rows; unrolled so that eight
+      // rows' loads are in flight at once (a runtime loop would wait for
+      // each load before issuing the next)
+#pragma unroll 8
       for (int i = 0; i < m; ++i) {
         const float bi = bias[i];
         if (kGateFull) {
@@ -119,6 +123,7 @@ __global__ __launch_bounds__(kCompThreads) void compress_kernel(
         }
       }
       if (!kGateFull) mx[1] = mx[2] = mx[3] = mx[0];
+#pragma unroll 8
       for (int i = 0; i < m; ++i) {
         const float bi = bias[i];
         float a[4];

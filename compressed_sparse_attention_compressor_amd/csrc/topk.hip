@@ -1,9 +1,17 @@
 // Per-query top-k of the indexer scores ([V4] "ハイブリッド注意：CSAとHCA",
 // CSA paragraph: the indexer picks the top-k compressed blocks of each
-// query; [V4.1] "推論カーネル" names a dedicated TopK kernel).
+// query; [V4.1] "推論カーネル" names a dedicated TopK kernel).  All paths
+// select exactly, on order-preserving uint32 keys, ties to the lower entry;
+// topk_plan picks one per launch shape:
+//   * rows of at most 32,768 scores (and candidate lists): one 512-thread
+//     workgroup per row with the keys in registers (topk_select.hpp);
+//   * rows with few siblings (B*Q < 256) longer than 4,096: slices whose own
+//     top-k candidates a second register-resident launch reduces;
+//   * few rows (B*Q < 256) of at least 65,536 scores: a radix selection
+//     spread over many workgroups (launch_radix, further below);
+//   * many rows longer than 32,768: the tiled LDS radix select below.
 //
-// Exact radix select on order-preserving uint32 keys, one 1024-thread
-// workgroup per query:
+// Tiled LDS radix select, one 1024-thread workgroup per query:
 //   * the scores of a tile (up to kTile of them) sit in LDS as keys, each
 //     thread owning a contiguous run, padded one word per 32 so that the
 //     strided runs do not collide on LDS banks;
@@ -13,8 +21,7 @@
 //   * a last pass keeps every key > T plus the first (by entry index)
 //     elements equal to T, and writes them in ascending order through two
 //     block-wide prefix sums.
-// Rows longer than kTile are processed tile by tile in every pass.  Rows of
-// at most 32,768 scores take the register-resident variant further below.
+// Rows longer than kTile are processed tile by tile in every pass.
 #include "csa_device.hpp"
 #include "csa_internal.hpp"
 #include "topk_select.hpp"

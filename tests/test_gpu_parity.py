@@ -481,6 +481,88 @@ def test_hier_pool_reindex_parity():
         check_topk(g_b[b, 0], ob, jb, sb, what=f"reindex b={b}")
 
 
+def test_hier_pool_many_queries():
+    """The pool and a Reindex layer over it for 70 causal query rows per
+    sequence (the prefill indexer, a block top-k over many rows, candidate
+    rescoring of many rows), m = 4, ragged entry counts."""
+    w = Workload("hq", 21, B=2, T=8192, m=4, d_idx=128, H_I=32, k=16, H=16, n_win=0, k_b=24, Q=70)
+    N, block, nb = w.N, 8, 6
+    planes = synthetic_cache(w)
+    n_ent = [N, 1500]
+    cache = _gpu_cache(planes, w.B, N, w.m, w.d_idx, n_ent)
+    rng = np.random.default_rng(21)
+    pos = np.sort(rng.integers(0, w.T, (w.B, w.Q)).astype(np.int32), axis=1)
+    pos[:, 0] = [2, 0]                               # no visible entry
+    pos[:, 1] = [3, 37]                              # one, and a partial block
+    qa = queries(w)
+    qb = queries(w, second=True)
+    pos_d = torch.from_numpy(pos).to(DEV)
+    scores = csa.index_scores(cache, qa["qI"].to(DEV), qa["w"].to(DEV), pos_d)
+    pool = csa.index_pool(cache, scores, pos_d, block, nb)
+    ib, _ = csa.index_topk(cache, qb["qI"].to(DEV), qb["w"].to(DEV), pos_d, w.k_b, cand=pool)
+    g_s, g_p, g_b = _np(scores), _np(pool), _np(ib)
+    ik, isc = planes["ikey"].numpy(), planes["iscale"].numpy()
+    for b in range(w.B):
+        for t in range(w.Q):
+            p = int(pos[b, t])
+            V = O.visible_count(p, w.m, n_ent[b])
+            ref, _ = O.block_pool(g_s[b, t, :V].astype(np.float64), V, block, nb)
+            np.testing.assert_array_equal(g_p[b, t], ref, err_msg=f"pool b={b} t={t} p={p}")
+            ob, _, jb, sb = O.index_topk(ik[b], isc[b], qb["qI"][b, t].numpy(), qb["w"][b, t].numpy(), p, w.m,
+                                         n_ent[b], w.k_b, cand=g_p[b, t])
+            check_topk(g_b[b, t], ob, jb, sb, what=f"reindex b={b} t={t}")
+
+
+def test_layer_stack_many_queries():
+    """A Full (pool) / Reindex / Reuse stack for 5 query rows per sequence at
+    different positions (one with nothing visible), fp32 output."""
+    import dataclasses
+    w = Workload("sq", 22, B=2, T=4096, m=4, d_idx=64, H_I=16, k=24, H=32, n_win=32, Q=5)
+    N = w.N
+    planes = synthetic_cache(w)
+    ents = [N, 700]
+    cache = _gpu_cache(planes, w.B, N, w.m, w.d_idx, ents)
+    pos = np.array([[4095, 2, 1000, 2999, 63], [4095, 3000, 11, 512, 2799]], np.int32)
+    pos_d = torch.from_numpy(pos).to(DEV)
+    swa, _ = raw_rows(w, 0, w.T)
+    s0 = torch.zeros(w.B, dtype=torch.int32, device=DEV)
+    spec = [dict(mode=csa.CSA2_FULL, k=24, pool_block=4, pool_blocks=10), dict(mode=csa.CSA2_REINDEX, k=12),
+            dict(mode=csa.CSA2_REUSE)]
+    layers, qs = [], []
+    for i, sp in enumerate(spec):
+        q = queries(dataclasses.replace(w, cfg=w.cfg + 100 * (i + 1)))
+        qs.append(q)
+        L = dict(mode=sp["mode"], q=q["q"].to(DEV), swa=swa.to(DEV), swa_pos0=s0, n_win=w.n_win,
+                 scale=w.softmax_scale, out_dtype=torch.float32)
+        if sp["mode"] != csa.CSA2_REUSE:
+            L.update(qI=q["qI"].to(DEV), w=q["w"].to(DEV), k=sp["k"])
+        if sp["mode"] == csa.CSA2_FULL:
+            L.update(cache=cache, pool_block=sp["pool_block"], pool_blocks=sp["pool_blocks"])
+        layers.append(L)
+    res = csa.layer_stack(layers, pos_d)
+    torch.cuda.synchronize()
+    ik, isc = planes["ikey"].numpy(), planes["iscale"].numpy()
+    sw = as_u16(swa)
+    for b in range(w.B):
+        for t in range(w.Q):
+            p = int(pos[b, t])
+            g_a = _np(res[0]["idx"])[b, t]
+            oa, _, js, sc = O.index_topk(ik[b], isc[b], qs[0]["qI"][b, t].numpy(), qs[0]["w"][b, t].numpy(), p, w.m,
+                                         ents[b], 24)
+            check_topk(g_a, oa, js, sc, what=f"full b={b} t={t}")
+            g_pool = _np(res[0]["pool"])[b, t]
+            g_b = _np(res[1]["idx"])[b, t]
+            ob, _, jb, sb = O.index_topk(ik[b], isc[b], qs[1]["qI"][b, t].numpy(), qs[1]["w"][b, t].numpy(), p, w.m,
+                                         ents[b], 12, cand=g_pool)
+            check_topk(g_b, ob, jb, sb, what=f"reindex b={b} t={t}")
+            for i, sel in ((0, g_a), (1, g_b), (2, g_b)):
+                o, _ = O.sparse_attention(as_u16(qs[i]["q"][b, t]), planes["nope"][b].numpy(),
+                                          planes["nscale"][b].numpy(), as_u16(planes["rope"][b]), sel, sw[b], 0, p,
+                                          w.n_win, w.softmax_scale, w.m, ents[b])
+                g = _np(res[i]["out"])[b, t].astype(np.float64)
+                assert row_rel_err(g, o).max() <= TOL[torch.float32], f"layer {i} b={b} t={t}"
+
+
 def test_layer_stack_parity():
     """An 8-layer CSA2 stack through csa2_layer_stack ([V4.1] Fig. 4 modes,
     Fig. 5 pool): Full with a pool, Reuse, Reindex over the pool, Reuse, a

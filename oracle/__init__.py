@@ -33,7 +33,10 @@ from .formats import (  # noqa: F401
     e8m0_to_f64,
     mxfp4_encode,
     mxfp4_decode,
+    mxfp8_encode,
+    mxfp8_decode,
     E2M1_VALUES,
+    E4M3_VALUES,
 )
 from .csa import (  # noqa: F401
     visible_count,
@@ -50,6 +53,8 @@ from .csa import (  # noqa: F401
     block_pool,
     hier_pair,
     csa2_stack,
+    swa_encode,
+    swa_decode,
     FULL,
     REINDEX,
     REUSE,

@@ -41,6 +41,8 @@ from .formats import (
     f32_to_bf16,
     mxfp4_decode,
     mxfp4_encode,
+    mxfp8_decode,
+    mxfp8_encode,
 )
 
 
@@ -221,15 +223,33 @@ def attention(q_u16, keys: np.ndarray, scale) -> tuple[np.ndarray, np.ndarray]:
     return o, lse
 
 
-def _window_rows(swa_u16, swa_pos0: int, p: int, n_win: int) -> np.ndarray:
-    """Raw rows of the sliding window of a query at p that the buffer holds."""
+def _window_rows(swa, swa_pos0: int, p: int, n_win: int) -> np.ndarray:
+    """Raw rows of the sliding window of a query at p that the buffer holds;
+    ``swa`` holds bf16 bit patterns (uint16) or decoded float64 rows."""
+    swa = np.asarray(swa)
     if n_win <= 0 or p < 0:
-        return np.zeros((0, np.asarray(swa_u16).shape[-1]))
+        return np.zeros((0, swa.shape[-1]))
     lo = max(0, p - n_win + 1, int(swa_pos0))
-    hi = min(p, int(swa_pos0) + np.asarray(swa_u16).shape[0] - 1)
+    hi = min(p, int(swa_pos0) + swa.shape[0] - 1)
     if hi < lo:
-        return np.zeros((0, np.asarray(swa_u16).shape[-1]))
-    return bf16_to_f64(np.asarray(swa_u16)[lo - swa_pos0: hi - swa_pos0 + 1])
+        return np.zeros((0, swa.shape[-1]))
+    rows = swa[lo - swa_pos0: hi - swa_pos0 + 1]
+    return rows.astype(np.float64) if rows.dtype == np.float64 else bf16_to_f64(rows)
+
+
+def swa_encode(x_u16, d_nope: int = 512) -> dict:
+    """bf16 window rows [S][D] -> FP8 window planes ([V4.1] "FP4 主 KV キャッシュ":
+    the sliding-window KV stays FP8): ``codes`` uint8 [S][d_nope] (MXFP8 of the
+    content channels), ``scales`` uint8 [S][d_nope/32], ``rope`` uint16
+    [S][D - d_nope] (the positional channels' bf16 bits, unchanged)."""
+    x = np.asarray(x_u16)
+    codes, scales = mxfp8_encode(bf16_to_f64(x[:, :d_nope]))
+    return dict(codes=codes, scales=scales, rope=x[:, d_nope:].copy())
+
+
+def swa_decode(codes, scales, rope) -> np.ndarray:
+    """FP8 window planes -> float64 rows [S][D]."""
+    return np.concatenate([mxfp8_decode(codes, scales), bf16_to_f64(rope)], axis=-1)
 
 
 def sparse_attention(q_u16, nope, nscale, rope, idx, swa_u16, swa_pos0, p, n_win, scale,

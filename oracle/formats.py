@@ -8,6 +8,12 @@ E8M0 scale byte, and each element is an E2M1 code.  The positional (RoPE)
 channels stay bf16, as both [V4] (section "ハイブリッド注意：CSAとHCA",
 storage paragraph) and [V4.1] state.  Indexer queries are OCP E4M3.
 
+The sliding-window rows, which [V4.1] keeps in FP8 because they are
+sensitive to quantisation, take the same OCP MX form with E4M3 elements
+(MXFP8) for their 512 content channels and bf16 for the positional ones;
+the pages give no FP8 scale format, and MX keeps the window in the family
+of the main cache.
+
 Encoding rule for a block (OCP MX, scale computed from the block maximum):
   X = floor(log2(max |v|)) - 2, clamped to [-127, 127], scale byte X + 127;
   each v / 2^X is rounded to the nearest E2M1 value, ties to the code with an
@@ -98,6 +104,62 @@ def mxfp4_encode(v) -> tuple[np.ndarray, np.ndarray]:
     packed = (code[..., 0::2] | (code[..., 1::2] << 4)).astype(np.uint8)
     packed = packed.reshape(v.shape[:-1] + (16 * nb,))
     return packed, (x + 127).astype(np.uint8)
+
+
+# Non-negative finite E4M3 magnitudes of codes 0..126 (code 127 is NaN).
+E4M3_VALUES = None  # filled below
+
+
+def _e4m3_table() -> np.ndarray:
+    return e4m3_to_f64(np.arange(127, dtype=np.uint8))
+
+
+E4M3_VALUES = _e4m3_table()
+
+
+def _e4m3_round(mag: np.ndarray) -> np.ndarray:
+    """Magnitude (>= 0, already divided by the block scale) -> E4M3 code
+    0..126: nearest value, ties to the even code (the even mantissa bit),
+    saturating at 448 (code 126)."""
+    mag = np.asarray(mag, dtype=np.float64)
+    hi = np.clip(np.searchsorted(E4M3_VALUES, mag, side="left"), 0, 126)
+    lo = np.clip(hi - 1, 0, 126)
+    dlo = np.abs(mag - E4M3_VALUES[lo])
+    dhi = np.abs(E4M3_VALUES[hi] - mag)
+    code = np.where(dlo < dhi, lo, np.where(dhi < dlo, hi, np.where(lo % 2 == 0, lo, hi)))
+    return np.where(mag >= E4M3_VALUES[126], 126, code).astype(np.int64)
+
+
+def mxfp8_encode(v) -> tuple[np.ndarray, np.ndarray]:
+    """Values [..., 32*nb] -> (E4M3 codes uint8 [..., 32*nb], scale bytes uint8 [..., nb]).
+
+    OCP MX with E4M3 elements (the largest E4M3 exponent is 8): per block of
+    32 channels X = floor(log2(max |v|)) - 8, clamped to [-127, 127], scale
+    byte X + 127 (0 for an all-zero block); each v / 2^X is rounded to the
+    nearest E4M3 value, ties to even, saturated at 448; the sign bit is set
+    for negative values (also when the magnitude rounds to 0).
+    """
+    v = np.asarray(v, dtype=np.float64)
+    if v.shape[-1] % 32:
+        raise ValueError("MXFP8 blocks are 32 channels")
+    nb = v.shape[-1] // 32
+    blk = v.reshape(v.shape[:-1] + (nb, 32))
+    amax = np.max(np.abs(blk), axis=-1)
+    _, ex = np.frexp(amax)
+    x = np.where(amax > 0, ex.astype(np.int64) - 1 - 8, -127)
+    x = np.clip(x, -127, 127)
+    scaled = blk / np.exp2(x.astype(np.float64))[..., None]
+    code = _e4m3_round(np.abs(scaled)) | np.where(scaled < 0, 0x80, 0)
+    return code.astype(np.uint8).reshape(v.shape), (x + 127).astype(np.uint8)
+
+
+def mxfp8_decode(codes, scales) -> np.ndarray:
+    """(E4M3 codes [..., 32*nb], scale bytes [..., nb]) -> float64 [..., 32*nb]."""
+    codes = np.asarray(codes, dtype=np.uint8)
+    scales = np.asarray(scales, dtype=np.uint8)
+    nb = scales.shape[-1]
+    vals = e4m3_to_f64(codes).reshape(codes.shape[:-1] + (nb, 32))
+    return (vals * e8m0_to_f64(scales)[..., None]).reshape(codes.shape)
 
 
 def mxfp4_decode(packed, scales) -> np.ndarray:

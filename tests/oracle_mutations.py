@@ -38,6 +38,10 @@ muts = [
  ("csa.py", "            pool = None\n            if L.get", "            if L.get"),
  ("csa.py", "            full = L[\"cache\"]\n", "            full = full if full is not None else L[\"cache\"]\n"),
  ("csa.py", "src = CAND_POOL if pool is not None else CAND_SELECTION", "src = CAND_SELECTION"),
+ ("formats.py", "x = np.where(amax > 0, ex.astype(np.int64) - 1 - 8, -127)", "x = np.where(amax > 0, ex.astype(np.int64) - 1 - 7, -127)"),
+ ("formats.py", "np.where(lo % 2 == 0, lo, hi)", "np.where(lo % 2 == 1, lo, hi)"),
+ ("formats.py", "code = _e4m3_round(np.abs(scaled)) | np.where(scaled < 0, 0x80, 0)", "code = _e4m3_round(np.abs(scaled)) | np.where(scaled < -2.0 ** -9, 0x80, 0)"),
+ ("csa.py", "return dict(codes=codes, scales=scales, rope=x[:, d_nope:].copy())", "return dict(codes=codes, scales=scales, rope=x[:, d_nope - 1:-1].copy())"),
 ]
 missed = 0
 root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))

@@ -26,6 +26,9 @@ from .ops import (  # noqa: F401
     CAND_POOL,
     topk,
     sparse_attn,
+    sparse_attn_w8,
+    hca_dense_attn_w8,
+    swa_encode,
     workspace_bytes,
     WS_DENSE_ATTN,
     WS_INDEX_POOL,

@@ -264,10 +264,18 @@ int csa_index_pool(const csa_cache_t *cache, const float *scores, const int32_t 
       csa::launch_index_pool(view_of(cache), scores, q_pos, Q, block, n_blocks, pool_out, ws, stream));
 }
 
-int csa_sparse_attn(const csa_cache_t *cache, const uint16_t *q, int H, const int32_t *q_pos, int Q,
-                    const int32_t *idx, int k, const uint16_t *swa, const int32_t *swa_pos0, int S, int n_win,
-                    float softmax_scale, int out_dtype, void *out, float *lse, void *ws, size_t ws_bytes,
-                    hipStream_t stream) {
+// The window rows of an attention call: bf16 rows (swa) or FP8 planes (w8).
+static int check_window8(const uint8_t *codes, const uint8_t *scales, const uint16_t *rope, int n_win) {
+  if (n_win <= 0) return CSA_OK;
+  if (!codes || !scales || !rope) return CSA_ERR_NULL;
+  if (!aligned16(codes) || !aligned16(rope)) return CSA_ERR_ALIGN;
+  return CSA_OK;
+}
+
+static int sparse_attn_impl(const csa_cache_t *cache, const uint16_t *q, int H, const int32_t *q_pos, int Q,
+                            const int32_t *idx, int k, const uint16_t *swa, const csa::SwaPlanes *w8,
+                            const int32_t *swa_pos0, int S, int n_win, float softmax_scale, int out_dtype, void *out,
+                            float *lse, void *ws, size_t ws_bytes, hipStream_t stream) {
   int st = check_attn_common(cache, q, H, q_pos, Q, swa, swa_pos0, S, n_win, softmax_scale, out_dtype, out);
   if (st) return st;
   if (k < 0) return CSA_ERR_SHAPE;
@@ -279,13 +287,14 @@ int csa_sparse_attn(const csa_cache_t *cache, const uint16_t *q, int H, const in
   if (ws_bytes < need) return CSA_ERR_WORKSPACE;
   if (need > 0 && !aligned16(ws)) return CSA_ERR_ALIGN;
   const csa::CacheView v = view_of(cache);
-  return status_of(csa::launch_attention(v, q, H, q_pos, Q, idx, k, false, swa, swa_pos0, S, n_win, softmax_scale,
-                                         out_dtype == CSA_OUT_BF16, out, lse, ws, stream));
+  return status_of(csa::launch_attention(v, q, H, q_pos, Q, idx, k, false, swa, w8, swa_pos0, S, n_win,
+                                         softmax_scale, out_dtype == CSA_OUT_BF16, out, lse, ws, stream));
 }
 
-int hca_dense_attn(const csa_cache_t *cache, const uint16_t *q, int H, const int32_t *q_pos, int Q,
-                   const uint16_t *swa, const int32_t *swa_pos0, int S, int n_win, float softmax_scale,
-                   int out_dtype, void *out, float *lse, void *ws, size_t ws_bytes, hipStream_t stream) {
+static int dense_attn_impl(const csa_cache_t *cache, const uint16_t *q, int H, const int32_t *q_pos, int Q,
+                           const uint16_t *swa, const csa::SwaPlanes *w8, const int32_t *swa_pos0, int S, int n_win,
+                           float softmax_scale, int out_dtype, void *out, float *lse, void *ws, size_t ws_bytes,
+                           hipStream_t stream) {
   int st = check_attn_common(cache, q, H, q_pos, Q, swa, swa_pos0, S, n_win, softmax_scale, out_dtype, out);
   if (st) return st;
   if (Q == 0 || cache->B == 0) return CSA_OK;
@@ -294,8 +303,57 @@ int hca_dense_attn(const csa_cache_t *cache, const uint16_t *q, int H, const int
   if (ws_bytes < need) return CSA_ERR_WORKSPACE;
   if (need > 0 && !aligned16(ws)) return CSA_ERR_ALIGN;
   const csa::CacheView v = view_of(cache);
-  return status_of(csa::launch_attention(v, q, H, q_pos, Q, nullptr, 0, true, swa, swa_pos0, S, n_win, softmax_scale,
-                                         out_dtype == CSA_OUT_BF16, out, lse, ws, stream));
+  return status_of(csa::launch_attention(v, q, H, q_pos, Q, nullptr, 0, true, swa, w8, swa_pos0, S, n_win,
+                                         softmax_scale, out_dtype == CSA_OUT_BF16, out, lse, ws, stream));
+}
+
+int csa_sparse_attn(const csa_cache_t *cache, const uint16_t *q, int H, const int32_t *q_pos, int Q,
+                    const int32_t *idx, int k, const uint16_t *swa, const int32_t *swa_pos0, int S, int n_win,
+                    float softmax_scale, int out_dtype, void *out, float *lse, void *ws, size_t ws_bytes,
+                    hipStream_t stream) {
+  return sparse_attn_impl(cache, q, H, q_pos, Q, idx, k, swa, nullptr, swa_pos0, S, n_win, softmax_scale, out_dtype,
+                          out, lse, ws, ws_bytes, stream);
+}
+
+int hca_dense_attn(const csa_cache_t *cache, const uint16_t *q, int H, const int32_t *q_pos, int Q,
+                   const uint16_t *swa, const int32_t *swa_pos0, int S, int n_win, float softmax_scale,
+                   int out_dtype, void *out, float *lse, void *ws, size_t ws_bytes, hipStream_t stream) {
+  return dense_attn_impl(cache, q, H, q_pos, Q, swa, nullptr, swa_pos0, S, n_win, softmax_scale, out_dtype, out, lse,
+                         ws, ws_bytes, stream);
+}
+
+int csa_sparse_attn_w8(const csa_cache_t *cache, const uint16_t *q, int H, const int32_t *q_pos, int Q,
+                       const int32_t *idx, int k, const uint8_t *swa_codes, const uint8_t *swa_scales,
+                       const uint16_t *swa_rope, const int32_t *swa_pos0, int S, int n_win, float softmax_scale,
+                       int out_dtype, void *out, float *lse, void *ws, size_t ws_bytes, hipStream_t stream) {
+  int st = check_window8(swa_codes, swa_scales, swa_rope, n_win);
+  if (st) return st;
+  const csa::SwaPlanes w8{swa_codes, swa_scales, swa_rope};
+  // the rope plane stands in for the bf16 rows in the shared checks
+  return sparse_attn_impl(cache, q, H, q_pos, Q, idx, k, swa_rope, &w8, swa_pos0, S, n_win, softmax_scale, out_dtype,
+                          out, lse, ws, ws_bytes, stream);
+}
+
+int hca_dense_attn_w8(const csa_cache_t *cache, const uint16_t *q, int H, const int32_t *q_pos, int Q,
+                      const uint8_t *swa_codes, const uint8_t *swa_scales, const uint16_t *swa_rope,
+                      const int32_t *swa_pos0, int S, int n_win, float softmax_scale, int out_dtype, void *out,
+                      float *lse, void *ws, size_t ws_bytes, hipStream_t stream) {
+  int st = check_window8(swa_codes, swa_scales, swa_rope, n_win);
+  if (st) return st;
+  const csa::SwaPlanes w8{swa_codes, swa_scales, swa_rope};
+  return dense_attn_impl(cache, q, H, q_pos, Q, swa_rope, &w8, swa_pos0, S, n_win, softmax_scale, out_dtype, out,
+                         lse, ws, ws_bytes, stream);
+}
+
+int csa_swa_encode(const uint16_t *x, int64_t x_stride_b, int B, int S, uint8_t *codes, uint8_t *scales,
+                   uint16_t *rope, hipStream_t stream) {
+  if (B < 0 || S < 0) return CSA_ERR_SHAPE;
+  if (B == 0 || S == 0) return CSA_OK;
+  if (!x || !codes || !scales || !rope) return CSA_ERR_NULL;
+  if (B > 1 && x_stride_b < (int64_t)S * csa::kD) return CSA_ERR_SHAPE;
+  if (!aligned16(x) || !aligned16(codes) || !aligned16(rope) || (x_stride_b % 8)) return CSA_ERR_ALIGN;
+  if ((int64_t)B * S > (int64_t)INT32_MAX * 16) return CSA_ERR_UNSUPPORTED;
+  return status_of(csa::launch_swa_encode(x, x_stride_b, B, S, codes, scales, rope, stream));
 }
 
 // ---------------------------------------------------------------------------

@@ -66,6 +66,9 @@ struct AttnArgs {
   const int32_t *idx;
   int k;
   const uint16_t *swa;
+  const uint8_t *swa_codes;    // FP8 window rows (with kW8): MXFP8 codes [B][S][512],
+  const uint8_t *swa_scales;   // their E8M0 scales [B][S][16],
+  const uint16_t *swa_rope;    // and the bf16 positional channels [B][S][64]
   const int32_t *swa_pos0;
   int S, n_win;
   float scale_log2;
@@ -84,10 +87,13 @@ struct ChunkShare {
   static constexpr int kRope = (kRopeTasks + NT - 1) / NT;
   static constexpr int kEnt = kFp4 + kRope;
   static constexpr int kWin = (kWinTasks + NT - 1) / NT;
+  // FP8 window rows: 32-byte MXFP8 blocks (two pieces) plus rope pieces
+  static constexpr int kW8 = 2 * kFp4 + kRope;
   // hold a whole chunk in registers (and fetch it ahead) when it is small
-  static constexpr bool kAhead = kEnt <= 9 && kWin <= 9;
+  static constexpr bool kAhead = kEnt <= 9 && kWin <= 9 && kW8 <= 9;
   static constexpr int kWinBatch = kAhead ? kWin : 9;
-  static constexpr int kRaw = kEnt > kWinBatch ? kEnt : kWinBatch;
+  static constexpr int kRaw0 = kEnt > kWinBatch ? kEnt : kWinBatch;
+  static constexpr int kRaw = kRaw0 > kW8 ? kRaw0 : kW8;
 };
 
 template <int NT>
@@ -170,6 +176,77 @@ __device__ __forceinline__ void store_entries(uint16_t *K, const int *src, const
   }
 }
 
+// FP8 window rows: per row 16 MXFP8 blocks (32 code bytes + one E8M0
+// scale) and 8 rope pieces, laid out as the MXFP4 tasks of an entry chunk.
+template <int NT>
+__device__ __forceinline__ void load_win8(const AttnArgs &a, int b, const int *src, RawChunk<NT> &r) {
+  using CS = ChunkShare<NT>;
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int u = 0; u < CS::kFp4; ++u) {
+    const int t = min(tid + u * NT, kFp4Tasks - 1);
+    const int key = t >> 4, blk = t & 15;
+    const int64_t row = (int64_t)b * a.S + min(max(src[key], 0), a.S - 1);
+    const uint4 *cp = reinterpret_cast<const uint4 *>(a.swa_codes + row * kDNope + blk * 32);
+    r.v[2 * u] = cp[0];
+    r.v[2 * u + 1] = cp[1];
+    r.s[u] = a.swa_scales[row * kNopeScales + blk];
+  }
+#pragma unroll
+  for (int u = 0; u < CS::kRope; ++u) {
+    const int t = min(tid + u * NT, kRopeTasks - 1);
+    const int key = t >> 3, part = t & 7;
+    const int64_t row = (int64_t)b * a.S + min(max(src[key], 0), a.S - 1);
+    r.v[2 * CS::kFp4 + u] = *reinterpret_cast<const uint4 *>(a.swa_rope + row * kDRope + part * 8);
+  }
+}
+
+template <int NT>
+__device__ __forceinline__ void store_win8(uint16_t *K, const int *src, const RawChunk<NT> &r) {
+  using CS = ChunkShare<NT>;
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int u = 0; u < CS::kFp4; ++u) {
+    const int t = tid + u * NT;
+    if (t >= kFp4Tasks) break;
+    const int key = t >> 4, blk = t & 15;
+    uint4 *dst = reinterpret_cast<uint4 *>(K + key * kKRow + blk * 32);
+    if (src[key] >= 0) {
+      // E4M3 x 2^(s-127) -> bf16 (hardware conversion, two codes per call);
+      // exact for the rows the encoder writes
+      const float sc = e8m0_to_f32(r.s[u]);
+      const uint4 c0 = r.v[2 * u], c1 = r.v[2 * u + 1];
+#define CSA_CVT8(w, hi) __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, sc, hi))
+      // quarter i of the 32 decoded channels = codes 8i..8i+7 = words 2i, 2i+1,
+      // stored in the lane-dependent order of the MXFP4 path
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int qi = (i + blk + (blk >> 2)) & 3;
+        const uint32_t w0 = qi == 0 ? c0.x : (qi == 1 ? c0.z : (qi == 2 ? c1.x : c1.z));
+        const uint32_t w1 = qi == 0 ? c0.y : (qi == 1 ? c0.w : (qi == 2 ? c1.y : c1.w));
+        dst[qi] = uint4{CSA_CVT8(w0, false), CSA_CVT8(w0, true), CSA_CVT8(w1, false), CSA_CVT8(w1, true)};
+      }
+#undef CSA_CVT8
+    } else {
+      const uint4 z = {0u, 0u, 0u, 0u};
+      dst[0] = z;
+      dst[1] = z;
+      dst[2] = z;
+      dst[3] = z;
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < CS::kRope; ++u) {
+    const int t = tid + u * NT;
+    if (t < kRopeTasks) {
+      const int key = t >> 3, part = t & 7;
+      uint4 v = r.v[2 * CS::kFp4 + u];
+      if (src[key] < 0) v = uint4{0u, 0u, 0u, 0u};
+      *reinterpret_cast<uint4 *>(K + key * kKRow + kDNope + part * 8) = v;
+    }
+  }
+}
+
 // Window rows: `nb` 16-byte pieces per thread starting at task t0.
 template <int NT, int nb>
 __device__ __forceinline__ void load_window(const AttnArgs &a, int b, const int *src, int t0, RawChunk<NT> &r) {
@@ -198,7 +275,7 @@ __device__ __forceinline__ void store_window(uint16_t *K, const int *src, int t0
   }
 }
 
-template <int HG, bool kSplitP, bool kDense, bool kDupQK>
+template <int HG, bool kSplitP, bool kDense, bool kDupQK, bool kW8>
 __global__ __launch_bounds__(HG * 128) void attn_kernel(AttnArgs a) {
   constexpr int NT = HG * 128;
   constexpr int kQSteps = kDupQK ? kKSteps : kKSteps / 2;  // channel steps of this wave's Q K^T
@@ -412,35 +489,40 @@ __global__ __launch_bounds__(HG * 128) void attn_kernel(AttnArgs a) {
   int ci = 0;
   auto run_chunks = [&](auto win_tag, int c_lo, int c_hi) __attribute__((always_inline)) {
     constexpr bool kWin = decltype(win_tag)::value;
+    constexpr bool kWin16 = kWin && !kW8;   // bf16 window rows
     RawChunk<NT> raw;
+    // whole-chunk loads and stores of entry chunks and FP8 window chunks
+    auto ld = [&](int sb) __attribute__((always_inline)) {
+      if (kWin16) load_window<NT, CS::kWinBatch>(a, b, src_s[sb], 0, raw);
+      else if (kWin) load_win8<NT>(a, b, src_s[sb], raw);
+      else load_entries<NT>(a, b, src_s[sb], raw);
+    };
+    auto st = [&](uint16_t *K, int sb) __attribute__((always_inline)) {
+      if (kWin16) store_window<NT, CS::kWinBatch>(K, src_s[sb], 0, raw);
+      else if (kWin) store_win8<NT>(K, src_s[sb], raw);
+      else store_entries<NT>(K, src_s[sb], raw);
+    };
     lds_barrier();
-    if (CS::kAhead) {
-      if (kWin) load_window<NT, CS::kWinBatch>(a, b, src_s[ci % 3], 0, raw);
-      else load_entries<NT>(a, b, src_s[ci % 3], raw);
-    }
+    if (CS::kAhead) ld(ci % 3);
     for (int c0 = c_lo; c0 < c_hi; c0 += kKC, ++ci) {
       uint16_t *K = Kl[ci & 1];
       const int sb = ci % 3, sn = (ci + 1) % 3;
       const int jn = kWin ? -1 : fetch_slot(c0 + kKC);
       if (CS::kAhead) {
-        if (kWin) store_window<NT, CS::kWinBatch>(K, src_s[sb], 0, raw);
-        else store_entries<NT>(K, src_s[sb], raw);
-      } else if (kWin) {
+        st(K, sb);
+      } else if (kWin16) {
         for (int t0 = 0; t0 < kWinTasks; t0 += CS::kWinBatch * NT) {
           load_window<NT, CS::kWinBatch>(a, b, src_s[sb], t0, raw);
           store_window<NT, CS::kWinBatch>(K, src_s[sb], t0, raw);
         }
       } else {
-        load_entries<NT>(a, b, src_s[sb], raw);
-        store_entries<NT>(K, src_s[sb], raw);
+        ld(sb);
+        st(K, sb);
       }
       publish_slot(c0 + kKC, jn, sn);
       lds_barrier();
       const bool kv0 = src_s[sb][r] >= 0, kv1 = src_s[sb][16 + r] >= 0;
-      if (CS::kAhead) {
-        if (kWin) load_window<NT, CS::kWinBatch>(a, b, src_s[sn], 0, raw);
-        else load_entries<NT>(a, b, src_s[sn], raw);
-      }
+      if (CS::kAhead) ld(sn);
       compute_chunk(K, kv0, kv1);
     }
   };
@@ -599,28 +681,32 @@ size_t attn_workspace_bytes(int B, int Q, int H, int n_main, int n_win) {
 #define CSA_ATTN_DUP_QK 0
 #endif
 template <int HG, bool kSplitP>
-static void launch_hg(const AttnArgs &a, bool dense, dim3 grid, hipStream_t stream) {
+static void launch_hg(const AttnArgs &a, bool dense, bool w8, dim3 grid, hipStream_t stream) {
   constexpr bool kDup = CSA_ATTN_DUP_QK != 0;
-  if (dense)
-    attn_kernel<HG, kSplitP, true, kDup><<<grid, HG * 128, 0, stream>>>(a);
+  if (dense && w8)
+    attn_kernel<HG, kSplitP, true, kDup, true><<<grid, HG * 128, 0, stream>>>(a);
+  else if (dense)
+    attn_kernel<HG, kSplitP, true, kDup, false><<<grid, HG * 128, 0, stream>>>(a);
+  else if (w8)
+    attn_kernel<HG, kSplitP, false, kDup, true><<<grid, HG * 128, 0, stream>>>(a);
   else
-    attn_kernel<HG, kSplitP, false, kDup><<<grid, HG * 128, 0, stream>>>(a);
+    attn_kernel<HG, kSplitP, false, kDup, false><<<grid, HG * 128, 0, stream>>>(a);
 }
 
 template <bool kSplitP>
-static void launch_split(const AttnArgs &a, bool dense, dim3 grid, hipStream_t stream) {
+static void launch_split(const AttnArgs &a, bool dense, bool w8, dim3 grid, hipStream_t stream) {
   switch (a.H / 16) {
-    case 1: launch_hg<1, kSplitP>(a, dense, grid, stream); break;
-    case 2: launch_hg<2, kSplitP>(a, dense, grid, stream); break;
-    case 4: launch_hg<4, kSplitP>(a, dense, grid, stream); break;
-    default: launch_hg<8, kSplitP>(a, dense, grid, stream); break;
+    case 1: launch_hg<1, kSplitP>(a, dense, w8, grid, stream); break;
+    case 2: launch_hg<2, kSplitP>(a, dense, w8, grid, stream); break;
+    case 4: launch_hg<4, kSplitP>(a, dense, w8, grid, stream); break;
+    default: launch_hg<8, kSplitP>(a, dense, w8, grid, stream); break;
   }
 }
 
 hipError_t launch_attention(const CacheView &c, const uint16_t *q, int H, const int32_t *q_pos, int Q,
-                            const int32_t *idx, int k, bool dense, const uint16_t *swa, const int32_t *swa_pos0,
-                            int S, int n_win, float scale, bool out_bf16, void *out, float *lse, void *ws,
-                            hipStream_t stream) {
+                            const int32_t *idx, int k, bool dense, const uint16_t *swa, const SwaPlanes *swa8,
+                            const int32_t *swa_pos0, int S, int n_win, float scale, bool out_bf16, void *out,
+                            float *lse, void *ws, hipStream_t stream) {
   const AttnShape sh = attn_shape(c.B, Q, dense ? c.N_cap : k, n_win);
   AttnArgs a;
   a.nope = c.nope;
@@ -636,6 +722,9 @@ hipError_t launch_attention(const CacheView &c, const uint16_t *q, int H, const 
   a.idx = idx;
   a.k = k;
   a.swa = swa;
+  a.swa_codes = swa8 ? swa8->codes : nullptr;
+  a.swa_scales = swa8 ? swa8->scales : nullptr;
+  a.swa_rope = swa8 ? swa8->rope : nullptr;
   a.swa_pos0 = swa_pos0;
   a.S = S;
   a.n_win = n_win;
@@ -650,9 +739,9 @@ hipError_t launch_attention(const CacheView &c, const uint16_t *q, int H, const 
   a.ws_ml = a.ws_o ? a.ws_o + po : nullptr;
   dim3 grid((unsigned)(sh.nsplit * Q), c.B);
   if (out_bf16)
-    launch_split<false>(a, dense, grid, stream);
+    launch_split<false>(a, dense, swa8 != nullptr, grid, stream);
   else
-    launch_split<true>(a, dense, grid, stream);
+    launch_split<true>(a, dense, swa8 != nullptr, grid, stream);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || sh.nsplit == 1) return e;
   const int64_t n_items = (int64_t)c.B * Q * H * (kD / 8);

@@ -62,6 +62,28 @@ __device__ __forceinline__ uint32_t e2m1_encode(float v, float inv_scale) {
   return c | (v < 0.0f ? 8u : 0u);
 }
 
+// MXFP8 (E4M3 elements) block exponent X = floor(log2 amax) - 8 clamped to
+// [-127, 127], as the E8M0 byte X + 127: the exponent field minus 8, and 0
+// for maxima below 2^-118 (subnormal and zero maxima included).
+__device__ __forceinline__ uint32_t mx8_scale_byte(float amax) {
+  int e = (int)((__float_as_uint(amax) >> 23) & 0xFFu);
+  return (uint32_t)(e >= 8 ? e - 8 : 0);
+}
+
+// Magnitude a >= 0 (already divided by the block scale, exactly) -> E4M3
+// code 0..126: nearest value, ties to the even code, saturating at 448.
+// Below 2^-6 the codes step by 2^-9 (subnormals, and 2^-6 itself as code 8);
+// above, a * 2^(3 - e) in [8, 16) rounds to 8 + the mantissa, a carry to 16
+// moving into the exponent.  Scaling by powers of two is exact, and rintf
+// rounds half to even.
+__device__ __forceinline__ uint32_t e4m3_code(float a) {
+  if (a >= 448.0f) return 0x7Eu;
+  if (a < 0.015625f) return (uint32_t)__builtin_rintf(a * 512.0f);
+  const int e = (int)((__float_as_uint(a) >> 23) & 0xFFu) - 127;  // -6 .. 8
+  const float t = a * __uint_as_float((uint32_t)(130 - e) << 23);  // a * 2^(3 - e)
+  return (uint32_t)((e + 7) << 3) + (uint32_t)__builtin_rintf(t) - 8u;
+}
+
 // 1 / 2^X for the block byte s (X = s - 127), exactly: 2^(127 - s).
 __device__ __forceinline__ float mx_inv_scale(uint32_t s) { return __uint_as_float((254u - s) << 23); }
 

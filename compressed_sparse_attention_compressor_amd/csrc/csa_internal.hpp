@@ -61,6 +61,17 @@ size_t pool_workspace_bytes(int B, int Q, int N_cap, int block, int n_blocks);
 hipError_t launch_index_pool(const CacheView &c, const float *scores, const int32_t *q_pos, int Q, int block,
                              int n_blocks, int32_t *pool, void *ws, hipStream_t stream);
 
+// FP8 window rows: bf16 rows [B][S][576] (row stride 576, sequence stride
+// x_stride_b) -> codes [B][S][512], scales [B][S][16], rope [B][S][64].
+hipError_t launch_swa_encode(const uint16_t *x, int64_t x_stride_b, int B, int S, uint8_t *codes, uint8_t *scales,
+                             uint16_t *rope, hipStream_t stream);
+// The planes of FP8 window rows for the attention (nullptr: bf16 rows).
+struct SwaPlanes {
+  const uint8_t *codes;
+  const uint8_t *scales;
+  const uint16_t *rope;
+};
+
 struct AttnShape {
   int nsplit;       // key-range splits per query
   int per_split;    // key slots per split (a multiple of the chunk size)
@@ -70,7 +81,7 @@ AttnShape attn_shape(int B, int Q, int n_main, int n_win);
 size_t attn_workspace_bytes(int B, int Q, int H, int n_main, int n_win);
 
 hipError_t launch_attention(const CacheView &c, const uint16_t *q, int H, const int32_t *q_pos, int Q,
-                            const int32_t *idx, int k, bool dense, const uint16_t *swa,
+                            const int32_t *idx, int k, bool dense, const uint16_t *swa, const SwaPlanes *swa8,
                             const int32_t *swa_pos0, int S, int n_win, float scale, bool out_bf16,
                             void *out, float *lse, void *ws, hipStream_t stream);
 

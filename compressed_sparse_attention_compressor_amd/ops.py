@@ -282,3 +282,60 @@ def hca_dense_attn(cache: Cache, q, q_pos, swa, swa_pos0, n_win, scale, out_dtyp
                                int(n_win), float(scale), OUT_BF16 if out_dtype == torch.bfloat16 else OUT_F32,
                                _ptr(out), _ptr(lse), _ptr(ws), wsb, _stream()), "hca_dense_attn")
     return out, lse
+
+
+def swa_encode(x, codes=None, scales=None, rope=None):
+    """bf16 window rows x [B][S][576] -> FP8 window planes (codes uint8
+    [B][S][512], scales uint8 [B][S][16], rope bf16 [B][S][64])."""
+    _need(x, torch.bfloat16, "x")
+    B, S = x.shape[0], x.shape[1]
+    if x.stride(2) != 1 or x.stride(1) != D:
+        raise ValueError("x rows must be contiguous")
+    dev = x.device
+    codes = codes if codes is not None else torch.empty(B, S, D_NOPE, dtype=torch.uint8, device=dev)
+    scales = scales if scales is not None else torch.empty(B, S, D_NOPE // 32, dtype=torch.uint8, device=dev)
+    rope = rope if rope is not None else torch.empty(B, S, D_ROPE, dtype=torch.bfloat16, device=dev)
+    check(lib().csa_swa_encode(_ptr(x), x.stride(0), B, S, _ptr(codes), _ptr(scales), _ptr(rope), _stream()),
+          "csa_swa_encode")
+    return codes, scales, rope
+
+
+def sparse_attn_w8(cache: Cache, q, q_pos, idx, swa8, swa_pos0, n_win, scale, out_dtype=torch.bfloat16, ws=None,
+                   out=None, lse=None):
+    """sparse_attn with the window rows as the FP8 planes (codes, scales, rope) of swa_encode."""
+    _need(q, torch.bfloat16, "q")
+    B, Q, H = q.shape[0], q.shape[1], q.shape[2]
+    k = idx.shape[2] if idx is not None else 0
+    codes, scales, rope = swa8
+    S = codes.shape[1]
+    dev = q.device
+    out = _attn_out(B, Q, H, out_dtype, dev, out)
+    lse = lse if lse is not None else torch.empty(B, Q, H, dtype=torch.float32, device=dev)
+    need = workspace_bytes(WS_SPARSE_ATTN, B, Q, H, k, n_win)
+    ws, wsb = _workspace(need, ws, dev)
+    cs = cache.struct()
+    check(lib().csa_sparse_attn_w8(ctypes.byref(cs), _ptr(q), H, _ptr(q_pos), Q, _ptr(idx), k, _ptr(codes),
+                                   _ptr(scales), _ptr(rope), _ptr(swa_pos0), S, int(n_win), float(scale),
+                                   OUT_BF16 if out_dtype == torch.bfloat16 else OUT_F32, _ptr(out), _ptr(lse),
+                                   _ptr(ws), wsb, _stream()), "csa_sparse_attn_w8")
+    return out, lse
+
+
+def hca_dense_attn_w8(cache: Cache, q, q_pos, swa8, swa_pos0, n_win, scale, out_dtype=torch.bfloat16, ws=None,
+                      out=None, lse=None):
+    """hca_dense_attn with the window rows as FP8 planes."""
+    _need(q, torch.bfloat16, "q")
+    B, Q, H = q.shape[0], q.shape[1], q.shape[2]
+    codes, scales, rope = swa8
+    S = codes.shape[1]
+    dev = q.device
+    out = _attn_out(B, Q, H, out_dtype, dev, out)
+    lse = lse if lse is not None else torch.empty(B, Q, H, dtype=torch.float32, device=dev)
+    need = workspace_bytes(WS_DENSE_ATTN, B, Q, H, cache.N_cap, n_win)
+    ws, wsb = _workspace(need, ws, dev)
+    cs = cache.struct()
+    check(lib().hca_dense_attn_w8(ctypes.byref(cs), _ptr(q), H, _ptr(q_pos), Q, _ptr(codes), _ptr(scales), _ptr(rope),
+                                  _ptr(swa_pos0), S, int(n_win), float(scale),
+                                  OUT_BF16 if out_dtype == torch.bfloat16 else OUT_F32, _ptr(out), _ptr(lse),
+                                  _ptr(ws), wsb, _stream()), "hca_dense_attn_w8")
+    return out, lse

@@ -195,6 +195,37 @@ int hca_dense_attn(const csa_cache_t *cache, const uint16_t *q, int H, const int
                    const uint16_t *swa, const int32_t *swa_pos0, int S, int n_win, float softmax_scale,
                    int out_dtype, void *out, float *lse, void *ws, size_t ws_bytes, hipStream_t stream);
 
+/* FP8 window rows ([V4.1] "FP4 主 KV キャッシュ": the sliding-window KV stays
+ * FP8, being sensitive to quantisation).  csa_swa_encode turns bf16 raw rows
+ * into three planes, per row:
+ *   codes   uint8  [B][S][512]  the content channels 0..511 as OCP MXFP8
+ *                               E4M3 codes, one byte per channel
+ *   scales  uint8  [B][S][16]   E8M0 byte of channels 32s..32s+31:
+ *                               X = floor(log2 max|v|) - 8 clamped to
+ *                               [-127, 127], byte X + 127 (0 for a zero block);
+ *                               codes round v / 2^X to the nearest E4M3 value,
+ *                               ties to even, saturate at 448, and keep the
+ *                               sign of negative values
+ *   rope    uint16 [B][S][64]   channels 512..575, the bf16 bits unchanged
+ *   x       bf16 [B][S][576], row stride 576, sequence stride x_stride_b
+ *           (>= S*576 when B > 1, a multiple of 8); x, codes and rope 16-byte
+ *           aligned.
+ * Decoding (E4M3 x 2^(s-127)) is exact in bf16 for every row it writes.
+ * csa_sparse_attn_w8 and hca_dense_attn_w8 are csa_sparse_attn and
+ * hca_dense_attn with the window rows read from such planes (same
+ * positions: row s of sequence b is raw position swa_pos0[b] + s); every
+ * other argument, the workspace and the results are as there. */
+int csa_swa_encode(const uint16_t *x, int64_t x_stride_b, int B, int S, uint8_t *codes, uint8_t *scales,
+                   uint16_t *rope, hipStream_t stream);
+int csa_sparse_attn_w8(const csa_cache_t *cache, const uint16_t *q, int H, const int32_t *q_pos, int Q,
+                       const int32_t *idx, int k, const uint8_t *swa_codes, const uint8_t *swa_scales,
+                       const uint16_t *swa_rope, const int32_t *swa_pos0, int S, int n_win, float softmax_scale,
+                       int out_dtype, void *out, float *lse, void *ws, size_t ws_bytes, hipStream_t stream);
+int hca_dense_attn_w8(const csa_cache_t *cache, const uint16_t *q, int H, const int32_t *q_pos, int Q,
+                      const uint8_t *swa_codes, const uint8_t *swa_scales, const uint16_t *swa_rope,
+                      const int32_t *swa_pos0, int S, int n_win, float softmax_scale, int out_dtype, void *out,
+                      float *lse, void *ws, size_t ws_bytes, hipStream_t stream);
+
 /* A stack of CSA2 layers for the same query tokens ([V4.1], CSA2 paragraph
  * and Fig. 4: every layer is statically Full, Reindex or Reuse; Fig. 5: the
  * first Full layer may build the hierarchical candidate pool).  The stack is

@@ -752,6 +752,128 @@ def test_dense_attention_parity(name, w, N_cap, n_entries, pos, dtype):
     _check_attn(out, lse, o, l, dtype, name)
 
 
+# ----------------------------------------------------------------------------- FP8 window rows
+
+
+def _special_rows(rng, S):
+    """bf16 window rows with N(0,1) values and, in some 32-channel blocks,
+    zeros, bf16 subnormals, huge values, values that saturate, and exact
+    midpoints between E4M3 values."""
+    x = rng.standard_normal((S, 576)).astype(np.float32) * np.exp(rng.uniform(-8, 8, (S, 1))).astype(np.float32)
+    x[0, :32] = 0.0
+    x[1, 32:64] = np.float32(2.0 ** -130) * rng.integers(-3, 4, 32)
+    x[2, 64:96] = rng.standard_normal(32).astype(np.float32) * 1e30
+    x[3, 96:128] = 1.0
+    x[3, 100] = 1.9                                           # saturates (1.9 * 2^8 > 448)
+    mids = (O.E4M3_VALUES[:-1] + O.E4M3_VALUES[1:]) / 2
+    x[4, 128:160] = (rng.choice(mids, 32) * 2.0 ** -8).astype(np.float32)
+    x[4, 128] = 256 * 2.0 ** -8                               # fixes the block scale at 2^-8
+    x[5, 160:192] = -0.0
+    t = torch.from_numpy(x).to(torch.bfloat16)
+    return t
+
+
+def test_swa_encode_bit_exact():
+    rng = np.random.default_rng(31)
+    B, S = 3, 70
+    x = torch.stack([_special_rows(rng, S) for _ in range(B)])
+    codes, scales, rope = csa.swa_encode(x.to(DEV))
+    torch.cuda.synchronize()
+    for b in range(B):
+        ref = O.swa_encode(as_u16(x[b]))
+        np.testing.assert_array_equal(_np(codes)[b], ref["codes"], err_msg=f"codes b={b}")
+        np.testing.assert_array_equal(_np(scales)[b], ref["scales"], err_msg=f"scales b={b}")
+        np.testing.assert_array_equal(_np(rope)[b], ref["rope"], err_msg=f"rope b={b}")
+
+
+def _decoded_bf16_rows(codes, scales, rope):
+    rows = O.swa_decode(_np(codes), _np(scales), _np(rope))
+    u = O.f32_to_bf16(rows.astype(np.float32))
+    assert np.array_equal(O.bf16_to_f64(u), rows)          # exact in bf16
+    return torch.from_numpy(u.view(np.int16)).view(torch.bfloat16)
+
+
+W8_CASES = [
+    # (name, workload, N_cap, n_entries, positions, window rows S, swa_pos0, dense)
+    ("sparse-h64", Workload("w8a", 23, B=2, T=2000, m=4, d_idx=0, H_I=0, k=60, H=64, n_win=128, Q=2), 500,
+     [500, 400], [[1999, 700], [1603, 1999]], 300, [1750, 1700], False),
+    ("sparse-h16", Workload("w8b", 24, B=1, T=1200, m=4, d_idx=0, H_I=0, k=40, H=16, n_win=100, Q=3), 300, [300],
+     [[1199, 1150, 1100]], 160, [1040], False),
+    ("dense-h64", Workload("w8c", 25, B=2, T=8192, m=128, d_idx=0, H_I=0, k=0, H=64, n_win=128, Q=1), 64, [64, 50],
+     [[8191], [7000]], 256, [7936, 6900], True),
+]
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=["f32", "bf16"])
+@pytest.mark.parametrize("name,w,N_cap,n_entries,pos,S,swa_pos0,dense", W8_CASES, ids=[c[0] for c in W8_CASES])
+def test_w8_window_equals_bf16_window_on_decoded_rows(name, w, N_cap, n_entries, pos, S, swa_pos0, dense, dtype):
+    """Attention with FP8 window planes against attention with bf16 rows
+    holding the decoded values (exact in bf16): bit-identical outputs and
+    LSE.  The planes come from the encoder and, in a second pass, are drawn
+    directly (random valid codes, scale bytes 100..154)."""
+    pos = np.array(pos, np.int32)
+    planes, qs, _, _ = _attn_inputs(w, N_cap, n_entries, pos)
+    cache = _gpu_cache(planes, w.B, N_cap, w.m, 0, n_entries)
+    rng = np.random.default_rng(w.cfg)
+    x = torch.stack([_special_rows(rng, S) for _ in range(w.B)]).to(DEV)
+    enc = csa.swa_encode(x)
+    drawn = (torch.from_numpy(rng.integers(0, 0x7F, (w.B, S, 512)) | (rng.integers(0, 2, (w.B, S, 512)) * 0x80))
+             .to(torch.uint8).to(DEV),
+             torch.from_numpy(rng.integers(100, 155, (w.B, S, 16))).to(torch.uint8).to(DEV), enc[2])
+    s0 = torch.tensor(swa_pos0, dtype=torch.int32, device=DEV)
+    q, qp = qs["q"].to(DEV), torch.from_numpy(pos).to(DEV)
+    idx = None
+    if not dense:
+        idx = np.full((w.B, w.Q, w.k), -1, np.int32)
+        for b in range(w.B):
+            for t in range(w.Q):
+                V = O.visible_count(int(pos[b, t]), w.m, n_entries[b])
+                n = min(w.k - 1, V)
+                idx[b, t, :n] = np.sort(rng.choice(V, n, replace=False))
+        idx = torch.from_numpy(idx).to(DEV)
+    for pl in (enc, drawn):
+        rows = torch.stack([_decoded_bf16_rows(pl[0][b], pl[1][b], pl[2][b]) for b in range(w.B)]).to(DEV)
+        if dense:
+            o8, l8 = csa.hca_dense_attn_w8(cache, q, qp, pl, s0, w.n_win, w.softmax_scale, out_dtype=dtype)
+            o16, l16 = csa.hca_dense_attn(cache, q, qp, rows, s0, w.n_win, w.softmax_scale, out_dtype=dtype)
+        else:
+            o8, l8 = csa.sparse_attn_w8(cache, q, qp, idx, pl, s0, w.n_win, w.softmax_scale, out_dtype=dtype)
+            o16, l16 = csa.sparse_attn(cache, q, qp, idx, rows, s0, w.n_win, w.softmax_scale, out_dtype=dtype)
+        torch.cuda.synchronize()
+        assert torch.equal(o8.view(torch.int16) if dtype == torch.bfloat16 else o8.view(torch.int32),
+                           o16.view(torch.int16) if dtype == torch.bfloat16 else o16.view(torch.int32)), name
+        assert torch.equal(l8.view(torch.int32), l16.view(torch.int32)), name
+
+
+def test_w8_window_attention_against_oracle():
+    w = W8_CASES[0][1]
+    pos = np.array(W8_CASES[0][4], np.int32)
+    n_entries, S, swa_pos0 = W8_CASES[0][3], W8_CASES[0][5], W8_CASES[0][6]
+    planes, qs, _, _ = _attn_inputs(w, W8_CASES[0][2], n_entries, pos)
+    cache = _gpu_cache(planes, w.B, W8_CASES[0][2], w.m, 0, n_entries)
+    x = torch.stack([normal_bf16(w.seed, TensorId.SWA, (1, S, 576), first_seq=b)[0] for b in range(w.B)])
+    enc = csa.swa_encode(x.to(DEV))
+    rng = np.random.default_rng(5)
+    idx = np.full((w.B, w.Q, w.k), -1, np.int32)
+    for b in range(w.B):
+        for t in range(w.Q):
+            V = O.visible_count(int(pos[b, t]), w.m, n_entries[b])
+            idx[b, t, :30] = np.sort(rng.choice(V, 30, replace=False))
+    out, lse = csa.sparse_attn_w8(cache, qs["q"].to(DEV), torch.from_numpy(pos).to(DEV), torch.from_numpy(idx).to(DEV),
+                                  enc, torch.tensor(swa_pos0, dtype=torch.int32, device=DEV), w.n_win,
+                                  w.softmax_scale, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    nope, nsc, rope = planes["nope"].numpy(), planes["nscale"].numpy(), as_u16(planes["rope"])
+    for b in range(w.B):
+        pl = O.swa_encode(as_u16(x[b]))
+        rows = O.swa_decode(pl["codes"], pl["scales"], pl["rope"])
+        for t in range(w.Q):
+            o, l = O.sparse_attention(as_u16(qs["q"][b, t]), nope[b], nsc[b], rope[b], idx[b, t], rows, swa_pos0[b],
+                                      int(pos[b, t]), w.n_win, w.softmax_scale, w.m, n_entries[b])
+            assert row_rel_err(_np(out)[b, t], o).max() <= TOL[torch.float32]
+            assert np.abs(_np(lse)[b, t] - l).max() <= 1e-4 * max(1.0, np.abs(l).max())
+
+
 def test_attention_with_no_keys_is_zero():
     w = Workload("nk", 17, B=1, T=64, m=4, d_idx=0, H_I=0, k=8, H=16, n_win=0, Q=2)
     planes, qs, swa, s0 = _attn_inputs(w, 16, [16], np.array([[2, 1]], np.int32))

@@ -105,6 +105,7 @@ def build_layers(w, L, dev, log_every=8):
         ly.x_blk = x_last[:, -w.m:].clone()
         ly.z_blk = z_last.clone()
         ly.swa = x_last[:, -w.n_win:].clone()
+        ly.swa8 = csa.swa_encode(ly.swa)     # the same rows as FP8 window planes
         ly.swa_pos0 = torch.full((w.B,), w.T - w.n_win, dtype=torch.int32, device=dev)
         ly.idx = torch.empty(w.B, 1, w.k, dtype=torch.int32, device=dev)
         ly.out = torch.empty(w.B, 1, w.H, 576, dtype=torch.bfloat16, device=dev)
@@ -181,6 +182,10 @@ def main():
 
     def st_topk(ly):
         csa.topk(ly.cache, scores_ws, ly.q_pos, w.k, out=ly.idx, ws=topk_ws if topk_ws_bytes else None)
+
+    def st_attn_w8(ly):
+        csa.sparse_attn_w8(ly.cache, ly.q, ly.q_pos, ly.idx, ly.swa8, ly.swa_pos0, w.n_win, w.softmax_scale,
+                           out_dtype=torch.bfloat16, ws=attn_ws, out=ly.out, lse=ly.lse)
 
     def st_attn(ly):
         csa.sparse_attn(ly.cache, ly.q, ly.q_pos, ly.idx, ly.swa, ly.swa_pos0, w.n_win, w.softmax_scale,
@@ -285,6 +290,40 @@ def main():
         stage_us[names[f]] = a.elapsed_time(b) * 1e3 / (reps * R)
     log(f"[bench] stage averages (us): {stage_us}")
 
+    # The same step with the window rows as FP8 planes (the window KV format
+    # the pages state); reported beside the headline, which keeps bf16 rows.
+    w8 = None
+    if not args.only_index:
+        g8 = capture(lambda: [(st_append(layers[l]), st_topk(layers[l]), st_attn_w8(layers[l])) for l in range(L)])
+        g8.replay()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(max(1, K // L)):
+            g8.replay()
+        b.record()
+        torch.cuda.synchronize()
+        ms8 = a.elapsed_time(b) / (max(1, K // L) * L)
+        del g8
+        ga = capture(lambda: [st_attn_w8(layers[i % L]) for i in range(R)])
+        ga.replay()
+        torch.cuda.synchronize()
+        a.record()
+        for _ in range(5):
+            ga.replay()
+        b.record()
+        torch.cuda.synchronize()
+        attn8_us = a.elapsed_time(b) * 1e3 / (5 * R)
+        del ga
+        by8 = step_bytes(w)
+        win16 = w.B * 2 * w.n_win * 576
+        win8 = w.B * w.n_win * (512 + 16 + 128)
+        step8 = by8["step"] - win16 + win8
+        w8 = {"window": "MXFP8 content channels + bf16 positional channels (656 B per row)",
+              "ms_per_step": round(ms8, 6), "q_tokens_per_s": round(w.B / (ms8 * 1e-3), 1), "step_bytes": step8,
+              "achieved_GBps": round(step8 / (ms8 * 1e-3) / 1e9, 1), "sparse_attn_us": round(attn8_us, 3)}
+        log(f"[bench] FP8 window step {ms8 * 1e3:.2f} us, attention {attn8_us:.2f} us")
+
     by = step_bytes(w)
     # the dominant kernel: the fused append + indexer launch
     idx_us = stage_us["compress+index_scores"]
@@ -318,6 +357,7 @@ def main():
         "step_bytes": by["step"],
         "stage_us": {k: round(v, 3) for k, v in stage_us.items()},
         "ms_per_step_spread": spread,
+        "fp8_window": w8,
         "warm_one_layer": {"ms_per_step": round(warm_ms, 6), "q_tokens_per_s": round(w.B / (warm_ms * 1e-3), 1),
                            "note": "one layer's cache replayed L times in a row (warm); not the headline"},
         "roofline": {"bound": "hbm", "kernel": "append_index_kernel (decode append + indexer)",

@@ -203,3 +203,29 @@ def test_layer_stack_checks(L):
 def test_index_pool_grid_limit(L):
     # 2^24 query rows x 128 blocks of 256: beyond a 32-bit flattened grid
     assert _pool(L, _cache(B=1, N=32768), Q=1 << 24, block=1, nb=1) == EUNSUP
+
+
+def test_fp8_window_checks(L):
+    # csa_swa_encode(x, x_stride_b, B, S, codes, scales, rope, stream)
+    enc = L.csa_swa_encode
+    assert enc(None, 100 * 576, 2, 100, P, P, P, None) == ENULL
+    assert enc(P, 100 * 576, 2, 100, P, None, P, None) == ENULL
+    assert enc(P, 100 * 576, -1, 100, P, P, P, None) == ESHAPE
+    assert enc(P, 50 * 576, 2, 100, P, P, P, None) == ESHAPE          # rows of two sequences overlap
+    assert enc(P + 2, 100 * 576, 2, 100, P, P, P, None) == EALIGN
+    assert enc(P, 100 * 576 + 4, 2, 100, P, P, P, None) == EALIGN
+    assert enc(P, 0, 0, 100, None, None, None, None) == OK            # nothing to do
+    # csa_sparse_attn_w8 / hca_dense_attn_w8: the window planes are checked first
+    def sw8(codes=P, scales=P, rope=P, nw=128):
+        return L.csa_sparse_attn_w8(ctypes.byref(_cache()), P, 64, P, 1, P, 16, codes, scales, rope, P, 128, nw, 1.0,
+                                    1, P, None, P, 1 << 30, None)
+    assert sw8(codes=None) == ENULL
+    assert sw8(scales=None) == ENULL
+    assert sw8(codes=P + 4) == EALIGN
+    assert sw8(rope=P + 8) == EALIGN
+    assert L.csa_sparse_attn_w8(ctypes.byref(_cache()), P, 48, P, 1, P, 16, P, P, P, P, 128, 128, 1.0, 1, P, None, P,
+                                1 << 30, None) == EUNSUP
+    assert L.hca_dense_attn_w8(ctypes.byref(_cache(d_idx=0)), P, 64, P, 1, None, P, P, P, 128, 128, 1.0, 1, P, None,
+                               P, 1 << 30, None) == ENULL
+    assert L.csa_sparse_attn_w8(ctypes.byref(_cache()), P, 64, P, 0, P, 16, P, P, P, P, 128, 128, 1.0, 1, P, None,
+                                P, 1 << 30, None) == OK                # Q = 0: nothing to launch

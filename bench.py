@@ -563,6 +563,14 @@ def _oracle_threads():
         return 1
 
 
+def _host_cpus() -> str:
+    """The host the oracle ran on: affinity cores, os.cpu_count() and the
+    BLAS thread count (the oracle runs its sequences one after another, so
+    only the BLAS calls inside it use more than one core)."""
+    return (f"host: {len(os.sched_getaffinity(0))} cores in the affinity mask, os.cpu_count() = {os.cpu_count()}, "
+            f"BLAS threads = {_oracle_threads()}")
+
+
 def hca_leg(L=16, K=256):
     """HCA dense decode: 8 sequences at 1,048,576 raw tokens (m = 128, 8,192
     entries), every head attending to every entry plus the window; one step
@@ -918,11 +926,7 @@ def cpu_baseline(w, nseq, min_seconds=10.0):
     import oracle as O
     from synth.workloads import as_u16, params, queries, raw_rows, synthetic_cache
 
-    try:
-        import threadpoolctl
-        threads = max([p.get("num_threads", 1) for p in threadpoolctl.threadpool_info()] or [1])
-    except Exception:  # pragma: no cover
-        threads = 1
+    threads = _oracle_threads()
     bias, wik = params(w)
     qs = queries(w)
     planes = synthetic_cache(w, nseq=nseq)
@@ -944,7 +948,8 @@ def cpu_baseline(w, nseq, min_seconds=10.0):
     dt = time.perf_counter() - t0
     return {"value": round(done / dt, 3), "unit": "query-tokens/s", "cores": int(threads), "kind": "oracle",
             "sample": f"{passes} passes over {nseq} of {w.B} sequences of one decode step (compress block, index "
-                      f"{w.N} entries, top-{w.k}, attention): {done} query tokens in {dt:.2f} s"}
+                      f"{w.N} entries, top-{w.k}, attention): {done} query tokens in {dt:.2f} s; "
+                      f"{_host_cpus()}"}
 
 
 if __name__ == "__main__":

@@ -377,7 +377,18 @@ __device__ __forceinline__ void append_and_score(const AppendArgs &ap, uint8_t *
     const int i = tid + u * kIdxThreads;
     if (i < kQBytes / 16) *reinterpret_cast<uint4 *>(qs + i * 16) = qv_stage[u];
   }
-  __syncthreads();
+  // the projection's first batch of W_IK loads goes out now and stays in
+  // flight across the LDS-only barrier and the main entry's encoding
+  const int nq = d_idx / 4;
+  const int part = tid / nq, pq = tid % nq;
+  const bool projects = part < kAppSlices;
+  const uint2 *wp = reinterpret_cast<const uint2 *>(ap.w_ik + (int64_t)((projects ? part : 0) * kAppSlice) * d_idx +
+                                                    4 * pq);
+  constexpr int kBatch = kAppSlice / 2;
+  uint2 wv0[kBatch];
+#pragma unroll
+  for (int j = 0; j < kBatch; ++j) wv0[j] = wp[(int64_t)j * nq];
+  lds_barrier();
 
   // 2. MXFP4 main entry and bf16 rope channels
   {
@@ -390,26 +401,38 @@ __device__ __forceinline__ void append_and_score(const AppendArgs &ap, uint8_t *
 
   // 3. indexer key: thread (slice p, output quad q) accumulates channels
   //    [72p, 72p+72) of outputs 4q..4q+3 in channel order (one 8-byte W_IK
-  //    load per channel serves the four); the slices are added in order
+  //    load per channel serves the four), in batches of loads issued
+  //    together; the slices are added in order
   {
-    const int nq = d_idx / 4;
-    const int part = tid / nq, q = tid % nq;
-    if (part < kAppSlices) {
-      const uint2 *wp = reinterpret_cast<const uint2 *>(ap.w_ik + (int64_t)(part * kAppSlice) * d_idx + 4 * q);
+    const int q = pq;
+    if (projects) {
       const float4 *cp = reinterpret_cast<const float4 *>(&cs[part * kAppSlice]);
       float acc[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 6
-      for (int u4 = 0; u4 < kAppSlice / 4; ++u4) {
-        const float4 c4 = cp[u4];
-        const float cc[4] = {c4.x, c4.y, c4.z, c4.w};
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const uint2 wv = wp[(int64_t)(4 * u4 + j) * nq];
-          acc[0] = fmaf(cc[j], bf16_to_f32(wv.x & 0xFFFFu), acc[0]);
-          acc[1] = fmaf(cc[j], bf16_to_f32(wv.x >> 16), acc[1]);
-          acc[2] = fmaf(cc[j], bf16_to_f32(wv.y & 0xFFFFu), acc[2]);
-          acc[3] = fmaf(cc[j], bf16_to_f32(wv.y >> 16), acc[3]);
+      for (int h = 0; h < kAppSlice / kBatch; ++h) {
+        uint2 wv[kBatch];
+        if (h == 0) {
+#pragma unroll
+          for (int j = 0; j < kBatch; ++j) wv[j] = wv0[j];
+        } else {
+#pragma unroll
+          for (int j = 0; j < kBatch; ++j) wv[j] = wp[(int64_t)(h * kBatch + j) * nq];
         }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int u4 = 0; u4 < kBatch / 4; ++u4) {
+          const float4 c4 = cp[h * (kBatch / 4) + u4];
+          const float cc[4] = {c4.x, c4.y, c4.z, c4.w};
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const uint2 w2 = wv[4 * u4 + j];
+            acc[0] = fmaf(cc[j], bf16_to_f32(w2.x & 0xFFFFu), acc[0]);
+            acc[1] = fmaf(cc[j], bf16_to_f32(w2.x >> 16), acc[1]);
+            acc[2] = fmaf(cc[j], bf16_to_f32(w2.y & 0xFFFFu), acc[2]);
+            acc[3] = fmaf(cc[j], bf16_to_f32(w2.y >> 16), acc[3]);
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
       }
 #pragma unroll
       for (int j = 0; j < 4; ++j) kpart[part][4 * q + j] = acc[j];
@@ -476,9 +499,13 @@ __device__ __forceinline__ void append_and_score(const AppendArgs &ap, uint8_t *
   if (lane == 16 * t_new + r_new && ap.entry < vis) scores[(int64_t)b * Q * Ns + ap.entry] = res;
 }
 
-// Grid: B append workgroups first, then B x tiles indexer workgroups.
+// Grid: B append workgroups first, then B x tiles indexer workgroups.  The
+// append workgroups' dependent chain (rows, pooling, two batches of W_IK
+// loads, encoding, the entry's score) ends the launch when it is slower than
+// the key stream; the register bound keeps room for a whole 36-load batch
+// at the indexer's own occupancy (5 waves per SIMD with 32 heads, 4 with 64).
 template <int HT, bool kGateFull>
-__global__ __launch_bounds__(kIdxThreads) void append_index_kernel(
+__global__ __launch_bounds__(kIdxThreads, HT >= 4 ? 4 : 5) void append_index_kernel(
     AppendArgs ap, uint8_t *__restrict__ ikey, uint8_t *__restrict__ iscale, const int32_t *__restrict__ n_entries,
     int N_cap, int d_idx, const uint8_t *__restrict__ q_idx, const float *__restrict__ w_idx, int H_I,
     const int32_t *__restrict__ q_pos, int Q, float *__restrict__ scores, int B, int tiles) {

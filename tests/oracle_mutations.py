@@ -42,6 +42,9 @@ muts = [
  ("formats.py", "np.where(lo % 2 == 0, lo, hi)", "np.where(lo % 2 == 1, lo, hi)"),
  ("formats.py", "code = _e4m3_round(np.abs(scaled)) | np.where(scaled < 0, 0x80, 0)", "code = _e4m3_round(np.abs(scaled)) | np.where(scaled < -2.0 ** -9, 0x80, 0)"),
  ("csa.py", "return dict(codes=codes, scales=scales, rope=x[:, d_nope:].copy())", "return dict(codes=codes, scales=scales, rope=x[:, d_nope - 1:-1].copy())"),
+ ("csa.py", "layer_b[\"qI\"], layer_b[\"w\"],\n                                   p, m, n_entries, k_b, cand=idx_a)", "layer_a[\"qI\"], layer_b[\"w\"],\n                                   p, m, n_entries, k_b, cand=idx_a)"),
+ ("csa.py", "p, m, n_entries, k_b, cand=idx_a)", "p, m, n_entries, k_b)"),
+ ("csa.py", "o_b, lse_b = sparse_attention(layer_b[\"q\"]", "o_b, lse_b = sparse_attention(layer_a[\"q\"]"),
 ]
 missed = 0
 root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))

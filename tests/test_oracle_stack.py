@@ -17,11 +17,13 @@ from oracle import (
     REINDEX,
     REUSE,
     block_pool,
+    csa2_pair,
     csa2_stack,
     index_topk,
     mxfp4_encode,
     sparse_attention,
 )
+from oracle.formats import e4m3_to_f64, mxfp4_decode
 
 M, NWIN, SCALE = 4, 16, 0.05
 
@@ -145,3 +147,37 @@ def test_invalid_stacks():
     with pytest.raises(ValueError):
         csa2_stack([dict(mode=FULL, cache=_cache(rng, 100), k=8, **a), dict(mode=REINDEX, k=8, cand=CAND_POOL, **a)],
                    P, M, NWIN)
+
+
+def test_csa2_pair_against_the_definition():
+    """Full then Reindex ([V4.1] Fig. 4) for one query: layer B's selection is
+    the k_b best of layer A's selection under B's own indexer query, scored
+    here entry by entry from the indexer's definition (sum over heads of
+    w_h * ReLU(q_h . k_j) on the decoded keys); the same query at the same k
+    reproduces layer A; k_b at or above A's count keeps all of A."""
+    rng = np.random.default_rng(6)
+    c = _cache(rng, 700)
+    a, b = _q(rng), _q(rng)
+    r = csa2_pair(c, a, b, P, M, 700, NWIN, SCALE, 64, 16)
+    sel_a = r["idx_a"][r["idx_a"] >= 0]
+    sel_b = r["idx_b"][r["idx_b"] >= 0]
+    assert len(sel_a) == 64 and len(sel_b) == 16
+    assert set(sel_b.tolist()) <= set(sel_a.tolist())
+    keys = mxfp4_decode(c["ikey"], c["iscale"])
+    qI = e4m3_to_f64(b["qI"])
+    wb = b["w"].astype(np.float64)
+    score = {}
+    for j in sel_a.tolist():
+        score[j] = sum(wb[h] * max(0.0, float(np.dot(qI[h], keys[j]))) for h in range(len(wb)))
+    best = sorted(score, key=lambda j: (-score[j], j))[:16]
+    assert sorted(best) == sorted(sel_b.tolist())
+    # layer B attends with its own query and window over the shared cache
+    o, lse = sparse_attention(b["q"], c["nope"], c["nscale"], c["rope"], r["idx_b"], b["swa"], b["swa_pos0"], P,
+                              NWIN, SCALE, M, 700)
+    np.testing.assert_array_equal(r["o_b"], o)
+    np.testing.assert_array_equal(r["lse_b"], lse)
+    same = csa2_pair(c, a, a, P, M, 700, NWIN, SCALE, 64, 64)
+    np.testing.assert_array_equal(same["idx_b"], same["idx_a"])
+    np.testing.assert_array_equal(same["o_b"], same["o_a"])
+    wide = csa2_pair(c, a, b, P, M, 700, NWIN, SCALE, 64, 100)
+    assert set(wide["idx_b"][wide["idx_b"] >= 0].tolist()) == set(sel_a.tolist())

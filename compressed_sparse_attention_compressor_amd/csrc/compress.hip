@@ -225,10 +225,132 @@ __global__ __launch_bounds__(kCompThreads) void compress_kernel(
   }
 }
 
+// Long blocks without an indexer key (HCA, m = 128): one workgroup per
+// (entry, sequence, 64-channel group).  Thread (row group rg, channel quad
+// q) takes rows rg, rg + 16, ... of its four channels, so each pass issues
+// its loads together (m / 16 rows per thread) instead of walking all m rows;
+// the row groups' maxima, then their weighted sums, are combined through
+// LDS (maximum, then sums in row-group order).  Each term is the same
+// exp(a_i - max) as in compress_kernel; only the summation order differs.
+// Group g < 8 encodes MX blocks 2g and 2g + 1 of the main entry; group 8
+// holds the bf16 rope channels.
+constexpr int kLongCh = 64;
+constexpr int kLongQuads = kLongCh / 4;
+constexpr int kLongRG = kCompThreads / kLongQuads;
+static_assert(kD % kLongCh == 0 && kDNope % kLongCh == 0 && kDRope == kLongCh, "channel groups");
+
+template <bool kGateFull>
+__global__ __launch_bounds__(kCompThreads) void compress_long_kernel(
+    const uint16_t *__restrict__ x, int64_t x_stride_b, const uint16_t *__restrict__ z, int64_t z_stride_b,
+    const float *__restrict__ bias, int m, int64_t entry0, uint8_t *__restrict__ nope, uint8_t *__restrict__ nscale,
+    uint16_t *__restrict__ rope, int N_cap) {
+  __shared__ float red_a[kLongRG][kLongCh];
+  __shared__ float red_b[kLongRG][kLongCh];
+  __shared__ float cs[kLongCh];
+  const int j = blockIdx.x, b = blockIdx.y, cg = blockIdx.z;
+  const int tid = threadIdx.x, q = tid % kLongQuads, rg = tid / kLongQuads;
+  const int c = cg * kLongCh + 4 * q;
+  const uint16_t *xb = x + (int64_t)b * x_stride_b;
+  const uint16_t *zb = z + (int64_t)b * z_stride_b;
+  const int64_t row0 = (int64_t)j * m;
+
+  // pass 1: gate maxima of this thread's rows
+  float mx[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+#pragma unroll 8
+  for (int i = rg; i < m; i += kLongRG) {
+    const float bi = bias[i];
+    if (kGateFull) {
+      const uint2 gg = *reinterpret_cast<const uint2 *>(zb + (row0 + i) * kD + c);
+      mx[0] = fmaxf(mx[0], bf16_to_f32(gg.x & 0xFFFFu) + bi);
+      mx[1] = fmaxf(mx[1], bf16_to_f32(gg.x >> 16) + bi);
+      mx[2] = fmaxf(mx[2], bf16_to_f32(gg.y & 0xFFFFu) + bi);
+      mx[3] = fmaxf(mx[3], bf16_to_f32(gg.y >> 16) + bi);
+    } else {
+      mx[0] = fmaxf(mx[0], bf16_to_f32(zb[row0 + i]) + bi);
+    }
+  }
+  if (!kGateFull) mx[1] = mx[2] = mx[3] = mx[0];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) red_a[rg][4 * q + u] = mx[u];
+  __syncthreads();
+  if (tid < kLongCh) {
+    float v = red_a[0][tid];
+    for (int r = 1; r < kLongRG; ++r) v = fmaxf(v, red_a[r][tid]);
+    cs[tid] = v;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int u = 0; u < 4; ++u) mx[u] = cs[4 * q + u];
+
+  // pass 2: weighted sums of this thread's rows
+  float den[4] = {0.f, 0.f, 0.f, 0.f};
+  float num[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 8
+  for (int i = rg; i < m; i += kLongRG) {
+    const float bi = bias[i];
+    float a[4];
+    if (kGateFull) {
+      const uint2 gg = *reinterpret_cast<const uint2 *>(zb + (row0 + i) * kD + c);
+      a[0] = bf16_to_f32(gg.x & 0xFFFFu) + bi;
+      a[1] = bf16_to_f32(gg.x >> 16) + bi;
+      a[2] = bf16_to_f32(gg.y & 0xFFFFu) + bi;
+      a[3] = bf16_to_f32(gg.y >> 16) + bi;
+    } else {
+      a[0] = a[1] = a[2] = a[3] = bf16_to_f32(zb[row0 + i]) + bi;
+    }
+    const uint2 v = *reinterpret_cast<const uint2 *>(xb + (row0 + i) * kD + c);
+    const float xv[4] = {bf16_to_f32(v.x & 0xFFFFu), bf16_to_f32(v.x >> 16), bf16_to_f32(v.y & 0xFFFFu),
+                         bf16_to_f32(v.y >> 16)};
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const float w = expf(a[u] - mx[u]);
+      den[u] += w;
+      num[u] = fmaf(w, xv[u], num[u]);
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    red_a[rg][4 * q + u] = den[u];
+    red_b[rg][4 * q + u] = num[u];
+  }
+  __syncthreads();
+  if (tid < kLongCh) {
+    float d = 0.f, n = 0.f;
+    for (int r = 0; r < kLongRG; ++r) {
+      d += red_a[r][tid];
+      n += red_b[r][tid];
+    }
+    cs[tid] = n / d;
+  }
+  __syncthreads();
+
+  const int64_t row = (int64_t)b * N_cap + entry0 + j;
+  if (cg < kDNope / kLongCh) {
+    if (tid < kLongCh / 2) {
+      uint32_t sb;
+      const uint32_t byte = encode_pair(cs[2 * tid], cs[2 * tid + 1], sb);
+      nope[row * kNopeBytes + cg * (kLongCh / 2) + tid] = (uint8_t)byte;
+      if ((tid & 15) == 0) nscale[row * kNopeScales + cg * (kLongCh / 32) + (tid >> 4)] = (uint8_t)sb;
+    }
+  } else if (tid < kDRope) {
+    rope[row * kDRope + tid] = (uint16_t)f32_to_bf16(cs[tid]);
+  }
+}
+
 hipError_t launch_compress(const uint16_t *x, int64_t x_stride_b, const uint16_t *z, int64_t z_stride_b,
                            int G, const float *bias, const uint16_t *w_ik, int64_t entry0, int n_chunk,
                            const CacheView &c, hipStream_t stream) {
   if (n_chunk <= 0 || c.B <= 0) return hipSuccess;
+  if (!w_ik && c.m > kSmallM) {
+    const dim3 grid((unsigned)n_chunk, c.B, kD / kLongCh);
+    if (G == kD)
+      compress_long_kernel<true><<<grid, kCompThreads, 0, stream>>>(x, x_stride_b, z, z_stride_b, bias, c.m, entry0,
+                                                                    c.nope, c.nscale, c.rope, c.N_cap);
+    else
+      compress_long_kernel<false><<<grid, kCompThreads, 0, stream>>>(x, x_stride_b, z, z_stride_b, bias, c.m, entry0,
+                                                                     c.nope, c.nscale, c.rope, c.N_cap);
+    return hipGetLastError();
+  }
   // Few workgroups (decode appends): spread the key blocks over workgroups,
   // each recomputing the pooled rows it needs; many: one workgroup per group.
   const int groups = (n_chunk + kEPB - 1) / kEPB;

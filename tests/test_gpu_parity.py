@@ -129,6 +129,14 @@ COMPRESS_CASES = [
      False),
     ("gate1-chunked-ragged", Workload("g1", 6, B=3, T=148, m=4, d_idx=128, H_I=32, k=8, H=64, n_win=8), [64, 84], 1,
      True),
+    # blocks longer than 8 rows without an indexer key: rows spread over 16
+    # row groups per 64-channel workgroup (m = 12 leaves four groups empty)
+    ("hca-m128-gate1", Workload("hg", 23, B=2, T=1024, m=128, d_idx=0, H_I=0, k=0, H=64, n_win=128), [1024], 1,
+     False),
+    ("m24-chunked", Workload("m24", 24, B=3, T=960, m=24, d_idx=0, H_I=0, k=0, H=64, n_win=128), [384, 576], 576,
+     False),
+    ("m12", Workload("m12", 25, B=2, T=600, m=12, d_idx=0, H_I=0, k=0, H=64, n_win=128), [600], 576, False),
+    ("m256", Workload("m256", 27, B=1, T=1024, m=256, d_idx=0, H_I=0, k=0, H=64, n_win=128), [1024], 576, False),
 ]
 
 

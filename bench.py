@@ -137,8 +137,9 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the path has no multi-GPU "
-              "component in this build", file=sys.stderr)
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}): sequences are independent, so "
+              "N GPUs would each run this same single-GPU step on B/N sequences; no multi-GPU path is "
+              "implemented", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np

@@ -945,6 +945,7 @@ def test_end_to_end_tiny_decode():
 TOPK_CASES = [
     # (name, B, Q, Ns, visible per row, k, rounding that creates ties)
     ("two-stage-ties", 2, 1, 20000, [20000, 13001], 300, 1.0),
+    ("two-stage-ties-k600", 2, 1, 20000, [20000, 13001], 600, 1.0),
     ("two-stage-k-over-slice", 1, 1, 32768, [32768], 5000, 0.05),
     ("single-stage-ragged", 3, 2, 1003, [1003, 999, 17], 64, 0.5),
     # rows of at least 65,536 with few siblings: multi-workgroup radix selection
@@ -954,6 +955,13 @@ TOPK_CASES = [
     ("radix-all-equal", 1, 1, 65536, [65536], 1000, 1e9),
     ("radix-k1", 1, 2, 80000, [80000, 1], 1, 0.01),
     ("radix-k2048", 1, 1, 262144, [262144], 2048, 0.001),
+    # more two-stage shapes: ragged rows, all equal, a length not a multiple
+    # of 4, k above a row's visible count, a crowded threshold value
+    ("two-stage-ragged", 3, 1, 32768, [32768, 4097, 5000], 512, 0.1),
+    ("two-stage-all-equal", 1, 2, 30000, [30000, 9000], 512, 1e9),
+    ("two-stage-odd-length", 1, 2, 30001, [30001, 12345], 100, 0.05),
+    ("two-stage-k-over-visible", 2, 1, 8192, [8192, 300], 512, 0.1),
+    ("two-stage-ties-crowd", 1, 1, 20000, [20000], 512, 2.0),
     # 256 rows longer than a register-resident row: the tiled selection
     ("tiled-many-rows", 16, 16, 33000, [33000, 32769, 100], 100, 0.1),
     ("sign-crossing", 2, 1, 8192, [8192, 6000], 5000, 0.001),   # the k-th score is negative

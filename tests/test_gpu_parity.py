@@ -964,6 +964,10 @@ TOPK_CASES = [
     ("two-stage-ties-crowd", 1, 1, 20000, [20000], 512, 2.0),
     # 256 rows longer than a register-resident row: the tiled selection
     ("tiled-many-rows", 16, 16, 33000, [33000, 32769, 100], 100, 0.1),
+    # causal rows of one launch (visible counts spread over the rows, as in a
+    # prefill), one workgroup per row
+    ("many-rows-causal", 1, 300, 16384, None, 1024, 0.1),
+    ("many-rows-causal-odd", 2, 150, 9999, None, 64, 0.5),
     ("sign-crossing", 2, 1, 8192, [8192, 6000], 5000, 0.001),   # the k-th score is negative
     ("all-equal", 1, 2, 3000, [3000, 2500], 100, 1e9),         # every score rounds to 0
 ]
@@ -976,6 +980,9 @@ def test_topk_stage_parity(name, B, Q, Ns, vis, k, rnd):
     raw = normal_f32(99, TensorId.W, (B * Q, Ns)).numpy().astype(np.float64)
     sc = (np.round(raw / rnd) * rnd).astype(np.float32).reshape(B, Q, Ns)
     # visibility through positions: m = 1, entry j visible when j <= p
+    # (None: counts spread over the rows, as in a causal prefill)
+    if vis is None:
+        vis = [min(Ns, (r * Ns) // (B * Q) + 1) for r in range(B * Q)]
     vis = np.array(vis[:B * Q] + [Ns] * (B * Q - len(vis)))[:B * Q].reshape(B, Q)
     pos = (vis - 1).astype(np.int32)
     planes = dict(nope=np.zeros((B, 1, 256), np.uint8), nscale=np.zeros((B, 1, 16), np.uint8),

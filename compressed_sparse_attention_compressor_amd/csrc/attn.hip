@@ -532,7 +532,64 @@ __global__ __launch_bounds__(HG * 128) void attn_kernel(AttnArgs a) {
   if (w_lo < s_end) run_chunks(std::true_type{}, w_lo, s_end);  // its first list was published by the last entry chunk
 
   const int h0 = hg * 16;
-  if (a.nsplit == 1) {
+  // bf16 results leave through LDS as 16-byte stores: the wave's 16 heads x
+  // 288 channels in two halves of 144 channels, staged in the key tile no
+  // wave reads any more (the one before the last chunk's: every wave passed
+  // the last chunk's barrier after computing on it).  dst points at head
+  // h0's row at channel cbase; rows are kD apart.
+  constexpr bool kStaged = HG <= 4;  // 2*HG waves x 4,608 bytes within one key tile
+  static_assert(!kStaged || 2 * HG * 16 * (kHalfD / 2) <= kKC * kKRow, "staging fits a key tile");
+  auto store_bf16 = [&](uint16_t *dst, const float (&mul)[4]) __attribute__((always_inline)) {
+    constexpr int kHalfCh = kHalfD / 2;  // 144
+    uint16_t *stg = &Kl[ci & 1][0] + wave * (16 * kHalfCh);
+#pragma unroll
+    for (int hc = 0; hc < 2; ++hc) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int jj = 0; jj < kHalfNT / 2; ++jj)
+          stg[(4 * g + i) * kHalfCh + 16 * jj + r] = (uint16_t)f32_to_bf16(O[hc * (kHalfNT / 2) + jj][i] * mul[i]);
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+#pragma unroll
+      for (int it = 0; it < (16 * kHalfCh / 8 + 63) / 64; ++it) {
+        const int vi = lane + 64 * it;
+        if (vi < 16 * kHalfCh / 8) {
+          const int row = vi / (kHalfCh / 8), c8 = (vi % (kHalfCh / 8)) * 8;
+          const uint4 v = *reinterpret_cast<const uint4 *>(stg + row * kHalfCh + c8);
+          *reinterpret_cast<uint4 *>(dst + (int64_t)row * kD + hc * kHalfCh + c8) = v;
+        }
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+    }
+  };
+  if (a.nsplit == 1 && a.out_bf16 && kStaged) {
+    float inv[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) inv[i] = lsum[i] > 0.f ? 1.f / lsum[i] : 0.f;
+    store_bf16(reinterpret_cast<uint16_t *>(a.out) + (qrow * a.H + h0) * kD + cbase, inv);
+    if (a.lse && r == 0 && half == 0) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int hh = h0 + 4 * g + i;
+        a.lse[qrow * a.H + hh] = lsum[i] > 0.f ? (m2[i] + log2f(lsum[i])) * 0.69314718055994531f : -INFINITY;
+      }
+    }
+  } else if (a.nsplit != 1 && a.out_bf16 && kStaged) {
+    const float one[4] = {1.f, 1.f, 1.f, 1.f};
+    store_bf16(reinterpret_cast<uint16_t *>(a.ws_o) + ((qrow * a.nsplit + split) * a.H + h0) * kD + cbase, one);
+    if (r == 0 && half == 0) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int64_t pr = (qrow * a.nsplit + split) * a.H + h0 + 4 * g + i;
+        a.ws_ml[pr * 2 + 0] = m2[i];
+        a.ws_ml[pr * 2 + 1] = lsum[i];
+      }
+    }
+  } else if (a.nsplit == 1) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int hh = h0 + 4 * g + i;

@@ -635,11 +635,13 @@ __global__ __launch_bounds__(HG * 128) void attn_kernel(AttnArgs a) {
 // with M the largest m_s.  One thread per 8 channels of one (query, head):
 // 16-byte loads of bf16 partials (8-byte halves of fp32 ones), the split
 // weights formed once per thread, and the loads over splits issued together
-// (up to kMergeUnroll at a time).  Partials are fp32, or bf16 when the
+// (up to kU at a time).  Partials are fp32, or bf16 when the
 // result is bf16.
 constexpr int kMergeThreads = 256;
-constexpr int kMergeUnroll = 8;
-template <bool kBf16>
+// kU: splits whose loads go out together (8, or 16 / 32 for bf16 partials of
+// many splits, so that the HCA step's 29 splits take one memory round).
+// bf16 partials stay packed in registers until they are weighted.
+template <bool kBf16, int kU>
 __global__ __launch_bounds__(kMergeThreads) void attn_merge_kernel(const float *__restrict__ ws_o,
                                                                    const float *__restrict__ ws_ml, int nsplit, int H,
                                                                    int64_t n_items, void *out, float *lse) {
@@ -650,39 +652,31 @@ __global__ __launch_bounds__(kMergeThreads) void attn_merge_kernel(const float *
   const int c8 = (int)(item % kGroups) * 8;
   const int64_t qrow = qh / H, hh = qh % H;
   auto pr_of = [&](int s) { return (qrow * nsplit + s) * H + hh; };
-  // One round of loads for up to kMergeUnroll splits: every split's (m, l)
-  // and partial row are issued together and the maximum is formed from the
-  // loaded values (a separate pass for the maximum would wait on memory twice).
+  // One round of loads for up to kU splits: every split's (m, l) and partial
+  // row are issued together and the maximum is formed from the loaded values
+  // (a separate pass for the maximum would wait on memory twice).
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   float L = 0.f;
   float M = -INFINITY;
-  for (int s0 = 0; s0 < nsplit; s0 += kMergeUnroll) {
-    float2 ml[kMergeUnroll];
-    float v[kMergeUnroll][8];
+  for (int s0 = 0; s0 < nsplit; s0 += kU) {
+    float2 ml[kU];
+    uint4 raw[kBf16 ? kU : 2 * kU];
 #pragma unroll
-    for (int u = 0; u < kMergeUnroll; ++u) {
+    for (int u = 0; u < kU; ++u) {
       const int64_t pr = pr_of(min(s0 + u, nsplit - 1));
       ml[u] = *reinterpret_cast<const float2 *>(ws_ml + pr * 2);
       if (kBf16) {
-        const uint4 p = *reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(ws_o) + pr * kD + c8);
-        const uint32_t w4[4] = {p.x, p.y, p.z, p.w};
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          v[u][2 * j] = bf16_to_f32(w4[j] & 0xFFFFu);
-          v[u][2 * j + 1] = bf16_to_f32(w4[j] >> 16);
-        }
+        raw[u] = *reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(ws_o) + pr * kD + c8);
       } else {
-        const float4 p0 = *reinterpret_cast<const float4 *>(ws_o + pr * kD + c8);
-        const float4 p1 = *reinterpret_cast<const float4 *>(ws_o + pr * kD + c8 + 4);
-        v[u][0] = p0.x; v[u][1] = p0.y; v[u][2] = p0.z; v[u][3] = p0.w;
-        v[u][4] = p1.x; v[u][5] = p1.y; v[u][6] = p1.z; v[u][7] = p1.w;
+        raw[2 * u] = *reinterpret_cast<const uint4 *>(ws_o + pr * kD + c8);
+        raw[2 * u + 1] = *reinterpret_cast<const uint4 *>(ws_o + pr * kD + c8 + 4);
       }
     }
     // running maximum over the splits seen so far; earlier sums are rescaled
-    // when it moves (only with more than kMergeUnroll splits)
+    // when it moves (only with more than kU splits)
     float Mn = M;
 #pragma unroll
-    for (int u = 0; u < kMergeUnroll; ++u)
+    for (int u = 0; u < kU; ++u)
       if (s0 + u < nsplit) Mn = fmaxf(Mn, ml[u].x);
     if (Mn != -INFINITY) {
       const float r = M == -INFINITY ? 0.f : exp2f(M - Mn);
@@ -690,11 +684,25 @@ __global__ __launch_bounds__(kMergeThreads) void attn_merge_kernel(const float *
 #pragma unroll
       for (int j = 0; j < 8; ++j) acc[j] *= r;
 #pragma unroll
-      for (int u = 0; u < kMergeUnroll; ++u) {
+      for (int u = 0; u < kU; ++u) {
         const float wgt = (s0 + u < nsplit && ml[u].x != -INFINITY) ? exp2f(ml[u].x - Mn) : 0.f;
         L += wgt * (wgt != 0.f ? ml[u].y : 0.f);
+        float v[8];
+        if (kBf16) {
+          const uint32_t w4[4] = {raw[u].x, raw[u].y, raw[u].z, raw[u].w};
 #pragma unroll
-        for (int j = 0; j < 8; ++j) acc[j] = fmaf(wgt, v[u][j], acc[j]);
+          for (int j = 0; j < 4; ++j) {
+            v[2 * j] = bf16_to_f32(w4[j] & 0xFFFFu);
+            v[2 * j + 1] = bf16_to_f32(w4[j] >> 16);
+          }
+        } else {
+          const uint4 p0 = raw[kBf16 ? 0 : 2 * u], p1 = raw[kBf16 ? 0 : 2 * u + 1];
+          v[0] = __uint_as_float(p0.x); v[1] = __uint_as_float(p0.y); v[2] = __uint_as_float(p0.z);
+          v[3] = __uint_as_float(p0.w); v[4] = __uint_as_float(p1.x); v[5] = __uint_as_float(p1.y);
+          v[6] = __uint_as_float(p1.z); v[7] = __uint_as_float(p1.w);
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[j] = fmaf(wgt, v[j], acc[j]);
       }
       M = Mn;
     }
@@ -803,10 +811,14 @@ hipError_t launch_attention(const CacheView &c, const uint16_t *q, int H, const 
   if (e != hipSuccess || sh.nsplit == 1) return e;
   const int64_t n_items = (int64_t)c.B * Q * H * (kD / 8);
   const unsigned nb = (unsigned)((n_items + kMergeThreads - 1) / kMergeThreads);
-  if (out_bf16)
-    attn_merge_kernel<true><<<nb, kMergeThreads, 0, stream>>>(a.ws_o, a.ws_ml, sh.nsplit, H, n_items, out, lse);
+  if (out_bf16 && sh.nsplit > 16)
+    attn_merge_kernel<true, 32><<<nb, kMergeThreads, 0, stream>>>(a.ws_o, a.ws_ml, sh.nsplit, H, n_items, out, lse);
+  else if (out_bf16 && sh.nsplit > 8)
+    attn_merge_kernel<true, 16><<<nb, kMergeThreads, 0, stream>>>(a.ws_o, a.ws_ml, sh.nsplit, H, n_items, out, lse);
+  else if (out_bf16)
+    attn_merge_kernel<true, 8><<<nb, kMergeThreads, 0, stream>>>(a.ws_o, a.ws_ml, sh.nsplit, H, n_items, out, lse);
   else
-    attn_merge_kernel<false><<<nb, kMergeThreads, 0, stream>>>(a.ws_o, a.ws_ml, sh.nsplit, H, n_items, out, lse);
+    attn_merge_kernel<false, 8><<<nb, kMergeThreads, 0, stream>>>(a.ws_o, a.ws_ml, sh.nsplit, H, n_items, out, lse);
   return hipGetLastError();
 }
 

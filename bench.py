@@ -125,6 +125,9 @@ def main():
     ap.add_argument("--kernel-reps", type=int, default=64)
     ap.add_argument("--cpu-sample", type=int, default=32, help="sequences the oracle baseline runs (0 = skip)")
     ap.add_argument("--only-index", action="store_true", help="run only the fused append + indexer launches (for counter passes)")
+    ap.add_argument("--only", choices=["index", "topk", "attn"], default=None,
+                    help="run only this stage of the decode step (for counter passes; the step's inputs are "
+                         "prepared once by one eager step)")
     ap.add_argument("--prefill-reps", type=int, default=3, help="timed passes of the 64K prefill chunk (0 = skip)")
     ap.add_argument("--hca-steps", type=int, default=256, help="graph-timed HCA 1M decode steps (0 = skip)")
     ap.add_argument("--csa2-steps", type=int, default=64, help="graph-timed CSA2 two-layer 1M decode steps (0 = skip)")
@@ -135,6 +138,8 @@ def main():
     ap.add_argument("--replays", type=int, default=20, help="individually timed graph replays (>= 20)")
     ap.add_argument("--copy-calibration", action="store_true", help="run a plain device copy of known size")
     args = ap.parse_args()
+    if args.only_index:
+        args.only = "index"
 
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}): sequences are independent, so "
@@ -193,8 +198,14 @@ def main():
                         out_dtype=torch.bfloat16, ws=attn_ws, out=ly.out, lse=ly.lse)
 
     stages = [st_append, st_topk, st_attn]
-    if args.only_index:
-        stages = [st_append]
+    if args.only:
+        # one eager step per layer prepares the scores and selections the
+        # stage reads
+        for l in range(L):
+            for f in stages:
+                f(layers[l])
+        torch.cuda.synchronize()
+        stages = [{"index": st_append, "topk": st_topk, "attn": st_attn}[args.only]]
 
     def step(l):
         for f in stages:
@@ -276,7 +287,7 @@ def main():
     stage_us = {}
     names = {st_append: "compress+index_scores", st_compress: "compress", st_index: "index_scores", st_topk: "topk",
              st_attn: "sparse_attn"}
-    timed = stages if args.only_index else [st_append, st_compress, st_index, st_topk, st_attn]
+    timed = stages if args.only else [st_append, st_compress, st_index, st_topk, st_attn]
     for f in timed:
         g = capture(lambda f=f: [f(layers[i % L]) for i in range(R)])
         g.replay()
@@ -294,7 +305,7 @@ def main():
     # The same step with the window rows as FP8 planes (the window KV format
     # the pages state); reported beside the headline, which keeps bf16 rows.
     w8 = None
-    if not args.only_index:
+    if not args.only:
         g8 = capture(lambda: [(st_append(layers[l]), st_topk(layers[l]), st_attn_w8(layers[l])) for l in range(L)])
         g8.replay()
         torch.cuda.synchronize()
@@ -327,7 +338,7 @@ def main():
 
     by = step_bytes(w)
     # the dominant kernel: the fused append + indexer launch
-    idx_us = stage_us["compress+index_scores"]
+    idx_us = stage_us.get("compress+index_scores", float("nan"))
     dom_bytes = by["index"] + by["compress"]
     achieved = dom_bytes / (idx_us * 1e-6) / 1e9
     traffic = None
@@ -366,28 +377,28 @@ def main():
                      "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic, "bytes_per_launch": dom_bytes,
                      "avg_launch_us": round(idx_us, 3)},
     }
-    if args.only_index:
+    if args.only:
         result["value"] = None
 
-    if args.prefill_reps > 0 and not args.only_index:
+    if args.prefill_reps > 0 and not args.only:
         del layers, scores_ws, topk_ws, attn_ws
         torch.cuda.empty_cache()
         result["prefill"] = prefill_leg(args.prefill_reps, oracle=args.cpu_sample > 0)
 
-    if args.hca_steps > 0 and not args.only_index:
+    if args.hca_steps > 0 and not args.only:
         torch.cuda.empty_cache()
         result["hca"] = hca_leg(K=args.hca_steps)
-    if args.csa2_steps > 0 and not args.only_index:
+    if args.csa2_steps > 0 and not args.only:
         torch.cuda.empty_cache()
         result["csa2"] = csa2_leg(K=args.csa2_steps)
-    if args.hier_steps > 0 and not args.only_index:
+    if args.hier_steps > 0 and not args.only:
         torch.cuda.empty_cache()
         result["csa2_hier"] = hier_leg(K=args.hier_steps)
-    if args.stack_steps > 0 and not args.only_index:
+    if args.stack_steps > 0 and not args.only:
         torch.cuda.empty_cache()
         result["csa2_stack"] = stack_leg(K=args.stack_steps)
 
-    if args.cpu_sample > 0 and not args.only_index:
+    if args.cpu_sample > 0 and not args.only:
         result["cpu_baseline"] = cpu_baseline(w, args.cpu_sample)
 
     print(json.dumps(result), flush=True)

@@ -35,4 +35,10 @@ from .ops import (  # noqa: F401
     WS_INDEX_TOPK,
     WS_SPARSE_ATTN,
     WS_TOPK,
+    FLAG_CAND,
+    FLAG_ENTRIES,
+    FLAG_IDX_ORDER,
+    FLAG_IDX_RANGE,
+    FLAG_WINDOW,
+    read_device_flags,
 )

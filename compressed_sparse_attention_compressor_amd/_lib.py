@@ -94,6 +94,7 @@ _SIGS = {
     "csa_status_str": (ctypes.c_char_p, [c_int]),
     "csa_version": (c_int, []),
     "csa_last_hip_error": (c_int, []),
+    "csa_read_device_flags": (c_int, [c_void_p, ctypes.POINTER(ctypes.c_uint32)]),
 }
 
 _lib = None

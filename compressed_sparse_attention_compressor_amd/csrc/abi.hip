@@ -2,13 +2,60 @@
 // No HIP call is made before every check has passed.
 #include <math.h>
 
+#include <atomic>
+#include <mutex>
+
 #include "../../include/csa.h"
 #include "csa_device.hpp"
 #include "csa_internal.hpp"
 
+// The device word of data-dependent faults (CSA_FLAG_* bits), one per GPU,
+// and the word csa_read_device_flags exchanges it into.
+__device__ uint32_t g_fault_word;
+__device__ uint32_t g_fault_taken;
+
+__global__ void take_fault_word_kernel(uint32_t *word, uint32_t *taken) { *taken = atomicExch(word, 0u); }
+
 namespace {
 
 thread_local int g_last_hip_error = 0;
+
+constexpr int kMaxDevices = 64;
+std::atomic<uint32_t *> g_word_ptr[kMaxDevices];
+std::atomic<uint32_t *> g_taken_ptr[kMaxDevices];
+std::mutex g_word_mu;
+
+// Device addresses of the two words on the current device, looked up once
+// per device (the host-side names are not device addresses).
+hipError_t fault_words(uint32_t **word, uint32_t **taken) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  uint32_t *w = g_word_ptr[dev].load(std::memory_order_acquire);
+  if (!w) {
+    std::lock_guard<std::mutex> lock(g_word_mu);
+    w = g_word_ptr[dev].load(std::memory_order_acquire);
+    if (!w) {
+      uint32_t *t = nullptr;
+      e = hipGetSymbolAddress(reinterpret_cast<void **>(&w), HIP_SYMBOL(g_fault_word));
+      if (e == hipSuccess) e = hipGetSymbolAddress(reinterpret_cast<void **>(&t), HIP_SYMBOL(g_fault_taken));
+      if (e != hipSuccess) return e;
+      g_taken_ptr[dev].store(t, std::memory_order_release);
+      g_word_ptr[dev].store(w, std::memory_order_release);
+    }
+  }
+  *word = w;
+  if (taken) *taken = g_taken_ptr[dev].load(std::memory_order_acquire);
+  return hipSuccess;
+}
+
+// The fault word for the kernels (null when it cannot be found: faults then
+// go unrecorded, results are unchanged).
+uint32_t *fault_word() {
+  uint32_t *w = nullptr;
+  return fault_words(&w, nullptr) == hipSuccess ? w : nullptr;
+}
 
 constexpr int kMaxH = 128;
 constexpr int kMaxHI = 64;
@@ -53,6 +100,7 @@ csa::CacheView view_of(const csa_cache_t *c) {
   v.N_cap = c->N_cap;
   v.d_idx = c->d_idx;
   v.m = c->m;
+  v.flags = fault_word();
   return v;
 }
 
@@ -89,7 +137,22 @@ int check_attn_common(const csa_cache_t *cache, const uint16_t *q, int H, const 
 
 extern "C" {
 
-int csa_version(void) { return 10000; }
+int csa_version(void) { return 10100; }
+
+int csa_read_device_flags(hipStream_t stream, uint32_t *flags) {
+  if (!flags) return CSA_ERR_NULL;
+  uint32_t *word = nullptr, *taken = nullptr;
+  hipError_t e = fault_words(&word, &taken);
+  if (e != hipSuccess) return status_of(e);
+  take_fault_word_kernel<<<1, 1, 0, stream>>>(word, taken);
+  e = hipGetLastError();
+  uint32_t v = 0;
+  if (e == hipSuccess) e = hipMemcpyAsync(&v, taken, sizeof(v), hipMemcpyDeviceToHost, stream);
+  if (e == hipSuccess) e = hipStreamSynchronize(stream);
+  if (e != hipSuccess) return status_of(e);
+  *flags = v;
+  return CSA_OK;
+}
 
 int csa_last_hip_error(void) { return g_last_hip_error; }
 

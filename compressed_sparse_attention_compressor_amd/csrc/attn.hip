@@ -9,10 +9,8 @@
 // Work split: one workgroup per (query, key-range split), a pair of waves
 // per 16 query heads (heads are the MFMA M dimension, so a key is decoded
 // once per workgroup and shared by every head); each wave of a pair owns
-// half of the 576 output channels.  The logits either come from both waves
-// computing the full Q K^T (kDupQK: no exchange, twice the products) or
-// from each wave's half of the channels, the halves swapped through LDS.
-// A query's key slots are its selected
+// half of the 576 output channels and computes Q K^T over that half; the
+// halves are swapped through LDS.  A query's key slots are its selected
 // entries (padded to a multiple of the chunk size) followed by its window
 // rows, so every chunk of 32 slots holds one kind of row and is fetched
 // with the loads of that kind only.  Per chunk:
@@ -78,6 +76,7 @@ struct AttnArgs {
   float *ws_o;
   float *ws_ml;
   int nsplit, per_split;
+  uint32_t *flags;             // device fault word (may be null)
 };
 
 // Per-thread share of one chunk's raw bytes for NT threads.
@@ -275,16 +274,16 @@ __device__ __forceinline__ void store_window(uint16_t *K, const int *src, int t0
   }
 }
 
-template <int HG, bool kSplitP, bool kDense, bool kDupQK, bool kW8>
+template <int HG, bool kSplitP, bool kDense, bool kW8>
 __global__ __launch_bounds__(HG * 128) void attn_kernel(AttnArgs a) {
   constexpr int NT = HG * 128;
-  constexpr int kQSteps = kDupQK ? kKSteps : kKSteps / 2;  // channel steps of this wave's Q K^T
+  constexpr int kQSteps = kKSteps / 2;  // channel steps of this wave's Q K^T
   using CS = ChunkShare<NT>;
   // Key-major bf16 tiles of the chunk (double buffered); the P V operand is
   // read transposed from the same tile with ds_read_b64_tr_b16.
   __shared__ __attribute__((aligned(16))) uint16_t Kl[2][kKC * kKRow];
   __shared__ __attribute__((aligned(16))) uint16_t Pl[2 * HG][kSplitP ? 2 : 1][16 * kPRow];
-  __shared__ __attribute__((aligned(16))) float Sx[kDupQK ? 1 : 2 * HG][2 * 4 * 64];
+  __shared__ __attribute__((aligned(16))) float Sx[2 * HG][2 * 4 * 64];
   // Slot lists of three consecutive chunks: the list of chunk c + 1 is
   // written while a slower wave may still read that of chunk c.
   __shared__ int src_s[3][kKC];
@@ -299,17 +298,21 @@ __global__ __launch_bounds__(HG * 128) void attn_kernel(AttnArgs a) {
   const int64_t qrow = (int64_t)b * a.Q + q;
   const int s_begin = split * a.per_split;
   // A slot's index load and its publication are split so that other loads
-  // can be issued in between.
+  // can be issued in between.  The index of the slot before is loaded with
+  // it (same cache lines) for the ascending-order check.
   auto fetch_slot = [&](int c0) __attribute__((always_inline)) {
-    // unconditional load from a clamped address (no wait on the query's
+    // unconditional loads from clamped addresses (no wait on the query's
     // position); the slot's validity is applied when it is published
     const int slot = c0 + (tid & (kKC - 1));
-    if (kDense || a.k <= 0) return slot;
-    return a.idx[qrow * a.k + min(slot, a.k - 1)];
+    if (kDense || a.k <= 0) return int2{slot, slot - 1};
+    const int sc = min(slot, a.k - 1);
+    const int32_t *ip = a.idx + qrow * a.k;
+    return int2{ip[sc], ip[max(sc - 1, 0)]};
   };
-  const int j_first = fetch_slot(s_begin);
+  const int2 j_first = fetch_slot(s_begin);
   const int p = a.q_pos[qrow];
-  const int nE = min(a.n_entries[b], a.N_cap);
+  const int nE_raw = a.n_entries[b];
+  const int nE = min(nE_raw, a.N_cap);
   const int V = p >= 0 ? max(0, min(nE, (p + 1) / a.m)) : 0;
   const int n_main = kDense ? V : a.k;
   const int n_main_pad = (n_main + kKC - 1) / kKC * kKC;
@@ -322,16 +325,31 @@ __global__ __launch_bounds__(HG * 128) void attn_kernel(AttnArgs a) {
   }
   const int n_slots = n_main_pad + n_swa;
   const int s_end = min(n_slots, s_begin + a.per_split);
+  if (tid == 0 && split == 0) {
+    // per (sequence, query): an entry count outside [0, N_cap], window rows
+    // that the buffer does not hold (they are skipped)
+    uint32_t f = (nE_raw < 0 || nE_raw > a.N_cap) ? kFaultEntries : 0u;
+    if (a.n_win > 0 && p >= 0 && (swa0 > max(0, p - a.n_win + 1) || p > swa0 + a.S - 1)) f |= kFaultWindow;
+    if (f) raise_fault(a.flags, f);
+  }
 
   // Slot -> source row: an entry index (entry chunks) or a row of the window
-  // buffer (window chunks); -1 = nothing.
-  auto publish_slot = [&](int c0, int j, int sb) __attribute__((always_inline)) {
+  // buffer (window chunks); -1 = nothing.  Selected indices outside
+  // [-1, V) and neighbours that are not strictly ascending raise fault bits
+  // (the former are skipped, the latter attended as given).
+  auto publish_slot = [&](int c0, int2 jj, int sb) __attribute__((always_inline)) {
     if (tid < kKC) {
       const int slot = c0 + tid;
+      const int j = jj.x;
       int src = -1;
       if (slot < s_end) {
         if (slot < n_main_pad) {
           if (slot < n_main && j >= 0 && j < V) src = j;
+          if (!kDense && slot < n_main) {
+            uint32_t f = (j < -1 || j >= V) ? kFaultIdxRange : 0u;
+            if (slot > 0 && j >= 0 && jj.y >= 0 && j <= jj.y) f |= kFaultIdxOrder;
+            if (f) raise_fault(a.flags, f);
+          }
         } else {
           src = win_lo + (slot - n_main_pad) - swa0;
         }
@@ -352,8 +370,8 @@ __global__ __launch_bounds__(HG * 128) void attn_kernel(AttnArgs a) {
 
   v8bf Qf[kQSteps];
   if (s_begin < s_end) {
-    const int j0 = j_first;  // issued before the query loads
-    const uint16_t *qp = a.q + (qrow * a.H + hg * 16 + r) * kD + (kDupQK ? 0 : cbase) + 8 * g;
+    const int2 j0 = j_first;  // issued before the query loads
+    const uint16_t *qp = a.q + (qrow * a.H + hg * 16 + r) * kD + cbase + 8 * g;
 #pragma unroll
     for (int kk = 0; kk < kQSteps; ++kk) Qf[kk] = *reinterpret_cast<const v8bf *>(qp + 32 * kk);
     publish_slot(s_begin, j0, 0);
@@ -365,7 +383,7 @@ __global__ __launch_bounds__(HG * 128) void attn_kernel(AttnArgs a) {
     S0 = v4f{0.f, 0.f, 0.f, 0.f};
     S1 = v4f{0.f, 0.f, 0.f, 0.f};
     {
-      const uint16_t *k0 = K + r * kKRow + (kDupQK ? 0 : cbase) + 8 * g;
+      const uint16_t *k0 = K + r * kKRow + cbase + 8 * g;
       const uint16_t *k1 = k0 + 16 * kKRow;
 #pragma unroll
       for (int kk = 0; kk < kQSteps; ++kk) {
@@ -378,23 +396,21 @@ __global__ __launch_bounds__(HG * 128) void attn_kernel(AttnArgs a) {
   };
   // Adds the partner wave's half of the channels (one LDS-only barrier).
   auto exchange = [&](v4f &S0, v4f &S1) __attribute__((always_inline)) {
-    if (!kDupQK) {
-      // the partner's half of the channels, added in a fixed order of the
-      // halves so that both waves of the pair agree bit for bit
-      float *sx = &Sx[kDupQK ? 0 : wave][0];
+    // the partner's half of the channels, added in a fixed order of the
+    // halves so that both waves of the pair agree bit for bit
+    float *sx = &Sx[wave][0];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        sx[i * 64 + lane] = S0[i];
-        sx[(4 + i) * 64 + lane] = S1[i];
-      }
-      lds_barrier();
-      const float *so = &Sx[kDupQK ? 0 : wave ^ 1][0];
+    for (int i = 0; i < 4; ++i) {
+      sx[i * 64 + lane] = S0[i];
+      sx[(4 + i) * 64 + lane] = S1[i];
+    }
+    lds_barrier();
+    const float *so = &Sx[wave ^ 1][0];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float o0 = so[i * 64 + lane], o1 = so[(4 + i) * 64 + lane];
-        S0[i] = half == 0 ? S0[i] + o0 : o0 + S0[i];
-        S1[i] = half == 0 ? S1[i] + o1 : o1 + S1[i];
-      }
+    for (int i = 0; i < 4; ++i) {
+      const float o0 = so[i * 64 + lane], o1 = so[(4 + i) * 64 + lane];
+      S0[i] = half == 0 ? S0[i] + o0 : o0 + S0[i];
+      S1[i] = half == 0 ? S1[i] + o1 : o1 + S1[i];
     }
   };
   // Online softmax of one chunk's logits, then O += P V with the chunk's
@@ -507,7 +523,7 @@ __global__ __launch_bounds__(HG * 128) void attn_kernel(AttnArgs a) {
     for (int c0 = c_lo; c0 < c_hi; c0 += kKC, ++ci) {
       uint16_t *K = Kl[ci & 1];
       const int sb = ci % 3, sn = (ci + 1) % 3;
-      const int jn = kWin ? -1 : fetch_slot(c0 + kKC);
+      const int2 jn = kWin ? int2{-1, -1} : fetch_slot(c0 + kKC);
       if (CS::kAhead) {
         st(K, sb);
       } else if (kWin16) {
@@ -742,20 +758,16 @@ size_t attn_workspace_bytes(int B, int Q, int H, int n_main, int n_win) {
   return (size_t)B * Q * s.nsplit * H * (kD + 2) * sizeof(float);
 }
 
-#ifndef CSA_ATTN_DUP_QK
-#define CSA_ATTN_DUP_QK 0
-#endif
 template <int HG, bool kSplitP>
 static void launch_hg(const AttnArgs &a, bool dense, bool w8, dim3 grid, hipStream_t stream) {
-  constexpr bool kDup = CSA_ATTN_DUP_QK != 0;
   if (dense && w8)
-    attn_kernel<HG, kSplitP, true, kDup, true><<<grid, HG * 128, 0, stream>>>(a);
+    attn_kernel<HG, kSplitP, true, true><<<grid, HG * 128, 0, stream>>>(a);
   else if (dense)
-    attn_kernel<HG, kSplitP, true, kDup, false><<<grid, HG * 128, 0, stream>>>(a);
+    attn_kernel<HG, kSplitP, true, false><<<grid, HG * 128, 0, stream>>>(a);
   else if (w8)
-    attn_kernel<HG, kSplitP, false, kDup, true><<<grid, HG * 128, 0, stream>>>(a);
+    attn_kernel<HG, kSplitP, false, true><<<grid, HG * 128, 0, stream>>>(a);
   else
-    attn_kernel<HG, kSplitP, false, kDup, false><<<grid, HG * 128, 0, stream>>>(a);
+    attn_kernel<HG, kSplitP, false, false><<<grid, HG * 128, 0, stream>>>(a);
 }
 
 template <bool kSplitP>
@@ -799,6 +811,7 @@ hipError_t launch_attention(const CacheView &c, const uint16_t *q, int H, const 
   a.out_bf16 = out_bf16 ? 1 : 0;
   a.nsplit = sh.nsplit;
   a.per_split = sh.per_split;
+  a.flags = c.flags;
   const size_t po = (size_t)c.B * Q * sh.nsplit * H * kD;
   a.ws_o = reinterpret_cast<float *>(ws);
   a.ws_ml = a.ws_o ? a.ws_o + po : nullptr;

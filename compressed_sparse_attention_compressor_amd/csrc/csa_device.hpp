@@ -185,6 +185,19 @@ __device__ __forceinline__ uint32_t encode_pair(float v0, float v1, uint32_t &sb
   return e2m1_encode(v0, inv) | (e2m1_encode(v1, inv) << 4);
 }
 
+// Data-dependent faults: skipped on the device, recorded as bits of a device
+// word that csa_read_device_flags returns (the public CSA_FLAG_* values).
+constexpr uint32_t kFaultIdxRange = 1u;   // a selected index outside [-1, visible)
+constexpr uint32_t kFaultIdxOrder = 2u;   // neighbouring selected indices not strictly ascending
+constexpr uint32_t kFaultWindow = 4u;     // window rows of a query missing from the window buffer
+constexpr uint32_t kFaultCand = 8u;       // a candidate outside [-1, visible) or not strictly ascending
+constexpr uint32_t kFaultEntries = 16u;   // an entry count outside [0, N_cap]
+
+// Sets fault bits with a global (vector-memory) atomic; the word may be absent.
+__device__ __forceinline__ void raise_fault(uint32_t *flags, uint32_t bits) {
+  if (flags) atomicOr(flags, bits);
+}
+
 // Marks a workspace score slot that holds no candidate.
 constexpr uint32_t kNoScoreBits = 0xFFFFFFFFu;
 

@@ -16,6 +16,7 @@ struct CacheView {
   uint8_t *iscale;
   const int32_t *n_entries;
   int B, N_cap, d_idx, m;
+  uint32_t *flags;  // device word of data-dependent faults (kFault* bits); may be null
 };
 
 hipError_t launch_compress(const uint16_t *x, int64_t x_stride_b, const uint16_t *z, int64_t z_stride_b,

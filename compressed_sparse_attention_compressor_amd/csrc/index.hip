@@ -46,7 +46,7 @@ __device__ __forceinline__ void index_body(
     const uint8_t *__restrict__ ikey, const uint8_t *__restrict__ iscale, const int32_t *__restrict__ n_entries,
     int N_cap, int d_idx, int m, const uint8_t *__restrict__ q_idx, const float *__restrict__ w_idx, int H_I,
     const int32_t *__restrict__ q_pos, int Q, const int32_t *__restrict__ cand, int C, float *__restrict__ scores,
-    int Ns, int bx, int by, int bz, int skip) {
+    int Ns, int bx, int by, int bz, int skip, uint32_t *flags) {
   // Indexer queries of this workgroup (QB queries x 16*HT heads x d_idx bytes),
   // staged once so that the waves read their MFMA fragments from LDS.
   __shared__ __attribute__((aligned(16))) uint8_t qs[QB * HT * 16 * 128];
@@ -134,12 +134,18 @@ __device__ __forceinline__ void index_body(
   v4i kv[kIters];
   int sbv[kIters];
   int ent[kIters];
+  int prv[kCand ? kIters : 1];  // the candidate before each slot (order check)
   bool use[kIters];
 #pragma unroll
   for (int it = 0; it < kIters; ++it) {
     const int slot = base + it * 16 + r;
     int e = slot;
-    if (kCand) e = cand[((int64_t)b * Q + q0) * C + min(slot, C - 1)];
+    if (kCand) {
+      const int32_t *cp = cand + ((int64_t)b * Q + q0) * C;
+      const int sc = min(slot, C - 1);
+      e = cp[sc];
+      prv[it] = (slot > 0 && slot < C) ? cp[max(sc - 1, 0)] : -1;
+    }
     ent[it] = (kCand && slot >= C) ? -1 : e;
     const bool inb = kCand ? (ent[it] >= 0 && ent[it] < N_cap) : (slot < N_cap);
     use[it] = inb && g < kb;
@@ -188,7 +194,9 @@ __device__ __forceinline__ void index_body(
     }
 
   // 4. Visibility of this workgroup's queries (uniform loads).
-  const int nE = min(n_entries[b], N_cap);
+  const int nE_raw = n_entries[b];
+  const int nE = min(nE_raw, N_cap);
+  if (threadIdx.x == 0 && bx == 0 && by == 0 && (nE_raw < 0 || nE_raw > N_cap)) raise_fault(flags, kFaultEntries);
   int vis[QB];
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
@@ -230,6 +238,16 @@ __device__ __forceinline__ void index_body(
     if (kCand) {
       const int t0 = ent[grp * 4], t1 = ent[grp * 4 + 1], t2 = ent[grp * 4 + 2], t3 = ent[grp * 4 + 3];
       e_l = g == 0 ? t0 : g == 1 ? t1 : g == 2 ? t2 : t3;
+      // every lane group loaded every tile's candidates: lane (g, r) checks
+      // its own tile g, slot r (a candidate outside [-1, visible), or a
+      // neighbour pair that is not strictly ascending: skipped / as given)
+      if (slot < C) {
+        const int u0 = prv[grp * 4], u1 = prv[grp * 4 + 1], u2 = prv[grp * 4 + 2], u3 = prv[grp * 4 + 3];
+        const int pe = g == 0 ? u0 : g == 1 ? u1 : g == 2 ? u2 : u3;
+        uint32_t f = (e_l < -1 || e_l >= vis[0]) ? kFaultCand : 0u;
+        if (e_l >= 0 && pe >= 0 && e_l <= pe) f |= kFaultCand;
+        if (f) raise_fault(flags, f);
+      }
     }
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
@@ -252,9 +270,9 @@ __global__ __launch_bounds__(kIdxThreads) void index_scores_kernel(
     const uint8_t *__restrict__ ikey, const uint8_t *__restrict__ iscale, const int32_t *__restrict__ n_entries,
     int N_cap, int d_idx, int m, const uint8_t *__restrict__ q_idx, const float *__restrict__ w_idx, int H_I,
     const int32_t *__restrict__ q_pos, int Q, const int32_t *__restrict__ cand, int C, float *__restrict__ scores,
-    int Ns) {
+    int Ns, uint32_t *flags) {
   index_body<HT, QB, kCand>(ikey, iscale, n_entries, N_cap, d_idx, m, q_idx, w_idx, H_I, q_pos, Q, cand, C, scores, Ns,
-                            blockIdx.x, blockIdx.y, blockIdx.z, -1);
+                            blockIdx.x, blockIdx.y, blockIdx.z, -1, flags);
 }
 
 // ---------------------------------------------------------------------------
@@ -508,7 +526,7 @@ template <int HT, bool kGateFull>
 __global__ __launch_bounds__(kIdxThreads, HT >= 4 ? 4 : 5) void append_index_kernel(
     AppendArgs ap, uint8_t *__restrict__ ikey, uint8_t *__restrict__ iscale, const int32_t *__restrict__ n_entries,
     int N_cap, int d_idx, const uint8_t *__restrict__ q_idx, const float *__restrict__ w_idx, int H_I,
-    const int32_t *__restrict__ q_pos, int Q, float *__restrict__ scores, int B, int tiles) {
+    const int32_t *__restrict__ q_pos, int Q, float *__restrict__ scores, int B, int tiles, uint32_t *flags) {
   const int w = blockIdx.x;
   if (w < B) {
     append_and_score<HT, kGateFull>(ap, ikey, iscale, n_entries, N_cap, d_idx, q_idx, w_idx, H_I, q_pos, Q, scores,
@@ -517,7 +535,7 @@ __global__ __launch_bounds__(kIdxThreads, HT >= 4 ? 4 : 5) void append_index_ker
   }
   const int t = w - B;
   index_body<HT, 1, false>(ikey, iscale, n_entries, N_cap, d_idx, ap.m, q_idx, w_idx, H_I, q_pos, Q, nullptr, 0,
-                           scores, N_cap, t % tiles, 0, t / tiles, ap.entry);
+                           scores, N_cap, t % tiles, 0, t / tiles, ap.entry, flags);
 }
 
 template <int HT>
@@ -528,11 +546,11 @@ static void launch_append(const AppendArgs &ap, bool gate_full, const CacheView 
   if (gate_full)
     append_index_kernel<HT, true><<<grid, kIdxThreads, 0, stream>>>(ap, c.ikey, c.iscale, c.n_entries, c.N_cap,
                                                                     c.d_idx, q_idx, w_idx, H_I, q_pos, 1, scores,
-                                                                    c.B, tiles);
+                                                                    c.B, tiles, c.flags);
   else
     append_index_kernel<HT, false><<<grid, kIdxThreads, 0, stream>>>(ap, c.ikey, c.iscale, c.n_entries, c.N_cap,
                                                                      c.d_idx, q_idx, w_idx, H_I, q_pos, 1, scores,
-                                                                     c.B, tiles);
+                                                                     c.B, tiles, c.flags);
 }
 
 bool append_index_fusable(int m, int64_t T, int Q, int G, const uint16_t *w_ik, int B) {
@@ -559,7 +577,7 @@ template <int HT, int QB, bool kCand>
 static void launch_idx(dim3 grid, hipStream_t stream, const CacheView &c, const uint8_t *q_idx, const float *w_idx,
                        int H_I, const int32_t *q_pos, int Q, const int32_t *cand, int C, float *scores, int Ns) {
   index_scores_kernel<HT, QB, kCand><<<grid, kIdxThreads, 0, stream>>>(
-      c.ikey, c.iscale, c.n_entries, c.N_cap, c.d_idx, c.m, q_idx, w_idx, H_I, q_pos, Q, cand, C, scores, Ns);
+      c.ikey, c.iscale, c.n_entries, c.N_cap, c.d_idx, c.m, q_idx, w_idx, H_I, q_pos, Q, cand, C, scores, Ns, c.flags);
 }
 
 // ---------------------------------------------------------------------------
@@ -591,7 +609,8 @@ template <int HT, int DI>
 __global__ __launch_bounds__(kPfWaves * 64) void index_prefill_kernel(
     const uint8_t *__restrict__ ikey, const uint8_t *__restrict__ iscale, const int32_t *__restrict__ n_entries,
     int N_cap, int m, const uint8_t *__restrict__ q_idx, const float *__restrict__ w_idx, int H_I,
-    const int32_t *__restrict__ q_pos, int Q, float *__restrict__ scores, int n_qblk, int n_chunk) {
+    const int32_t *__restrict__ q_pos, int Q, float *__restrict__ scores, int n_qblk, int n_chunk,
+    uint32_t *flags) {
   constexpr int QW = 8 / HT;  // queries per wave
   constexpr int d_idx = DI;
   // Workgroup i runs on XCD i % 8: the chunks of one query block follow each
@@ -612,7 +631,9 @@ __global__ __launch_bounds__(kPfWaves * 64) void index_prefill_kernel(
   // Loads below are unconditional, from clamped addresses, and masked with
   // bit operations: a load under a condition (even a uniform one) is moved
   // into a branch that waits for it before the next load is issued.
-  const int nE = min(n_entries[b], N_cap);
+  const int nE_raw = n_entries[b];
+  const int nE = min(nE_raw, N_cap);
+  if (L == 0 && threadIdx.x == 0 && (nE_raw < 0 || nE_raw > N_cap)) raise_fault(flags, kFaultEntries);
   int pos[QW];
 #pragma unroll
   for (int qw = 0; qw < QW; ++qw) pos[qw] = q_pos[(int64_t)b * Q + min(q0 + qw, Q - 1)];
@@ -739,10 +760,10 @@ static void launch_prefill(const CacheView &c, const uint8_t *q_idx, const float
   dim3 grid(((n_qblk + 7) / 8) * 8 * n_chunk, c.B);
   if (c.d_idx == 128)
     index_prefill_kernel<HT, 128><<<grid, kPfWaves * 64, 0, stream>>>(
-        c.ikey, c.iscale, c.n_entries, c.N_cap, c.m, q_idx, w_idx, H_I, q_pos, Q, scores, n_qblk, n_chunk);
+        c.ikey, c.iscale, c.n_entries, c.N_cap, c.m, q_idx, w_idx, H_I, q_pos, Q, scores, n_qblk, n_chunk, c.flags);
   else
     index_prefill_kernel<HT, 64><<<grid, kPfWaves * 64, 0, stream>>>(
-        c.ikey, c.iscale, c.n_entries, c.N_cap, c.m, q_idx, w_idx, H_I, q_pos, Q, scores, n_qblk, n_chunk);
+        c.ikey, c.iscale, c.n_entries, c.N_cap, c.m, q_idx, w_idx, H_I, q_pos, Q, scores, n_qblk, n_chunk, c.flags);
 }
 
 template <int HT>

@@ -339,3 +339,18 @@ def hca_dense_attn_w8(cache: Cache, q, q_pos, swa8, swa_pos0, n_win, scale, out_
                                   OUT_BF16 if out_dtype == torch.bfloat16 else OUT_F32, _ptr(out), _ptr(lse),
                                   _ptr(ws), wsb, _stream()), "hca_dense_attn_w8")
     return out, lse
+
+
+FLAG_IDX_RANGE = 1
+FLAG_IDX_ORDER = 2
+FLAG_WINDOW = 4
+FLAG_CAND = 8
+FLAG_ENTRIES = 16
+
+
+def read_device_flags() -> int:
+    """Reads and clears the current GPU's fault word (CSA_FLAG_* bits) on the
+    current stream; waits for that stream."""
+    v = ctypes.c_uint32(0)
+    check(lib().csa_read_device_flags(_stream(), ctypes.byref(v)), "csa_read_device_flags")
+    return int(v.value)

@@ -28,7 +28,11 @@
  *   rows at positions max(0, p - n_win + 1, swa_pos0[b]) .. p that the
  *   window buffer holds.
  * - Data-dependent problems (an index outside the visible range, a window
- *   row the buffer does not hold) are skipped on the device, never trapped.
+ *   row the buffer does not hold, ...) are skipped on the device, never
+ *   trapped, and recorded as bits of a per-GPU device word that
+ *   csa_read_device_flags returns (see there).
+ * - The calls keep no host state between calls except, per GPU, the device
+ *   address of that fault word, looked up on the first call on the GPU.
  */
 #ifndef CSA_H_
 #define CSA_H_
@@ -177,7 +181,10 @@ int csa_index_pool(const csa_cache_t *cache, const float *scores, const int32_t 
  * applied to the rope channels.
  *
  *   q        bf16 [B][Q][H][576]         q_pos int32 [B][Q]
- *   idx      int32 [B][Q][k]; -1 and entries not visible at q_pos are skipped
+ *   idx      int32 [B][Q][k]; -1 and entries not visible at q_pos are skipped;
+ *            a repeated index is attended once per occurrence (the list is
+ *            expected ascending, as csa_index_topk writes it, but order does
+ *            not change the result)
  *   swa      bf16 [B][S][576] raw rows, row r of sequence b = position swa_pos0[b] + r
  *   swa_pos0 int32 [B]                   n_win >= 0 (0 = no window branch)
  *   out      [B][Q][H][576] fp32 or bf16 (out_dtype)
@@ -299,6 +306,36 @@ const char *csa_status_str(int status);
 int csa_version(void);
 /* hipError_t of the last CSA_ERR_HIP on this host thread. */
 int csa_last_hip_error(void);
+
+/* Data-dependent faults seen on the device ([V4] Fig. 3 fixes what is
+ * attended: the selected entries a query can see plus its window rows;
+ * inputs outside that are skipped, never trapped, and leave a bit here).
+ * Kernels OR these bits into one word per GPU with vector-memory atomics:
+ *   CSA_FLAG_IDX_RANGE  csa_sparse_attn*: a selected index outside
+ *                       [-1, visible entries) (skipped; -1 is padding)
+ *   CSA_FLAG_IDX_ORDER  csa_sparse_attn*: two neighbouring selected indices
+ *                       (both >= 0) not strictly ascending, e.g. a repeat
+ *                       (attended as given, once per occurrence)
+ *   CSA_FLAG_WINDOW     attention: a query's window positions
+ *                       max(0, p - n_win + 1) .. p not all held by the window
+ *                       buffer (the missing rows are skipped)
+ *   CSA_FLAG_CAND       indexer with `cand`: a candidate outside
+ *                       [-1, visible entries) (skipped), or two neighbouring
+ *                       candidates (both >= 0) not strictly ascending
+ *   CSA_FLAG_ENTRIES    n_entries[b] outside [0, N_cap] (clamped)
+ * csa_read_device_flags enqueues, on `stream`, an atomic exchange of the
+ * current GPU's word with 0, copies the old value to *flags (host memory)
+ * and waits for the stream: unlike every other call it synchronises.  Bits
+ * set by work still running on other streams are reported by a later read.
+ * Returns CSA_ERR_NULL for a null `flags`, CSA_ERR_HIP on a HIP failure. */
+enum {
+  CSA_FLAG_IDX_RANGE = 1,
+  CSA_FLAG_IDX_ORDER = 2,
+  CSA_FLAG_WINDOW = 4,
+  CSA_FLAG_CAND = 8,
+  CSA_FLAG_ENTRIES = 16
+};
+int csa_read_device_flags(hipStream_t stream, uint32_t *flags);
 
 #ifdef __cplusplus
 }

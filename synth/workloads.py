@@ -132,21 +132,64 @@ def as_u16(t: torch.Tensor) -> np.ndarray:
     return t.detach().cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
 
 
-def synthetic_cache(w: Workload, device="cpu", N_cap=None, seq0=0, nseq=None):
+def synthetic_cache(w: Workload, device="cpu", N_cap=None, seq0=0, nseq=None, scales="narrow", rope_zero=False):
     """Cache planes drawn directly (for checking the stages after the compressor
-    at full size): uniform E2M1 code bytes, E8M0 scales in 124..127 (values up
-    to 6 in magnitude, like encoded N(0,1) data), bf16 N(0,1) rope channels."""
+    at full size): uniform E2M1 code bytes, bf16 N(0,1) rope channels and
+    E8M0 scale bytes chosen by ``scales``:
+
+    * "narrow": 124..127 (values up to 6 in magnitude, like encoded N(0,1) data);
+    * "wide": per 32-channel block, one of five kinds picked by the block's
+      hash: a zero block (scale byte 0 and every code 0, as the encoder
+      writes for an all-zero block), scale byte 0 with the drawn codes
+      (values down to 2^-128, fp32 and bf16 subnormals), 1..100, 128..140
+      (values up to 6 * 2^13), or the common 120..127;
+    * "tiny": scale bytes 0..3 with the drawn codes and some zero blocks,
+      so that whole entries hold values near the bottom of the fp32 range.
+
+    rope_zero: positional channels all zero (so that the MXFP4 channels alone
+    set the size of a row)."""
     N_cap = w.N if N_cap is None else N_cap
     nseq = w.B if nseq is None else nseq
     out = {}
-    out["nope"] = _rows_bytes(w, TensorId.NOPE, nseq, N_cap, 256, device, seq0)
-    out["nscale"] = (124 + _rows_bytes(w, TensorId.NSCALE, nseq, N_cap, 16, device, seq0) % 4).to(torch.uint8)
+
+    def planes(tid_codes, tid_scales, width):
+        codes = _rows_bytes(w, tid_codes, nseq, N_cap, width, device, seq0)
+        h = _rows_hash(w, tid_scales, nseq, N_cap, width // 16, device, seq0)
+        if scales == "narrow":
+            sc = 124 + h % 4
+            return codes, sc.to(torch.uint8)
+        kind = (h >> 8) % 8
+        if scales == "wide":
+            sc = torch.where(kind == 2, 1 + h % 100,
+                             torch.where(kind == 3, 128 + h % 13, torch.where(kind <= 1, 0, 120 + h % 8)))
+            zero = kind == 0
+        elif scales == "tiny":
+            sc = h % 4
+            zero = kind == 0
+        else:
+            raise ValueError(scales)
+        blk = codes.view(nseq, N_cap, width // 16, 16)
+        blk = torch.where(zero[..., None], torch.zeros_like(blk), blk)
+        return blk.reshape(nseq, N_cap, width), sc.to(torch.uint8)
+
+    out["nope"], out["nscale"] = planes(TensorId.NOPE, TensorId.NSCALE, 256)
     out["rope"] = normal_bf16(w.seed, TensorId.ROPE, (nseq, N_cap, 64), device=device, first_seq=seq0)
+    if rope_zero:
+        out["rope"] = torch.zeros_like(out["rope"])
     if w.d_idx:
-        out["ikey"] = _rows_bytes(w, TensorId.IKEY, nseq, N_cap, w.d_idx // 2, device, seq0)
-        out["iscale"] = (124 + _rows_bytes(w, TensorId.ISCALE, nseq, N_cap, w.d_idx // 32, device, seq0)
-                         % 4).to(torch.uint8)
+        out["ikey"], out["iscale"] = planes(TensorId.IKEY, TensorId.ISCALE, w.d_idx // 2)
     return out
+
+
+def _rows_hash(w, tid, nseq, N_cap, width, device, seq0):
+    from .gen import hash32
+    out = torch.empty((nseq, N_cap * width), dtype=torch.int64, device=device)
+    step = 1 << 24
+    for b in range(nseq):
+        for s in range(0, N_cap * width, step):
+            n = min(step, N_cap * width - s)
+            out[b, s:s + n] = hash32(w.seed, tid, seq0 + b, s, n, device)
+    return out.view(nseq, N_cap, width)
 
 
 def _rows_bytes(w, tid, nseq, N_cap, width, device, seq0):

@@ -17,7 +17,7 @@ from __future__ import annotations
 
 import numpy as np
 
-from oracle import bf16_to_f64, mxfp4_decode
+from oracle import bf16_to_f64, e4m3_to_f64, mxfp4_decode
 
 _BOUNDS = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0])
 
@@ -92,26 +92,49 @@ def check_topk(g_idx, o_idx, js, scores, rel=1e-4, what=""):
     return len(d) // 2
 
 
-def index_score_tol(qI_u8, w_f32, iscale_rows, ref):
+def index_score_tol(qI_u8, w_f32, ikey_rows, iscale_rows, ref=None):
     """Per-entry bound on |GPU score - oracle score| for the indexer.
 
-    Two parts: fp32 accumulation (1e-5 of the row's largest score), and the
-    matrix instruction's handling of E4M3 subnormal query codes (exponent
-    field 0, mantissa m): their products with E2M1 codes are kept only to a
-    multiple of 2^-9 before the block scale, so each such product may lose up
-    to 2^-10 x its block's scale (measured on gfx950; E4M3 x E2M1 products of
-    normal codes come out exact).  The loss passes through ReLU (1-Lipschitz)
-    and the head weight: sum_h |w_h| * sum_c [q_hc subnormal] 2^-10 * S_j(c).
+    Three parts:
+    * fp32 evaluation of the sums: any order of summing the d_idx products of
+      a head and then the H_I weighted heads errs by at most
+      (d_idx + H_I) * 2^-24 relative to the sum of the absolute terms,
+      sum_h |w_h| * sum_c |q_hc * k_jc|; 1e-5 covers d_idx + H_I <= 160;
+    * rounding in the subnormal range (keys with tiny block scales): at most
+      2^-149 per operation, (d_idx + H_I) * 2^-149 * sum_h |w_h|;
+    * the matrix instruction's handling of E4M3 subnormal query codes
+      (exponent field 0, mantissa m): their products with E2M1 codes are
+      kept only to a multiple of 2^-9 before the block scale, so each such
+      product may lose up to 2^-10 x its block's scale (measured on gfx950;
+      E4M3 x E2M1 products of normal codes come out exact).  The loss passes
+      through ReLU (1-Lipschitz) and the head weight:
+      sum_h |w_h| * sum_c [q_hc subnormal] 2^-10 * S_j(c).
     """
     q = np.asarray(qI_u8, dtype=np.uint8)
-    sub = ((q & 0x78) == 0) & ((q & 0x07) != 0)                 # [H][d]
-    nb = q.shape[1] // 32
-    n_hb = sub.reshape(q.shape[0], nb, 32).sum(axis=2)           # [H][nb]
-    wa = np.abs(np.asarray(w_f32, dtype=np.float64))
-    per_blk = (n_hb * wa[:, None]).sum(axis=0)                   # [nb]
-    S = np.exp2(np.asarray(iscale_rows, dtype=np.float64)[:, :nb] - 127.0)  # [V][nb]
-    scale = np.abs(ref).max() if len(ref) else 0.0
-    return 1e-5 * scale + 2.0 ** -10 * (S @ per_blk)
+    H, d = q.shape
+    wa = np.abs(np.asarray(w_f32, dtype=np.float32).astype(np.float64))
+    k = np.abs(mxfp4_decode(np.asarray(ikey_rows), np.asarray(iscale_rows)))    # [V][d]
+    qa = np.abs(e4m3_to_f64(q))                                                 # [H][d]
+    mag = (k @ qa.T) @ wa                                                       # [V]
+    sub = ((q & 0x78) == 0) & ((q & 0x07) != 0)                                 # [H][d]
+    nb = d // 32
+    n_hb = sub.reshape(H, nb, 32).sum(axis=2)                                   # [H][nb]
+    per_blk = (n_hb * wa[:, None]).sum(axis=0)                                  # [nb]
+    S = np.exp2(np.asarray(iscale_rows, dtype=np.float64)[:, :nb] - 127.0)     # [V][nb]
+    return 1e-5 * mag + (d + H) * 2.0 ** -149 * wa.sum() + 2.0 ** -10 * (S @ per_blk)
+
+
+def compress_bounds(out, m, W=None):
+    """Error bounds of the GPU's fp32 pooling (and key projection) for each
+    pooled value: (8 + 2m) * 2^-22 * sum of the absolute weighted terms, and
+    for indexer keys 2^-14 * |kI| (bf16 W_IK products in fp32) plus the
+    pooled-value bound carried through |W|."""
+    pool_b = (8 + 2 * m) * 2.0 ** -22 * out["pooled_abs"]
+    kb = None
+    if W is not None:
+        Wa = np.abs(bf16_to_f64(W))
+        kb = 2.0 ** -14 * out["kI_abs"] + (8 + 2 * m) * 2.0 ** -22 * (out["pooled_abs"] @ Wa)
+    return pool_b, kb
 
 
 def row_rel_err(g, r):

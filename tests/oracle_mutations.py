@@ -45,6 +45,8 @@ muts = [
  ("csa.py", "layer_b[\"qI\"], layer_b[\"w\"],\n                                   p, m, n_entries, k_b, cand=idx_a)", "layer_a[\"qI\"], layer_b[\"w\"],\n                                   p, m, n_entries, k_b, cand=idx_a)"),
  ("csa.py", "p, m, n_entries, k_b, cand=idx_a)", "p, m, n_entries, k_b)"),
  ("csa.py", "o_b, lse_b = sparse_attention(layer_b[\"q\"]", "o_b, lse_b = sparse_attention(layer_a[\"q\"]"),
+ ("csa.py", "return np.concatenate([mxfp4_decode(nope, nscale), bf16_to_f64(rope)], axis=-1)", "return np.concatenate([bf16_to_f64(rope), mxfp4_decode(nope, nscale)], axis=-1)"),
+ ("csa.py", "return np.concatenate([mxfp4_decode(nope, nscale), bf16_to_f64(rope)], axis=-1)", "return np.concatenate([mxfp4_decode(nope, nscale), bf16_to_f64(rope)[..., ::-1]], axis=-1)"),
 ]
 missed = 0
 root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))

@@ -229,3 +229,8 @@ def test_fp8_window_checks(L):
                                P, 1 << 30, None) == ENULL
     assert L.csa_sparse_attn_w8(ctypes.byref(_cache()), P, 64, P, 0, P, 16, P, P, P, P, 128, 128, 1.0, 1, P, None,
                                 P, 1 << 30, None) == OK                # Q = 0: nothing to launch
+
+
+def test_read_device_flags_null(L):
+    # a null output pointer fails before any HIP call
+    assert L.csa_read_device_flags(None, None) == ENULL

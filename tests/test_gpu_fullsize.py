@@ -13,7 +13,7 @@ import torch
 
 import compressed_sparse_attention_compressor_amd as csa
 import oracle as O
-from gpu_check import check_topk, compare_bf16_rounding, compare_mxfp4, row_rel_err
+from gpu_check import check_topk, compare_bf16_rounding, compare_mxfp4, compress_bounds, row_rel_err
 from synth.workloads import (
     BATCHED_DECODE,
     CSA2_DECODE,
@@ -302,8 +302,79 @@ def test_prefill_64k_fullsize_sampled():
     for n, t in enumerate(sample):
         p = int(t)
         oi, _, js, s = O.index_topk(pc["ikey"][0], pc["iscale"][0], qI[n], wt[n], p, w.m, w.N, w.k)
-        swaps = check_topk(g_idx[n], oi, js, s, what=f"query {p}")
-        if swaps == 0:
-            o, _ = O.sparse_attention(as_u16(qq[n]), pc["nope"][0], pc["nscale"][0], pc["rope"][0], oi, xc, 0, p,
-                                      w.n_win, w.softmax_scale, w.m, w.N)
-            assert row_rel_err(g_out[n], o).max() <= 2e-2, p
+        check_topk(g_idx[n], oi, js, s, what=f"query {p}")
+        # the attention stage on the same cache bytes and the GPU's selection
+        o, _ = O.sparse_attention(as_u16(qq[n]), pc["nope"][0], pc["nscale"][0], pc["rope"][0], g_idx[n], xc, 0, p,
+                                  w.n_win, w.softmax_scale, w.m, w.N)
+        assert row_rel_err(g_out[n], o).max() <= 2e-2, p
+
+
+def _prefill_sample(T, m, rng, n_random):
+    """Query positions of the prefill end-to-end check: the first tokens
+    (nothing or little visible), positions around entry boundaries and around
+    the compressor's 4,096-token chunk edges, the last token, and random ones."""
+    edges = [0, 1, 2, 3, 4, 5, 6, 7, 8, 11, 12, 15, 16, 127, 128, 129, 130, 131]
+    for t in (4096, 8192, 32768, 61440):
+        edges += [t - m - 1, t - m, t - 2, t - 1, t, t + 1, t + m - 1, t + m]
+    edges += [T - m - 1, T - m, T - 2, T - 1]
+    pos = np.unique(np.concatenate([np.array(edges), rng.integers(0, T, n_random)]))
+    return pos[(pos >= 0) & (pos < T)]
+
+
+def test_prefill_64k_end_to_end():
+    """The 65,536-token prefill chunk end to end ([V4] Fig. 3: compressor ->
+    indexer -> top-k -> attention with the window): the GPU compresses the
+    whole stream and every one of the 16,384 entries and indexer keys is
+    compared with the oracle's compressor; then, on sampled queries, the
+    GPU's selection against the oracle's indexer on the GPU's keys, the
+    GPU's attention against the oracle on the GPU's cache and selection
+    (stage-wise), and against the oracle pipeline run from the raw inputs
+    alone (end to end)."""
+    w = PREFILL
+    bias, wik = params(w)
+    x, z = raw_rows(w, 0, w.T)
+    cache = csa.Cache(w.B, w.N, w.m, w.d_idx, device=DEV)
+    cache.n_entries.fill_(w.N)
+    xd = x.to(DEV)
+    csa.compress(cache, xd, z.to(DEV), bias.to(DEV), wik.to(DEV))
+    qs = queries(w, device=DEV)
+    idx, _ = csa.index_topk(cache, qs["qI"], qs["w"], qs["q_pos"], w.k)
+    s0 = torch.zeros(1, dtype=torch.int32, device=DEV)
+    out, lse = csa.sparse_attn(cache, qs["q"], qs["q_pos"], idx, xd, s0, w.n_win, w.softmax_scale,
+                               out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    # the compressor: all 16,384 entries and keys
+    o = O.compress(as_u16(x[0]), as_u16(z[0]), bias.numpy(), as_u16(wik), w.m)
+    pb, kb = compress_bounds(o, w.m, as_u16(wik))
+    gn, gs, gr = _np(cache.nope[0]), _np(cache.nscale[0]), _np(cache.rope[0])
+    gk, gks = _np(cache.ikey[0]), _np(cache.iscale[0])
+    ex = compare_mxfp4(gn, gs, o["nope"], o["nscale"], o["pooled"][:, :512], pb[:, :512], "prefill nope")
+    ex_k = compare_mxfp4(gk, gks, o["ikey"], o["iscale"], o["kI"], kb, "prefill ikey")
+    rz = compare_bf16_rounding(gr, o["pooled"][:, 512:], pb[:, 512:], "prefill rope")
+    print(f"prefill compressor: {ex} + {ex_k} exempted codes, {rz} rope roundings over {w.N} entries")
+    assert ex + ex_k <= 1e-4 * w.N * (512 + w.d_idx)
+    # sampled queries
+    sample = _prefill_sample(w.T, w.m, np.random.default_rng(7), 260)
+    assert len(sample) >= 256
+    sel = torch.from_numpy(sample).to(DEV)
+    g_idx = _np(idx[0, sel])
+    g_out = O.bf16_to_f64(_np(out[0, sel]))
+    g_lse = _np(lse[0, sel]).astype(np.float64)
+    qI, wt = _np(qs["qI"][0, sel]), _np(qs["w"][0, sel])
+    qq = qs["q"][0, sel].cpu()
+    xc = as_u16(x[0])
+    swaps = 0
+    for n, t in enumerate(sample):
+        p = int(t)
+        qb = as_u16(qq[n])
+        si, _, sj, ss = O.index_topk(gk, gks, qI[n], wt[n], p, w.m, w.N, w.k)
+        check_topk(g_idx[n], si, sj, ss, what=f"stage-wise top-k, query {p}")
+        so, sl = O.sparse_attention(qb, gn, gs, gr, g_idx[n], xc, 0, p, w.n_win, w.softmax_scale, w.m, w.N)
+        assert row_rel_err(g_out[n], so).max() <= 2e-2, f"stage-wise attention, query {p}"
+        assert np.abs(g_lse[n] - sl).max() <= 1e-4 * max(1.0, np.abs(sl).max()), f"stage-wise lse, query {p}"
+        oi, _, oj, os_ = O.index_topk(o["ikey"], o["iscale"], qI[n], wt[n], p, w.m, w.N, w.k)
+        swaps += check_topk(g_idx[n], oi, oj, os_, what=f"end-to-end top-k, query {p}")
+        eo, _ = O.sparse_attention(qb, o["nope"], o["nscale"], o["rope"], oi, xc, 0, p, w.n_win, w.softmax_scale,
+                                   w.m, w.N)
+        assert row_rel_err(g_out[n], eo).max() <= 2e-2, f"end-to-end attention, query {p}"
+    print(f"prefill: {len(sample)} queries compared stage-wise and end to end, {swaps} near-tie swaps")

@@ -16,6 +16,7 @@ from gpu_check import (
     check_topk,
     compare_bf16_rounding,
     compare_mxfp4,
+    compress_bounds,
     decode_cache_rows,
     index_score_tol,
     row_rel_err,
@@ -60,15 +61,6 @@ def _gpu_cache(planes, B, N_cap, m, d_idx, n_entries):
     if isinstance(planes["rope"], np.ndarray):
         p["rope"] = torch.from_numpy(np.ascontiguousarray(planes["rope"]).view(np.int16)).view(torch.bfloat16).to(DEV)
     return csa.Cache(B, N_cap, m, d_idx, planes=p)
-
-
-def _compress_bounds(out, m, W=None):
-    pool_b = (8 + 2 * m) * 2.0 ** -22 * out["pooled_abs"]
-    kb = None
-    if W is not None:
-        Wa = np.abs(O.bf16_to_f64(W))
-        kb = 2.0 ** -14 * out["kI_abs"] + (8 + 2 * m) * 2.0 ** -22 * (out["pooled_abs"] @ Wa)
-    return pool_b, kb
 
 
 # ----------------------------------------------------------------------------- generators
@@ -157,7 +149,7 @@ def test_compress_parity(name, w, chunks, G, with_keys):
     total = exempt = 0
     for b in range(w.B):
         o = O.compress(as_u16(x[b]), as_u16(z[b]), bias.numpy(), as_u16(wik) if with_keys else None, w.m)
-        pb, kb = _compress_bounds(o, w.m, as_u16(wik) if with_keys else None)
+        pb, kb = compress_bounds(o, w.m, as_u16(wik) if with_keys else None)
         exempt += compare_mxfp4(_np(cache.nope[b]), _np(cache.nscale[b]), o["nope"], o["nscale"],
                                 o["pooled"][:, :512], pb[:, :512], f"{name} nope b={b}")
         exempt += compare_bf16_rounding(_np(cache.rope[b]), o["pooled"][:, 512:], pb[:, 512:], f"{name} rope")
@@ -172,8 +164,8 @@ def test_compress_parity(name, w, chunks, G, with_keys):
 # ----------------------------------------------------------------------------- indexer + top-k
 
 
-def _index_case(w, N_cap, n_entries, pos, k, seed_off=0):
-    planes = synthetic_cache(w, N_cap=N_cap)
+def _index_case(w, N_cap, n_entries, pos, k, seed_off=0, scales="narrow"):
+    planes = synthetic_cache(w, N_cap=N_cap, scales=scales)
     qs = queries(w, nq=pos.shape[1])
     qs["q_pos"] = torch.from_numpy(pos.astype(np.int32))
     return planes, qs
@@ -262,6 +254,19 @@ SCORE_CASES = [
     # positions and unsorted ones
     ("decode", Workload("s1", 21, B=2, T=8000, m=4, d_idx=128, H_I=32, k=1, H=64, n_win=0), 2000, [2000, 1234],
      "last"),
+    # key scale bytes over the whole range (zero blocks, byte 0 with
+    # subnormal values, 1..100, 128..140), and keys near the bottom of the
+    # fp32 range only, through the decode, several-query and prefill kernels
+    ("decode-wide", Workload("s8", 28, B=2, T=8000, m=4, d_idx=128, H_I=32, k=1, H=64, n_win=0), 2000, [2000, 1500],
+     "last", "wide"),
+    ("qb4-wide", Workload("s9", 29, B=1, T=8000, m=4, d_idx=128, H_I=32, k=1, H=64, n_win=0, Q=5), 2000, [2000],
+     "causal", "wide"),
+    ("prefill-wide-d64", Workload("s10", 30, B=1, T=6000, m=4, d_idx=64, H_I=16, k=1, H=64, n_win=0, Q=70), 1500,
+     [1500], "causal", "wide"),
+    ("decode-tiny", Workload("s11", 31, B=1, T=8000, m=4, d_idx=128, H_I=32, k=1, H=64, n_win=0), 2000, [2000],
+     "last", "tiny"),
+    ("prefill-tiny", Workload("s12", 32, B=1, T=6000, m=4, d_idx=128, H_I=32, k=1, H=64, n_win=0, Q=66), 1500,
+     [1500], "causal", "tiny"),
     ("qb4", Workload("s2", 22, B=1, T=8000, m=4, d_idx=128, H_I=32, k=1, H=64, n_win=0, Q=7), 2000, [2000],
      "causal"),
     ("prefill-h32", Workload("s3", 23, B=2, T=9300, m=4, d_idx=128, H_I=32, k=1, H=64, n_win=0, Q=100), 2300,
@@ -279,8 +284,11 @@ SCORE_CASES = [
 ]
 
 
-@pytest.mark.parametrize("name,w,N_cap,n_entries,kind", SCORE_CASES, ids=[c[0] for c in SCORE_CASES])
-def test_index_scores_stage_parity(name, w, N_cap, n_entries, kind):
+SCORE_CASES = [c if len(c) == 6 else c + ("narrow",) for c in SCORE_CASES]
+
+
+@pytest.mark.parametrize("name,w,N_cap,n_entries,kind,scales", SCORE_CASES, ids=[c[0] for c in SCORE_CASES])
+def test_index_scores_stage_parity(name, w, N_cap, n_entries, kind, scales):
     """Every score the indexer writes against the oracle, and every slot it
     must not write (entries a query cannot see) left as it was."""
     rng = np.random.default_rng(w.cfg)
@@ -292,7 +300,7 @@ def test_index_scores_stage_parity(name, w, N_cap, n_entries, kind):
         pos[:, -1] = w.T - 1
     else:
         pos = rng.integers(-1, w.T, (w.B, w.Q)).astype(np.int32)
-    planes, qs = _index_case(w, N_cap, n_entries, pos, 1)
+    planes, qs = _index_case(w, N_cap, n_entries, pos, 1, scales=scales)
     cache = _gpu_cache(planes, w.B, N_cap, w.m, w.d_idx, n_entries)
     sentinel = 0x7FC0ABCD
     buf = torch.full((w.B, pos.shape[1], N_cap), sentinel, dtype=torch.int32, device=DEV)
@@ -308,7 +316,7 @@ def test_index_scores_stage_parity(name, w, N_cap, n_entries, kind):
             qI, wt = qs["qI"][b, t].numpy(), qs["w"][b, t].numpy()
             ref = O.index_scores(ik[b], isc[b], qI, wt, np.arange(V))
             g = got[b, t, :V].view(np.float32).astype(np.float64)
-            tol = index_score_tol(qI, wt, isc[b, :V], ref)
+            tol = index_score_tol(qI, wt, ik[b, :V], isc[b, :V], ref)
             bad = np.nonzero(np.abs(g - ref) > tol)[0]
             assert len(bad) == 0, (f"{name} b={b} t={t} pos={pos[b, t]} V={V}: {len(bad)} bad entries, first "
                                    f"{bad[:8].tolist()}, got {g[bad[:4]].tolist()} want {ref[bad[:4]].tolist()}")
@@ -659,8 +667,8 @@ def test_layer_stack_parity():
 # ----------------------------------------------------------------------------- attention
 
 
-def _attn_inputs(w, N_cap, n_entries, pos, S=None, swa_pos0=None):
-    planes = synthetic_cache(w, N_cap=N_cap)
+def _attn_inputs(w, N_cap, n_entries, pos, S=None, swa_pos0=None, scales="narrow", rope_zero=False):
+    planes = synthetic_cache(w, N_cap=N_cap, scales=scales, rope_zero=rope_zero)
     qs = queries(w, nq=pos.shape[1])
     S = S if S is not None else max(1, w.T)
     swa_pos0 = np.zeros(w.B, np.int32) if swa_pos0 is None else np.asarray(swa_pos0, np.int32)
@@ -757,6 +765,59 @@ def test_dense_attention_parity(name, w, N_cap, n_entries, pos, dtype):
                                   torch.from_numpy(s0).to(DEV), w.n_win, w.softmax_scale, out_dtype=dtype)
     torch.cuda.synchronize()
     o, l = _oracle_attn(planes, qs, swa, s0, pos, None, w, n_entries, True, w.softmax_scale)
+    _check_attn(out, lse, o, l, dtype, name)
+
+
+SCALE_CASES = [
+    # (name, workload, N_cap, n_entries, positions, scales, rope zero, softmax scale, dense)
+    # scale bytes over the whole range: the softmax scale keeps the largest
+    # logits near 10 (entries reach 6 * 2^13), so the softmax stays well
+    # conditioned while zero blocks and subnormal values sit beside them
+    ("sparse-wide", Workload("sw1", 40, B=2, T=4000, m=4, d_idx=0, H_I=0, k=96, H=64, n_win=32, Q=2), 1000,
+     [1000, 777], [[3999, 1500], [3103, 3999]], "wide", False, 2.0 ** -13 / 24, False),
+    ("dense-wide", Workload("sw2", 41, B=2, T=8192, m=128, d_idx=0, H_I=0, k=0, H=64, n_win=64, Q=1), 64,
+     [64, 50], [[8191], [7000]], "wide", False, 2.0 ** -13 / 24, True),
+    # entries near the bottom of the fp32 range only (scale bytes 0..3, zero
+    # positional channels, no window): logits round to 0 on both sides and
+    # every output is a mean of values down to 2^-128, so a flush of
+    # subnormal values to zero anywhere on the path shows in the row error
+    ("sparse-tiny", Workload("sw3", 42, B=1, T=2000, m=4, d_idx=0, H_I=0, k=64, H=16, n_win=0, Q=2), 500,
+     [500], [[1999, 999]], "tiny", True, 1.0 / 24, False),
+    ("dense-tiny", Workload("sw4", 43, B=1, T=4096, m=128, d_idx=0, H_I=0, k=0, H=64, n_win=0), 32, [32],
+     [[4095]], "tiny", True, 1.0 / 24, True),
+]
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=["f32", "bf16"])
+@pytest.mark.parametrize("name,w,N_cap,n_entries,pos,scales,rz,scale,dense", SCALE_CASES,
+                         ids=[c[0] for c in SCALE_CASES])
+def test_attention_scale_range(name, w, N_cap, n_entries, pos, scales, rz, scale, dense, dtype):
+    """Sparse and dense attention on cache planes whose E8M0 bytes span the
+    whole range (the FP4 -> bf16 conversion with byte 0, small and large
+    scales, zero blocks), against the oracle on the same bytes."""
+    pos = np.array(pos, np.int32)
+    planes, qs, swa, s0 = _attn_inputs(w, N_cap, n_entries, pos, scales=scales, rope_zero=rz)
+    B, Q = pos.shape
+    cache = _gpu_cache(planes, B, N_cap, w.m, 0, n_entries)
+    idx = None
+    if not dense:
+        rng = np.random.default_rng(w.cfg)
+        idx = np.full((B, Q, w.k), -1, np.int32)
+        for b in range(B):
+            for t in range(Q):
+                V = O.visible_count(int(pos[b, t]), w.m, n_entries[b])
+                n = min(w.k, V)
+                idx[b, t, :n] = np.sort(rng.choice(V, n, replace=False))
+    args = (cache, qs["q"].to(DEV), torch.from_numpy(pos).to(DEV))
+    win = (swa.to(DEV), torch.from_numpy(s0).to(DEV), w.n_win, scale)
+    if dense:
+        out, lse = csa.hca_dense_attn(*args, *win, out_dtype=dtype)
+    else:
+        out, lse = csa.sparse_attn(*args, torch.from_numpy(idx).to(DEV), *win, out_dtype=dtype)
+    torch.cuda.synchronize()
+    o, l = _oracle_attn(planes, qs, swa, s0, pos, idx, w, n_entries, dense, scale)
+    if scales == "tiny":
+        assert np.abs(o).max() < 2.0 ** -120                  # the case is what it claims
     _check_attn(out, lse, o, l, dtype, name)
 
 
@@ -926,20 +987,35 @@ def test_end_to_end_tiny_decode():
                                w.softmax_scale, out_dtype=torch.float32)
     torch.cuda.synchronize()
     o = O.compress(as_u16(x[0]), as_u16(z[0]), bias.numpy(), as_u16(wik), w.m)
-    pb, kb = _compress_bounds(o, w.m, as_u16(wik))
+    pb, kb = compress_bounds(o, w.m, as_u16(wik))
     ex = compare_mxfp4(_np(cache.nope[0]), _np(cache.nscale[0]), o["nope"], o["nscale"], o["pooled"][:, :512],
                        pb[:, :512], "e2e nope")
     ex += compare_mxfp4(_np(cache.ikey[0]), _np(cache.iscale[0]), o["ikey"], o["iscale"], o["kI"], kb, "e2e ikey")
+    rz = compare_bf16_rounding(_np(cache.rope[0]), o["pooled"][:, 512:], pb[:, 512:], "e2e rope")
     p = w.T - 1
-    oi, _, js, s = O.index_topk(o["ikey"], o["iscale"], qs["qI"][0, 0].numpy(), qs["w"][0, 0].numpy(), p, w.m, w.N,
-                                w.k)
-    swaps = check_topk(_np(idx)[0, 0], oi, js, s, what="e2e top-k")
-    if ex == 0 and swaps == 0:
-        oo, ol = O.sparse_attention(as_u16(qs["q"][0, 0]), o["nope"], o["nscale"], o["rope"], oi, as_u16(swa[0]),
-                                    w.T - w.n_win, p, w.n_win, w.softmax_scale, w.m, w.N)
-        err = row_rel_err(_np(out)[0, 0], oo)
-        assert err.max() <= 1e-3, err.max()
-        assert np.abs(_np(lse)[0, 0] - ol).max() <= 1e-4 * max(1.0, np.abs(ol).max())
+    qI, wt = qs["qI"][0, 0].numpy(), qs["w"][0, 0].numpy()
+    gi = _np(idx)[0, 0]
+    gn, gs, gr = _np(cache.nope[0]), _np(cache.nscale[0]), _np(cache.rope[0])
+    # stage-wise, always: the oracle's indexer on the GPU's key planes, and
+    # the oracle's attention on the GPU's cache planes and the GPU's selection
+    si, _, sj, ss = O.index_topk(_np(cache.ikey[0]), _np(cache.iscale[0]), qI, wt, p, w.m, w.N, w.k)
+    check_topk(gi, si, sj, ss, what="e2e top-k on the GPU's keys")
+    so, sl = O.sparse_attention(as_u16(qs["q"][0, 0]), gn, gs, gr, gi, as_u16(swa[0]), w.T - w.n_win, p, w.n_win,
+                                w.softmax_scale, w.m, w.N)
+    assert row_rel_err(_np(out)[0, 0], so).max() <= 1e-3
+    assert np.abs(_np(lse)[0, 0] - sl).max() <= 1e-4 * max(1.0, np.abs(sl).max())
+    # end to end, always: the oracle pipeline from the raw inputs (its own
+    # cache and selection).  A code exempted at a rounding boundary or a
+    # near-tie swapped in the selection moves the result by far less than
+    # the tolerance of a bf16 result; with neither, the fp32 bar holds.
+    oi, _, js, s = O.index_topk(o["ikey"], o["iscale"], qI, wt, p, w.m, w.N, w.k)
+    swaps = check_topk(gi, oi, js, s, what="e2e top-k")
+    oo, ol = O.sparse_attention(as_u16(qs["q"][0, 0]), o["nope"], o["nscale"], o["rope"], oi, as_u16(swa[0]),
+                                w.T - w.n_win, p, w.n_win, w.softmax_scale, w.m, w.N)
+    err = row_rel_err(_np(out)[0, 0], oo).max()
+    print(f"e2e: {ex} exempted codes, {rz} rope roundings, {swaps} swaps, row error {err:.2e}")
+    assert err <= (1e-3 if ex == 0 and rz == 0 and swaps == 0 else 2e-2), err
+    assert np.abs(_np(lse)[0, 0] - ol).max() <= 1e-3 * max(1.0, np.abs(ol).max())
 
 
 TOPK_CASES = [

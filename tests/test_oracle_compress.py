@@ -144,3 +144,36 @@ def test_indexer_key_projection_matches_torch():
 def test_rejects_ragged_block():
     with pytest.raises(ValueError):
         compress(np.zeros((6, D), np.uint16), np.zeros((6, D), np.uint16), np.zeros(4, np.float32), None, 4)
+
+
+def test_decode_entries_places_every_channel():
+    """decode_entries of an m = 1 compress gives back the raw rows exactly
+    when every value is representable: channels 0..511 as the MXFP4 decode
+    of grid values (one power-of-two scale per block of 32), channels
+    512..575 as the bf16 rows themselves.  Every channel holds a value that
+    identifies it, so a swapped, shifted or reversed channel range fails."""
+    from oracle import decode_entries
+
+    grid = np.array([0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+    rows = []
+    for r in range(6):
+        v = np.empty(D)
+        for blk in range(16):
+            # block maximum 6 * 2^X fixes the block scale at 2^X; the other
+            # 31 values are grid values times 2^X with a per-channel sign
+            X = (blk + 3 * r) % 9 - 4
+            vals = grid[(np.arange(32) + blk + r) % 7] * 2.0 ** X
+            vals[(blk + r) % 32] = 6.0 * 2.0 ** X
+            vals *= np.where((np.arange(32) + r) % 3 == 0, -1.0, 1.0)
+            v[32 * blk:32 * blk + 32] = vals
+        # positional channels: distinct bf16 values (128 + c) * 2^(r - 7)
+        v[512:] = (128.0 + np.arange(64)) * 2.0 ** (r - 7)
+        rows.append(v)
+    x64 = np.array(rows)
+    x = _bf16(x64)
+    np.testing.assert_array_equal(bf16_to_f64(x), x64)           # exact in bf16
+    z = _rand(np.random.default_rng(9), (6, D))
+    out = compress(x, z, np.zeros(1, np.float32), None, m=1)
+    dec = decode_entries(out["nope"], out["nscale"], out["rope"])
+    assert dec.shape == (6, D)
+    np.testing.assert_array_equal(dec, x64)

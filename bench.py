@@ -125,7 +125,7 @@ def main():
     ap.add_argument("--kernel-reps", type=int, default=64)
     ap.add_argument("--cpu-sample", type=int, default=32, help="sequences the oracle baseline runs (0 = skip)")
     ap.add_argument("--only-index", action="store_true", help="run only the fused append + indexer launches (for counter passes)")
-    ap.add_argument("--only", choices=["index", "topk", "attn"], default=None,
+    ap.add_argument("--only", choices=["index", "topk", "attn", "front"], default=None,
                     help="run only this stage of the decode step (for counter passes; the step's inputs are "
                          "prepared once by one eager step)")
     ap.add_argument("--prefill-reps", type=int, default=3, help="timed passes of the 64K prefill chunk (0 = skip)")
@@ -174,6 +174,9 @@ def main():
     topk_ws = torch.empty(max(topk_ws_bytes, 16), dtype=torch.uint8, device=dev)
     attn_ws_bytes = csa.workspace_bytes(csa.WS_SPARSE_ATTN, w.B, 1, w.H, w.k, w.n_win)
     attn_ws = torch.empty(max(attn_ws_bytes, 16), dtype=torch.uint8, device=dev)
+    # the front half's workspace (scores, then the top-k count hint, which
+    # every call leaves zero for the next)
+    front_ws = torch.zeros(csa.workspace_bytes(csa.WS_INDEX_TOPK, w.B, 1, w.k, w.N, 0), dtype=torch.uint8, device=dev)
 
     def st_compress(ly):
         csa.compress(ly.cache, ly.x_blk, ly.z_blk, bias, wik, tok_begin=w.T - w.m)
@@ -189,6 +192,12 @@ def main():
     def st_topk(ly):
         csa.topk(ly.cache, scores_ws, ly.q_pos, w.k, out=ly.idx, ws=topk_ws if topk_ws_bytes else None)
 
+    def st_front(ly):
+        # decode append + indexer (one launch, counting the scores for the
+        # top-k), then the hinted top-k (compaction, final selection)
+        csa.compress_index_topk(ly.cache, ly.x_blk, ly.z_blk, bias, wik, w.T - w.m, ly.qI, ly.w, ly.q_pos, w.k,
+                                ws=front_ws, out=ly.idx)
+
     def st_attn_w8(ly):
         csa.sparse_attn_w8(ly.cache, ly.q, ly.q_pos, ly.idx, ly.swa8, ly.swa_pos0, w.n_win, w.softmax_scale,
                            out_dtype=torch.bfloat16, ws=attn_ws, out=ly.out, lse=ly.lse)
@@ -197,15 +206,15 @@ def main():
         csa.sparse_attn(ly.cache, ly.q, ly.q_pos, ly.idx, ly.swa, ly.swa_pos0, w.n_win, w.softmax_scale,
                         out_dtype=torch.bfloat16, ws=attn_ws, out=ly.out, lse=ly.lse)
 
-    stages = [st_append, st_topk, st_attn]
+    stages = [st_front, st_attn]
     if args.only:
         # one eager step per layer prepares the scores and selections the
         # stage reads
         for l in range(L):
-            for f in stages:
+            for f in [st_append, st_topk, st_attn]:
                 f(layers[l])
         torch.cuda.synchronize()
-        stages = [{"index": st_append, "topk": st_topk, "attn": st_attn}[args.only]]
+        stages = [{"index": st_append, "topk": st_topk, "attn": st_attn, "front": st_front}[args.only]]
 
     def step(l):
         for f in stages:
@@ -285,9 +294,9 @@ def main():
     # the kernels run on.
     R = args.kernel_reps
     stage_us = {}
-    names = {st_append: "compress+index_scores", st_compress: "compress", st_index: "index_scores", st_topk: "topk",
-             st_attn: "sparse_attn"}
-    timed = stages if args.only else [st_append, st_compress, st_index, st_topk, st_attn]
+    names = {st_front: "compress+index_topk", st_append: "compress+index_scores", st_compress: "compress",
+             st_index: "index_scores", st_topk: "topk_two_stage", st_attn: "sparse_attn"}
+    timed = stages if args.only else [st_front, st_append, st_compress, st_index, st_topk, st_attn]
     for f in timed:
         g = capture(lambda f=f: [f(layers[i % L]) for i in range(R)])
         g.replay()
@@ -306,7 +315,7 @@ def main():
     # the pages state); reported beside the headline, which keeps bf16 rows.
     w8 = None
     if not args.only:
-        g8 = capture(lambda: [(st_append(layers[l]), st_topk(layers[l]), st_attn_w8(layers[l])) for l in range(L)])
+        g8 = capture(lambda: [(st_front(layers[l]), st_attn_w8(layers[l])) for l in range(L)])
         g8.replay()
         torch.cuda.synchronize()
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)

@@ -12,6 +12,7 @@ from .ops import (  # noqa: F401
     Cache,
     compress,
     compress_index_scores,
+    compress_index_topk,
     hca_dense_attn,
     index_scores,
     index_pool,

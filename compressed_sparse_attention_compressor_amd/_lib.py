@@ -74,6 +74,9 @@ _SIGS = {
     "csa_compress_index_scores": (c_int, [c_void_p, c_int64, c_void_p, c_int64, c_int, c_void_p, c_void_p, c_int64,
                                           c_int64, ctypes.POINTER(CacheT), c_void_p, c_void_p, c_int, c_void_p, c_int,
                                           c_void_p, c_size_t, c_void_p]),
+    "csa_compress_index_topk": (c_int, [c_void_p, c_int64, c_void_p, c_int64, c_int, c_void_p, c_void_p, c_int64,
+                                        c_int64, ctypes.POINTER(CacheT), c_void_p, c_void_p, c_int, c_void_p, c_int,
+                                        c_int, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]),
     "csa_index_pool": (c_int, [ctypes.POINTER(CacheT), c_void_p, c_void_p, c_int, c_int, c_int, c_void_p, c_void_p,
                                c_size_t, c_void_p]),
     "csa_sparse_attn": (c_int, [ctypes.POINTER(CacheT), c_void_p, c_int, c_void_p, c_int, c_void_p, c_int, c_void_p,

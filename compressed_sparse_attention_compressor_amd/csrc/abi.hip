@@ -117,6 +117,20 @@ size_t topk_ws_bytes(int B, int Q, int Ns, int k, bool cand) {
   return csa::topk_plan(B, Q, Ns, k).ws_bytes;
 }
 
+// Full scans of one query per workgroup (Q < 4) of at most 32,768 entries
+// select in one launch from the scores and the indexer's histogram hint.
+bool hint_path(int B, int Q, int N_cap, int k, bool cand) {
+  return !cand && Q > 0 && Q < 4 && csa::topk_hint_fits(B, Q, N_cap, k);
+}
+
+// Workspace of csa_index_topk: the scores, then the hinted top-k's (the
+// hint first) or the top-k's own.
+size_t index_topk_ws_bytes(int B, int Q, int N_cap, int k, int C, bool cand) {
+  const size_t s = align256(index_ws_bytes(B, Q, N_cap, cand ? C : 0));
+  if (hint_path(B, Q, N_cap, k, cand)) return s + csa::topk_hint_ws_bytes(B, Q, N_cap);
+  return s + topk_ws_bytes(B, Q, cand ? C : N_cap, k, cand);
+}
+
 int check_attn_common(const csa_cache_t *cache, const uint16_t *q, int H, const int32_t *q_pos, int Q,
                       const uint16_t *swa, const int32_t *swa_pos0, int S, int n_win, float scale, int out_dtype,
                       void *out) {
@@ -172,8 +186,7 @@ const char *csa_status_str(int status) {
 size_t csa_workspace_bytes(int op, int B, int Q, int H_or_k, int n, int C) {
   if (B <= 0 || Q <= 0) return 0;
   switch (op) {
-    case CSA_WS_INDEX_TOPK:
-      return align256(index_ws_bytes(B, Q, n, C)) + topk_ws_bytes(B, Q, C > 0 ? C : n, H_or_k, C > 0);
+    case CSA_WS_INDEX_TOPK: return index_topk_ws_bytes(B, Q, n, H_or_k, C, C > 0);
     case CSA_WS_TOPK: return topk_ws_bytes(B, Q, n, H_or_k, false);
     case CSA_WS_INDEX_POOL:
       if (C < 1 || C > kMaxPoolBlock || H_or_k < 1 || n < 0) return 0;
@@ -271,12 +284,20 @@ int csa_index_topk(const csa_cache_t *cache, const uint8_t *q_idx, const float *
   if (st) return st;
   if (Q == 0 || cache->B == 0 || k == 0) return CSA_OK;
   const size_t sbytes = index_ws_bytes(cache->B, Q, cache->N_cap, cand ? C : 0);
-  const size_t tbytes = topk_ws_bytes(cache->B, Q, cand ? C : cache->N_cap, k, cand != nullptr);
-  const size_t need = align256(sbytes) + tbytes;
+  const size_t need = index_topk_ws_bytes(cache->B, Q, cache->N_cap, k, C, cand != nullptr);
   if (need > 0 && !ws) return CSA_ERR_NULL;
   if (ws_bytes < need) return CSA_ERR_WORKSPACE;
   if (!aligned16(ws)) return CSA_ERR_ALIGN;
   float *scores = reinterpret_cast<float *>(ws);
+  if (hint_path(cache->B, Q, cache->N_cap, k, cand != nullptr)) {
+    uint32_t *hint = reinterpret_cast<uint32_t *>(reinterpret_cast<char *>(ws) + align256(sbytes));
+    const csa::CacheView v = view_of(cache);
+    hipError_t e = csa::launch_index_scores(v, q_idx, w_idx, H_I, q_pos, Q, nullptr, 0, scores, stream, hint);
+    if (e == hipSuccess)
+      e = csa::launch_topk_hint(v, scores, cache->N_cap, q_pos, Q, k, idx_out, score_out, hint, stream);
+    return status_of(e);
+  }
+  const size_t tbytes = need - align256(sbytes);
   st = csa_index_scores(cache, q_idx, w_idx, H_I, q_pos, Q, cand, C, scores, sbytes, stream);
   if (st) return st;
   void *tws = tbytes ? reinterpret_cast<char *>(ws) + align256(sbytes) : nullptr;
@@ -300,6 +321,41 @@ int csa_compress_index_scores(const uint16_t *x, int64_t x_stride_b, const uint1
   st = csa_compress(x, x_stride_b, z, z_stride_b, G, pos_bias, w_ik, tok_begin, T, cache, stream);
   if (st) return st;
   return csa_index_scores(cache, q_idx, w_idx, H_I, q_pos, Q, nullptr, 0, scores, scores_bytes, stream);
+}
+
+int csa_compress_index_topk(const uint16_t *x, int64_t x_stride_b, const uint16_t *z, int64_t z_stride_b, int G,
+                            const float *pos_bias, const uint16_t *w_ik, int64_t tok_begin, int64_t T,
+                            const csa_cache_t *cache, const uint8_t *q_idx, const float *w_idx, int H_I,
+                            const int32_t *q_pos, int Q, int k, int32_t *idx_out, float *score_out, void *ws,
+                            size_t ws_bytes, hipStream_t stream) {
+  int st = check_compress_args(x, x_stride_b, z, z_stride_b, G, pos_bias, w_ik, tok_begin, T, cache);
+  if (st) return st;
+  st = check_index_args(cache, q_idx, w_idx, H_I, q_pos, Q, nullptr, 0);
+  if (st) return st;
+  st = check_topk_args(cache, q_pos, Q, nullptr, 0, k, idx_out);
+  if (st) return st;
+  if (cache->B > 0 && Q > 0 && k > 0) {
+    const size_t need = index_topk_ws_bytes(cache->B, Q, cache->N_cap, k, 0, false);
+    if (need > 0 && !ws) return CSA_ERR_NULL;
+    if (ws_bytes < need) return CSA_ERR_WORKSPACE;
+    if (!aligned16(ws)) return CSA_ERR_ALIGN;
+  }
+  if (cache->B > 0 && Q > 0 && k > 0 && T > 0 && cache->N_cap > 0 &&
+      csa::append_index_fusable(cache->m, T, Q, G, w_ik, cache->B) &&
+      hint_path(cache->B, Q, cache->N_cap, k, false)) {
+    float *scores = reinterpret_cast<float *>(ws);
+    uint32_t *hint = reinterpret_cast<uint32_t *>(reinterpret_cast<char *>(ws) +
+                                                  align256(index_ws_bytes(cache->B, Q, cache->N_cap, 0)));
+    const csa::CacheView v = view_of(cache);
+    hipError_t e = csa::launch_append_index(x, x_stride_b, z, z_stride_b, G, pos_bias, w_ik, tok_begin / cache->m, v,
+                                            q_idx, w_idx, H_I, q_pos, scores, stream, hint);
+    if (e == hipSuccess)
+      e = csa::launch_topk_hint(v, scores, cache->N_cap, q_pos, Q, k, idx_out, score_out, hint, stream);
+    return status_of(e);
+  }
+  st = csa_compress(x, x_stride_b, z, z_stride_b, G, pos_bias, w_ik, tok_begin, T, cache, stream);
+  if (st) return st;
+  return csa_index_topk(cache, q_idx, w_idx, H_I, q_pos, Q, nullptr, 0, k, idx_out, score_out, ws, ws_bytes, stream);
 }
 
 int csa_index_pool(const csa_cache_t *cache, const float *scores, const int32_t *q_pos, int Q, int block,

@@ -198,6 +198,12 @@ __device__ __forceinline__ void raise_fault(uint32_t *flags, uint32_t bits) {
   if (flags) atomicOr(flags, bits);
 }
 
+// Top-k hint: a per-row count of scores by the top 32 - kHintShift bits of their
+// order-preserving keys (score_key), written by the indexer launch that
+// writes the scores and consumed (and left zero) by the top-k launch.
+constexpr int kHintShift = 21;
+constexpr int kHintBins = 1 << (32 - kHintShift);
+
 // Marks a workspace score slot that holds no candidate.
 constexpr uint32_t kNoScoreBits = 0xFFFFFFFFu;
 

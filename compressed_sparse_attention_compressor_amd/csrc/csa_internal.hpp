@@ -25,9 +25,12 @@ hipError_t launch_compress(const uint16_t *x, int64_t x_stride_b, const uint16_t
 
 // Scores of every scanned entry (full scan: [B][Q][N_cap], candidates:
 // [B][Q][C]) into `scores`; slots without a candidate get kNoScoreBits.
+// hint: null, or kHintBins uint32 per row (zero on entry) that a one-query
+// full scan (Q < 4) fills with the row's score histogram for
+// launch_topk_hint; other shapes leave it untouched.
 hipError_t launch_index_scores(const CacheView &c, const uint8_t *q_idx, const float *w_idx, int H_I,
                                const int32_t *q_pos, int Q, const int32_t *cand, int C, float *scores,
-                               hipStream_t stream);
+                               hipStream_t stream, uint32_t *hint = nullptr);
 
 // Decode append fused with the indexer: csa_compress of one entry per
 // sequence (entry `entry`, from rows 0..m-1 of the x/z chunk) followed by
@@ -38,7 +41,7 @@ bool append_index_fusable(int m, int64_t T, int Q, int G, const uint16_t *w_ik, 
 hipError_t launch_append_index(const uint16_t *x, int64_t x_stride_b, const uint16_t *z, int64_t z_stride_b, int G,
                                const float *bias, const uint16_t *w_ik, int64_t entry, const CacheView &c,
                                const uint8_t *q_idx, const float *w_idx, int H_I, const int32_t *q_pos,
-                               float *scores, hipStream_t stream);
+                               float *scores, hipStream_t stream, uint32_t *hint = nullptr);
 
 // Top-k plan: rows with few siblings are split into `nsl` slices of S
 // scores whose own top-k candidates (ws_bytes of workspace) are reduced in
@@ -54,6 +57,16 @@ TopkPlan topk_plan(int B, int Q, int Ns, int k);
 hipError_t launch_topk(const CacheView &c, const float *scores, int Ns, const int32_t *q_pos, int Q,
                        const int32_t *cand, int C, int k, int32_t *idx_out, float *score_out, void *ws,
                        hipStream_t stream);
+
+// Top-k of full-scan rows from their scores and the indexer's histogram
+// hint, for the shapes topk_hint_fits() accepts (few rows of at most 32,768
+// scores).  ws (topk_hint_ws_bytes) starts with the hint, kHintBins uint32
+// per row, which the indexer launch filled and this call leaves zero; the
+// rest holds the compacted candidates.
+bool topk_hint_fits(int B, int Q, int Ns, int k);
+size_t topk_hint_ws_bytes(int B, int Q, int Ns);
+hipError_t launch_topk_hint(const CacheView &c, const float *scores, int Ns, const int32_t *q_pos, int Q, int k,
+                            int32_t *idx_out, float *score_out, void *ws, hipStream_t stream);
 
 // Hierarchical indexer pool: block maxima of full-scan scores, the best
 // n_blocks blocks, and their visible entries as a candidate list

@@ -46,10 +46,18 @@ __device__ __forceinline__ void index_body(
     const uint8_t *__restrict__ ikey, const uint8_t *__restrict__ iscale, const int32_t *__restrict__ n_entries,
     int N_cap, int d_idx, int m, const uint8_t *__restrict__ q_idx, const float *__restrict__ w_idx, int H_I,
     const int32_t *__restrict__ q_pos, int Q, const int32_t *__restrict__ cand, int C, float *__restrict__ scores,
-    int Ns, int bx, int by, int bz, int skip, uint32_t *flags) {
+    int Ns, int bx, int by, int bz, int skip, uint32_t *flags, uint32_t *hint) {
   // Indexer queries of this workgroup (QB queries x 16*HT heads x d_idx bytes),
   // staged once so that the waves read their MFMA fragments from LDS.
   __shared__ __attribute__((aligned(16))) uint8_t qs[QB * HT * 16 * 128];
+  // One-query full scans may also count their scores by the top bits of the
+  // order-preserving key for the top-k launch (kHintBins per row, added
+  // into the row's global counts at the end).
+  constexpr bool kHintable = QB == 1 && !kCand;
+  __shared__ uint32_t hint_lds[kHintable ? kHintBins : 1];
+  const bool use_hint = kHintable && hint != nullptr;
+  if (use_hint)
+    for (int i = threadIdx.x; i < kHintBins; i += kIdxThreads) hint_lds[i] = 0u;
   const int b = bz;
   const int q0 = by * QB;
   const int lane = threadIdx.x & 63;
@@ -260,7 +268,16 @@ __device__ __forceinline__ void index_body(
         if (slot < C) dst[slot] = res;
       } else if (slot < vis[qb] && slot != skip) {
         dst[slot] = res;
+        if (use_hint) atomicAdd(&hint_lds[score_key(res) >> kHintShift], 1u);
       }
+    }
+  }
+  if (use_hint) {
+    __syncthreads();
+    uint32_t *hg = hint + ((int64_t)b * Q + q0) * kHintBins;
+    for (int i = threadIdx.x; i < kHintBins; i += kIdxThreads) {
+      const uint32_t c = hint_lds[i];
+      if (c) atomicAdd(hg + i, c);
     }
   }
 }
@@ -270,9 +287,9 @@ __global__ __launch_bounds__(kIdxThreads) void index_scores_kernel(
     const uint8_t *__restrict__ ikey, const uint8_t *__restrict__ iscale, const int32_t *__restrict__ n_entries,
     int N_cap, int d_idx, int m, const uint8_t *__restrict__ q_idx, const float *__restrict__ w_idx, int H_I,
     const int32_t *__restrict__ q_pos, int Q, const int32_t *__restrict__ cand, int C, float *__restrict__ scores,
-    int Ns, uint32_t *flags) {
+    int Ns, uint32_t *flags, uint32_t *hint) {
   index_body<HT, QB, kCand>(ikey, iscale, n_entries, N_cap, d_idx, m, q_idx, w_idx, H_I, q_pos, Q, cand, C, scores, Ns,
-                            blockIdx.x, blockIdx.y, blockIdx.z, -1, flags);
+                            blockIdx.x, blockIdx.y, blockIdx.z, -1, flags, hint);
 }
 
 // ---------------------------------------------------------------------------
@@ -312,7 +329,7 @@ __device__ __forceinline__ void append_and_score(const AppendArgs &ap, uint8_t *
                                                  int N_cap, int d_idx, const uint8_t *__restrict__ q_idx,
                                                  const float *__restrict__ w_idx, int H_I,
                                                  const int32_t *__restrict__ q_pos, int Q, float *__restrict__ scores,
-                                                 int Ns, int b) {
+                                                 int Ns, int b, uint32_t *hint) {
   __shared__ __attribute__((aligned(16))) float cs[kD];
   __shared__ float kpart[kAppSlices][128];
   __shared__ float ks[128];
@@ -514,7 +531,10 @@ __device__ __forceinline__ void append_and_score(const AppendArgs &ap, uint8_t *
                                     t_new == 3 ? sum : 0.f);
   const int nE = min(n_entries[b], N_cap);
   const int vis = max(0, min(nE, (q_pos[(int64_t)b * Q] + 1) / m));
-  if (lane == 16 * t_new + r_new && ap.entry < vis) scores[(int64_t)b * Q * Ns + ap.entry] = res;
+  if (lane == 16 * t_new + r_new && ap.entry < vis) {
+    scores[(int64_t)b * Q * Ns + ap.entry] = res;
+    if (hint) atomicAdd(hint + (int64_t)b * Q * kHintBins + (score_key(res) >> kHintShift), 1u);
+  }
 }
 
 // Grid: B append workgroups first, then B x tiles indexer workgroups.  The
@@ -526,31 +546,33 @@ template <int HT, bool kGateFull>
 __global__ __launch_bounds__(kIdxThreads, HT >= 4 ? 4 : 5) void append_index_kernel(
     AppendArgs ap, uint8_t *__restrict__ ikey, uint8_t *__restrict__ iscale, const int32_t *__restrict__ n_entries,
     int N_cap, int d_idx, const uint8_t *__restrict__ q_idx, const float *__restrict__ w_idx, int H_I,
-    const int32_t *__restrict__ q_pos, int Q, float *__restrict__ scores, int B, int tiles, uint32_t *flags) {
+    const int32_t *__restrict__ q_pos, int Q, float *__restrict__ scores, int B, int tiles, uint32_t *flags,
+    uint32_t *hint) {
   const int w = blockIdx.x;
   if (w < B) {
     append_and_score<HT, kGateFull>(ap, ikey, iscale, n_entries, N_cap, d_idx, q_idx, w_idx, H_I, q_pos, Q, scores,
-                                    N_cap, w);
+                                    N_cap, w, hint);
     return;
   }
   const int t = w - B;
   index_body<HT, 1, false>(ikey, iscale, n_entries, N_cap, d_idx, ap.m, q_idx, w_idx, H_I, q_pos, Q, nullptr, 0,
-                           scores, N_cap, t % tiles, 0, t / tiles, ap.entry, flags);
+                           scores, N_cap, t % tiles, 0, t / tiles, ap.entry, flags, hint);
 }
 
 template <int HT>
 static void launch_append(const AppendArgs &ap, bool gate_full, const CacheView &c, const uint8_t *q_idx,
-                          const float *w_idx, int H_I, const int32_t *q_pos, float *scores, hipStream_t stream) {
+                          const float *w_idx, int H_I, const int32_t *q_pos, float *scores, hipStream_t stream,
+                          uint32_t *hint) {
   const int tiles = (c.N_cap + kIdxWGEntries - 1) / kIdxWGEntries;
   const unsigned grid = (unsigned)(c.B + c.B * tiles);
   if (gate_full)
     append_index_kernel<HT, true><<<grid, kIdxThreads, 0, stream>>>(ap, c.ikey, c.iscale, c.n_entries, c.N_cap,
                                                                     c.d_idx, q_idx, w_idx, H_I, q_pos, 1, scores,
-                                                                    c.B, tiles, c.flags);
+                                                                    c.B, tiles, c.flags, hint);
   else
     append_index_kernel<HT, false><<<grid, kIdxThreads, 0, stream>>>(ap, c.ikey, c.iscale, c.n_entries, c.N_cap,
                                                                      c.d_idx, q_idx, w_idx, H_I, q_pos, 1, scores,
-                                                                     c.B, tiles, c.flags);
+                                                                     c.B, tiles, c.flags, hint);
 }
 
 bool append_index_fusable(int m, int64_t T, int Q, int G, const uint16_t *w_ik, int B) {
@@ -561,23 +583,25 @@ bool append_index_fusable(int m, int64_t T, int Q, int G, const uint16_t *w_ik, 
 hipError_t launch_append_index(const uint16_t *x, int64_t x_stride_b, const uint16_t *z, int64_t z_stride_b, int G,
                                const float *bias, const uint16_t *w_ik, int64_t entry, const CacheView &c,
                                const uint8_t *q_idx, const float *w_idx, int H_I, const int32_t *q_pos,
-                               float *scores, hipStream_t stream) {
+                               float *scores, hipStream_t stream, uint32_t *hint) {
   AppendArgs ap{x, x_stride_b, z, z_stride_b, bias, w_ik, c.m, (int)entry, c.nope, c.nscale, c.rope};
   const bool full = G == kD;
   if (H_I <= 16)
-    launch_append<1>(ap, full, c, q_idx, w_idx, H_I, q_pos, scores, stream);
+    launch_append<1>(ap, full, c, q_idx, w_idx, H_I, q_pos, scores, stream, hint);
   else if (H_I <= 32)
-    launch_append<2>(ap, full, c, q_idx, w_idx, H_I, q_pos, scores, stream);
+    launch_append<2>(ap, full, c, q_idx, w_idx, H_I, q_pos, scores, stream, hint);
   else
-    launch_append<4>(ap, full, c, q_idx, w_idx, H_I, q_pos, scores, stream);
+    launch_append<4>(ap, full, c, q_idx, w_idx, H_I, q_pos, scores, stream, hint);
   return hipGetLastError();
 }
 
 template <int HT, int QB, bool kCand>
 static void launch_idx(dim3 grid, hipStream_t stream, const CacheView &c, const uint8_t *q_idx, const float *w_idx,
-                       int H_I, const int32_t *q_pos, int Q, const int32_t *cand, int C, float *scores, int Ns) {
+                       int H_I, const int32_t *q_pos, int Q, const int32_t *cand, int C, float *scores, int Ns,
+                       uint32_t *hint = nullptr) {
   index_scores_kernel<HT, QB, kCand><<<grid, kIdxThreads, 0, stream>>>(
-      c.ikey, c.iscale, c.n_entries, c.N_cap, c.d_idx, c.m, q_idx, w_idx, H_I, q_pos, Q, cand, C, scores, Ns, c.flags);
+      c.ikey, c.iscale, c.n_entries, c.N_cap, c.d_idx, c.m, q_idx, w_idx, H_I, q_pos, Q, cand, C, scores, Ns, c.flags,
+      hint);
 }
 
 // ---------------------------------------------------------------------------
@@ -768,7 +792,7 @@ static void launch_prefill(const CacheView &c, const uint8_t *q_idx, const float
 
 template <int HT>
 static void dispatch_idx(const CacheView &c, const uint8_t *q_idx, const float *w_idx, int H_I, const int32_t *q_pos,
-                         int Q, const int32_t *cand, int C, float *scores, hipStream_t stream) {
+                         int Q, const int32_t *cand, int C, float *scores, hipStream_t stream, uint32_t *hint) {
   if (cand) {
     const int Ns = C;
     dim3 grid((C + kIdxWGEntries - 1) / kIdxWGEntries, Q, c.B);
@@ -780,19 +804,19 @@ static void dispatch_idx(const CacheView &c, const uint8_t *q_idx, const float *
     launch_idx<HT, 4, false>(grid, stream, c, q_idx, w_idx, H_I, q_pos, Q, nullptr, 0, scores, c.N_cap);
   } else {
     dim3 grid((c.N_cap + kIdxWGEntries - 1) / kIdxWGEntries, Q, c.B);
-    launch_idx<HT, 1, false>(grid, stream, c, q_idx, w_idx, H_I, q_pos, Q, nullptr, 0, scores, c.N_cap);
+    launch_idx<HT, 1, false>(grid, stream, c, q_idx, w_idx, H_I, q_pos, Q, nullptr, 0, scores, c.N_cap, hint);
   }
 }
 
 hipError_t launch_index_scores(const CacheView &c, const uint8_t *q_idx, const float *w_idx, int H_I,
                                const int32_t *q_pos, int Q, const int32_t *cand, int C, float *scores,
-                               hipStream_t stream) {
+                               hipStream_t stream, uint32_t *hint) {
   if (H_I <= 16)
-    dispatch_idx<1>(c, q_idx, w_idx, H_I, q_pos, Q, cand, C, scores, stream);
+    dispatch_idx<1>(c, q_idx, w_idx, H_I, q_pos, Q, cand, C, scores, stream, hint);
   else if (H_I <= 32)
-    dispatch_idx<2>(c, q_idx, w_idx, H_I, q_pos, Q, cand, C, scores, stream);
+    dispatch_idx<2>(c, q_idx, w_idx, H_I, q_pos, Q, cand, C, scores, stream, hint);
   else
-    dispatch_idx<4>(c, q_idx, w_idx, H_I, q_pos, Q, cand, C, scores, stream);
+    dispatch_idx<4>(c, q_idx, w_idx, H_I, q_pos, Q, cand, C, scores, stream, hint);
   return hipGetLastError();
 }
 

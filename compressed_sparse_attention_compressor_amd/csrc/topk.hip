@@ -313,6 +313,327 @@ __global__ __launch_bounds__(kRegThreads) void topk_reg_kernel(const float *__re
 }
 
 // ---------------------------------------------------------------------------
+// Rows with a histogram hint (decode: few rows of at most 32,768 scores).
+// The indexer launch that wrote a row's scores also counted them by the top
+// 11 bits of their order-preserving keys (kHintBins words per row).  Two
+// launches, both spread over the whole GPU where the bytes are:
+//   1. compaction: one workgroup per slice of 4,096 scores reads the row's
+//      counts, finds the bin holding the k-th largest key (one block scan,
+//      the same in every slice) and writes the slice's keys in that bin or
+//      above, in entry order, with its counts above / inside the bin;
+//   2. final: one workgroup per row checks the counts of all slices against
+//      the hint, settles the exact threshold among the candidates of the
+//      bin (a histogram of the next 11 bits, then a gather-and-rank of at
+//      most 64 keys or one more radix pass) and places the selection.  It
+//      leaves the row's hint zero for the next indexer launch.
+// A hint that does not match the scores (a workspace that an earlier call
+// did not leave zero), or a threshold bin with more candidates than one
+// workgroup holds, only costs time: the final launch then selects from the
+// whole row.
+constexpr int kHintSlice = 4096;                      // scores per compaction workgroup
+constexpr int kHintPer = kHintSlice / kRegThreads;    // 8 contiguous scores per thread
+constexpr int kHintCand = 8;                          // candidates per thread in the final launch
+constexpr int kHintSlot = kRegThreads * kHintCand / (kRegN / kHintSlice);  // 512 candidate slots read per slice
+
+struct HintArgs {
+  const float *scores;
+  int Ns;
+  const int32_t *n_entries;
+  int N_cap, m;
+  const int32_t *q_pos;
+  int Q, k, nsl;
+  uint32_t *hint;       // [rows][kHintBins]
+  int32_t *cand_i;      // [rows][nsl * kHintSlice] entry of each candidate
+  uint32_t *cand_k;     // [rows][nsl * kHintSlice] its key
+  int32_t *slice_info;  // [rows][nsl][3]: keys above the bin, keys in it, visible keys
+  int32_t *row_info;    // [rows][4]: bin, keys above it (hint), keys in it (hint), hint total
+  int32_t *idx_out;
+  float *score_out;
+};
+
+__device__ __forceinline__ int hint_visible(const HintArgs &a, int b, int64_t row) {
+  const int nE = min(a.n_entries[b], a.N_cap);
+  return max(0, min(min(nE, (a.q_pos[row] + 1) / a.m), a.Ns));
+}
+
+// The hint's block scan: thread t holds bins 2047 - 4t .. 2044 - 4t.  Returns
+// the hint total and, when 0 < min(k, total) < total, the bin holding the
+// min(k, total)-th largest key, the count above it and inside it (bin -1:
+// every counted key is taken).  Two barriers; sh holds NT/64 + 3 ints.
+__device__ __forceinline__ void hint_bin(uint4 hc, int k, int *sh, int &bin, int &above, int &inside, int &all) {
+  constexpr int kW = kRegThreads / 64;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int c[4] = {(int)hc.w, (int)hc.z, (int)hc.y, (int)hc.x};  // descending bins
+  const int tot = c[0] + c[1] + c[2] + c[3];
+  const int inc = wave_incl_scan(tot);
+  if (lane == 63) sh[wave] = inc;
+  __syncthreads();
+  int base = 0, sum = 0;
+#pragma unroll
+  for (int w = 0; w < kW; ++w) {
+    const int t = sh[w];
+    base += w < wave ? t : 0;
+    sum += t;
+  }
+  all = __builtin_amdgcn_readfirstlane(sum);
+  const int ke = min(k, all);
+  if (tid == 0) sh[kW] = -1;
+  __syncthreads();
+  int ab = base + inc - tot;
+  if (ke > 0 && ke < all) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if (ab < ke && ke <= ab + c[j]) {
+        sh[kW] = kHintBins - 1 - 4 * tid - j;
+        sh[kW + 1] = ab;
+        sh[kW + 2] = c[j];
+      }
+      ab += c[j];
+    }
+  }
+  __syncthreads();
+  bin = __builtin_amdgcn_readfirstlane(sh[kW]);
+  above = bin >= 0 ? __builtin_amdgcn_readfirstlane(sh[kW + 1]) : 0;
+  inside = bin >= 0 ? __builtin_amdgcn_readfirstlane(sh[kW + 2]) : 0;
+}
+
+__global__ __launch_bounds__(kRegThreads) void topk_hint_compact_kernel(HintArgs a) {
+  constexpr int kW = kRegThreads / 64;
+  __shared__ int sh[kW + 3];
+  __shared__ int wsum[3][kW];
+  const int q = blockIdx.x / a.nsl, sl = blockIdx.x % a.nsl, b = blockIdx.y;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int64_t row = (int64_t)b * a.Q + q;
+  const uint4 hc = *reinterpret_cast<const uint4 *>(a.hint + row * kHintBins + (kHintBins - 4 - 4 * tid));
+  const int off = sl * kHintSlice;
+  const int e0 = off + kHintPer * tid;                     // this thread's first element
+  const float *src = a.scores + row * a.Ns;
+  uint32_t key[kHintPer];
+  auto to_key = [](float x) { return __float_as_uint(x) != kNoScoreBits ? score_key(x) : 0u; };
+  if ((a.Ns & 3) == 0) {
+#pragma unroll
+    for (int v = 0; v < kHintPer / 4; ++v) {
+      const float4 t4 = *reinterpret_cast<const float4 *>(src + min(e0 + 4 * v, a.Ns - 4));
+      key[4 * v + 0] = to_key(t4.x);
+      key[4 * v + 1] = to_key(t4.y);
+      key[4 * v + 2] = to_key(t4.z);
+      key[4 * v + 3] = to_key(t4.w);
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < kHintPer; ++j) key[j] = to_key(src[min(e0 + j, a.Ns - 1)]);
+  }
+  const int n = hint_visible(a, b, row);
+#pragma unroll
+  for (int j = 0; j < kHintPer; ++j)
+    if (e0 + j >= n) key[j] = 0u;
+
+  int bin, above, inside, all;
+  hint_bin(hc, a.k, sh, bin, above, inside, all);
+  // candidates: every visible key in the bin or above (all of them when the
+  // hint takes every key)
+  const uint32_t lo = bin >= 0 ? (uint32_t)bin : 0u;
+  int ng = 0, ne = 0, nv = 0;
+#pragma unroll
+  for (int j = 0; j < kHintPer; ++j) {
+    const uint32_t kk = key[j];
+    const uint32_t d = kk >> kHintShift;
+    nv += kk != 0u;
+    ng += kk != 0u && d > lo;
+    ne += kk != 0u && d == lo;
+  }
+  const int mine = ng + ne;
+  const int inc = wave_incl_scan(mine);
+  if (lane == 63) wsum[0][wave] = inc;
+  const int wg = wave_sum(ng), we = wave_sum(ne), wv = wave_sum(nv);
+  if (lane == 0) {
+    wsum[1][wave] = wg;
+    wsum[2][wave] = we * 65536 + wv;  // both below 65,536 per wave
+  }
+  __syncthreads();
+  int base = 0, sg = 0, se = 0, sv = 0;
+#pragma unroll
+  for (int w = 0; w < kW; ++w) {
+    base += w < wave ? wsum[0][w] : 0;
+    sg += wsum[1][w];
+    se += wsum[2][w] >> 16;
+    sv += wsum[2][w] & 0xFFFF;
+  }
+  int pos = base + inc - mine;
+  const int64_t cb = row * (int64_t)a.nsl * kHintSlice + off;
+#pragma unroll
+  for (int j = 0; j < kHintPer; ++j) {
+    const uint32_t kk = key[j];
+    if (kk != 0u && (kk >> kHintShift) >= lo) {
+      a.cand_i[cb + pos] = e0 + j;
+      a.cand_k[cb + pos] = kk;
+      ++pos;
+    }
+  }
+  if (tid == 0) {
+    int32_t *si = a.slice_info + (row * a.nsl + sl) * 3;
+    si[0] = sg;
+    si[1] = se;
+    si[2] = sv;
+    if (sl == 0) {
+      int32_t *ri = a.row_info + row * 4;
+      ri[0] = bin;
+      ri[1] = above;
+      ri[2] = inside;
+      ri[3] = all;
+    }
+  }
+}
+
+__global__ __launch_bounds__(kRegThreads) void topk_hint_final_kernel(HintArgs a) {
+  constexpr int NT = kRegThreads;
+  constexpr int kW = NT / 64;
+  constexpr int kFullPer = kRegN / NT;  // 64: the fallback holds a whole row
+  constexpr int kMaxSl = kRegN / kHintSlice;
+  __shared__ int hist[kW * kBins];      // also the placement's staging area
+  __shared__ int sh[kW + 3];
+  __shared__ int wred[3 * kW];
+  __shared__ uint32_t bin_keys[64];
+  __shared__ int cnt[2 * (kFullPer / 4) * kW];
+  __shared__ int n_bin;
+  constexpr int kStage = kW * kBins / 2;
+  int (*hist2)[kBins] = reinterpret_cast<int (*)[kBins]>(hist);
+  const int q = blockIdx.x, b = blockIdx.y;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int64_t row = (int64_t)b * a.Q + q;
+  int32_t *out_i = a.idx_out + row * a.k;
+  float *out_s = a.score_out ? a.score_out + row * a.k : nullptr;
+
+  // The candidates in entry order, loaded before their counts are known:
+  // element i = v*(4*NT) + 4*tid + u is position i % kHintSlot of slice
+  // i / kHintSlot (slots past a slice's count are masked below; a slice with
+  // more than kHintSlot candidates sends the row to the fallback).
+  uint32_t key[kHintCand];
+  int32_t cid[kHintCand];
+#pragma unroll
+  for (int j = 0; j < kHintCand; ++j) {
+    const int i = (j >> 2) * (4 * NT) + 4 * tid + (j & 3);
+    const int s = min(i / kHintSlot, a.nsl - 1);
+    const int64_t at = (row * a.nsl + s) * (int64_t)kHintSlice + (i % kHintSlot);
+    key[j] = a.cand_k[at];
+    cid[j] = a.cand_i[at];
+  }
+  // counts of every slice (uniform loads), checked against the hint
+  const int32_t *ri = a.row_info + row * 4;
+  const int bin = ri[0], above = ri[1], inside = ri[2], all = ri[3];
+  int cnt_s[kMaxSl];
+  int sg = 0, se = 0, sv = 0;
+  bool big = false;
+#pragma unroll
+  for (int s = 0; s < kMaxSl; ++s) {
+    const bool in = s < a.nsl;
+    const int32_t *si = a.slice_info + (row * a.nsl + (in ? s : 0)) * 3;
+    const int g = in ? si[0] : 0, e = in ? si[1] : 0, v = in ? si[2] : 0;
+    sg += g;
+    se += e;
+    sv += v;
+    cnt_s[s] = g + e;
+    big = big || g + e > kHintSlot;
+  }
+  const int n_valid = sv;
+  const int k_eff = min(a.k, n_valid);
+  // the hint matches when its total is the row's visible count and, with a
+  // threshold bin, the counts above and inside it are the scores' own
+  const bool ok = all == n_valid && !big && (bin >= 0 ? (sg == above && se == inside) : true);
+  if (tid < kHintBins / 4)  // the hint is left zero for the next indexer launch
+    *reinterpret_cast<uint4 *>(a.hint + row * kHintBins + 4 * tid) = uint4{0u, 0u, 0u, 0u};
+  if (ok) {
+#pragma unroll
+    for (int j = 0; j < kHintCand; ++j) {
+      const int i = (j >> 2) * (4 * NT) + 4 * tid + (j & 3);
+      const int s = i / kHintSlot;
+      int c = 0;
+#pragma unroll
+      for (int t = 0; t < kMaxSl; ++t) c = s == t ? cnt_s[t] : c;
+      if (s >= a.nsl || i % kHintSlot >= c) {
+        key[j] = 0u;
+        cid[j] = -1;
+      }
+    }
+    for (int i = tid; i < kBins; i += NT) hist[i] = 0;
+    if (tid == 0) n_bin = 0;
+    __syncthreads();  // the histogram is zero before any thread adds to it
+    uint32_t thr = 1u;  // every candidate (all visible keys) when there is no bin
+    int need = 0, n_eq = 0;
+    if (bin >= 0) {
+      // the next 11 bits of the keys in the bin
+#pragma unroll
+      for (int j = 0; j < kHintCand; ++j)
+        if (key[j] != 0u && (key[j] >> kHintShift) == (uint32_t)bin) atomicAdd(&hist[(key[j] >> 10) & 0x7FFu], 1);
+      __syncthreads();
+      int k_rem = k_eff - above;
+      int e2, ab, tt;
+      find_digit<NT>(hist2, 1, kBins, k_rem, sh, e2, ab, tt);
+      k_rem -= ab;
+      const uint32_t p12 = ((uint32_t)bin << 11) | (uint32_t)e2;
+      const int c2 = __builtin_amdgcn_readfirstlane(hist[e2]);
+      if (c2 <= 64) {
+        int mine = 0;
+#pragma unroll
+        for (int j = 0; j < kHintCand; ++j) mine += key[j] != 0u && (key[j] >> 10) == p12;
+        const int winc = wave_incl_scan(mine);
+        const int wtot = __builtin_amdgcn_readlane(winc, 63);
+        int wb = 0;
+        if (wtot > 0) {
+          if (lane == 63) wb = atomicAdd(&n_bin, wtot);
+          wb = __builtin_amdgcn_readlane(wb, 63);
+        }
+        int pos = wb + winc - mine;
+#pragma unroll
+        for (int j = 0; j < kHintCand; ++j)
+          if (key[j] != 0u && (key[j] >> 10) == p12) bin_keys[pos++] = key[j];
+        __syncthreads();
+        rank_gathered<NT>(bin_keys, c2, k_rem, sh, thr, need, n_eq);
+      } else {
+        // a crowded bin: one more pass over bits 9..0
+        __syncthreads();
+        for (int i = tid; i < kBins; i += NT) hist[i] = 0;
+        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < kHintCand; ++j)
+          if (key[j] != 0u && (key[j] >> 10) == p12) atomicAdd(&hist[key[j] & 0x3FFu], 1);
+        __syncthreads();
+        int e3;
+        find_digit<NT>(hist2, 1, 1024, k_rem, sh, e3, ab, tt);
+        k_rem -= ab;
+        thr = (p12 << 10) | (uint32_t)e3;
+        need = k_rem;
+        n_eq = __builtin_amdgcn_readfirstlane(hist[e3]);  // every key equal to thr lies in this bin
+      }
+    }
+    place_selected<NT, kHintCand, true, kStage>(key, cid, thr, need, n_eq, k_eff, a.k, cnt, hist,
+                                                reinterpret_cast<float *>(hist + kStage), out_i, out_s,
+                                                [](int i) { return i; });
+    return;
+  }
+  // the hint did not match: select from the whole row
+  const float *src = a.scores + row * a.Ns;
+  const int n = hint_visible(a, b, row);
+  uint32_t fkey[kFullPer];
+  auto to_key = [](float x) { return __float_as_uint(x) != kNoScoreBits ? score_key(x) : 0u; };
+#pragma unroll
+  for (int j = 0; j < kFullPer; ++j) {
+    const int i = (j >> 2) * (4 * NT) + 4 * tid + (j & 3);
+    const float x = src[min(i, max(a.Ns - 1, 0))];
+    fkey[j] = i < n ? to_key(x) : 0u;
+  }
+  int ke, need, n_eq;
+  uint32_t thr;
+  linear_threshold<NT, kFullPer>(fkey, a.k, hist, sh, wred, bin_keys, &n_bin, ke, thr, need, n_eq);
+  const int32_t no_cid[1] = {0};
+  place_selected<NT, kFullPer, false, kStage>(fkey, no_cid, thr, need, n_eq, ke, a.k, cnt, hist,
+                                              reinterpret_cast<float *>(hist + kStage), out_i, out_s,
+                                              [](int i) { return i; });
+}
+
+// ---------------------------------------------------------------------------
 // Few, long rows (B*Q < 256 rows of at least 65,536 scores): a radix
 // selection spread over slices of 4,096 scores per workgroup, the digits of
 // the order-preserving key (11, 11 and 10 bits) resolved one launch at a
@@ -658,6 +979,44 @@ static void launch_one(const CacheView &c, const float *scores, int Ns, int len,
   else
     topk_tiled_kernel<<<dim3(Q, c.B), kTopkThreads, 0, stream>>>(scores, Ns, c.n_entries, c.N_cap, c.m, q_pos, Q, cand,
                                                                  C, k, idx_out, score_out);
+}
+
+bool topk_hint_fits(int B, int Q, int Ns, int k) {
+  return (int64_t)B * Q < 256 && Ns > 0 && Ns <= kRegN && k > 0;
+}
+
+size_t topk_hint_ws_bytes(int B, int Q, int Ns) {
+  const int64_t rows = (int64_t)B * Q;
+  const int nsl = (Ns + kHintSlice - 1) / kHintSlice;
+  return (size_t)rows * ((size_t)kHintBins * 4 + (size_t)nsl * kHintSlice * 8 + (size_t)nsl * 3 * 4 + 4 * 4);
+}
+
+hipError_t launch_topk_hint(const CacheView &c, const float *scores, int Ns, const int32_t *q_pos, int Q, int k,
+                            int32_t *idx_out, float *score_out, void *ws, hipStream_t stream) {
+  const int64_t rows = (int64_t)c.B * Q;
+  const int nsl = (Ns + kHintSlice - 1) / kHintSlice;
+  HintArgs a;
+  a.scores = scores;
+  a.Ns = Ns;
+  a.n_entries = c.n_entries;
+  a.N_cap = c.N_cap;
+  a.m = c.m;
+  a.q_pos = q_pos;
+  a.Q = Q;
+  a.k = k;
+  a.nsl = nsl;
+  a.hint = reinterpret_cast<uint32_t *>(ws);
+  a.cand_i = reinterpret_cast<int32_t *>(a.hint + rows * kHintBins);
+  a.cand_k = reinterpret_cast<uint32_t *>(a.cand_i + rows * nsl * kHintSlice);
+  a.slice_info = reinterpret_cast<int32_t *>(a.cand_k + rows * nsl * kHintSlice);
+  a.row_info = a.slice_info + rows * nsl * 3;
+  a.idx_out = idx_out;
+  a.score_out = score_out;
+  topk_hint_compact_kernel<<<dim3(Q * nsl, c.B), kRegThreads, 0, stream>>>(a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  topk_hint_final_kernel<<<dim3(Q, c.B), kRegThreads, 0, stream>>>(a);
+  return hipGetLastError();
 }
 
 hipError_t launch_topk(const CacheView &c, const float *scores, int Ns, const int32_t *q_pos, int Q,

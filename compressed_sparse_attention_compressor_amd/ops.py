@@ -67,11 +67,11 @@ def workspace_bytes(op, B, Q, H, n_or_k, C=0) -> int:
     return int(lib().csa_workspace_bytes(op, B, Q, H, n_or_k, C))
 
 
-def _workspace(nbytes, ws, device):
+def _workspace(nbytes, ws, device, zero=False):
     if nbytes == 0:
         return None, 0
     if ws is None:
-        ws = torch.empty(nbytes, dtype=torch.uint8, device=device)
+        ws = (torch.zeros if zero else torch.empty)(nbytes, dtype=torch.uint8, device=device)
     return ws, ws.numel() * ws.element_size()
 
 
@@ -130,10 +130,42 @@ def index_topk(cache: Cache, q_idx, w_idx, q_pos, k, cand=None, want_scores=Fals
     idx = out if out is not None else torch.empty(B, Q, k, dtype=torch.int32, device=dev)
     sc = torch.empty(B, Q, k, dtype=torch.float32, device=dev) if want_scores else None
     need = workspace_bytes(WS_INDEX_TOPK, B, Q, k, cache.N_cap, C)
-    ws, wsb = _workspace(need, ws, dev)
+    # a zeroed workspace lets the first call start from the indexer's hint
+    ws, wsb = _workspace(need, ws, dev, zero=True)
     cs = cache.struct()
     check(lib().csa_index_topk(ctypes.byref(cs), _ptr(q_idx), _ptr(w_idx), H_I, _ptr(q_pos), Q, _ptr(cand), C, int(k),
                                _ptr(idx), _ptr(sc), _ptr(ws), wsb, _stream()), "csa_index_topk")
+    return idx, sc
+
+
+def compress_index_topk(cache: Cache, x, z, pos_bias, w_ik, tok_begin, q_idx, w_idx, q_pos, k, want_scores=False,
+                        ws=None, out=None):
+    """compress() then a full-scan index_topk(): the decode step's front half
+    (append + indexer in one launch for a one-entry decode append, then the
+    hinted top-k).  Returns (idx, scores or None)."""
+    _need(x, torch.bfloat16, "x")
+    _need(z, torch.bfloat16, "z")
+    _need(pos_bias, torch.float32, "pos_bias")
+    _need(q_idx, torch.uint8, "q_idx")
+    _need(w_idx, torch.float32, "w_idx")
+    _need(q_pos, torch.int32, "q_pos")
+    B, T = x.shape[0], x.shape[1]
+    G = z.shape[2]
+    if x.stride(2) != 1 or x.stride(1) != D or z.stride(2) != 1 or z.stride(1) != G:
+        raise ValueError("x and z rows must be contiguous")
+    if w_ik is not None:
+        _need(w_ik, torch.bfloat16, "w_ik")
+    Q, H_I = q_idx.shape[1], q_idx.shape[2]
+    dev = q_idx.device
+    idx = out if out is not None else torch.empty(B, Q, k, dtype=torch.int32, device=dev)
+    sc = torch.empty(B, Q, k, dtype=torch.float32, device=dev) if want_scores else None
+    need = workspace_bytes(WS_INDEX_TOPK, B, Q, k, cache.N_cap, 0)
+    ws, wsb = _workspace(need, ws, dev, zero=True)
+    cs = cache.struct()
+    check(lib().csa_compress_index_topk(_ptr(x), x.stride(0), _ptr(z), z.stride(0), G, _ptr(pos_bias), _ptr(w_ik),
+                                        int(tok_begin), int(T), ctypes.byref(cs), _ptr(q_idx), _ptr(w_idx), H_I,
+                                        _ptr(q_pos), Q, int(k), _ptr(idx), _ptr(sc), _ptr(ws), wsb, _stream()),
+          "csa_compress_index_topk")
     return idx, sc
 
 

@@ -119,7 +119,17 @@ int csa_compress(const uint16_t *x, int64_t x_stride_b, const uint16_t *z, int64
  *            NULL for a full scan (C ignored)
  *   idx_out  int32 [B][Q][k]      score_out fp32 [B][Q][k] or NULL (NaN in padding)
  *   ws       >= csa_workspace_bytes(CSA_WS_INDEX_TOPK, ...) bytes, 256-byte aligned
- *            (fp32 scores of every scanned entry, then the top-k workspace). */
+ *            (fp32 scores of every scanned entry, then the top-k workspace).
+ * A full scan of one to three queries per sequence (fewer than 256 rows)
+ * over at most 32,768 entries selects from a histogram hint: the indexer
+ * launch also counts each row's scores by the top 11 bits of their
+ * order-preserving keys into the workspace; a compaction launch over
+ * slices of 4,096 scores keeps the keys in the bin of the k-th largest
+ * and above, and a final launch per row settles the selection among them
+ * and leaves the counts zero.  The counts are checked against the scores
+ * themselves, so any workspace contents give the same result; counts that
+ * do not match (a workspace that was not zero on its first use) only make
+ * that one call select from the whole row, more slowly. */
 int csa_index_topk(const csa_cache_t *cache, const uint8_t *q_idx, const float *w_idx, int H_I,
                    const int32_t *q_pos, int Q, const int32_t *cand, int C, int k, int32_t *idx_out,
                    float *score_out, void *ws, size_t ws_bytes, hipStream_t stream);
@@ -149,6 +159,19 @@ int csa_compress_index_scores(const uint16_t *x, int64_t x_stride_b, const uint1
                               const float *pos_bias, const uint16_t *w_ik, int64_t tok_begin, int64_t T,
                               const csa_cache_t *cache, const uint8_t *q_idx, const float *w_idx, int H_I,
                               const int32_t *q_pos, int Q, float *scores, size_t scores_bytes, hipStream_t stream);
+
+/* The decode step's front half in two launches: csa_compress_index_scores
+ * followed by the top-k of csa_index_topk (full scan, no candidates), with
+ * the same arguments, checks and results.  ws is the workspace of
+ * csa_index_topk (csa_workspace_bytes(CSA_WS_INDEX_TOPK, B, Q, k, N_cap, 0));
+ * when the append fuses with the indexer (see csa_compress_index_scores)
+ * and the top-k takes the hinted path (see csa_index_topk), the whole call
+ * is three launches: append + indexer, compaction, final selection. */
+int csa_compress_index_topk(const uint16_t *x, int64_t x_stride_b, const uint16_t *z, int64_t z_stride_b, int G,
+                            const float *pos_bias, const uint16_t *w_ik, int64_t tok_begin, int64_t T,
+                            const csa_cache_t *cache, const uint8_t *q_idx, const float *w_idx, int H_I,
+                            const int32_t *q_pos, int Q, int k, int32_t *idx_out, float *score_out, void *ws,
+                            size_t ws_bytes, hipStream_t stream);
 
 /* Candidate pool of the hierarchical sparse indexer ([V4.1] "Hierarchical
  * Sparse Indexer" bullet and Fig. 5: the first Full layer ranks blocks of

@@ -67,6 +67,8 @@ _SIGS = {
                              ctypes.POINTER(CacheT), c_void_p]),
     "csa_index_topk": (c_int, [ctypes.POINTER(CacheT), c_void_p, c_void_p, c_int, c_void_p, c_int, c_void_p, c_int,
                                c_int, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]),
+    "csa_index_topk_noalloc": (c_int, [ctypes.POINTER(CacheT), c_void_p, c_void_p, c_int, c_void_p, c_int, c_void_p,
+                                       c_int, c_int, c_void_p, c_void_p, c_void_p]),
     "csa_index_scores": (c_int, [ctypes.POINTER(CacheT), c_void_p, c_void_p, c_int, c_void_p, c_int, c_void_p,
                                  c_int, c_void_p, c_size_t, c_void_p]),
     "csa_topk": (c_int, [ctypes.POINTER(CacheT), c_void_p, c_void_p, c_int, c_void_p, c_int, c_int, c_void_p,

@@ -16,6 +16,12 @@ __device__ uint32_t g_fault_taken;
 
 __global__ void take_fault_word_kernel(uint32_t *word, uint32_t *taken) { *taken = atomicExch(word, 0u); }
 
+// Fixed scratch of csa_index_topk_noalloc, one copy per GPU, held until the
+// process ends.  Host code never passes this name to a kernel (on the host
+// it is only a stand-in): the device address comes from hipGetSymbolAddress,
+// looked up once per device.
+static __device__ __align__(256) uint8_t scratch[CSA_NOALLOC_SCRATCH_BYTES];
+
 namespace {
 
 thread_local int g_last_hip_error = 0;
@@ -47,6 +53,29 @@ hipError_t fault_words(uint32_t **word, uint32_t **taken) {
   }
   *word = w;
   if (taken) *taken = g_taken_ptr[dev].load(std::memory_order_acquire);
+  return hipSuccess;
+}
+
+std::atomic<void *> g_scratch_ptr[kMaxDevices];
+
+// Device address of this GPU's scratch (the current device's), looked up on
+// the first call on the device.
+hipError_t scratch_address(void **out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  void *p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lock(g_word_mu);
+    p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (!p) {
+      e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      if (e != hipSuccess) return e;
+      g_scratch_ptr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
   return hipSuccess;
 }
 
@@ -179,6 +208,7 @@ const char *csa_status_str(int status) {
     case CSA_ERR_UNSUPPORTED: return "sizes outside the supported envelope";
     case CSA_ERR_WORKSPACE: return "workspace too small";
     case CSA_ERR_HIP: return "HIP launch failure";
+    case CSA_ERR_SCRATCH: return "the call needs more than the fixed scratch of the allocation-free entry point";
     default: return "unknown status";
   }
 }
@@ -302,6 +332,26 @@ int csa_index_topk(const csa_cache_t *cache, const uint8_t *q_idx, const float *
   if (st) return st;
   void *tws = tbytes ? reinterpret_cast<char *>(ws) + align256(sbytes) : nullptr;
   return csa_topk(cache, scores, q_pos, Q, cand, C, k, idx_out, score_out, tws, tbytes, stream);
+}
+
+int csa_index_topk_noalloc(const csa_cache_t *cache, const uint8_t *q_idx, const float *w_idx, int H_I,
+                           const int32_t *q_pos, int Q, const int32_t *cand, int C, int k, int32_t *idx_out,
+                           float *score_out, hipStream_t stream) {
+  int st = check_index_args(cache, q_idx, w_idx, H_I, q_pos, Q, cand, C);
+  if (st) return st;
+  st = check_topk_args(cache, q_pos, Q, cand, C, k, idx_out);
+  if (st) return st;
+  if (Q == 0 || cache->B == 0 || k == 0) return CSA_OK;
+  const size_t need = index_topk_ws_bytes(cache->B, Q, cache->N_cap, k, C, cand != nullptr);
+  if (need > (size_t)CSA_NOALLOC_SCRATCH_BYTES) return CSA_ERR_SCRATCH;
+  void *ws = nullptr;
+  hipError_t e = scratch_address(&ws);
+  if (e != hipSuccess) return status_of(e);
+  // nothing in the scratch has to start at zero: the top-k hint counts are
+  // checked against the scores (every call leaves them zero, and the array
+  // starts zero)
+  return csa_index_topk(cache, q_idx, w_idx, H_I, q_pos, Q, cand, C, k, idx_out, score_out, ws,
+                        (size_t)CSA_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 int csa_compress_index_scores(const uint16_t *x, int64_t x_stride_b, const uint16_t *z, int64_t z_stride_b, int G,

@@ -52,7 +52,8 @@ typedef enum {
   CSA_ERR_ALIGN = -3,       /* a plane or tensor is not 16-byte aligned         */
   CSA_ERR_UNSUPPORTED = -4, /* sizes outside the supported envelope             */
   CSA_ERR_WORKSPACE = -5,   /* workspace smaller than csa_workspace_bytes()     */
-  CSA_ERR_HIP = -6          /* a kernel launch failed (csa_last_hip_error())    */
+  CSA_ERR_HIP = -6,         /* a kernel launch failed (csa_last_hip_error())    */
+  CSA_ERR_SCRATCH = -7      /* more than CSA_NOALLOC_SCRATCH_BYTES needed        */
 } csa_status;
 
 typedef enum { CSA_OUT_F32 = 0, CSA_OUT_BF16 = 1 } csa_out_dtype;
@@ -133,6 +134,22 @@ int csa_compress(const uint16_t *x, int64_t x_stride_b, const uint16_t *z, int64
 int csa_index_topk(const csa_cache_t *cache, const uint8_t *q_idx, const float *w_idx, int H_I,
                    const int32_t *q_pos, int Q, const int32_t *cand, int C, int k, int32_t *idx_out,
                    float *score_out, void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* csa_index_topk for callers that cannot allocate (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * arguments without the workspace, the same checks and the same results.
+ * The workspace is a fixed device array of CSA_NOALLOC_SCRATCH_BYTES in the
+ * library, one per GPU, held from the first call on that GPU until the
+ * process ends; the call itself allocates nothing.  A call whose
+ * csa_workspace_bytes(CSA_WS_INDEX_TOPK, ...) exceeds that size returns
+ * CSA_ERR_SCRATCH and launches nothing (the batched 128K decode, 32 rows of
+ * 32,768 entries at k = 512, needs 12.9 MB).  Every call on a GPU uses that
+ * GPU's one array: calls that overlap on one GPU (other streams or host
+ * threads) race and must be serialised by the caller. */
+#define CSA_NOALLOC_SCRATCH_BYTES (16u << 20)
+int csa_index_topk_noalloc(const csa_cache_t *cache, const uint8_t *q_idx, const float *w_idx, int H_I,
+                           const int32_t *q_pos, int Q, const int32_t *cand, int C, int k, int32_t *idx_out,
+                           float *score_out, hipStream_t stream);
 
 /* The two stages of csa_index_topk as separate calls (same semantics):
  * csa_index_scores writes the score of every scanned entry into

@@ -234,3 +234,12 @@ def test_fp8_window_checks(L):
 def test_read_device_flags_null(L):
     # a null output pointer fails before any HIP call
     assert L.csa_read_device_flags(None, None) == ENULL
+
+
+def test_noalloc_rejects_beyond_the_fixed_scratch(L):
+    # 64 rows of 65,536 entries need far more than the fixed scratch: the call
+    # is refused on the host, before any HIP call
+    c = _cache(B=64, N=65536)
+    assert L.csa_index_topk_noalloc(ctypes.byref(c), P, P, 32, P, 1, None, 0, 512, P, None, None) == -7
+    assert L.csa_status_str(-7)
+    assert L.csa_index_topk_noalloc(None, P, P, 32, P, 1, None, 0, 512, P, None, None) == ENULL

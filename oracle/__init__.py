@@ -47,6 +47,7 @@ from .csa import (  # noqa: F401
     topk_select,
     index_topk,
     attention,
+    rope_rotate,
     sparse_attention,
     dense_attention,
     csa2_pair,

@@ -27,8 +27,20 @@ design notes of the repository):
 * Attention [V4], Fig. 3 and Fig. 4: one softmax over the union of the
   selected (or, for HCA, all visible) compressed entries and the sliding
   window of raw rows at positions max(0, p - n_win + 1) .. p; the key and
-  the value are the same full D-channel decoded entry; no rotation is
-  applied to the positional channels (they are data here).
+  the value are the same full D-channel decoded entry.  Without a rotary
+  base the positional channels are data.
+* Fused RoPE epilogue ([V4.1], "推論カーネル" bullet: a fused
+  RoPE-attention-RoPE-cast kernel; [V4], CSA paragraph: the positional
+  channels are stored in BF16), taken when a rotary base is given: the
+  last d_rope channels of the query, of every key and of every window row
+  are rotated as adjacent pairs (2i, 2i+1) by the angle pos * base^(-2i /
+  d_rope), the rotation of the original rotary embedding; the query's
+  position is p, a compressed entry's is its last raw token (j+1)*m - 1,
+  a window row's is its own raw position.  The rotated operands are
+  rounded to bf16, the precision the channels are stored in, and the same
+  rotated key is the value.  After the softmax-weighted sum, the output's
+  positional channels are rotated back by -p; the cast to the output type
+  follows.
 """
 
 from __future__ import annotations
@@ -202,17 +214,52 @@ def block_pool(scores, V: int, block: int, n_blocks: int) -> tuple[np.ndarray, n
     return pool, kept
 
 
-def attention(q_u16, keys: np.ndarray, scale) -> tuple[np.ndarray, np.ndarray]:
+def rope_rotate(x, pos, base, sign: float = 1.0) -> np.ndarray:
+    """Rotary rotation of the positional channels, float64.
+
+    x float64 [..., d] (d even, the positional channels only); pos an integer
+    or an array broadcasting against x's leading dimensions.  Channel pair
+    (2i, 2i+1) is turned by sign * pos * base^(-2i/d) radians:
+    (a, b) -> (a cos t - b sin t, a sin t + b cos t).
+    """
+    x = np.asarray(x, dtype=np.float64)
+    d = x.shape[-1]
+    theta = float(base) ** (-2.0 * np.arange(d // 2, dtype=np.float64) / d)
+    t = sign * np.asarray(pos, dtype=np.float64)[..., None] * theta
+    c, s = np.cos(t), np.sin(t)
+    a, b = x[..., 0::2], x[..., 1::2]
+    out = np.empty(np.broadcast_shapes(x.shape, c.shape[:-1] + (d,)))
+    out[..., 0::2] = a * c - b * s
+    out[..., 1::2] = a * s + b * c
+    return out
+
+
+def _rotated_bf16(rows, pos, base, d_rope: int) -> np.ndarray:
+    """rows float64 [n][D]: the last d_rope channels rotated by pos and
+    rounded to bf16 (through their float32 value); the others unchanged."""
+    out = np.array(rows, dtype=np.float64, copy=True)
+    rot = rope_rotate(out[:, -d_rope:], pos, base)
+    out[:, -d_rope:] = bf16_to_f64(f32_to_bf16(rot.astype(np.float32)))
+    return out
+
+
+def attention(q_u16, keys: np.ndarray, scale, rope=None) -> tuple[np.ndarray, np.ndarray]:
     """Softmax attention of H query heads over n keys, the value equal to the key.
 
     q_u16 bf16 bits [H][D]; keys float64 [n][D]; scale is the float32
-    softmax scale.  Returns (o float64 [H][D], lse float64 [H]); with no key
-    at all o = 0 and lse = -inf.
+    softmax scale.  ``rope`` (optional) = dict(base, p, pos [n], d_rope):
+    the fused rotary epilogue (query rotated by p, key j by pos[j], output
+    rotated back by -p).  Returns (o float64 [H][D], lse float64 [H]); with
+    no key at all o = 0 and lse = -inf.
     """
     q = bf16_to_f64(q_u16)
     H, D = q.shape
     if keys.shape[0] == 0:
         return np.zeros((H, D)), np.full(H, -np.inf)
+    if rope is not None:
+        dr = int(rope.get("d_rope", 64))
+        q = _rotated_bf16(q, int(rope["p"]), rope["base"], dr)
+        keys = _rotated_bf16(keys, np.asarray(rope["pos"], dtype=np.int64), rope["base"], dr)
     s = float(np.float32(scale))
     logits = s * (q @ keys.T)
     mx = logits.max(axis=1, keepdims=True)
@@ -220,6 +267,8 @@ def attention(q_u16, keys: np.ndarray, scale) -> tuple[np.ndarray, np.ndarray]:
     den = e.sum(axis=1, keepdims=True)
     o = (e / den) @ keys
     lse = (mx + np.log(den))[:, 0]
+    if rope is not None:
+        o[:, -dr:] = rope_rotate(o[:, -dr:], int(rope["p"]), rope["base"], sign=-1.0)
     return o, lse
 
 
@@ -253,11 +302,13 @@ def swa_decode(codes, scales, rope) -> np.ndarray:
 
 
 def sparse_attention(q_u16, nope, nscale, rope, idx, swa_u16, swa_pos0, p, n_win, scale,
-                     m: int, n_entries: int):
+                     m: int, n_entries: int, rope_base=None):
     """Attention over the selected compressed entries plus the sliding window.
 
     ``idx`` lists entry indices; -1 and entries not visible at p are
-    skipped; a repeated index is attended once per occurrence.  Returns
+    skipped; a repeated index is attended once per occurrence.  With
+    ``rope_base`` the fused rotary epilogue applies (entry j at position
+    (j+1)*m - 1, window rows at their own positions).  Returns
     (o [H][D], lse [H]).
     """
     V = visible_count(p, m, n_entries)
@@ -265,14 +316,20 @@ def sparse_attention(q_u16, nope, nscale, rope, idx, swa_u16, swa_pos0, p, n_win
     sel = idx[(idx >= 0) & (idx < V)]
     ent = decode_entries(np.asarray(nope)[sel], np.asarray(nscale)[sel], np.asarray(rope)[sel])
     win = _window_rows(swa_u16, swa_pos0, p, n_win)
-    return attention(q_u16, np.concatenate([ent, win], axis=0), scale)
+    rp = None
+    if rope_base is not None:
+        lo = max(0, p - n_win + 1, int(swa_pos0)) if (n_win > 0 and p >= 0) else 0
+        pos = np.concatenate([(sel + 1) * m - 1, lo + np.arange(win.shape[0], dtype=np.int64)])
+        rp = dict(base=rope_base, p=p, pos=pos, d_rope=np.asarray(rope).shape[-1])
+    return attention(q_u16, np.concatenate([ent, win], axis=0), scale, rope=rp)
 
 
-def dense_attention(q_u16, nope, nscale, rope, swa_u16, swa_pos0, p, n_win, scale, m, n_entries):
+def dense_attention(q_u16, nope, nscale, rope, swa_u16, swa_pos0, p, n_win, scale, m, n_entries,
+                    rope_base=None):
     """HCA [V4], Fig. 4: every visible compressed entry plus the same window."""
     V = visible_count(p, m, n_entries)
     return sparse_attention(q_u16, nope, nscale, rope, np.arange(V), swa_u16, swa_pos0, p,
-                            n_win, scale, m, n_entries)
+                            n_win, scale, m, n_entries, rope_base=rope_base)
 
 
 def csa2_pair(cache: dict, layer_a: dict, layer_b: dict, p: int, m: int, n_entries: int,

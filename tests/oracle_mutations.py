@@ -47,6 +47,14 @@ muts = [
  ("csa.py", "o_b, lse_b = sparse_attention(layer_b[\"q\"]", "o_b, lse_b = sparse_attention(layer_a[\"q\"]"),
  ("csa.py", "return np.concatenate([mxfp4_decode(nope, nscale), bf16_to_f64(rope)], axis=-1)", "return np.concatenate([bf16_to_f64(rope), mxfp4_decode(nope, nscale)], axis=-1)"),
  ("csa.py", "return np.concatenate([mxfp4_decode(nope, nscale), bf16_to_f64(rope)], axis=-1)", "return np.concatenate([mxfp4_decode(nope, nscale), bf16_to_f64(rope)[..., ::-1]], axis=-1)"),
+ ("csa.py", "a, b = x[..., 0::2], x[..., 1::2]", "a, b = x[..., :d // 2], x[..., d // 2:]"),
+ ("csa.py", "out[..., 1::2] = a * s + b * c", "out[..., 1::2] = -a * s + b * c"),
+ ("csa.py", "theta = float(base) ** (-2.0 * np.arange(d // 2, dtype=np.float64) / d)", "theta = float(base) ** (-1.0 * np.arange(d // 2, dtype=np.float64) / d)"),
+ ("csa.py", "rope[\"base\"], sign=-1.0)", "rope[\"base\"], sign=1.0)"),
+ ("csa.py", "pos = np.concatenate([(sel + 1) * m - 1,", "pos = np.concatenate([sel * m,"),
+ ("csa.py", "lo + np.arange(win.shape[0], dtype=np.int64)])", "lo + 1 + np.arange(win.shape[0], dtype=np.int64)])"),
+ ("csa.py", "out[:, -d_rope:] = bf16_to_f64(f32_to_bf16(rot.astype(np.float32)))", "out[:, -d_rope:] = rot"),
+ ("csa.py", "q = _rotated_bf16(q, int(rope[\"p\"]), rope[\"base\"], dr)", "q = _rotated_bf16(q, 0, rope[\"base\"], dr)"),
 ]
 missed = 0
 root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))

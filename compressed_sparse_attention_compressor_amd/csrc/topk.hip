@@ -569,11 +569,10 @@ __global__ __launch_bounds__(kRegThreads) void topk_hint_final_kernel(HintArgs a
         if (key[j] != 0u && (key[j] >> kHintShift) == (uint32_t)bin) atomicAdd(&hist[(key[j] >> 10) & 0x7FFu], 1);
       __syncthreads();
       int k_rem = k_eff - above;
-      int e2, ab, tt;
-      find_digit<NT>(hist2, 1, kBins, k_rem, sh, e2, ab, tt);
+      int e2, ab, c2, tt;
+      find_digit<NT>(hist2, 1, kBins, k_rem, sh, e2, ab, c2, tt);
       k_rem -= ab;
       const uint32_t p12 = ((uint32_t)bin << 11) | (uint32_t)e2;
-      const int c2 = __builtin_amdgcn_readfirstlane(hist[e2]);
       if (c2 <= 64) {
         int mine = 0;
 #pragma unroll
@@ -601,11 +600,10 @@ __global__ __launch_bounds__(kRegThreads) void topk_hint_final_kernel(HintArgs a
           if (key[j] != 0u && (key[j] >> 10) == p12) atomicAdd(&hist[key[j] & 0x3FFu], 1);
         __syncthreads();
         int e3;
-        find_digit<NT>(hist2, 1, 1024, k_rem, sh, e3, ab, tt);
+        find_digit<NT>(hist2, 1, 1024, k_rem, sh, e3, ab, n_eq, tt);  // every key equal to thr lies in bin e3
         k_rem -= ab;
         thr = (p12 << 10) | (uint32_t)e3;
         need = k_rem;
-        n_eq = __builtin_amdgcn_readfirstlane(hist[e3]);  // every key equal to thr lies in this bin
       }
     }
     place_selected<NT, kHintCand, true, kStage>(key, cid, thr, need, n_eq, k_eff, a.k, cnt, hist,
@@ -701,7 +699,8 @@ __device__ __forceinline__ void rx_digit(const int *g, int nb, int k_rem, int (*
                                          int &above, int &total) {
   for (int i = threadIdx.x; i < nb; i += kRegThreads) hs[0][i] = g[i];
   __syncthreads();
-  find_digit<kRegThreads>(hs, 1, nb, k_rem, sh, digit, above, total);
+  int count;
+  find_digit<kRegThreads>(hs, 1, nb, k_rem, sh, digit, above, count, total);
 }
 
 // Adds this workgroup's histogram (LDS, nb bins) into the row's.

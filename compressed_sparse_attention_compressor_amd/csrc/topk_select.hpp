@@ -17,11 +17,13 @@ constexpr int kBins = 2048;
 // Finds the digit (of `nb` <= kBins bins) holding the k_rem-th largest
 // remaining element; the counts are summed over `nh` per-wave histograms.
 // Every thread returns the same digit, the number of elements in higher
-// digits and the histogram total; when the total is below k_rem the digit
-// is undefined.  Two barriers; uses sh[0 .. kW+2).
+// digits, the number in the digit itself and the histogram total; when the
+// total is below k_rem the digit is undefined.  Two barriers; uses
+// sh[0 .. kW+3).  The histogram is read only before the first barrier, so a
+// caller may rewrite it as soon as this returns.
 template <int NT>
 __device__ __forceinline__ void find_digit(const int (*hist)[kBins], int nh, int nb, int k_rem, int *sh, int &digit,
-                                           int &above_out, int &total) {
+                                           int &above_out, int &count_out, int &total) {
   constexpr int kW = NT / 64;
   constexpr int kMaxPer = kBins / NT;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -54,6 +56,7 @@ __device__ __forceinline__ void find_digit(const int (*hist)[kBins], int nh, int
     if (j < per && above < k_rem && k_rem <= above + c[j]) {
       sh[kW] = nb - 1 - (tid * per + j);
       sh[kW + 1] = above;
+      sh[kW + 2] = c[j];
     }
     above += c[j];
   }
@@ -62,6 +65,7 @@ __device__ __forceinline__ void find_digit(const int (*hist)[kBins], int nh, int
   // reaches after these reads.
   digit = __builtin_amdgcn_readfirstlane(sh[kW]);
   above_out = __builtin_amdgcn_readfirstlane(sh[kW + 1]);
+  count_out = __builtin_amdgcn_readfirstlane(sh[kW + 2]);
   total = __builtin_amdgcn_readfirstlane(all);
 }
 
@@ -289,9 +293,10 @@ __device__ __forceinline__ void linear_threshold(const uint32_t (&key)[kPer], in
       if (key[j] != 0u) atomicAdd(&hist[kBins - 2 - bj], 1);
     }
     __syncthreads();
-    int d1, above, tot;
-    find_digit<NT>(hist2, 1, kBins, k_eff, sh, d1, above, tot);
-    const int c1 = __builtin_amdgcn_readfirstlane(hist[d1]);
+    // (the bin's count comes from find_digit: a read of hist[d1] here would
+    // race with the zeroing of the crowded-bin passes below)
+    int d1, above, c1, tot;
+    find_digit<NT>(hist2, 1, kBins, k_eff, sh, d1, above, c1, tot);
     const uint32_t dhi = (uint32_t)(kBins - 2 - d1);
     auto in_dhi = [&](int j) { return ((binp[j >> 1] >> (16 * (j & 1))) & 0xFFFFu) == dhi; };
     int k_rem = k_eff - above;
@@ -322,8 +327,8 @@ __device__ __forceinline__ void linear_threshold(const uint32_t (&key)[kPer], in
       for (int j = 0; j < kPer; ++j)
         if (in_dhi(j)) atomicAdd(&hist[key[j] >> 21], 1);
       __syncthreads();
-      int e1, ab;
-      find_digit<NT>(hist2, 1, kBins, k_rem, sh, e1, ab, tot);
+      int e1, ab, ce;
+      find_digit<NT>(hist2, 1, kBins, k_rem, sh, e1, ab, ce, tot);
       k_rem -= ab;
       for (int i = tid; i < kBins; i += NT) hist[i] = 0;
       __syncthreads();
@@ -332,7 +337,7 @@ __device__ __forceinline__ void linear_threshold(const uint32_t (&key)[kPer], in
         if (in_dhi(j) && (key[j] >> 21) == (uint32_t)e1) atomicAdd(&hist[(key[j] >> 10) & 0x7FFu], 1);
       __syncthreads();
       int e2;
-      find_digit<NT>(hist2, 1, kBins, k_rem, sh, e2, ab, tot);
+      find_digit<NT>(hist2, 1, kBins, k_rem, sh, e2, ab, ce, tot);
       k_rem -= ab;
       const uint32_t p12 = ((uint32_t)e1 << 11) | (uint32_t)e2;
       for (int i = tid; i < kBins; i += NT) hist[i] = 0;
@@ -342,11 +347,10 @@ __device__ __forceinline__ void linear_threshold(const uint32_t (&key)[kPer], in
         if (in_dhi(j) && (key[j] >> 10) == p12) atomicAdd(&hist[key[j] & 0x3FFu], 1);
       __syncthreads();
       int e3;
-      find_digit<NT>(hist2, 1, 1024, k_rem, sh, e3, ab, tot);
+      find_digit<NT>(hist2, 1, 1024, k_rem, sh, e3, ab, n_eq, tot);  // every key equal to thr lies in bin e3
       k_rem -= ab;
       thr = (p12 << 10) | (uint32_t)e3;
       need = k_rem;
-      n_eq = __builtin_amdgcn_readfirstlane(hist[e3]);  // every key equal to thr lies in this bin
     }
   }
   k_eff_out = k_eff;

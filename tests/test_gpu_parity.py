@@ -1049,6 +1049,29 @@ TOPK_CASES = [
 ]
 
 
+def test_topk_crowded_threshold_bin_repeated():
+    """Rows whose k-th score sits in a bin of more than 64 equal keys take
+    the radix passes over that bin; every wave must agree on the bin's count
+    (it once came from an LDS read that raced with the passes' zeroing).
+    Three launches of 300 such rows, each checked against the oracle."""
+    B, Q, Ns, k = 1, 300, 16384, 1024
+    raw = normal_f32(98, TensorId.W, (B * Q, Ns)).numpy().astype(np.float64)
+    sc = (np.round(raw / 0.1) * 0.1).astype(np.float32).reshape(B, Q, Ns)
+    vis = np.array([min(Ns, (r * Ns) // Q + 1) for r in range(Q)]).reshape(B, Q)
+    cache = csa.Cache(B, Ns, 1, 0, planes=dict(
+        nope=torch.zeros(B, 1, 256, dtype=torch.uint8, device=DEV),
+        nscale=torch.zeros(B, 1, 16, dtype=torch.uint8, device=DEV),
+        rope=torch.zeros(B, 1, 64, dtype=torch.bfloat16, device=DEV), ikey=None, iscale=None,
+        n_entries=torch.full((B,), Ns, dtype=torch.int32, device=DEV)))
+    ref = [O.topk_select(sc[0, t, :int(vis[0, t])].astype(np.float64), np.arange(int(vis[0, t])), k)[0]
+           for t in range(Q)]
+    s_dev, p_dev = torch.from_numpy(sc).to(DEV), torch.from_numpy((vis - 1).astype(np.int32)).to(DEV)
+    for rep in range(3):
+        g = _np(csa.topk(cache, s_dev, p_dev, k)[0])
+        for t in range(Q):
+            np.testing.assert_array_equal(g[0, t], ref[t], err_msg=f"launch {rep} row {t}")
+
+
 @pytest.mark.parametrize("name,B,Q,Ns,vis,k,rnd", TOPK_CASES, ids=[c[0] for c in TOPK_CASES])
 def test_topk_stage_parity(name, B, Q, Ns, vis, k, rnd):
     """The top-k stage on generated scores with many exact ties, against

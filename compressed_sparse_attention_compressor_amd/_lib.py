@@ -59,6 +59,7 @@ class Csa2LayerT(ctypes.Structure):
         ("out_dtype", ctypes.c_int32),
         ("out", c_void_p),
         ("lse", c_void_p),
+        ("rope_base", c_float),
     ]
 
 
@@ -82,19 +83,19 @@ _SIGS = {
     "csa_index_pool": (c_int, [ctypes.POINTER(CacheT), c_void_p, c_void_p, c_int, c_int, c_int, c_void_p, c_void_p,
                                c_size_t, c_void_p]),
     "csa_sparse_attn": (c_int, [ctypes.POINTER(CacheT), c_void_p, c_int, c_void_p, c_int, c_void_p, c_int, c_void_p,
-                                c_void_p, c_int, c_int, c_float, c_int, c_void_p, c_void_p, c_void_p, c_size_t,
-                                c_void_p]),
+                                c_void_p, c_int, c_int, c_float, c_float, c_int, c_void_p, c_void_p, c_void_p,
+                                c_size_t, c_void_p]),
     "hca_dense_attn": (c_int, [ctypes.POINTER(CacheT), c_void_p, c_int, c_void_p, c_int, c_void_p, c_void_p, c_int,
-                               c_int, c_float, c_int, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]),
+                               c_int, c_float, c_float, c_int, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]),
     "csa2_layer_stack": (c_int, [ctypes.POINTER(Csa2LayerT), c_int, c_void_p, c_int, c_void_p, c_size_t, c_void_p]),
     "csa2_stack_workspace_bytes": (c_size_t, [ctypes.POINTER(Csa2LayerT), c_int, c_int]),
     "csa_swa_encode": (c_int, [c_void_p, c_int64, c_int, c_int, c_void_p, c_void_p, c_void_p, c_void_p]),
     "csa_sparse_attn_w8": (c_int, [ctypes.POINTER(CacheT), c_void_p, c_int, c_void_p, c_int, c_void_p, c_int,
-                                   c_void_p, c_void_p, c_void_p, c_void_p, c_int, c_int, c_float, c_int, c_void_p,
-                                   c_void_p, c_void_p, c_size_t, c_void_p]),
+                                   c_void_p, c_void_p, c_void_p, c_void_p, c_int, c_int, c_float, c_float, c_int,
+                                   c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]),
     "hca_dense_attn_w8": (c_int, [ctypes.POINTER(CacheT), c_void_p, c_int, c_void_p, c_int, c_void_p, c_void_p,
-                                  c_void_p, c_void_p, c_int, c_int, c_float, c_int, c_void_p, c_void_p, c_void_p,
-                                  c_size_t, c_void_p]),
+                                  c_void_p, c_void_p, c_int, c_int, c_float, c_float, c_int, c_void_p, c_void_p,
+                                  c_void_p, c_size_t, c_void_p]),
     "csa_workspace_bytes": (c_size_t, [c_int, c_int, c_int, c_int, c_int, c_int]),
     "csa_status_str": (ctypes.c_char_p, [c_int]),
     "csa_version": (c_int, []),

@@ -161,8 +161,8 @@ size_t index_topk_ws_bytes(int B, int Q, int N_cap, int k, int C, bool cand) {
 }
 
 int check_attn_common(const csa_cache_t *cache, const uint16_t *q, int H, const int32_t *q_pos, int Q,
-                      const uint16_t *swa, const int32_t *swa_pos0, int S, int n_win, float scale, int out_dtype,
-                      void *out) {
+                      const uint16_t *swa, const int32_t *swa_pos0, int S, int n_win, float scale,
+                      float rope_base, int out_dtype, void *out) {
   int st = check_cache(cache, false);
   if (st) return st;
   if (!q || !q_pos || !out) return CSA_ERR_NULL;
@@ -172,6 +172,7 @@ int check_attn_common(const csa_cache_t *cache, const uint16_t *q, int H, const 
   if (n_win > kMaxWin) return CSA_ERR_UNSUPPORTED;
   if (out_dtype != CSA_OUT_F32 && out_dtype != CSA_OUT_BF16) return CSA_ERR_UNSUPPORTED;
   if (!(scale == scale) || isinf(scale)) return CSA_ERR_SHAPE;
+  if (!(rope_base >= 0.f) || isinf(rope_base)) return CSA_ERR_SHAPE;  // NaN fails the comparison
   if (!aligned16(q) || !aligned16(out) || (n_win > 0 && !aligned16(swa))) return CSA_ERR_ALIGN;
   return CSA_OK;
 }
@@ -180,7 +181,7 @@ int check_attn_common(const csa_cache_t *cache, const uint16_t *q, int H, const 
 
 extern "C" {
 
-int csa_version(void) { return 10100; }
+int csa_version(void) { return 10200; }
 
 int csa_read_device_flags(hipStream_t stream, uint32_t *flags) {
   if (!flags) return CSA_ERR_NULL;
@@ -443,9 +444,10 @@ static int check_window8(const uint8_t *codes, const uint8_t *scales, const uint
 
 static int sparse_attn_impl(const csa_cache_t *cache, const uint16_t *q, int H, const int32_t *q_pos, int Q,
                             const int32_t *idx, int k, const uint16_t *swa, const csa::SwaPlanes *w8,
-                            const int32_t *swa_pos0, int S, int n_win, float softmax_scale, int out_dtype, void *out,
-                            float *lse, void *ws, size_t ws_bytes, hipStream_t stream) {
-  int st = check_attn_common(cache, q, H, q_pos, Q, swa, swa_pos0, S, n_win, softmax_scale, out_dtype, out);
+                            const int32_t *swa_pos0, int S, int n_win, float softmax_scale, float rope_base,
+                            int out_dtype, void *out, float *lse, void *ws, size_t ws_bytes, hipStream_t stream) {
+  int st = check_attn_common(cache, q, H, q_pos, Q, swa, swa_pos0, S, n_win, softmax_scale, rope_base, out_dtype,
+                             out);
   if (st) return st;
   if (k < 0) return CSA_ERR_SHAPE;
   if (k > 0 && !idx) return CSA_ERR_NULL;
@@ -457,14 +459,16 @@ static int sparse_attn_impl(const csa_cache_t *cache, const uint16_t *q, int H, 
   if (need > 0 && !aligned16(ws)) return CSA_ERR_ALIGN;
   const csa::CacheView v = view_of(cache);
   return status_of(csa::launch_attention(v, q, H, q_pos, Q, idx, k, false, swa, w8, swa_pos0, S, n_win,
-                                         softmax_scale, out_dtype == CSA_OUT_BF16, out, lse, ws, stream));
+                                         softmax_scale, rope_base, out_dtype == CSA_OUT_BF16, out, lse, ws,
+                                         stream));
 }
 
 static int dense_attn_impl(const csa_cache_t *cache, const uint16_t *q, int H, const int32_t *q_pos, int Q,
                            const uint16_t *swa, const csa::SwaPlanes *w8, const int32_t *swa_pos0, int S, int n_win,
-                           float softmax_scale, int out_dtype, void *out, float *lse, void *ws, size_t ws_bytes,
-                           hipStream_t stream) {
-  int st = check_attn_common(cache, q, H, q_pos, Q, swa, swa_pos0, S, n_win, softmax_scale, out_dtype, out);
+                           float softmax_scale, float rope_base, int out_dtype, void *out, float *lse, void *ws,
+                           size_t ws_bytes, hipStream_t stream) {
+  int st = check_attn_common(cache, q, H, q_pos, Q, swa, swa_pos0, S, n_win, softmax_scale, rope_base, out_dtype,
+                             out);
   if (st) return st;
   if (Q == 0 || cache->B == 0) return CSA_OK;
   const size_t need = csa::attn_workspace_bytes(cache->B, Q, H, cache->N_cap, n_win);
@@ -473,45 +477,48 @@ static int dense_attn_impl(const csa_cache_t *cache, const uint16_t *q, int H, c
   if (need > 0 && !aligned16(ws)) return CSA_ERR_ALIGN;
   const csa::CacheView v = view_of(cache);
   return status_of(csa::launch_attention(v, q, H, q_pos, Q, nullptr, 0, true, swa, w8, swa_pos0, S, n_win,
-                                         softmax_scale, out_dtype == CSA_OUT_BF16, out, lse, ws, stream));
+                                         softmax_scale, rope_base, out_dtype == CSA_OUT_BF16, out, lse, ws,
+                                         stream));
 }
 
 int csa_sparse_attn(const csa_cache_t *cache, const uint16_t *q, int H, const int32_t *q_pos, int Q,
                     const int32_t *idx, int k, const uint16_t *swa, const int32_t *swa_pos0, int S, int n_win,
-                    float softmax_scale, int out_dtype, void *out, float *lse, void *ws, size_t ws_bytes,
-                    hipStream_t stream) {
-  return sparse_attn_impl(cache, q, H, q_pos, Q, idx, k, swa, nullptr, swa_pos0, S, n_win, softmax_scale, out_dtype,
-                          out, lse, ws, ws_bytes, stream);
+                    float softmax_scale, float rope_base, int out_dtype, void *out, float *lse, void *ws,
+                    size_t ws_bytes, hipStream_t stream) {
+  return sparse_attn_impl(cache, q, H, q_pos, Q, idx, k, swa, nullptr, swa_pos0, S, n_win, softmax_scale, rope_base,
+                          out_dtype, out, lse, ws, ws_bytes, stream);
 }
 
 int hca_dense_attn(const csa_cache_t *cache, const uint16_t *q, int H, const int32_t *q_pos, int Q,
                    const uint16_t *swa, const int32_t *swa_pos0, int S, int n_win, float softmax_scale,
-                   int out_dtype, void *out, float *lse, void *ws, size_t ws_bytes, hipStream_t stream) {
-  return dense_attn_impl(cache, q, H, q_pos, Q, swa, nullptr, swa_pos0, S, n_win, softmax_scale, out_dtype, out, lse,
-                         ws, ws_bytes, stream);
+                   float rope_base, int out_dtype, void *out, float *lse, void *ws, size_t ws_bytes,
+                   hipStream_t stream) {
+  return dense_attn_impl(cache, q, H, q_pos, Q, swa, nullptr, swa_pos0, S, n_win, softmax_scale, rope_base, out_dtype,
+                         out, lse, ws, ws_bytes, stream);
 }
 
 int csa_sparse_attn_w8(const csa_cache_t *cache, const uint16_t *q, int H, const int32_t *q_pos, int Q,
                        const int32_t *idx, int k, const uint8_t *swa_codes, const uint8_t *swa_scales,
                        const uint16_t *swa_rope, const int32_t *swa_pos0, int S, int n_win, float softmax_scale,
-                       int out_dtype, void *out, float *lse, void *ws, size_t ws_bytes, hipStream_t stream) {
+                       float rope_base, int out_dtype, void *out, float *lse, void *ws, size_t ws_bytes,
+                       hipStream_t stream) {
   int st = check_window8(swa_codes, swa_scales, swa_rope, n_win);
   if (st) return st;
   const csa::SwaPlanes w8{swa_codes, swa_scales, swa_rope};
   // the rope plane stands in for the bf16 rows in the shared checks
-  return sparse_attn_impl(cache, q, H, q_pos, Q, idx, k, swa_rope, &w8, swa_pos0, S, n_win, softmax_scale, out_dtype,
-                          out, lse, ws, ws_bytes, stream);
+  return sparse_attn_impl(cache, q, H, q_pos, Q, idx, k, swa_rope, &w8, swa_pos0, S, n_win, softmax_scale, rope_base,
+                          out_dtype, out, lse, ws, ws_bytes, stream);
 }
 
 int hca_dense_attn_w8(const csa_cache_t *cache, const uint16_t *q, int H, const int32_t *q_pos, int Q,
                       const uint8_t *swa_codes, const uint8_t *swa_scales, const uint16_t *swa_rope,
-                      const int32_t *swa_pos0, int S, int n_win, float softmax_scale, int out_dtype, void *out,
-                      float *lse, void *ws, size_t ws_bytes, hipStream_t stream) {
+                      const int32_t *swa_pos0, int S, int n_win, float softmax_scale, float rope_base,
+                      int out_dtype, void *out, float *lse, void *ws, size_t ws_bytes, hipStream_t stream) {
   int st = check_window8(swa_codes, swa_scales, swa_rope, n_win);
   if (st) return st;
   const csa::SwaPlanes w8{swa_codes, swa_scales, swa_rope};
-  return dense_attn_impl(cache, q, H, q_pos, Q, swa_rope, &w8, swa_pos0, S, n_win, softmax_scale, out_dtype, out,
-                         lse, ws, ws_bytes, stream);
+  return dense_attn_impl(cache, q, H, q_pos, Q, swa_rope, &w8, swa_pos0, S, n_win, softmax_scale, rope_base,
+                         out_dtype, out, lse, ws, ws_bytes, stream);
 }
 
 int csa_swa_encode(const uint16_t *x, int64_t x_stride_b, int B, int S, uint8_t *codes, uint8_t *scales,
@@ -619,7 +626,7 @@ static int stack_plan(const csa2_layer_t *L, int n, const int32_t *q_pos, int Q,
     st.sel = sel;
     st.k = sel_k;
     if ((rc = check_attn_common(full, l.q, l.H, q_pos, Q, l.swa, l.swa_pos0, l.S, l.n_win, l.softmax_scale,
-                                l.out_dtype, l.out)))
+                                l.rope_base, l.out_dtype, l.out)))
       return rc;
     if (st.k > kMaxK) return CSA_ERR_UNSUPPORTED;
     if (Q == 0 || B == 0) {
@@ -673,7 +680,7 @@ int csa2_layer_stack(const csa2_layer_t *layers, int n_layers, const int32_t *q_
     }
     if (st == CSA_OK)
       st = csa_sparse_attn(s.cache, l.q, l.H, q_pos, Q, s.sel, s.k, l.swa, l.swa_pos0, l.S, l.n_win,
-                           l.softmax_scale, l.out_dtype, l.out, l.lse, rest, s.ws_rest, stream);
+                           l.softmax_scale, l.rope_base, l.out_dtype, l.out, l.lse, rest, s.ws_rest, stream);
   }
   return st;
 }

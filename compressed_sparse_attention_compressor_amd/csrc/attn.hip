@@ -29,6 +29,7 @@
 //      parts (hi + lo) so that the probabilities keep ~16 bits.
 // Splits write unnormalised (O, max, sum) partials that a merge kernel
 // combines; a single split writes the normalised output directly.
+#include <cmath>
 #include <type_traits>
 
 #include "csa_device.hpp"
@@ -77,7 +78,41 @@ struct AttnArgs {
   float *ws_ml;
   int nsplit, per_split;
   uint32_t *flags;             // device fault word (may be null)
+  // Fused rotary epilogue: rot != 0 turns channel pair (2i, 2i+1) of the
+  // 64 positional channels by pos * base^(-2i/64) radians; rot_turns[i] is
+  // base^(-2i/64) / (2 pi), the turn per position, in fp64.
+  int rot;
+  double rot_turns[kDRope / 2];
 };
+
+// cos and sin of the rotary angle of pair i at position pos: the angle in
+// turns is reduced to [0, 1) in fp64 (exact to ~1e-10 turn for positions
+// below 2^31), then the fp32 hardware cosine and sine (which take turns)
+// are evaluated on it.
+__device__ __forceinline__ float2 rope_cs(int64_t pos, double turns) {
+  const double t = (double)pos * turns;
+  const float r = (float)(t - floor(t));
+  return float2{__builtin_amdgcn_cosf(r), __builtin_amdgcn_sinf(r)};
+}
+
+// One word of two bf16 channels (2i low, 2i+1 high) turned by the angle
+// (c, s), rounded back to bf16.
+__device__ __forceinline__ uint32_t rope_pair(uint32_t w, float c, float s) {
+  const float x = __uint_as_float(w << 16), y = __uint_as_float(w & 0xFFFF0000u);
+  return f32_to_bf16(x * c - y * s) | (f32_to_bf16(x * s + y * c) << 16);
+}
+
+// 8 positional channels 8 part .. 8 part + 7 (four pairs) of a row at
+// position pos, rotated.
+__device__ __forceinline__ uint4 rope_piece(const AttnArgs &a, uint4 v, int64_t pos, int part) {
+  uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const float2 cs = rope_cs(pos, a.rot_turns[4 * part + k]);
+    w[k] = rope_pair(w[k], cs.x, cs.y);
+  }
+  return uint4{w[0], w[1], w[2], w[3]};
+}
 
 // Per-thread share of one chunk's raw bytes for NT threads.
 template <int NT>
@@ -127,7 +162,7 @@ __device__ __forceinline__ void load_entries(const AttnArgs &a, int b, const int
 }
 
 template <int NT>
-__device__ __forceinline__ void store_entries(uint16_t *K, const int *src, const RawChunk<NT> &r) {
+__device__ __forceinline__ void store_entries(const AttnArgs &a, uint16_t *K, const int *src, const RawChunk<NT> &r) {
   using CS = ChunkShare<NT>;
   const int tid = threadIdx.x;
 #pragma unroll
@@ -169,7 +204,10 @@ __device__ __forceinline__ void store_entries(uint16_t *K, const int *src, const
     if (t < kRopeTasks) {
       const int key = t >> 3, part = t & 7;
       uint4 v = r.v[CS::kFp4 + u];  // a value copy: a conditional between lvalues would pin r to memory
-      if (src[key] < 0) v = uint4{0u, 0u, 0u, 0u};
+      const int j = src[key];
+      // a compressed entry sits at its last raw token, (j + 1) m - 1
+      if (a.rot && j >= 0) v = rope_piece(a, v, (int64_t)(j + 1) * a.m - 1, part);
+      if (j < 0) v = uint4{0u, 0u, 0u, 0u};
       *reinterpret_cast<uint4 *>(K + key * kKRow + kDNope + part * 8) = v;
     }
   }
@@ -201,7 +239,8 @@ __device__ __forceinline__ void load_win8(const AttnArgs &a, int b, const int *s
 }
 
 template <int NT>
-__device__ __forceinline__ void store_win8(uint16_t *K, const int *src, const RawChunk<NT> &r) {
+__device__ __forceinline__ void store_win8(const AttnArgs &a, int swa0, uint16_t *K, const int *src,
+                                           const RawChunk<NT> &r) {
   using CS = ChunkShare<NT>;
   const int tid = threadIdx.x;
 #pragma unroll
@@ -240,7 +279,9 @@ __device__ __forceinline__ void store_win8(uint16_t *K, const int *src, const Ra
     if (t < kRopeTasks) {
       const int key = t >> 3, part = t & 7;
       uint4 v = r.v[2 * CS::kFp4 + u];
-      if (src[key] < 0) v = uint4{0u, 0u, 0u, 0u};
+      const int row = src[key];
+      if (a.rot && row >= 0) v = rope_piece(a, v, (int64_t)swa0 + row, part);  // a window row at its raw position
+      if (row < 0) v = uint4{0u, 0u, 0u, 0u};
       *reinterpret_cast<uint4 *>(K + key * kKRow + kDNope + part * 8) = v;
     }
   }
@@ -260,7 +301,8 @@ __device__ __forceinline__ void load_window(const AttnArgs &a, int b, const int 
 }
 
 template <int NT, int nb>
-__device__ __forceinline__ void store_window(uint16_t *K, const int *src, int t0, const RawChunk<NT> &r) {
+__device__ __forceinline__ void store_window(const AttnArgs &a, int swa0, uint16_t *K, const int *src, int t0,
+                                             const RawChunk<NT> &r) {
   const int tid = threadIdx.x;
 #pragma unroll
   for (int u = 0; u < nb; ++u) {
@@ -268,7 +310,10 @@ __device__ __forceinline__ void store_window(uint16_t *K, const int *src, int t0
     if (t < kWinTasks) {
       const int key = t / kRowPieces, part = t % kRowPieces;
       uint4 v = r.v[u];
-      if (src[key] < 0) v = uint4{0u, 0u, 0u, 0u};
+      const int row = src[key];
+      constexpr int kRope0 = kDNope / 8;  // first positional piece of a row
+      if (a.rot && row >= 0 && part >= kRope0) v = rope_piece(a, v, (int64_t)swa0 + row, part - kRope0);
+      if (row < 0) v = uint4{0u, 0u, 0u, 0u};
       *reinterpret_cast<uint4 *>(K + key * kKRow + part * 8) = v;
     }
   }
@@ -374,6 +419,17 @@ __global__ __launch_bounds__(HG * 128) void attn_kernel(AttnArgs a) {
     const uint16_t *qp = a.q + (qrow * a.H + hg * 16 + r) * kD + cbase + 8 * g;
 #pragma unroll
     for (int kk = 0; kk < kQSteps; ++kk) Qf[kk] = *reinterpret_cast<const v8bf *>(qp + 32 * kk);
+    if (a.rot) {
+      // the first rotation of the fused epilogue: the query's positional
+      // channels turned by its own position (rounded to bf16 as they are
+      // stored)
+#pragma unroll
+      for (int kk = 0; kk < kQSteps; ++kk) {
+        const int c0 = cbase + 32 * kk + 8 * g;
+        if (c0 >= kDNope)
+          Qf[kk] = __builtin_bit_cast(v8bf, rope_piece(a, __builtin_bit_cast(uint4, Qf[kk]), p, (c0 - kDNope) / 8));
+      }
+    }
     publish_slot(s_begin, j0, 0);
   }
 
@@ -514,9 +570,9 @@ __global__ __launch_bounds__(HG * 128) void attn_kernel(AttnArgs a) {
       else load_entries<NT>(a, b, src_s[sb], raw);
     };
     auto st = [&](uint16_t *K, int sb) __attribute__((always_inline)) {
-      if (kWin16) store_window<NT, CS::kWinBatch>(K, src_s[sb], 0, raw);
-      else if (kWin) store_win8<NT>(K, src_s[sb], raw);
-      else store_entries<NT>(K, src_s[sb], raw);
+      if (kWin16) store_window<NT, CS::kWinBatch>(a, swa0, K, src_s[sb], 0, raw);
+      else if (kWin) store_win8<NT>(a, swa0, K, src_s[sb], raw);
+      else store_entries<NT>(a, K, src_s[sb], raw);
     };
     lds_barrier();
     if (CS::kAhead) ld(ci % 3);
@@ -529,7 +585,7 @@ __global__ __launch_bounds__(HG * 128) void attn_kernel(AttnArgs a) {
       } else if (kWin16) {
         for (int t0 = 0; t0 < kWinTasks; t0 += CS::kWinBatch * NT) {
           load_window<NT, CS::kWinBatch>(a, b, src_s[sb], t0, raw);
-          store_window<NT, CS::kWinBatch>(K, src_s[sb], t0, raw);
+          store_window<NT, CS::kWinBatch>(a, swa0, K, src_s[sb], t0, raw);
         }
       } else {
         ld(sb);
@@ -547,6 +603,26 @@ __global__ __launch_bounds__(HG * 128) void attn_kernel(AttnArgs a) {
   const int w_lo = max(s_begin, n_main_pad);
   if (w_lo < s_end) run_chunks(std::true_type{}, w_lo, s_end);  // its first list was published by the last entry chunk
 
+  // The second rotation of the fused epilogue: the output's positional
+  // channels turned back by -p.  The rotation is linear, so it applies to
+  // unnormalised partials too.  Lane (g, r) holds channel cbase + 16 j + r of
+  // four heads; its pair partner is the neighbouring lane (r ^ 1).
+  if (a.rot) {
+#pragma unroll
+    for (int j = 0; j < kHalfNT; ++j) {
+      const int c = cbase + 16 * j;  // uniform in the wave
+      if (c < kDNope) continue;
+      const float2 cs = rope_cs(p, a.rot_turns[(c - kDNope + r) >> 1]);
+      const float sn = (r & 1) ? -cs.y : cs.y;  // (x, y) -> (x c + y s, y c - x s)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float mine = O[j][i];
+        const float other = __builtin_bit_cast(
+            float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, mine), 0xB1, 0xF, 0xF, false));
+        O[j][i] = mine * cs.x + other * sn;
+      }
+    }
+  }
   const int h0 = hg * 16;
   // bf16 results leave through LDS as 16-byte stores: the wave's 16 heads x
   // 288 channels in two halves of 144 channels, staged in the key tile no
@@ -782,8 +858,8 @@ static void launch_split(const AttnArgs &a, bool dense, bool w8, dim3 grid, hipS
 
 hipError_t launch_attention(const CacheView &c, const uint16_t *q, int H, const int32_t *q_pos, int Q,
                             const int32_t *idx, int k, bool dense, const uint16_t *swa, const SwaPlanes *swa8,
-                            const int32_t *swa_pos0, int S, int n_win, float scale, bool out_bf16, void *out,
-                            float *lse, void *ws, hipStream_t stream) {
+                            const int32_t *swa_pos0, int S, int n_win, float scale, double rope_base,
+                            bool out_bf16, void *out, float *lse, void *ws, hipStream_t stream) {
   const AttnShape sh = attn_shape(c.B, Q, dense ? c.N_cap : k, n_win);
   AttnArgs a;
   a.nope = c.nope;
@@ -812,6 +888,9 @@ hipError_t launch_attention(const CacheView &c, const uint16_t *q, int H, const 
   a.nsplit = sh.nsplit;
   a.per_split = sh.per_split;
   a.flags = c.flags;
+  a.rot = rope_base > 0.0 ? 1 : 0;
+  for (int i = 0; i < kDRope / 2; ++i)
+    a.rot_turns[i] = a.rot ? std::pow(rope_base, -2.0 * i / kDRope) / (2.0 * 3.14159265358979323846) : 0.0;
   const size_t po = (size_t)c.B * Q * sh.nsplit * H * kD;
   a.ws_o = reinterpret_cast<float *>(ws);
   a.ws_ml = a.ws_o ? a.ws_o + po : nullptr;

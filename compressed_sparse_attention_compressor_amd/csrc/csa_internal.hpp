@@ -96,7 +96,7 @@ size_t attn_workspace_bytes(int B, int Q, int H, int n_main, int n_win);
 
 hipError_t launch_attention(const CacheView &c, const uint16_t *q, int H, const int32_t *q_pos, int Q,
                             const int32_t *idx, int k, bool dense, const uint16_t *swa, const SwaPlanes *swa8,
-                            const int32_t *swa_pos0, int S, int n_win, float scale, bool out_bf16,
-                            void *out, float *lse, void *ws, hipStream_t stream);
+                            const int32_t *swa_pos0, int S, int n_win, float scale, double rope_base,
+                            bool out_bf16, void *out, float *lse, void *ws, hipStream_t stream);
 
 }  // namespace csa

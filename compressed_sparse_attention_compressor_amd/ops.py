@@ -225,7 +225,8 @@ def layer_stack(layers, q_pos, ws=None):
     (Full), ``qI``, ``w``, ``k``, ``cand`` (Reindex), ``pool_block`` /
     ``pool_blocks`` (Full), and for every layer ``q``, ``swa``, ``swa_pos0``,
     ``n_win``, ``scale`` and optionally ``out_dtype``, ``out``, ``lse``,
-    ``idx_out``, ``pool_out``.  Returns one dict per layer with ``out``,
+    ``idx_out``, ``pool_out``, ``rope_base`` (0 = positional channels as
+    stored; see sparse_attn).  Returns one dict per layer with ``out``,
     ``lse``, and ``idx`` / ``pool`` where the layer writes them.
     """
     B, Q = q_pos.shape
@@ -264,6 +265,7 @@ def layer_stack(layers, q_pos, ws=None):
         e.q, e.H, e.n_win = _ptr(q), H, int(L["n_win"])
         e.swa, e.swa_pos0, e.S = _ptr(swa), _ptr(L.get("swa_pos0")), swa.shape[1] if swa is not None else 0
         e.softmax_scale = float(L["scale"])
+        e.rope_base = float(L.get("rope_base", 0.0))
         e.out_dtype = OUT_BF16 if od == torch.bfloat16 else OUT_F32
         e.out, e.lse = _ptr(r["out"]), _ptr(r["lse"])
         res.append(r)
@@ -281,8 +283,9 @@ def _attn_out(B, Q, H, out_dtype, dev, out):
 
 
 def sparse_attn(cache: Cache, q, q_pos, idx, swa, swa_pos0, n_win, scale, out_dtype=torch.bfloat16, ws=None,
-                out=None, lse=None):
-    """Returns (out [B][Q][H][576], lse fp32 [B][Q][H])."""
+                out=None, lse=None, rope_base=0.0):
+    """Returns (out [B][Q][H][576], lse fp32 [B][Q][H]).  rope_base > 0
+    applies the fused rotary epilogue (csa_sparse_attn in include/csa.h)."""
     _need(q, torch.bfloat16, "q")
     B, Q, H = q.shape[0], q.shape[1], q.shape[2]
     k = idx.shape[2] if idx is not None else 0
@@ -294,13 +297,14 @@ def sparse_attn(cache: Cache, q, q_pos, idx, swa, swa_pos0, n_win, scale, out_dt
     ws, wsb = _workspace(need, ws, dev)
     cs = cache.struct()
     check(lib().csa_sparse_attn(ctypes.byref(cs), _ptr(q), H, _ptr(q_pos), Q, _ptr(idx), k, _ptr(swa), _ptr(swa_pos0),
-                                S, int(n_win), float(scale), OUT_BF16 if out_dtype == torch.bfloat16 else OUT_F32,
-                                _ptr(out), _ptr(lse), _ptr(ws), wsb, _stream()), "csa_sparse_attn")
+                                S, int(n_win), float(scale), float(rope_base),
+                                OUT_BF16 if out_dtype == torch.bfloat16 else OUT_F32, _ptr(out), _ptr(lse), _ptr(ws),
+                                wsb, _stream()), "csa_sparse_attn")
     return out, lse
 
 
 def hca_dense_attn(cache: Cache, q, q_pos, swa, swa_pos0, n_win, scale, out_dtype=torch.bfloat16, ws=None,
-                   out=None, lse=None):
+                   out=None, lse=None, rope_base=0.0):
     _need(q, torch.bfloat16, "q")
     B, Q, H = q.shape[0], q.shape[1], q.shape[2]
     S = swa.shape[1] if swa is not None else 0
@@ -311,8 +315,9 @@ def hca_dense_attn(cache: Cache, q, q_pos, swa, swa_pos0, n_win, scale, out_dtyp
     ws, wsb = _workspace(need, ws, dev)
     cs = cache.struct()
     check(lib().hca_dense_attn(ctypes.byref(cs), _ptr(q), H, _ptr(q_pos), Q, _ptr(swa), _ptr(swa_pos0), S,
-                               int(n_win), float(scale), OUT_BF16 if out_dtype == torch.bfloat16 else OUT_F32,
-                               _ptr(out), _ptr(lse), _ptr(ws), wsb, _stream()), "hca_dense_attn")
+                               int(n_win), float(scale), float(rope_base),
+                               OUT_BF16 if out_dtype == torch.bfloat16 else OUT_F32, _ptr(out), _ptr(lse), _ptr(ws),
+                               wsb, _stream()), "hca_dense_attn")
     return out, lse
 
 
@@ -333,7 +338,7 @@ def swa_encode(x, codes=None, scales=None, rope=None):
 
 
 def sparse_attn_w8(cache: Cache, q, q_pos, idx, swa8, swa_pos0, n_win, scale, out_dtype=torch.bfloat16, ws=None,
-                   out=None, lse=None):
+                   out=None, lse=None, rope_base=0.0):
     """sparse_attn with the window rows as the FP8 planes (codes, scales, rope) of swa_encode."""
     _need(q, torch.bfloat16, "q")
     B, Q, H = q.shape[0], q.shape[1], q.shape[2]
@@ -348,13 +353,13 @@ def sparse_attn_w8(cache: Cache, q, q_pos, idx, swa8, swa_pos0, n_win, scale, ou
     cs = cache.struct()
     check(lib().csa_sparse_attn_w8(ctypes.byref(cs), _ptr(q), H, _ptr(q_pos), Q, _ptr(idx), k, _ptr(codes),
                                    _ptr(scales), _ptr(rope), _ptr(swa_pos0), S, int(n_win), float(scale),
-                                   OUT_BF16 if out_dtype == torch.bfloat16 else OUT_F32, _ptr(out), _ptr(lse),
+                                   float(rope_base), OUT_BF16 if out_dtype == torch.bfloat16 else OUT_F32, _ptr(out), _ptr(lse),
                                    _ptr(ws), wsb, _stream()), "csa_sparse_attn_w8")
     return out, lse
 
 
 def hca_dense_attn_w8(cache: Cache, q, q_pos, swa8, swa_pos0, n_win, scale, out_dtype=torch.bfloat16, ws=None,
-                      out=None, lse=None):
+                      out=None, lse=None, rope_base=0.0):
     """hca_dense_attn with the window rows as FP8 planes."""
     _need(q, torch.bfloat16, "q")
     B, Q, H = q.shape[0], q.shape[1], q.shape[2]
@@ -367,7 +372,7 @@ def hca_dense_attn_w8(cache: Cache, q, q_pos, swa8, swa_pos0, n_win, scale, out_
     ws, wsb = _workspace(need, ws, dev)
     cs = cache.struct()
     check(lib().hca_dense_attn_w8(ctypes.byref(cs), _ptr(q), H, _ptr(q_pos), Q, _ptr(codes), _ptr(scales), _ptr(rope),
-                                  _ptr(swa_pos0), S, int(n_win), float(scale),
+                                  _ptr(swa_pos0), S, int(n_win), float(scale), float(rope_base),
                                   OUT_BF16 if out_dtype == torch.bfloat16 else OUT_F32, _ptr(out), _ptr(lse),
                                   _ptr(ws), wsb, _stream()), "hca_dense_attn_w8")
     return out, lse

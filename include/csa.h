@@ -229,18 +229,33 @@ int csa_index_pool(const csa_cache_t *cache, const float *scores, const int32_t 
  *   swa_pos0 int32 [B]                   n_win >= 0 (0 = no window branch)
  *   out      [B][Q][H][576] fp32 or bf16 (out_dtype)
  *   lse      fp32 [B][Q][H] natural-log sum of exp of the scaled logits, or NULL
- *   ws       >= csa_workspace_bytes(CSA_WS_SPARSE_ATTN, ...) bytes. */
+ *   ws       >= csa_workspace_bytes(CSA_WS_SPARSE_ATTN, ...) bytes.
+ *   rope_base  0: the 64 positional channels (576 - 64 .. 575) are used as
+ *            stored.  > 0 (finite): the fused RoPE-attention-RoPE-cast
+ *            epilogue ([V4.1] "推論カーネル": FlashMLA's fused kernel; [V4]
+ *            CSA paragraph: those channels are kept in BF16).  Channel pair
+ *            (2i, 2i+1) of the positional channels is turned by
+ *            pos * rope_base^(-2i/64) radians, (x, y) -> (x cos - y sin,
+ *            x sin + y cos): the query at its position q_pos, compressed
+ *            entry j at its last raw token (j+1)*m - 1, a window row at its
+ *            raw position; the rotated channels of q and of every key are
+ *            rounded to bf16 before the products, each rotated key is also
+ *            the value, and the output's positional channels are turned back
+ *            by -q_pos before the cast to out_dtype.  The cache and the
+ *            window rows hold the unrotated channels.  Negative, NaN or
+ *            infinite rope_base: CSA_ERR_SHAPE. */
 int csa_sparse_attn(const csa_cache_t *cache, const uint16_t *q, int H, const int32_t *q_pos, int Q,
                     const int32_t *idx, int k, const uint16_t *swa, const int32_t *swa_pos0, int S,
-                    int n_win, float softmax_scale, int out_dtype, void *out, float *lse, void *ws,
-                    size_t ws_bytes, hipStream_t stream);
+                    int n_win, float softmax_scale, float rope_base, int out_dtype, void *out, float *lse,
+                    void *ws, size_t ws_bytes, hipStream_t stream);
 
 /* Dense attention over every visible entry plus the window ([V4] Fig. 4,
  * HCA: no selection; the compressed stream is short).  Arguments as in
  * csa_sparse_attn without idx/k. */
 int hca_dense_attn(const csa_cache_t *cache, const uint16_t *q, int H, const int32_t *q_pos, int Q,
                    const uint16_t *swa, const int32_t *swa_pos0, int S, int n_win, float softmax_scale,
-                   int out_dtype, void *out, float *lse, void *ws, size_t ws_bytes, hipStream_t stream);
+                   float rope_base, int out_dtype, void *out, float *lse, void *ws, size_t ws_bytes,
+                   hipStream_t stream);
 
 /* FP8 window rows ([V4.1] "FP4 主 KV キャッシュ": the sliding-window KV stays
  * FP8, being sensitive to quantisation).  csa_swa_encode turns bf16 raw rows
@@ -267,11 +282,12 @@ int csa_swa_encode(const uint16_t *x, int64_t x_stride_b, int B, int S, uint8_t 
 int csa_sparse_attn_w8(const csa_cache_t *cache, const uint16_t *q, int H, const int32_t *q_pos, int Q,
                        const int32_t *idx, int k, const uint8_t *swa_codes, const uint8_t *swa_scales,
                        const uint16_t *swa_rope, const int32_t *swa_pos0, int S, int n_win, float softmax_scale,
-                       int out_dtype, void *out, float *lse, void *ws, size_t ws_bytes, hipStream_t stream);
+                       float rope_base, int out_dtype, void *out, float *lse, void *ws, size_t ws_bytes,
+                       hipStream_t stream);
 int hca_dense_attn_w8(const csa_cache_t *cache, const uint16_t *q, int H, const int32_t *q_pos, int Q,
                       const uint8_t *swa_codes, const uint8_t *swa_scales, const uint16_t *swa_rope,
-                      const int32_t *swa_pos0, int S, int n_win, float softmax_scale, int out_dtype, void *out,
-                      float *lse, void *ws, size_t ws_bytes, hipStream_t stream);
+                      const int32_t *swa_pos0, int S, int n_win, float softmax_scale, float rope_base,
+                      int out_dtype, void *out, float *lse, void *ws, size_t ws_bytes, hipStream_t stream);
 
 /* A stack of CSA2 layers for the same query tokens ([V4.1], CSA2 paragraph
  * and Fig. 4: every layer is statically Full, Reindex or Reuse; Fig. 5: the
@@ -317,6 +333,7 @@ typedef struct {
   int32_t out_dtype;         /* CSA_OUT_F32 or CSA_OUT_BF16                          */
   void *out;                 /* [B][Q][H][576]                                       */
   float *lse;                /* fp32 [B][Q][H] or NULL                               */
+  float rope_base;           /* 0, or the rotary base of the fused epilogue          */
 } csa2_layer_t;
 
 /*   n_layers  1..256

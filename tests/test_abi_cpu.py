@@ -96,8 +96,9 @@ def test_index_topk_checks(L):
 
 
 def _attn(L, c, q=P, H=64, qp=P, Q=1, idx=P, k=16, swa=P, s0=P, S=128, nw=128, scale=1.0, od=1, out=P,
-          ws=P, wsb=1 << 30):
-    return L.csa_sparse_attn(ctypes.byref(c), q, H, qp, Q, idx, k, swa, s0, S, nw, scale, od, out, None, ws, wsb, None)
+          ws=P, wsb=1 << 30, rope=0.0):
+    return L.csa_sparse_attn(ctypes.byref(c), q, H, qp, Q, idx, k, swa, s0, S, nw, scale, rope, od, out, None, ws, wsb,
+                             None)
 
 
 def test_attention_checks(L):
@@ -108,6 +109,10 @@ def test_attention_checks(L):
     assert _attn(L, _cache(), H=256) == EUNSUP
     assert _attn(L, _cache(), od=5) == EUNSUP
     assert _attn(L, _cache(), scale=float("nan")) == ESHAPE
+    assert _attn(L, _cache(), rope=-1.0) == ESHAPE
+    assert _attn(L, _cache(), rope=float("nan")) == ESHAPE
+    assert _attn(L, _cache(), rope=float("inf")) == ESHAPE
+    assert _attn(L, _cache(), rope=10000.0, Q=0) == OK
     assert _attn(L, _cache(), k=-2) == ESHAPE
     assert _attn(L, _cache(), nw=-1) == ESHAPE
     assert _attn(L, _cache(), out=P + 2) == EALIGN
@@ -115,7 +120,7 @@ def test_attention_checks(L):
     assert need > 0
     assert _attn(L, _cache(), wsb=need - 1) == EWS
     assert _attn(L, _cache(), Q=0) == OK
-    assert L.hca_dense_attn(ctypes.byref(_cache(d_idx=0)), None, 64, P, 1, P, P, 128, 128, 1.0, 1, P, None, P,
+    assert L.hca_dense_attn(ctypes.byref(_cache(d_idx=0)), None, 64, P, 1, P, P, 128, 128, 1.0, 0.0, 1, P, None, P,
                             1 << 30, None) == ENULL
 
 
@@ -218,17 +223,17 @@ def test_fp8_window_checks(L):
     # csa_sparse_attn_w8 / hca_dense_attn_w8: the window planes are checked first
     def sw8(codes=P, scales=P, rope=P, nw=128):
         return L.csa_sparse_attn_w8(ctypes.byref(_cache()), P, 64, P, 1, P, 16, codes, scales, rope, P, 128, nw, 1.0,
-                                    1, P, None, P, 1 << 30, None)
+                                    0.0, 1, P, None, P, 1 << 30, None)
     assert sw8(codes=None) == ENULL
     assert sw8(scales=None) == ENULL
     assert sw8(codes=P + 4) == EALIGN
     assert sw8(rope=P + 8) == EALIGN
-    assert L.csa_sparse_attn_w8(ctypes.byref(_cache()), P, 48, P, 1, P, 16, P, P, P, P, 128, 128, 1.0, 1, P, None, P,
-                                1 << 30, None) == EUNSUP
-    assert L.hca_dense_attn_w8(ctypes.byref(_cache(d_idx=0)), P, 64, P, 1, None, P, P, P, 128, 128, 1.0, 1, P, None,
-                               P, 1 << 30, None) == ENULL
-    assert L.csa_sparse_attn_w8(ctypes.byref(_cache()), P, 64, P, 0, P, 16, P, P, P, P, 128, 128, 1.0, 1, P, None,
-                                P, 1 << 30, None) == OK                # Q = 0: nothing to launch
+    assert L.csa_sparse_attn_w8(ctypes.byref(_cache()), P, 48, P, 1, P, 16, P, P, P, P, 128, 128, 1.0, 0.0, 1, P,
+                                None, P, 1 << 30, None) == EUNSUP
+    assert L.hca_dense_attn_w8(ctypes.byref(_cache(d_idx=0)), P, 64, P, 1, None, P, P, P, 128, 128, 1.0, 0.0, 1, P,
+                               None, P, 1 << 30, None) == ENULL
+    assert L.csa_sparse_attn_w8(ctypes.byref(_cache()), P, 64, P, 0, P, 16, P, P, P, P, 128, 128, 1.0, 0.0, 1, P,
+                                None, P, 1 << 30, None) == OK                # Q = 0: nothing to launch
 
 
 def test_read_device_flags_null(L):

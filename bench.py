@@ -30,6 +30,7 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
+ROPE_BASE = 10000.0  # rotary base of the fused-epilogue leg (the original rotary embedding's)
 METRIC = "CSA decode query-tokens/s + achieved HBM GB/s at 128K ctx (1 MI355X)"
 HBM_PEAK_GBPS = 8000.0
 FP8_PEAK_TFLOPS = 5000.0
@@ -312,10 +313,15 @@ def main():
     log(f"[bench] stage averages (us): {stage_us}")
 
     # The same step with the window rows as FP8 planes (the window KV format
-    # the pages state); reported beside the headline, which keeps bf16 rows.
-    w8 = None
-    if not args.only:
-        g8 = capture(lambda: [(st_front(layers[l]), st_attn_w8(layers[l])) for l in range(L)])
+    # the pages state), and that step with the fused rotary epilogue as well
+    # (rotary base 10,000); reported beside the headline, which keeps bf16
+    # rows and no rotation.
+    def st_attn_w8_rope(ly):
+        csa.sparse_attn_w8(ly.cache, ly.q, ly.q_pos, ly.idx, ly.swa8, ly.swa_pos0, w.n_win, w.softmax_scale,
+                           out_dtype=torch.bfloat16, ws=attn_ws, out=ly.out, lse=ly.lse, rope_base=ROPE_BASE)
+
+    def time_variant(st_a):
+        g8 = capture(lambda: [(st_front(layers[l]), st_a(layers[l])) for l in range(L)])
         g8.replay()
         torch.cuda.synchronize()
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -326,7 +332,7 @@ def main():
         torch.cuda.synchronize()
         ms8 = a.elapsed_time(b) / (max(1, K // L) * L)
         del g8
-        ga = capture(lambda: [st_attn_w8(layers[i % L]) for i in range(R)])
+        ga = capture(lambda: [st_a(layers[i % L]) for i in range(R)])
         ga.replay()
         torch.cuda.synchronize()
         a.record()
@@ -336,14 +342,26 @@ def main():
         torch.cuda.synchronize()
         attn8_us = a.elapsed_time(b) * 1e3 / (5 * R)
         del ga
+        return ms8, attn8_us
+
+    w8 = w8r = None
+    if not args.only:
         by8 = step_bytes(w)
         win16 = w.B * 2 * w.n_win * 576
         win8 = w.B * w.n_win * (512 + 16 + 128)
         step8 = by8["step"] - win16 + win8
+        ms8, attn8_us = time_variant(st_attn_w8)
         w8 = {"window": "MXFP8 content channels + bf16 positional channels (656 B per row)",
               "ms_per_step": round(ms8, 6), "q_tokens_per_s": round(w.B / (ms8 * 1e-3), 1), "step_bytes": step8,
               "achieved_GBps": round(step8 / (ms8 * 1e-3) / 1e9, 1), "sparse_attn_us": round(attn8_us, 3)}
         log(f"[bench] FP8 window step {ms8 * 1e3:.2f} us, attention {attn8_us:.2f} us")
+        msr, attnr_us = time_variant(st_attn_w8_rope)
+        w8r = {"window": "MXFP8 window rows", "rope_base": ROPE_BASE,
+               "epilogue": "q rotated by its position, entries at (j+1)m-1 and window rows at their positions "
+                           "rotated in the decode, output rotated back by -p, then cast to bf16",
+               "ms_per_step": round(msr, 6), "q_tokens_per_s": round(w.B / (msr * 1e-3), 1), "step_bytes": step8,
+               "achieved_GBps": round(step8 / (msr * 1e-3) / 1e9, 1), "sparse_attn_us": round(attnr_us, 3)}
+        log(f"[bench] FP8 window + rotary epilogue step {msr * 1e3:.2f} us, attention {attnr_us:.2f} us")
 
     by = step_bytes(w)
     # the dominant kernel: the fused append + indexer launch
@@ -379,6 +397,7 @@ def main():
         "stage_us": {k: round(v, 3) for k, v in stage_us.items()},
         "ms_per_step_spread": spread,
         "fp8_window": w8,
+        "fp8_window_rope": w8r,
         "warm_one_layer": {"ms_per_step": round(warm_ms, 6), "q_tokens_per_s": round(w.B / (warm_ms * 1e-3), 1),
                            "note": "one layer's cache replayed L times in a row (warm); not the headline"},
         "roofline": {"bound": "hbm", "kernel": "append_index_kernel (decode append + indexer)",

@@ -83,7 +83,22 @@ struct AttnArgs {
   // base^(-2i/64) / (2 pi), the turn per position, in fp64.
   int rot;
   double rot_turns[kDRope / 2];
+  // Workgroup -> (query row, split).  With xcd != 0 (at least 8 rows) every
+  // split of row r gets a linear id = r (mod 8): workgroups are dealt to the
+  // 8 XCDs round-robin by linear id, so a row's query, its partials and its
+  // merge stay in one XCD's L2.
+  int rows, xcd;
 };
+
+// The XCD-aware order: workgroup L sits on XCD L % 8 and takes the
+// (L / 8)-th (row, part) pair of that XCD's rows r = x, x + 8, ...
+// Returns false for the workgroups past the last row.
+__device__ __forceinline__ bool xcd_slot(int L, int per_row, int rows, int &row, int &part) {
+  const int x = L & 7, sidx = L >> 3;
+  row = x + 8 * (sidx / per_row);
+  part = sidx % per_row;
+  return row < rows;
+}
 
 // cos and sin of the rotary angle of pair i at position pos: the angle in
 // turns is reduced to [0, 1) in fp64 (exact to ~1e-10 turn for positions
@@ -333,7 +348,14 @@ __global__ __launch_bounds__(HG * 128) void attn_kernel(AttnArgs a) {
   // written while a slower wave may still read that of chunk c.
   __shared__ int src_s[3][kKC];
 
-  const int split = blockIdx.x % a.nsplit, q = blockIdx.x / a.nsplit, b = blockIdx.y;
+  int row_id, split;
+  if (a.xcd) {
+    if (!xcd_slot(blockIdx.x, a.nsplit, a.rows, row_id, split)) return;  // the whole workgroup, before any barrier
+  } else {
+    row_id = blockIdx.x / a.nsplit;
+    split = blockIdx.x % a.nsplit;
+  }
+  const int q = row_id % a.Q, b = row_id / a.Q;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4, r = lane & 15;
@@ -354,16 +376,27 @@ __global__ __launch_bounds__(HG * 128) void attn_kernel(AttnArgs a) {
     const int32_t *ip = a.idx + qrow * a.k;
     return int2{ip[sc], ip[max(sc - 1, 0)]};
   };
+  // Every load the prologue needs goes out in one round: the first slot's
+  // index, the query's position, the entry count, the window's first row
+  // and the query itself (valid addresses whatever the position turns out
+  // to be); nothing waits on another load.
   const int2 j_first = fetch_slot(s_begin);
   const int p = a.q_pos[qrow];
   const int nE_raw = a.n_entries[b];
+  const int swa0_raw = a.n_win > 0 ? a.swa_pos0[b] : 0;
+  v8bf Qf[kQSteps];
+  {
+    const uint16_t *qp = a.q + (qrow * a.H + hg * 16 + r) * kD + cbase + 8 * g;
+#pragma unroll
+    for (int kk = 0; kk < kQSteps; ++kk) Qf[kk] = *reinterpret_cast<const v8bf *>(qp + 32 * kk);
+  }
   const int nE = min(nE_raw, a.N_cap);
   const int V = p >= 0 ? max(0, min(nE, (p + 1) / a.m)) : 0;
   const int n_main = kDense ? V : a.k;
   const int n_main_pad = (n_main + kKC - 1) / kKC * kKC;
   int win_lo = 0, n_swa = 0, swa0 = 0;
   if (a.n_win > 0 && p >= 0) {
-    swa0 = a.swa_pos0[b];
+    swa0 = swa0_raw;
     win_lo = max(max(0, p - a.n_win + 1), swa0);
     const int win_hi = min(p, swa0 + a.S - 1);
     n_swa = max(0, win_hi - win_lo + 1);
@@ -413,12 +446,8 @@ __global__ __launch_bounds__(HG * 128) void attn_kernel(AttnArgs a) {
 #pragma unroll
   for (int j = 0; j < kHalfNT; ++j) O[j] = v4f{0.f, 0.f, 0.f, 0.f};
 
-  v8bf Qf[kQSteps];
   if (s_begin < s_end) {
-    const int2 j0 = j_first;  // issued before the query loads
-    const uint16_t *qp = a.q + (qrow * a.H + hg * 16 + r) * kD + cbase + 8 * g;
-#pragma unroll
-    for (int kk = 0; kk < kQSteps; ++kk) Qf[kk] = *reinterpret_cast<const v8bf *>(qp + 32 * kk);
+    const int2 j0 = j_first;
     if (a.rot) {
       // the first rotation of the fused epilogue: the query's positional
       // channels turned by its own position (rounded to bf16 as they are
@@ -736,10 +765,21 @@ constexpr int kMergeThreads = 256;
 template <bool kBf16, int kU>
 __global__ __launch_bounds__(kMergeThreads) void attn_merge_kernel(const float *__restrict__ ws_o,
                                                                    const float *__restrict__ ws_ml, int nsplit, int H,
-                                                                   int64_t n_items, void *out, float *lse) {
-  const int64_t item = (int64_t)blockIdx.x * kMergeThreads + threadIdx.x;  // (qrow, head, channel group of 8)
-  if (item >= n_items) return;
+                                                                   int64_t n_items, void *out, float *lse, int rows,
+                                                                   int xcd, int wg_per_row) {
   constexpr int kGroups = kD / 8;
+  int64_t item;  // (qrow, head, channel group of 8)
+  if (xcd) {
+    // the row's splits ran on XCD row % 8 (xcd_slot): merge it there
+    int row, part;
+    if (!xcd_slot(blockIdx.x, wg_per_row, rows, row, part)) return;
+    const int in_row = part * kMergeThreads + threadIdx.x;
+    if (in_row >= H * kGroups) return;
+    item = (int64_t)row * H * kGroups + in_row;
+  } else {
+    item = (int64_t)blockIdx.x * kMergeThreads + threadIdx.x;
+    if (item >= n_items) return;
+  }
   const int64_t qh = item / kGroups;  // qrow * H + head
   const int c8 = (int)(item % kGroups) * 8;
   const int64_t qrow = qh / H, hh = qh % H;
@@ -894,7 +934,9 @@ hipError_t launch_attention(const CacheView &c, const uint16_t *q, int H, const 
   const size_t po = (size_t)c.B * Q * sh.nsplit * H * kD;
   a.ws_o = reinterpret_cast<float *>(ws);
   a.ws_ml = a.ws_o ? a.ws_o + po : nullptr;
-  dim3 grid((unsigned)(sh.nsplit * Q), c.B);
+  a.rows = c.B * Q;
+  a.xcd = a.rows >= 8 && sh.nsplit > 1 ? 1 : 0;  // fewer rows would leave XCDs idle; one split has no merge
+  dim3 grid(a.xcd ? (unsigned)(8 * ((a.rows + 7) / 8) * sh.nsplit) : (unsigned)(sh.nsplit * a.rows));
   if (out_bf16)
     launch_split<false>(a, dense, swa8 != nullptr, grid, stream);
   else
@@ -902,15 +944,21 @@ hipError_t launch_attention(const CacheView &c, const uint16_t *q, int H, const 
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || sh.nsplit == 1) return e;
   const int64_t n_items = (int64_t)c.B * Q * H * (kD / 8);
-  const unsigned nb = (unsigned)((n_items + kMergeThreads - 1) / kMergeThreads);
+  const int wg_per_row = (H * (kD / 8) + kMergeThreads - 1) / kMergeThreads;
+  const unsigned nb = a.xcd ? (unsigned)(8 * ((a.rows + 7) / 8) * wg_per_row)
+                            : (unsigned)((n_items + kMergeThreads - 1) / kMergeThreads);
+#define CSA_MERGE(BF, U)                                                                                    \
+  attn_merge_kernel<BF, U><<<nb, kMergeThreads, 0, stream>>>(a.ws_o, a.ws_ml, sh.nsplit, H, n_items, out, lse, \
+                                                             a.rows, a.xcd, wg_per_row)
   if (out_bf16 && sh.nsplit > 16)
-    attn_merge_kernel<true, 32><<<nb, kMergeThreads, 0, stream>>>(a.ws_o, a.ws_ml, sh.nsplit, H, n_items, out, lse);
+    CSA_MERGE(true, 32);
   else if (out_bf16 && sh.nsplit > 8)
-    attn_merge_kernel<true, 16><<<nb, kMergeThreads, 0, stream>>>(a.ws_o, a.ws_ml, sh.nsplit, H, n_items, out, lse);
+    CSA_MERGE(true, 16);
   else if (out_bf16)
-    attn_merge_kernel<true, 8><<<nb, kMergeThreads, 0, stream>>>(a.ws_o, a.ws_ml, sh.nsplit, H, n_items, out, lse);
+    CSA_MERGE(true, 8);
   else
-    attn_merge_kernel<false, 8><<<nb, kMergeThreads, 0, stream>>>(a.ws_o, a.ws_ml, sh.nsplit, H, n_items, out, lse);
+    CSA_MERGE(false, 8);
+#undef CSA_MERGE
   return hipGetLastError();
 }
 

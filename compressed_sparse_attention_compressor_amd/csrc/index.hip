@@ -6,14 +6,19 @@
 //
 // The contraction runs on the gfx950 block-scaled MFMA
 // v_mfma_scale_f32_16x16x128_f8f6f4: A = 16 indexer heads x 128 channels of
-// E4M3 queries (unit scale byte 127), B = 128 channels x 16 entries of E2M1
+// E4M3 queries (block scales 1 or 2^-3, below), B = 128 channels x 16 entries of E2M1
 // keys with the entries' own E8M0 bytes as the B scales.  For the E2M1
 // operand, lane l supplies entry l%16 and channels 32(l/16)..+31 (low nibble
 // first), i.e. 16 contiguous key bytes, plus that block's scale byte: a wave
 // reads 16 whole 64-byte key rows per instruction (fully coalesced).  The
 // E4M3 operand of lane group g holds channels 16g..16g+15 and 64+16g..+15;
 // the scale of channel block b comes from lane group b for both operands
-// (established with an in-bounds probe of the instruction).  E4M3 x E2M1 products are exact in fp32;
+// (established with an in-bounds probe of the instruction).  E4M3 x E2M1
+// products of normal E4M3 codes are exact in fp32, those of subnormal codes
+// are not (the instruction keeps them to a multiple of 2^-9 before the
+// scales): every query block of 32 channels whose largest magnitude is at
+// most 56 is therefore multiplied by 2^3 and given the scale 2^-3, which
+// turns its subnormal codes into exact normal ones;
 // the 16x16 result (lane l: entry l%16, heads 4(l/16)..+3) goes through
 // ReLU and the head weights in registers, then two cross-lane adds finish
 // the head sum.
@@ -38,6 +43,65 @@ __device__ __forceinline__ float reduce_scatter4(float p0, float p1, float p2, f
   return __uint_as_float(z[0]) + __uint_as_float(z[1]);
 }
 
+// --- Query block rescaling (E4M3, blocks of 32 channels) ------------------
+// Nonzero when a byte of the 16 codes has a magnitude above 56 (code 0x66):
+// such a block keeps scale 1.
+__device__ __forceinline__ uint32_t e4m3_over56(uint4 v) {
+  auto o = [](uint32_t w) { return ((w & 0x7F7F7F7Fu) + 0x19191919u) & 0x80808080u; };
+  return o(v.x) | o(v.y) | o(v.z) | o(v.w);
+}
+
+// Four E4M3 codes times 2^3, exactly, for magnitudes up to 56: codes with an
+// exponent gain 3 in it; a subnormal m 2^-9 (m = 1..7) becomes the normal
+// code of m 2^-6, looked up in an 8-byte table with v_perm_b32.
+__device__ __forceinline__ uint32_t e4m3_times8(uint32_t w) {
+  const uint32_t mag = w & 0x7F7F7F7Fu;
+  const uint32_t nrm = ((mag & 0x78787878u) + 0x78787878u) & 0x80808080u;  // 0x80 where the exponent is nonzero
+  const uint32_t nmask = (nrm >> 7) * 0xFFu;
+  const uint32_t sub = __builtin_amdgcn_perm(0x1E1C1A18u, 0x14100800u, mag & 0x07070707u);
+  return (w & 0x80808080u) | ((mag + 0x18181818u) & nmask) | (sub & ~nmask);
+}
+
+__device__ __forceinline__ uint4 e4m3_times8(uint4 v) {
+  return uint4{e4m3_times8(v.x), e4m3_times8(v.y), e4m3_times8(v.z), e4m3_times8(v.w)};
+}
+
+constexpr int kQScale1 = 127;     // E8M0 byte of 1
+constexpr int kQScaleDiv8 = 124;  // E8M0 byte of 2^-3
+
+// A staged 16-byte piece of a query row: pieces 2j and 2j+1 of a row (block
+// j) sit in neighbouring lanes.  Rescales the piece when its block allows it
+// and returns the block's E8M0 byte.  Every lane of the wave must call it.
+__device__ __forceinline__ int e4m3_rescale_piece(uint4 &v) {
+  const int over = e4m3_over56(v) != 0u;
+  const int blk_over = over | __shfl_xor(over, 1);
+  if (!blk_over) v = e4m3_times8(v);
+  return blk_over ? kQScale1 : kQScaleDiv8;
+}
+
+// The A fragment of lane (g, r) (head row r; channels 16g..16g+15 in words
+// 0..3, 64+16g..+15 in words 4..7): blocks g/2 and 2 + g/2, each shared with
+// lane group g ^ 1.  Rescales the lane's halves of the blocks that allow it
+// and returns the E8M0 byte of block g, the scale this lane supplies.  Every
+// lane of the wave must call it.
+__device__ __forceinline__ int e4m3_rescale_fragment(v8i &A, int g, int r) {
+  const uint4 lo = {(uint32_t)A[0], (uint32_t)A[1], (uint32_t)A[2], (uint32_t)A[3]};
+  const uint4 hi = {(uint32_t)A[4], (uint32_t)A[5], (uint32_t)A[6], (uint32_t)A[7]};
+  const uint64_t bl = __ballot(e4m3_over56(lo) != 0u), bh = __ballot(e4m3_over56(hi) != 0u);
+  // bit 32 j + r: block j (of the low halves) resp. 2 + j (high) of head r is over
+  const uint64_t fl = bl | (bl >> 16), fh = bh | (bh >> 16);
+  const int sh = 32 * (g >> 1) + r;
+  if (!((fl >> sh) & 1)) {
+    const uint4 t = e4m3_times8(lo);
+    A[0] = (int)t.x; A[1] = (int)t.y; A[2] = (int)t.z; A[3] = (int)t.w;
+  }
+  if (!((fh >> sh) & 1)) {
+    const uint4 t = e4m3_times8(hi);
+    A[4] = (int)t.x; A[5] = (int)t.y; A[6] = (int)t.z; A[7] = (int)t.w;
+  }
+  return (((g < 2 ? fl : fh) >> (32 * (g & 1) + r)) & 1) ? kQScale1 : kQScaleDiv8;
+}
+
 // HT: head tiles of 16 (H_I <= 16 * HT).  QB: queries per wave.  The body of
 // one workgroup: entry tile bx, query block by, sequence b; the score of
 // entry `skip` (-1: none) is left to another workgroup.
@@ -50,6 +114,7 @@ __device__ __forceinline__ void index_body(
   // Indexer queries of this workgroup (QB queries x 16*HT heads x d_idx bytes),
   // staged once so that the waves read their MFMA fragments from LDS.
   __shared__ __attribute__((aligned(16))) uint8_t qs[QB * HT * 16 * 128];
+  __shared__ uint8_t qsc[QB * HT * 16 * 4];  // E8M0 byte of each query block
   // One-query full scans may also count their scores by the top bits of the
   // order-preserving key for the top-k launch (kHintBins per row, added
   // into the row's global counts at the end).
@@ -176,13 +241,16 @@ __device__ __forceinline__ void index_body(
       }
   }
 
-  // 3. Queries into LDS (zero rows beyond H_I and beyond Q).
+  // 3. Queries into LDS (zero rows beyond H_I and beyond Q), rescaled by
+  //    block, with each block's scale byte.
 #pragma unroll
   for (int u = 0; u < kQVec; ++u) {
     const int i = threadIdx.x + u * kIdxThreads;
+    const int sc = e4m3_rescale_piece(qv_stage[u]);
     if (i < QB * kQBytes / 16) {
       const int qb = i / (kQBytes / 16), rem = (i % (kQBytes / 16)) * 16;
       *reinterpret_cast<uint4 *>(qs + qb * kQBytes + rem) = qv_stage[u];
+      if (!(i & 1)) qsc[i >> 1] = (uint8_t)sc;
     }
   }
   // LDS-only barrier: the key loads stay in flight, each MFMA below waits
@@ -191,6 +259,7 @@ __device__ __forceinline__ void index_body(
   // E4M3 operand layout of the instruction: bytes 0..15 of lane group g hold
   // channels 16g..16g+15, bytes 16..31 hold channels 64+16g..+15.
   v8i A[QB][HT];
+  int sa[QB][HT];  // the scale of block g of head row r
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
@@ -199,6 +268,7 @@ __device__ __forceinline__ void index_body(
       const v4i lo = *reinterpret_cast<const v4i *>(qr + 16 * g);
       const v4i hi = *reinterpret_cast<const v4i *>(qr + 64 + 16 * g);
       A[qb][ht] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      sa[qb][ht] = qsc[(qb * HT * 16 + ht * 16 + r) * 4 + g];
     }
 
   // 4. Visibility of this workgroup's queries (uniform loads).
@@ -233,7 +303,7 @@ __device__ __forceinline__ void index_body(
 #pragma unroll
         for (int ht = 0; ht < HT; ++ht) {
           v4f acc = {0.f, 0.f, 0.f, 0.f};
-          acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A[qb][ht], Bm, acc, 0, 4, 0, 127, 0, sbu);
+          acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A[qb][ht], Bm, acc, 0, 4, 0, sa[qb][ht], 0, sbu);
 #pragma unroll
           for (int i = 0; i < 4; ++i) sum = fmaf(fmaxf(acc[i], 0.f), wv[qb][ht][i], sum);
         }
@@ -336,6 +406,7 @@ __device__ __forceinline__ void append_and_score(const AppendArgs &ap, uint8_t *
   __shared__ __attribute__((aligned(16))) uint8_t kc[64];
   __shared__ uint32_t ksc[4];
   __shared__ __attribute__((aligned(16))) uint8_t qs[HT * 16 * 128];
+  __shared__ uint8_t qsc[HT * 16 * 4];  // E8M0 byte of each query block
   const int tid = threadIdx.x;
   const int m = ap.m;
   const int nkb = d_idx / 32;
@@ -410,7 +481,11 @@ __device__ __forceinline__ void append_and_score(const AppendArgs &ap, uint8_t *
 #pragma unroll
   for (int u = 0; u < kQVec; ++u) {
     const int i = tid + u * kIdxThreads;
-    if (i < kQBytes / 16) *reinterpret_cast<uint4 *>(qs + i * 16) = qv_stage[u];
+    const int sc = e4m3_rescale_piece(qv_stage[u]);  // as in the indexer body
+    if (i < kQBytes / 16) {
+      *reinterpret_cast<uint4 *>(qs + i * 16) = qv_stage[u];
+      if (!(i & 1)) qsc[i >> 1] = (uint8_t)sc;
+    }
   }
   // the projection's first batch of W_IK loads goes out now and stays in
   // flight across the LDS-only barrier and the main entry's encoding
@@ -522,8 +597,9 @@ __device__ __forceinline__ void append_and_score(const AppendArgs &ap, uint8_t *
     const v4i lo = *reinterpret_cast<const v4i *>(qr + 16 * g);
     const v4i hi = *reinterpret_cast<const v4i *>(qr + 64 + 16 * g);
     const v8i A = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    const int sa = qsc[(ht * 16 + r) * 4 + g];
     v4f acc = {0.f, 0.f, 0.f, 0.f};
-    acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, Bm, acc, 0, 4, 0, 127, 0, sbu);
+    acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, Bm, acc, 0, 4, 0, sa, 0, sbu);
 #pragma unroll
     for (int i = 0; i < 4; ++i) sum = fmaf(fmaxf(acc[i], 0.f), wv[ht][i], sum);
   }
@@ -698,6 +774,7 @@ __global__ __launch_bounds__(kPfWaves * 64) void index_prefill_kernel(
   // zeroed in A, which zeroes their scores whatever weight they meet; rows
   // of queries past Q are never stored.
   v8i A[QW][HT];
+  int sa[QW][HT];  // the scale of block g of head row r
   float w[QW][HT][4];
 #pragma unroll
   for (int qw = 0; qw < QW; ++qw) {
@@ -711,6 +788,7 @@ __global__ __launch_bounds__(kPfWaves * 64) void index_prefill_kernel(
       const int ml = -(int)(h < H_I);
       const int mh = ml & -(int)(d_idx > 64);
       A[qw][ht] = v8i{lo[0] & ml, lo[1] & ml, lo[2] & ml, lo[3] & ml, hi[0] & mh, hi[1] & mh, hi[2] & mh, hi[3] & mh};
+      sa[qw][ht] = e4m3_rescale_fragment(A[qw][ht], g, r);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int hh = ht * 16 + g * 4 + i;
@@ -742,7 +820,7 @@ __global__ __launch_bounds__(kPfWaves * 64) void index_prefill_kernel(
 #pragma unroll
           for (int ht = 0; ht < HT; ++ht)
             acc[qw & 1][ht] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                A[qw][ht], Bm, v4f{0.f, 0.f, 0.f, 0.f}, 0, 4, 0, 127, 0, sbu);
+                A[qw][ht], Bm, v4f{0.f, 0.f, 0.f, 0.f}, 0, 4, 0, sa[qw][ht], 0, sbu);
         }
         if (qw > 0) {
           float s = 0.f;

@@ -95,20 +95,28 @@ def check_topk(g_idx, o_idx, js, scores, rel=1e-4, what=""):
 def index_score_tol(qI_u8, w_f32, ikey_rows, iscale_rows, ref=None):
     """Per-entry bound on |GPU score - oracle score| for the indexer.
 
-    Three parts:
-    * fp32 evaluation of the sums: any order of summing the d_idx products of
-      a head and then the H_I weighted heads errs by at most
-      (d_idx + H_I) * 2^-24 relative to the sum of the absolute terms,
+    Four parts:
+    * fp32 evaluation of the head sum: any order of summing the H_I weighted
+      heads (and of summing fp32 partials) errs by at most (d_idx + H_I) *
+      2^-24 relative to the sum of the absolute terms,
       sum_h |w_h| * sum_c |q_hc * k_jc|; 1e-5 covers d_idx + H_I <= 160;
+    * the block-scaled matrix instruction's own sum of one head's (up to)
+      128 products: measured on gfx950 to hold each such dot product only to
+      a fraction of its largest product (at most 3.3e-4 of it over query
+      codes spanning 2^-6..448 and key scale bytes 100..154; nearly exact
+      when the products span few binades); bounded here by 2^-9 x that
+      largest product: 2^-9 * sum_h |w_h| * max_c |q_hc * k_jc|;
     * rounding in the subnormal range (keys with tiny block scales): at most
       2^-149 per operation, (d_idx + H_I) * 2^-149 * sum_h |w_h|;
-    * the matrix instruction's handling of E4M3 subnormal query codes
-      (exponent field 0, mantissa m): their products with E2M1 codes are
-      kept only to a multiple of 2^-9 before the block scale, so each such
-      product may lose up to 2^-10 x its block's scale (measured on gfx950;
-      E4M3 x E2M1 products of normal codes come out exact).  The loss passes
-      through ReLU (1-Lipschitz) and the head weight:
-      sum_h |w_h| * sum_c [q_hc subnormal] 2^-10 * S_j(c).
+    * subnormal E4M3 query codes in a block of 32 channels that also holds a
+      magnitude above 56: the kernels multiply every other block by 2^3 (and
+      give it the scale 2^-3), which makes its subnormal codes normal, but
+      such a block keeps scale 1, and the instruction keeps products of
+      subnormal E4M3 codes with E2M1 codes only to a multiple of 2^-9 before
+      the block scale (measured on gfx950), a loss of up to 2^-10 x its key
+      block's scale per product, through ReLU (1-Lipschitz) and the head
+      weight: sum_h |w_h| * sum_{c in such blocks} [q_hc subnormal] 2^-10 *
+      S_j(c).  Zero for every query whose blocks all stay at or below 56.
     """
     q = np.asarray(qI_u8, dtype=np.uint8)
     H, d = q.shape
@@ -116,12 +124,17 @@ def index_score_tol(qI_u8, w_f32, ikey_rows, iscale_rows, ref=None):
     k = np.abs(mxfp4_decode(np.asarray(ikey_rows), np.asarray(iscale_rows)))    # [V][d]
     qa = np.abs(e4m3_to_f64(q))                                                 # [H][d]
     mag = (k @ qa.T) @ wa                                                       # [V]
-    sub = ((q & 0x78) == 0) & ((q & 0x07) != 0)                                 # [H][d]
+    big = np.empty(k.shape[0])
+    for j0 in range(0, k.shape[0], 512):                                        # max_c |q_hc k_jc|, chunked
+        big[j0:j0 + 512] = (k[j0:j0 + 512, None, :] * qa[None, :, :]).max(axis=2) @ wa
     nb = d // 32
-    n_hb = sub.reshape(H, nb, 32).sum(axis=2)                                   # [H][nb]
+    sub = ((q & 0x78) == 0) & ((q & 0x07) != 0)                                 # [H][d]
+    keeps1 = ((q & 0x7F).reshape(H, nb, 32) > 0x66).any(axis=2)                # [H][nb]
+    n_hb = sub.reshape(H, nb, 32).sum(axis=2) * keeps1                          # [H][nb]
     per_blk = (n_hb * wa[:, None]).sum(axis=0)                                  # [nb]
     S = np.exp2(np.asarray(iscale_rows, dtype=np.float64)[:, :nb] - 127.0)     # [V][nb]
-    return 1e-5 * mag + (d + H) * 2.0 ** -149 * wa.sum() + 2.0 ** -10 * (S @ per_blk)
+    return (1e-5 * mag + 2.0 ** -9 * big + (d + H) * 2.0 ** -149 * wa.sum()
+            + 2.0 ** -10 * (S @ per_blk))
 
 
 def compress_bounds(out, m, W=None):

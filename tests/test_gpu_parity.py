@@ -218,8 +218,9 @@ def test_indexer_single_products(Q):
     """Every E4M3 code against every E2M1 code, one product per score: query
     t has one nonzero channel (code t, skipping the two NaN codes) in head 0,
     weight 1, every key channel of entry j holds E2M1 code j, so that
-    score(t, j) = max(0, e4m3(t) * e2m1(j)).  Normal E4M3 codes must come out
-    exact; subnormal ones within the 2^-10 the indexer tolerance allows.
+    score(t, j) = max(0, e4m3(t) * e2m1(j)).  Every product must come out
+    exact: a code alone in its block of 32 channels is either above 56
+    (a normal code) or rescaled by 2^3, which makes a subnormal code normal.
     Q picks the launch shape (one query, several per workgroup, prefill)."""
     codes = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], dtype=np.uint8)
     sel = codes if Q == len(codes) else np.resize(np.array([0x01, 0x83, 0x08, 0xB5, 0x7E, 0xFE], np.uint8), Q)
@@ -241,10 +242,45 @@ def test_indexer_single_products(Q):
     qv = O.e4m3_to_f64(sel)
     kv = O.e2m1_to_f64(e2)
     ref = np.maximum(qv[:, None] * kv[None, :], 0.0)
-    sub = ((sel & 0x78) == 0) & ((sel & 0x07) != 0)
-    assert np.array_equal(got[~sub], ref[~sub])
-    if sub.any():
-        assert np.abs(got[sub] - ref[sub]).max() <= 2.0 ** -10
+    assert np.array_equal(got, ref)
+
+
+@pytest.mark.parametrize("Q", [1, 5, 70], ids=["decode", "qb", "prefill"])
+def test_indexer_subnormal_heavy_queries(Q):
+    """Query blocks full of subnormal E4M3 codes (beside normal ones up to
+    56) score exactly, through the block rescaling; a block that also holds
+    a magnitude above 56 keeps scale 1, and its subnormal products stay
+    within the 2^-10 per product that the score tolerance allows there."""
+    rng = np.random.default_rng(11)
+    H_I, d, N = 16, 128, 64
+    sub_codes = np.array([1, 2, 3, 4, 5, 6, 7, 0x81, 0x82, 0x85, 0x87], np.uint8)
+    qI = rng.choice(sub_codes, (1, Q, H_I, d)).astype(np.uint8)
+    qI[..., 5::9] = 0x66                        # 56 in some channels of blocks 0..3
+    qI[..., 1, 64:96] = rng.choice(sub_codes, 32)
+    qI[..., 1, 70] = 0x70                       # 256: block 2 of head 1 keeps scale 1
+    wI = rng.standard_normal((1, Q, H_I)).astype(np.float32)
+    ikey = rng.integers(0, 256, (1, N, d // 2), dtype=np.uint8)
+    iscale = rng.integers(120, 135, (1, N, d // 32), dtype=np.uint8)
+    planes = dict(nope=np.zeros((1, N, 256), np.uint8), nscale=np.full((1, N, 16), 127, np.uint8),
+                  rope=np.zeros((1, N, 64), np.uint16), ikey=ikey, iscale=iscale)
+    cache = _gpu_cache(planes, 1, N, 4, d, [N])
+    pos = torch.full((1, Q), 4 * N - 1, dtype=torch.int32, device=DEV)
+    # second set: head 1's large value lowered to 56, so every block is rescaled
+    qI2 = qI.copy()
+    qI2[..., 1, 70] = 0x66
+    for qq in (qI, qI2):
+        got = _np(csa.index_scores(cache, torch.from_numpy(qq).to(DEV), torch.from_numpy(wI).to(DEV), pos))[0]
+        for t in range(Q):
+            ref = O.index_scores(ikey[0], iscale[0], qq[0, t], wI[0, t], np.arange(N))
+            tol = index_score_tol(qq[0, t], wI[0, t], ikey[0], iscale[0], ref)
+            if qq is qI2:
+                # no block keeps scale 1: no subnormal term in the bound
+                kk = np.abs(O.mxfp4_decode(ikey[0], iscale[0]))
+                qa, wa = np.abs(O.e4m3_to_f64(qq[0, t])), np.abs(wI[0, t].astype(np.float64))
+                base = (1e-5 * ((kk @ qa.T) @ wa) + 2.0 ** -9 * ((kk[:, None, :] * qa[None]).max(axis=2) @ wa)
+                        + (d + H_I) * 2.0 ** -149 * wa.sum())
+                assert np.array_equal(tol, base)
+            assert np.all(np.abs(got[t].astype(np.float64) - ref) <= tol), f"query {t}"
 
 
 SCORE_CASES = [

@@ -245,6 +245,52 @@ def test_indexer_single_products(Q):
     assert np.array_equal(got, ref)
 
 
+INSTR_SUM_CASES = [
+    # (query codes, key scale byte range): normal codes only, spanning few or
+    # many binades, with and without blocks that keep scale 1 (a value > 56)
+    ("few-binades", "small", 120, 135),
+    ("many-binades-unit-keys", "wide", 127, 127),
+    ("many-binades-wide-keys", "wide", 100, 154),
+    ("scale1-blocks", "big", 120, 135),
+]
+
+
+@pytest.mark.parametrize("name,qkind,smin,smax", INSTR_SUM_CASES, ids=[c[0] for c in INSTR_SUM_CASES])
+def test_indexer_instruction_sum_bound(name, qkind, smin, smax):
+    """The property the indexer tolerance relies on: one head's dot product
+    of 128 E4M3 x E2M1 products (head weight 1, so the score is its ReLU)
+    comes out within 2^-9 of its largest product.  Measured worst cases are
+    near 2^-11.6 for codes spanning 2^-6..448 and far smaller for codes
+    spanning few binades; the figures are printed."""
+    rng = np.random.default_rng(5)
+    H_I, d, N = 16, 128, 256
+    normals = np.array([c for c in range(8, 0x67)] + [c | 0x80 for c in range(8, 0x67)], np.uint8)
+    if qkind == "small":
+        q = rng.choice(np.arange(8, 0x30, dtype=np.uint8), (H_I, d))
+    else:
+        q = rng.choice(normals, (H_I, d)).astype(np.uint8)
+        if qkind == "big":
+            q[:, 0::32] = 0x70
+    qI = q[None, None]
+    wI = np.zeros((1, 1, H_I), np.float32)
+    wI[..., 0] = 1.0
+    ikey = rng.integers(0, 256, (1, N, d // 2), dtype=np.uint8)
+    iscale = rng.integers(smin, smax + 1, (1, N, d // 32), dtype=np.uint8)
+    planes = dict(nope=np.zeros((1, N, 256), np.uint8), nscale=np.full((1, N, 16), 127, np.uint8),
+                  rope=np.zeros((1, N, 64), np.uint16), ikey=ikey, iscale=iscale)
+    cache = _gpu_cache(planes, 1, N, 4, d, [N])
+    pos = torch.full((1, 1), 4 * N - 1, dtype=torch.int32, device=DEV)
+    got = _np(csa.index_scores(cache, torch.from_numpy(qI).to(DEV), torch.from_numpy(wI).to(DEV), pos))[0, 0]
+    k = O.mxfp4_decode(ikey[0], iscale[0])
+    qv = O.e4m3_to_f64(q[0])
+    dots = k @ qv
+    big = np.abs(k * qv[None, :]).max(axis=1)
+    err = np.abs(got.astype(np.float64) - np.maximum(dots, 0.0))
+    worst = (err / big)[dots > 0].max()
+    print(f"{name}: worst |error| / largest product = {worst:.3e} (2^{np.log2(max(worst, 1e-30)):.1f})")
+    assert worst <= 2.0 ** -9
+
+
 @pytest.mark.parametrize("Q", [1, 5, 70], ids=["decode", "qb", "prefill"])
 def test_indexer_subnormal_heavy_queries(Q):
     """Query blocks full of subnormal E4M3 codes (beside normal ones up to

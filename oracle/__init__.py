@@ -42,6 +42,7 @@ from .csa import (  # noqa: F401
     visible_count,
     pool_block,
     compress,
+    compress_hidden,
     decode_entries,
     index_scores,
     topk_select,

@@ -94,8 +94,27 @@ def compress(x_u16, z_u16, bias_f32, w_ik_u16, m: int, d_nope: int = 512) -> dic
     absolute weighted terms, a bound on the size of the rounding error of any
     evaluation order), ``kI`` [N][d_idx] and ``kI_abs``.
     """
-    x = bf16_to_f64(x_u16)
-    z = bf16_to_f64(z_u16)
+    return _compress_rows(bf16_to_f64(x_u16), bf16_to_f64(z_u16), bias_f32, w_ik_u16, m, d_nope)
+
+
+def compress_hidden(h_u16, w_kv_u16, w_z_u16, bias_f32, w_ik_u16, m: int, d_nope: int = 512) -> dict:
+    """Compressor fed from hidden states ([V4.1] "アーキテクチャ", CED
+    paragraph, eq. 1: a decoder layer's KV entries C^l, Z^l are projected
+    from the encoder's last hidden state H^{L/2} by W^KV_l, W^Z_l).
+
+    h_u16 bf16 bits [T][d_model]; w_kv_u16 bf16 bits [d_model][D]; w_z_u16
+    bf16 bits [d_model][G] (G = D or 1).  The raw rows are x = H W^KV and the
+    gate logits z = H W^Z, exact products summed in float64 and used at that
+    precision (they are never rounded to a stream format: the projection
+    feeds the pooling directly); everything after is ``compress``.  Returns
+    ``compress``'s dict.
+    """
+    h = bf16_to_f64(h_u16)
+    return _compress_rows(h @ bf16_to_f64(w_kv_u16), h @ bf16_to_f64(w_z_u16), bias_f32, w_ik_u16, m, d_nope)
+
+
+def _compress_rows(x, z, bias_f32, w_ik_u16, m: int, d_nope: int) -> dict:
+    """The compressor on float64 raw rows x [T][D] and gate logits z [T][G]."""
     bias = np.asarray(bias_f32, dtype=np.float32).astype(np.float64)
     T, D = x.shape
     if T % m:

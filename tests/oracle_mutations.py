@@ -55,6 +55,8 @@ muts = [
  ("csa.py", "lo + np.arange(win.shape[0], dtype=np.int64)])", "lo + 1 + np.arange(win.shape[0], dtype=np.int64)])"),
  ("csa.py", "out[:, -d_rope:] = bf16_to_f64(f32_to_bf16(rot.astype(np.float32)))", "out[:, -d_rope:] = rot"),
  ("csa.py", "q = _rotated_bf16(q, int(rope[\"p\"]), rope[\"base\"], dr)", "q = _rotated_bf16(q, 0, rope[\"base\"], dr)"),
+ ("csa.py", "return _compress_rows(h @ bf16_to_f64(w_kv_u16), h @ bf16_to_f64(w_z_u16),", "return _compress_rows(h @ bf16_to_f64(w_z_u16)[:, :1] + h @ bf16_to_f64(w_kv_u16), h @ bf16_to_f64(w_z_u16),"),
+ ("csa.py", "return _compress_rows(h @ bf16_to_f64(w_kv_u16), h @ bf16_to_f64(w_z_u16),", "return _compress_rows(h @ bf16_to_f64(w_kv_u16), h @ bf16_to_f64(w_kv_u16)[:, :bf16_to_f64(w_z_u16).shape[1]],"),
 ]
 missed = 0
 root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))

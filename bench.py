@@ -31,6 +31,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 ROPE_BASE = 10000.0  # rotary base of the fused-epilogue leg (the original rotary embedding's)
+HIDDEN_D_MODEL = 4096  # hidden size of the compress-from-hidden-states leg (a stand-in)
 METRIC = "CSA decode query-tokens/s + achieved HBM GB/s at 128K ctx (1 MI355X)"
 HBM_PEAK_GBPS = 8000.0
 FP8_PEAK_TFLOPS = 5000.0
@@ -451,7 +452,7 @@ def prefill_leg(reps, oracle=True):
     import torch
 
     import compressed_sparse_attention_compressor_amd as csa
-    from synth.workloads import PREFILL as w, params, queries, raw_rows
+    from synth.workloads import PREFILL as w, hidden_inputs, params, queries, raw_rows
 
     dev = "cuda"
     t_start = time.time()
@@ -506,7 +507,33 @@ def prefill_leg(reps, oracle=True):
             "indexer_mfma": {"achieved": round(tflops, 2), "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
                              "frac": round(tflops / FP8_PEAK_TFLOPS, 4), "useful_flops": flops,
                              "note": "causal useful work only; E4M3 x E2M1 scaled MFMA issues at the FP8 rate"}}
-    del scores, out, cache, x, z
+    del scores, out, x, z
+    torch.cuda.empty_cache()
+    # The same chunk's compressor fed from hidden states (x = h W^KV and
+    # z = h W^Z formed and pooled inside csa_compress_hidden), d_model a
+    # stand-in: the pages give no hidden size.
+    h, wkv, wz = hidden_inputs(w, HIDDEN_D_MODEL, device=dev)
+    hws = torch.empty(max(16, csa.lib().csa_compress_hidden_ws_bytes(w.B, w.T, w.m, 1)), dtype=torch.uint8,
+                      device=dev)
+    csa.compress_hidden(cache, h, wkv, wz, bias, wik, ws=hws)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        csa.compress_hidden(cache, h, wkv, wz, bias, wik, ws=hws)
+    b.record()
+    torch.cuda.synchronize()
+    hms = a.elapsed_time(b) / reps
+    hflops = 2.0 * w.B * w.T * HIDDEN_D_MODEL * (576 + 576)
+    htf = hflops / (hms * 1e-3) / 1e12
+    log(f"[bench] prefill compress from hidden states (d_model {HIDDEN_D_MODEL}): {hms:.3f} ms, {htf:.1f} TFLOP/s")
+    res["compress_hidden"] = {"d_model": HIDDEN_D_MODEL, "G": 576, "ms": round(hms, 4),
+                              "projection_flops": hflops,
+                              "mfma": {"achieved": round(htf, 2), "peak": 2500.0, "unit": "TFLOP/s",
+                                       "frac": round(htf / 2500.0, 4)},
+                              "note": "x = h W^KV, z = h W^Z (bf16 MFMA, fp32 sums) pooled on chip; d_model is a "
+                                      "stand-in, the pages give no hidden size"}
+    del h, wkv, wz, hws, cache
     torch.cuda.empty_cache()
     if oracle:
         res["cpu_oracle"] = prefill_oracle(w)

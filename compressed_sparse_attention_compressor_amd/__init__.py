@@ -11,6 +11,7 @@ from .ops import (  # noqa: F401
     D_ROPE,
     Cache,
     compress,
+    compress_hidden,
     compress_index_scores,
     compress_index_topk,
     hca_dense_attn,

@@ -98,6 +98,9 @@ _SIGS = {
                                   c_void_p, c_size_t, c_void_p]),
     "csa_workspace_bytes": (c_size_t, [c_int, c_int, c_int, c_int, c_int, c_int]),
     "csa_status_str": (ctypes.c_char_p, [c_int]),
+    "csa_compress_hidden": (c_int, [c_void_p, c_int64, c_int, c_void_p, c_void_p, c_int, c_void_p, c_void_p, c_int64,
+                                    c_int64, ctypes.POINTER(CacheT), c_void_p, c_size_t, c_void_p]),
+    "csa_compress_hidden_ws_bytes": (c_size_t, [c_int, c_int64, c_int, c_int]),
     "csa_version": (c_int, []),
     "csa_last_hip_error": (c_int, []),
     "csa_read_device_flags": (c_int, [c_void_p, ctypes.POINTER(ctypes.c_uint32)]),

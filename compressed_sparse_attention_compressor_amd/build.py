@@ -29,7 +29,7 @@ FLAGS = [
     "-Wno-unused-result",
     "-I" + os.path.join(ROOT, "include"),
 ]
-SOURCES = ["abi.hip", "compress.hip", "index.hip", "topk.hip", "pool.hip", "swa.hip", "attn.hip"]
+SOURCES = ["abi.hip", "compress.hip", "compress_hidden.hip", "index.hip", "topk.hip", "pool.hip", "swa.hip", "attn.hip"]
 # The indexer folds every MFMA result through ReLU and the head weights on
 # the vector unit: results written to AGPRs would each need a copy first.
 # Attention has no NaN inputs or intermediates by construction (masked logits

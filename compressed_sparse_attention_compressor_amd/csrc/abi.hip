@@ -256,6 +256,42 @@ int csa_compress(const uint16_t *x, int64_t x_stride_b, const uint16_t *z, int64
                                         (int)(T / cache->m), v, stream));
 }
 
+static int check_hidden_args(const uint16_t *h, int64_t h_stride_b, int d_model, const uint16_t *w_kv,
+                             const uint16_t *w_z, int G, const float *pos_bias, const uint16_t *w_ik, int64_t tok_begin,
+                             int64_t T, const csa_cache_t *cache) {
+  int st = check_cache(cache, w_ik != nullptr);
+  if (st) return st;
+  if (!h || !w_kv || !w_z || !pos_bias) return CSA_ERR_NULL;
+  if (G != 1 && G != csa::kD) return CSA_ERR_UNSUPPORTED;
+  if (d_model < 32 || d_model > 16384 || d_model % 32) return CSA_ERR_UNSUPPORTED;
+  if (T < 0 || tok_begin < 0) return CSA_ERR_SHAPE;
+  if (tok_begin % cache->m || T % cache->m) return CSA_ERR_SHAPE;
+  if ((tok_begin + T) / cache->m > cache->N_cap) return CSA_ERR_SHAPE;
+  if (cache->B > 1 && h_stride_b < T * d_model) return CSA_ERR_SHAPE;
+  if (!aligned16(h) || !aligned16(w_kv) || !aligned16(w_z) || (h_stride_b % 8)) return CSA_ERR_ALIGN;
+  return CSA_OK;
+}
+
+size_t csa_compress_hidden_ws_bytes(int B, int64_t T, int m, int with_ikey) {
+  if (B < 0 || T < 0 || m < 1) return 0;
+  return csa::compress_hidden_ws_bytes(B, (int)(T / m), with_ikey != 0);
+}
+
+int csa_compress_hidden(const uint16_t *h, int64_t h_stride_b, int d_model, const uint16_t *w_kv,
+                        const uint16_t *w_z, int G, const float *pos_bias, const uint16_t *w_ik, int64_t tok_begin,
+                        int64_t T, const csa_cache_t *cache, void *ws, size_t ws_bytes, hipStream_t stream) {
+  int st = check_hidden_args(h, h_stride_b, d_model, w_kv, w_z, G, pos_bias, w_ik, tok_begin, T, cache);
+  if (st) return st;
+  if (T == 0 || cache->B == 0) return CSA_OK;
+  const size_t need = csa::compress_hidden_ws_bytes(cache->B, (int)(T / cache->m), w_ik != nullptr);
+  if (need > 0 && !ws) return CSA_ERR_NULL;
+  if (ws_bytes < need) return CSA_ERR_WORKSPACE;
+  if (need > 0 && !aligned16(ws)) return CSA_ERR_ALIGN;
+  const csa::CacheView v = view_of(cache);
+  return status_of(csa::launch_compress_hidden(h, h_stride_b, d_model, w_kv, w_z, G, pos_bias, w_ik,
+                                               tok_begin / cache->m, (int)(T / cache->m), v, ws, stream));
+}
+
 static int check_index_args(const csa_cache_t *cache, const uint8_t *q_idx, const float *w_idx, int H_I,
                             const int32_t *q_pos, int Q, const int32_t *cand, int C) {
   int st = check_cache(cache, true);

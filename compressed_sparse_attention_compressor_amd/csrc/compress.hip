@@ -23,12 +23,15 @@ constexpr int kEPB = 16;
 constexpr int kCompThreads = 256;
 constexpr int kSmallM = 8;   // blocks up to this many rows are pooled from registers
 
-template <bool kGateFull>
+// kPooled: the pooled fp32 rows come from `pooled` ([B][n_chunk][576], the
+// hidden-state compressor's output) and only the indexer key is made.
+template <bool kGateFull, bool kPooled = false>
 __global__ __launch_bounds__(kCompThreads) void compress_kernel(
     const uint16_t *__restrict__ x, int64_t x_stride_b, const uint16_t *__restrict__ z, int64_t z_stride_b,
     const float *__restrict__ bias, const uint16_t *__restrict__ w_ik, int m, int n_chunk, int64_t entry0,
     uint8_t *__restrict__ nope, uint8_t *__restrict__ nscale, uint16_t *__restrict__ rope,
-    uint8_t *__restrict__ ikey, uint8_t *__restrict__ iscale, int N_cap, int d_idx) {
+    uint8_t *__restrict__ ikey, uint8_t *__restrict__ iscale, int N_cap, int d_idx,
+    const float *__restrict__ pooled = nullptr) {
   __shared__ float cs[kEPB][kD];
   __shared__ float ks[kEPB][32];
   __shared__ float kpart[kCompThreads / 32][kEPB][32];
@@ -54,8 +57,15 @@ __global__ __launch_bounds__(kCompThreads) void compress_kernel(
     for (int u = 0; u < kSlice; ++u) wr[u] = wp[(int64_t)u * d_idx];
   }
 
+  if (kPooled) {
+    for (int t = tid; t < ne * (kD / 4); t += kCompThreads) {
+      const int e = t / (kD / 4), c = (t % (kD / 4)) * 4;
+      *reinterpret_cast<float4 *>(&cs[e][c]) =
+          *reinterpret_cast<const float4 *>(pooled + ((int64_t)b * n_chunk + j0 + e) * kD + c);
+    }
+  }
   // 1. pooling
-  for (int t = tid; t < ne * (kD / 4); t += kCompThreads) {
+  for (int t = tid; t < (kPooled ? 0 : ne * (kD / 4)); t += kCompThreads) {
     const int e = t / (kD / 4);
     const int c = (t % (kD / 4)) * 4;
     const int64_t row0 = (int64_t)(j0 + e) * m;
@@ -153,14 +163,14 @@ __global__ __launch_bounds__(kCompThreads) void compress_kernel(
   __syncthreads();
 
   // 2. MXFP4 main entry (bytes 0..255) and bf16 rope channels (workgroup z = 0)
-  for (int e = 0; e < (blockIdx.z == 0 ? ne : 0); ++e) {
+  for (int e = 0; e < (blockIdx.z == 0 && !kPooled ? ne : 0); ++e) {
     const int64_t row = (int64_t)b * N_cap + entry0 + j0 + e;
     uint32_t sb;
     const uint32_t byte = encode_pair(cs[e][2 * tid], cs[e][2 * tid + 1], sb);
     nope[row * kNopeBytes + tid] = (uint8_t)byte;
     if ((tid & 15) == 0) nscale[row * kNopeScales + (tid >> 4)] = (uint8_t)sb;
   }
-  for (int t = tid; t < (blockIdx.z == 0 ? ne * kDRope : 0); t += kCompThreads) {
+  for (int t = tid; t < (blockIdx.z == 0 && !kPooled ? ne * kDRope : 0); t += kCompThreads) {
     const int e = t / kDRope, c = t % kDRope;
     const int64_t row = (int64_t)b * N_cap + entry0 + j0 + e;
     rope[row * kDRope + c] = (uint16_t)f32_to_bf16(cs[e][kDNope + c]);
@@ -365,6 +375,20 @@ hipError_t launch_compress(const uint16_t *x, int64_t x_stride_b, const uint16_t
     compress_kernel<false><<<grid, kCompThreads, 0, stream>>>(x, x_stride_b, z, z_stride_b, bias, w_ik, c.m, n_chunk,
                                                               entry0, c.nope, c.nscale, c.rope, c.ikey, c.iscale,
                                                               c.N_cap, c.d_idx);
+  return hipGetLastError();
+}
+
+// The indexer keys of entries whose pooled fp32 rows are already made
+// (the hidden-state compressor): stage 3 of compress_kernel alone.
+hipError_t launch_ikey_from_pooled(const float *pooled, const uint16_t *w_ik, int64_t entry0, int n_chunk,
+                                   const CacheView &c, hipStream_t stream) {
+  const int groups = (n_chunk + kEPB - 1) / kEPB;
+  const int nkb = c.d_idx / 32;
+  const int zsplit = (int64_t)groups * c.B < 1024 ? nkb : 1;
+  dim3 grid(groups, c.B, zsplit);
+  compress_kernel<true, true><<<grid, kCompThreads, 0, stream>>>(nullptr, 0, nullptr, 0, nullptr, w_ik, c.m, n_chunk,
+                                                                  entry0, c.nope, c.nscale, c.rope, c.ikey, c.iscale,
+                                                                  c.N_cap, c.d_idx, pooled);
   return hipGetLastError();
 }
 

@@ -1,0 +1,282 @@
+// Compressor fed from hidden states ([V4.1] "アーキテクチャ", CED paragraph,
+// eq. 1: a decoder layer's KV entries are projected from the encoder's last
+// hidden state, C = H W^KV and Z = H W^Z), fused: the projections never
+// leave the chip.  Then the softmax-gated pooling of [V4] "ハイブリッド注意：
+// CSAとHCA" (CSA paragraph, Fig. 3), the MXFP4 main entry and the bf16
+// positional channels.
+//
+// One workgroup (4 waves) per (E consecutive entries, 64 channels,
+// sequence), E = 64/m entries of up to 64 tokens for m <= 64, one entry for
+// longer blocks (its tokens in sub-tiles of 64).  Per sub-tile of 64 tokens:
+//   1. x and z for 64 tokens x 64 channels on v_mfma_f32_16x16x32_bf16
+//      (fp32 accumulation of exact bf16 products), wave w owning tokens
+//      16w..16w+15; the H and W tiles of 32 k go through double-buffered LDS,
+//      the next step's global loads in flight during the MFMAs.  W is stored
+//      k-major as it is in memory and read transposed with
+//      ds_read_b64_tr_b16; both operands take the product's k in the order
+//      that read produces (MFMA k 8g + 4h + e is tile k 16h + 4g + e).
+//      One gate logit per token (G = 1) needs one extra MFMA per step: its
+//      B operand repeats W^Z in every column.
+//   2. x and z go through LDS to the pooling threads: per (entry, channel)
+//      a maximum over the block's logits plus bias, then exp-weighted sums
+//      (the stream compressor's arithmetic); blocks longer than a sub-tile
+//      keep a running (max, sum, weighted sum) per quarter of the tokens,
+//      combined at the end.
+//   3. the pooled fp32 values are encoded (MXFP4 blocks of 32 channels, or
+//      bf16 for the positional channels) and, when an indexer key follows,
+//      written to the workspace for that projection (compress.hip).
+#include "csa_device.hpp"
+#include "csa_internal.hpp"
+
+namespace csa {
+
+constexpr int kHTok = 64;            // tokens per sub-tile
+constexpr int kHCh = 64;             // channels per workgroup
+constexpr int kHK = 32;              // k per step
+constexpr int kHThreads = 256;
+constexpr int kHRowH = kHK + 8;      // H tile row (bf16): 80 bytes
+constexpr int kHRowW = kHCh + 16;    // W tile row (bf16): 160 bytes, as the attention key tile's 8-dword skew
+
+struct HiddenArgs {
+  const uint16_t *h;       // bf16 [B][*][d_model], row stride d_model, sequence stride h_stride_b
+  int64_t h_stride_b;
+  int d_model;
+  const uint16_t *w_kv;    // bf16 [d_model][576]
+  const uint16_t *w_z;     // bf16 [d_model][G]
+  const float *bias;       // [m]
+  int m;
+  int n_ent;               // entries written by the call
+  int64_t entry0;          // first of them (token 0 of h is its first token)
+  int E;                   // entries per workgroup
+  uint8_t *nope;
+  uint8_t *nscale;
+  uint16_t *rope;
+  int N_cap;
+  float *pooled;           // fp32 [B][n_ent][576] or null
+};
+
+template <bool kGateFull>
+__global__ __launch_bounds__(kHThreads) void compress_hidden_kernel(HiddenArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t Hs[2][kHTok * kHRowH];
+  __shared__ __attribute__((aligned(16))) uint16_t Wx[2][kHK * kHRowW];
+  __shared__ __attribute__((aligned(16))) uint16_t Wz[2][kGateFull ? kHK * kHRowW : kHK];
+  __shared__ float xs[kHTok][kHCh + 1];
+  __shared__ float zs[kHTok][kGateFull ? kHCh + 1 : 1];
+  __shared__ float cs[kHTok][kHCh];          // pooled rows (E <= 64); the long-block combine reuses it
+
+  const int b = blockIdx.z;
+  const int c0 = blockIdx.y * kHCh;
+  const int e0 = blockIdx.x * a.E;
+  const int ne = min(a.E, a.n_ent - e0);
+  const int ntok = ne * a.m;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 4, r = lane & 15;
+  const uint16_t *hb = a.h + (int64_t)b * a.h_stride_b + (int64_t)e0 * a.m * a.d_model;
+  const int nk = a.d_model / kHK;
+  const bool lng = a.m > kHTok;  // one entry, several sub-tiles
+
+  // Staging of one k-step: H 64 tokens x 32 k (16 bytes per thread), W^KV
+  // 32 k x 64 channels (16 bytes per thread), W^Z likewise or its 32 values.
+  const int ht = tid >> 2, hk = (tid & 3) * 8;    // H: token, k offset
+  const int wk = tid >> 3, wc = (tid & 7) * 8;    // W: k row, channel offset
+  auto load_step = [&](int st, int ks, uint4 &vh, uint4 &vx, uint4 &vz) __attribute__((always_inline)) {
+    const int tok = st + ht;
+    const uint16_t *hp = hb + (int64_t)min(tok, ntok - 1) * a.d_model + ks * kHK + hk;
+    vh = *reinterpret_cast<const uint4 *>(hp);
+    if (tok >= ntok) vh = uint4{0u, 0u, 0u, 0u};
+    const int64_t kr = (int64_t)ks * kHK + wk;
+    vx = *reinterpret_cast<const uint4 *>(a.w_kv + kr * kD + c0 + wc);
+    if (kGateFull) vz = *reinterpret_cast<const uint4 *>(a.w_z + kr * kD + c0 + wc);
+    else vz = *reinterpret_cast<const uint4 *>(a.w_z + (int64_t)ks * kHK + min(tid, 3) * 8);
+  };
+  auto store_step = [&](int buf, const uint4 &vh, const uint4 &vx, const uint4 &vz) __attribute__((always_inline)) {
+    *reinterpret_cast<uint4 *>(&Hs[buf][ht * kHRowH + hk]) = vh;
+    *reinterpret_cast<uint4 *>(&Wx[buf][wk * kHRowW + wc]) = vx;
+    if (kGateFull) *reinterpret_cast<uint4 *>(&Wz[buf][wk * kHRowW + wc]) = vz;
+    else if (tid < 4) *reinterpret_cast<uint4 *>(&Wz[buf][tid * 8]) = vz;
+  };
+
+  // long blocks: running (max, sum, weighted sum) of channel tid % 64 over
+  // token quarter tid / 64 of every sub-tile
+  float lmx = -INFINITY, lden = 0.f, lnum = 0.f;
+
+  for (int st = 0; st < ntok; st += kHTok) {
+    v4f X[kHCh / 16], Z[kGateFull ? kHCh / 16 : 1];
+#pragma unroll
+    for (int j = 0; j < kHCh / 16; ++j) X[j] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < (kGateFull ? kHCh / 16 : 1); ++j) Z[j] = v4f{0.f, 0.f, 0.f, 0.f};
+
+    uint4 vh, vx, vz;
+    load_step(st, 0, vh, vx, vz);
+    store_step(0, vh, vx, vz);
+    for (int ks = 0; ks < nk; ++ks) {
+      const int buf = ks & 1;
+      lds_barrier();  // step ks staged; every wave is done with step ks - 1's buffer
+      if (ks + 1 < nk) load_step(st, ks + 1, vh, vx, vz);
+      // A: token 16 wave + r, k {4g..4g+3, 16+4g..16+4g+3}
+      const uint16_t *hr = &Hs[buf][(16 * wave + r) * kHRowH + 4 * g];
+      const uint2 a0 = *reinterpret_cast<const uint2 *>(hr), a1 = *reinterpret_cast<const uint2 *>(hr + 16);
+      const v8bf A = __builtin_bit_cast(v8bf, uint4{a0.x, a0.y, a1.x, a1.y});
+      typedef __attribute__((address_space(3))) v4s lds_v4s;
+      const uint16_t *wb = &Wx[buf][(4 * g + (r >> 2)) * kHRowW + 4 * (r & 3)];
+#pragma unroll
+      for (int j = 0; j < kHCh / 16; ++j) {
+        const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s *)(wb + 16 * j));
+        const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s *)(wb + 16 * kHRowW + 16 * j));
+        const v8bf Bx = __builtin_bit_cast(v8bf, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        X[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, Bx, X[j], 0, 0, 0);
+      }
+      if (kGateFull) {
+        const uint16_t *zb = &Wz[buf][(4 * g + (r >> 2)) * kHRowW + 4 * (r & 3)];
+#pragma unroll
+        for (int j = 0; j < kHCh / 16; ++j) {
+          const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s *)(zb + 16 * j));
+          const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s *)(zb + 16 * kHRowW + 16 * j));
+          const v8bf Bz = __builtin_bit_cast(v8bf, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+          Z[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, Bz, Z[j], 0, 0, 0);
+        }
+      } else {
+        // W^Z in every column: lane (g, r) takes k {4g..4g+3, 16+4g..16+4g+3}
+        const uint2 z0 = *reinterpret_cast<const uint2 *>(&Wz[buf][4 * g]);
+        const uint2 z1 = *reinterpret_cast<const uint2 *>(&Wz[buf][16 + 4 * g]);
+        const v8bf Bz = __builtin_bit_cast(v8bf, uint4{z0.x, z0.y, z1.x, z1.y});
+        Z[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, Bz, Z[0], 0, 0, 0);
+      }
+      if (ks + 1 < nk) store_step(buf ^ 1, vh, vx, vz);
+    }
+
+    // x and z of this sub-tile to LDS: lane (g, r) holds tokens
+    // 16 wave + 4g + i, channel 16j + r
+#pragma unroll
+    for (int j = 0; j < kHCh / 16; ++j)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        xs[16 * wave + 4 * g + i][16 * j + r] = X[j][i];
+        if (kGateFull) zs[16 * wave + 4 * g + i][16 * j + r] = Z[j][i];
+        else if (j == 0 && r == 0) zs[16 * wave + 4 * g + i][0] = Z[0][i];
+      }
+    __syncthreads();
+
+    if (!lng) {
+      // every block of the workgroup lies in this one sub-tile
+      for (int p = tid; p < ne * kHCh; p += kHThreads) {
+        const int e = p / kHCh, c = p % kHCh;
+        const int t0 = e * a.m;
+        float mx = -INFINITY;
+        for (int i = 0; i < a.m; ++i) mx = fmaxf(mx, zs[t0 + i][kGateFull ? c : 0] + a.bias[i]);
+        float den = 0.f, num = 0.f;
+        for (int i = 0; i < a.m; ++i) {
+          const float w = expf(zs[t0 + i][kGateFull ? c : 0] + a.bias[i] - mx);
+          den += w;
+          num = fmaf(w, xs[t0 + i][c], num);
+        }
+        cs[e][c] = num / den;
+      }
+    } else {
+      const int c = tid % kHCh, q4 = tid / kHCh;
+      const int i1 = min(kHTok, ntok - st);
+      for (int i = q4 * (kHTok / 4); i < min(i1, (q4 + 1) * (kHTok / 4)); ++i) {
+        const float v = zs[i][kGateFull ? c : 0] + a.bias[st + i];
+        if (v > lmx) {
+          const float s = expf(lmx - v);  // 0 on the first token
+          lden *= s;
+          lnum *= s;
+          lmx = v;
+        }
+        const float w = expf(v - lmx);
+        lden += w;
+        lnum = fmaf(w, xs[i][c], lnum);
+      }
+    }
+    __syncthreads();  // xs / zs are rewritten by the next sub-tile
+  }
+
+  if (lng) {
+    // the four token quarters of each channel, combined in quarter order
+    float *part = &cs[0][0];  // [3][4][64]: max, sum, weighted sum
+    part[(0 * 4 + tid / kHCh) * kHCh + tid % kHCh] = lmx;
+    part[(1 * 4 + tid / kHCh) * kHCh + tid % kHCh] = lden;
+    part[(2 * 4 + tid / kHCh) * kHCh + tid % kHCh] = lnum;
+    __syncthreads();
+    float res = 0.f;
+    if (tid < kHCh) {
+      float M = -INFINITY;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) M = fmaxf(M, part[(0 * 4 + q) * kHCh + tid]);
+      float den = 0.f, num = 0.f;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float mq = part[(0 * 4 + q) * kHCh + tid];
+        const float s = mq == -INFINITY ? 0.f : expf(mq - M);
+        den = fmaf(part[(1 * 4 + q) * kHCh + tid], s, den);
+        num = fmaf(part[(2 * 4 + q) * kHCh + tid], s, num);
+      }
+      res = num / den;
+    }
+    __syncthreads();
+    if (tid < kHCh) cs[0][tid] = res;
+    __syncthreads();
+  } else {
+    __syncthreads();
+  }
+
+  // 3. encoding: MXFP4 blocks 2y, 2y + 1 of the main entry, or the bf16
+  //    positional channels; 16 lanes per 32-channel block
+  for (int t = tid; t < (c0 < kDNope ? ne * 32 : 0); t += kHThreads) {
+    const int e = t >> 5, half = (t >> 4) & 1, l = t & 15;
+    uint32_t sb;
+    const uint32_t byte = encode_pair(cs[e][32 * half + 2 * l], cs[e][32 * half + 2 * l + 1], sb);
+    const int64_t row = (int64_t)b * a.N_cap + a.entry0 + e0 + e;
+    const int kb = c0 / 32 + half;
+    a.nope[row * kNopeBytes + kb * 16 + l] = (uint8_t)byte;
+    if (l == 0) a.nscale[row * kNopeScales + kb] = (uint8_t)sb;
+  }
+  for (int t = tid; t < (c0 >= kDNope ? ne * kHCh : 0); t += kHThreads) {
+    const int e = t / kHCh, c = t % kHCh;
+    const int64_t row = (int64_t)b * a.N_cap + a.entry0 + e0 + e;
+    a.rope[row * kDRope + c] = (uint16_t)f32_to_bf16(cs[e][c]);
+  }
+  if (a.pooled)
+    for (int t = tid; t < ne * kHCh; t += kHThreads) {
+      const int e = t / kHCh, c = t % kHCh;
+      a.pooled[((int64_t)b * a.n_ent + e0 + e) * kD + c0 + c] = cs[e][c];
+    }
+}
+
+size_t compress_hidden_ws_bytes(int B, int n_ent, bool has_ik) {
+  return has_ik ? (size_t)B * n_ent * kD * sizeof(float) : 0;
+}
+
+hipError_t launch_compress_hidden(const uint16_t *h, int64_t h_stride_b, int d_model, const uint16_t *w_kv,
+                                  const uint16_t *w_z, int G, const float *bias, const uint16_t *w_ik,
+                                  int64_t entry0, int n_ent, const CacheView &c, void *ws, hipStream_t stream) {
+  if (n_ent <= 0 || c.B <= 0) return hipSuccess;
+  HiddenArgs a;
+  a.h = h;
+  a.h_stride_b = h_stride_b;
+  a.d_model = d_model;
+  a.w_kv = w_kv;
+  a.w_z = w_z;
+  a.bias = bias;
+  a.m = c.m;
+  a.n_ent = n_ent;
+  a.entry0 = entry0;
+  a.E = c.m <= kHTok ? kHTok / c.m : 1;
+  a.nope = c.nope;
+  a.nscale = c.nscale;
+  a.rope = c.rope;
+  a.N_cap = c.N_cap;
+  a.pooled = w_ik ? reinterpret_cast<float *>(ws) : nullptr;
+  const dim3 grid((unsigned)((n_ent + a.E - 1) / a.E), kD / kHCh, c.B);
+  if (G == kD)
+    compress_hidden_kernel<true><<<grid, kHThreads, 0, stream>>>(a);
+  else
+    compress_hidden_kernel<false><<<grid, kHThreads, 0, stream>>>(a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || !w_ik) return e;
+  return launch_ikey_from_pooled(a.pooled, w_ik, entry0, n_ent, c, stream);
+}
+
+}  // namespace csa

@@ -94,6 +94,16 @@ struct AttnShape {
 AttnShape attn_shape(int B, int Q, int n_main, int n_win);
 size_t attn_workspace_bytes(int B, int Q, int H, int n_main, int n_win);
 
+// Hidden-state compressor (compress_hidden.hip): H W^KV and H W^Z pooled
+// without leaving the chip; with w_ik the pooled rows pass through `ws`
+// (compress_hidden_ws_bytes) to the indexer-key projection.
+size_t compress_hidden_ws_bytes(int B, int n_ent, bool has_ik);
+hipError_t launch_compress_hidden(const uint16_t *h, int64_t h_stride_b, int d_model, const uint16_t *w_kv,
+                                  const uint16_t *w_z, int G, const float *bias, const uint16_t *w_ik,
+                                  int64_t entry0, int n_ent, const CacheView &c, void *ws, hipStream_t stream);
+hipError_t launch_ikey_from_pooled(const float *pooled, const uint16_t *w_ik, int64_t entry0, int n_chunk,
+                                   const CacheView &c, hipStream_t stream);
+
 hipError_t launch_attention(const CacheView &c, const uint16_t *q, int H, const int32_t *q_pos, int Q,
                             const int32_t *idx, int k, bool dense, const uint16_t *swa, const SwaPlanes *swa8,
                             const int32_t *swa_pos0, int S, int n_win, float scale, double rope_base,

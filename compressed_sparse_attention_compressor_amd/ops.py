@@ -91,6 +91,26 @@ def compress(cache: Cache, x, z, pos_bias, w_ik=None, tok_begin=0):
                              int(tok_begin), int(T), ctypes.byref(cs), _stream()), "csa_compress")
 
 
+def compress_hidden(cache: Cache, h, w_kv, w_z, pos_bias, w_ik=None, tok_begin=0, ws=None):
+    """Compressor fed from hidden states: h bf16 [B][T][d_model], w_kv bf16
+    [d_model][576], w_z bf16 [d_model][G] (G = 576 or 1), pos_bias fp32 [m];
+    x = h w_kv and z = h w_z are pooled on the GPU without being written out.
+    Writes entries tok_begin/m .. (tok_begin+T)/m - 1 (csa_compress_hidden)."""
+    for t, n in ((h, "h"), (w_kv, "w_kv"), (w_z, "w_z")):
+        _need(t, torch.bfloat16, n)
+    if h.stride(2) != 1 or h.stride(1) != h.shape[2]:
+        raise ValueError("h rows must be contiguous")
+    B, T, d_model = h.shape
+    G = w_z.shape[1]
+    need = lib().csa_compress_hidden_ws_bytes(B, T, cache.m, int(w_ik is not None))
+    ws, wsb = _workspace(need, ws, h.device)
+    cs = cache.struct()
+    check(lib().csa_compress_hidden(_ptr(h), h.stride(0), d_model, _ptr(w_kv), _ptr(w_z), G, _ptr(pos_bias),
+                                    _ptr(w_ik), int(tok_begin), T, ctypes.byref(cs), _ptr(ws), wsb, _stream()),
+          "csa_compress_hidden")
+    return ws
+
+
 def compress_index_scores(cache: Cache, x, z, pos_bias, w_ik, tok_begin, q_idx, w_idx, q_pos, scores=None):
     """compress() then a full-scan index_scores() (one launch for a one-entry decode append)."""
     _need(x, torch.bfloat16, "x")

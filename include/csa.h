@@ -103,6 +103,28 @@ int csa_compress(const uint16_t *x, int64_t x_stride_b, const uint16_t *z, int64
                  const float *pos_bias, const uint16_t *w_ik, int64_t tok_begin, int64_t T,
                  const csa_cache_t *cache, hipStream_t stream);
 
+/* The compressor fed from hidden states ([V4.1] "アーキテクチャ", CED
+ * paragraph, eq. 1: a decoder layer's KV entries C^l, Z^l are projected
+ * from the encoder's last hidden state by W^KV_l, W^Z_l), fused: the raw
+ * rows x = H W^KV and the gate logits z = H W^Z are formed on the GPU's
+ * matrix cores (fp32 sums of exact bf16 products) and pooled without being
+ * written out; everything after is csa_compress (same planes, same
+ * pooling, same quantisation).
+ *   h        bf16 [B][*][d_model] hidden states, row stride d_model,
+ *            sequence stride h_stride_b (>= T*d_model when B > 1, a
+ *            multiple of 8); h row 0 of each sequence is token tok_begin
+ *   d_model  a multiple of 32 in [32, 16384]
+ *   w_kv     bf16 [d_model][576]     w_z  bf16 [d_model][G], G = 576 or 1
+ *   pos_bias, w_ik, tok_begin, T, cache: as in csa_compress
+ *   ws       >= csa_compress_hidden_ws_bytes(B, T, m, w_ik != NULL) bytes,
+ *            16-byte aligned (the pooled fp32 rows, on their way to the
+ *            indexer-key projection); NULL when that is 0.
+ * h, w_kv, w_z 16-byte aligned.  n_entries is not modified. */
+int csa_compress_hidden(const uint16_t *h, int64_t h_stride_b, int d_model, const uint16_t *w_kv,
+                        const uint16_t *w_z, int G, const float *pos_bias, const uint16_t *w_ik, int64_t tok_begin,
+                        int64_t T, const csa_cache_t *cache, void *ws, size_t ws_bytes, hipStream_t stream);
+size_t csa_compress_hidden_ws_bytes(int B, int64_t T, int m, int with_ikey);
+
 /* Lightning indexer + per-query top-k ([V4] CSA paragraph: FP4,
  * ReLU-scored multi-head dot product; top-k compressed blocks per query.
  * [V4.1] Fig. 4, Reindex mode: with `cand`, only an earlier layer's

@@ -49,6 +49,9 @@ class TensorId(enum.IntEnum):
     ROPE = 18
     IKEY = 19
     ISCALE = 20
+    HID = 21       # hidden states feeding the projections, bf16 [B][T][d_model]
+    W_KV = 22      # raw-row projection, bf16 [d_model][576]
+    W_Z = 23       # gate-logit projection, bf16 [d_model][G]
 
 
 def config_seed(cfg: int) -> int:

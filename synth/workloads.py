@@ -122,6 +122,17 @@ def queries(w: Workload, device="cpu", second=False, q0=0, nq=None):
     return out
 
 
+def hidden_inputs(w: Workload, d_model: int, G: int = D, t0: int = 0, t1=None, device="cpu"):
+    """Hidden states h bf16 [B][t1-t0][d_model] N(0,1) and the projections
+    W^KV bf16 [d_model][576], W^Z bf16 [d_model][G], both N(0, 1/d_model), so
+    that x = h W^KV and z = h W^Z follow the N(0,1) stream recipe."""
+    t1 = w.T if t1 is None else t1
+    h = normal_bf16(w.seed, TensorId.HID, (w.B, t1 - t0, d_model), device=device, first_elem=t0 * d_model)
+    wkv = normal_bf16(w.seed, TensorId.W_KV, (1, d_model, D), scale=1.0 / math.sqrt(d_model), device=device)[0]
+    wz = normal_bf16(w.seed, TensorId.W_Z, (1, d_model, G), scale=1.0 / math.sqrt(d_model), device=device)[0]
+    return h, wkv, wz
+
+
 def second_layer_window(w: Workload, t0: int, t1: int, device="cpu"):
     """The second layer's own window rows (positions t0..t1-1)."""
     return normal_bf16(w.seed, TensorId.SWA_B, (w.B, t1 - t0, D), device=device, first_elem=t0 * D)

@@ -34,7 +34,7 @@ def _declared():
 
 def test_every_declared_symbol_is_exported(L):
     names = _declared()
-    assert {"csa_compress", "csa_index_topk", "csa_sparse_attn", "hca_dense_attn"} <= set(names)
+    assert {"csa_compress", "csa_compress_hidden", "csa_index_topk", "csa_sparse_attn", "hca_dense_attn"} <= set(names)
     for n in names:
         assert hasattr(L, n), n
     assert set(_lib._SIGS) == set(names)
@@ -234,6 +234,22 @@ def test_fp8_window_checks(L):
                                None, P, 1 << 30, None) == ENULL
     assert L.csa_sparse_attn_w8(ctypes.byref(_cache()), P, 64, P, 0, P, 16, P, P, P, P, 128, 128, 1.0, 0.0, 1, P,
                                 None, P, 1 << 30, None) == OK                # Q = 0: nothing to launch
+
+
+def test_compress_hidden_checks(L):
+    c = ctypes.byref(_cache())
+    def ch(h=P, hs=64 * 128, d=128, wkv=P, wz=P, G=576, bias=P, wik=None, tb=0, T=64, ws=None, wsb=0):
+        return L.csa_compress_hidden(h, hs, d, wkv, wz, G, bias, wik, tb, T, c, ws, wsb, None)
+    assert ch(h=None) == ENULL
+    assert ch(wz=None) == ENULL
+    assert ch(d=100) == EUNSUP          # not a multiple of 32
+    assert ch(d=0) == EUNSUP
+    assert ch(G=7) == EUNSUP
+    assert ch(T=6) == ESHAPE            # not a multiple of m
+    assert ch(h=P + 2) == EALIGN
+    assert ch(T=0) == OK                # nothing to do
+    assert L.csa_compress_hidden_ws_bytes(2, 64, 4, 1) == 2 * 16 * 576 * 4
+    assert L.csa_compress_hidden_ws_bytes(2, 64, 4, 0) == 0
 
 
 def test_read_device_flags_null(L):

@@ -10,7 +10,9 @@ import ctypes
 import os
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libcsa.so")
+# CSA_LIBRARY names another build of the same ABI (the sanitized host-only
+# build that the CPU tests can run against)
+LIB_PATH = os.environ.get("CSA_LIBRARY") or os.path.join(_PKG, "libcsa.so")
 
 c_void_p = ctypes.c_void_p
 c_int = ctypes.c_int

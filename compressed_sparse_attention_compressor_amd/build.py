@@ -65,6 +65,41 @@ def build(verbose: bool = True) -> str:
     return LIB
 
 
+# Sanitized build: the host code (argument checks,
+# workspace sizing, dispatch) instrumented with AddressSanitizer and
+# UndefinedBehaviorSanitizer (the device code is built as usual, never run
+# by the CPU ABI tests, which never reach a launch).  The sanitizer flags go to the host pass
+# only (-Xarch_host before each); the link is a plain clang++ line.
+CLANGXX = os.environ.get("CLANGXX", "/opt/rocm/llvm/bin/clang++")
+SAN_COMPILE = ["-O1", "-Xarch_host", "-g", "-Xarch_host", "-fno-omit-frame-pointer",
+               "-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+               "-Xarch_host", "-fno-sanitize-recover=all"]
+SAN_LINK = ["-fsanitize=address,undefined", "-shared-libasan"]
+
+
+def build_host_sanitized(out_dir: str) -> str:
+    """Builds the sanitized host-only libcsa.so into out_dir; returns its path."""
+    os.makedirs(out_dir, exist_ok=True)
+
+    def one(src):
+        obj = os.path.join(out_dir, os.path.splitext(src)[0] + ".o")
+        cmd = [HIPCC, *FLAGS, *EXTRA.get(src, []), *SAN_COMPILE, "-c", os.path.join(CSRC, src), "-o", obj]
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"host-only compile failed on {src}:\n{r.stderr}")
+        return obj
+
+    workers = min(len(SOURCES), max(1, (os.cpu_count() or 2) // 2))
+    with concurrent.futures.ThreadPoolExecutor(workers) as ex:
+        objs = list(ex.map(one, SOURCES))
+    out = os.path.join(out_dir, "libcsa_san.so")
+    link = [CLANGXX, "-shared", "-fPIC", *objs, *SAN_LINK, "-L/opt/rocm/lib", "-lamdhip64", "-o", out]
+    r = subprocess.run(link, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("sanitized link failed:\n" + r.stderr)
+    return out
+
+
 if __name__ == "__main__":
     build()
     sys.exit(0)

@@ -176,7 +176,7 @@ __device__ __forceinline__ void load_entries(const AttnArgs &a, int b, const int
   }
 }
 
-template <int NT>
+template <int NT, bool kRot>
 __device__ __forceinline__ void store_entries(const AttnArgs &a, uint16_t *K, const int *src, const RawChunk<NT> &r) {
   using CS = ChunkShare<NT>;
   const int tid = threadIdx.x;
@@ -221,7 +221,7 @@ __device__ __forceinline__ void store_entries(const AttnArgs &a, uint16_t *K, co
       uint4 v = r.v[CS::kFp4 + u];  // a value copy: a conditional between lvalues would pin r to memory
       const int j = src[key];
       // a compressed entry sits at its last raw token, (j + 1) m - 1
-      if (a.rot && j >= 0) v = rope_piece(a, v, (int64_t)(j + 1) * a.m - 1, part);
+      if (kRot && j >= 0) v = rope_piece(a, v, (int64_t)(j + 1) * a.m - 1, part);
       if (j < 0) v = uint4{0u, 0u, 0u, 0u};
       *reinterpret_cast<uint4 *>(K + key * kKRow + kDNope + part * 8) = v;
     }
@@ -253,7 +253,7 @@ __device__ __forceinline__ void load_win8(const AttnArgs &a, int b, const int *s
   }
 }
 
-template <int NT>
+template <int NT, bool kRot>
 __device__ __forceinline__ void store_win8(const AttnArgs &a, int swa0, uint16_t *K, const int *src,
                                            const RawChunk<NT> &r) {
   using CS = ChunkShare<NT>;
@@ -295,7 +295,7 @@ __device__ __forceinline__ void store_win8(const AttnArgs &a, int swa0, uint16_t
       const int key = t >> 3, part = t & 7;
       uint4 v = r.v[2 * CS::kFp4 + u];
       const int row = src[key];
-      if (a.rot && row >= 0) v = rope_piece(a, v, (int64_t)swa0 + row, part);  // a window row at its raw position
+      if (kRot && row >= 0) v = rope_piece(a, v, (int64_t)swa0 + row, part);  // a window row at its raw position
       if (row < 0) v = uint4{0u, 0u, 0u, 0u};
       *reinterpret_cast<uint4 *>(K + key * kKRow + kDNope + part * 8) = v;
     }
@@ -315,7 +315,7 @@ __device__ __forceinline__ void load_window(const AttnArgs &a, int b, const int 
   }
 }
 
-template <int NT, int nb>
+template <int NT, int nb, bool kRot>
 __device__ __forceinline__ void store_window(const AttnArgs &a, int swa0, uint16_t *K, const int *src, int t0,
                                              const RawChunk<NT> &r) {
   const int tid = threadIdx.x;
@@ -327,14 +327,14 @@ __device__ __forceinline__ void store_window(const AttnArgs &a, int swa0, uint16
       uint4 v = r.v[u];
       const int row = src[key];
       constexpr int kRope0 = kDNope / 8;  // first positional piece of a row
-      if (a.rot && row >= 0 && part >= kRope0) v = rope_piece(a, v, (int64_t)swa0 + row, part - kRope0);
+      if (kRot && row >= 0 && part >= kRope0) v = rope_piece(a, v, (int64_t)swa0 + row, part - kRope0);
       if (row < 0) v = uint4{0u, 0u, 0u, 0u};
       *reinterpret_cast<uint4 *>(K + key * kKRow + part * 8) = v;
     }
   }
 }
 
-template <int HG, bool kSplitP, bool kDense, bool kW8>
+template <int HG, bool kSplitP, bool kDense, bool kW8, bool kRot>
 __global__ __launch_bounds__(HG * 128) void attn_kernel(AttnArgs a) {
   constexpr int NT = HG * 128;
   constexpr int kQSteps = kKSteps / 2;  // channel steps of this wave's Q K^T
@@ -448,7 +448,7 @@ __global__ __launch_bounds__(HG * 128) void attn_kernel(AttnArgs a) {
 
   if (s_begin < s_end) {
     const int2 j0 = j_first;
-    if (a.rot) {
+    if (kRot) {
       // the first rotation of the fused epilogue: the query's positional
       // channels turned by its own position (rounded to bf16 as they are
       // stored)
@@ -599,9 +599,9 @@ __global__ __launch_bounds__(HG * 128) void attn_kernel(AttnArgs a) {
       else load_entries<NT>(a, b, src_s[sb], raw);
     };
     auto st = [&](uint16_t *K, int sb) __attribute__((always_inline)) {
-      if (kWin16) store_window<NT, CS::kWinBatch>(a, swa0, K, src_s[sb], 0, raw);
-      else if (kWin) store_win8<NT>(a, swa0, K, src_s[sb], raw);
-      else store_entries<NT>(a, K, src_s[sb], raw);
+      if (kWin16) store_window<NT, CS::kWinBatch, kRot>(a, swa0, K, src_s[sb], 0, raw);
+      else if (kWin) store_win8<NT, kRot>(a, swa0, K, src_s[sb], raw);
+      else store_entries<NT, kRot>(a, K, src_s[sb], raw);
     };
     lds_barrier();
     if (CS::kAhead) ld(ci % 3);
@@ -614,7 +614,7 @@ __global__ __launch_bounds__(HG * 128) void attn_kernel(AttnArgs a) {
       } else if (kWin16) {
         for (int t0 = 0; t0 < kWinTasks; t0 += CS::kWinBatch * NT) {
           load_window<NT, CS::kWinBatch>(a, b, src_s[sb], t0, raw);
-          store_window<NT, CS::kWinBatch>(a, swa0, K, src_s[sb], t0, raw);
+          store_window<NT, CS::kWinBatch, kRot>(a, swa0, K, src_s[sb], t0, raw);
         }
       } else {
         ld(sb);
@@ -636,7 +636,7 @@ __global__ __launch_bounds__(HG * 128) void attn_kernel(AttnArgs a) {
   // channels turned back by -p.  The rotation is linear, so it applies to
   // unnormalised partials too.  Lane (g, r) holds channel cbase + 16 j + r of
   // four heads; its pair partner is the neighbouring lane (r ^ 1).
-  if (a.rot) {
+  if (kRot) {
 #pragma unroll
     for (int j = 0; j < kHalfNT; ++j) {
       const int c = cbase + 16 * j;  // uniform in the wave
@@ -874,16 +874,27 @@ size_t attn_workspace_bytes(int B, int Q, int H, int n_main, int n_win) {
   return (size_t)B * Q * s.nsplit * H * (kD + 2) * sizeof(float);
 }
 
+template <int HG, bool kSplitP, bool kRot>
+static void launch_hg_rot(const AttnArgs &a, bool dense, bool w8, dim3 grid, hipStream_t stream) {
+  if (dense && w8)
+    attn_kernel<HG, kSplitP, true, true, kRot><<<grid, HG * 128, 0, stream>>>(a);
+  else if (dense)
+    attn_kernel<HG, kSplitP, true, false, kRot><<<grid, HG * 128, 0, stream>>>(a);
+  else if (w8)
+    attn_kernel<HG, kSplitP, false, true, kRot><<<grid, HG * 128, 0, stream>>>(a);
+  else
+    attn_kernel<HG, kSplitP, false, false, kRot><<<grid, HG * 128, 0, stream>>>(a);
+}
+
+// The rotary epilogue is a separate instantiation: its rotation sits in the
+// chunk loop's decode, and the registers it needs would otherwise be held
+// by the kernel without it too.
 template <int HG, bool kSplitP>
 static void launch_hg(const AttnArgs &a, bool dense, bool w8, dim3 grid, hipStream_t stream) {
-  if (dense && w8)
-    attn_kernel<HG, kSplitP, true, true><<<grid, HG * 128, 0, stream>>>(a);
-  else if (dense)
-    attn_kernel<HG, kSplitP, true, false><<<grid, HG * 128, 0, stream>>>(a);
-  else if (w8)
-    attn_kernel<HG, kSplitP, false, true><<<grid, HG * 128, 0, stream>>>(a);
+  if (a.rot)
+    launch_hg_rot<HG, kSplitP, true>(a, dense, w8, grid, stream);
   else
-    attn_kernel<HG, kSplitP, false, false><<<grid, HG * 128, 0, stream>>>(a);
+    launch_hg_rot<HG, kSplitP, false>(a, dense, w8, grid, stream);
 }
 
 template <bool kSplitP>

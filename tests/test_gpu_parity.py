@@ -1183,3 +1183,51 @@ def test_topk_stage_parity(name, B, Q, Ns, vis, k, rnd):
             sel = oi >= 0
             np.testing.assert_array_equal(gs[b, t][sel], os_[sel].astype(np.float32))
             assert np.all(np.isnan(gs[b, t][~sel]))
+
+
+SPLIT_SHAPE_CASES = [
+    # (name, workload, N_cap, n_entries, positions, dense): chosen for the
+    # launch shape they produce
+    # one query over 300 entries + 128 window rows: 14 splits, the bf16
+    # merge that loads 16 splits per round
+    ("merge-14-splits", Workload("ss1", 60, B=1, T=1200, m=4, d_idx=0, H_I=0, k=0, H=64, n_win=128), 300, [300],
+     [[1199]], True),
+    # 256 query rows: one split, results written directly (bf16 staged
+    # through LDS), at 16, 32 and 64 heads
+    ("one-split-h16", Workload("ss2", 61, B=2, T=2048, m=4, d_idx=0, H_I=0, k=48, H=16, n_win=64, Q=128), 512,
+     [512, 400], None, False),
+    ("one-split-h32", Workload("ss3", 62, B=2, T=2048, m=4, d_idx=0, H_I=0, k=48, H=32, n_win=64, Q=128), 512,
+     [512, 400], None, False),
+    ("one-split-h64", Workload("ss4", 63, B=2, T=2048, m=4, d_idx=0, H_I=0, k=48, H=64, n_win=64, Q=128), 512,
+     [512, 400], None, False),
+]
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=["f32", "bf16"])
+@pytest.mark.parametrize("name,w,N_cap,n_entries,pos,dense", SPLIT_SHAPE_CASES, ids=[c[0] for c in SPLIT_SHAPE_CASES])
+def test_attention_split_shapes(name, w, N_cap, n_entries, pos, dense, dtype):
+    """Launch shapes at the edges of the split and merge code: outputs and
+    LSE against the oracle for every row."""
+    rng = np.random.default_rng(w.cfg)
+    if pos is None:
+        pos = np.sort(rng.integers(w.n_win, w.T, (w.B, w.Q)), axis=1).astype(np.int32)
+    pos = np.array(pos, np.int32)
+    planes, qs, swa, s0 = _attn_inputs(w, N_cap, n_entries, pos)
+    B, Q = pos.shape
+    cache = _gpu_cache(planes, B, N_cap, w.m, 0, n_entries)
+    args = (cache, qs["q"].to(DEV), torch.from_numpy(pos).to(DEV))
+    win = (swa.to(DEV), torch.from_numpy(s0).to(DEV), w.n_win, w.softmax_scale)
+    idx = None
+    if dense:
+        out, lse = csa.hca_dense_attn(*args, *win, out_dtype=dtype)
+    else:
+        idx = np.full((B, Q, w.k), -1, np.int32)
+        for b in range(B):
+            for t in range(Q):
+                V = O.visible_count(int(pos[b, t]), w.m, n_entries[b])
+                n = min(w.k, V)
+                idx[b, t, :n] = np.sort(rng.choice(V, n, replace=False))
+        out, lse = csa.sparse_attn(*args, torch.from_numpy(idx).to(DEV), *win, out_dtype=dtype)
+    torch.cuda.synchronize()
+    o, l = _oracle_attn(planes, qs, swa, s0, pos, idx, w, n_entries, dense, w.softmax_scale)
+    _check_attn(out, lse, o, l, dtype, name)

@@ -57,12 +57,21 @@ struct HiddenArgs {
 
 template <bool kGateFull>
 __global__ __launch_bounds__(kHThreads) void compress_hidden_kernel(HiddenArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t Hs[2][kHTok * kHRowH];
-  __shared__ __attribute__((aligned(16))) uint16_t Wx[2][kHK * kHRowW];
-  __shared__ __attribute__((aligned(16))) uint16_t Wz[2][kGateFull ? kHK * kHRowW : kHK];
-  __shared__ float xs[kHTok][kHCh + 1];
-  __shared__ float zs[kHTok][kGateFull ? kHCh + 1 : 1];
-  __shared__ float cs[kHTok][kHCh];          // pooled rows (E <= 64); the long-block combine reuses it
+  // One LDS region for both phases of a sub-tile (a barrier separates
+  // them): the double-buffered H / W tiles of the k loop, then x, z and the
+  // pooled rows of the epilogue.  At about 49 KB, three workgroups fit on a CU.
+  constexpr int kHsB = 2 * kHTok * kHRowH * 2, kWxB = 2 * kHK * kHRowW * 2;
+  constexpr int kWzB = 2 * (kGateFull ? kHK * kHRowW : kHK) * 2;
+  constexpr int kXsB = kHTok * (kHCh + 1) * 4, kZsB = kHTok * (kGateFull ? kHCh + 1 : 1) * 4;
+  constexpr int kCsB = kHTok * kHCh * 4;
+  constexpr int kLoopB = kHsB + kWxB + kWzB, kEpiB = kXsB + kZsB + kCsB;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kLoopB > kEpiB ? kLoopB : kEpiB];
+  auto Hs = reinterpret_cast<uint16_t (*)[kHTok * kHRowH]>(smem);
+  auto Wx = reinterpret_cast<uint16_t (*)[kHK * kHRowW]>(smem + kHsB);
+  auto Wz = reinterpret_cast<uint16_t (*)[kGateFull ? kHK * kHRowW : kHK]>(smem + kHsB + kWxB);
+  auto xs = reinterpret_cast<float (*)[kHCh + 1]>(smem);
+  auto zs = reinterpret_cast<float (*)[kGateFull ? kHCh + 1 : 1]>(smem + kXsB);
+  auto cs = reinterpret_cast<float (*)[kHCh]>(smem + kXsB + kZsB);  // pooled rows (E <= 64), then the long-block combine
 
   const int b = blockIdx.z;
   const int c0 = blockIdx.y * kHCh;
@@ -147,6 +156,7 @@ __global__ __launch_bounds__(kHThreads) void compress_hidden_kernel(HiddenArgs a
       if (ks + 1 < nk) store_step(buf ^ 1, vh, vx, vz);
     }
 
+    __syncthreads();  // the k loop's tiles are done with: the region becomes x and z
     // x and z of this sub-tile to LDS: lane (g, r) holds tokens
     // 16 wave + 4g + i, channel 16j + r
 #pragma unroll

@@ -308,8 +308,10 @@ __global__ __launch_bounds__(kRegThreads) void topk_reg_kernel(const float *__re
     if ((j >> 2) * kSlice + 4 * tid + (j & 3) >= n) key[j] = 0u;
 
   const int64_t orow = row * nsl + sl;
+  // every slot at or past n is empty (in a causal prefill about half of a
+  // row): the selection skips the 4*kRegThreads-element slices beyond it
   select_keys<kPer, kPrefetch>(key, cid, k, idx_out + orow * k, score_out ? score_out + orow * k : nullptr,
-                               [&](int i) { return kCand ? csrc[i] : off + i; });
+                               [&](int i) { return kCand ? csrc[i] : off + i; }, __builtin_amdgcn_readfirstlane(n));
 }
 
 // ---------------------------------------------------------------------------

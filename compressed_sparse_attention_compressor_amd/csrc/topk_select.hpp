@@ -114,7 +114,7 @@ template <int NT, int kPer, bool kPrefetch, int kStage, typename IdOf>
 __device__ __forceinline__ void place_selected(const uint32_t (&key)[kPer], const int32_t (&cid)[kPrefetch ? kPer : 1],
                                                uint32_t thr, int need, int n_eq, int k_eff, int k, int *cnt,
                                                int32_t *st_i, float *st_s, int32_t *__restrict__ out_i,
-                                               float *__restrict__ out_s, IdOf id_of) {
+                                               float *__restrict__ out_s, IdOf id_of, int n_live = 1 << 30) {
   constexpr int kW = NT / 64;
   constexpr int kV = kPer / 4;              // slices of 4*NT elements
   constexpr int kSlice = NT * 4;
@@ -131,10 +131,12 @@ __device__ __forceinline__ void place_selected(const uint32_t (&key)[kPer], cons
 #pragma unroll
     for (int v = 0; v < kV; ++v) {
       int gc = 0, ec = 0;
+      if (v * kSlice < n_live) {
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        gc += __popcll(__ballot(sure(key[4 * v + u])));
-        if (!simple) ec += __popcll(__ballot(key[4 * v + u] == thr));
+        for (int u = 0; u < 4; ++u) {
+          gc += __popcll(__ballot(sure(key[4 * v + u])));
+          if (!simple) ec += __popcll(__ballot(key[4 * v + u] == thr));
+        }
       }
       if (lane == 0) {
         cnt[v * kW + wave] = gc;
@@ -159,6 +161,7 @@ __device__ __forceinline__ void place_selected(const uint32_t (&key)[kPer], cons
     }
 #pragma unroll
     for (int v = 0; v < kV; ++v) {
+      if (v * kSlice >= n_live) continue;  // a slice of empty slots selects nothing
       const int e = v * kW + wave;
       int gb = (e & 1) ? __builtin_amdgcn_readlane(gx[1], e >> 1) : __builtin_amdgcn_readlane(gx[0], e >> 1);
       int eb = 0;
@@ -225,10 +228,13 @@ __device__ __forceinline__ void place_selected(const uint32_t (&key)[kPer], cons
 template <int NT, int kPer>
 __device__ __forceinline__ void linear_threshold(const uint32_t (&key)[kPer], int k, int *hist, int *sh, int *wred,
                                                  uint32_t *bin_keys, int *n_bin, int &k_eff_out, uint32_t &thr_out,
-                                                 int &need_out, int &n_eq_out) {
+                                                 int &need_out, int &n_eq_out, int n_live = 1 << 30) {
   constexpr int kW = NT / 64;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  // key j lies in a slice of 4*NT elements that may start past n_live, the
+  // bound beyond which every slot is empty: such slices are skipped whole
+  auto live = [&](int j) { return (j >> 2) * (4 * NT) < n_live; };
   int (*hist2)[kBins] = reinterpret_cast<int (*)[kBins]>(hist);
   for (int i = tid; i < kBins; i += NT) hist[i] = 0;
   if (tid == 0) *n_bin = 0;
@@ -241,6 +247,7 @@ __device__ __forceinline__ void linear_threshold(const uint32_t (&key)[kPer], in
     int nv = 0;
 #pragma unroll
     for (int j = 0; j < kPer; ++j) {
+      if (!live(j)) continue;
       mx = key[j] > mx ? key[j] : mx;
       const uint32_t c = key[j] ? ~key[j] : 0u;
       mnc = c > mnc ? c : mnc;
@@ -287,6 +294,10 @@ __device__ __forceinline__ void linear_threshold(const uint32_t (&key)[kPer], in
     uint32_t binp[(kPer + 1) / 2];
 #pragma unroll
     for (int j = 0; j < kPer; ++j) {
+      if (!live(j)) {
+        binp[j >> 1] = 0xFFFFFFFFu;
+        continue;
+      }
       const uint32_t bj = key[j] != 0u ? bin_of(key[j]) : 0xFFFFu;
       if (j & 1) binp[j >> 1] |= bj << 16;
       else binp[j >> 1] = bj;
@@ -298,7 +309,7 @@ __device__ __forceinline__ void linear_threshold(const uint32_t (&key)[kPer], in
     int d1, above, c1, tot;
     find_digit<NT>(hist2, 1, kBins, k_eff, sh, d1, above, c1, tot);
     const uint32_t dhi = (uint32_t)(kBins - 2 - d1);
-    auto in_dhi = [&](int j) { return ((binp[j >> 1] >> (16 * (j & 1))) & 0xFFFFu) == dhi; };
+    auto in_dhi = [&](int j) { return live(j) && ((binp[j >> 1] >> (16 * (j & 1))) & 0xFFFFu) == dhi; };
     int k_rem = k_eff - above;
     if (c1 <= 64) {
       // 2a. gather the threshold bin (one LDS atomic per wave) and rank it
@@ -369,7 +380,8 @@ __device__ __forceinline__ void linear_threshold(const uint32_t (&key)[kPer], in
 // published through a further barrier.
 template <int kPer, bool kPrefetch, typename IdOf>
 __device__ __forceinline__ void select_keys(uint32_t (&key)[kPer], const int32_t (&cid)[kPrefetch ? kPer : 1], int k,
-                                            int32_t *__restrict__ out_i, float *__restrict__ out_s, IdOf id_of) {
+                                            int32_t *__restrict__ out_i, float *__restrict__ out_s, IdOf id_of,
+                                            int n_live = 1 << 30) {
   constexpr int NT = kRegThreads;
   constexpr int kW = NT / 64;
   constexpr int kE = (kPer / 4) * kW;
@@ -383,10 +395,10 @@ __device__ __forceinline__ void select_keys(uint32_t (&key)[kPer], const int32_t
   __shared__ int n_bin;
   int k_eff, need, n_eq;
   uint32_t thr;
-  linear_threshold<NT, kPer>(key, k, hist, sh, wred, bin_keys, &n_bin, k_eff, thr, need, n_eq);
+  linear_threshold<NT, kPer>(key, k, hist, sh, wred, bin_keys, &n_bin, k_eff, thr, need, n_eq, n_live);
   // the histogram's last reads precede the placement's first barrier
   place_selected<NT, kPer, kPrefetch, kStage>(key, cid, thr, need, n_eq, k_eff, k, cnt, hist,
-                                              reinterpret_cast<float *>(hist + kStage), out_i, out_s, id_of);
+                                              reinterpret_cast<float *>(hist + kStage), out_i, out_s, id_of, n_live);
 }
 
 }  // namespace csa

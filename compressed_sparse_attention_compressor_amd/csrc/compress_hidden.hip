@@ -55,23 +55,31 @@ struct HiddenArgs {
   float *pooled;           // fp32 [B][n_ent][576] or null
 };
 
-template <bool kGateFull>
+// kRB: 16-token row blocks per wave.  With kRB = 2 a sub-tile is 128
+// tokens, wave w owning rows 16w..16w+15 of each 64-token half: every k-step
+// issues twice the MFMAs per barrier and reuses each W operand read from
+// LDS for both row blocks.  The epilogue runs half by half (pool, encode and
+// write the half's entries), so the block size must divide 64; kRB = 1 takes
+// every other block size, long blocks (m > 64) included.
+template <bool kGateFull, int kRB>
 __global__ __launch_bounds__(kHThreads) void compress_hidden_kernel(HiddenArgs a) {
+  constexpr int kTok = kHTok * kRB;  // tokens per sub-tile
   // One LDS region for both phases of a sub-tile (a barrier separates
   // them): the double-buffered H / W tiles of the k loop, then x, z and the
-  // pooled rows of the epilogue.  At about 49 KB, three workgroups fit on a CU.
-  constexpr int kHsB = 2 * kHTok * kHRowH * 2, kWxB = 2 * kHK * kHRowW * 2;
+  // pooled rows of the epilogue (one 64-token half at a time).  At about
+  // 49 KB, three workgroups fit on a CU.
+  constexpr int kHsB = 2 * kTok * kHRowH * 2, kWxB = 2 * kHK * kHRowW * 2;
   constexpr int kWzB = 2 * (kGateFull ? kHK * kHRowW : kHK) * 2;
   constexpr int kXsB = kHTok * (kHCh + 1) * 4, kZsB = kHTok * (kGateFull ? kHCh + 1 : 1) * 4;
   constexpr int kCsB = kHTok * kHCh * 4;
   constexpr int kLoopB = kHsB + kWxB + kWzB, kEpiB = kXsB + kZsB + kCsB;
   __shared__ __attribute__((aligned(16))) uint8_t smem[kLoopB > kEpiB ? kLoopB : kEpiB];
-  auto Hs = reinterpret_cast<uint16_t (*)[kHTok * kHRowH]>(smem);
+  auto Hs = reinterpret_cast<uint16_t (*)[kTok * kHRowH]>(smem);
   auto Wx = reinterpret_cast<uint16_t (*)[kHK * kHRowW]>(smem + kHsB);
   auto Wz = reinterpret_cast<uint16_t (*)[kGateFull ? kHK * kHRowW : kHK]>(smem + kHsB + kWxB);
   auto xs = reinterpret_cast<float (*)[kHCh + 1]>(smem);
   auto zs = reinterpret_cast<float (*)[kGateFull ? kHCh + 1 : 1]>(smem + kXsB);
-  auto cs = reinterpret_cast<float (*)[kHCh]>(smem + kXsB + kZsB);  // pooled rows (E <= 64), then the long-block combine
+  auto cs = reinterpret_cast<float (*)[kHCh]>(smem + kXsB + kZsB);  // pooled rows of a half, then the long-block combine
 
   const int b = blockIdx.z;
   const int c0 = blockIdx.y * kHCh;
@@ -83,51 +91,66 @@ __global__ __launch_bounds__(kHThreads) void compress_hidden_kernel(HiddenArgs a
   const int g = lane >> 4, r = lane & 15;
   const uint16_t *hb = a.h + (int64_t)b * a.h_stride_b + (int64_t)e0 * a.m * a.d_model;
   const int nk = a.d_model / kHK;
-  const bool lng = a.m > kHTok;  // one entry, several sub-tiles
+  const bool lng = a.m > kHTok;  // one entry, several sub-tiles (kRB = 1 only)
+  const int e_half = kRB == 1 ? a.E : kHTok / a.m;  // entries per 64-token half
 
-  // Staging of one k-step: H 64 tokens x 32 k (16 bytes per thread), W^KV
-  // 32 k x 64 channels (16 bytes per thread), W^Z likewise or its 32 values.
-  const int ht = tid >> 2, hk = (tid & 3) * 8;    // H: token, k offset
+  // Staging of one k-step: H kTok tokens x 32 k (16 bytes per thread and row
+  // block), W^KV 32 k x 64 channels (16 bytes per thread), W^Z likewise or
+  // its 32 values.
+  const int ht = tid >> 2, hk = (tid & 3) * 8;    // H: token (of a 64-token half), k offset
   const int wk = tid >> 3, wc = (tid & 7) * 8;    // W: k row, channel offset
-  auto load_step = [&](int st, int ks, uint4 &vh, uint4 &vx, uint4 &vz) __attribute__((always_inline)) {
-    const int tok = st + ht;
-    const uint16_t *hp = hb + (int64_t)min(tok, ntok - 1) * a.d_model + ks * kHK + hk;
-    vh = *reinterpret_cast<const uint4 *>(hp);
-    if (tok >= ntok) vh = uint4{0u, 0u, 0u, 0u};
+  struct Stage { uint4 h[kRB], x, z; };
+  auto load_step = [&](int st, int ks, Stage &v) __attribute__((always_inline)) {
+#pragma unroll
+    for (int rb = 0; rb < kRB; ++rb) {
+      const int tok = st + kHTok * rb + ht;
+      const uint16_t *hp = hb + (int64_t)min(tok, ntok - 1) * a.d_model + ks * kHK + hk;
+      v.h[rb] = *reinterpret_cast<const uint4 *>(hp);
+      if (tok >= ntok) v.h[rb] = uint4{0u, 0u, 0u, 0u};
+    }
     const int64_t kr = (int64_t)ks * kHK + wk;
-    vx = *reinterpret_cast<const uint4 *>(a.w_kv + kr * kD + c0 + wc);
-    if (kGateFull) vz = *reinterpret_cast<const uint4 *>(a.w_z + kr * kD + c0 + wc);
-    else vz = *reinterpret_cast<const uint4 *>(a.w_z + (int64_t)ks * kHK + min(tid, 3) * 8);
+    v.x = *reinterpret_cast<const uint4 *>(a.w_kv + kr * kD + c0 + wc);
+    if (kGateFull) v.z = *reinterpret_cast<const uint4 *>(a.w_z + kr * kD + c0 + wc);
+    else v.z = *reinterpret_cast<const uint4 *>(a.w_z + (int64_t)ks * kHK + min(tid, 3) * 8);
   };
-  auto store_step = [&](int buf, const uint4 &vh, const uint4 &vx, const uint4 &vz) __attribute__((always_inline)) {
-    *reinterpret_cast<uint4 *>(&Hs[buf][ht * kHRowH + hk]) = vh;
-    *reinterpret_cast<uint4 *>(&Wx[buf][wk * kHRowW + wc]) = vx;
-    if (kGateFull) *reinterpret_cast<uint4 *>(&Wz[buf][wk * kHRowW + wc]) = vz;
-    else if (tid < 4) *reinterpret_cast<uint4 *>(&Wz[buf][tid * 8]) = vz;
+  auto store_step = [&](int buf, const Stage &v) __attribute__((always_inline)) {
+#pragma unroll
+    for (int rb = 0; rb < kRB; ++rb)
+      *reinterpret_cast<uint4 *>(&Hs[buf][(kHTok * rb + ht) * kHRowH + hk]) = v.h[rb];
+    *reinterpret_cast<uint4 *>(&Wx[buf][wk * kHRowW + wc]) = v.x;
+    if (kGateFull) *reinterpret_cast<uint4 *>(&Wz[buf][wk * kHRowW + wc]) = v.z;
+    else if (tid < 4) *reinterpret_cast<uint4 *>(&Wz[buf][tid * 8]) = v.z;
   };
 
   // long blocks: running (max, sum, weighted sum) of channel tid % 64 over
   // token quarter tid / 64 of every sub-tile
   float lmx = -INFINITY, lden = 0.f, lnum = 0.f;
 
-  for (int st = 0; st < ntok; st += kHTok) {
-    v4f X[kHCh / 16], Z[kGateFull ? kHCh / 16 : 1];
+  for (int st = 0; st < ntok; st += kTok) {
+    v4f X[kRB][kHCh / 16], Z[kRB][kGateFull ? kHCh / 16 : 1];
 #pragma unroll
-    for (int j = 0; j < kHCh / 16; ++j) X[j] = v4f{0.f, 0.f, 0.f, 0.f};
+    for (int rb = 0; rb < kRB; ++rb) {
 #pragma unroll
-    for (int j = 0; j < (kGateFull ? kHCh / 16 : 1); ++j) Z[j] = v4f{0.f, 0.f, 0.f, 0.f};
+      for (int j = 0; j < kHCh / 16; ++j) X[rb][j] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int j = 0; j < (kGateFull ? kHCh / 16 : 1); ++j) Z[rb][j] = v4f{0.f, 0.f, 0.f, 0.f};
+    }
 
-    uint4 vh, vx, vz;
-    load_step(st, 0, vh, vx, vz);
-    store_step(0, vh, vx, vz);
+    Stage v;
+    load_step(st, 0, v);
+    store_step(0, v);
     for (int ks = 0; ks < nk; ++ks) {
       const int buf = ks & 1;
       lds_barrier();  // step ks staged; every wave is done with step ks - 1's buffer
-      if (ks + 1 < nk) load_step(st, ks + 1, vh, vx, vz);
-      // A: token 16 wave + r, k {4g..4g+3, 16+4g..16+4g+3}
-      const uint16_t *hr = &Hs[buf][(16 * wave + r) * kHRowH + 4 * g];
-      const uint2 a0 = *reinterpret_cast<const uint2 *>(hr), a1 = *reinterpret_cast<const uint2 *>(hr + 16);
-      const v8bf A = __builtin_bit_cast(v8bf, uint4{a0.x, a0.y, a1.x, a1.y});
+      if (ks + 1 < nk) load_step(st, ks + 1, v);
+      // A: token 64 rb + 16 wave + r, k {4g..4g+3, 16+4g..16+4g+3}
+      v8bf A[kRB];
+#pragma unroll
+      for (int rb = 0; rb < kRB; ++rb) {
+        const uint16_t *hr = &Hs[buf][(kHTok * rb + 16 * wave + r) * kHRowH + 4 * g];
+        const uint2 a0 = *reinterpret_cast<const uint2 *>(hr), a1 = *reinterpret_cast<const uint2 *>(hr + 16);
+        A[rb] = __builtin_bit_cast(v8bf, uint4{a0.x, a0.y, a1.x, a1.y});
+      }
       typedef __attribute__((address_space(3))) v4s lds_v4s;
       const uint16_t *wb = &Wx[buf][(4 * g + (r >> 2)) * kHRowW + 4 * (r & 3)];
 #pragma unroll
@@ -135,7 +158,8 @@ __global__ __launch_bounds__(kHThreads) void compress_hidden_kernel(HiddenArgs a
         const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s *)(wb + 16 * j));
         const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s *)(wb + 16 * kHRowW + 16 * j));
         const v8bf Bx = __builtin_bit_cast(v8bf, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-        X[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, Bx, X[j], 0, 0, 0);
+#pragma unroll
+        for (int rb = 0; rb < kRB; ++rb) X[rb][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[rb], Bx, X[rb][j], 0, 0, 0);
       }
       if (kGateFull) {
         const uint16_t *zb = &Wz[buf][(4 * g + (r >> 2)) * kHRowW + 4 * (r & 3)];
@@ -144,63 +168,92 @@ __global__ __launch_bounds__(kHThreads) void compress_hidden_kernel(HiddenArgs a
           const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s *)(zb + 16 * j));
           const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s *)(zb + 16 * kHRowW + 16 * j));
           const v8bf Bz = __builtin_bit_cast(v8bf, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-          Z[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, Bz, Z[j], 0, 0, 0);
+#pragma unroll
+          for (int rb = 0; rb < kRB; ++rb)
+            Z[rb][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[rb], Bz, Z[rb][j], 0, 0, 0);
         }
       } else {
         // W^Z in every column: lane (g, r) takes k {4g..4g+3, 16+4g..16+4g+3}
         const uint2 z0 = *reinterpret_cast<const uint2 *>(&Wz[buf][4 * g]);
         const uint2 z1 = *reinterpret_cast<const uint2 *>(&Wz[buf][16 + 4 * g]);
         const v8bf Bz = __builtin_bit_cast(v8bf, uint4{z0.x, z0.y, z1.x, z1.y});
-        Z[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, Bz, Z[0], 0, 0, 0);
+#pragma unroll
+        for (int rb = 0; rb < kRB; ++rb) Z[rb][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[rb], Bz, Z[rb][0], 0, 0, 0);
       }
-      if (ks + 1 < nk) store_step(buf ^ 1, vh, vx, vz);
+      if (ks + 1 < nk) store_step(buf ^ 1, v);
     }
 
-    __syncthreads();  // the k loop's tiles are done with: the region becomes x and z
-    // x and z of this sub-tile to LDS: lane (g, r) holds tokens
-    // 16 wave + 4g + i, channel 16j + r
 #pragma unroll
-    for (int j = 0; j < kHCh / 16; ++j)
+    for (int hh = 0; hh < kRB; ++hh) {
+      __syncthreads();  // the k loop's tiles (or the previous half) are done with: the region becomes x and z
+      // x and z of this 64-token half to LDS: lane (g, r) holds tokens
+      // 16 wave + 4g + i, channel 16j + r
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        xs[16 * wave + 4 * g + i][16 * j + r] = X[j][i];
-        if (kGateFull) zs[16 * wave + 4 * g + i][16 * j + r] = Z[j][i];
-        else if (j == 0 && r == 0) zs[16 * wave + 4 * g + i][0] = Z[0][i];
-      }
-    __syncthreads();
+      for (int j = 0; j < kHCh / 16; ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          xs[16 * wave + 4 * g + i][16 * j + r] = X[hh][j][i];
+          if (kGateFull) zs[16 * wave + 4 * g + i][16 * j + r] = Z[hh][j][i];
+          else if (j == 0 && r == 0) zs[16 * wave + 4 * g + i][0] = Z[hh][0][i];
+        }
+      __syncthreads();
 
-    if (!lng) {
-      // every block of the workgroup lies in this one sub-tile
-      for (int p = tid; p < ne * kHCh; p += kHThreads) {
-        const int e = p / kHCh, c = p % kHCh;
-        const int t0 = e * a.m;
-        float mx = -INFINITY;
-        for (int i = 0; i < a.m; ++i) mx = fmaxf(mx, zs[t0 + i][kGateFull ? c : 0] + a.bias[i]);
-        float den = 0.f, num = 0.f;
-        for (int i = 0; i < a.m; ++i) {
-          const float w = expf(zs[t0 + i][kGateFull ? c : 0] + a.bias[i] - mx);
-          den += w;
-          num = fmaf(w, xs[t0 + i][c], num);
+      if (!lng) {
+        // the entries of this half lie in it whole
+        const int eh0 = hh * e_half, neh = max(0, min(e_half, ne - eh0));
+        for (int p = tid; p < neh * kHCh; p += kHThreads) {
+          const int e = p / kHCh, c = p % kHCh;
+          const int t0 = e * a.m;
+          float mx = -INFINITY;
+          for (int i = 0; i < a.m; ++i) mx = fmaxf(mx, zs[t0 + i][kGateFull ? c : 0] + a.bias[i]);
+          float den = 0.f, num = 0.f;
+          for (int i = 0; i < a.m; ++i) {
+            const float w = expf(zs[t0 + i][kGateFull ? c : 0] + a.bias[i] - mx);
+            den += w;
+            num = fmaf(w, xs[t0 + i][c], num);
+          }
+          cs[e][c] = num / den;
         }
-        cs[e][c] = num / den;
-      }
-    } else {
-      const int c = tid % kHCh, q4 = tid / kHCh;
-      const int i1 = min(kHTok, ntok - st);
-      for (int i = q4 * (kHTok / 4); i < min(i1, (q4 + 1) * (kHTok / 4)); ++i) {
-        const float v = zs[i][kGateFull ? c : 0] + a.bias[st + i];
-        if (v > lmx) {
-          const float s = expf(lmx - v);  // 0 on the first token
-          lden *= s;
-          lnum *= s;
-          lmx = v;
+        __syncthreads();
+        // encoding: MXFP4 blocks 2y, 2y + 1 of the main entry, or the bf16
+        // positional channels; 16 lanes per 32-channel block
+        for (int t = tid; t < (c0 < kDNope ? neh * 32 : 0); t += kHThreads) {
+          const int e = t >> 5, half = (t >> 4) & 1, l = t & 15;
+          uint32_t sb;
+          const uint32_t byte = encode_pair(cs[e][32 * half + 2 * l], cs[e][32 * half + 2 * l + 1], sb);
+          const int64_t row = (int64_t)b * a.N_cap + a.entry0 + e0 + eh0 + e;
+          const int kb = c0 / 32 + half;
+          a.nope[row * kNopeBytes + kb * 16 + l] = (uint8_t)byte;
+          if (l == 0) a.nscale[row * kNopeScales + kb] = (uint8_t)sb;
         }
-        const float w = expf(v - lmx);
-        lden += w;
-        lnum = fmaf(w, xs[i][c], lnum);
+        for (int t = tid; t < (c0 >= kDNope ? neh * kHCh : 0); t += kHThreads) {
+          const int e = t / kHCh, c = t % kHCh;
+          const int64_t row = (int64_t)b * a.N_cap + a.entry0 + e0 + eh0 + e;
+          a.rope[row * kDRope + c] = (uint16_t)f32_to_bf16(cs[e][c]);
+        }
+        if (a.pooled)
+          for (int t = tid; t < neh * kHCh; t += kHThreads) {
+            const int e = t / kHCh, c = t % kHCh;
+            a.pooled[((int64_t)b * a.n_ent + e0 + eh0 + e) * kD + c0 + c] = cs[e][c];
+          }
+      } else {
+        const int c = tid % kHCh, q4 = tid / kHCh;
+        const int i1 = min(kHTok, ntok - st);
+        for (int i = q4 * (kHTok / 4); i < min(i1, (q4 + 1) * (kHTok / 4)); ++i) {
+          const float v = zs[i][kGateFull ? c : 0] + a.bias[st + i];
+          if (v > lmx) {
+            const float s = expf(lmx - v);  // 0 on the first token
+            lden *= s;
+            lnum *= s;
+            lmx = v;
+          }
+          const float w = expf(v - lmx);
+          lden += w;
+          lnum = fmaf(w, xs[i][c], lnum);
+        }
       }
     }
-    __syncthreads();  // xs / zs are rewritten by the next sub-tile
+    __syncthreads();  // xs / zs / cs are rewritten by the next sub-tile
   }
 
   if (lng) {
@@ -228,31 +281,23 @@ __global__ __launch_bounds__(kHThreads) void compress_hidden_kernel(HiddenArgs a
     __syncthreads();
     if (tid < kHCh) cs[0][tid] = res;
     __syncthreads();
-  } else {
-    __syncthreads();
-  }
-
-  // 3. encoding: MXFP4 blocks 2y, 2y + 1 of the main entry, or the bf16
-  //    positional channels; 16 lanes per 32-channel block
-  for (int t = tid; t < (c0 < kDNope ? ne * 32 : 0); t += kHThreads) {
-    const int e = t >> 5, half = (t >> 4) & 1, l = t & 15;
-    uint32_t sb;
-    const uint32_t byte = encode_pair(cs[e][32 * half + 2 * l], cs[e][32 * half + 2 * l + 1], sb);
-    const int64_t row = (int64_t)b * a.N_cap + a.entry0 + e0 + e;
-    const int kb = c0 / 32 + half;
-    a.nope[row * kNopeBytes + kb * 16 + l] = (uint8_t)byte;
-    if (l == 0) a.nscale[row * kNopeScales + kb] = (uint8_t)sb;
-  }
-  for (int t = tid; t < (c0 >= kDNope ? ne * kHCh : 0); t += kHThreads) {
-    const int e = t / kHCh, c = t % kHCh;
-    const int64_t row = (int64_t)b * a.N_cap + a.entry0 + e0 + e;
-    a.rope[row * kDRope + c] = (uint16_t)f32_to_bf16(cs[e][c]);
-  }
-  if (a.pooled)
-    for (int t = tid; t < ne * kHCh; t += kHThreads) {
-      const int e = t / kHCh, c = t % kHCh;
-      a.pooled[((int64_t)b * a.n_ent + e0 + e) * kD + c0 + c] = cs[e][c];
+    // one entry: its encoding as above
+    for (int t = tid; t < (c0 < kDNope ? 32 : 0); t += kHThreads) {
+      const int half = (t >> 4) & 1, l = t & 15;
+      uint32_t sb;
+      const uint32_t byte = encode_pair(cs[0][32 * half + 2 * l], cs[0][32 * half + 2 * l + 1], sb);
+      const int64_t row = (int64_t)b * a.N_cap + a.entry0 + e0;
+      const int kb = c0 / 32 + half;
+      a.nope[row * kNopeBytes + kb * 16 + l] = (uint8_t)byte;
+      if (l == 0) a.nscale[row * kNopeScales + kb] = (uint8_t)sb;
     }
+    for (int t = tid; t < (c0 >= kDNope ? kHCh : 0); t += kHThreads) {
+      const int64_t row = (int64_t)b * a.N_cap + a.entry0 + e0;
+      a.rope[row * kDRope + t] = (uint16_t)f32_to_bf16(cs[0][t]);
+    }
+    if (a.pooled)
+      for (int t = tid; t < kHCh; t += kHThreads) a.pooled[((int64_t)b * a.n_ent + e0) * kD + c0 + t] = cs[0][t];
+  }
 }
 
 size_t compress_hidden_ws_bytes(int B, int n_ent, bool has_ik) {
@@ -273,17 +318,24 @@ hipError_t launch_compress_hidden(const uint16_t *h, int64_t h_stride_b, int d_m
   a.m = c.m;
   a.n_ent = n_ent;
   a.entry0 = entry0;
-  a.E = c.m <= kHTok ? kHTok / c.m : 1;
+  // 128-token sub-tiles when the block size divides 64 (the epilogue's
+  // halves then hold whole blocks), else 64
+  const bool wide = c.m <= kHTok && kHTok % c.m == 0;
+  a.E = wide ? 2 * kHTok / c.m : (c.m <= kHTok ? kHTok / c.m : 1);
   a.nope = c.nope;
   a.nscale = c.nscale;
   a.rope = c.rope;
   a.N_cap = c.N_cap;
   a.pooled = w_ik ? reinterpret_cast<float *>(ws) : nullptr;
   const dim3 grid((unsigned)((n_ent + a.E - 1) / a.E), kD / kHCh, c.B);
-  if (G == kD)
-    compress_hidden_kernel<true><<<grid, kHThreads, 0, stream>>>(a);
+  if (G == kD && wide)
+    compress_hidden_kernel<true, 2><<<grid, kHThreads, 0, stream>>>(a);
+  else if (G == kD)
+    compress_hidden_kernel<true, 1><<<grid, kHThreads, 0, stream>>>(a);
+  else if (wide)
+    compress_hidden_kernel<false, 2><<<grid, kHThreads, 0, stream>>>(a);
   else
-    compress_hidden_kernel<false><<<grid, kHThreads, 0, stream>>>(a);
+    compress_hidden_kernel<false, 1><<<grid, kHThreads, 0, stream>>>(a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !w_ik) return e;
   return launch_ikey_from_pooled(a.pooled, w_ik, entry0, n_ent, c, stream);

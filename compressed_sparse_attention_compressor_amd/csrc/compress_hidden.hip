@@ -53,6 +53,7 @@ struct HiddenArgs {
   uint16_t *rope;
   int N_cap;
   float *pooled;           // fp32 [B][n_ent][576] or null
+  int B;                   // sequences
 };
 
 // kRB: 16-token row blocks per wave.  With kRB = 2 a sub-tile is 128
@@ -81,9 +82,18 @@ __global__ __launch_bounds__(kHThreads) void compress_hidden_kernel(HiddenArgs a
   auto zs = reinterpret_cast<float (*)[kGateFull ? kHCh + 1 : 1]>(smem + kXsB);
   auto cs = reinterpret_cast<float (*)[kHCh]>(smem + kXsB + kZsB);  // pooled rows of a half, then the long-block combine
 
-  const int b = blockIdx.z;
-  const int c0 = blockIdx.y * kHCh;
-  const int e0 = blockIdx.x * a.E;
+  // Workgroup L runs on XCD L % 8.  The 9 channel blocks of one token tile
+  // (sequence b, tile t) get ids that share that remainder and follow each
+  // other on their XCD, so the tile's hidden states are read from HBM once
+  // and then from that XCD's L2.
+  const int L = blockIdx.x;
+  const int n_tiles = (a.n_ent + a.E - 1) / a.E;
+  const int sidx = L >> 3;
+  const int T = 8 * (sidx / (kD / kHCh)) + (L & 7);  // sequence-major tile index
+  if (T >= n_tiles * a.B) return;  // the whole workgroup, before any barrier
+  const int b = T / n_tiles;
+  const int c0 = (sidx % (kD / kHCh)) * kHCh;
+  const int e0 = (T % n_tiles) * a.E;
   const int ne = min(a.E, a.n_ent - e0);
   const int ntok = ne * a.m;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -327,7 +337,9 @@ hipError_t launch_compress_hidden(const uint16_t *h, int64_t h_stride_b, int d_m
   a.rope = c.rope;
   a.N_cap = c.N_cap;
   a.pooled = w_ik ? reinterpret_cast<float *>(ws) : nullptr;
-  const dim3 grid((unsigned)((n_ent + a.E - 1) / a.E), kD / kHCh, c.B);
+  a.B = c.B;
+  const int64_t tiles = (int64_t)c.B * ((n_ent + a.E - 1) / a.E);
+  const dim3 grid((unsigned)(8 * ((tiles + 7) / 8) * (kD / kHCh)));
   if (G == kD && wide)
     compress_hidden_kernel<true, 2><<<grid, kHThreads, 0, stream>>>(a);
   else if (G == kD)

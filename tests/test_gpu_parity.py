@@ -6,6 +6,8 @@ are in gpu_check.py.
 
 import math
 
+import zlib
+
 import numpy as np
 import pytest
 import torch
@@ -1183,6 +1185,63 @@ def test_topk_stage_parity(name, B, Q, Ns, vis, k, rnd):
             sel = oi >= 0
             np.testing.assert_array_equal(gs[b, t][sel], os_[sel].astype(np.float32))
             assert np.all(np.isnan(gs[b, t][~sel]))
+
+
+# Whole rows of up to 16,384 scores in launches of at least 256 rows (one
+# workgroup per row, as in a causal prefill) under score patterns that stress
+# the linear-bin threshold: a strided block of outliers, all equal, a large
+# k, coarse ties.
+MANY_ROW_CASES = [
+    # (name, rows, Ns, k, score pattern)
+    ("rows-normal", 256, 16384, 1024, "normal"),
+    ("rows-k64", 300, 12000, 64, "normal"),
+    ("rows-strided-outliers", 256, 16384, 1024, "high-at-samples"),
+    ("rows-all-equal", 256, 16384, 1024, "equal"),
+    ("rows-k3500", 256, 16384, 3500, "normal"),
+    ("rows-causal-ties", 320, 16384, 1024, "ties"),
+]
+
+
+def _row_scores(rows, Ns, mode, seed):
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((rows, Ns)).astype(np.float32)
+    if mode == "equal":
+        return np.zeros((rows, Ns), np.float32)
+    if mode == "ties":
+        return np.round(x * 4) / 4
+    if mode == "high-at-samples":
+        # every fourth element of every other 2,048-element slice far above the rest
+        i = np.arange(Ns)
+        at = (i % 4 == 0) & ((i // 2048) % 2 == 0)
+        x[:, at] += 100.0
+    return x
+
+
+@pytest.mark.parametrize("name,rows,Ns,k,mode", MANY_ROW_CASES, ids=[c[0] for c in MANY_ROW_CASES])
+def test_topk_many_whole_rows(name, rows, Ns, k, mode):
+    """One workgroup per row over many rows gives the oracle's selection:
+    largest first, ties to the lower entry, in entry order.  Visible counts
+    are spread over the rows as in a causal prefill."""
+    sc = _row_scores(rows, Ns, mode, zlib.crc32(name.encode()))
+    B, Q = 1, rows
+    vis = np.array([min(Ns, max(1, Ns - (r * 37) % (Ns // 2))) if r % 5 else min(Ns, (r * Ns) // rows + 1)
+                    for r in range(rows)]).reshape(B, Q)
+    pos = (vis - 1).astype(np.int32)
+    cache = csa.Cache(B, Ns, 1, 0, planes=dict(
+        nope=torch.zeros(B, 1, 256, dtype=torch.uint8, device=DEV), nscale=torch.zeros(B, 1, 16, dtype=torch.uint8,
+                                                                                     device=DEV),
+        rope=torch.zeros(B, 1, 64, dtype=torch.bfloat16, device=DEV), ikey=None, iscale=None,
+        n_entries=torch.full((B,), Ns, dtype=torch.int32, device=DEV)))
+    idx, s_out = csa.topk(cache, torch.from_numpy(sc.reshape(B, Q, Ns)).to(DEV), torch.from_numpy(pos).to(DEV), k,
+                          want_scores=True)
+    g, gs = _np(idx), _np(s_out)
+    for t in range(Q):
+        n = int(vis[0, t])
+        oi, os_ = O.topk_select(sc[t, :n].astype(np.float64), np.arange(n), k)
+        np.testing.assert_array_equal(g[0, t], oi, err_msg=f"{name} row={t} n={n}")
+        sel = oi >= 0
+        np.testing.assert_array_equal(gs[0, t][sel], os_[sel].astype(np.float32))
+        assert np.all(np.isnan(gs[0, t][~sel]))
 
 
 SPLIT_SHAPE_CASES = [

@@ -1037,6 +1037,40 @@ def test_attention_with_no_keys_is_zero():
     assert torch.all(out == 0) and torch.all(torch.isneginf(lse))
 
 
+REPEAT_CASES = [
+    # 16 heads, one chunk per split (98 splits, bf16 partials through the
+    # 32-split merge): each call is a fresh set of workgroups, so a race in
+    # the kernel, or a result read before the instruction that produces it
+    # has written it back, shows up as a wrong row in some of the calls
+    ("dense-h16-98-splits", Workload("dm", 16, B=1, T=12000, m=4, d_idx=0, H_I=0, k=0, H=16, n_win=128), 3000,
+     [3000], [[11999]]),
+    # 64 heads, 256 query rows of one sequence: one split per row, bf16
+    # results written straight from the workgroup (the prefill launch shape)
+    ("dense-h64-rows", Workload("dr", 17, B=1, T=4096, m=4, d_idx=0, H_I=0, k=0, H=64, n_win=128, Q=256), 1024,
+     [1024], [list(range(4095 - 255 * 15, 4096, 15))]),
+]
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=["f32", "bf16"])
+@pytest.mark.parametrize("name,w,N_cap,n_entries,pos", REPEAT_CASES, ids=[c[0] for c in REPEAT_CASES])
+def test_attention_repeated_calls(name, w, N_cap, n_entries, pos, dtype):
+    pos = np.array(pos, np.int32)
+    planes, qs, swa, s0 = _attn_inputs(w, N_cap, n_entries, pos)
+    cache = _gpu_cache(planes, w.B, N_cap, w.m, 0, n_entries)
+    o, l = _oracle_attn(planes, qs, swa, s0, pos, None, w, n_entries, True, w.softmax_scale)
+    q, p_d, swa_d, s0_d = qs["q"].to(DEV), torch.from_numpy(pos).to(DEV), swa.to(DEV), torch.from_numpy(s0).to(DEV)
+    first = None
+    for rep in range(12):
+        out, lse = csa.hca_dense_attn(cache, q, p_d, swa_d, s0_d, w.n_win, w.softmax_scale, out_dtype=dtype)
+        torch.cuda.synchronize()
+        _check_attn(out, lse, o, l, dtype, f"{name} call {rep}")
+        # the same launch gives the same bits every time
+        if first is None:
+            first = (out.clone(), lse.clone())
+        else:
+            assert torch.equal(out, first[0]) and torch.equal(lse, first[1]), f"{name} call {rep} differs"
+
+
 def test_hca_equals_sparse_with_every_entry():
     w = Workload("eq", 18, B=1, T=4096, m=4, d_idx=0, H_I=0, k=1024, H=64, n_win=128)
     planes, qs, swa, s0 = _attn_inputs(w, 1024, [1024], np.array([[4095]], np.int32))

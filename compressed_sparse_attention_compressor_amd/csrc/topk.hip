@@ -267,18 +267,18 @@ __global__ __launch_bounds__(kRegThreads) void topk_reg_kernel(const float *__re
 
   // Unconditional loads from clamped addresses first (loads inside per-lane
   // branches are serialised by the compiler); the row length is applied after.
-  uint32_t key[kPer];  // key[4v + u]; 0 = not a candidate
+  uint32_t key[kPer];  // key[4v + u] (raw score bits until converted); 0 = not a candidate
   int32_t cid[kPrefetch ? kPer : 1];
-  auto to_key = [](float x) { return __float_as_uint(x) != kNoScoreBits ? score_key(x) : 0u; };
+  auto to_key = [](uint32_t bits) { return bits != kNoScoreBits ? score_key(__uint_as_float(bits)) : 0u; };
   if (len >= 4 && ((Ns | off | len) & 3) == 0) {
 #pragma unroll
     for (int v = 0; v < kV; ++v) {
       const int i0 = min(v * kSlice + 4 * tid, len - 4);
-      const float4 t4 = *reinterpret_cast<const float4 *>(src + i0);
-      key[4 * v + 0] = to_key(t4.x);
-      key[4 * v + 1] = to_key(t4.y);
-      key[4 * v + 2] = to_key(t4.z);
-      key[4 * v + 3] = to_key(t4.w);
+      const uint4 t4 = *reinterpret_cast<const uint4 *>(src + i0);
+      key[4 * v + 0] = t4.x;
+      key[4 * v + 1] = t4.y;
+      key[4 * v + 2] = t4.z;
+      key[4 * v + 3] = t4.w;
       if constexpr (kPrefetch) {
         const int4 c4 = *reinterpret_cast<const int4 *>(csrc + i0);
         cid[4 * v + 0] = c4.x;
@@ -291,7 +291,7 @@ __global__ __launch_bounds__(kRegThreads) void topk_reg_kernel(const float *__re
 #pragma unroll
     for (int j = 0; j < kPer; ++j) {
       const int i = min((j >> 2) * kSlice + 4 * tid + (j & 3), len - 1);
-      key[j] = len > 0 ? to_key(src[i]) : 0u;
+      key[j] = len > 0 ? __float_as_uint(src[i]) : kNoScoreBits;
       if constexpr (kPrefetch) cid[j] = len > 0 ? csrc[i] : -1;
     }
   }
@@ -302,16 +302,30 @@ __global__ __launch_bounds__(kRegThreads) void topk_reg_kernel(const float *__re
     const int nE = min(n_entries[b], N_cap);
     n = max(0, min(nE, (q_pos[row] + 1) / m));
   }
-  n = max(0, min(n - off, len));            // elements of this slice
+  n = __builtin_amdgcn_readfirstlane(max(0, min(n - off, len)));  // elements of this slice
+  // keys from the raw bits, per slice of 4*NT elements: slices past n are
+  // empty (about half of a causal prefill row), slices before it need no
+  // per-element test
 #pragma unroll
-  for (int j = 0; j < kPer; ++j)
-    if ((j >> 2) * kSlice + 4 * tid + (j & 3) >= n) key[j] = 0u;
+  for (int v = 0; v < kV; ++v) {
+    if (v * kSlice >= n) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) key[4 * v + u] = 0u;
+    } else if ((v + 1) * kSlice <= n) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) key[4 * v + u] = to_key(key[4 * v + u]);
+    } else {
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        key[4 * v + u] = v * kSlice + 4 * tid + u < n ? to_key(key[4 * v + u]) : 0u;
+    }
+  }
 
   const int64_t orow = row * nsl + sl;
   // every slot at or past n is empty (in a causal prefill about half of a
   // row): the selection skips the 4*kRegThreads-element slices beyond it
   select_keys<kPer, kPrefetch>(key, cid, k, idx_out + orow * k, score_out ? score_out + orow * k : nullptr,
-                               [&](int i) { return kCand ? csrc[i] : off + i; }, __builtin_amdgcn_readfirstlane(n));
+                               [&](int i) { return kCand ? csrc[i] : off + i; }, n);
 }
 
 // ---------------------------------------------------------------------------

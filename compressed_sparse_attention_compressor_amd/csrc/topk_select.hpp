@@ -385,9 +385,11 @@ __device__ __forceinline__ void select_keys(uint32_t (&key)[kPer], const int32_t
   constexpr int NT = kRegThreads;
   constexpr int kW = NT / 64;
   constexpr int kE = (kPer / 4) * kW;
-  // the histogram area doubles as the staging area of the placement
-  constexpr int kStage = kW * kBins / 2;
-  __shared__ int hist[kW * kBins];
+  // the histogram area doubles as the staging area of the placement, sized
+  // for selections of up to 2,048 (larger ones are written out directly):
+  // 16 KB, so that three workgroups of 512 threads share a CU
+  constexpr int kStage = 2048;
+  __shared__ int hist[kBins > 2 * kStage ? kBins : 2 * kStage];
   __shared__ int sh[kW + 3];
   __shared__ int wred[3 * kW];
   __shared__ uint32_t bin_keys[64];

@@ -134,8 +134,8 @@ __device__ __forceinline__ void place_selected(const uint32_t (&key)[kPer], cons
       if (v * kSlice < n_live) {
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-          gc += __popcll(__ballot(sure(key[4 * v + u])));
-          if (!simple) ec += __popcll(__ballot(key[4 * v + u] == thr));
+          gc += __popcll(__builtin_amdgcn_ballot_w64(sure(key[4 * v + u])));
+          if (!simple) ec += __popcll(__builtin_amdgcn_ballot_w64(key[4 * v + u] == thr));
         }
       }
       if (lane == 0) {
@@ -168,8 +168,8 @@ __device__ __forceinline__ void place_selected(const uint32_t (&key)[kPer], cons
       if (!simple) eb = (e & 1) ? __builtin_amdgcn_readlane(ex[1], e >> 1) : __builtin_amdgcn_readlane(ex[0], e >> 1);
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        gb += __popcll(__ballot(sure(key[4 * v + u])) & below);
-        if (!simple) eb += __popcll(__ballot(key[4 * v + u] == thr) & below);
+        gb += __popcll(__builtin_amdgcn_ballot_w64(sure(key[4 * v + u])) & below);
+        if (!simple) eb += __popcll(__builtin_amdgcn_ballot_w64(key[4 * v + u] == thr) & below);
       }
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
@@ -241,21 +241,22 @@ __device__ __forceinline__ void linear_threshold(const uint32_t (&key)[kPer], in
   uint32_t *wmax = reinterpret_cast<uint32_t *>(wred), *wmin = wmax + kW;
   int *wcnt = wred + 2 * kW;
 
-  // 1. maximum, minimum and count of the valid keys
+  // 1. maximum, minimum and count of the valid keys (the count from the
+  //    ballots of the validity test, on the scalar unit)
   {
-    uint32_t mx = 0, mnc = 0;  // mnc: complement of the minimum
+    uint32_t mx = 0, mn = 0xFFFFFFFFu;
     int nv = 0;
 #pragma unroll
     for (int j = 0; j < kPer; ++j) {
       if (!live(j)) continue;
+      const bool valid = key[j] != 0u;
       mx = key[j] > mx ? key[j] : mx;
-      const uint32_t c = key[j] ? ~key[j] : 0u;
-      mnc = c > mnc ? c : mnc;
-      nv += key[j] != 0u;
+      const uint32_t c = valid ? key[j] : 0xFFFFFFFFu;
+      mn = c < mn ? c : mn;
+      nv += __popcll(__builtin_amdgcn_ballot_w64(valid));
     }
     mx = wave_max_u32(mx);
-    mnc = wave_max_u32(mnc);
-    nv = wave_sum(nv);
+    const uint32_t mnc = wave_max_u32(~mn);  // complement of the minimum (0: no valid key)
     if (lane == 0) {
       wmax[wave] = mx;
       wmin[wave] = mnc;
@@ -312,21 +313,22 @@ __device__ __forceinline__ void linear_threshold(const uint32_t (&key)[kPer], in
     auto in_dhi = [&](int j) { return live(j) && ((binp[j >> 1] >> (16 * (j & 1))) & 0xFFFFu) == dhi; };
     int k_rem = k_eff - above;
     if (c1 <= 64) {
-      // 2a. gather the threshold bin (one LDS atomic per wave) and rank it
-      int mine = 0;
+      // 2a. gather the threshold bin and rank it.  One pass: a ballot per
+      //     key, and on the rare non-empty one an LDS atomic reserves its
+      //     slots, each key going to its ballot's lanes below it.
+      const uint64_t below = lane ? (~0ull >> (64 - lane)) : 0ull;
 #pragma unroll
-      for (int j = 0; j < kPer; ++j) mine += in_dhi(j);
-      const int inc = wave_incl_scan(mine);
-      const int wtot = __builtin_amdgcn_readlane(inc, 63);
-      int base = 0;
-      if (wtot > 0) {
-        if (lane == 63) base = atomicAdd(n_bin, wtot);
-        base = __builtin_amdgcn_readlane(base, 63);
+      for (int j = 0; j < kPer; ++j) {
+        if (!live(j)) continue;  // uniform: the ballot takes the comparison itself
+        const bool in = ((binp[j >> 1] >> (16 * (j & 1))) & 0xFFFFu) == dhi;
+        const uint64_t mk = __builtin_amdgcn_ballot_w64(in);
+        if (mk) {
+          int pos = 0;
+          if (lane == 0) pos = atomicAdd(n_bin, (int)__popcll(mk));
+          pos = __builtin_amdgcn_readfirstlane(pos);
+          if (in) bin_keys[pos + __popcll(mk & below)] = key[j];
+        }
       }
-      int pos = base + inc - mine;
-#pragma unroll
-      for (int j = 0; j < kPer; ++j)
-        if (in_dhi(j)) bin_keys[pos++] = key[j];
       __syncthreads();
       rank_gathered<NT>(bin_keys, c1, k_rem, sh, thr, need, n_eq);
     } else {

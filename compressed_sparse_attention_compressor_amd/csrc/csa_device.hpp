@@ -108,6 +108,12 @@ __device__ __forceinline__ int dpp_i32(int x) {
 // Inclusive prefix sum over the 64 lanes of a wave: shifts by 1, 2, 4, 8
 // within each row of 16 lanes, then the row totals carried into the rows
 // above (row_bcast:15 into rows 1 and 3, row_bcast:31 into rows 2 and 3).
+// acc + the number of lanes below this one whose bit is set in the wave
+// mask mk (v_mbcnt_lo / v_mbcnt_hi: two instructions, the add included).
+__device__ __forceinline__ int lanes_below(uint64_t mk, int acc) {
+  return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(mk >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mk, (uint32_t)acc));
+}
+
 __device__ __forceinline__ int wave_incl_scan(int x) {
   x += dpp_i32<0x111>(x);
   x += dpp_i32<0x112>(x);

@@ -124,18 +124,22 @@ __device__ __forceinline__ void place_selected(const uint32_t (&key)[kPer], cons
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const bool staged = k_eff <= kStage;
   if (k_eff > 0) {
+    // taken outright: key >= thr when simple, key > thr otherwise.  Each
+    // case has loops of its own, so that a ballot takes one comparison.
     const bool simple = need == n_eq;
-    // taken outright: key >= thr when simple, key > thr otherwise
-    auto sure = [&](uint32_t kk) { return simple ? kk >= thr : kk > thr; };
-    const uint64_t below = lane ? (~0ull >> (64 - lane)) : 0ull;
 #pragma unroll
     for (int v = 0; v < kV; ++v) {
       int gc = 0, ec = 0;
       if (v * kSlice < n_live) {
+        if (simple) {
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          gc += __popcll(__builtin_amdgcn_ballot_w64(sure(key[4 * v + u])));
-          if (!simple) ec += __popcll(__builtin_amdgcn_ballot_w64(key[4 * v + u] == thr));
+          for (int u = 0; u < 4; ++u) gc += __popcll(__builtin_amdgcn_ballot_w64(key[4 * v + u] >= thr));
+        } else {
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            gc += __popcll(__builtin_amdgcn_ballot_w64(key[4 * v + u] > thr));
+            ec += __popcll(__builtin_amdgcn_ballot_w64(key[4 * v + u] == thr));
+          }
         }
       }
       if (lane == 0) {
@@ -159,49 +163,76 @@ __device__ __forceinline__ void place_selected(const uint32_t (&key)[kPer], cons
         ex[1] = qi - q1;
       }
     }
-#pragma unroll
-    for (int v = 0; v < kV; ++v) {
-      if (v * kSlice >= n_live) continue;  // a slice of empty slots selects nothing
-      const int e = v * kW + wave;
-      int gb = (e & 1) ? __builtin_amdgcn_readlane(gx[1], e >> 1) : __builtin_amdgcn_readlane(gx[0], e >> 1);
-      int eb = 0;
-      if (!simple) eb = (e & 1) ? __builtin_amdgcn_readlane(ex[1], e >> 1) : __builtin_amdgcn_readlane(ex[0], e >> 1);
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        gb += __popcll(__builtin_amdgcn_ballot_w64(sure(key[4 * v + u])) & below);
-        if (!simple) eb += __popcll(__builtin_amdgcn_ballot_w64(key[4 * v + u] == thr) & below);
+    // staged selections keep their keys; the copy-out turns them into scores
+    uint32_t *st_k = reinterpret_cast<uint32_t *>(st_s);
+    auto put = [&](int p, int32_t id, uint32_t kk) __attribute__((always_inline)) {
+      if (staged) {
+        st_i[p] = id;
+        st_k[p] = kk;
+      } else {
+        out_i[p] = id;
+        if (out_s) out_s[p] = key_score(kk);
       }
+    };
+    if (simple) {
+      // every key >= thr is taken, k_eff of them: no tie count, no bound test
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const uint32_t kk = key[4 * v + u];
-        const bool is_gt = sure(kk), is_eq = !simple && kk == thr;
-        if (is_gt || (is_eq && eb < need)) {
-          const int p = gb + min(eb, need);
-          if (p < k_eff) {
-            const int i = v * kSlice + 4 * tid + u;
+      for (int v = 0; v < kV; ++v) {
+        if (v * kSlice >= n_live) continue;  // a slice of empty slots selects nothing
+        const int e = v * kW + wave;
+        int gb = (e & 1) ? __builtin_amdgcn_readlane(gx[1], e >> 1) : __builtin_amdgcn_readlane(gx[0], e >> 1);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) gb = lanes_below(__builtin_amdgcn_ballot_w64(key[4 * v + u] >= thr), gb);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const uint32_t kk = key[4 * v + u];
+          if (kk >= thr) {
             int32_t id;
             if constexpr (kPrefetch) id = cid[4 * v + u];
-            else id = id_of(i);
-            if (staged) {
-              st_i[p] = id;
-              st_s[p] = key_score(kk);
-            } else {
-              out_i[p] = id;
-              if (out_s) out_s[p] = key_score(kk);
-            }
+            else id = id_of(v * kSlice + 4 * tid + u);
+            put(gb, id, kk);
+            ++gb;
           }
         }
-        gb += is_gt;
-        eb += is_eq;
+      }
+    } else {
+#pragma unroll
+      for (int v = 0; v < kV; ++v) {
+        if (v * kSlice >= n_live) continue;
+        const int e = v * kW + wave;
+        int gb = (e & 1) ? __builtin_amdgcn_readlane(gx[1], e >> 1) : __builtin_amdgcn_readlane(gx[0], e >> 1);
+        int eb = (e & 1) ? __builtin_amdgcn_readlane(ex[1], e >> 1) : __builtin_amdgcn_readlane(ex[0], e >> 1);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          gb = lanes_below(__builtin_amdgcn_ballot_w64(key[4 * v + u] > thr), gb);
+          eb = lanes_below(__builtin_amdgcn_ballot_w64(key[4 * v + u] == thr), eb);
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const uint32_t kk = key[4 * v + u];
+          const bool is_gt = kk > thr, is_eq = kk == thr;
+          if (is_gt || (is_eq && eb < need)) {
+            const int p = gb + min(eb, need);
+            if (p < k_eff) {
+              int32_t id;
+              if constexpr (kPrefetch) id = cid[4 * v + u];
+              else id = id_of(v * kSlice + 4 * tid + u);
+              put(p, id, kk);
+            }
+          }
+          gb += is_gt;
+          eb += is_eq;
+        }
       }
     }
   }
   if (staged) {
     __syncthreads();
+    const uint32_t *st_k = reinterpret_cast<const uint32_t *>(st_s);
     for (int j = tid; j < k; j += NT) {
       const bool sel = j < k_eff;
       out_i[j] = sel ? st_i[j] : -1;
-      if (out_s) out_s[j] = sel ? st_s[j] : __uint_as_float(kNoScoreBits);  // a NaN marks an empty slot
+      if (out_s) out_s[j] = sel ? key_score(st_k[j]) : __uint_as_float(kNoScoreBits);  // a NaN marks an empty slot
     }
   } else {
     for (int j = k_eff + tid; j < k; j += NT) {
@@ -316,7 +347,6 @@ __device__ __forceinline__ void linear_threshold(const uint32_t (&key)[kPer], in
       // 2a. gather the threshold bin and rank it.  One pass: a ballot per
       //     key, and on the rare non-empty one an LDS atomic reserves its
       //     slots, each key going to its ballot's lanes below it.
-      const uint64_t below = lane ? (~0ull >> (64 - lane)) : 0ull;
 #pragma unroll
       for (int j = 0; j < kPer; ++j) {
         if (!live(j)) continue;  // uniform: the ballot takes the comparison itself
@@ -326,7 +356,7 @@ __device__ __forceinline__ void linear_threshold(const uint32_t (&key)[kPer], in
           int pos = 0;
           if (lane == 0) pos = atomicAdd(n_bin, (int)__popcll(mk));
           pos = __builtin_amdgcn_readfirstlane(pos);
-          if (in) bin_keys[pos + __popcll(mk & below)] = key[j];
+          if (in) bin_keys[lanes_below(mk, pos)] = key[j];
         }
       }
       __syncthreads();

@@ -42,15 +42,16 @@ def test_graph_replays_match_eager():
     win = win.to(DEV)
     s0 = torch.full((w.B,), w.T - w.n_win, dtype=torch.int32, device=DEV)
 
-    # two rows of 70,000 scores (m = 1: entry j visible when j <= position)
-    LN, LK = 70000, 500
+    # two rows of 1,048,576 scores (m = 1: entry j visible when j <= position):
+    # few rows this long take the multi-workgroup radix selection
+    LN, LK = 1 << 20, 2048
     long_sc = normal_f32(77, TensorId.W, (2, LN)).to(DEV).view(2, 1, LN)
     long_cache = csa.Cache(2, LN, 1, 0, planes=dict(
         nope=torch.zeros(2, 1, 256, dtype=torch.uint8, device=DEV),
         nscale=torch.zeros(2, 1, 16, dtype=torch.uint8, device=DEV),
         rope=torch.zeros(2, 1, 64, dtype=torch.bfloat16, device=DEV), ikey=None, iscale=None,
         n_entries=torch.full((2,), LN, dtype=torch.int32, device=DEV)))
-    long_pos = torch.tensor([[LN - 1], [40000]], dtype=torch.int32, device=DEV)
+    long_pos = torch.tensor([[LN - 1], [400000]], dtype=torch.int32, device=DEV)
 
     PB, PN = 8, 64
     sizes = dict(topk=csa.workspace_bytes(csa.WS_TOPK, w.B, 1, w.k, N),

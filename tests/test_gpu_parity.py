@@ -1149,6 +1149,8 @@ TOPK_CASES = [
     ("radix-all-equal", 1, 1, 65536, [65536], 1000, 1e9),
     ("radix-k1", 1, 2, 80000, [80000, 1], 1, 0.01),
     ("radix-k2048", 1, 1, 262144, [262144], 2048, 0.001),
+    ("radix-1m-k2048", 1, 1, 1 << 20, [1 << 20], 2048, 0.001),
+    ("radix-512k-k4096", 2, 1, 1 << 19, [1 << 19, 300001], 4096, 0.1),
     # more two-stage shapes: ragged rows, all equal, a length not a multiple
     # of 4, k above a row's visible count, a crowded threshold value
     ("two-stage-ragged", 3, 1, 32768, [32768, 4097, 5000], 512, 0.1),

@@ -590,22 +590,21 @@ __global__ __launch_bounds__(kRegThreads) void topk_hint_final_kernel(HintArgs a
       k_rem -= ab;
       const uint32_t p12 = ((uint32_t)bin << 11) | (uint32_t)e2;
       if (c2 <= 64) {
-        int mine = 0;
+        // gather the bin's keys: a ballot per key, and on a non-empty one an
+        // LDS atomic reserves its slots
 #pragma unroll
-        for (int j = 0; j < kHintCand; ++j) mine += key[j] != 0u && (key[j] >> 10) == p12;
-        const int winc = wave_incl_scan(mine);
-        const int wtot = __builtin_amdgcn_readlane(winc, 63);
-        int wb = 0;
-        if (wtot > 0) {
-          if (lane == 63) wb = atomicAdd(&n_bin, wtot);
-          wb = __builtin_amdgcn_readlane(wb, 63);
+        for (int j = 0; j < kHintCand; ++j) {
+          const bool in = key[j] != 0u && (key[j] >> 10) == p12;
+          const uint64_t mk = __builtin_amdgcn_ballot_w64(in);
+          if (mk) {
+            int pos = 0;
+            if (lane == 0) pos = atomicAdd(&n_bin, (int)__popcll(mk));
+            pos = __builtin_amdgcn_readfirstlane(pos);
+            if (in) bin_keys[lanes_below(mk, pos)] = key[j];
+          }
         }
-        int pos = wb + winc - mine;
-#pragma unroll
-        for (int j = 0; j < kHintCand; ++j)
-          if (key[j] != 0u && (key[j] >> 10) == p12) bin_keys[pos++] = key[j];
         __syncthreads();
-        rank_gathered<NT>(bin_keys, c2, k_rem, sh, thr, need, n_eq);
+        rank_gathered<NT>(bin_keys, c2, k_rem, sh, hist, thr, need, n_eq);  // the histogram is free now
       } else {
         // a crowded bin: one more pass over bits 9..0
         __syncthreads();

@@ -69,28 +69,41 @@ __device__ __forceinline__ void find_digit(const int (*hist)[kBins], int nh, int
   total = __builtin_amdgcn_readfirstlane(all);
 }
 
-// Wave 0 ranks the c1 (<= 64) keys gathered in bin_keys and publishes the
-// exact threshold key (the k_rem-th largest of them), how many keys equal
-// to it are taken and how many there are; every thread returns them.  One
-// barrier; uses sh[kW .. kW+3).
+// The waves rank the c1 (<= 64) keys gathered in bin_keys together: wave w
+// compares every lane's key with keys w, w + NT/64, ..., the counts (keys
+// greater, keys greater or equal; both below 2^16) meet in part (NT ints),
+// and wave 0 publishes the exact threshold key (the k_rem-th largest of
+// them), how many keys equal to it are taken and how many there are; every
+// thread returns them.  Two barriers; uses sh[kW .. kW+3) and part, which
+// no thread may read or write between the caller's last barrier and the
+// return.
 template <int NT>
-__device__ __forceinline__ void rank_gathered(const uint32_t *bin_keys, int c1, int k_rem, int *sh, uint32_t &thr,
-                                              int &need, int &n_eq) {
+__device__ __forceinline__ void rank_gathered(const uint32_t *bin_keys, int c1, int k_rem, int *sh, int *part,
+                                              uint32_t &thr, int &need, int &n_eq) {
   constexpr int kW = NT / 64;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const uint32_t kl = lane < c1 ? bin_keys[lane] : 0u;
+  int gt = 0, ge = 0;
+  for (int j = wave; j < c1; j += kW) {
+    const uint32_t kj = (uint32_t)__builtin_amdgcn_readlane((int)kl, j);
+    gt += kj > kl;
+    ge += kj >= kl;
+  }
+  part[wave * 64 + lane] = gt | (ge << 16);
+  __syncthreads();
   if (wave == 0) {
-    const uint32_t kl = lane < c1 ? bin_keys[lane] : 0u;
-    int gt = 0, ge = 0;
-    for (int j = 0; j < c1; ++j) {
-      const uint32_t kj = (uint32_t)__builtin_amdgcn_readlane((int)kl, j);
-      gt += kj > kl;
-      ge += kj >= kl;
+    int g = 0, e = 0;
+#pragma unroll
+    for (int w = 0; w < kW; ++w) {
+      const int v = part[w * 64 + lane];
+      g += v & 0xFFFF;
+      e += v >> 16;
     }
-    if (lane < c1 && gt < k_rem && k_rem <= ge) {  // every lane holding the threshold key agrees
+    if (lane < c1 && g < k_rem && k_rem <= e) {  // every lane holding the threshold key agrees
       sh[kW] = (int)kl;
-      sh[kW + 1] = k_rem - gt;
-      sh[kW + 2] = ge - gt;
+      sh[kW + 1] = k_rem - g;
+      sh[kW + 2] = e - g;
     }
   }
   __syncthreads();
@@ -360,7 +373,7 @@ __device__ __forceinline__ void linear_threshold(const uint32_t (&key)[kPer], in
         }
       }
       __syncthreads();
-      rank_gathered<NT>(bin_keys, c1, k_rem, sh, thr, need, n_eq);
+      rank_gathered<NT>(bin_keys, c1, k_rem, sh, hist, thr, need, n_eq);  // the histogram is free now
     } else {
       // 2b. a crowded bin (many equal or nearly equal scores): radix passes
       //     over the keys of that bin, bits 31..21, 20..10 and 9..0

@@ -561,10 +561,14 @@ __global__ __launch_bounds__(kRegThreads) void topk_hint_final_kernel(HintArgs a
   if (tid < kHintBins / 4)  // the hint is left zero for the next indexer launch
     *reinterpret_cast<uint4 *>(a.hint + row * kHintBins + 4 * tid) = uint4{0u, 0u, 0u, 0u};
   if (ok) {
+    // the slice of element i is the same in the whole wave: a 4*NT-element
+    // step holds whole slices, and a slice spans kHintSlot/256 waves
+    static_assert((4 * NT) % kHintSlot == 0 && kHintSlot % 256 == 0, "slices of whole waves");
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 #pragma unroll
     for (int j = 0; j < kHintCand; ++j) {
       const int i = (j >> 2) * (4 * NT) + 4 * tid + (j & 3);
-      const int s = i / kHintSlot;
+      const int s = (j >> 2) * (4 * NT / kHintSlot) + wave / (kHintSlot / 256);  // i / kHintSlot
       int c = 0;
 #pragma unroll
       for (int t = 0; t < kMaxSl; ++t) c = s == t ? cnt_s[t] : c;

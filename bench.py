@@ -736,6 +736,10 @@ def csa2_leg(L=8, K=64):
     sc_b = torch.empty(w.B, 1, w.k, dtype=torch.float32, device=dev)
     tws_b = csa.workspace_bytes(csa.WS_TOPK, w.B, 1, w.k, w.N)
     tws = torch.empty(max(tws_b, 16), dtype=torch.uint8, device=dev)
+    # the fused scores + top-k call (its indexer launch also clears the radix
+    # selection's histograms, one launch fewer than the two calls)
+    itws = torch.zeros(max(csa.workspace_bytes(csa.WS_INDEX_TOPK, w.B, 1, w.k, w.N, 0), 16), dtype=torch.uint8,
+                       device=dev)
     aws = torch.empty(max(csa.workspace_bytes(csa.WS_SPARSE_ATTN, w.B, 1, w.H, w.k, w.n_win), 16), dtype=torch.uint8,
                       device=dev)
     bws = torch.empty(max(csa.workspace_bytes(csa.WS_SPARSE_ATTN, w.B, 1, w.H, w.k_b, w.n_win), 16),
@@ -743,8 +747,7 @@ def csa2_leg(L=8, K=64):
 
     def layer_a(l):
         c = caches[l]
-        csa.index_scores(c, qa[l]["qI"], qa[l]["w"], qa[l]["q_pos"], scores=sc_a)
-        csa.topk(c, sc_a, qa[l]["q_pos"], w.k, out=ia[l], ws=tws if tws_b else None)
+        csa.index_topk(c, qa[l]["qI"], qa[l]["w"], qa[l]["q_pos"], w.k, ws=itws, out=ia[l])
         csa.sparse_attn(c, qa[l]["q"], qa[l]["q_pos"], ia[l], x_win, s0, w.n_win, w.softmax_scale,
                         out_dtype=torch.bfloat16, ws=aws, out=oa[l], lse=la[l])
 
@@ -760,6 +763,9 @@ def csa2_leg(L=8, K=64):
     ms_b = ms - ms_a
     # stage by stage (each a graph of K launches over the rotating layers)
     stage_us = {
+        "a_index_topk": _graph_ms(lambda: [csa.index_topk(caches[i % L], qa[i % L]["qI"], qa[i % L]["w"],
+                                                          qa[i % L]["q_pos"], w.k, ws=itws, out=ia[i % L])
+                                           for i in range(K)], K),
         "a_index_scores": _graph_ms(lambda: [csa.index_scores(caches[i % L], qa[i % L]["qI"], qa[i % L]["w"],
                                                               qa[i % L]["q_pos"], scores=sc_a) for i in range(K)], K),
         "a_topk": _graph_ms(lambda: [csa.topk(caches[i % L], sc_a, qa[i % L]["q_pos"], w.k, out=ia[i % L],

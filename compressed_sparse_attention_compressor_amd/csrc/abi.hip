@@ -342,6 +342,24 @@ int csa_topk(const csa_cache_t *cache, const float *scores, const int32_t *q_pos
       csa::launch_topk(view_of(cache), scores, Ns, q_pos, Q, cand, C, k, idx_out, score_out, ws, stream));
 }
 
+// A full scan's scores, then its top-k from tws (topk_ws_bytes of it).  When
+// the top-k is the radix selection, the indexer launch clears the radix
+// histograms as a side job and the selection skips its clearing launch.
+// The caller has applied every argument and workspace check of both calls.
+static hipError_t full_scan_topk(const csa_cache_t *cache, const uint8_t *q_idx, const float *w_idx, int H_I,
+                                 const int32_t *q_pos, int Q, int k, float *scores, int32_t *idx_out,
+                                 float *score_out, void *tws, hipStream_t stream) {
+  const csa::CacheView v = view_of(cache);
+  if (cache->N_cap == 0) return csa::launch_topk(v, scores, 0, q_pos, Q, nullptr, 0, k, idx_out, score_out, tws, stream);
+  const size_t zb = csa::topk_radix_zero_bytes(cache->B, Q, cache->N_cap, k);
+  const bool fold = zb > 0 && tws && csa::index_can_zero(Q, false);
+  hipError_t e = csa::launch_index_scores(v, q_idx, w_idx, H_I, q_pos, Q, nullptr, 0, scores, stream, nullptr,
+                                          fold ? tws : nullptr, fold ? zb : 0);
+  if (e == hipSuccess)
+    e = csa::launch_topk(v, scores, cache->N_cap, q_pos, Q, nullptr, 0, k, idx_out, score_out, tws, stream, fold);
+  return e;
+}
+
 int csa_index_topk(const csa_cache_t *cache, const uint8_t *q_idx, const float *w_idx, int H_I,
                    const int32_t *q_pos, int Q, const int32_t *cand, int C, int k, int32_t *idx_out,
                    float *score_out, void *ws, size_t ws_bytes, hipStream_t stream) {
@@ -365,9 +383,11 @@ int csa_index_topk(const csa_cache_t *cache, const uint8_t *q_idx, const float *
     return status_of(e);
   }
   const size_t tbytes = need - align256(sbytes);
+  void *tws = tbytes ? reinterpret_cast<char *>(ws) + align256(sbytes) : nullptr;
+  if (!cand)
+    return status_of(full_scan_topk(cache, q_idx, w_idx, H_I, q_pos, Q, k, scores, idx_out, score_out, tws, stream));
   st = csa_index_scores(cache, q_idx, w_idx, H_I, q_pos, Q, cand, C, scores, sbytes, stream);
   if (st) return st;
-  void *tws = tbytes ? reinterpret_cast<char *>(ws) + align256(sbytes) : nullptr;
   return csa_topk(cache, scores, q_pos, Q, cand, C, k, idx_out, score_out, tws, tbytes, stream);
 }
 
@@ -706,14 +726,16 @@ int csa2_layer_stack(const csa2_layer_t *layers, int n_layers, const int32_t *q_
     const StackStep &s = steps[i];
     float *scores = reinterpret_cast<float *>(ws);
     void *rest = s.ws_rest ? reinterpret_cast<char *>(ws) + s.ws_scores : nullptr;
-    if (l.mode != CSA2_REUSE) {
+    if (l.mode == CSA2_FULL) {
+      st = status_of(full_scan_topk(s.cache, l.q_idx, l.w_idx, l.H_I, q_pos, Q, l.k, scores, l.idx_out, nullptr,
+                                    s.ws_rest ? rest : nullptr, stream));
+    } else if (l.mode != CSA2_REUSE) {
       st = csa_index_scores(s.cache, l.q_idx, l.w_idx, l.H_I, q_pos, Q, s.cand, s.C, scores, s.ws_scores, stream);
       if (st == CSA_OK)
         st = csa_topk(s.cache, scores, q_pos, Q, s.cand, s.C, l.k, l.idx_out, nullptr, rest, s.ws_rest, stream);
-      if (st == CSA_OK && l.mode == CSA2_FULL && l.pool_blocks > 0)
-        st = csa_index_pool(s.cache, scores, q_pos, Q, l.pool_block, l.pool_blocks, l.pool_out, rest, s.ws_rest,
-                            stream);
     }
+    if (st == CSA_OK && l.mode == CSA2_FULL && l.pool_blocks > 0)
+      st = csa_index_pool(s.cache, scores, q_pos, Q, l.pool_block, l.pool_blocks, l.pool_out, rest, s.ws_rest, stream);
     if (st == CSA_OK)
       st = csa_sparse_attn(s.cache, l.q, l.H, q_pos, Q, s.sel, s.k, l.swa, l.swa_pos0, l.S, l.n_win,
                            l.softmax_scale, l.rope_base, l.out_dtype, l.out, l.lse, rest, s.ws_rest, stream);

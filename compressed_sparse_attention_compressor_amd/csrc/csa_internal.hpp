@@ -28,9 +28,14 @@ hipError_t launch_compress(const uint16_t *x, int64_t x_stride_b, const uint16_t
 // hint: null, or kHintBins uint32 per row (zero on entry) that a one-query
 // full scan (Q < 4) fills with the row's score histogram for
 // launch_topk_hint; other shapes leave it untouched.
+// zero / zero_bytes: null, or 16-byte-aligned bytes (a multiple of 16) that
+// the same launch clears for the next one; only the shapes index_can_zero()
+// accepts (others return hipErrorInvalidValue and launch nothing).
+bool index_can_zero(int Q, bool cand);
 hipError_t launch_index_scores(const CacheView &c, const uint8_t *q_idx, const float *w_idx, int H_I,
                                const int32_t *q_pos, int Q, const int32_t *cand, int C, float *scores,
-                               hipStream_t stream, uint32_t *hint = nullptr);
+                               hipStream_t stream, uint32_t *hint = nullptr, void *zero = nullptr,
+                               size_t zero_bytes = 0);
 
 // Decode append fused with the indexer: csa_compress of one entry per
 // sequence (entry `entry`, from rows 0..m-1 of the x/z chunk) followed by
@@ -53,10 +58,16 @@ struct TopkPlan {
   bool radix = false;  // multi-workgroup radix selection (few, long rows)
 };
 TopkPlan topk_plan(int B, int Q, int Ns, int k);
+// Bytes at the start of a radix plan's workspace that must be zero when
+// its selection starts (0 for other plans).
+size_t topk_radix_zero_bytes(int B, int Q, int Ns, int k);
 
+// prezeroed: the first topk_radix_zero_bytes() of ws are already zero (an
+// earlier launch on the stream cleared them), so the radix selection skips
+// its clearing launch.
 hipError_t launch_topk(const CacheView &c, const float *scores, int Ns, const int32_t *q_pos, int Q,
                        const int32_t *cand, int C, int k, int32_t *idx_out, float *score_out, void *ws,
-                       hipStream_t stream);
+                       hipStream_t stream, bool prezeroed = false);
 
 // Top-k of full-scan rows from their scores and the indexer's histogram
 // hint, for the shapes topk_hint_fits() accepts (few rows of at most 32,768

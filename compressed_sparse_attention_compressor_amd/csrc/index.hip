@@ -352,12 +352,21 @@ __device__ __forceinline__ void index_body(
   }
 }
 
+// zero4 / n_zero4: a side job, 16-byte words of the next launch's workspace
+// that must start at zero (the radix top-k's histograms), cleared by the
+// whole grid before its own work, so that the next launch needs no
+// clearing launch of its own.
 template <int HT, int QB, bool kCand>
 __global__ __launch_bounds__(kIdxThreads) void index_scores_kernel(
     const uint8_t *__restrict__ ikey, const uint8_t *__restrict__ iscale, const int32_t *__restrict__ n_entries,
     int N_cap, int d_idx, int m, const uint8_t *__restrict__ q_idx, const float *__restrict__ w_idx, int H_I,
     const int32_t *__restrict__ q_pos, int Q, const int32_t *__restrict__ cand, int C, float *__restrict__ scores,
-    int Ns, uint32_t *flags, uint32_t *hint) {
+    int Ns, uint32_t *flags, uint32_t *hint, uint4 *zero4, int64_t n_zero4) {
+  if (zero4) {
+    const int64_t wg = ((int64_t)blockIdx.z * gridDim.y + blockIdx.y) * gridDim.x + blockIdx.x;
+    const int64_t stride = (int64_t)gridDim.x * gridDim.y * gridDim.z * kIdxThreads;
+    for (int64_t i = wg * kIdxThreads + threadIdx.x; i < n_zero4; i += stride) zero4[i] = uint4{0u, 0u, 0u, 0u};
+  }
   index_body<HT, QB, kCand>(ikey, iscale, n_entries, N_cap, d_idx, m, q_idx, w_idx, H_I, q_pos, Q, cand, C, scores, Ns,
                             blockIdx.x, blockIdx.y, blockIdx.z, -1, flags, hint);
 }
@@ -674,10 +683,10 @@ hipError_t launch_append_index(const uint16_t *x, int64_t x_stride_b, const uint
 template <int HT, int QB, bool kCand>
 static void launch_idx(dim3 grid, hipStream_t stream, const CacheView &c, const uint8_t *q_idx, const float *w_idx,
                        int H_I, const int32_t *q_pos, int Q, const int32_t *cand, int C, float *scores, int Ns,
-                       uint32_t *hint = nullptr) {
+                       uint32_t *hint = nullptr, void *zero = nullptr, size_t zero_bytes = 0) {
   index_scores_kernel<HT, QB, kCand><<<grid, kIdxThreads, 0, stream>>>(
       c.ikey, c.iscale, c.n_entries, c.N_cap, c.d_idx, c.m, q_idx, w_idx, H_I, q_pos, Q, cand, C, scores, Ns, c.flags,
-      hint);
+      hint, reinterpret_cast<uint4 *>(zero), (int64_t)(zero_bytes / 16));
 }
 
 // ---------------------------------------------------------------------------
@@ -868,9 +877,14 @@ static void launch_prefill(const CacheView &c, const uint8_t *q_idx, const float
         c.ikey, c.iscale, c.n_entries, c.N_cap, c.m, q_idx, w_idx, H_I, q_pos, Q, scores, n_qblk, n_chunk, c.flags);
 }
 
+// The launch shapes that can clear words for the next launch (one-query
+// full scans; see index_scores_kernel).
+bool index_can_zero(int Q, bool cand) { return !cand && Q > 0 && Q < 4; }
+
 template <int HT>
 static void dispatch_idx(const CacheView &c, const uint8_t *q_idx, const float *w_idx, int H_I, const int32_t *q_pos,
-                         int Q, const int32_t *cand, int C, float *scores, hipStream_t stream, uint32_t *hint) {
+                         int Q, const int32_t *cand, int C, float *scores, hipStream_t stream, uint32_t *hint,
+                         void *zero, size_t zero_bytes) {
   if (cand) {
     const int Ns = C;
     dim3 grid((C + kIdxWGEntries - 1) / kIdxWGEntries, Q, c.B);
@@ -882,19 +896,23 @@ static void dispatch_idx(const CacheView &c, const uint8_t *q_idx, const float *
     launch_idx<HT, 4, false>(grid, stream, c, q_idx, w_idx, H_I, q_pos, Q, nullptr, 0, scores, c.N_cap);
   } else {
     dim3 grid((c.N_cap + kIdxWGEntries - 1) / kIdxWGEntries, Q, c.B);
-    launch_idx<HT, 1, false>(grid, stream, c, q_idx, w_idx, H_I, q_pos, Q, nullptr, 0, scores, c.N_cap, hint);
+    launch_idx<HT, 1, false>(grid, stream, c, q_idx, w_idx, H_I, q_pos, Q, nullptr, 0, scores, c.N_cap, hint, zero,
+                             zero_bytes);
   }
 }
 
 hipError_t launch_index_scores(const CacheView &c, const uint8_t *q_idx, const float *w_idx, int H_I,
                                const int32_t *q_pos, int Q, const int32_t *cand, int C, float *scores,
-                               hipStream_t stream, uint32_t *hint) {
+                               hipStream_t stream, uint32_t *hint, void *zero, size_t zero_bytes) {
+  if (zero && (!index_can_zero(Q, cand != nullptr) || (zero_bytes & 15) != 0 ||
+               (reinterpret_cast<uintptr_t>(zero) & 15) != 0))
+    return hipErrorInvalidValue;
   if (H_I <= 16)
-    dispatch_idx<1>(c, q_idx, w_idx, H_I, q_pos, Q, cand, C, scores, stream, hint);
+    dispatch_idx<1>(c, q_idx, w_idx, H_I, q_pos, Q, cand, C, scores, stream, hint, zero, zero_bytes);
   else if (H_I <= 32)
-    dispatch_idx<2>(c, q_idx, w_idx, H_I, q_pos, Q, cand, C, scores, stream, hint);
+    dispatch_idx<2>(c, q_idx, w_idx, H_I, q_pos, Q, cand, C, scores, stream, hint, zero, zero_bytes);
   else
-    dispatch_idx<4>(c, q_idx, w_idx, H_I, q_pos, Q, cand, C, scores, stream, hint);
+    dispatch_idx<4>(c, q_idx, w_idx, H_I, q_pos, Q, cand, C, scores, stream, hint, zero, zero_bytes);
   return hipGetLastError();
 }
 

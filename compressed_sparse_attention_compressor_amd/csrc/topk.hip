@@ -912,7 +912,7 @@ __global__ __launch_bounds__(kRegThreads) void rx_place_kernel(RxArgs a) {
 }
 
 static hipError_t launch_radix(const CacheView &c, const float *scores, int Ns, const int32_t *q_pos, int Q, int k,
-                               int32_t *idx_out, float *score_out, void *ws, hipStream_t stream) {
+                               int32_t *idx_out, float *score_out, void *ws, hipStream_t stream, bool prezeroed) {
   const int rows = c.B * Q;
   const int nsl = (Ns + kRxSlice - 1) / kRxSlice;
   RxArgs a;
@@ -932,8 +932,8 @@ static hipError_t launch_radix(const CacheView &c, const float *scores, int Ns, 
   a.desc = a.counts + (size_t)rows * nsl * 2;
   a.idx_out = idx_out;
   a.score_out = score_out;
-  const int nz = rows * (2048 + 2048 + 1024);
-  rx_zero_kernel<<<(nz + 255) / 256, 256, 0, stream>>>(a.hist1, nz);
+  const int nz = rows * (2048 + 2048 + 1024);  // the histograms, topk_radix_zero_bytes()
+  if (!prezeroed) rx_zero_kernel<<<(nz + 255) / 256, 256, 0, stream>>>(a.hist1, nz);
   const dim3 grid(Q * nsl, c.B);
   rx_hist_kernel<1><<<grid, kRegThreads, 0, stream>>>(a);
   rx_hist_kernel<2><<<grid, kRegThreads, 0, stream>>>(a);
@@ -999,6 +999,10 @@ static void launch_one(const CacheView &c, const float *scores, int Ns, int len,
                                                                  C, k, idx_out, score_out);
 }
 
+size_t topk_radix_zero_bytes(int B, int Q, int Ns, int k) {
+  return topk_plan(B, Q, Ns, k).radix ? (size_t)B * Q * (2048 + 2048 + 1024) * sizeof(int) : 0;
+}
+
 bool topk_hint_fits(int B, int Q, int Ns, int k) {
   return (int64_t)B * Q < 256 && Ns > 0 && Ns <= kRegN && k > 0;
 }
@@ -1039,9 +1043,9 @@ hipError_t launch_topk_hint(const CacheView &c, const float *scores, int Ns, con
 
 hipError_t launch_topk(const CacheView &c, const float *scores, int Ns, const int32_t *q_pos, int Q,
                        const int32_t *cand, int C, int k, int32_t *idx_out, float *score_out, void *ws,
-                       hipStream_t stream) {
+                       hipStream_t stream, bool prezeroed) {
   const TopkPlan p = cand ? TopkPlan{1, Ns, 0} : topk_plan(c.B, Q, Ns, k);
-  if (p.radix) return launch_radix(c, scores, Ns, q_pos, Q, k, idx_out, score_out, ws, stream);
+  if (p.radix) return launch_radix(c, scores, Ns, q_pos, Q, k, idx_out, score_out, ws, stream, prezeroed);
   if (p.nsl == 1) {
     launch_one(c, scores, Ns, Ns, q_pos, Q, cand, C, k, idx_out, score_out, 1, Ns, stream);
     return hipGetLastError();

@@ -663,27 +663,40 @@ def test_layer_stack_many_queries():
                 assert row_rel_err(g, o).max() <= TOL[torch.float32], f"layer {i} b={b} t={t}"
 
 
-def test_layer_stack_parity():
-    """An 8-layer CSA2 stack through csa2_layer_stack ([V4.1] Fig. 4 modes,
-    Fig. 5 pool): Full with a pool, Reuse, Reindex over the pool, Reuse, a
-    second Full on another cache, Reindex over its selection, Reindex by a
-    full scan, Reuse.  Checked stage by stage: each layer's selection
-    against the oracle's (up to near-ties) given the GPU's upstream pool or
-    selection, the pool's blocks against the oracle's block maxima, and every
-    layer's attention against the oracle over the selection that layer used."""
+STACK_CASES = [
+    # Full with a pool, Reuse, Reindex over the pool, Reuse, a second Full on
+    # another cache, Reindex over its selection, Reindex by a full scan, Reuse
+    ("eight-layers", Workload("st", 13, B=3, T=16384, m=4, d_idx=128, H_I=32, k=64, H=64, n_win=64),
+     lambda N: [[N, N - 5, 301], [N - 100, N, 500]],
+     [dict(mode=csa.CSA2_FULL, c=0, k=64, pool_block=8, pool_blocks=16), dict(mode=csa.CSA2_REUSE),
+      dict(mode=csa.CSA2_REINDEX, k=32, cand=csa.CAND_AUTO), dict(mode=csa.CSA2_REUSE),
+      dict(mode=csa.CSA2_FULL, c=1, k=48), dict(mode=csa.CSA2_REINDEX, k=16, cand=csa.CAND_SELECTION),
+      dict(mode=csa.CSA2_REINDEX, k=40, cand=csa.CAND_SCAN), dict(mode=csa.CSA2_REUSE)]),
+    # rows of 70,000 entries: the Full layers' selections take the radix
+    # path, whose histograms the indexer launch clears
+    ("long-rows-radix", Workload("sl", 14, B=2, T=280000, m=4, d_idx=128, H_I=32, k=64, H=64, n_win=64),
+     lambda N: [[N, N - 7], [N - 100, N]],
+     [dict(mode=csa.CSA2_FULL, c=0, k=64, pool_block=8, pool_blocks=16),
+      dict(mode=csa.CSA2_REINDEX, k=32, cand=csa.CAND_AUTO), dict(mode=csa.CSA2_FULL, c=1, k=48),
+      dict(mode=csa.CSA2_REUSE)]),
+]
+
+
+@pytest.mark.parametrize("name,w,ents_of,spec", STACK_CASES, ids=[c[0] for c in STACK_CASES])
+def test_layer_stack_parity(name, w, ents_of, spec):
+    """A CSA2 stack through csa2_layer_stack ([V4.1] Fig. 4 modes, Fig. 5
+    pool).  Checked stage by stage: each layer's selection against the
+    oracle's (up to near-ties) given the GPU's upstream pool or selection,
+    the pool's blocks against the oracle's block maxima, and every layer's
+    attention against the oracle over the selection that layer used."""
     import dataclasses
-    w = Workload("st", 13, B=3, T=16384, m=4, d_idx=128, H_I=32, k=64, H=64, n_win=64)
     N = w.N
-    ents = [[N, N - 5, 301], [N - 100, N, 500]]
+    ents = ents_of(N)
     caches_np = [synthetic_cache(w), synthetic_cache(dataclasses.replace(w, cfg=w.cfg + 50))]
     caches = [_gpu_cache(pl, w.B, N, w.m, w.d_idx, ne) for pl, ne in zip(caches_np, ents)]
     pos = torch.full((w.B, 1), w.T - 1, dtype=torch.int32, device=DEV)
     swa, _ = raw_rows(w, w.T - w.n_win, w.T)
     s0 = torch.full((w.B,), w.T - w.n_win, dtype=torch.int32, device=DEV)
-    spec = [dict(mode=csa.CSA2_FULL, c=0, k=64, pool_block=8, pool_blocks=16), dict(mode=csa.CSA2_REUSE),
-            dict(mode=csa.CSA2_REINDEX, k=32, cand=csa.CAND_AUTO), dict(mode=csa.CSA2_REUSE),
-            dict(mode=csa.CSA2_FULL, c=1, k=48), dict(mode=csa.CSA2_REINDEX, k=16, cand=csa.CAND_SELECTION),
-            dict(mode=csa.CSA2_REINDEX, k=40, cand=csa.CAND_SCAN), dict(mode=csa.CSA2_REUSE)]
     layers, qs = [], []
     for i, sp in enumerate(spec):
         q = queries(dataclasses.replace(w, cfg=w.cfg + 100 * (i + 1)))

@@ -51,15 +51,18 @@ __device__ __forceinline__ uint32_t e4m3_over56(uint4 v) {
   return o(v.x) | o(v.y) | o(v.z) | o(v.w);
 }
 
-// Four E4M3 codes times 2^3, exactly, for magnitudes up to 56: codes with an
-// exponent gain 3 in it; a subnormal m 2^-9 (m = 1..7) becomes the normal
-// code of m 2^-6, looked up in an 8-byte table with v_perm_b32.
+// Four E4M3 codes times 2^3, exactly, for magnitudes up to 56 (the products
+// stay within E4M3's range, 448, and subnormal codes m 2^-9 become the normal
+// m 2^-6): decoded to fp32 times 8 and encoded again, two codes per
+// conversion, four instructions for the word.
 __device__ __forceinline__ uint32_t e4m3_times8(uint32_t w) {
-  const uint32_t mag = w & 0x7F7F7F7Fu;
-  const uint32_t nrm = ((mag & 0x78787878u) + 0x78787878u) & 0x80808080u;  // 0x80 where the exponent is nonzero
-  const uint32_t nmask = (nrm >> 7) * 0xFFu;
-  const uint32_t sub = __builtin_amdgcn_perm(0x1E1C1A18u, 0x14100800u, mag & 0x07070707u);
-  return (w & 0x80808080u) | ((mag + 0x18181818u) & nmask) | (sub & ~nmask);
+  typedef float v2f __attribute__((ext_vector_type(2)));
+  typedef short v2s __attribute__((ext_vector_type(2)));
+  const v2f lo = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w, 8.0f, false);  // codes 0 and 1, times 8
+  const v2f hi = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w, 8.0f, true);   // codes 2 and 3
+  v2s r = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(v2s{0, 0}, lo.x, lo.y, 1.0f, false);
+  r = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(r, hi.x, hi.y, 1.0f, true);
+  return __builtin_bit_cast(uint32_t, r);
 }
 
 __device__ __forceinline__ uint4 e4m3_times8(uint4 v) {
@@ -87,7 +90,8 @@ __device__ __forceinline__ int e4m3_rescale_piece(uint4 &v) {
 __device__ __forceinline__ int e4m3_rescale_fragment(v8i &A, int g, int r) {
   const uint4 lo = {(uint32_t)A[0], (uint32_t)A[1], (uint32_t)A[2], (uint32_t)A[3]};
   const uint4 hi = {(uint32_t)A[4], (uint32_t)A[5], (uint32_t)A[6], (uint32_t)A[7]};
-  const uint64_t bl = __ballot(e4m3_over56(lo) != 0u), bh = __ballot(e4m3_over56(hi) != 0u);
+  const uint64_t bl = __builtin_amdgcn_ballot_w64(e4m3_over56(lo) != 0u);
+  const uint64_t bh = __builtin_amdgcn_ballot_w64(e4m3_over56(hi) != 0u);
   // bit 32 j + r: block j (of the low halves) resp. 2 + j (high) of head r is over
   const uint64_t fl = bl | (bl >> 16), fh = bh | (bh >> 16);
   const int sh = 32 * (g >> 1) + r;

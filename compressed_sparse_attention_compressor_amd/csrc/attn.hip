@@ -753,49 +753,52 @@ __global__ __launch_bounds__(HG * 128) void attn_kernel(AttnArgs a) {
 }
 
 // Combines the splits: output = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s
-// with M the largest m_s.  One thread per 8 channels of one (query, head):
-// 16-byte loads of bf16 partials (8-byte halves of fp32 ones), the split
-// weights formed once per thread, and the loads over splits issued together
-// (up to kU at a time).  Partials are fp32, or bf16 when the
-// result is bf16.
+// with M the largest m_s.  kT adjacent lanes share one (query, head, group
+// of 8 channels): lane t takes splits t, t + kT, t + 2 kT, ... and keeps its
+// own (max, sum, 8 weighted channels); the kT states are then combined by
+// DPP moves inside the lane quad (exchange with lane ^ 1, then lane ^ 2),
+// and lane t = 0 writes.  Each lane issues the loads of up to kU of its
+// splits in one round: 16-byte loads of bf16 partials (8-byte halves of
+// fp32 ones) and the (max, sum) pairs, the maximum formed from the loaded
+// values.  With many splits (the dense 1M step's 29) the lanes of a group
+// wait on a quarter of the loads each, and the grid has kT times the
+// workgroups.  Partials are fp32, or bf16 when the result is bf16.
 constexpr int kMergeThreads = 256;
-// kU: splits whose loads go out together (8, or 16 / 32 for bf16 partials of
-// many splits, so that the HCA step's 29 splits take one memory round).
-// bf16 partials stay packed in registers until they are weighted.
-template <bool kBf16, int kU>
+template <bool kBf16, int kU, int kT>
 __global__ __launch_bounds__(kMergeThreads) void attn_merge_kernel(const float *__restrict__ ws_o,
                                                                    const float *__restrict__ ws_ml, int nsplit, int H,
                                                                    int64_t n_items, void *out, float *lse, int rows,
                                                                    int xcd, int wg_per_row) {
+  static_assert(kT == 1 || kT == 2 || kT == 4, "lane groups within a DPP quad");
+  static_assert(kMergeThreads % kT == 0, "groups never straddle a workgroup");
   constexpr int kGroups = kD / 8;
-  int64_t item;  // (qrow, head, channel group of 8)
+  const int t = threadIdx.x % kT;
+  int64_t item;  // (qrow, head, channel group of 8); the same for the kT lanes of a group
   if (xcd) {
     // the row's splits ran on XCD row % 8 (xcd_slot): merge it there
     int row, part;
     if (!xcd_slot(blockIdx.x, wg_per_row, rows, row, part)) return;
-    const int in_row = part * kMergeThreads + threadIdx.x;
-    if (in_row >= H * kGroups) return;
+    const int in_row = (part * kMergeThreads + threadIdx.x) / kT;
+    if (in_row >= H * kGroups) return;  // whole groups only
     item = (int64_t)row * H * kGroups + in_row;
   } else {
-    item = (int64_t)blockIdx.x * kMergeThreads + threadIdx.x;
+    item = ((int64_t)blockIdx.x * kMergeThreads + threadIdx.x) / kT;
     if (item >= n_items) return;
   }
   const int64_t qh = item / kGroups;  // qrow * H + head
   const int c8 = (int)(item % kGroups) * 8;
   const int64_t qrow = qh / H, hh = qh % H;
   auto pr_of = [&](int s) { return (qrow * nsplit + s) * H + hh; };
-  // One round of loads for up to kU splits: every split's (m, l) and partial
-  // row are issued together and the maximum is formed from the loaded values
-  // (a separate pass for the maximum would wait on memory twice).
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   float L = 0.f;
   float M = -INFINITY;
-  for (int s0 = 0; s0 < nsplit; s0 += kU) {
+  const int n_per = (nsplit + kT - 1) / kT;  // splits of the busiest lane
+  for (int u0 = 0; u0 < n_per; u0 += kU) {
     float2 ml[kU];
     uint4 raw[kBf16 ? kU : 2 * kU];
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
-      const int64_t pr = pr_of(min(s0 + u, nsplit - 1));
+      const int64_t pr = pr_of(min(t + kT * (u0 + u), nsplit - 1));
       ml[u] = *reinterpret_cast<const float2 *>(ws_ml + pr * 2);
       if (kBf16) {
         raw[u] = *reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(ws_o) + pr * kD + c8);
@@ -805,11 +808,11 @@ __global__ __launch_bounds__(kMergeThreads) void attn_merge_kernel(const float *
       }
     }
     // running maximum over the splits seen so far; earlier sums are rescaled
-    // when it moves (only with more than kU splits)
+    // when it moves (only with more than kU splits per lane)
     float Mn = M;
 #pragma unroll
     for (int u = 0; u < kU; ++u)
-      if (s0 + u < nsplit) Mn = fmaxf(Mn, ml[u].x);
+      if (t + kT * (u0 + u) < nsplit) Mn = fmaxf(Mn, ml[u].x);
     if (Mn != -INFINITY) {
       const float r = M == -INFINITY ? 0.f : exp2f(M - Mn);
       L *= r;
@@ -817,7 +820,7 @@ __global__ __launch_bounds__(kMergeThreads) void attn_merge_kernel(const float *
       for (int j = 0; j < 8; ++j) acc[j] *= r;
 #pragma unroll
       for (int u = 0; u < kU; ++u) {
-        const float wgt = (s0 + u < nsplit && ml[u].x != -INFINITY) ? exp2f(ml[u].x - Mn) : 0.f;
+        const float wgt = (t + kT * (u0 + u) < nsplit && ml[u].x != -INFINITY) ? exp2f(ml[u].x - Mn) : 0.f;
         L += wgt * (wgt != 0.f ? ml[u].y : 0.f);
         float v[8];
         if (kBf16) {
@@ -839,6 +842,23 @@ __global__ __launch_bounds__(kMergeThreads) void attn_merge_kernel(const float *
       M = Mn;
     }
   }
+  // The kT lane states combined: quad_perm [1,0,3,2] (lane ^ 1), then
+  // [2,3,0,1] (lane ^ 2).  A state with no key (M = -inf) weighs 0.
+  auto combine = [&](auto ctrl_tag) __attribute__((always_inline)) {
+    constexpr int kCtrl = decltype(ctrl_tag)::value;
+    auto mv = [](float x) { return __int_as_float(dpp_i32<kCtrl>(__float_as_int(x))); };
+    const float Mp = mv(M), Lp = mv(L);
+    const float Mn = fmaxf(M, Mp);
+    const float ws = M == -INFINITY ? 0.f : exp2f(M - Mn);
+    const float wp = Mp == -INFINITY ? 0.f : exp2f(Mp - Mn);
+    L = L * ws + Lp * wp;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[j] = acc[j] * ws + mv(acc[j]) * wp;
+    M = Mn;
+  };
+  if (kT >= 2) combine(std::integral_constant<int, 0xB1>{});
+  if (kT >= 4) combine(std::integral_constant<int, 0x4E>{});
+  if (t != 0) return;
   const float inv = L > 0.f ? 1.f / L : 0.f;
   if (kBf16) {
     uint32_t w4[4];
@@ -955,20 +975,21 @@ hipError_t launch_attention(const CacheView &c, const uint16_t *q, int H, const 
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || sh.nsplit == 1) return e;
   const int64_t n_items = (int64_t)c.B * Q * H * (kD / 8);
-  const int wg_per_row = (H * (kD / 8) + kMergeThreads - 1) / kMergeThreads;
+  // lanes per merged item: the splits spread over 1, 2 or 4 lanes
+  const int lanes = sh.nsplit > 16 ? 4 : (sh.nsplit > 8 ? 2 : 1);
+  const int wg_per_row = (H * (kD / 8) * lanes + kMergeThreads - 1) / kMergeThreads;
   const unsigned nb = a.xcd ? (unsigned)(8 * ((a.rows + 7) / 8) * wg_per_row)
-                            : (unsigned)((n_items + kMergeThreads - 1) / kMergeThreads);
-#define CSA_MERGE(BF, U)                                                                                    \
-  attn_merge_kernel<BF, U><<<nb, kMergeThreads, 0, stream>>>(a.ws_o, a.ws_ml, sh.nsplit, H, n_items, out, lse, \
-                                                             a.rows, a.xcd, wg_per_row)
-  if (out_bf16 && sh.nsplit > 16)
-    CSA_MERGE(true, 32);
-  else if (out_bf16 && sh.nsplit > 8)
-    CSA_MERGE(true, 16);
-  else if (out_bf16)
-    CSA_MERGE(true, 8);
-  else
-    CSA_MERGE(false, 8);
+                            : (unsigned)((n_items * lanes + kMergeThreads - 1) / kMergeThreads);
+#define CSA_MERGE(BF, T)                                                                                       \
+  attn_merge_kernel<BF, 8, T><<<nb, kMergeThreads, 0, stream>>>(a.ws_o, a.ws_ml, sh.nsplit, H, n_items, out, lse, \
+                                                                a.rows, a.xcd, wg_per_row)
+  if (lanes == 4) {
+    if (out_bf16) CSA_MERGE(true, 4); else CSA_MERGE(false, 4);
+  } else if (lanes == 2) {
+    if (out_bf16) CSA_MERGE(true, 2); else CSA_MERGE(false, 2);
+  } else {
+    if (out_bf16) CSA_MERGE(true, 1); else CSA_MERGE(false, 1);
+  }
 #undef CSA_MERGE
   return hipGetLastError();
 }

@@ -1308,6 +1308,15 @@ SPLIT_SHAPE_CASES = [
      [512, 400], None, False),
     ("one-split-h64", Workload("ss4", 63, B=2, T=2048, m=4, d_idx=0, H_I=0, k=48, H=64, n_win=64, Q=128), 512,
      [512, 400], None, False),
+    # one query over 2,000 entries + 128 window rows: 67 splits, the merge
+    # spreading them over 4 lanes with 17 splits each (three rounds of loads
+    # per lane, the running maximum moved between rounds)
+    ("merge-67-splits", Workload("ss5", 64, B=1, T=8100, m=4, d_idx=0, H_I=0, k=0, H=64, n_win=128), 2000, [2000],
+     [[8099]], True),
+    # k = 640 slots of which 100 / 60 hold entries: 21 splits, most of them
+    # without any key (maximum -inf, sum 0) in the 4-lane combine
+    ("merge-empty-splits", Workload("ss6", 65, B=2, T=400, m=4, d_idx=0, H_I=0, k=640, H=32, n_win=32), 100,
+     [100, 60], [[399], [399]], False),
 ]
 
 

@@ -1,7 +1,8 @@
 """The benchmark times the path from HIP graphs.  A graph of one decode step
 (the fused append + indexer, the two-stage top-k, the hierarchical pool,
 split attention and its merge with a bf16 window, the FP8 window encode and
-the attention reading it) and of a radix top-k over long rows is replayed
+the attention reading it, dense attention whose merge spreads its splits
+over four lanes) and of a radix top-k over long rows is replayed
 several times, with eager runs of the same calls on the same workspaces and
 unrelated GPU work between the replays.  Every replay must give the eager
 results bit for bit: no stale workspace state carried between launches, no
@@ -57,7 +58,8 @@ def test_graph_replays_match_eager():
     sizes = dict(topk=csa.workspace_bytes(csa.WS_TOPK, w.B, 1, w.k, N),
                  attn=csa.workspace_bytes(csa.WS_SPARSE_ATTN, w.B, 1, w.H, w.k, w.n_win),
                  pool=csa.workspace_bytes(csa.WS_INDEX_POOL, w.B, 1, PN, N, PB),
-                 radix=csa.workspace_bytes(csa.WS_TOPK, 2, 1, LK, LN))
+                 radix=csa.workspace_bytes(csa.WS_TOPK, 2, 1, LK, LN),
+                 dense=csa.workspace_bytes(csa.WS_DENSE_ATTN, w.B, 1, w.H, N, w.n_win))
     # the paths under test: two-stage and radix top-k, split attention
     assert sizes["topk"] > 0 and sizes["attn"] > 0 and sizes["radix"] > 0
     ws = {k: torch.empty(max(v, 16), dtype=torch.uint8, device=DEV) for k, v in sizes.items()}
@@ -74,7 +76,9 @@ def test_graph_replays_match_eager():
                     rope=torch.empty(w.B, w.n_win, 64, dtype=torch.bfloat16, device=DEV),
                     out8=torch.empty(w.B, 1, w.H, 576, dtype=torch.float32, device=DEV),
                     lse8=torch.empty(w.B, 1, w.H, dtype=torch.float32, device=DEV),
-                    lidx=torch.empty(2, 1, LK, dtype=torch.int32, device=DEV))
+                    lidx=torch.empty(2, 1, LK, dtype=torch.int32, device=DEV),
+                    dout=torch.empty(w.B, 1, w.H, 576, dtype=torch.float32, device=DEV),
+                    dlse=torch.empty(w.B, 1, w.H, dtype=torch.float32, device=DEV))
 
     def step(o):
         o["scores"].fill_(0.0)   # slots the indexer leaves unwritten start from a fixed value
@@ -88,12 +92,17 @@ def test_graph_replays_match_eager():
         csa.sparse_attn_w8(cache, qs["q"], qs["q_pos"], o["idx"], sw8, s0, w.n_win, w.softmax_scale,
                            out_dtype=torch.float32, ws=ws["attn"], out=o["out8"], lse=o["lse8"])
         csa.topk(long_cache, long_sc, long_pos, LK, out=o["lidx"], ws=ws["radix"])
+        # dense attention over every entry: 52 splits per row, merged four
+        # lanes per output group in two rounds of loads per lane
+        csa.hca_dense_attn(cache, qs["q"], qs["q_pos"], win, s0, w.n_win, w.softmax_scale,
+                           out_dtype=torch.float32, ws=ws["dense"], out=o["dout"], lse=o["dlse"])
 
     ref = outputs()
     step(ref)
     torch.cuda.synchronize()
     assert bool((ref["idx"] >= 0).all()) and bool((ref["lidx"][0] >= 0).all())
     assert torch.isfinite(ref["lse"]).all() and torch.isfinite(ref["lse8"]).all()
+    assert torch.isfinite(ref["dlse"]).all()
 
     g_out = outputs()
     side = torch.cuda.Stream()

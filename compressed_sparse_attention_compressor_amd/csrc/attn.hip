@@ -788,7 +788,13 @@ __global__ __launch_bounds__(kMergeThreads) void attn_merge_kernel(const float *
   const int64_t qh = item / kGroups;  // qrow * H + head
   const int c8 = (int)(item % kGroups) * 8;
   const int64_t qrow = qh / H, hh = qh % H;
-  auto pr_of = [&](int s) { return (qrow * nsplit + s) * H + hh; };
+  // Split s of this item: partial row (qrow * nsplit + s) * H + hh.  The
+  // row's base is formed once in 64 bits; a split's offset from it,
+  // s * H * (kD + 2) elements at most, stays far below 2^31.
+  const int64_t pr0 = qrow * nsplit * H + hh;
+  const float *ml_base = ws_ml + pr0 * 2;
+  const uint16_t *o16_base = reinterpret_cast<const uint16_t *>(ws_o) + pr0 * kD + c8;
+  const float *o32_base = ws_o + pr0 * kD + c8;
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   float L = 0.f;
   float M = -INFINITY;
@@ -798,13 +804,13 @@ __global__ __launch_bounds__(kMergeThreads) void attn_merge_kernel(const float *
     uint4 raw[kBf16 ? kU : 2 * kU];
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
-      const int64_t pr = pr_of(min(t + kT * (u0 + u), nsplit - 1));
-      ml[u] = *reinterpret_cast<const float2 *>(ws_ml + pr * 2);
+      const int ds = min(t + kT * (u0 + u), nsplit - 1) * H;  // partial rows past the base
+      ml[u] = *reinterpret_cast<const float2 *>(ml_base + ds * 2);
       if (kBf16) {
-        raw[u] = *reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(ws_o) + pr * kD + c8);
+        raw[u] = *reinterpret_cast<const uint4 *>(o16_base + ds * kD);
       } else {
-        raw[2 * u] = *reinterpret_cast<const uint4 *>(ws_o + pr * kD + c8);
-        raw[2 * u + 1] = *reinterpret_cast<const uint4 *>(ws_o + pr * kD + c8 + 4);
+        raw[2 * u] = *reinterpret_cast<const uint4 *>(o32_base + ds * kD);
+        raw[2 * u + 1] = *reinterpret_cast<const uint4 *>(o32_base + ds * kD + 4);
       }
     }
     // running maximum over the splits seen so far; earlier sums are rescaled
@@ -814,13 +820,15 @@ __global__ __launch_bounds__(kMergeThreads) void attn_merge_kernel(const float *
     for (int u = 0; u < kU; ++u)
       if (t + kT * (u0 + u) < nsplit) Mn = fmaxf(Mn, ml[u].x);
     if (Mn != -INFINITY) {
-      const float r = M == -INFINITY ? 0.f : exp2f(M - Mn);
+      // v_exp_f32 directly: a weight below 2^-126 of the largest adds nothing
+      const float r = M == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(M - Mn);
       L *= r;
 #pragma unroll
       for (int j = 0; j < 8; ++j) acc[j] *= r;
 #pragma unroll
       for (int u = 0; u < kU; ++u) {
-        const float wgt = (t + kT * (u0 + u) < nsplit && ml[u].x != -INFINITY) ? exp2f(ml[u].x - Mn) : 0.f;
+        const float wgt =
+            (t + kT * (u0 + u) < nsplit && ml[u].x != -INFINITY) ? __builtin_amdgcn_exp2f(ml[u].x - Mn) : 0.f;
         L += wgt * (wgt != 0.f ? ml[u].y : 0.f);
         float v[8];
         if (kBf16) {
@@ -849,8 +857,8 @@ __global__ __launch_bounds__(kMergeThreads) void attn_merge_kernel(const float *
     auto mv = [](float x) { return __int_as_float(dpp_i32<kCtrl>(__float_as_int(x))); };
     const float Mp = mv(M), Lp = mv(L);
     const float Mn = fmaxf(M, Mp);
-    const float ws = M == -INFINITY ? 0.f : exp2f(M - Mn);
-    const float wp = Mp == -INFINITY ? 0.f : exp2f(Mp - Mn);
+    const float ws = M == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(M - Mn);
+    const float wp = Mp == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(Mp - Mn);
     L = L * ws + Lp * wp;
 #pragma unroll
     for (int j = 0; j < 8; ++j) acc[j] = acc[j] * ws + mv(acc[j]) * wp;

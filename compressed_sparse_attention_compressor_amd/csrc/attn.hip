@@ -502,35 +502,45 @@ __global__ __launch_bounds__(HG * 128) void attn_kernel(AttnArgs a) {
   // rows as V.
   auto softmax_pv = [&](const uint16_t *K, const v4f &S0, const v4f &S1, bool kv0, bool kv1)
                         __attribute__((always_inline)) {
-    float alpha[4], p0[4], p1[4];
+    float p0[4], p1[4], mold[4], mref[4];
+    bool moved = false;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const float x0 = kv0 ? S0[i] * a.scale_log2 : -INFINITY;
-      const float x1 = kv1 ? S1[i] * a.scale_log2 : -INFINITY;
-      const float tmax = row16_max(fmaxf(x0, x1));
+      // raw logits, masked; the scale (positive) is applied to the row
+      // maximum and inside the exponent (max(a c, b c) = c max(a, b) exactly)
+      const float r0 = kv0 ? S0[i] : -INFINITY;
+      const float r1 = kv1 ? S1[i] : -INFINITY;
+      const float tmax = row16_max(fmaxf(r0, r1)) * a.scale_log2;
       // The running maximum moves only when the chunk's maximum exceeds it by
       // more than 2^8 (or on the first keys): the result is the same for any
       // reference value, probabilities stay below 256, and the rescale of O
       // below is skipped in the common case.
       const float mn = (tmax > m2[i] + 8.f) ? tmax : m2[i];
       // branch-free: with no key yet (mn = -inf) the reference 0 gives
-      // p = 0 and alpha = 0 on an empty state.  v_exp_f32 directly: results
-      // below 2^-126 of the reference do not matter to these sums.
-      const float mref = mn == -INFINITY ? 0.f : mn;
-      alpha[i] = __builtin_amdgcn_exp2f(m2[i] - mref);
-      p0[i] = __builtin_amdgcn_exp2f(x0 - mref);
-      p1[i] = __builtin_amdgcn_exp2f(x1 - mref);
-      lsum[i] = lsum[i] * alpha[i] + row16_sum(p0[i] + p1[i]);
+      // p = 0 (and alpha = 0 below on an empty state).  v_exp_f32 directly:
+      // results below 2^-126 of the reference do not matter to these sums.
+      mref[i] = mn == -INFINITY ? 0.f : mn;
+      p0[i] = __builtin_amdgcn_exp2f(fmaf(r0, a.scale_log2, -mref[i]));
+      p1[i] = __builtin_amdgcn_exp2f(fmaf(r1, a.scale_log2, -mref[i]));
+      moved = moved || mn != m2[i];
+      mold[i] = m2[i];
       m2[i] = mn;
     }
-    const bool moved = alpha[0] != 1.f || alpha[1] != 1.f || alpha[2] != 1.f || alpha[3] != 1.f;
     if (__builtin_amdgcn_ballot_w64(moved)) {
+      float alpha[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        alpha[i] = __builtin_amdgcn_exp2f(mold[i] - mref[i]);
+        lsum[i] *= alpha[i];
+      }
 #pragma unroll
       for (int j = 0; j < kHalfNT; ++j) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) O[j][i] *= alpha[i];
       }
     }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) lsum[i] += row16_sum(p0[i] + p1[i]);
     // P (bf16, or hi + lo) through this wave's LDS tile into the A layout
     // (LDS operations of one wave complete in order).  The product's key
     // order is permuted against the tile rows: MFMA key 8b + 4h + e (b < 4,

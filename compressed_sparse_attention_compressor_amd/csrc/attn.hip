@@ -38,6 +38,11 @@
 namespace csa {
 
 constexpr int kKC = 32;           // key slots per chunk
+// The running maximum before any key: finite, so that it can serve as the
+// exponent's reference as it is (exp2 of a logit minus it is 0 for a masked
+// key, -inf, and for a real one it is replaced first), and far below every
+// logit in the log2 domain.
+constexpr float kNoMax = -3.0e38f;
 // Key-major LDS row (bf16 elements).  Padding of 16 elements: with a
 // 1184-byte row the Q K^T operand reads (16 rows x 16 bytes per lane group)
 // run conflict-free, measured 4 LDS cycles per instruction against 8 with
@@ -440,7 +445,7 @@ __global__ __launch_bounds__(HG * 128) void attn_kernel(AttnArgs a) {
   v4f O[kHalfNT];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    m2[i] = -INFINITY;
+    m2[i] = kNoMax;
     lsum[i] = 0.f;
   }
 #pragma unroll
@@ -516,10 +521,11 @@ __global__ __launch_bounds__(HG * 128) void attn_kernel(AttnArgs a) {
       // reference value, probabilities stay below 256, and the rescale of O
       // below is skipped in the common case.
       const float mn = (tmax > m2[i] + 8.f) ? tmax : m2[i];
-      // branch-free: with no key yet (mn = -inf) the reference 0 gives
-      // p = 0 (and alpha = 0 below on an empty state).  v_exp_f32 directly:
-      // results below 2^-126 of the reference do not matter to these sums.
-      mref[i] = mn == -INFINITY ? 0.f : mn;
+      // With no key yet the reference is kNoMax and every p is 0 (masked
+      // logits are -inf); the first keys move it (alpha = 0 below on the
+      // empty state).  v_exp_f32 directly: results below 2^-126 of the
+      // reference do not matter to these sums.
+      mref[i] = mn;
       p0[i] = __builtin_amdgcn_exp2f(fmaf(r0, a.scale_log2, -mref[i]));
       p1[i] = __builtin_amdgcn_exp2f(fmaf(r1, a.scale_log2, -mref[i]));
       moved = moved || mn != m2[i];
@@ -716,7 +722,7 @@ __global__ __launch_bounds__(HG * 128) void attn_kernel(AttnArgs a) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int64_t pr = (qrow * a.nsplit + split) * a.H + h0 + 4 * g + i;
-        a.ws_ml[pr * 2 + 0] = m2[i];
+        a.ws_ml[pr * 2 + 0] = lsum[i] > 0.f ? m2[i] : -INFINITY;  // -inf: a split without keys
         a.ws_ml[pr * 2 + 1] = lsum[i];
       }
     }
@@ -755,7 +761,7 @@ __global__ __launch_bounds__(HG * 128) void attn_kernel(AttnArgs a) {
         for (int j = 0; j < kHalfNT; ++j) o[16 * j + r] = O[j][i];
       }
       if (r == 0 && half == 0) {
-        a.ws_ml[pr * 2 + 0] = m2[i];
+        a.ws_ml[pr * 2 + 0] = lsum[i] > 0.f ? m2[i] : -INFINITY;  // -inf: a split without keys
         a.ws_ml[pr * 2 + 1] = lsum[i];
       }
     }

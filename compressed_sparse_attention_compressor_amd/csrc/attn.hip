@@ -19,14 +19,17 @@
 //      converts two codes per instruction); the raw bytes of the next chunk
 //      are fetched into registers while the current one is computed (the
 //      tile and the slot lists are multi-buffered, one barrier per chunk);
-//   2. S = Q K^T on v_mfma_f32_16x16x32_bf16 (lane: key l%16, heads
-//      4(l/16)..+3), online softmax in the log2 domain with DPP row
-//      reductions (both waves of a pair hold bit-identical logits);
-//   3. P goes through a small per-wave LDS tile to become the A operand of
-//      O += P V; the V operand (keys along K) is read transposed from the
-//      same key-major tile with ds_read_b64_tr_b16, so no second copy of
-//      the keys is written.  With fp32 outputs P is split into two bf16
-//      parts (hi + lo) so that the probabilities keep ~16 bits.
+//   2. S^T = K Q^T on v_mfma_f32_16x16x32_bf16 (lane (g, r): head r, keys
+//      4g..4g+3 of each 16-key tile), online softmax per head in the log2
+//      domain, reduced in registers and across the lane groups by permlane
+//      swaps (both waves of a pair hold bit-identical logits);
+//   3. the lane's 8 probabilities are its A operand of O += P V as they are
+//      (the MFMA key order is permuted against the tile rows to match), so
+//      P never goes through LDS; the V operand (keys along K) is read
+//      transposed from the same key-major tile with ds_read_b64_tr_b16, so
+//      no second copy of the keys is written.  With fp32 outputs P is split
+//      into two bf16 parts (hi + lo) so that the probabilities keep ~16
+//      bits.
 // Splits write unnormalised (O, max, sum) partials that a merge kernel
 // combines; a single split writes the normalised output directly.
 #include <cmath>
@@ -48,7 +51,6 @@ constexpr float kNoMax = -3.0e38f;
 // run conflict-free, measured 4 LDS cycles per instruction against 8 with
 // 8 elements of padding.
 constexpr int kKRow = kD + 16;
-constexpr int kPRow = kKC + 8;
 constexpr int kHalfD = kD / 2;    // output channels per wave of a pair
 constexpr int kHalfNT = kHalfD / 16;  // 18 channel tiles of 16 (P V)
 constexpr int kKSteps = kD / 32;  // 18 channel steps of 32 (Q K^T)
@@ -103,6 +105,23 @@ __device__ __forceinline__ bool xcd_slot(int L, int per_row, int rows, int &row,
   row = x + 8 * (sidx / per_row);
   part = sidx % per_row;
   return row < rows;
+}
+
+// Reductions over the four lane groups g (lanes r, r + 16, r + 32, r + 48):
+// a swap of the 32-lane halves, then of the 16-lane rows inside them.  Every
+// lane takes the same operands in the same order, so the four groups end
+// with the same bits.
+__device__ __forceinline__ float allgroups_max(float v) {
+  const auto x = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(x[0]), __uint_as_float(x[1]));
+  const auto y = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(y[0]), __uint_as_float(y[1]));
+}
+__device__ __forceinline__ float allgroups_sum(float v) {
+  const auto x = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(x[0]) + __uint_as_float(x[1]);
+  const auto y = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(y[0]) + __uint_as_float(y[1]);
 }
 
 // cos and sin of the rotary angle of pair i at position pos: the angle in
@@ -347,11 +366,10 @@ __global__ __launch_bounds__(HG * 128) void attn_kernel(AttnArgs a) {
   // Key-major bf16 tiles of the chunk (double buffered); the P V operand is
   // read transposed from the same tile with ds_read_b64_tr_b16.
   __shared__ __attribute__((aligned(16))) uint16_t Kl[2][kKC * kKRow];
-  __shared__ __attribute__((aligned(16))) uint16_t Pl[2 * HG][kSplitP ? 2 : 1][16 * kPRow];
   __shared__ __attribute__((aligned(16))) float Sx[2 * HG][2 * 4 * 64];
   // Slot lists of three consecutive chunks: the list of chunk c + 1 is
   // written while a slower wave may still read that of chunk c.
-  __shared__ int src_s[3][kKC];
+  __shared__ __attribute__((aligned(16))) int src_s[3][kKC];
 
   int row_id, split;
   if (a.xcd) {
@@ -441,13 +459,10 @@ __global__ __launch_bounds__(HG * 128) void attn_kernel(AttnArgs a) {
     }
   };
 
-  float m2[4], lsum[4];
+  // Softmax state of head r (lane (g, r); the four lane groups hold the same
+  // bits): the running maximum in the log2 domain and the running sum.
+  float hm = kNoMax, hl = 0.f;
   v4f O[kHalfNT];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    m2[i] = kNoMax;
-    lsum[i] = 0.f;
-  }
 #pragma unroll
   for (int j = 0; j < kHalfNT; ++j) O[j] = v4f{0.f, 0.f, 0.f, 0.f};
 
@@ -467,8 +482,11 @@ __global__ __launch_bounds__(HG * 128) void attn_kernel(AttnArgs a) {
     publish_slot(s_begin, j0, 0);
   }
 
-  // S = Q K^T of one chunk for two tiles of 16 keys (two independent MFMA
-  // chains), over this wave's channels.
+  // S^T = K Q^T of one chunk for two tiles of 16 keys (two independent MFMA
+  // chains), over this wave's channels: the key tile is the A operand and
+  // the query the B operand (the same registers as Q K^T, in the other
+  // slots), so lane (g, r) gets head r's logits for tile rows 4g..4g+3
+  // (S0) and 16+4g..16+4g+3 (S1).
   auto qk_part = [&](const uint16_t *K, v4f &S0, v4f &S1) __attribute__((always_inline)) {
     S0 = v4f{0.f, 0.f, 0.f, 0.f};
     S1 = v4f{0.f, 0.f, 0.f, 0.f};
@@ -477,9 +495,9 @@ __global__ __launch_bounds__(HG * 128) void attn_kernel(AttnArgs a) {
       const uint16_t *k1 = k0 + 16 * kKRow;
 #pragma unroll
       for (int kk = 0; kk < kQSteps; ++kk) {
-        S0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Qf[kk], *reinterpret_cast<const v8bf *>(k0 + 32 * kk), S0, 0, 0,
+        S0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*reinterpret_cast<const v8bf *>(k0 + 32 * kk), Qf[kk], S0, 0, 0,
                                                      0);
-        S1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Qf[kk], *reinterpret_cast<const v8bf *>(k1 + 32 * kk), S1, 0, 0,
+        S1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*reinterpret_cast<const v8bf *>(k1 + 32 * kk), Qf[kk], S1, 0, 0,
                                                      0);
       }
     }
@@ -505,74 +523,76 @@ __global__ __launch_bounds__(HG * 128) void attn_kernel(AttnArgs a) {
   };
   // Online softmax of one chunk's logits, then O += P V with the chunk's
   // rows as V.
-  auto softmax_pv = [&](const uint16_t *K, const v4f &S0, const v4f &S1, bool kv0, bool kv1)
+  // Online softmax of one chunk's logits for head r, then O += P V with the
+  // chunk's rows as V.  src: the chunk's slot list (-1 = no key).
+  auto softmax_pv = [&](const uint16_t *K, const v4f &S0, const v4f &S1, const int *src)
                         __attribute__((always_inline)) {
-    float p0[4], p1[4], mold[4], mref[4];
-    bool moved = false;
+    const int4 s0 = *reinterpret_cast<const int4 *>(src + 4 * g);
+    const int4 s1 = *reinterpret_cast<const int4 *>(src + 16 + 4 * g);
+    const int sv[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+    // raw logits, masked; the scale (positive) is applied to the row
+    // maximum and inside the exponent (max(a c, b c) = c max(a, b) exactly)
+    float x[8];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      // raw logits, masked; the scale (positive) is applied to the row
-      // maximum and inside the exponent (max(a c, b c) = c max(a, b) exactly)
-      const float r0 = kv0 ? S0[i] : -INFINITY;
-      const float r1 = kv1 ? S1[i] : -INFINITY;
-      const float tmax = row16_max(fmaxf(r0, r1)) * a.scale_log2;
-      // The running maximum moves only when the chunk's maximum exceeds it by
-      // more than 2^8 (or on the first keys): the result is the same for any
-      // reference value, probabilities stay below 256, and the rescale of O
-      // below is skipped in the common case.
-      const float mn = (tmax > m2[i] + 8.f) ? tmax : m2[i];
-      // With no key yet the reference is kNoMax and every p is 0 (masked
-      // logits are -inf); the first keys move it (alpha = 0 below on the
-      // empty state).  v_exp_f32 directly: results below 2^-126 of the
-      // reference do not matter to these sums.
-      mref[i] = mn;
-      p0[i] = __builtin_amdgcn_exp2f(fmaf(r0, a.scale_log2, -mref[i]));
-      p1[i] = __builtin_amdgcn_exp2f(fmaf(r1, a.scale_log2, -mref[i]));
-      moved = moved || mn != m2[i];
-      mold[i] = m2[i];
-      m2[i] = mn;
+      x[i] = sv[i] >= 0 ? S0[i] : -INFINITY;
+      x[4 + i] = sv[4 + i] >= 0 ? S1[i] : -INFINITY;
     }
-    if (__builtin_amdgcn_ballot_w64(moved)) {
-      float alpha[4];
+    // head r's maximum: the lane's 8 keys, then the four lane groups
+    // (permlane swaps of the 32-lane and 16-lane halves; every group ends
+    // with the same bits)
+    float mx = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])), fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
+    mx = allgroups_max(mx);
+    const float tmax = mx * a.scale_log2;
+    // The running maximum moves only when the chunk's maximum exceeds it by
+    // more than 2^8 (or on the first keys): the result is the same for any
+    // reference value, probabilities stay below 256, and the rescale of O
+    // below is skipped in the common case.  With no key yet the reference
+    // is kNoMax and every p is 0 (masked logits are -inf); the first keys
+    // move it (alpha = 0 on the empty state).  v_exp_f32 directly: results
+    // below 2^-126 of the reference do not matter to these sums.
+    const float mn = (tmax > hm + 8.f) ? tmax : hm;
+    float pv[8];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        alpha[i] = __builtin_amdgcn_exp2f(mold[i] - mref[i]);
-        lsum[i] *= alpha[i];
-      }
+    for (int e = 0; e < 8; ++e) pv[e] = __builtin_amdgcn_exp2f(fmaf(x[e], a.scale_log2, -mn));
+    if (__builtin_amdgcn_ballot_w64(mn != hm)) {
+      // O rows are heads 4g..4g+3 (lane (g, r)); their factors come from
+      // lanes 16g + 4g + i, whose head is 4g + i
+      const float alpha = __builtin_amdgcn_exp2f(hm - mn);
+      hl *= alpha;
+      float al[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        al[i] = __int_as_float(__builtin_amdgcn_ds_bpermute(4 * (20 * g + i), __float_as_int(alpha)));
 #pragma unroll
       for (int j = 0; j < kHalfNT; ++j) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) O[j][i] *= alpha[i];
+        for (int i = 0; i < 4; ++i) O[j][i] *= al[i];
       }
     }
+    hm = mn;
+    hl += allgroups_sum(((pv[0] + pv[1]) + (pv[2] + pv[3])) + ((pv[4] + pv[5]) + (pv[6] + pv[7])));
+    // P stays in registers: lane (g, r) holds P[head r][MFMA keys 8g..8g+7],
+    // exactly its A operand of P V.  The product's key order is permuted
+    // against the tile rows: MFMA key 8b + 4h + e (b < 4, h, e < 4) is tile
+    // row 16h + 4b + e, so that each transposed V read below covers 8
+    // consecutive rows per 32 lanes, which a 1184-byte row stride spreads
+    // over all LDS banks (measured conflict-free); with b = g that is tile
+    // rows 4g + e (S0) and 16 + 4g + e (S1), the lane's own logits.
+    uint32_t hi[8];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) lsum[i] += row16_sum(p0[i] + p1[i]);
-    // P (bf16, or hi + lo) through this wave's LDS tile into the A layout
-    // (LDS operations of one wave complete in order).  The product's key
-    // order is permuted against the tile rows: MFMA key 8b + 4h + e (b < 4,
-    // h, e < 4) is tile row 16h + 4b + e, so that each transposed V read
-    // below covers 8 consecutive rows per 32 lanes, which a 1184-byte row
-    // stride spreads over all LDS banks (measured conflict-free); tile row
-    // r goes to P column 8(r/4) + r%4, tile row 16 + r to 8(r/4) + 4 + r%4.
-    uint16_t *pw = &Pl[wave][0][0];
-    const int pc0 = 8 * (r >> 2) + (r & 3);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint32_t hi0 = f32_to_bf16(p0[i]), hi1 = f32_to_bf16(p1[i]);
-      pw[(4 * g + i) * kPRow + pc0] = (uint16_t)hi0;
-      pw[(4 * g + i) * kPRow + pc0 + 4] = (uint16_t)hi1;
-      if (kSplitP) {
-        uint16_t *pl = &Pl[wave][kSplitP ? 1 : 0][0];
-        pl[(4 * g + i) * kPRow + pc0] = (uint16_t)f32_to_bf16(p0[i] - bf16_to_f32(hi0));
-        pl[(4 * g + i) * kPRow + pc0 + 4] = (uint16_t)f32_to_bf16(p1[i] - bf16_to_f32(hi1));
-      }
-    }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
-    const v8bf Pa = *reinterpret_cast<const v8bf *>(&Pl[wave][0][r * kPRow + 8 * g]);
+    for (int e = 0; e < 8; ++e) hi[e] = f32_to_bf16(pv[e]);
+    const v8bf Pa = __builtin_bit_cast(
+        v8bf, uint4{hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16), hi[4] | (hi[5] << 16), hi[6] | (hi[7] << 16)});
     v8bf Pb;
-    if (kSplitP) Pb = *reinterpret_cast<const v8bf *>(&Pl[wave][kSplitP ? 1 : 0][r * kPRow + 8 * g]);
+    if (kSplitP) {
+      // fp32 outputs: the probabilities as bf16 hi + lo (about 16 bits)
+      uint32_t lo[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) lo[e] = f32_to_bf16(pv[e] - bf16_to_f32(hi[e]));
+      Pb = __builtin_bit_cast(
+          v8bf, uint4{lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16), lo[4] | (lo[5] << 16), lo[6] | (lo[7] << 16)});
+    }
     // O += P V over this wave's 18 channel tiles; lane (g, r) needs
     // V[MFMA keys 8g..8g+7][channel c + r], i.e. tile rows 4g..4g+3 and
     // 16+4g..16+4g+3: two transposed 4x16 reads of the key-major tile.
@@ -580,20 +600,20 @@ __global__ __launch_bounds__(HG * 128) void attn_kernel(AttnArgs a) {
     const uint16_t *vb = K + (4 * g + (r >> 2)) * kKRow + cbase + 4 * (r & 3);
 #pragma unroll
     for (int j = 0; j < kHalfNT; ++j) {
-      const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s *)(vb + 16 * j));
-      const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s *)(vb + 16 * kKRow + 16 * j));
-      const v8s both = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+      const v4s lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s *)(vb + 16 * j));
+      const v4s hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s *)(vb + 16 * kKRow + 16 * j));
+      const v8s both = __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
       const v8bf Bv = __builtin_bit_cast(v8bf, both);
       O[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Pa, Bv, O[j], 0, 0, 0);
       if (kSplitP) O[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Pb, Bv, O[j], 0, 0, 0);
     }
   };
   // One chunk of decoded keys in K: logits, online softmax, O += P V.
-  auto compute_chunk = [&](const uint16_t *K, bool kv0, bool kv1) __attribute__((always_inline)) {
+  auto compute_chunk = [&](const uint16_t *K, const int *src) __attribute__((always_inline)) {
     v4f S0, S1;
     qk_part(K, S0, S1);
     exchange(S0, S1);
-    softmax_pv(K, S0, S1, kv0, kv1);
+    softmax_pv(K, S0, S1, src);
   };
 
   // Chunks of one kind in [c_lo, c_hi): decode the fetched rows into K,
@@ -638,9 +658,8 @@ __global__ __launch_bounds__(HG * 128) void attn_kernel(AttnArgs a) {
       }
       publish_slot(c0 + kKC, jn, sn);
       lds_barrier();
-      const bool kv0 = src_s[sb][r] >= 0, kv1 = src_s[sb][16 + r] >= 0;
       if (CS::kAhead) ld(sn);
-      compute_chunk(K, kv0, kv1);
+      compute_chunk(K, src_s[sb]);
     }
   };
   const int e_hi = min(s_end, n_main_pad);
@@ -667,6 +686,13 @@ __global__ __launch_bounds__(HG * 128) void attn_kernel(AttnArgs a) {
         O[j][i] = mine * cs.x + other * sn;
       }
     }
+  }
+  // The state of the output rows' heads 4g + i, from lanes 16g + 4g + i.
+  float m2[4], lsum[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    m2[i] = __int_as_float(__builtin_amdgcn_ds_bpermute(4 * (20 * g + i), __float_as_int(hm)));
+    lsum[i] = __int_as_float(__builtin_amdgcn_ds_bpermute(4 * (20 * g + i), __float_as_int(hl)));
   }
   const int h0 = hg * 16;
   // bf16 results leave through LDS as 16-byte stores: the wave's 16 heads x

@@ -107,6 +107,14 @@ __device__ __forceinline__ bool xcd_slot(int L, int per_row, int rows, int &row,
   return row < rows;
 }
 
+// Two fp32 values as bf16 (round to nearest even) in one word, low first:
+// one v_cvt_pk_bf16_f32.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  typedef float v2f_t __attribute__((ext_vector_type(2)));
+  typedef __bf16 v2bf_t __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v2f_t{lo, hi}, v2bf_t));
+}
+
 // Reductions over the four lane groups g (lanes r, r + 16, r + 32, r + 48):
 // a swap of the 32-lane halves, then of the 16-lane rows inside them.  Every
 // lane takes the same operands in the same order, so the four groups end
@@ -370,6 +378,8 @@ __global__ __launch_bounds__(HG * 128) void attn_kernel(AttnArgs a) {
   // Slot lists of three consecutive chunks: the list of chunk c + 1 is
   // written while a slower wave may still read that of chunk c.
   __shared__ __attribute__((aligned(16))) int src_s[3][kKC];
+  // per slot of those lists: 0 for a key, -inf for none (added to the logit)
+  __shared__ __attribute__((aligned(16))) float bias_s[3][kKC];
 
   int row_id, split;
   if (a.xcd) {
@@ -456,6 +466,7 @@ __global__ __launch_bounds__(HG * 128) void attn_kernel(AttnArgs a) {
         }
       }
       src_s[sb][tid] = src;
+      bias_s[sb][tid] = src >= 0 ? 0.f : -INFINITY;
     }
   };
 
@@ -524,20 +535,16 @@ __global__ __launch_bounds__(HG * 128) void attn_kernel(AttnArgs a) {
   // Online softmax of one chunk's logits, then O += P V with the chunk's
   // rows as V.
   // Online softmax of one chunk's logits for head r, then O += P V with the
-  // chunk's rows as V.  src: the chunk's slot list (-1 = no key).
-  auto softmax_pv = [&](const uint16_t *K, const v4f &S0, const v4f &S1, const int *src)
+  // chunk's rows as V.  bias: the chunk's slot biases (0 / -inf).
+  auto softmax_pv = [&](const uint16_t *K, const v4f &S0, const v4f &S1, const float *bias)
                         __attribute__((always_inline)) {
-    const int4 s0 = *reinterpret_cast<const int4 *>(src + 4 * g);
-    const int4 s1 = *reinterpret_cast<const int4 *>(src + 16 + 4 * g);
-    const int sv[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
-    // raw logits, masked; the scale (positive) is applied to the row
-    // maximum and inside the exponent (max(a c, b c) = c max(a, b) exactly)
-    float x[8];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      x[i] = sv[i] >= 0 ? S0[i] : -INFINITY;
-      x[4 + i] = sv[4 + i] >= 0 ? S1[i] : -INFINITY;
-    }
+    const float4 b0 = *reinterpret_cast<const float4 *>(bias + 4 * g);
+    const float4 b1 = *reinterpret_cast<const float4 *>(bias + 16 + 4 * g);
+    // raw logits, masked by adding the slot's 0 / -inf (exact either way);
+    // the scale (positive) is applied to the row maximum and inside the
+    // exponent (max(a c, b c) = c max(a, b) exactly)
+    const float x[8] = {S0[0] + b0.x, S0[1] + b0.y, S0[2] + b0.z, S0[3] + b0.w,
+                        S1[0] + b1.x, S1[1] + b1.y, S1[2] + b1.z, S1[3] + b1.w};
     // head r's maximum: the lane's 8 keys, then the four lane groups
     // (permlane swaps of the 32-lane and 16-lane halves; every group ends
     // with the same bits)
@@ -579,19 +586,19 @@ __global__ __launch_bounds__(HG * 128) void attn_kernel(AttnArgs a) {
     // consecutive rows per 32 lanes, which a 1184-byte row stride spreads
     // over all LDS banks (measured conflict-free); with b = g that is tile
     // rows 4g + e (S0) and 16 + 4g + e (S1), the lane's own logits.
-    uint32_t hi[8];
+    uint32_t hw[4];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) hi[e] = f32_to_bf16(pv[e]);
-    const v8bf Pa = __builtin_bit_cast(
-        v8bf, uint4{hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16), hi[4] | (hi[5] << 16), hi[6] | (hi[7] << 16)});
+    for (int e = 0; e < 4; ++e) hw[e] = pack_bf16x2(pv[2 * e], pv[2 * e + 1]);
+    const v8bf Pa = __builtin_bit_cast(v8bf, uint4{hw[0], hw[1], hw[2], hw[3]});
     v8bf Pb;
     if (kSplitP) {
       // fp32 outputs: the probabilities as bf16 hi + lo (about 16 bits)
-      uint32_t lo[8];
+      uint32_t lw[4];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) lo[e] = f32_to_bf16(pv[e] - bf16_to_f32(hi[e]));
-      Pb = __builtin_bit_cast(
-          v8bf, uint4{lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16), lo[4] | (lo[5] << 16), lo[6] | (lo[7] << 16)});
+      for (int e = 0; e < 4; ++e)
+        lw[e] = pack_bf16x2(pv[2 * e] - __uint_as_float(hw[e] << 16),
+                            pv[2 * e + 1] - __uint_as_float(hw[e] & 0xFFFF0000u));
+      Pb = __builtin_bit_cast(v8bf, uint4{lw[0], lw[1], lw[2], lw[3]});
     }
     // O += P V over this wave's 18 channel tiles; lane (g, r) needs
     // V[MFMA keys 8g..8g+7][channel c + r], i.e. tile rows 4g..4g+3 and
@@ -609,11 +616,11 @@ __global__ __launch_bounds__(HG * 128) void attn_kernel(AttnArgs a) {
     }
   };
   // One chunk of decoded keys in K: logits, online softmax, O += P V.
-  auto compute_chunk = [&](const uint16_t *K, const int *src) __attribute__((always_inline)) {
+  auto compute_chunk = [&](const uint16_t *K, const float *bias) __attribute__((always_inline)) {
     v4f S0, S1;
     qk_part(K, S0, S1);
     exchange(S0, S1);
-    softmax_pv(K, S0, S1, src);
+    softmax_pv(K, S0, S1, bias);
   };
 
   // Chunks of one kind in [c_lo, c_hi): decode the fetched rows into K,
@@ -659,7 +666,7 @@ __global__ __launch_bounds__(HG * 128) void attn_kernel(AttnArgs a) {
       publish_slot(c0 + kKC, jn, sn);
       lds_barrier();
       if (CS::kAhead) ld(sn);
-      compute_chunk(K, src_s[sb]);
+      compute_chunk(K, bias_s[sb]);
     }
   };
   const int e_hi = min(s_end, n_main_pad);

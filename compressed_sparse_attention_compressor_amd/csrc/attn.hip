@@ -227,14 +227,14 @@ __device__ __forceinline__ void store_entries(const AttnArgs &a, uint16_t *K, co
       // the four 16-byte quarters of the block are stored in a lane-dependent
       // order, (i + blk + blk / 4) mod 4: lanes of one key row would otherwise
       // hit the same banks (measured 8 LDS cycles per store against 32)
-      const uint32_t cw[4] = {c.x, c.y, c.z, c.w};
+      // the words rotated by rot in two select stages (by 1, then by 2),
+      // so that store i takes quarter (i + rot) & 3 from register i
+      const int rot = (blk + (blk >> 2)) & 3;
+      const bool r1 = rot & 1, r2 = rot & 2;
+      const uint32_t a0 = r1 ? c.y : c.x, a1 = r1 ? c.z : c.y, a2 = r1 ? c.w : c.z, a3 = r1 ? c.x : c.w;
+      const uint32_t cw[4] = {r2 ? a2 : a0, r2 ? a3 : a1, r2 ? a0 : a2, r2 ? a1 : a3};
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int qi = (i + blk + (blk >> 2)) & 3;
-        // the source word by value selects (no selection between array lvalues)
-        const uint32_t w = qi == 0 ? cw[0] : (qi == 1 ? cw[1] : (qi == 2 ? cw[2] : cw[3]));
-        dst[qi] = CSA_CVT4(w);
-      }
+      for (int i = 0; i < 4; ++i) dst[(i + rot) & 3] = CSA_CVT4(cw[i]);
 #undef CSA_CVT4
 #undef CSA_CVT
     } else {
@@ -517,19 +517,18 @@ __global__ __launch_bounds__(HG * 128) void attn_kernel(AttnArgs a) {
   auto exchange = [&](v4f &S0, v4f &S1) __attribute__((always_inline)) {
     // the partner's half of the channels, added in a fixed order of the
     // halves so that both waves of the pair agree bit for bit
-    float *sx = &Sx[wave][0];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      sx[i * 64 + lane] = S0[i];
-      sx[(4 + i) * 64 + lane] = S1[i];
-    }
+    // 8 values per lane as two 16-byte stores and loads
+    float4 *sx = reinterpret_cast<float4 *>(&Sx[wave][0]) + 2 * lane;
+    sx[0] = float4{S0[0], S0[1], S0[2], S0[3]};
+    sx[1] = float4{S1[0], S1[1], S1[2], S1[3]};
     lds_barrier();
-    const float *so = &Sx[wave ^ 1][0];
+    const float4 *so = reinterpret_cast<const float4 *>(&Sx[wave ^ 1][0]) + 2 * lane;
+    const float4 o0 = so[0], o1 = so[1];
+    const float p0[4] = {o0.x, o0.y, o0.z, o0.w}, p1[4] = {o1.x, o1.y, o1.z, o1.w};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const float o0 = so[i * 64 + lane], o1 = so[(4 + i) * 64 + lane];
-      S0[i] = half == 0 ? S0[i] + o0 : o0 + S0[i];
-      S1[i] = half == 0 ? S1[i] + o1 : o1 + S1[i];
+      S0[i] = half == 0 ? S0[i] + p0[i] : p0[i] + S0[i];
+      S1[i] = half == 0 ? S1[i] + p1[i] : p1[i] + S1[i];
     }
   };
   // Online softmax of one chunk's logits, then O += P V with the chunk's
